@@ -1,0 +1,208 @@
+/*
+ * dory.h - C ABI of the looped normalized-GPT forward pass on gfx950 (MI355X).
+ *
+ * The model. An input block of layers runs once, a shared recurrent block
+ * runs n_loops = k times with the input block's output re-injected before
+ * every pass, and an output block runs once ("Dory1.0-4B: A Looped
+ * Normalized-GPT", ai.info summary, Key Contributions 1 and Methodology in
+ * Plain English; goremy.ai blog "Dory 1.0 4B Benchmarks", What is
+ * Dory1.0-4B?). Every layer is an attention sublayer and a SwiGLU sublayer,
+ * each closed by the nGPT hypersphere update
+ *     h <- norm(h + alpha * (norm(y) - h))
+ * (summary, Methodology in Plain English). Attention layers are either
+ * sliding-window or full, with grouped-query heads, RoPE (one base per layer
+ * type), per-head L2-normalised q and k, and a sigmoid output gate (same
+ * section). Keys and values are cached per loop or in last-loop mode, where
+ * every loop overwrites one cache per recurrent layer (goremy.ai blog, How
+ * does looping work at inference time?; broadside review "NVIDIA Nemotron
+ * Labs Dory 1.0 4B", Key ideas).
+ *
+ * Conventions used by every call below.
+ *   - All sizes are element counts unless a name ends in _bytes.
+ *   - "device" pointers are HIP device memory (for example from PyTorch);
+ *     "host" pointers are ordinary CPU memory.
+ *   - The caller owns ALL device memory: weights, the KV buffer and the
+ *     workspace. The library owns only its host-side context. No call after
+ *     dory_create allocates device memory.
+ *   - Compute calls enqueue work on the stream given to dory_create and
+ *     return before it finishes; the caller synchronises that stream before
+ *     it reads results on the host.
+ *   - Validation happens on the host before anything is enqueued. A call
+ *     that returns an error has enqueued nothing and changed no state.
+ *   - The bfloat16 type is passed as its 16-bit pattern (uint16_t storage).
+ */
+#ifndef DORY_H
+#define DORY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DORY_OK = 0,
+  DORY_E_ARG = -1,       /* null pointer, bad size, inconsistent config      */
+  DORY_E_CAPACITY = -2,  /* batch, chunk or context beyond the capacity       */
+  DORY_E_LOOPS = -3,     /* n_loops < 1, > max_loops or > the per-loop caches,
+                            or a loop-count change inside a per-loop sequence */
+  DORY_E_KV_MODE = -4,   /* kv mode other than the one the buffer was laid out for */
+  DORY_E_STATE = -5,     /* decode/logits before any prefill, batch change mid-sequence */
+  DORY_E_HIP = -6        /* a HIP runtime call failed; see dory_last_error   */
+} dory_status;
+
+typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype;
+
+/* Per-loop: one cache per loop of each recurrent attention layer, so KV
+ * memory grows with k. Last-loop: one cache per recurrent layer, overwritten
+ * by every loop; the footprint equals the one-loop size at any k. */
+typedef enum { DORY_KV_PER_LOOP = 0, DORY_KV_LAST_LOOP = 1 } dory_kv_mode;
+
+/* Model shape and capacity. Copied by dory_create (layer_is_full included). */
+typedef struct {
+  int32_t d_model;        /* residual-stream width d                                  */
+  int32_t n_q_heads;      /* query heads                                               */
+  int32_t n_kv_heads;     /* key/value heads; n_q_heads / n_kv_heads in {1,2,3,4,6,8}  */
+  int32_t head_dim;       /* 64 or 128                                                 */
+  int32_t d_ff;           /* SwiGLU hidden width                                       */
+  int32_t vocab;          /* tied embedding / LM-head rows                             */
+  int32_t n_in, n_rec, n_out;   /* input / recurrent / output layers                   */
+  int32_t window;         /* sliding window in keys, the query included: t-W < s <= t  */
+  const uint8_t* layer_is_full; /* host [n_in+n_rec+n_out]: 1 full attention, 0 window */
+  double rope_base_swa;   /* RoPE base of sliding-window layers                        */
+  double rope_base_full;  /* RoPE base of full-attention layers                        */
+  int32_t dtype;          /* dory_dtype of weights, activations and KV cache           */
+  int32_t attn_gate;      /* 0 none, 1 elementwise sigmoid gate, 2 one gate per q head */
+  float attn_scale;       /* softmax scale on q.k of unit vectors; <= 0: sqrt(head_dim) */
+  float logit_scale;      /* LM-head scale; <= 0: sqrt(d_model)                        */
+  float combine_wh;       /* loop re-injection x_j = norm(wh*h_{j-1} + we*e), j >= 2   */
+  float combine_we;
+  int32_t max_batch;      /* sequences per call                                        */
+  int32_t max_ctx;        /* positions per sequence                                    */
+  int32_t max_chunk;      /* positions per prefill chunk (longer prompts are chunked)  */
+  int32_t max_loops;      /* largest n_loops accepted                                  */
+} dory_config;
+
+/* Weights, all device pointers, row-major, of the config's dtype except alpha.
+ * Arrays of per-layer pointers are host arrays of n_layers entries, copied by
+ * dory_create; the device memory they point to must outlive the context.
+ *   embed [vocab, d]                       input embedding and tied LM head
+ *   qkvg  [q_dim + 2*kv_dim + gate_dim, d] rows: q | k | v | gate
+ *         (q_dim = n_q*hd, kv_dim = n_kv*hd, gate_dim = q_dim, n_q or 0)
+ *   o     [d, q_dim]                       attention output projection
+ *   ug    [2*d_ff, d]                      rows 0..d_ff-1: u, rows d_ff..: v;
+ *                                          the activation is u * silu(v)
+ *   down  [d, d_ff]                        MLP down projection
+ *   alpha_attn, alpha_mlp: float32 [d]     per-channel nGPT update weights   */
+typedef struct {
+  const void* embed;
+  const void* const* qkvg;
+  const void* const* o;
+  const void* const* ug;
+  const void* const* down;
+  const float* const* alpha_attn;
+  const float* const* alpha_mlp;
+} dory_weights;
+
+typedef struct dory_ctx dory_ctx;
+
+/* ---- host-only queries (no HIP call; usable without a GPU) -------------- */
+
+/* DORY_OK if the config is consistent and within the kernels' limits. */
+dory_status dory_validate_config(const dory_config* cfg);
+
+/* Bytes of the KV buffer for a kv mode. kv_loops is the number of per-loop
+ * caches per recurrent layer (ignored in last-loop mode). Layout: caches
+ * numbered layer by layer (a recurrent layer in per-loop mode owns kv_loops
+ * consecutive ids, loop j -> base + j - 1); cache c holds K then V, each
+ * [max_batch][n_kv][slots_c][head_dim], with slots = max_ctx for full layers
+ * and min(window, max_ctx) for sliding layers (a ring, slot = pos mod window).
+ * Returns 0 for an invalid config. */
+size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops);
+
+/* Bytes of the workspace dory_create needs (activations for max_batch *
+ * max_chunk rows, attention partials, RoPE tables, logits). 0 if invalid. */
+size_t dory_workspace_bytes(const dory_config* cfg);
+
+/* Where the KV of (layer, loop, pos) lives: cache id, slot, and the element
+ * offsets of K and V of batch row 0, kv head 0 in the KV buffer. loop is
+ * 1-based for recurrent layers and ignored for the others. */
+dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops,
+                         int32_t layer, int32_t loop, int32_t pos,
+                         int32_t* cache_id, int32_t* slot,
+                         int64_t* k_offset, int64_t* v_offset);
+
+const char* dory_status_string(dory_status s);
+
+/* ---- context ------------------------------------------------------------ */
+
+/* Binds caller memory; host-only (no HIP call). The first dory_prefill on
+ * the context builds the RoPE tables (angles in float64, stored float32) in
+ * the workspace on the stream. kv_dev must hold dory_kv_bytes(cfg, kv_mode,
+ * kv_loops) bytes and ws_dev dory_workspace_bytes(cfg); both 256-byte
+ * aligned. stream is a hipStream_t (NULL = the null stream). */
+dory_status dory_create(const dory_config* cfg, const dory_weights* w,
+                        void* kv_dev, size_t kv_bytes, int32_t kv_mode, int32_t kv_loops,
+                        void* ws_dev, size_t ws_bytes, void* stream, dory_ctx** out);
+
+void dory_destroy(dory_ctx* ctx);
+
+/* Forget the sequence: position 0, no kv mode or loop count fixed yet.
+ * Cache contents are not cleared; they are never read before rewritten. */
+dory_status dory_reset(dory_ctx* ctx);
+
+/* Process n prompt positions of `batch` sequences: tokens_dev is device
+ * int32 [batch, n]. Prompts longer than max_chunk are cut into chunks of
+ * max_chunk positions, processed in order. Afterwards the logits of the last
+ * position and its greedy token are held in the context.
+ * Errors: DORY_E_LOOPS, DORY_E_KV_MODE, DORY_E_CAPACITY (pos + n > max_ctx,
+ * batch > max_batch), DORY_E_STATE (batch differs from the sequence's). */
+dory_status dory_prefill(dory_ctx* ctx, const int32_t* tokens_dev, int32_t batch, int32_t n,
+                         int32_t n_loops, int32_t kv_mode);
+
+/* One decode position. tokens_dev: device int32 [batch], or NULL to feed the
+ * greedy tokens of the previous call. next_tokens_dev: device int32 [batch]
+ * that receives the greedy argmax (lowest index on ties), or NULL. In
+ * last-loop mode n_loops may change from call to call; in per-loop mode it
+ * must stay the sequence's. Errors as dory_prefill, plus DORY_E_STATE before
+ * any prefill. */
+dory_status dory_decode_step(dory_ctx* ctx, const int32_t* tokens_dev, int32_t n_loops,
+                             int32_t kv_mode, int32_t* next_tokens_dev);
+
+/* Copy the float32 logits [batch, vocab] of the last processed position to
+ * out_dev (device). DORY_E_STATE before any prefill. */
+dory_status dory_logits(dory_ctx* ctx, float* out_dev);
+
+/* Text of the last error on this context (empty if none). */
+const char* dory_last_error(const dory_ctx* ctx);
+
+/* Test tap: when trace_dev is not NULL, every layer application copies the
+ * float32 residual stream h [rows, d_model] after its MLP update into
+ * trace_dev + app * rows * d_model, app counting from 0 within each prefill
+ * chunk or decode call; the buffer must hold max_apps entries (calls with more
+ * layer applications return DORY_E_CAPACITY). NULL turns the tap off. */
+dory_status dory_set_trace(dory_ctx* ctx, float* trace_dev, int32_t max_apps);
+
+/* ---- single-kernel entry points (used by the kernel tests) -------------- */
+
+/* y = x . W^T on the stream. x [M, ldx-strided rows of K], W [N, K] (dtype),
+ * epilogue 0: y float32 [M, N] scaled by `scale`;
+ * epilogue 1: SwiGLU, N = 2*F: y (dtype) [M, F] = u * silu(v), u = cols 0..F-1,
+ *             v = cols F..2F-1.
+ * algo 0 picks by M, 1 forces the matrix-vector kernel (M <= 8), 2 the tiled
+ * matrix kernel. */
+dory_status dory_op_linear(int32_t dtype, const void* x, int64_t ldx, const void* W, void* y,
+                           int32_t M, int32_t N, int32_t K, int32_t epilogue, float scale,
+                           int32_t algo, void* stream);
+
+/* out[b] = argmax_v logits[b, v] (lowest index on ties); logits device float32
+ * [B, V], out device int32 [B]. scratch_dev: device, >= dory_argmax_scratch_bytes. */
+size_t dory_argmax_scratch_bytes(int32_t B, int32_t V);
+dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out,
+                           void* scratch_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DORY_H */

@@ -1,0 +1,404 @@
+// C ABI and host runtime of the looped nGPT forward pass: argument
+// validation (before anything is enqueued), KV-buffer binding, and the loop
+// controller that runs the input block once, the shared recurrent block
+// n_loops times with the input block's output re-injected before every pass,
+// and the output block once.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dory.h"
+#include "kernels.h"
+#include "plan.h"
+
+using namespace dory;
+
+struct dory_ctx {
+  Plan plan;
+  KvLayout kv;
+  const void* embed = nullptr;
+  std::vector<const void*> qkvg, o, ug, down;
+  std::vector<const float*> alpha_attn, alpha_mlp;
+  char* kvb = nullptr;
+  char* ws = nullptr;
+  hipStream_t st = nullptr;
+  // sequence state
+  int pos = 0, batch = 0, seq_loops = 0, kv_mode_seq = -1;
+  bool has_logits = false;
+  bool device_ready = false;  // RoPE tables built, flags cleared
+  // test tap
+  float* trace = nullptr;
+  int trace_max = 0;
+  std::string err;
+};
+
+namespace {
+
+template <typename P>
+P* wsp(dory_ctx* c, size_t off) { return (P*)(c->ws + off); }
+
+dory_status set_err(dory_ctx* c, dory_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+#define HIP_TRY(ctx, call)                                                                         \
+  do {                                                                                             \
+    hipError_t e_ = (call);                                                                        \
+    if (e_ != hipSuccess)                                                                          \
+      return set_err(ctx, DORY_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));          \
+  } while (0)
+
+int choose_splits(int keys, int B, int nkv) {
+  int s = (keys + 63) / 64;                       // at least one 64-key tile per split
+  const int want = (512 + B * nkv - 1) / (B * nkv);  // about two workgroups per CU
+  if (s > want) s = want;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
+// One layer application (attention sublayer + MLP sublayer) on `rows` rows.
+dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int app) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const WsLayout& W = P.ws;
+  const int rows = B * n;
+  const int dt = C.dtype;
+  const int full = P.is_full[l];
+  const int cid = c->kv.first_id[l] + ((P.recurrent(l) && c->kv.kv_mode == DORY_KV_PER_LOOP) ? loop - 1 : 0);
+  const int slots = P.slots(l);
+  char* kc = c->kvb + (size_t)c->kv.offset[cid] * P.elem;
+  char* vc = kc + (size_t)C.max_batch * C.n_kv_heads * slots * C.head_dim * P.elem;
+  float* h = wsp<float>(c, W.h);
+  void* xb = c->ws + W.xb;
+  float* qkvg = wsp<float>(c, W.qkvg);
+  float* y = wsp<float>(c, W.y);
+  hipStream_t st = c->st;
+
+  HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->qkvg[l], qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f, 0, st));
+
+  RopeArgs ra{};
+  ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
+  ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
+  ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
+  ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
+  const bool direct = (n == 1);  // one position: its slot holds no key any query of this call needs
+  ra.kc = direct ? kc : nullptr; ra.vc = direct ? vc : nullptr;
+  ra.slots = slots; ra.window = C.window; ra.is_full = full;
+  HIP_TRY(c, launch_rope_qk(dt, ra, st));
+
+  AttnArgs aa{};
+  aa.q = c->ws + W.q; aa.kw = c->ws + W.kw; aa.vw = c->ws + W.vw; aa.kc = kc; aa.vc = vc;
+  aa.B = B; aa.n = n; aa.p0 = c->pos; aa.nq = C.n_q_heads; aa.nkv = C.n_kv_heads; aa.hd = C.head_dim;
+  aa.slots = slots; aa.window = C.window; aa.is_full = full;
+  const int keys = full ? c->pos + 1 : std::min(c->pos + 1, C.window);
+  aa.n_split = (n == 1) ? choose_splits(keys, B, C.n_kv_heads) : 1;
+  aa.scale = P.attn_scale;
+  aa.part = wsp<float>(c, W.part);
+  HIP_TRY(c, launch_attn_split(dt, aa, st));
+  HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
+                                 c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
+  if (!direct)
+    HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
+                               slots, C.window, full, st));
+
+  HIP_TRY(c, launch_linear(dt, c->ws + W.ob, P.q_dim, c->o[l], y, rows, C.d_model, P.q_dim, 0, 1.f, 0, st));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st));
+  HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->ug[l], c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f, 0, st));
+  HIP_TRY(c, launch_linear(dt, c->ws + W.a, C.d_ff, c->down[l], y, rows, C.d_model, C.d_ff, 0, 1.f, 0, st));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st));
+  if (c->trace)
+    HIP_TRY(c, hipMemcpyAsync(c->trace + (size_t)app * rows * C.d_model, h, (size_t)rows * C.d_model * 4,
+                              hipMemcpyDeviceToDevice, st));
+  return DORY_OK;
+}
+
+// First compute call on a context: RoPE tables and the device error flags.
+dory_status device_init(dory_ctx* c) {
+  if (c->device_ready) return DORY_OK;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  HIP_TRY(c, launch_rope_table(wsp<float2>(c, P.ws.rope_swa), C.max_ctx, C.head_dim, C.rope_base_swa, c->st));
+  HIP_TRY(c, launch_rope_table(wsp<float2>(c, P.ws.rope_full), C.max_ctx, C.head_dim, C.rope_base_full, c->st));
+  HIP_TRY(c, hipMemsetAsync(c->ws + P.ws.flags, 0, 256, c->st));
+  c->device_ready = true;
+  return DORY_OK;
+}
+
+// n new positions of B sequences (one prefill chunk or one decode step).
+dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, int n, int k, bool logits) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const WsLayout& W = P.ws;
+  const int rows = B * n;
+  const int dt = C.dtype;
+  float* h = wsp<float>(c, W.h);
+  float* e = wsp<float>(c, W.e);
+  void* xb = c->ws + W.xb;
+  hipStream_t st = c->st;
+
+  // gather the chunk's token ids into rows r = b*n + i
+  const int32_t* trows = tok;
+  if (B > 1 && tok_ld != n) {
+    int32_t* dst = wsp<int32_t>(c, W.part);  // free until the first attention of this call
+    HIP_TRY(c, hipMemcpy2DAsync(dst, (size_t)n * 4, tok, (size_t)tok_ld * 4, (size_t)n * 4, B,
+                                hipMemcpyDeviceToDevice, st));
+    trows = dst;
+  }
+  HIP_TRY(c, launch_embed(dt, trows, c->embed, h, C.n_in == 0 ? e : nullptr, xb, rows, C.d_model, C.vocab,
+                          wsp<int>(c, W.flags), st));
+  int app = 0;
+  for (int l = 0; l < C.n_in; ++l) {
+    dory_status s = run_layer(c, l, 0, B, n, l == C.n_in - 1 ? e : nullptr, app++);
+    if (s != DORY_OK) return s;
+  }
+  for (int j = 1; j <= k; ++j) {
+    if (j >= 2) HIP_TRY(c, launch_combine(dt, h, e, C.combine_wh, C.combine_we, xb, rows, C.d_model, st));
+    for (int l = C.n_in; l < C.n_in + C.n_rec; ++l) {
+      dory_status s = run_layer(c, l, j, B, n, nullptr, app++);
+      if (s != DORY_OK) return s;
+    }
+  }
+  for (int l = C.n_in + C.n_rec; l < P.n_layers; ++l) {
+    dory_status s = run_layer(c, l, 0, B, n, nullptr, app++);
+    if (s != DORY_OK) return s;
+  }
+  if (logits) {
+    const char* last = (const char*)xb + (size_t)(n - 1) * C.d_model * P.elem;
+    HIP_TRY(c, launch_linear(dt, last, (int64_t)n * C.d_model, c->embed, wsp<float>(c, W.logits), B, C.vocab,
+                             C.d_model, 0, P.logit_scale, 0, st));
+    HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st));
+    c->has_logits = true;
+  }
+  return DORY_OK;
+}
+
+dory_status check_call(dory_ctx* c, int B, int n, int n_loops, int kv_mode) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  if (kv_mode != c->kv.kv_mode)
+    return set_err(c, DORY_E_KV_MODE, "kv mode differs from the one the KV buffer was laid out for");
+  if (c->kv_mode_seq >= 0 && kv_mode != c->kv_mode_seq)
+    return set_err(c, DORY_E_KV_MODE, "kv mode changed inside a sequence");
+  if (n_loops < 1 || n_loops > C.max_loops) return set_err(c, DORY_E_LOOPS, "n_loops outside [1, max_loops]");
+  if (kv_mode == DORY_KV_PER_LOOP) {
+    if (n_loops > c->kv.kv_loops) return set_err(c, DORY_E_LOOPS, "n_loops exceeds the allocated per-loop caches");
+    if (c->seq_loops && n_loops != c->seq_loops)
+      return set_err(c, DORY_E_LOOPS, "per-loop caching needs one loop count for the whole sequence");
+  }
+  if (B < 1 || B > C.max_batch) return set_err(c, DORY_E_CAPACITY, "batch outside [1, max_batch]");
+  if (c->pos > 0 && B != c->batch) return set_err(c, DORY_E_STATE, "batch changed inside a sequence");
+  if ((int64_t)c->pos + n > C.max_ctx) return set_err(c, DORY_E_CAPACITY, "context overflow (pos + n > max_ctx)");
+  if (c->trace) {
+    const int apps = C.n_in + C.n_out + n_loops * C.n_rec;
+    if (apps > c->trace_max) return set_err(c, DORY_E_CAPACITY, "trace buffer too small for this call");
+  }
+  return DORY_OK;
+}
+
+void commit_call(dory_ctx* c, int B, int n, int n_loops, int kv_mode) {
+  c->batch = B;
+  c->kv_mode_seq = kv_mode;
+  if (kv_mode == DORY_KV_PER_LOOP) c->seq_loops = n_loops;
+  c->pos += n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dory_status_string(dory_status s) {
+  switch (s) {
+    case DORY_OK: return "ok";
+    case DORY_E_ARG: return "invalid argument";
+    case DORY_E_CAPACITY: return "capacity exceeded";
+    case DORY_E_LOOPS: return "invalid loop count";
+    case DORY_E_KV_MODE: return "invalid kv mode";
+    case DORY_E_STATE: return "invalid state";
+    case DORY_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+dory_status dory_validate_config(const dory_config* cfg) {
+  Plan p;
+  std::string why;
+  return make_plan(cfg, &p, &why);
+}
+
+size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops) {
+  Plan p;
+  if (make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  KvLayout kv;
+  if (make_kv_layout(p, kv_mode, kv_loops, &kv, nullptr) != DORY_OK) return 0;
+  return kv.bytes;
+}
+
+size_t dory_workspace_bytes(const dory_config* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  return p.ws.total;
+}
+
+dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops, int32_t layer, int32_t loop,
+                         int32_t pos, int32_t* cache_id, int32_t* slot, int64_t* k_offset, int64_t* v_offset) {
+  Plan p;
+  dory_status s = make_plan(cfg, &p, nullptr);
+  if (s != DORY_OK) return s;
+  KvLayout kv;
+  s = make_kv_layout(p, kv_mode, kv_loops, &kv, nullptr);
+  if (s != DORY_OK) return s;
+  if (layer < 0 || layer >= p.n_layers || pos < 0 || pos >= p.cfg.max_ctx) return DORY_E_ARG;
+  int j = 0;
+  if (p.recurrent(layer) && kv.kv_mode == DORY_KV_PER_LOOP) {
+    if (loop < 1 || loop > kv.kv_loops) return DORY_E_LOOPS;
+    j = loop - 1;
+  }
+  const int id = kv.first_id[layer] + j;
+  const int sl = p.is_full[layer] ? pos : pos % p.cfg.window;
+  const int64_t half = (int64_t)p.cfg.max_batch * p.cfg.n_kv_heads * p.slots(layer) * p.cfg.head_dim;
+  if (cache_id) *cache_id = id;
+  if (slot) *slot = sl;
+  if (k_offset) *k_offset = kv.offset[id] + (int64_t)sl * p.cfg.head_dim;
+  if (v_offset) *v_offset = kv.offset[id] + half + (int64_t)sl * p.cfg.head_dim;
+  return DORY_OK;
+}
+
+dory_status dory_create(const dory_config* cfg, const dory_weights* w, void* kv_dev, size_t kv_bytes,
+                        int32_t kv_mode, int32_t kv_loops, void* ws_dev, size_t ws_bytes, void* stream,
+                        dory_ctx** out) {
+  if (!out) return DORY_E_ARG;
+  *out = nullptr;
+  dory_ctx* c = new dory_ctx();
+  std::string why;
+  dory_status s = make_plan(cfg, &c->plan, &why);
+  if (s == DORY_OK) s = make_kv_layout(c->plan, kv_mode, kv_loops, &c->kv, &why);
+  if (s != DORY_OK) {
+    delete c;
+    return s;
+  }
+  const Plan& P = c->plan;
+  if (!w || !w->embed || !w->qkvg || !w->o || !w->ug || !w->down || !w->alpha_attn || !w->alpha_mlp || !kv_dev ||
+      !ws_dev) {
+    delete c;
+    return DORY_E_ARG;
+  }
+  if (kv_bytes < c->kv.bytes || ws_bytes < P.ws.total || ((uintptr_t)kv_dev & 255) || ((uintptr_t)ws_dev & 255)) {
+    delete c;
+    return DORY_E_ARG;
+  }
+  c->embed = w->embed;
+  for (int l = 0; l < P.n_layers; ++l) {
+    if (!w->qkvg[l] || !w->o[l] || !w->ug[l] || !w->down[l] || !w->alpha_attn[l] || !w->alpha_mlp[l]) {
+      delete c;
+      return DORY_E_ARG;
+    }
+    c->qkvg.push_back(w->qkvg[l]);
+    c->o.push_back(w->o[l]);
+    c->ug.push_back(w->ug[l]);
+    c->down.push_back(w->down[l]);
+    c->alpha_attn.push_back(w->alpha_attn[l]);
+    c->alpha_mlp.push_back(w->alpha_mlp[l]);
+  }
+  c->kvb = (char*)kv_dev;
+  c->ws = (char*)ws_dev;
+  c->st = (hipStream_t)stream;
+  *out = c;
+  return DORY_OK;
+}
+
+void dory_destroy(dory_ctx* ctx) { delete ctx; }
+
+dory_status dory_reset(dory_ctx* c) {
+  if (!c) return DORY_E_ARG;
+  c->pos = 0;
+  c->batch = 0;
+  c->seq_loops = 0;
+  c->kv_mode_seq = -1;
+  c->has_logits = false;
+  c->err.clear();
+  return DORY_OK;
+}
+
+dory_status dory_prefill(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, int32_t n, int32_t n_loops,
+                         int32_t kv_mode) {
+  if (!c) return DORY_E_ARG;
+  if (!tokens_dev) return set_err(c, DORY_E_ARG, "tokens_dev is NULL");
+  if (n < 0) return set_err(c, DORY_E_ARG, "n < 0");
+  if (n == 0) return DORY_OK;
+  dory_status s = check_call(c, batch, n, n_loops, kv_mode);
+  if (s != DORY_OK) return s;
+  c->err.clear();
+  s = device_init(c);
+  if (s != DORY_OK) return s;
+  const int chunk = c->plan.cfg.max_chunk;
+  for (int s0 = 0; s0 < n; s0 += chunk) {
+    const int m = std::min(chunk, n - s0);
+    const bool last = s0 + m >= n;
+    s = run_forward(c, tokens_dev + s0, n, batch, m, n_loops, last);
+    if (s != DORY_OK) return s;
+    commit_call(c, batch, m, n_loops, kv_mode);
+  }
+  return DORY_OK;
+}
+
+dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_loops, int32_t kv_mode,
+                             int32_t* next_tokens_dev) {
+  if (!c) return DORY_E_ARG;
+  if (c->pos == 0 || !c->has_logits) return set_err(c, DORY_E_STATE, "decode before prefill");
+  dory_status s = check_call(c, c->batch, 1, n_loops, kv_mode);
+  if (s != DORY_OK) return s;
+  c->err.clear();
+  const Plan& P = c->plan;
+  const int32_t* tok = tokens_dev ? tokens_dev : wsp<int32_t>(c, P.ws.next);
+  s = run_forward(c, tok, 1, c->batch, 1, n_loops, true);
+  if (s != DORY_OK) return s;
+  commit_call(c, c->batch, 1, n_loops, kv_mode);
+  if (next_tokens_dev)
+    HIP_TRY(c, hipMemcpyAsync(next_tokens_dev, c->ws + P.ws.next, (size_t)c->batch * 4, hipMemcpyDeviceToDevice,
+                              c->st));
+  return DORY_OK;
+}
+
+dory_status dory_logits(dory_ctx* c, float* out_dev) {
+  if (!c || !out_dev) return DORY_E_ARG;
+  if (!c->has_logits) return set_err(c, DORY_E_STATE, "no logits before prefill");
+  HIP_TRY(c, hipMemcpyAsync(out_dev, c->ws + c->plan.ws.logits, (size_t)c->batch * c->plan.cfg.vocab * 4,
+                            hipMemcpyDeviceToDevice, c->st));
+  return DORY_OK;
+}
+
+const char* dory_last_error(const dory_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+dory_status dory_set_trace(dory_ctx* c, float* trace_dev, int32_t max_apps) {
+  if (!c) return DORY_E_ARG;
+  if (trace_dev && max_apps < 1) return DORY_E_ARG;
+  c->trace = trace_dev;
+  c->trace_max = trace_dev ? max_apps : 0;
+  return DORY_OK;
+}
+
+dory_status dory_op_linear(int32_t dtype, const void* x, int64_t ldx, const void* W, void* y, int32_t M, int32_t N,
+                           int32_t K, int32_t epilogue, float scale, int32_t algo, void* stream) {
+  if (!x || !W || !y) return DORY_E_ARG;
+  if ((dtype != DORY_F32 && dtype != DORY_BF16) || M < 0 || N < 1 || K < 1 || ldx < K) return DORY_E_ARG;
+  if (epilogue != 0 && epilogue != 1) return DORY_E_ARG;
+  if (epilogue == 1 && N % 2) return DORY_E_ARG;
+  if (algo < 0 || algo > 2) return DORY_E_ARG;
+  hipError_t e = launch_linear(dtype, x, ldx, W, y, M, N, K, epilogue, scale, algo, (hipStream_t)stream);
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
+size_t dory_argmax_scratch_bytes(int32_t B, int32_t V) { return B > 0 && V > 0 ? argmax_partials(B, V) * 8 : 0; }
+
+dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, void* scratch, void* stream) {
+  if (!logits || !out || !scratch || B < 1 || V < 1) return DORY_E_ARG;
+  hipError_t e = launch_argmax(logits, B, V, out, scratch, (hipStream_t)stream);
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,386 @@
+// Linear layers y = x . W^T of the looped nGPT (the fused q|k|v|gate
+// projection, the attention output projection, the SwiGLU up/gate projection
+// and the down projection, and the tied LM head).
+//
+//  * k_gemv_vec: decode (M <= 8 rows). HBM-bound weight streaming: each wave
+//    owns ROWS weight rows, every lane loads 16 B per row per step, the
+//    activations sit in LDS, and a wave reduction closes each dot product.
+//  * k_gemm_mfma: prefill, bfloat16. 128x128x64 workgroup tiles, four waves
+//    of 64x64, v_mfma_f32_32x32x16_bf16, LDS rows padded by 16 B, the next
+//    K tile prefetched into registers while the current one is multiplied.
+//  * k_gemm_simple / k_gemv_scalar: float32 models and ragged shapes.
+//
+// Epilogue 1 (SwiGLU) pairs row o of u with row F + o of v inside one wave
+// and stores u * silu(v) in the model dtype.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
+
+__device__ __forceinline__ float silu_(float v) { return v / (1.0f + expf(-v)); }
+
+__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const bf16*) {
+  float s = bf_lo(w.x) * bf_lo(x.x);
+  s = fmaf(bf_hi(w.x), bf_hi(x.x), s);
+  s = fmaf(bf_lo(w.y), bf_lo(x.y), s);
+  s = fmaf(bf_hi(w.y), bf_hi(x.y), s);
+  s = fmaf(bf_lo(w.z), bf_lo(x.z), s);
+  s = fmaf(bf_hi(w.z), bf_hi(x.z), s);
+  s = fmaf(bf_lo(w.w), bf_lo(x.w), s);
+  s = fmaf(bf_hi(w.w), bf_hi(x.w), s);
+  return s;
+}
+
+__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const float*) {
+  float s = __uint_as_float(w.x) * __uint_as_float(x.x);
+  s = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), s);
+  s = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), s);
+  s = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), s);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV, vector path (K a multiple of 16 B worth of elements, rows aligned)
+// ---------------------------------------------------------------------------
+template <typename T, int MB, int ROWS, int EPI>
+__global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64_t ldx, const T* __restrict__ W,
+                                                 void* __restrict__ y, int M, int N, int K, float scale) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 * ROWS : ROWS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* xs = (T*)smem;
+  const int nv = K / VEC;
+  for (int m = 0; m < M; ++m)
+    for (int v = threadIdx.x; v < nv; v += 256)
+      ((u32x4*)(xs + (size_t)m * K))[v] = ((const u32x4*)(x + (size_t)m * ldx))[v];
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o0 = (blockIdx.x * 4 + wave) * ROWS;
+  if (o0 >= nout) return;
+  const T* wr[NR];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int o = min(o0 + r, nout - 1);
+    wr[r] = W + (size_t)o * K;
+    if (EPI == EPI_SWIGLU) wr[ROWS + r] = W + (size_t)(nout + o) * K;
+  }
+  float acc[MB][NR];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+
+#pragma unroll 2
+  for (int v = lane; v < nv; v += 64) {
+    u32x4 wv[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) wv[j] = __builtin_nontemporal_load(((const u32x4*)wr[j]) + v);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m < M) {
+        const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j], xv, (const T*)nullptr);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= M) break;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const float s = wave_sum(acc[m][r]);
+      if (EPI == EPI_SWIGLU) {
+        const float g = wave_sum(acc[m][ROWS + r]);
+        if (lane == 0 && o0 + r < nout) ((T*)y)[(size_t)m * nout + o0 + r] = from_f<T>(s * silu_(g));
+      } else {
+        if (lane == 0 && o0 + r < nout) ((float*)y)[(size_t)m * N + o0 + r] = s * scale;
+      }
+    }
+  }
+}
+
+// Scalar GEMV (any K, any alignment): one wave per output.
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void k_gemv_scalar(const T* __restrict__ x, int64_t ldx, const T* __restrict__ W,
+                                                    void* __restrict__ y, int M, int N, int K, float scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o = blockIdx.x * 4 + wave;
+  const int m = blockIdx.y;
+  if (o >= nout) return;
+  const T* xr = x + (size_t)m * ldx;
+  const T* w0 = W + (size_t)o * K;
+  const T* w1 = W + (size_t)(nout + o) * K;
+  float s0 = 0.f, s1 = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float xv = to_f(xr[k]);
+    s0 = fmaf(to_f(w0[k]), xv, s0);
+    if (EPI == EPI_SWIGLU) s1 = fmaf(to_f(w1[k]), xv, s1);
+  }
+  s0 = wave_sum(s0);
+  if (EPI == EPI_SWIGLU) s1 = wave_sum(s1);
+  if (lane == 0) {
+    if (EPI == EPI_SWIGLU)
+      ((T*)y)[(size_t)m * nout + o] = from_f<T>(s0 * silu_(s1));
+    else
+      ((float*)y)[(size_t)m * N + o] = s0 * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM (bfloat16 in, float32 accumulate)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;  // 144-byte LDS rows
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, int64_t lda,
+                                                  const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
+                                                  int K, float scale) {
+  __shared__ __align__(16) bf16 As[GBM * GLD];
+  __shared__ __align__(16) bf16 Bs[GBN * GLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * GBM;
+  const int F = N / 2;
+  const int n0 = EPI == EPI_SWIGLU ? blockIdx.x * (GBN / 2) : blockIdx.x * GBN;
+
+  // each thread moves 4 x 16 B of A and of B per K tile
+  int arow[4], brow[4], col8[4];
+  bool aok[4], bok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3;
+    col8[i] = (c & 7) * 8;
+    arow[i] = m0 + r;
+    aok[i] = arow[i] < M;
+    int br;
+    if (EPI == EPI_SWIGLU) {
+      const int nb = r >> 5;
+      const int o = n0 + (nb >> 1) * 32 + (r & 31);
+      bok[i] = o < F;
+      br = (nb & 1 ? F : 0) + o;
+    } else {
+      br = n0 + r;
+      bok[i] = br < N;
+    }
+    brow[i] = br;
+  }
+  uint4 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + col8[i];
+      const bool kin = k < K;
+      ra[i] = (aok[i] && kin) ? *(const uint4*)(A + (size_t)arow[i] * lda + k) : make_uint4(0, 0, 0, 0);
+      rb[i] = (bok[i] && kin) ? *(const uint4*)(B + (size_t)brow[i] * K + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid + 256 * i) >> 3;
+      *(uint4*)(As + r * GLD + col8[i]) = ra[i];
+      *(uint4*)(Bs + r * GLD + col8[i]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  for (int k0 = 0; k0 < K; k0 += GBK) {
+    const bool more = k0 + GBK < K;
+    if (more) gload(k0 + GBK);
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8_t*)(As + (wm * 64 + i * 32 + lr) * GLD + ks * 16 + lk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(Bs + (wn * 64 + j * 32 + lr) * GLD + ks * 16 + lk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= M) continue;
+      if (EPI == EPI_SWIGLU) {
+        const int o = n0 + wn * 32 + lr;
+        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * silu_(acc[i][1][r]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + lr;
+          if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Simple tiled GEMM for float32 models and ragged shapes: 64x64 tiles, each
+// thread a 4x4 block, K in steps of 16 through LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_simple(const T* __restrict__ A, int64_t lda, const T* __restrict__ B,
+                                                    void* __restrict__ C, int M, int N, int K, float scale) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[2][16][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  float acc[2][4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int rr = e >> 4, kk = e & 15;
+      const int gm = m0 + rr, gn = n0 + rr, gk = k0 + kk;
+      As[kk][rr] = (gm < M && gk < K) ? to_f(A[(size_t)gm * lda + gk]) : 0.f;
+      Bs[0][kk][rr] = (gn < nout && gk < K) ? to_f(B[(size_t)gn * K + gk]) : 0.f;
+      if (EPI == EPI_SWIGLU) Bs[1][kk][rr] = (gn < nout && gk < K) ? to_f(B[(size_t)(nout + gn) * K + gk]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b0[j] = Bs[0][kk][tx * 4 + j];
+        b1[j] = EPI == EPI_SWIGLU ? Bs[1][kk][tx * 4 + j] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[0][i][j] = fmaf(a[i], b0[j], acc[0][i][j]);
+          if (EPI == EPI_SWIGLU) acc[1][i][j] = fmaf(a[i], b1[j], acc[1][i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= nout) continue;
+      if (EPI == EPI_SWIGLU)
+        ((T*)C)[(size_t)row * nout + col] = from_f<T>(acc[0][i][j] * silu_(acc[1][i][j]));
+      else
+        ((float*)C)[(size_t)row * N + col] = acc[0][i][j] * scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <typename T, int EPI>
+static hipError_t gemv_dispatch(const T* x, int64_t ldx, const T* W, void* y, int M, int N, int K, float scale,
+                                hipStream_t st) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const bool vec_ok = (K % VEC == 0) && (ldx % VEC == 0) && (((uintptr_t)x & 15) == 0) &&
+                      (((uintptr_t)W & 15) == 0);
+  const size_t osz = EPI == EPI_SWIGLU ? sizeof(T) : sizeof(float);
+  const int ostride = EPI == EPI_SWIGLU ? nout : N;
+  if (!vec_ok) {
+    dim3 grid((nout + 3) / 4, M);
+    hipLaunchKernelGGL((k_gemv_scalar<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
+    return hipGetLastError();
+  }
+  // rows per launch limited by LDS (64 KB of staged activations)
+  int mb = (int)((64 * 1024) / ((size_t)K * sizeof(T)));
+  mb = mb < 1 ? 1 : (mb > 8 ? 8 : mb);
+  for (int m0 = 0; m0 < M; m0 += mb) {
+    const int mm = M - m0 < mb ? M - m0 : mb;
+    const T* xm = x + (size_t)m0 * ldx;
+    void* ym = (char*)y + (size_t)m0 * ostride * osz;
+    const size_t lds = (size_t)mm * K * sizeof(T);
+    // two rows per wave unless that leaves too few workgroups to fill 256 CUs
+    const int rows = (nout >= 4096) ? 2 : 1;
+    const int grid = (nout + 4 * rows - 1) / (4 * rows);
+#define DORY_GEMV(MBV, RV) \
+  hipLaunchKernelGGL((k_gemv_vec<T, MBV, RV, EPI>), dim3(grid), dim3(256), lds, st, xm, ldx, W, ym, mm, N, K, scale)
+    if (rows == 2) {
+      if (mm == 1) DORY_GEMV(1, 2); else if (mm == 2) DORY_GEMV(2, 2); else if (mm <= 4) DORY_GEMV(4, 2); else DORY_GEMV(8, 2);
+    } else {
+      if (mm == 1) DORY_GEMV(1, 1); else if (mm == 2) DORY_GEMV(2, 1); else if (mm <= 4) DORY_GEMV(4, 1); else DORY_GEMV(8, 1);
+    }
+#undef DORY_GEMV
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int EPI>
+static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, int M, int N, int K, float scale,
+                                hipStream_t st) {
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  if (sizeof(T) == 2 && K % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0)) {
+    const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
+    dim3 grid(nt, (M + GBM - 1) / GBM);
+    hipLaunchKernelGGL((k_gemm_mfma<EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                       scale);
+  } else {
+    dim3 grid((nout + 63) / 64, (M + 63) / 64);
+    hipLaunchKernelGGL((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K, int epi,
+                         float scale, int algo, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const bool gemv = algo == 1 || (algo == 0 && M <= 8);
+#define DORY_LIN(T)                                                                                       \
+  do {                                                                                                    \
+    if (epi == EPI_SWIGLU)                                                                                \
+      return gemv ? gemv_dispatch<T, EPI_SWIGLU>((const T*)x, ldx, (const T*)W, y, M, N, K, scale, st)   \
+                  : gemm_dispatch<T, EPI_SWIGLU>((const T*)x, ldx, (const T*)W, y, M, N, K, scale, st);  \
+    return gemv ? gemv_dispatch<T, EPI_F32>((const T*)x, ldx, (const T*)W, y, M, N, K, scale, st)        \
+                : gemm_dispatch<T, EPI_F32>((const T*)x, ldx, (const T*)W, y, M, N, K, scale, st);       \
+  } while (0)
+  if (dtype == 0) DORY_LIN(float);
+  DORY_LIN(bf16);
+#undef DORY_LIN
+}
+
+}  // namespace dory

@@ -1,0 +1,353 @@
+// Row-wise kernels of the looped nGPT forward: embedding + norm, the nGPT
+// hypersphere update, the loop re-injection, RoPE tables, RoPE with per-head
+// q/k normalisation, the KV-cache writer and the greedy argmax.
+//
+// Row kernels use one 256-thread workgroup per row of d_model elements, each
+// thread holding EPT elements in registers, so a row is read from memory once
+// and the two L2 norms are workgroup reductions.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+constexpr int kRowThreads = 256;
+
+// ---------------------------------------------------------------------------
+// embedding: h = norm(E[tok])
+// ---------------------------------------------------------------------------
+template <typename T, int EPT>
+__global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict__ tok, const T* __restrict__ E,
+                                                      float* __restrict__ h, float* __restrict__ h2,
+                                                      T* __restrict__ xb, int d, int vocab, int* err) {
+  __shared__ float sh[kRowThreads / 64];
+  const int r = blockIdx.x;
+  int t = tok[r];
+  if (t < 0 || t >= vocab) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    t = t < 0 ? 0 : vocab - 1;
+  }
+  const T* e = E + (size_t)t * d;
+  float v[EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    v[j] = i < d ? to_f(e[i]) : 0.f;
+    ss += v[j] * v[j];
+  }
+  const float inv = inv_norm(block_sum<kRowThreads>(ss, sh));
+  const size_t o = (size_t)r * d;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    if (i < d) {
+      const float x = v[j] * inv;
+      h[o + i] = x;
+      xb[o + i] = from_f<T>(x);
+      if (h2) h2[o + i] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// nGPT update: h = norm(h + alpha * (norm(y) - h))
+// ---------------------------------------------------------------------------
+template <typename T, int EPT>
+__global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, const float* __restrict__ y,
+                                                       const float* __restrict__ alpha, T* __restrict__ xb,
+                                                       float* __restrict__ h2, int d) {
+  __shared__ float sh[kRowThreads / 64];
+  const size_t o = (size_t)blockIdx.x * d;
+  float yv[EPT], hv[EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    yv[j] = i < d ? y[o + i] : 0.f;
+    hv[j] = i < d ? h[o + i] : 0.f;
+    ss += yv[j] * yv[j];
+  }
+  const float iy = inv_norm(block_sum<kRowThreads>(ss, sh));
+  float st = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    const float a = i < d ? alpha[i] : 0.f;
+    hv[j] = hv[j] + a * (yv[j] * iy - hv[j]);
+    st += hv[j] * hv[j];
+  }
+  const float ih = inv_norm(block_sum<kRowThreads>(st, sh));
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    if (i < d) {
+      const float x = hv[j] * ih;
+      h[o + i] = x;
+      xb[o + i] = from_f<T>(x);
+      if (h2) h2[o + i] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// loop re-injection: h = norm(wh * h + we * e)
+// ---------------------------------------------------------------------------
+template <typename T, int EPT>
+__global__ __launch_bounds__(kRowThreads) void k_combine(float* __restrict__ h, const float* __restrict__ e,
+                                                        float wh, float we, T* __restrict__ xb, int d) {
+  __shared__ float sh[kRowThreads / 64];
+  const size_t o = (size_t)blockIdx.x * d;
+  float v[EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    v[j] = i < d ? wh * h[o + i] + we * e[o + i] : 0.f;
+    ss += v[j] * v[j];
+  }
+  const float inv = inv_norm(block_sum<kRowThreads>(ss, sh));
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = threadIdx.x + j * kRowThreads;
+    if (i < d) {
+      const float x = v[j] * inv;
+      h[o + i] = x;
+      xb[o + i] = from_f<T>(x);
+    }
+  }
+}
+
+template <template <typename, int> class K, typename T>
+struct RowDispatch;
+
+#define DORY_ROW_LAUNCH(KERNEL, T, d, rows, st, ...)                                                   \
+  do {                                                                                                 \
+    if ((d) <= 4 * kRowThreads)                                                                        \
+      hipLaunchKernelGGL((KERNEL<T, 4>), dim3(rows), dim3(kRowThreads), 0, st, __VA_ARGS__);           \
+    else if ((d) <= 8 * kRowThreads)                                                                   \
+      hipLaunchKernelGGL((KERNEL<T, 8>), dim3(rows), dim3(kRowThreads), 0, st, __VA_ARGS__);           \
+    else if ((d) <= 16 * kRowThreads)                                                                  \
+      hipLaunchKernelGGL((KERNEL<T, 16>), dim3(rows), dim3(kRowThreads), 0, st, __VA_ARGS__);          \
+    else                                                                                               \
+      hipLaunchKernelGGL((KERNEL<T, 32>), dim3(rows), dim3(kRowThreads), 0, st, __VA_ARGS__);          \
+  } while (0)
+
+hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, float* h2, void* xb, int rows,
+                        int d, int vocab, int* err, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 0)
+    DORY_ROW_LAUNCH(k_embed, float, d, rows, st, tok, (const float*)E, h, h2, (float*)xb, d, vocab, err);
+  else
+    DORY_ROW_LAUNCH(k_embed, bf16, d, rows, st, tok, (const bf16*)E, h, h2, (bf16*)xb, d, vocab, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2, int rows,
+                         int d, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 0)
+    DORY_ROW_LAUNCH(k_update, float, d, rows, st, h, y, alpha, (float*)xb, h2, d);
+  else
+    DORY_ROW_LAUNCH(k_update, bf16, d, rows, st, h, y, alpha, (bf16*)xb, h2, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int dtype, float* h, const float* e, float wh, float we, void* xb, int rows, int d,
+                          hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 0)
+    DORY_ROW_LAUNCH(k_combine, float, d, rows, st, h, e, wh, we, (float*)xb, d);
+  else
+    DORY_ROW_LAUNCH(k_combine, bf16, d, rows, st, h, e, wh, we, (bf16*)xb, d);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RoPE tables: angle = pos * base^(-2i/hd) in float64 (an fp32 product of a
+// position near 262144 with theta loses ~1e-2 rad), stored as float (cos, sin)
+// ---------------------------------------------------------------------------
+__global__ void k_rope_table(float2* __restrict__ tab, int max_ctx, int hd, double base) {
+  const int half = hd / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)max_ctx * half) return;
+  const int pos = (int)(idx / half);
+  const int i = (int)(idx % half);
+  const double theta = pow(base, -2.0 * (double)i / (double)hd);
+  const double ang = (double)pos * theta;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipStream_t st) {
+  const int64_t n = (int64_t)max_ctx * (hd / 2);
+  const int blocks = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(k_rope_table, dim3(blocks), dim3(256), 0, st, tab, max_ctx, hd, base);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RoPE + per-head L2 norm of q and k, plain copy of v, optional cache write.
+// One wave per (row, head); lane l owns the rotation pair (l, l + hd/2).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int head = blockIdx.x * 4 + wave;
+  const int r = blockIdx.y;
+  const int nh = a.nq + 2 * a.nkv;
+  if (head >= nh) return;
+  const int half = a.hd / 2;
+  const int b = r / a.n, i = r % a.n;
+  const int pos = a.p0 + i;
+  const float* src = a.qkvg + (size_t)r * a.ld + (size_t)head * a.hd;
+  if (lane >= half) return;
+  float x1 = src[lane], x2 = src[lane + half];
+  T* dst;
+  T* cdst = nullptr;
+  if (head < a.nq + a.nkv) {
+    const float2 cs = a.tab[(size_t)pos * half + lane];
+    const float r1 = x1 * cs.x - x2 * cs.y;
+    const float r2 = x2 * cs.x + x1 * cs.y;
+    // lanes >= half returned early; the wave sum below only sees active lanes
+    float ss = r1 * r1 + r2 * r2;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float other = __shfl_xor(ss, o, 64);
+      if ((lane ^ o) < half) ss += other;
+    }
+    const float inv = inv_norm(ss);
+    x1 = r1 * inv;
+    x2 = r2 * inv;
+  }
+  if (head < a.nq) {
+    dst = (T*)a.q_out + ((size_t)r * a.nq + head) * a.hd;
+  } else {
+    const bool isk = head < a.nq + a.nkv;
+    const int kvh = isk ? head - a.nq : head - a.nq - a.nkv;
+    dst = (T*)(isk ? a.k_out : a.v_out) + ((size_t)r * a.nkv + kvh) * a.hd;
+    if (a.kc) {
+      const int slot = a.is_full ? pos : pos % a.window;
+      cdst = (T*)(isk ? a.kc : a.vc) + (((size_t)b * a.nkv + kvh) * a.slots + slot) * a.hd;
+    }
+  }
+  const T y1 = from_f<T>(x1), y2 = from_f<T>(x2);
+  dst[lane] = y1;
+  dst[lane + half] = y2;
+  if (cdst) {
+    cdst[lane] = y1;
+    cdst[lane + half] = y2;
+  }
+}
+
+hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  const int nh = a.nq + 2 * a.nkv;
+  dim3 grid((nh + 3) / 4, a.rows);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_rope_qk<float>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_rope_qk<bf16>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// KV writer after a multi-position call (attention has already read the old
+// ring contents). Block = one row; copies k and v of all kv heads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, const T* __restrict__ vw,
+                                                 T* __restrict__ kc, T* __restrict__ vc, int n, int p0, int nkv,
+                                                 int hd, int slots, int window, int is_full) {
+  const int r = blockIdx.x;
+  const int b = r / n, i = r % n;
+  if (!is_full && i < n - slots) return;  // overwritten later in this call
+  const int pos = p0 + i;
+  const int slot = is_full ? pos : pos % window;
+  const int kvd = nkv * hd;
+  for (int e = threadIdx.x; e < 2 * kvd; e += blockDim.x) {
+    const bool isk = e < kvd;
+    const int x = isk ? e : e - kvd;
+    const int kvh = x / hd, c = x % hd;
+    const T val = (isk ? kw : vw)[(size_t)r * kvd + x];
+    (isk ? kc : vc)[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
+  }
+}
+
+hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, void* kc, void* vc, int B, int n, int p0,
+                           int nkv, int hd, int slots, int window, int is_full, hipStream_t st) {
+  if (B * n <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_kv_write<float>, dim3(B * n), dim3(256), 0, st, (const float*)kw, (const float*)vw,
+                       (float*)kc, (float*)vc, n, p0, nkv, hd, slots, window, is_full);
+  else
+    hipLaunchKernelGGL(k_kv_write<bf16>, dim3(B * n), dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw,
+                       (bf16*)kc, (bf16*)vc, n, p0, nkv, hd, slots, window, is_full);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// greedy argmax, lowest index on ties, two passes
+// ---------------------------------------------------------------------------
+constexpr int kArgBlock = 1024;  // logits per partial (matches the plan)
+
+__device__ __forceinline__ void arg_better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__device__ __forceinline__ void block_argmax(float& bv, int& bi) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    arg_better(bv, bi, ov, oi);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  bv = sv[0];
+  bi = si[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k) arg_better(bv, bi, sv[k], si[k]);
+}
+
+__global__ __launch_bounds__(256) void k_argmax_part(const float* __restrict__ logits, int V, int nblk,
+                                                    float2* __restrict__ part) {
+  const int b = blockIdx.y, blk = blockIdx.x;
+  const float* row = logits + (size_t)b * V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  const int lo = blk * kArgBlock;
+  const int hi = min(V, lo + kArgBlock);
+  for (int i = lo + threadIdx.x; i < hi; i += 256) arg_better(bv, bi, row[i], i);
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blk] = make_float2(bv, __int_as_float(bi));
+}
+
+__global__ __launch_bounds__(256) void k_argmax_final(const float2* __restrict__ part, int nblk,
+                                                     int32_t* __restrict__ out) {
+  const int b = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = threadIdx.x; k < nblk; k += 256) {
+    const float2 p = part[(size_t)b * nblk + k];
+    arg_better(bv, bi, p.x, __float_as_int(p.y));
+  }
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) out[b] = bi == 0x7fffffff ? 0 : bi;
+}
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  const int nblk = (V + kArgBlock - 1) / kArgBlock;
+  hipLaunchKernelGGL(k_argmax_part, dim3(nblk, B), dim3(256), 0, st, logits, V, nblk, (float2*)scratch);
+  hipLaunchKernelGGL(k_argmax_final, dim3(B), dim3(256), 0, st, (const float2*)scratch, nblk, out);
+  return hipGetLastError();
+}
+
+}  // namespace dory

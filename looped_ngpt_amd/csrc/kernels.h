@@ -1,0 +1,67 @@
+// Launch wrappers of the gfx950 kernels. Plain pointers and sizes; every
+// wrapper enqueues on `st` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dory {
+
+// h = norm(E[tok]) per row; xb = h in the model dtype; h2 (optional) = h.
+hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, float* h2, void* xb,
+                        int rows, int d, int vocab, int* err, hipStream_t st);
+
+// nGPT step per row: h = norm(h + alpha * (norm(y) - h)); xb = h (dtype); h2 (optional) = h.
+hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2,
+                         int rows, int d, hipStream_t st);
+
+// Loop re-injection per row: h = norm(wh * h + we * e); xb = h (dtype).
+hipError_t launch_combine(int dtype, float* h, const float* e, float wh, float we, void* xb, int rows,
+                          int d, hipStream_t st);
+
+// tab[pos][i] = (cos, sin)(pos * base^(-2i/hd)), angles in float64.
+hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipStream_t st);
+
+// Rows r = b*n + i at position p0 + i. Reads q|k|v of the fused projection
+// (float32, row stride ld); writes RoPE'd, per-head unit q and k and plain v
+// in the model dtype to q_out [rows][nq][hd], k_out / v_out [rows][nkv][hd].
+// If kc is not NULL also writes k, v to the cache slot of each position
+// (only valid when no other position of the same launch maps to that slot).
+struct RopeArgs {
+  const float* qkvg; int64_t ld;
+  const float2* tab;
+  int p0, n, rows, nq, nkv, hd;
+  void* q_out; void* k_out; void* v_out;
+  void* kc; void* vc; int slots, window, is_full;
+};
+hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st);
+
+// Copies this call's K/V rows into the cache: every row of a full layer, the
+// last min(n, slots) rows of a sliding-window ring.
+hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, void* kc, void* vc, int B, int n,
+                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st);
+
+// Split-K softmax attention. For query row r = b*n + i (position p0 + i) and
+// query head hq (kv head hq / G) the allowed keys are s <= t (and t - s <
+// window for sliding layers); keys s >= p0 come from kw/vw, earlier ones from
+// the cache. Writes (m, l, acc[hd]) per (r, hq, split) to part.
+struct AttnArgs {
+  const void* q; const void* kw; const void* vw; const void* kc; const void* vc;
+  int B, n, p0, nq, nkv, hd, slots, window, is_full, n_split;
+  float scale;
+  float* part;
+};
+hipError_t launch_attn_split(int dtype, const AttnArgs& a, hipStream_t st);
+
+// Merges the splits, applies the sigmoid gate (gate 1: elementwise, 2: per
+// head, 0: none) read from the fused projection, stores ob [rows][nq*hd] (dtype).
+hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off,
+                               int gate, void* ob, int rows, int nq, int hd, int n_split, hipStream_t st);
+
+// y = x . W^T (see dory_op_linear).
+hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K,
+                         int epi, float scale, int algo, hipStream_t st);
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st);
+
+}  // namespace dory

@@ -1,0 +1,133 @@
+// Host-only plan: validation, KV layout, workspace layout (no HIP calls).
+#include "plan.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace dory {
+
+int Plan::slots(int l) const {
+  if (is_full[l]) return cfg.max_ctx;
+  return cfg.window < cfg.max_ctx ? cfg.window : cfg.max_ctx;
+}
+
+static dory_status fail(std::string* why, const char* msg) {
+  if (why) *why = msg;
+  return DORY_E_ARG;
+}
+
+dory_status make_plan(const dory_config* c, Plan* p, std::string* why) {
+  if (!c) return fail(why, "config is NULL");
+  if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->d_ff <= 0 || c->vocab <= 0)
+    return fail(why, "model sizes must be positive");
+  if (c->n_in < 0 || c->n_rec < 0 || c->n_out < 0 || c->n_in + c->n_rec + c->n_out < 1)
+    return fail(why, "layer split must be non-negative with at least one layer");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(why, "head_dim must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads != 0) return fail(why, "n_q_heads must be a multiple of n_kv_heads");
+  {
+    const int g = c->n_q_heads / c->n_kv_heads;
+    if (g != 1 && g != 2 && g != 3 && g != 4 && g != 6 && g != 8)
+      return fail(why, "query heads per kv head must be 1, 2, 3, 4, 6 or 8");
+  }
+  if (c->window < 1) return fail(why, "window must be >= 1");
+  if (!c->layer_is_full) return fail(why, "layer_is_full is NULL");
+  if (c->dtype != DORY_F32 && c->dtype != DORY_BF16) return fail(why, "dtype must be DORY_F32 or DORY_BF16");
+  if (c->attn_gate < 0 || c->attn_gate > 2) return fail(why, "attn_gate must be 0, 1 or 2");
+  if (!(c->rope_base_swa > 1.0) || !(c->rope_base_full > 1.0)) return fail(why, "RoPE bases must be > 1");
+  if (c->max_batch < 1 || c->max_ctx < 1 || c->max_chunk < 1 || c->max_loops < 1)
+    return fail(why, "capacities must be >= 1");
+  if (c->max_chunk > c->max_ctx) return fail(why, "max_chunk must not exceed max_ctx");
+  if (c->dtype == DORY_BF16 && (c->d_model % 8 || c->d_ff % 8 || c->head_dim % 8))
+    return fail(why, "bfloat16 models need d_model, d_ff and head_dim multiples of 8");
+  if ((int64_t)c->max_batch * c->max_chunk > (1 << 24)) return fail(why, "max_batch * max_chunk too large");
+  if (!std::isfinite(c->combine_wh) || !std::isfinite(c->combine_we)) return fail(why, "combine weights must be finite");
+
+  p->cfg = *c;
+  p->n_layers = c->n_in + c->n_rec + c->n_out;
+  p->is_full.assign(c->layer_is_full, c->layer_is_full + p->n_layers);
+  for (auto& f : p->is_full) f = f ? 1 : 0;
+  p->cfg.layer_is_full = nullptr;  // the plan keeps its own copy
+  p->q_dim = c->n_q_heads * c->head_dim;
+  p->kv_dim = c->n_kv_heads * c->head_dim;
+  p->gate_dim = c->attn_gate == 1 ? p->q_dim : (c->attn_gate == 2 ? c->n_q_heads : 0);
+  p->qkvg_dim = p->q_dim + 2 * p->kv_dim + p->gate_dim;
+  p->elem = c->dtype == DORY_F32 ? 4 : 2;
+  p->max_rows = c->max_batch * c->max_chunk;
+  p->attn_scale = c->attn_scale > 0.f ? c->attn_scale : std::sqrt((float)c->head_dim);
+  p->logit_scale = c->logit_scale > 0.f ? c->logit_scale : std::sqrt((float)c->d_model);
+  p->ws = make_ws_layout(*p);
+  return DORY_OK;
+}
+
+dory_status make_kv_layout(const Plan& p, int kv_mode, int kv_loops, KvLayout* kv, std::string* why) {
+  if (kv_mode != DORY_KV_PER_LOOP && kv_mode != DORY_KV_LAST_LOOP) {
+    if (why) *why = "unknown kv mode";
+    return DORY_E_KV_MODE;
+  }
+  if (kv_mode == DORY_KV_LAST_LOOP) kv_loops = 1;
+  if (kv_loops < 1 || kv_loops > p.cfg.max_loops) {
+    if (why) *why = "kv_loops must be in [1, max_loops]";
+    return DORY_E_LOOPS;
+  }
+  kv->kv_mode = kv_mode;
+  kv->kv_loops = kv_loops;
+  kv->first_id.assign(p.n_layers, 0);
+  kv->n_ids.assign(p.n_layers, 1);
+  kv->offset.clear();
+  kv->id_layer.clear();
+  int64_t off = 0;
+  const int64_t per_slot = (int64_t)p.cfg.max_batch * p.cfg.n_kv_heads * p.cfg.head_dim;
+  for (int l = 0; l < p.n_layers; ++l) {
+    kv->first_id[l] = (int)kv->offset.size();
+    kv->n_ids[l] = (p.recurrent(l) && kv_mode == DORY_KV_PER_LOOP) ? kv_loops : 1;
+    for (int j = 0; j < kv->n_ids[l]; ++j) {
+      kv->offset.push_back(off);
+      kv->id_layer.push_back(l);
+      off += 2 * per_slot * p.slots(l);
+    }
+  }
+  kv->bytes = (size_t)off * p.elem;
+  return DORY_OK;
+}
+
+size_t argmax_partials(int32_t B, int32_t V) {
+  return (size_t)B * ((V + kArgmaxBlock - 1) / kArgmaxBlock);
+}
+
+WsLayout make_ws_layout(const Plan& p) {
+  WsLayout w;
+  const auto& c = p.cfg;
+  const size_t R = (size_t)p.max_rows;
+  const size_t el = p.elem;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = at;
+    at = align_up(at + (bytes ? bytes : 1));
+    return o;
+  };
+  const size_t rope = (size_t)c.max_ctx * (c.head_dim / 2) * 8;
+  w.rope_swa = take(rope);
+  w.rope_full = take(rope);
+  w.h = take(R * c.d_model * 4);
+  w.e = take(R * c.d_model * 4);
+  w.xb = take(R * c.d_model * el);
+  w.qkvg = take(R * p.qkvg_dim * 4);
+  w.q = take(R * p.q_dim * el);
+  w.kw = take(R * p.kv_dim * el);
+  w.vw = take(R * p.kv_dim * el);
+  const size_t dec = (size_t)c.max_batch * c.n_q_heads * kMaxSplits;
+  const size_t pre = R * c.n_q_heads;
+  w.part = take((dec > pre ? dec : pre) * (c.head_dim + 2) * 4);
+  w.ob = take(R * p.q_dim * el);
+  w.y = take(R * c.d_model * 4);
+  w.a = take(R * c.d_ff * el);
+  w.logits = take((size_t)c.max_batch * c.vocab * 4);
+  w.next = take((size_t)c.max_batch * 4);
+  w.amax = take(argmax_partials(c.max_batch, c.vocab) * 8);
+  w.flags = take(256);
+  w.total = at;
+  return w;
+}
+
+}  // namespace dory

@@ -1,0 +1,67 @@
+// Host-only model plan: config validation, KV-buffer layout and workspace
+// layout. No HIP calls here, so this part is testable on a machine without a
+// GPU through the host-only entry points of dory.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "dory.h"
+
+namespace dory {
+
+constexpr int kMaxHeadDim = 128;
+constexpr int kMaxSplits = 64;        // split-K pieces per (row, kv head) in decode attention
+constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t rope_swa = 0, rope_full = 0;  // float2 [max_ctx][hd/2]
+  size_t h = 0, e = 0, xb = 0;         // [rows, d]   f32, f32, dtype
+  size_t qkvg = 0;                     // [rows, qkvg_dim] f32
+  size_t q = 0, kw = 0, vw = 0;        // [rows, n_q|n_kv, hd] dtype
+  size_t part = 0;                     // attention partials f32
+  size_t ob = 0;                       // [rows, q_dim] dtype
+  size_t y = 0;                        // [rows, d] f32
+  size_t a = 0;                        // [rows, d_ff] dtype
+  size_t logits = 0;                   // [max_batch, vocab] f32
+  size_t next = 0;                     // [max_batch] int32
+  size_t amax = 0;                     // argmax partials
+  size_t flags = 0;                    // device error flags
+  size_t total = 0;
+};
+
+struct Plan {
+  dory_config cfg{};
+  std::vector<uint8_t> is_full;
+  int n_layers = 0, q_dim = 0, kv_dim = 0, gate_dim = 0, qkvg_dim = 0, elem = 0;
+  int max_rows = 0;
+  float attn_scale = 0.f, logit_scale = 0.f;
+  WsLayout ws;
+  bool recurrent(int l) const { return l >= cfg.n_in && l < cfg.n_in + cfg.n_rec; }
+  int slots(int l) const;
+};
+
+// Fills `plan` from `cfg`; returns DORY_OK or DORY_E_ARG with `why` set.
+dory_status make_plan(const dory_config* cfg, Plan* plan, std::string* why);
+
+struct KvLayout {
+  int kv_mode = DORY_KV_LAST_LOOP, kv_loops = 1;
+  std::vector<int> first_id;           // per layer: first cache id
+  std::vector<int> n_ids;              // per layer: caches owned
+  std::vector<int64_t> offset;         // per cache id: element offset of K (V follows)
+  std::vector<int> id_layer;           // per cache id: its layer
+  size_t bytes = 0;
+};
+
+dory_status make_kv_layout(const Plan& p, int kv_mode, int kv_loops, KvLayout* kv, std::string* why);
+
+WsLayout make_ws_layout(const Plan& p);
+
+size_t argmax_partials(int32_t B, int32_t V);
+
+}  // namespace dory

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/dory.h declares, its KV layout equals the oracle's spec
+bit for bit, and argument validation returns the documented codes without
+touching HIP."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import looped_ngpt_amd as dory
+from looped_ngpt_amd import binding
+from oracle import kvspec
+from synth.configs import ModelConfig, get_config, pattern_alternating, pattern_every4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dory.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dory_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert sorted(binding.EXPORTS) == decl
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dory_\w+)", nm))
+    for f in decl:
+        assert f in exported, f
+        assert hasattr(dory.lib(), f)
+
+
+def small(**kw):
+    base = dict(name="t", d_model=64, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=96, vocab=128,
+                n_in=2, n_rec=3, n_out=1, window=5, layer_is_full=pattern_alternating(6), dtype="bf16")
+    base.update(kw)
+    return ModelConfig(**base)
+
+
+@pytest.mark.parametrize("model,max_ctx,batch", [(small(), 11, 1), (small(dtype="f32", window=64), 40, 3),
+                                                 (get_config("c36"), 8448, 1), (get_config("c72"), 16640, 1),
+                                                 (get_config("c36"), 32896, 64)])
+def test_kv_bytes_match_spec(model, max_ctx, batch):
+    c, _keep = dory.make_config(model, max_batch=batch, max_ctx=max_ctx, max_chunk=min(max_ctx, 64))
+    for mode, code in dory.KV_MODES.items():
+        for loops in (1, 2, 3, 4, 8):
+            assert dory.kv_bytes(c, code, loops) == kvspec.kv_bytes(model, mode, loops, max_ctx, batch)
+
+
+def test_last_loop_bytes_flat_per_loop_linear():
+    c, _k = dory.make_config(get_config("c72"), max_batch=1, max_ctx=16640, max_chunk=8192)
+    last = [dory.kv_bytes(c, dory.DORY_KV_LAST_LOOP, k) for k in (1, 2, 3, 4)]
+    per = [dory.kv_bytes(c, dory.DORY_KV_PER_LOOP, k) for k in (1, 2, 3, 4)]
+    assert len(set(last)) == 1 and per[0] == last[0]
+    assert len({per[i + 1] - per[i] for i in range(3)}) == 1
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_kv_slot_bit_exact(mode):
+    model = small(n_rec=2, layer_is_full=pattern_every4(5), n_in=2, n_out=1)
+    B, T, loops = 2, 13, 3
+    c, _k = dory.make_config(model, max_batch=B, max_ctx=T, max_chunk=T)
+    code = dory.KV_MODES[mode]
+    for l in range(model.n_layers):
+        js = range(1, loops + 1) if model.is_recurrent(l) else [0]
+        for j in js:
+            for p in range(T):
+                cid, slot, ko, vo = dory.kv_slot(c, code, loops, l, j, p)
+                assert cid == kvspec.cache_id(model, mode, loops, l, j)
+                assert slot == kvspec.slot(model, T, l, p)
+                assert ko == kvspec.element_offset(model, mode, loops, T, B, l, j, "K", 0, 0, p)
+                assert vo == kvspec.element_offset(model, mode, loops, T, B, l, j, "V", 0, 0, p)
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(n_q_heads=5, n_kv_heads=1), dict(window=0),
+                                 dict(d_ff=100), dict(attn_gate=3), dict(rope_base_swa=1.0),
+                                 dict(n_in=0, n_rec=0, n_out=0, layer_is_full=())])
+def test_invalid_configs(bad):
+    m = small(**bad)
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16)
+    assert dory.validate_config(c) == dory.DORY_E_ARG
+    assert dory.kv_bytes(c, 0, 1) == 0 and dory.workspace_bytes(c) == 0
+
+
+def test_capacity_configs():
+    m = small()
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=32)    # chunk > ctx
+    assert dory.validate_config(c) == dory.DORY_E_ARG
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, max_loops=2)
+    assert dory.validate_config(c) == dory.DORY_OK
+    assert dory.kv_bytes(c, dory.DORY_KV_PER_LOOP, 3) == 0                 # more caches than max_loops
+
+
+class FakeCtx:
+    """A context bound to fake, aligned device addresses: only the validation
+    paths (which return before any HIP call) may be exercised with it."""
+
+    def __init__(self, model, *, kv_mode="last_loop", kv_loops=1, max_batch=2, max_ctx=16, max_loops=4,
+                 kv_bytes=None, ws_bytes=None, kv_addr=1 << 20, ws_addr=1 << 30):
+        L = model.n_layers
+        self.c, self._k = dory.make_config(model, max_batch=max_batch, max_ctx=max_ctx, max_chunk=8,
+                                           max_loops=max_loops)
+        arrs = [(ctypes.c_void_p * L)(*[(1 << 16) * (l + 1) for l in range(L)]) for _ in range(6)]
+        self._arrs = arrs
+        vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        self.w = binding.DoryWeights(embed=1 << 12, qkvg=vp(arrs[0]), o=vp(arrs[1]), ug=vp(arrs[2]),
+                                     down=vp(arrs[3]), alpha_attn=vp(arrs[4]), alpha_mlp=vp(arrs[5]))
+        code = dory.KV_MODES[kv_mode]
+        kvb = dory.kv_bytes(self.c, code, kv_loops) if kv_bytes is None else kv_bytes
+        wsb = dory.workspace_bytes(self.c) if ws_bytes is None else ws_bytes
+        h = ctypes.c_void_p()
+        self.status = dory.lib().dory_create(ctypes.byref(self.c), ctypes.byref(self.w), kv_addr, kvb, code,
+                                             kv_loops, ws_addr, wsb, None, ctypes.byref(h))
+        self.h = h
+
+    def __del__(self):
+        if self.h:
+            dory.lib().dory_destroy(self.h)
+
+
+def test_create_validation():
+    m = small()
+    assert FakeCtx(m).status == dory.DORY_OK
+    assert FakeCtx(m, kv_bytes=100).status == dory.DORY_E_ARG
+    assert FakeCtx(m, ws_bytes=100).status == dory.DORY_E_ARG
+    assert FakeCtx(m, kv_addr=(1 << 20) + 8).status == dory.DORY_E_ARG
+    assert FakeCtx(m, kv_mode="per_loop", kv_loops=5).status == dory.DORY_E_LOOPS
+
+
+def test_call_validation_codes():
+    m = small()
+    L = dory.lib()
+    f = FakeCtx(m, kv_mode="per_loop", kv_loops=2)
+    assert f.status == dory.DORY_OK
+    h = f.h
+    tok = 1 << 14
+    PL, LL = dory.DORY_KV_PER_LOOP, dory.DORY_KV_LAST_LOOP
+    assert L.dory_decode_step(h, tok, 2, PL, None) == dory.DORY_E_STATE
+    assert L.dory_logits(h, 1 << 14) == dory.DORY_E_STATE
+    assert L.dory_prefill(h, None, 1, 4, 2, PL) == dory.DORY_E_ARG
+    assert L.dory_prefill(h, tok, 1, 4, 0, PL) == dory.DORY_E_LOOPS
+    assert L.dory_prefill(h, tok, 1, 4, 5, PL) == dory.DORY_E_LOOPS          # > max_loops
+    assert L.dory_prefill(h, tok, 1, 4, 3, PL) == dory.DORY_E_LOOPS          # > per-loop caches
+    assert L.dory_prefill(h, tok, 1, 4, 2, LL) == dory.DORY_E_KV_MODE
+    assert L.dory_prefill(h, tok, 3, 4, 2, PL) == dory.DORY_E_CAPACITY       # batch
+    assert L.dory_prefill(h, tok, 1, 17, 2, PL) == dory.DORY_E_CAPACITY      # context
+    assert L.dory_prefill(h, tok, 1, 0, 2, PL) == dory.DORY_OK               # empty: no-op
+    assert L.dory_decode_step(h, tok, 2, PL, None) == dory.DORY_E_STATE      # still nothing prefilled
+    assert L.dory_set_trace(h, 1 << 14, 0) == dory.DORY_E_ARG
+    assert L.dory_set_trace(h, 1 << 14, 3) == dory.DORY_OK
+    assert L.dory_prefill(h, tok, 1, 4, 2, PL) == dory.DORY_E_CAPACITY       # 2+1+2*3 apps > 3
+    assert L.dory_set_trace(h, None, 0) == dory.DORY_OK
+    assert b"capacity" in L.dory_status_string(dory.DORY_E_CAPACITY)
+    assert L.dory_reset(h) == dory.DORY_OK
+    assert L.dory_reset(None) == dory.DORY_E_ARG
+
+
+def test_op_validation():
+    L = dory.lib()
+    assert L.dory_op_linear(2, 1 << 12, 8, 1 << 12, 1 << 12, 1, 8, 8, 0, 1.0, 0, None) == dory.DORY_E_ARG
+    assert L.dory_op_linear(1, 1 << 12, 4, 1 << 12, 1 << 12, 1, 8, 8, 0, 1.0, 0, None) == dory.DORY_E_ARG  # ldx < K
+    assert L.dory_op_linear(1, 1 << 12, 8, 1 << 12, 1 << 12, 1, 7, 8, 1, 1.0, 0, None) == dory.DORY_E_ARG  # odd SwiGLU N
+    assert L.dory_op_argmax(None, 1, 8, 1 << 12, 1 << 12, None) == dory.DORY_E_ARG
+    assert dory.argmax_scratch_bytes(2, 3000) == 2 * 3 * 8

@@ -1,0 +1,87 @@
+"""Single-kernel GPU checks through the C ABI: the linear kernels (matrix-
+vector, MFMA and simple tiled paths, both epilogues) against a float64 numpy
+product of the same stored values, and the greedy argmax bit for bit against
+numpy.argmax (lowest index on ties)."""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import looped_ngpt_amd as dory  # noqa: E402
+from synth.gen import f32_to_bf16_bits, bf16_bits_to_f32  # noqa: E402
+
+
+def _dev(a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+CASES = [
+    # dtype, M, N, K, epilogue, algo
+    ("f32", 1, 683, 256, 0, 1), ("f32", 3, 1024, 683, 0, 1), ("f32", 8, 2048, 256, 0, 1),
+    ("f32", 2, 2 * 683, 256, 1, 1), ("f32", 130, 683, 256, 0, 2), ("f32", 70, 2 * 683, 256, 1, 2),
+    ("bf16", 1, 8192, 3072, 0, 1), ("bf16", 1, 3072, 8192, 0, 1), ("bf16", 4, 1000, 3072, 0, 1),
+    ("bf16", 1, 2 * 8192, 3072, 1, 1), ("bf16", 5, 2 * 1000, 2304, 1, 1), ("bf16", 1, 3072, 2304, 0, 1),
+    ("bf16", 130, 1000, 3072, 0, 2), ("bf16", 256, 8192, 3072, 0, 2), ("bf16", 200, 2 * 1000, 3072, 1, 2),
+    ("bf16", 64, 3072, 8192, 0, 2), ("bf16", 33, 2304, 2304, 0, 2), ("bf16", 97, 2 * 6144, 2304, 1, 2),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,epi,algo", CASES)
+def test_linear(dt, M, N, K, epi, algo):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+    if dt == "bf16":
+        xs, Ws = f32_to_bf16_bits(x), f32_to_bf16_bits(W)
+        x64, W64 = bf16_bits_to_f32(xs).astype(np.float64), bf16_bits_to_f32(Ws).astype(np.float64)
+        code = dory.DORY_BF16
+    else:
+        xs, Ws, x64, W64 = x, W, x.astype(np.float64), W.astype(np.float64)
+        code = dory.DORY_F32
+    scale = 1.7 if epi == 0 else 1.0
+    ref = (x64 @ W64.T) * scale
+    if epi == 1:
+        F = N // 2
+        u, v = ref[:, :F], ref[:, F:]
+        ref = u * v / (1.0 + np.exp(-v))
+        ydt = torch.int16 if dt == "bf16" else torch.float32
+        y = torch.zeros((M, F), dtype=ydt, device="cuda")
+    else:
+        y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    print(f"linear {dt} M={M} N={N} K={K} epi={epi} algo={algo}", flush=True)
+    dory.op_linear(code, _dev(xs), _dev(Ws), y, M, N, K, epilogue=epi, scale=scale, algo=algo)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if got.dtype == np.int16:
+        got = bf16_bits_to_f32(got.view(np.uint16)).astype(np.float64)
+        tol = np.abs(ref) * 2.0 ** -8 + 1e-4
+    else:
+        tol = 2e-5 * math.sqrt(K) * max(1.0, scale)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"max err {err.max()}"
+
+
+def test_argmax_ties_and_specials():
+    V = 131072 + 77
+    B = 6
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((B, V)).astype(np.float32)
+    L[1] = 0.0
+    L[1, [5, 70000, 7]] = 3.0                      # ties: lowest index wins
+    L[2] = -np.inf
+    L[2, 10], L[2, 3] = -0.0, 0.0                  # -0 == +0: index 3
+    L[3, [100, 200]] = np.inf
+    L[4] = -np.inf                                 # every logit -inf: index 0
+    L[5, V - 1] = 50.0                             # the ragged tail
+    out = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(dory.argmax_scratch_bytes(B, V), dtype=torch.uint8, device="cuda")
+    dory.op_argmax(_dev(L), out, scratch)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), np.argmax(L, axis=1))

@@ -1,0 +1,189 @@
+"""End-to-end parity of the HIP library with the oracle, through the C ABI.
+
+float32 model: max |logit difference| <= 1e-3 against the float64 oracle.
+bfloat16 models: max |logit difference| <= 3e-2 against the float64 oracle
+that rounds to bfloat16 where the library stores bfloat16, and 100% greedy
+agreement over the decode horizon. KV placement and argmax are bit-exact;
+per-loop and last-loop caching are bit-identical at k = 1; reruns are
+bit-identical.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import looped_ngpt_amd as dory  # noqa: E402
+from gpu_run import generate, session, teacher_forced  # noqa: E402
+from oracle import kvspec  # noqa: E402
+from oracle.ngpt import LoopedNGPT  # noqa: E402
+from synth.configs import get_config, scaled_config  # noqa: E402
+from synth.gen import make_tokens, make_weights  # noqa: E402
+
+F32_TOL = 1e-3
+BF16_TOL = 3e-2
+
+_cache = {}
+
+
+def model_and_weights(name):
+    if name not in _cache:
+        if name == "tiny":
+            m = get_config("tiny")
+        elif name == "c36w":          # the 36-layer model's widths, 2/2/2 layers (layer 3 full)
+            m = scaled_config(get_config("c36"), n_in=2, n_rec=2, n_out=2)
+        elif name == "c72w":          # the 72-layer model's widths, 1/3/1 layers (layer 3 full)
+            m = scaled_config(get_config("c72"), n_in=1, n_rec=3, n_out=1)
+        else:
+            raise KeyError(name)
+        w = make_weights(m)
+        _cache[name] = (m, w, dory.upload_weights(m, w))
+    return _cache[name]
+
+
+def _report(tag, gl, ol):
+    d = np.abs(gl - ol)
+    print(f"{tag}: max|dlogit| {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    return d.max()
+
+
+# ---------------------------------------------------------------------------
+# float32 tiny model (d 256, 2/2/2, SWA 64 / full alternating), prompt 128,
+# 32 greedy steps at k = 2, both cache modes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_tiny_f32_generate(mode):
+    m, w, dw = model_and_weights("tiny")
+    k, steps = 2, 32
+    prompt = make_tokens(m, 0, (1, 128))
+    ora = LoopedNGPT(m, w, max_ctx=256)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode)
+    print(f"tiny {mode}: oracle tokens {o_tok[0, :8]}...", flush=True)
+    s = session(m, dw, batch=1, max_ctx=256, chunk=128, kv_mode=mode, k=k)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"tiny {mode} free-running", g_log, o_log) <= F32_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])          # library argmax == numpy argmax
+    np.testing.assert_array_equal(np.argmax(g_log, axis=-1).T, g_tok)
+    assert ora.max_norm_dev <= 1e-4
+
+
+def test_tiny_f32_batched_chunked_long():
+    """B = 3 sequences, a 600-token prompt in 128-position chunks (the 64-slot
+    rings wrap inside and across chunks, many attention splits), 12 steps at
+    k = 3 in last-loop mode (chunk-schedule dependent: same schedule on both)."""
+    m, w, dw = model_and_weights("tiny")
+    B, n, k, steps, chunk = 3, 600, 3, 12, 128
+    prompt = make_tokens(m, 1, (B, n))
+    ora = LoopedNGPT(m, w, max_ctx=640, batch=B)
+    o_tok, o_log = ora.generate(prompt, steps, k, "last_loop", chunk=chunk)
+    s = session(m, dw, batch=B, max_ctx=640, chunk=chunk, kv_mode="last_loop", k=k)
+    g_tok, g_log, _ = generate(s, prompt, steps, k)
+    assert _report("tiny batched chunked", g_log, o_log) <= F32_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+
+
+def test_tiny_elastic_depth_last_loop():
+    """Last-loop mode accepts a different k on every call (1, 4, 2, 3)."""
+    m, w, dw = model_and_weights("tiny")
+    prompt = make_tokens(m, 2, (1, 40))
+    ks = [1, 4, 2, 3]
+    ora = LoopedNGPT(m, w, max_ctx=64)
+    ol = [ora.call(prompt, ks[0], "last_loop")]
+    s = session(m, dw, batch=1, max_ctx=64, chunk=64, kv_mode="last_loop", k=1)
+    s.prefill(torch.from_numpy(prompt).cuda(), ks[0])
+    gl = [s.logits().cpu().numpy()]
+    toks = [5, 900, 17]
+    for t, k in zip(toks, ks[1:]):
+        ol.append(ora.call(np.array([[t]]), k, "last_loop"))
+        s.decode(torch.tensor([t], dtype=torch.int32, device="cuda"), k)
+        gl.append(s.logits().cpu().numpy())
+    assert _report("tiny elastic", np.stack(gl), np.stack(ol)) <= F32_TOL
+
+
+def test_tiny_kv_placement_bit_exact():
+    """After prefill + decode in per-loop mode at k = 2 the KV buffer holds,
+    at exactly the spec's offsets, the oracle's K/V of the live positions, and
+    every other slot still holds the sentinel the buffer was filled with."""
+    m, w, dw = model_and_weights("tiny")
+    k, n, steps, T = 2, 90, 6, 128
+    prompt = make_tokens(m, 3, (1, n))
+    ora = LoopedNGPT(m, w, max_ctx=T)
+    o_tok, _ = ora.generate(prompt, steps, k, "per_loop")
+    s = session(m, dw, batch=1, max_ctx=T, chunk=64, kv_mode="per_loop", k=k)
+    s.kv.view(torch.int32).fill_(0x7FC00001)                   # NaN sentinel
+    generate(s, prompt, steps, k)
+    kv = s.kv.view(torch.float32).cpu().numpy()
+    ctx = n + steps - 1                                         # positions written
+    hd, nkv = m.head_dim, m.n_kv_heads
+    written = np.zeros(kv.shape, dtype=bool)
+    for l in range(m.n_layers):
+        loops = range(1, k + 1) if m.is_recurrent(l) else [0]
+        for j in loops:
+            key = (l, j if m.is_recurrent(l) else 0)
+            live = range(ctx) if m.layer_is_full[l] else range(max(0, ctx - m.window), ctx)
+            for p in live:
+                for which in "KV":
+                    for h in range(nkv):
+                        off = kvspec.element_offset(m, "per_loop", k, T, 1, l, j, which, 0, h, p)
+                        got = kv[off:off + hd]
+                        ref = ora.cache[key][which][0, h, p]
+                        np.testing.assert_allclose(got, ref, atol=2e-5, err_msg=f"L{l} loop{j} {which} pos{p}")
+                        written[off:off + hd] = True
+    # everything else (the full layers' slots >= ctx; the rings are all live
+    # since ctx > W) still holds the sentinel
+    assert np.all(kv[~written].view(np.uint32) == 0x7FC00001)
+    for l in range(m.n_layers):
+        if not m.layer_is_full[l]:
+            continue
+        loops = range(1, k + 1) if m.is_recurrent(l) else [0]
+        for j in loops:
+            off = kvspec.element_offset(m, "per_loop", k, T, 1, l, j, "K", 0, 0, ctx)
+            assert np.all(kv[off:off + hd].view(np.uint32) == 0x7FC00001)
+
+
+def test_tiny_k1_modes_bit_identical_and_deterministic():
+    m, w, dw = model_and_weights("tiny")
+    prompt = make_tokens(m, 4, (1, 70))
+    runs = []
+    for mode in ("per_loop", "last_loop", "last_loop"):
+        s = session(m, dw, batch=1, max_ctx=128, chunk=32, kv_mode=mode, k=1)
+        runs.append(generate(s, prompt, 8, 1)[1])
+    np.testing.assert_array_equal(runs[0], runs[1])
+    np.testing.assert_array_equal(runs[1], runs[2])
+
+
+def test_state_errors_on_gpu():
+    m, w, dw = model_and_weights("tiny")
+    s = session(m, dw, batch=1, max_ctx=64, chunk=64, kv_mode="per_loop", k=2)
+    s.prefill(torch.from_numpy(make_tokens(m, 5, (1, 8))).cuda(), 2)
+    with pytest.raises(dory.DoryError) as e:
+        s.decode(None, 1)                                   # k change in per-loop mode
+    assert e.value.status == dory.DORY_E_LOOPS
+    with pytest.raises(dory.DoryError) as e:
+        s.decode(None, 2, kv_mode="last_loop")              # other mode
+    assert e.value.status == dory.DORY_E_KV_MODE
+    s.decode(None, 2)
+    s.reset()
+    s.prefill(torch.from_numpy(make_tokens(m, 5, (1, 8))).cuda(), 2)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 at the 4B-shaped widths (fewer layers so the oracle finishes)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,k,mode,n,steps", [("c36w", 2, "last_loop", 64, 12),
+                                                 ("c36w", 2, "per_loop", 40, 8),
+                                                 ("c72w", 3, "per_loop", 33, 8)])
+def test_bf16_widths(name, k, mode, n, steps):
+    m, w, dw = model_and_weights(name)
+    prompt = make_tokens(m, 6, (1, n))
+    ora = LoopedNGPT(m, w, max_ctx=n + steps + 1)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode)
+    margins = np.sort(o_log, axis=-1)
+    print(f"{name}: min top1-top2 margin {np.min(margins[..., -1] - margins[..., -2]):.3e}", flush=True)
+    s = session(m, dw, batch=1, max_ctx=n + steps + 1, chunk=n, kv_mode=mode, k=k)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"{name} {mode} k={k}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
