@@ -14,6 +14,14 @@ from typing import Dict, Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdory.so")
 
+# PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+# Loading torch first makes the loader bind libdory.so to that runtime, so
+# one process never holds two HIP runtimes (the second finds no device).
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # host-only use (sizes, layout, validation) needs no torch
+    _torch = None
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m looped_ngpt_amd.build` "
                       "(the HIP library is the only implementation; there is no fallback)")

@@ -62,7 +62,12 @@ int choose_splits(int keys, int B, int nkv) {
 }
 
 // One layer application (attention sublayer + MLP sublayer) on `rows` rows.
-dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int app) {
+// write_kv: store this application's K/V in the cache. In last-loop mode the
+// recurrent layers store only on the final loop: earlier loops read this
+// call's positions from the workspace and earlier positions from the cache,
+// which must still hold the previous calls' entries (a ring slot overwritten
+// by loop 1 would lose keys that loop 2 still needs).
+dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int app, bool write_kv) {
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
   const WsLayout& W = P.ws;
@@ -86,7 +91,8 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
   ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
   ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
-  const bool direct = (n == 1);  // one position: its slot holds no key any query of this call needs
+  // one position: its slot holds no key that any query of this call needs
+  const bool direct = (n == 1) && write_kv;
   ra.kc = direct ? kc : nullptr; ra.vc = direct ? vc : nullptr;
   ra.slots = slots; ra.window = C.window; ra.is_full = full;
   HIP_TRY(c, launch_rope_qk(dt, ra, st));
@@ -102,7 +108,7 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   HIP_TRY(c, launch_attn_split(dt, aa, st));
   HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
                                  c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
-  if (!direct)
+  if (write_kv && !direct)
     HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
                                slots, C.window, full, st));
 
@@ -153,18 +159,19 @@ dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, 
                           wsp<int>(c, W.flags), st));
   int app = 0;
   for (int l = 0; l < C.n_in; ++l) {
-    dory_status s = run_layer(c, l, 0, B, n, l == C.n_in - 1 ? e : nullptr, app++);
+    dory_status s = run_layer(c, l, 0, B, n, l == C.n_in - 1 ? e : nullptr, app++, true);
     if (s != DORY_OK) return s;
   }
   for (int j = 1; j <= k; ++j) {
     if (j >= 2) HIP_TRY(c, launch_combine(dt, h, e, C.combine_wh, C.combine_we, xb, rows, C.d_model, st));
+    const bool write_kv = c->kv.kv_mode == DORY_KV_PER_LOOP || j == k;
     for (int l = C.n_in; l < C.n_in + C.n_rec; ++l) {
-      dory_status s = run_layer(c, l, j, B, n, nullptr, app++);
+      dory_status s = run_layer(c, l, j, B, n, nullptr, app++, write_kv);
       if (s != DORY_OK) return s;
     }
   }
   for (int l = C.n_in + C.n_rec; l < P.n_layers; ++l) {
-    dory_status s = run_layer(c, l, 0, B, n, nullptr, app++);
+    dory_status s = run_layer(c, l, 0, B, n, nullptr, app++, true);
     if (s != DORY_OK) return s;
   }
   if (logits) {
