@@ -184,6 +184,18 @@ const char* dory_last_error(const dory_ctx* ctx);
  * layer applications return DORY_E_CAPACITY). NULL turns the tap off. */
 dory_status dory_set_trace(dory_ctx* ctx, float* trace_dev, int32_t max_apps);
 
+/* Kernel timing tap. When kind is not 0, every launch of one kernel class is
+ * bracketed by HIP events recorded on the context's stream:
+ *   1 SwiGLU up/gate projection   2 fused q|k|v|gate projection
+ *   3 down projection             4 attention output projection
+ *   5 split-K attention
+ * At most max_launches launches are recorded (later ones are not). The events
+ * are created here (host objects, no device memory); kind 0 releases them.
+ * dory_kernel_time waits for the stream, returns the summed event time (ms)
+ * and the count of recorded launches, and starts a new recording. */
+dory_status dory_set_kernel_timing(dory_ctx* ctx, int32_t kind, int32_t max_launches);
+dory_status dory_kernel_time(dory_ctx* ctx, double* total_ms, int32_t* launches);
+
 /* ---- single-kernel entry points (used by the kernel tests) -------------- */
 
 /* y = x . W^T on the stream. x [M, ldx-strided rows of K], W [N, K] (dtype),

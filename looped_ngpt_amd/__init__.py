@@ -1,12 +1,21 @@
 """Looped normalized-GPT forward pass on gfx950 (MI355X).
 
 The implementation is the HIP library libdory.so (include/dory.h); this
-package is its thin Python binding. Importing it without the built library
-raises: there is no CPU fallback.
+package is its thin Python binding. The binding loads on first use of any
+name below and raises ImportError if the library is not built: there is no
+CPU fallback. (`looped_ngpt_amd.build` imports without the library.)
 """
-from .binding import (  # noqa: F401
-    DoryError, Session, make_config, validate_config, kv_bytes, workspace_bytes, kv_slot,
-    upload_weights, op_linear, op_argmax, argmax_scratch_bytes, lib, EXPORTS,
-    DORY_OK, DORY_E_ARG, DORY_E_CAPACITY, DORY_E_LOOPS, DORY_E_KV_MODE, DORY_E_STATE, DORY_E_HIP,
-    DORY_F32, DORY_BF16, DORY_KV_PER_LOOP, DORY_KV_LAST_LOOP, KV_MODES,
+_NAMES = (
+    "DoryError", "Session", "make_config", "validate_config", "kv_bytes", "workspace_bytes", "kv_slot",
+    "upload_weights", "op_linear", "op_argmax", "argmax_scratch_bytes", "lib", "EXPORTS",
+    "DORY_OK", "DORY_E_ARG", "DORY_E_CAPACITY", "DORY_E_LOOPS", "DORY_E_KV_MODE", "DORY_E_STATE", "DORY_E_HIP",
+    "DORY_F32", "DORY_BF16", "DORY_KV_PER_LOOP", "DORY_KV_LAST_LOOP", "KV_MODES",
 )
+__all__ = list(_NAMES)
+
+
+def __getattr__(name):
+    if name in _NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -35,7 +35,8 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 # every function dory.h declares, for the export check
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
-           "dory_decode_step", "dory_logits", "dory_last_error", "dory_set_trace", "dory_op_linear",
+           "dory_decode_step", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_kernel_timing",
+           "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax"]
 
 
@@ -78,6 +79,8 @@ _sig = {
     "dory_logits": (_I, [_P, _P]),
     "dory_last_error": (ctypes.c_char_p, [_P]),
     "dory_set_trace": (_I, [_P, _P, _I]),
+    "dory_set_kernel_timing": (_I, [_P, _I, _I]),
+    "dory_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]),
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
     "dory_argmax_scratch_bytes": (ctypes.c_size_t, [_I, _I]),
     "dory_op_argmax": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -236,6 +239,17 @@ class Session:
     def reset(self) -> None:
         self._check(_lib.dory_reset(self.h))
         self.batch = None
+
+    TIME_KINDS = {"ug": 1, "qkvg": 2, "down": 3, "o": 4, "attn": 5}
+
+    def set_kernel_timing(self, kind: Optional[str], max_launches: int = 0) -> None:
+        self._check(_lib.dory_set_kernel_timing(self.h, self.TIME_KINDS[kind] if kind else 0, max_launches))
+
+    def kernel_time(self):
+        """(summed milliseconds, launches) recorded since the last read."""
+        ms, n = ctypes.c_double(), _I()
+        self._check(_lib.dory_kernel_time(self.h, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def set_trace(self, buf, max_apps: int) -> None:
         self._trace = buf

@@ -33,13 +33,37 @@ struct dory_ctx {
   // test tap
   float* trace = nullptr;
   int trace_max = 0;
+  // timing tap
+  int time_kind = 0;
+  std::vector<hipEvent_t> ev;
+  size_t ev_used = 0;
   std::string err;
+  ~dory_ctx() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
 
 template <typename P>
 P* wsp(dory_ctx* c, size_t off) { return (P*)(c->ws + off); }
+
+enum { TIME_NONE = 0, TIME_UG = 1, TIME_QKVG = 2, TIME_DOWN = 3, TIME_O = 4, TIME_ATTN = 5 };
+
+// Event bracket around one launch of the timed kernel class.
+struct TimeScope {
+  dory_ctx* c;
+  bool on;
+  TimeScope(dory_ctx* ctx, int kind) : c(ctx), on(ctx->time_kind == kind && ctx->ev_used + 2 <= ctx->ev.size()) {
+    if (on) (void)hipEventRecord(c->ev[c->ev_used], c->st);
+  }
+  ~TimeScope() {
+    if (on) {
+      (void)hipEventRecord(c->ev[c->ev_used + 1], c->st);
+      c->ev_used += 2;
+    }
+  }
+};
 
 dory_status set_err(dory_ctx* c, dory_status s, const std::string& msg) {
   if (c) c->err = msg;
@@ -84,7 +108,10 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   float* y = wsp<float>(c, W.y);
   hipStream_t st = c->st;
 
-  HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->qkvg[l], qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f, 0, st));
+  {
+    TimeScope ts(c, TIME_QKVG);
+    HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->qkvg[l], qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f, 0, st));
+  }
 
   RopeArgs ra{};
   ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
@@ -105,17 +132,29 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   aa.n_split = (n == 1) ? choose_splits(keys, B, C.n_kv_heads) : 1;
   aa.scale = P.attn_scale;
   aa.part = wsp<float>(c, W.part);
-  HIP_TRY(c, launch_attn_split(dt, aa, st));
+  {
+    TimeScope ts(c, TIME_ATTN);
+    HIP_TRY(c, launch_attn_split(dt, aa, st));
+  }
   HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
                                  c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
   if (write_kv && !direct)
     HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
                                slots, C.window, full, st));
 
-  HIP_TRY(c, launch_linear(dt, c->ws + W.ob, P.q_dim, c->o[l], y, rows, C.d_model, P.q_dim, 0, 1.f, 0, st));
+  {
+    TimeScope ts(c, TIME_O);
+    HIP_TRY(c, launch_linear(dt, c->ws + W.ob, P.q_dim, c->o[l], y, rows, C.d_model, P.q_dim, 0, 1.f, 0, st));
+  }
   HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st));
-  HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->ug[l], c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f, 0, st));
-  HIP_TRY(c, launch_linear(dt, c->ws + W.a, C.d_ff, c->down[l], y, rows, C.d_model, C.d_ff, 0, 1.f, 0, st));
+  {
+    TimeScope ts(c, TIME_UG);
+    HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->ug[l], c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f, 0, st));
+  }
+  {
+    TimeScope ts(c, TIME_DOWN);
+    HIP_TRY(c, launch_linear(dt, c->ws + W.a, C.d_ff, c->down[l], y, rows, C.d_model, C.d_ff, 0, 1.f, 0, st));
+  }
   HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st));
   if (c->trace)
     HIP_TRY(c, hipMemcpyAsync(c->trace + (size_t)app * rows * C.d_model, h, (size_t)rows * C.d_model * 4,
@@ -386,6 +425,41 @@ dory_status dory_set_trace(dory_ctx* c, float* trace_dev, int32_t max_apps) {
   if (trace_dev && max_apps < 1) return DORY_E_ARG;
   c->trace = trace_dev;
   c->trace_max = trace_dev ? max_apps : 0;
+  return DORY_OK;
+}
+
+dory_status dory_set_kernel_timing(dory_ctx* c, int32_t kind, int32_t max_launches) {
+  if (!c) return DORY_E_ARG;
+  if (kind < TIME_NONE || kind > TIME_ATTN || (kind != TIME_NONE && max_launches < 1)) return DORY_E_ARG;
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  c->ev.clear();
+  c->ev_used = 0;
+  c->time_kind = TIME_NONE;
+  if (kind == TIME_NONE) return DORY_OK;
+  c->ev.resize((size_t)2 * max_launches);
+  for (auto& e : c->ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      c->ev.clear();
+      return set_err(c, DORY_E_HIP, std::string("hipEventCreate: ") + hipGetErrorString(r));
+    }
+  }
+  c->time_kind = kind;
+  return DORY_OK;
+}
+
+dory_status dory_kernel_time(dory_ctx* c, double* total_ms, int32_t* launches) {
+  if (!c || !total_ms || !launches) return DORY_E_ARG;
+  HIP_TRY(c, hipStreamSynchronize(c->st));
+  double t = 0.0;
+  for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+    float ms = 0.f;
+    HIP_TRY(c, hipEventElapsedTime(&ms, c->ev[i], c->ev[i + 1]));
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int32_t)(c->ev_used / 2);
+  c->ev_used = 0;
   return DORY_OK;
 }
 
