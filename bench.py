@@ -48,8 +48,10 @@ def decode_bytes(m, k, ctx_mean, B=1):
 
 
 def ug_bytes(m, B=1):
-    """Algorithmic bytes of one SwiGLU up/gate projection launch (B rows)."""
-    return 2 * m.d_ff * m.d_model * 2 + B * m.d_model * 2 + B * m.d_ff * 2
+    """Algorithmic bytes of one SwiGLU up/gate projection launch (B rows): the
+    two weight matrices, the prologue's inputs (sublayer output y, residual h,
+    alpha; float32) and outputs (new residual, float32; activation, bf16)."""
+    return 2 * m.d_ff * m.d_model * 2 + B * m.d_model * 4 * 3 + B * m.d_model * 4 + B * m.d_ff * 2
 
 
 def prefill_flops(m, k, n):
@@ -210,7 +212,7 @@ def main():
         ach = ug_bytes(model) / (ug_ms / 1e3)
         roof = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK, 4), "traffic": None,
-                "kernel": "k_gemv_vec (SwiGLU up/gate projection, M=1, N=2x8192, K=3072, bf16)",
+                "kernel": "k_gemv_pro<1,6,SwiGLU> (up/gate projection with the nGPT update prologue, M=1, N=2x8192, K=3072, bf16)",
                 "bytes_per_launch": ug_bytes(model), "avg_launch_us": round(ug_ms * 1e3, 2)}
     cpu = None
     if not args.no_cpu:

@@ -77,13 +77,17 @@ dory_status set_err(dory_ctx* c, dory_status s, const std::string& msg) {
       return set_err(ctx, DORY_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));          \
   } while (0)
 
-int choose_splits(int keys, int B, int nkv) {
-  int s = (keys + 63) / 64;                       // at least one 64-key tile per split
-  const int want = (512 + B * nkv - 1) / (B * nkv);  // about two workgroups per CU
-  if (s > want) s = want;
+// Key splits of decode attention: about 128 keys per workgroup, at most
+// kMaxSplits, and no more than ~4 workgroups per CU over all (row, kv head).
+int choose_splits_decode(int keys, int B, int nkv) {
+  int s = (keys + 127) / 128;
+  const int cap = (1024 + B * nkv - 1) / (B * nkv);
+  if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : s;
 }
+
+dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv);
 
 // One layer application (attention sublayer + MLP sublayer) on `rows` rows.
 // write_kv: store this application's K/V in the cache. In last-loop mode the
@@ -113,34 +117,37 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->qkvg[l], qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f, 0, st));
   }
 
-  RopeArgs ra{};
-  ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
-  ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
-  ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
-  ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
-  // one position: its slot holds no key that any query of this call needs
-  const bool direct = (n == 1) && write_kv;
-  ra.kc = direct ? kc : nullptr; ra.vc = direct ? vc : nullptr;
-  ra.slots = slots; ra.window = C.window; ra.is_full = full;
-  HIP_TRY(c, launch_rope_qk(dt, ra, st));
+  if (n == 1) {
+    dory_status s = decode_attention(c, l, loop, B, write_kv);
+    if (s != DORY_OK) return s;
+  } else {
+    RopeArgs ra{};
+    ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
+    ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
+    ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
+    ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
+    ra.kc = nullptr; ra.vc = nullptr;
+    ra.slots = slots; ra.window = C.window; ra.is_full = full;
+    HIP_TRY(c, launch_rope_qk(dt, ra, st));
 
-  AttnArgs aa{};
-  aa.q = c->ws + W.q; aa.kw = c->ws + W.kw; aa.vw = c->ws + W.vw; aa.kc = kc; aa.vc = vc;
-  aa.B = B; aa.n = n; aa.p0 = c->pos; aa.nq = C.n_q_heads; aa.nkv = C.n_kv_heads; aa.hd = C.head_dim;
-  aa.slots = slots; aa.window = C.window; aa.is_full = full;
-  const int keys = full ? c->pos + 1 : std::min(c->pos + 1, C.window);
-  aa.n_split = (n == 1) ? choose_splits(keys, B, C.n_kv_heads) : 1;
-  aa.scale = P.attn_scale;
-  aa.part = wsp<float>(c, W.part);
-  {
-    TimeScope ts(c, TIME_ATTN);
-    HIP_TRY(c, launch_attn_split(dt, aa, st));
+    AttnArgs aa{};
+    aa.q = c->ws + W.q; aa.kw = c->ws + W.kw; aa.vw = c->ws + W.vw; aa.kc = kc; aa.vc = vc;
+    aa.B = B; aa.n = n; aa.p0 = c->pos; aa.nq = C.n_q_heads; aa.nkv = C.n_kv_heads; aa.hd = C.head_dim;
+    aa.slots = slots; aa.window = C.window; aa.is_full = full;
+    aa.n_split = 1;
+    aa.scale = P.attn_scale;
+    aa.part = wsp<float>(c, W.part);
+    {
+      TimeScope ts(c, TIME_ATTN);
+      HIP_TRY(c, launch_attn_split(dt, aa, st));
+    }
+    HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
+                                   c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
+    // after attention: the ring slots of this call's positions held keys it needed
+    if (write_kv)
+      HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
+                                 slots, C.window, full, st));
   }
-  HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
-                                 c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
-  if (write_kv && !direct)
-    HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
-                               slots, C.window, full, st));
 
   {
     TimeScope ts(c, TIME_O);
@@ -159,6 +166,125 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   if (c->trace)
     HIP_TRY(c, hipMemcpyAsync(c->trace + (size_t)app * rows * C.d_model, h, (size_t)rows * C.d_model * 4,
                               hipMemcpyDeviceToDevice, st));
+  return DORY_OK;
+}
+
+// Decode attention of layer l (loop j) on the fused projection rows: RoPE,
+// q/k norm, split-K attention, new key/value into the cache, merge and gate.
+dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const WsLayout& W = P.ws;
+  const int full = P.is_full[l];
+  const int cid = c->kv.first_id[l] + ((P.recurrent(l) && c->kv.kv_mode == DORY_KV_PER_LOOP) ? loop - 1 : 0);
+  const int slots = P.slots(l);
+  char* kc = c->kvb + (size_t)c->kv.offset[cid] * P.elem;
+  char* vc = kc + (size_t)C.max_batch * C.n_kv_heads * slots * C.head_dim * P.elem;
+  float* qkvg = wsp<float>(c, W.qkvg);
+  AttnDecArgs da{};
+  da.qkvg = qkvg; da.ld = P.qkvg_dim;
+  da.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
+  da.t = c->pos; da.B = B; da.nq = C.n_q_heads; da.nkv = C.n_kv_heads; da.hd = C.head_dim;
+  da.slots = slots; da.window = C.window; da.is_full = full; da.write_kv = write_kv ? 1 : 0;
+  const int keys = full ? c->pos + 1 : std::min(c->pos + 1, C.window);
+  da.n_split = choose_splits_decode(keys, B, C.n_kv_heads);
+  da.scale = P.attn_scale;
+  da.kc = kc; da.vc = vc;
+  da.part = wsp<float>(c, W.part);
+  {
+    TimeScope ts(c, TIME_ATTN);
+    HIP_TRY(c, launch_attn_decode(C.dtype, da, c->st));
+  }
+  HIP_TRY(c, launch_attn_merge(C.dtype, da.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
+                               c->ws + W.ob, B, C.n_q_heads, C.head_dim, da.n_split, c->st));
+  return DORY_OK;
+}
+
+// Decode with the nGPT updates folded into the consuming projections: per
+// layer application the q|k|v|gate GEMV (its prologue applies the previous
+// MLP update, and at the start of loops >= 2 the re-injection of e), the
+// fused attention + merge, the output GEMV, the up/gate GEMV (prologue: the
+// attention update) and the down GEMV. Residuals alternate between two
+// buffers so the workgroup writing the new one never races readers of the old.
+bool fused_decode_ok(const dory_ctx* c, int B) {
+  const dory_config& C = c->plan.cfg;
+  return C.dtype == DORY_BF16 && !c->trace && C.n_rec >= 1 && B <= 8 && (size_t)B * C.d_model * 2 <= 64 * 1024 &&
+         C.d_model <= 8192;
+}
+
+dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const WsLayout& W = P.ws;
+  const int dt = C.dtype;
+  const int d = C.d_model;
+  hipStream_t st = c->st;
+  float* cur = wsp<float>(c, W.h);
+  float* alt = wsp<float>(c, W.hb);
+  float* e = wsp<float>(c, W.e);
+  float* y = wsp<float>(c, W.y);
+  float* qkvg = wsp<float>(c, W.qkvg);
+  void* xb = c->ws + W.xb;
+  HIP_TRY(c, launch_embed(dt, tok, c->embed, cur, C.n_in == 0 ? e : nullptr, xb, B, d, C.vocab,
+                          wsp<int>(c, W.flags), st));
+  const float* pending_alpha = nullptr;  // MLP update not yet applied to the residual
+  auto app = [&](int l, int j, bool write_kv) -> dory_status {
+    if (pending_alpha) {
+      const bool first_rec = l == C.n_in;
+      GemvPro pr{};
+      pr.y = y; pr.h_in = cur; pr.alpha = pending_alpha;
+      pr.e = (first_rec && j >= 2) ? e : nullptr;
+      pr.wh = C.combine_wh; pr.we = C.combine_we;
+      pr.h_out = alt;
+      pr.e_out = (first_rec && j == 1) ? e : nullptr;
+      TimeScope ts(c, TIME_QKVG);
+      HIP_TRY(c, launch_linear_pro(pr, c->qkvg[l], qkvg, B, P.qkvg_dim, d, 0, 1.f, st));
+      std::swap(cur, alt);
+    } else {
+      TimeScope ts(c, TIME_QKVG);
+      HIP_TRY(c, launch_linear(dt, xb, d, c->qkvg[l], qkvg, B, P.qkvg_dim, d, 0, 1.f, 0, st));
+    }
+    dory_status s = decode_attention(c, l, j, B, write_kv);
+    if (s != DORY_OK) return s;
+    {
+      TimeScope ts(c, TIME_O);
+      HIP_TRY(c, launch_linear(dt, c->ws + W.ob, P.q_dim, c->o[l], y, B, d, P.q_dim, 0, 1.f, 0, st));
+    }
+    {
+      GemvPro pr{};
+      pr.y = y; pr.h_in = cur; pr.alpha = c->alpha_attn[l];
+      pr.h_out = alt;
+      TimeScope ts(c, TIME_UG);
+      HIP_TRY(c, launch_linear_pro(pr, c->ug[l], c->ws + W.a, B, 2 * C.d_ff, d, 1, 1.f, st));
+      std::swap(cur, alt);
+    }
+    {
+      TimeScope ts(c, TIME_DOWN);
+      HIP_TRY(c, launch_linear(dt, c->ws + W.a, C.d_ff, c->down[l], y, B, d, C.d_ff, 0, 1.f, 0, st));
+    }
+    pending_alpha = c->alpha_mlp[l];
+    return DORY_OK;
+  };
+  for (int l = 0; l < C.n_in; ++l) {
+    dory_status s = app(l, 0, true);
+    if (s != DORY_OK) return s;
+  }
+  for (int j = 1; j <= k; ++j) {
+    const bool write_kv = c->kv.kv_mode == DORY_KV_PER_LOOP || j == k;
+    for (int l = C.n_in; l < C.n_in + C.n_rec; ++l) {
+      dory_status s = app(l, j, write_kv);
+      if (s != DORY_OK) return s;
+    }
+  }
+  for (int l = C.n_in + C.n_rec; l < P.n_layers; ++l) {
+    dory_status s = app(l, 0, true);
+    if (s != DORY_OK) return s;
+  }
+  // the last MLP update, then the tied LM head on the updated residual
+  HIP_TRY(c, launch_update(dt, cur, y, pending_alpha, xb, nullptr, B, d, st));
+  HIP_TRY(c, launch_linear(dt, xb, d, c->embed, wsp<float>(c, W.logits), B, C.vocab, d, 0, P.logit_scale, 0, st));
+  HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st));
+  c->has_logits = true;
   return DORY_OK;
 }
 
@@ -401,7 +527,8 @@ dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_l
   c->err.clear();
   const Plan& P = c->plan;
   const int32_t* tok = tokens_dev ? tokens_dev : wsp<int32_t>(c, P.ws.next);
-  s = run_forward(c, tok, 1, c->batch, 1, n_loops, true);
+  s = fused_decode_ok(c, c->batch) ? run_decode_fused(c, tok, c->batch, n_loops)
+                                    : run_forward(c, tok, 1, c->batch, 1, n_loops, true);
   if (s != DORY_OK) return s;
   commit_call(c, c->batch, 1, n_loops, kv_mode);
   if (next_tokens_dev)

@@ -242,3 +242,332 @@ hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, 
 }
 
 }  // namespace dory
+
+namespace dory {
+
+// ---------------------------------------------------------------------------
+// Fused decode attention. Each wave streams its own keys (8 keys per step,
+// 8 lanes per key) with its own running max / sum, so the key loop has no
+// workgroup barrier; the four waves are merged once at the end through LDS.
+// Load order matters because vector loads complete in issue order: the few
+// projection values that q and the new key need (L2-resident) are requested
+// first, then the cache rows of the wave's first U steps (HBM), and RoPE /
+// normalisation run while the cache rows are in flight. Lane `sub` of a key
+// holds 16-byte chunks sub, sub + 8, ... of the row, so every load
+// instruction reads 128 contiguous bytes per key.
+// ---------------------------------------------------------------------------
+template <typename T, int HD, int G>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
+  constexpr int KG = 8;              // keys per wave step
+  constexpr int LPK = 8;             // lanes per key
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NV = HD / (LPK * VEC);  // 16-byte chunks per lane per key row
+  constexpr int DPL = NV * VEC;         // dims per lane
+  constexpr int U = 4;               // key steps whose loads are in flight together
+  constexpr int NI = (G + 2 + 3) / 4;  // setup items per wave (q heads, new key, new value)
+  constexpr float LOG2E = 1.4426950408889634f;
+
+  __shared__ float qs[G][HD];
+  __shared__ __align__(16) T selfk[HD];
+  __shared__ __align__(16) T selfv[HD];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wacc[4][G][HD];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
+  const int t = a.t;
+  const int lo = a.is_full ? 0 : max(0, t - a.window + 1);
+  const int L = t - lo + 1;
+  int per = (L + a.n_split - 1) / a.n_split;
+  per = (per + 4 * KG - 1) / (4 * KG) * (4 * KG);
+  const int s_lo = lo + split * per;
+  const int s_hi = min(t + 1, s_lo + per);
+  const bool has_self = s_lo <= t && t < s_hi;
+  const int half = HD / 2;
+
+  // (1) projection values for q heads / new key / new value (L2). Loads are
+  // unconditional from clamped addresses (straight-line code keeps the
+  // wait counts exact); unused values are never stored.
+  const float* row = a.qkvg + (size_t)b * a.ld;
+  const int ln = min(lane, half - 1);
+  float x1[NI], x2[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = min(wave + 4 * it, G + 1);
+    const float* src = item < G ? row + (size_t)(kvh * G + item) * HD
+                                : row + (size_t)a.nq * HD + (size_t)(item - G) * a.nkv * HD + (size_t)kvh * HD;
+    x1[it] = src[ln];
+    x2[it] = src[ln + half];
+  }
+  const float2 cs = a.tab[(size_t)t * half + ln];
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
+
+  // (2) cache rows of the first U steps (HBM); out-of-range keys and the new
+  // position load a valid slot and are masked when used
+  const int kg = lane / LPK, sub = lane % LPK;
+  const T* kc = (const T*)a.kc;
+  const T* vc = (const T*)a.vc;
+  const size_t head_base = ((size_t)b * a.nkv + kvh) * a.slots;
+  u32x4 kv[U][NV], vv[U][NV];
+  auto issue = [&](int base0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = base0 + u * 4 * KG + kg;
+      const int sl = (s < s_hi && s != t) ? s : lo;
+      const int slot = a.is_full ? sl : sl % a.window;
+      const size_t o = (head_base + slot) * HD + sub * VEC;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        kv[u][i] = *(const u32x4*)(kc + o + i * LPK * VEC);
+        vv[u][i] = *(const u32x4*)(vc + o + i * LPK * VEC);
+      }
+    }
+  };
+  const int first = s_lo + wave * KG;
+  issue(first);
+
+  // (3) RoPE at t, unit norm, storage rounding; q pre-scaled for exp2
+  const float qscale = a.scale * LOG2E;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = wave + 4 * it;
+    const float y1 = lane < half ? x1[it] : 0.f, y2 = lane < half ? x2[it] : 0.f;
+    const float r1 = y1 * cs.x - y2 * cs.y;
+    const float r2 = y2 * cs.x + y1 * cs.y;
+    const float inv = inv_norm(wave_sum(r1 * r1 + r2 * r2));
+    const bool rot = item <= G;  // q heads and the new key; the value is copied
+    const T z1 = from_f<T>(rot ? r1 * inv : y1), z2 = from_f<T>(rot ? r2 * inv : y2);
+    if (lane < half && item < G + 2) {
+      if (item < G) {
+        qs[item][lane] = to_f(z1) * qscale;
+        qs[item][lane + half] = to_f(z2) * qscale;
+      } else if (has_self) {
+        T* dst = item == G ? selfk : selfv;
+        dst[lane] = z1;
+        dst[lane + half] = z2;
+      }
+    }
+  }
+  __syncthreads();
+  if (has_self && a.write_kv && tid < HD) {
+    // the slot of t held t - W (outside every window of this call) or nothing
+    const int slot = a.is_full ? t : t % a.window;
+    const size_t o = (head_base + slot) * HD + tid;
+    ((T*)a.kc)[o] = selfk[tid];
+    ((T*)a.vc)[o] = selfv[tid];
+  }
+
+  // this lane's dims: chunks sub, sub + 8, ... of VEC elements
+  float qr[G][DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) qr[g][i * VEC + j] = qs[g][(i * LPK + sub) * VEC + j];
+
+  float m[G], l[G], acc[G][DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[g][i] = 0.f;
+  }
+
+  for (int base0 = first; base0 < s_hi; base0 += 4 * KG * U) {
+    if (base0 != first) issue(base0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = base0 + u * 4 * KG;
+      if (base >= s_hi) break;  // wave-uniform
+      const int s = base + kg;
+      const bool valid = s < s_hi;
+      if (valid && s == t) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          kv[u][i] = *(const u32x4*)(selfk + (i * LPK + sub) * VEC);
+          vv[u][i] = *(const u32x4*)(selfv + (i * LPK + sub) * VEC);
+        }
+      }
+      float kf[DPL], vf[DPL];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (!valid) vv[u][i] = u32x4{0, 0, 0, 0};  // masked keys: p = 0 must not meet NaN
+        const uint32_t* kw = (const uint32_t*)&kv[u][i];
+        const uint32_t* vw = (const uint32_t*)&vv[u][i];
+        if (sizeof(T) == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kf[i * 8 + 2 * j] = bf_lo(kw[j]);
+            kf[i * 8 + 2 * j + 1] = bf_hi(kw[j]);
+            vf[i * 8 + 2 * j] = bf_lo(vw[j]);
+            vf[i * 8 + 2 * j + 1] = bf_hi(vw[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kf[i * 4 + j] = __uint_as_float(kw[j]);
+            vf[i * 4 + j] = __uint_as_float(vw[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) d = fmaf(qr[g][i], kf[i], d);
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        d += __shfl_xor(d, 4, 64);
+        const float sc = valid ? d : -INFINITY;
+        float mt = fmaxf(sc, __shfl_xor(sc, 8, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m[g], mt);
+        const float alpha = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mn);
+        const float p = valid ? exp2f(sc - mn) : 0.f;
+        float ps = p + __shfl_xor(p, 8, 64);
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l[g] = l[g] * alpha + ps;
+        m[g] = mn;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[g][i] = fmaf(p, vf[i], acc[g][i] * alpha);
+      }
+    }
+  }
+
+  // sum the 8 key groups of the wave (same running max across the wave)
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      float v = acc[g][i];
+      v += __shfl_xor(v, 8, 64);
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      acc[g][i] = v;
+    }
+  if (kg == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) wacc[wave][g][(i * LPK + sub) * VEC + j] = acc[g][i * VEC + j];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      wm[wave][g] = m[g];
+      wl[wave][g] = l[g];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * HD; e += 256) {
+    const int g = e / HD, d = e % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
+    float Ls = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (wm[w][g] == -INFINITY) continue;
+        const float f = exp2f(wm[w][g] - M);
+        Ls = fmaf(wl[w][g], f, Ls);
+        A = fmaf(wacc[w][g][d], f, A);
+      }
+    }
+    float* out = a.part + (((size_t)b * a.nq + kvh * G + g) * a.n_split + split) * (HD + 2);
+    out[2 + d] = A;
+    if (d == 0) {
+      out[0] = M;
+      out[1] = Ls;
+    }
+  }
+
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(const float* __restrict__ part, const float* __restrict__ qkvg,
+                                                  int64_t ld, int gate_off, int gate, T* __restrict__ ob, int nq,
+                                                  int n_split) {
+  __shared__ float wsh[64];
+  __shared__ float lsh[64];
+  __shared__ float red[HD / 64];
+  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const float* p = part + ((size_t)b * nq + hq) * n_split * (HD + 2);
+  // every split's max and sum at once (n_split <= 64)
+  const float ms = d < n_split ? p[(size_t)d * (HD + 2)] : -INFINITY;
+  const float ls = d < n_split ? p[(size_t)d * (HD + 2) + 1] : 0.f;
+  float M = wave_max(ms);
+  if (HD > 64) {
+    if ((d & 63) == 0) red[d >> 6] = M;
+    __syncthreads();
+    M = red[0];
+    for (int i = 1; i < HD / 64; ++i) M = fmaxf(M, red[i]);
+  }
+  if (d < n_split) {
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    wsh[d] = w;
+    lsh[d] = ls * w;
+  }
+  __syncthreads();
+  float L = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < n_split; ++s) {
+    L += lsh[s];
+    o = fmaf(p[(size_t)s * (HD + 2) + 2 + d], wsh[s], o);
+  }
+  const float* gr = qkvg + (size_t)b * ld + gate_off;
+  const float g = gate == 1 ? sigmoidf_(gr[hq * HD + d]) : (gate == 2 ? sigmoidf_(gr[hq]) : 1.f);
+  ob[((size_t)b * nq + hq) * HD + d] = from_f<T>(o / L * g);
+}
+
+template <typename T, int HD>
+static hipError_t attn_dec_hd(const AttnDecArgs& a, hipStream_t st) {
+  dim3 grid(a.n_split, a.B * a.nkv);
+  switch (a.nq / a.nkv) {
+    case 1: hipLaunchKernelGGL((k_attn_decode<T, HD, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_decode<T, HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_decode<T, HD, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_decode<T, HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_attn_decode<T, HD, 6>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_attn_decode<T, HD, 8>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (a.hd == 64) return attn_dec_hd<float, 64>(a, st);
+    if (a.hd == 128) return attn_dec_hd<float, 128>(a, st);
+  } else {
+    if (a.hd == 64) return attn_dec_hd<bf16, 64>(a, st);
+    if (a.hd == 128) return attn_dec_hd<bf16, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off, int gate,
+                             void* ob, int B, int nq, int hd, int n_split, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  dim3 grid(nq, B);
+#define DORY_MRG(T, HDV)                                                                                  \
+  hipLaunchKernelGGL((k_attn_merge<T, HDV>), grid, dim3(HDV), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, nq, \
+                     n_split)
+  if (dtype == 0) {
+    if (hd == 64) DORY_MRG(float, 64); else if (hd == 128) DORY_MRG(float, 128); else return hipErrorInvalidValue;
+  } else {
+    if (hd == 64) DORY_MRG(bf16, 64); else if (hd == 128) DORY_MRG(bf16, 128); else return hipErrorInvalidValue;
+  }
+#undef DORY_MRG
+  return hipGetLastError();
+}
+
+}  // namespace dory

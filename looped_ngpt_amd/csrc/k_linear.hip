@@ -104,6 +104,271 @@ __global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64
   }
 }
 
+// GEMV for bfloat16 decode, row loads first. Each of the 8 waves of a
+// workgroup owns one output (two weight rows for SwiGLU). All CH 16-byte
+// chunks of its rows are requested before the activations are staged in LDS,
+// so the HBM latency of the weights overlaps the activation staging and the
+// workgroup barrier; then each lane multiplies its chunks and a wave
+// reduction closes the dot products.
+template <int MB, int CH, int EPI>
+__global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, int64_t ldx,
+                                                  const bf16* __restrict__ W, void* __restrict__ y, int M, int N,
+                                                  int K, float scale) {
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* xs = (bf16*)smem;
+  const int nv = K / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o = blockIdx.x * 8 + wave;
+  const bool live = o < nout;
+  const int oc = live ? o : nout - 1;
+
+  // activations first (vector loads complete in issue order), then weights
+  constexpr int XV = (MB * CH + 7) / 8;  // MB rows x nv <= 64*CH vectors over 512 threads
+  u32x4 xr[XV];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + 512 * q;
+    const int ec = min(e, M * nv - 1);
+    xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  u32x4 wv[NR][CH];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const u32x4* wr = (const u32x4*)(W + (size_t)(j ? nout + oc : oc) * K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // clamped, unconditional: straight-line loads keep exact wait counts;
+      // chunks past the row are ignored in the product below
+      const int v = min(lane + 64 * c, nv - 1);
+      wv[j][c] = __builtin_nontemporal_load(wr + v);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + 512 * q;
+    if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float acc[MB][NR];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int v = lane + 64 * c;
+    if (v < nv) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < M) {
+          const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
+#pragma unroll
+          for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j][c], xv, (const bf16*)nullptr);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= M) break;
+    const float s = wave_sum(acc[m][0]);
+    if (EPI == EPI_SWIGLU) {
+      const float g = wave_sum(acc[m][NR - 1]);
+      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
+    } else {
+      if (lane == 0) ((float*)y)[(size_t)m * N + o] = s * scale;
+    }
+  }
+}
+
+template <int MB, int EPI>
+static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                             hipStream_t st) {
+  const int ch = (K / 8 + 63) / 64;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const dim3 grid((nout + 7) / 8);
+  const size_t lds = (size_t)M * K * 2;
+#define DORY_ROWS(C) \
+  case C: hipLaunchKernelGGL((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale); return true;
+  switch (ch) {
+    DORY_ROWS(1) DORY_ROWS(2) DORY_ROWS(3) DORY_ROWS(4) DORY_ROWS(5) DORY_ROWS(6) DORY_ROWS(8) DORY_ROWS(12)
+    DORY_ROWS(16)
+    default: return false;
+  }
+#undef DORY_ROWS
+}
+
+// k_gemv_rows with the residual update in the prologue (see launch_linear_pro).
+template <int MB, int CH, int EPI>
+__global__ __launch_bounds__(512) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W, void* __restrict__ y,
+                                                 int M, int N, int K, float scale) {
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ float sh[8];
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* xs = (bf16*)smem;
+  const int nv = K / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o = blockIdx.x * 8 + wave;
+  const bool live = o < nout;
+  const int oc = live ? o : nout - 1;
+
+  // prologue inputs of row 0 first (vector loads complete in issue order),
+  // then the weights; element i = threadIdx.x + 512*c (CH*512 >= K)
+  constexpr int EPT = CH;
+  // e is read unconditionally (from y when there is no re-injection) so that
+  // no branch separates these loads
+  const float* ep = pr.e ? pr.e : pr.y;
+  float yv[EPT], hv[EPT], av[EPT], ev[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) {
+    const int i = min((int)threadIdx.x + 512 * c, K - 1);
+    const bool in = threadIdx.x + 512 * c < K;
+    const float y0 = pr.y[i], h0 = pr.h_in[i], a0 = pr.alpha[i], e0 = ep[i];
+    yv[c] = in ? y0 : 0.f;
+    hv[c] = in ? h0 : 0.f;
+    av[c] = in ? a0 : 0.f;
+    ev[c] = in ? e0 : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  u32x4 wv[NR][CH];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const u32x4* wr = (const u32x4*)(W + (size_t)(j ? nout + oc : oc) * K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // clamped, unconditional: straight-line loads keep exact wait counts;
+      // chunks past the row are ignored in the product below
+      const int v = min(lane + 64 * c, nv - 1);
+      wv[j][c] = __builtin_nontemporal_load(wr + v);
+    }
+  }
+
+  for (int m = 0; m < M; ++m) {
+    const size_t ro = (size_t)m * K;
+    if (m > 0) {
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        const int i = threadIdx.x + 512 * c;
+        yv[c] = i < K ? pr.y[ro + i] : 0.f;
+        hv[c] = i < K ? pr.h_in[ro + i] : 0.f;
+        ev[c] = i < K ? ep[ro + i] : 0.f;
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) ss += yv[c] * yv[c];
+    const float iy = inv_norm(block_sum<512>(ss, sh));
+    float st = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      hv[c] = hv[c] + av[c] * (yv[c] * iy - hv[c]);
+      st += hv[c] * hv[c];
+    }
+    const float ih = inv_norm(block_sum<512>(st, sh));
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
+    if (pr.e_out && blockIdx.x == 0) {
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        const int i = threadIdx.x + 512 * c;
+        if (i < K) pr.e_out[ro + i] = hv[c];
+      }
+    }
+    if (pr.e) {
+      float sv = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        const int i = threadIdx.x + 512 * c;
+        yv[c] = i < K ? pr.wh * hv[c] + pr.we * ev[c] : 0.f;
+        sv += yv[c] * yv[c];
+      }
+      const float iv = inv_norm(block_sum<512>(sv, sh));
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
+    }
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      const int i = threadIdx.x + 512 * c;
+      if (i < K) {
+        xs[ro + i] = from_f<bf16>(hv[c]);
+        if (blockIdx.x == 0) pr.h_out[ro + i] = hv[c];
+      }
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float acc[MB][NR];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int v = lane + 64 * c;
+    if (v < nv) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < M) {
+          const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
+#pragma unroll
+          for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j][c], xv, (const bf16*)nullptr);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= M) break;
+    const float s = wave_sum(acc[m][0]);
+    if (EPI == EPI_SWIGLU) {
+      const float g = wave_sum(acc[m][NR - 1]);
+      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
+    } else {
+      if (lane == 0) ((float*)y)[(size_t)m * N + o] = s * scale;
+    }
+  }
+}
+
+template <int MB, int EPI>
+static hipError_t gemv_pro_launch(const GemvPro& p, const bf16* W, void* y, int M, int N, int K, float scale,
+                                  hipStream_t st) {
+  const int ch = (K / 8 + 63) / 64;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const dim3 grid((nout + 7) / 8);
+  const size_t lds = (size_t)M * K * 2;
+#define DORY_PRO(C) \
+  case C: hipLaunchKernelGGL((k_gemv_pro<MB, C, EPI>), grid, dim3(512), lds, st, p, W, y, M, N, K, scale); break;
+  switch (ch) {
+    DORY_PRO(4) DORY_PRO(5) DORY_PRO(6) DORY_PRO(8) DORY_PRO(12) DORY_PRO(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef DORY_PRO
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, int N, int K, int epi, float scale,
+                             hipStream_t st) {
+  if (M < 1 || M > 8 || K % 8 || (size_t)M * K * 2 > 64 * 1024 || ((uintptr_t)W & 15)) return hipErrorInvalidValue;
+  const bf16* w = (const bf16*)W;
+#define DORY_PRO_M(E)                                                                                    \
+  if (M == 1) return gemv_pro_launch<1, E>(p, w, y, M, N, K, scale, st);                                  \
+  if (M == 2) return gemv_pro_launch<2, E>(p, w, y, M, N, K, scale, st);                                  \
+  if (M <= 4) return gemv_pro_launch<4, E>(p, w, y, M, N, K, scale, st);                                  \
+  return gemv_pro_launch<8, E>(p, w, y, M, N, K, scale, st);
+  if (epi == EPI_SWIGLU) {
+    DORY_PRO_M(EPI_SWIGLU)
+  }
+  DORY_PRO_M(EPI_F32)
+#undef DORY_PRO_M
+}
+
 // Scalar GEMV (any K, any alignment): one wave per output.
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void k_gemv_scalar(const T* __restrict__ x, int64_t ldx, const T* __restrict__ W,
@@ -324,6 +589,28 @@ static hipError_t gemv_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     dim3 grid((nout + 3) / 4, M);
     hipLaunchKernelGGL((k_gemv_scalar<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
     return hipGetLastError();
+  }
+  if (sizeof(T) == 2) {
+    // row-loads-first kernel: up to 8 rows per launch, staged rows within 64 KB
+    int mb = (int)((64 * 1024) / ((size_t)K * 2));
+    mb = mb > 8 ? 8 : mb;
+    bool ok = mb >= 1;
+    for (int m0 = 0; ok && m0 < M; m0 += mb) {
+      const int mm = M - m0 < mb ? M - m0 : mb;
+      const bf16* xm = (const bf16*)x + (size_t)m0 * ldx;
+      void* ym = (char*)y + (size_t)m0 * ostride * osz;
+      if (mm == 1) ok = gemv_rows_launch<1, EPI>(xm, ldx, (const bf16*)W, ym, mm, N, K, scale, st);
+      else if (mm == 2) ok = gemv_rows_launch<2, EPI>(xm, ldx, (const bf16*)W, ym, mm, N, K, scale, st);
+      else if (mm <= 4) ok = gemv_rows_launch<4, EPI>(xm, ldx, (const bf16*)W, ym, mm, N, K, scale, st);
+      else ok = gemv_rows_launch<8, EPI>(xm, ldx, (const bf16*)W, ym, mm, N, K, scale, st);
+      if (ok) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      } else if (m0 != 0) {
+        return hipErrorInvalidValue;  // chunk count is a property of K: never changes mid-way
+      }
+    }
+    if (ok) return hipSuccess;
   }
   // rows per launch limited by LDS (64 KB of staged activations)
   int mb = (int)((64 * 1024) / ((size_t)K * sizeof(T)));

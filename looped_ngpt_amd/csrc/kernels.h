@@ -58,9 +58,48 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off,
                                int gate, void* ob, int rows, int nq, int hd, int n_split, hipStream_t st);
 
+// Decode attention for one new position t of B sequences (all at position t),
+// fused with RoPE and the q/k normalisation: every workgroup (key split,
+// sequence x kv head) builds its G query heads from the fused projection; the
+// workgroup whose split holds t also builds the new key/value (and writes
+// them to the cache slot of t when write_kv). Keys s < t come from the cache.
+// Writes partials (m in log2 units, l, acc[hd]) per (b, q head, split).
+struct AttnDecArgs {
+  const float* qkvg; int64_t ld;
+  const float2* tab;
+  int t, B, nq, nkv, hd, slots, window, is_full, write_kv, n_split;
+  float scale;
+  void* kc; void* vc;
+  float* part;
+};
+hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st);
+
+// Merges the decode partials (log2 units), applies the sigmoid gate (gate 1
+// elementwise, 2 per head, 0 none; read at gate_off of the projection row),
+// stores the gated heads in ob [B][nq*hd]. One workgroup per (q head, row).
+// (A last-workgroup merge inside the attention kernel needs device-scope
+// fences, which cost far more than this launch on gfx950.)
+hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off, int gate,
+                             void* ob, int B, int nq, int hd, int n_split, hipStream_t st);
+
 // y = x . W^T (see dory_op_linear).
 hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K,
                          int epi, float scale, int algo, hipStream_t st);
+
+// Decode GEMV whose input row is produced in its own prologue: every
+// workgroup first issues its weight loads, then computes for each of the M
+// rows   u = norm(h_in + alpha * (norm(y) - h_in))            (nGPT update)
+//        x = e ? norm(wh * u + we * e) : u                    (loop re-injection)
+// in float32, stages bfloat16(x) in LDS and multiplies. Workgroup 0 writes x
+// to h_out (the new residual) and, if e_out, u to e_out. bfloat16 only,
+// M <= 8, K = d_model <= 8192. Returns hipErrorInvalidValue when unsupported.
+struct GemvPro {
+  const float* y; const float* h_in; const float* alpha; const float* e;
+  float wh, we;
+  float* h_out; float* e_out;
+};
+hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, int N, int K, int epi, float scale,
+                             hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st);
 

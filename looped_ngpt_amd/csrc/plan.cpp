@@ -112,6 +112,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.h = take(R * c.d_model * 4);
   w.e = take(R * c.d_model * 4);
   w.xb = take(R * c.d_model * el);
+  w.hb = take((size_t)c.max_batch * c.d_model * 4);
   w.qkvg = take(R * p.qkvg_dim * 4);
   w.q = take(R * p.q_dim * el);
   w.kw = take(R * p.kv_dim * el);
