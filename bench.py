@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--headline-k", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-steps", type=int, default=16, help="decode steps of the kernel-timing pass")
+    ap.add_argument("--graphs", action="store_true", help="replay decode steps as recorded HIP graphs")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -151,7 +152,9 @@ def main():
     if args.headline_k not in ks:
         ks.append(args.headline_k)
     n, K, Wm = args.prompt, args.steps, args.warmup
-    max_ctx = n + Wm + K + args.kernel_steps + 2
+    # positions needed, rounded to 256 (a multiple of 4 keeps the cached
+    # values' 4-position runs aligned for the matrix-core decode attention)
+    max_ctx = (n + Wm + K + args.kernel_steps + 2 + 255) // 256 * 256
 
     t0 = time.perf_counter()
     w = make_weights_device(model, dev)
@@ -167,6 +170,7 @@ def main():
     ug_ms = None
     sess = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=n, kv_mode="last_loop",
                         stream=stream, device=dev)
+    sess.set_graphs(args.graphs)
     for k in ks:
         sess.reset()
         torch.cuda.synchronize()
@@ -183,11 +187,14 @@ def main():
             sess.decode(None, k)
         torch.cuda.synchronize()
         e0.record(stream)
+        th = time.perf_counter()
         for _ in range(K):
             sess.decode(None, k)
+        host_ms = (time.perf_counter() - th) * 1e3  # enqueue time: host-bound if close to ms
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
+        print(f"[bench] k={k} host enqueue {host_ms / K:.3f} ms/step", file=sys.stderr, flush=True)
         ctx_mean = n + Wm + (K - 1) / 2.0
         step_bytes = decode_bytes(model, k, ctx_mean)
         by_k[k] = {"tokens_per_s": K / (ms / 1e3), "ms_per_step": ms / K,

@@ -79,7 +79,8 @@ typedef struct {
   float combine_wh;       /* loop re-injection x_j = norm(wh*h_{j-1} + we*e), j >= 2   */
   float combine_we;
   int32_t max_batch;      /* sequences per call                                        */
-  int32_t max_ctx;        /* positions per sequence                                    */
+  int32_t max_ctx;        /* positions per sequence (bfloat16 decode attention runs on
+                             the matrix cores when max_ctx and window are multiples of 4) */
   int32_t max_chunk;      /* positions per prefill chunk (longer prompts are chunked)  */
   int32_t max_loops;      /* largest n_loops accepted                                  */
 } dory_config;
@@ -115,10 +116,12 @@ dory_status dory_validate_config(const dory_config* cfg);
 /* Bytes of the KV buffer for a kv mode. kv_loops is the number of per-loop
  * caches per recurrent layer (ignored in last-loop mode). Layout: caches
  * numbered layer by layer (a recurrent layer in per-loop mode owns kv_loops
- * consecutive ids, loop j -> base + j - 1); cache c holds K then V, each
- * [max_batch][n_kv][slots_c][head_dim], with slots = max_ctx for full layers
- * and min(window, max_ctx) for sliding layers (a ring, slot = pos mod window).
- * Returns 0 for an invalid config. */
+ * consecutive ids, loop j -> base + j - 1); cache c holds K as
+ * [max_batch][n_kv][slots_c][head_dim] and then V transposed per head as
+ * [max_batch][n_kv][head_dim][slots_c] (keys contiguous for each dimension,
+ * the operand order of the P.V matrix-core product), with slots = max_ctx
+ * for full layers and min(window, max_ctx) for sliding layers (a ring,
+ * slot = pos mod window). Returns 0 for an invalid config. */
 size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops);
 
 /* Bytes of the workspace dory_create needs (activations for max_batch *
@@ -126,8 +129,9 @@ size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops);
 size_t dory_workspace_bytes(const dory_config* cfg);
 
 /* Where the KV of (layer, loop, pos) lives: cache id, slot, and the element
- * offsets of K and V of batch row 0, kv head 0 in the KV buffer. loop is
- * 1-based for recurrent layers and ignored for the others. */
+ * offsets of dimension 0 of K and of V for batch row 0, kv head 0 in the KV
+ * buffer (K's dimensions follow contiguously, V's every slots_c elements).
+ * loop is 1-based for recurrent layers and ignored for the others. */
 dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops,
                          int32_t layer, int32_t loop, int32_t pos,
                          int32_t* cache_id, int32_t* slot,
@@ -183,6 +187,20 @@ const char* dory_last_error(const dory_ctx* ctx);
  * chunk or decode call; the buffer must hold max_apps entries (calls with more
  * layer applications return DORY_E_CAPACITY). NULL turns the tap off. */
 dory_status dory_set_trace(dory_ctx* ctx, float* trace_dev, int32_t max_apps);
+
+/* Recorded decode steps. With enable != 0, decode steps that continue from
+ * the previous greedy tokens (tokens_dev NULL) on a bfloat16 model are
+ * recorded once per (n_loops, batch) as a HIP graph and replayed afterwards on
+ * a private stream that two events order after and before the context's
+ * stream. enable = 0 (the default) launches every step kernel by kernel and
+ * frees the recorded graphs. Results are bit-identical either way: every
+ * kernel argument of a decode step is the same at every position (the
+ * position is a device counter that prefill sets and each decode step's
+ * argmax advances), which also lets a caller record dory_decode_step into a
+ * graph of its own. Replays cost less host time per step and, on ROCm 7.2,
+ * slightly more GPU time, so they pay off only when the host is the
+ * bottleneck. */
+dory_status dory_set_graphs(dory_ctx* ctx, int32_t enable);
 
 /* Kernel timing tap. When kind is not 0, every launch of one kernel class is
  * bracketed by HIP events recorded on the context's stream:

@@ -33,13 +33,33 @@ struct dory_ctx {
   // test tap
   float* trace = nullptr;
   int trace_max = 0;
+  // recorded decode steps, keyed by (n_loops, batch)
+  // Recorded and replayed on a private stream (the caller's may be the null
+  // stream, which cannot be recorded), ordered after and before the caller's
+  // stream by two events.
+  bool graphs_on = false;
+  struct Graph { int k, B; hipGraph_t g; hipGraphExec_t x; };
+  std::vector<Graph> graphs;
+  hipStream_t gst = nullptr;
+  hipEvent_t gev[2] = {nullptr, nullptr};
   // timing tap
   int time_kind = 0;
   std::vector<hipEvent_t> ev;
   size_t ev_used = 0;
   std::string err;
+  void drop_graphs() {
+    for (auto& g : graphs) {
+      (void)hipGraphExecDestroy(g.x);
+      (void)hipGraphDestroy(g.g);
+    }
+    graphs.clear();
+  }
   ~dory_ctx() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    drop_graphs();
+    for (hipEvent_t e : gev)
+      if (e) (void)hipEventDestroy(e);
+    if (gst) (void)hipStreamDestroy(gst);
   }
 };
 
@@ -184,10 +204,15 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
   AttnDecArgs da{};
   da.qkvg = qkvg; da.ld = P.qkvg_dim;
   da.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
-  da.t = c->pos; da.B = B; da.nq = C.n_q_heads; da.nkv = C.n_kv_heads; da.hd = C.head_dim;
+  da.t_dev = wsp<int>(c, W.pos); da.B = B; da.nq = C.n_q_heads; da.nkv = C.n_kv_heads; da.hd = C.head_dim;
   da.slots = slots; da.window = C.window; da.is_full = full; da.write_kv = write_kv ? 1 : 0;
-  const int keys = full ? c->pos + 1 : std::min(c->pos + 1, C.window);
-  da.n_split = choose_splits_decode(keys, B, C.n_kv_heads);
+  // split count from the capacity (not the position), so a recorded graph
+  // replays at every step; the kernel spreads the actual keys over the splits
+  const int key_cap = full ? C.max_ctx : std::min(C.window, C.max_ctx);
+  if (attn_decode_uses_mfma(C.dtype, C.head_dim, slots, C.window, full))
+    da.n_split = choose_splits_decode(((key_cap + 31) / 32 + 1) * 32, B, C.n_kv_heads);  // 32-position tiles
+  else
+    da.n_split = choose_splits_decode(key_cap, B, C.n_kv_heads);
   da.scale = P.attn_scale;
   da.kc = kc; da.vc = vc;
   da.part = wsp<float>(c, W.part);
@@ -196,7 +221,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
     HIP_TRY(c, launch_attn_decode(C.dtype, da, c->st));
   }
   HIP_TRY(c, launch_attn_merge(C.dtype, da.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
-                               c->ws + W.ob, B, C.n_q_heads, C.head_dim, da.n_split, c->st));
+                                 c->ws + W.ob, B, C.n_q_heads, C.head_dim, da.n_split, c->st));
   return DORY_OK;
 }
 
@@ -208,8 +233,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
 // buffers so the workgroup writing the new one never races readers of the old.
 bool fused_decode_ok(const dory_ctx* c, int B) {
   const dory_config& C = c->plan.cfg;
-  return C.dtype == DORY_BF16 && !c->trace && C.n_rec >= 1 && B <= 8 && (size_t)B * C.d_model * 2 <= 64 * 1024 &&
-         C.d_model <= 8192;
+  return C.dtype == DORY_BF16 && !c->trace && C.n_rec >= 1 && linear_pro_supported(B, C.d_model);
 }
 
 dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
@@ -283,7 +307,8 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
   // the last MLP update, then the tied LM head on the updated residual
   HIP_TRY(c, launch_update(dt, cur, y, pending_alpha, xb, nullptr, B, d, st));
   HIP_TRY(c, launch_linear(dt, xb, d, c->embed, wsp<float>(c, W.logits), B, C.vocab, d, 0, P.logit_scale, 0, st));
-  HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st));
+  HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st,
+                           wsp<int>(c, W.pos)));
   c->has_logits = true;
   return DORY_OK;
 }
@@ -301,7 +326,10 @@ dory_status device_init(dory_ctx* c) {
 }
 
 // n new positions of B sequences (one prefill chunk or one decode step).
-dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, int n, int k, bool logits) {
+// decode: the device position already equals c->pos (set by the last prefill,
+// advanced by every decode step's argmax).
+dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, int n, int k, bool logits,
+                        bool decode = false) {
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
   const WsLayout& W = P.ws;
@@ -320,6 +348,7 @@ dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, 
                                 hipMemcpyDeviceToDevice, st));
     trows = dst;
   }
+  if (n == 1 && !decode) HIP_TRY(c, launch_set_pos(wsp<int>(c, W.pos), c->pos, st));  // decode kernels read it
   HIP_TRY(c, launch_embed(dt, trows, c->embed, h, C.n_in == 0 ? e : nullptr, xb, rows, C.d_model, C.vocab,
                           wsp<int>(c, W.flags), st));
   int app = 0;
@@ -343,9 +372,52 @@ dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, 
     const char* last = (const char*)xb + (size_t)(n - 1) * C.d_model * P.elem;
     HIP_TRY(c, launch_linear(dt, last, (int64_t)n * C.d_model, c->embed, wsp<float>(c, W.logits), B, C.vocab,
                              C.d_model, 0, P.logit_scale, 0, st));
-    HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st));
+    HIP_TRY(c, launch_argmax(wsp<float>(c, W.logits), B, C.vocab, wsp<int32_t>(c, W.next), c->ws + W.amax, st,
+                             decode ? wsp<int>(c, W.pos) : nullptr));
     c->has_logits = true;
   }
+  return DORY_OK;
+}
+
+// One decode step as a recorded HIP graph (recorded on first use for this
+// (n_loops, batch); every argument is step-invariant: the position comes from
+// the device counter and the tokens from the previous step's argmax).
+dory_status decode_graph(dory_ctx* c, int k) {
+  const int B = c->batch;
+  if (!c->gst) {
+    HIP_TRY(c, hipStreamCreateWithFlags(&c->gst, hipStreamNonBlocking));
+    for (hipEvent_t& e : c->gev) HIP_TRY(c, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
+  hipGraphExec_t x = nullptr;
+  for (auto& g : c->graphs)
+    if (g.k == k && g.B == B) x = g.x;
+  if (!x) {
+    dory_ctx::Graph g{k, B, nullptr, nullptr};
+    hipStream_t user = c->st;
+    c->st = c->gst;
+    hipError_t e = hipStreamBeginCapture(c->gst, hipStreamCaptureModeThreadLocal);
+    dory_status s = e == hipSuccess ? run_decode_fused(c, wsp<int32_t>(c, c->plan.ws.next), B, k) : DORY_OK;
+    if (e == hipSuccess) e = hipStreamEndCapture(c->gst, &g.g);
+    c->st = user;
+    if (s != DORY_OK || e != hipSuccess) {
+      if (g.g) (void)hipGraphDestroy(g.g);
+      if (s != DORY_OK) return s;
+      return set_err(c, DORY_E_HIP, std::string("recording the decode step: ") + hipGetErrorString(e));
+    }
+    e = hipGraphInstantiate(&g.x, g.g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(g.g);
+      return set_err(c, DORY_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    }
+    c->graphs.push_back(g);
+    x = g.x;
+  }
+  HIP_TRY(c, hipEventRecord(c->gev[0], c->st));
+  HIP_TRY(c, hipStreamWaitEvent(c->gst, c->gev[0], 0));
+  HIP_TRY(c, hipGraphLaunch(x, c->gst));
+  HIP_TRY(c, hipEventRecord(c->gev[1], c->gst));
+  HIP_TRY(c, hipStreamWaitEvent(c->st, c->gev[1], 0));
+  c->has_logits = true;
   return DORY_OK;
 }
 
@@ -436,7 +508,7 @@ dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loo
   if (cache_id) *cache_id = id;
   if (slot) *slot = sl;
   if (k_offset) *k_offset = kv.offset[id] + (int64_t)sl * p.cfg.head_dim;
-  if (v_offset) *v_offset = kv.offset[id] + half + (int64_t)sl * p.cfg.head_dim;
+  if (v_offset) *v_offset = kv.offset[id] + half + sl;  // V is [hd][slots]: dim d at + d * slots
   return DORY_OK;
 }
 
@@ -515,6 +587,7 @@ dory_status dory_prefill(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, 
     if (s != DORY_OK) return s;
     commit_call(c, batch, m, n_loops, kv_mode);
   }
+  HIP_TRY(c, launch_set_pos(wsp<int>(c, c->plan.ws.pos), c->pos, c->st));  // next decode position
   return DORY_OK;
 }
 
@@ -527,8 +600,13 @@ dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_l
   c->err.clear();
   const Plan& P = c->plan;
   const int32_t* tok = tokens_dev ? tokens_dev : wsp<int32_t>(c, P.ws.next);
-  s = fused_decode_ok(c, c->batch) ? run_decode_fused(c, tok, c->batch, n_loops)
-                                    : run_forward(c, tok, 1, c->batch, 1, n_loops, true);
+  const bool fused = fused_decode_ok(c, c->batch);
+  if (fused && c->graphs_on && !tokens_dev && c->time_kind == 0) {
+    s = decode_graph(c, n_loops);
+  } else {
+    s = fused ? run_decode_fused(c, tok, c->batch, n_loops)
+              : run_forward(c, tok, 1, c->batch, 1, n_loops, true, true);
+  }
   if (s != DORY_OK) return s;
   commit_call(c, c->batch, 1, n_loops, kv_mode);
   if (next_tokens_dev)
@@ -552,6 +630,13 @@ dory_status dory_set_trace(dory_ctx* c, float* trace_dev, int32_t max_apps) {
   if (trace_dev && max_apps < 1) return DORY_E_ARG;
   c->trace = trace_dev;
   c->trace_max = trace_dev ? max_apps : 0;
+  return DORY_OK;
+}
+
+dory_status dory_set_graphs(dory_ctx* c, int32_t enable) {
+  if (!c) return DORY_E_ARG;
+  c->graphs_on = enable != 0;
+  if (!c->graphs_on) c->drop_graphs();
   return DORY_OK;
 }
 

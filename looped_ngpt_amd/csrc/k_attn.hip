@@ -73,25 +73,31 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     for (int e = tid; e < TK * VPK; e += 256) {
       const int kk = e / VPK, c = e % VPK;
       uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      const int s = s0 + kk;
+      const bool cached = kk < nk && s < a.p0;  // its values come from the loop below
       if (kk < nk) {
-        const int s = s0 + kk;
-        const T* ks;
-        const T* vs;
         if (s >= a.p0) {
           const size_t o = ((size_t)(b * a.n + (s - a.p0)) * a.nkv + kvh) * HD;
-          ks = kw + o;
-          vs = vw + o;
+          kv4 = ((const uint4*)(kw + o))[c];
+          vv4 = ((const uint4*)(vw + o))[c];
         } else {
           const int slot = a.is_full ? s : s % a.window;
-          const size_t o = (((size_t)b * a.nkv + kvh) * a.slots + slot) * HD;
-          ks = kc + o;
-          vs = vc + o;
+          kv4 = ((const uint4*)(kc + (((size_t)b * a.nkv + kvh) * a.slots + slot) * HD))[c];
         }
-        kv4 = ((const uint4*)ks)[c];
-        vv4 = ((const uint4*)vs)[c];
       }
       *(uint4*)(Ks + kk * KLD + c * VEC) = kv4;
-      *(uint4*)(Vs + kk * HD + c * VEC) = vv4;
+      if (!cached) *(uint4*)(Vs + kk * HD + c * VEC) = vv4;
+    }
+    // cached values are stored transposed ([hd][slots]): consecutive threads
+    // take consecutive keys of one dimension
+    const size_t vhead = ((size_t)b * a.nkv + kvh) * HD * a.slots;
+    for (int e = tid; e < TK * HD; e += 256) {
+      const int d = e / TK, kk = e % TK;
+      const int s = s0 + kk;
+      if (kk < nk && s < a.p0) {
+        const int slot = a.is_full ? s : s % a.window;
+        Vs[kk * HD + d] = vc[vhead + (size_t)d * a.slots + slot];
+      }
     }
     __syncthreads();
 
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int split = blockIdx.x;
   const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
-  const int t = a.t;
+  const int t = *a.t_dev;  // position of the new key (device counter: graph-replayable)
   const int lo = a.is_full ? 0 : max(0, t - a.window + 1);
   const int L = t - lo + 1;
   int per = (L + a.n_split - 1) / a.n_split;
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
   const T* vc = (const T*)a.vc;
   const size_t head_base = ((size_t)b * a.nkv + kvh) * a.slots;
   u32x4 kv[U][NV], vv[U][NV];
+  const T* vt = vc + head_base * HD;  // this head's transposed values [hd][slots]
   auto issue = [&](int base0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -320,7 +327,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         kv[u][i] = *(const u32x4*)(kc + o + i * LPK * VEC);
-        vv[u][i] = *(const u32x4*)(vc + o + i * LPK * VEC);
+        T tmp[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) tmp[j] = vt[(size_t)((i * LPK + sub) * VEC + j) * a.slots + slot];
+        vv[u][i] = *(const u32x4*)tmp;
       }
     }
   };
@@ -353,9 +363,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
   if (has_self && a.write_kv && tid < HD) {
     // the slot of t held t - W (outside every window of this call) or nothing
     const int slot = a.is_full ? t : t % a.window;
-    const size_t o = (head_base + slot) * HD + tid;
-    ((T*)a.kc)[o] = selfk[tid];
-    ((T*)a.vc)[o] = selfv[tid];
+    ((T*)a.kc)[(head_base + slot) * HD + tid] = selfk[tid];
+    ((T*)a.vc)[(head_base * HD) + (size_t)tid * a.slots + slot] = selfv[tid];  // V^T [hd][slots]
   }
 
   // this lane's dims: chunks sub, sub + 8, ... of VEC elements
@@ -491,6 +500,248 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
 
 }
 
+// ---------------------------------------------------------------------------
+// Decode attention on the matrix cores (bfloat16). Keys are taken in tiles of
+// 32 positions; per tile a wave computes the scores as S^T = K . Q^T with
+// v_mfma_f32_16x16x32_bf16 (rows = 16 keys, columns = the G query heads padded
+// to 16, depth = head dims), so lane l ends up with the scores of head l%16
+// for keys 4*(l/16)+i of each 16-key half. Those probabilities are exactly
+// the B operand of O^T = V^T . P^T once the 32 keys are taken in the order
+// {4g..4g+3, 16+4g..16+4g+3} for lane group g, so the P.V product needs no
+// shuffles: the A operand reads the transposed cache values V^T[dim][keys]
+// (two 8-byte runs per lane). Online softmax runs per head column; the only
+// cross-lane steps are the 4-group max and sum (xor 16, 32).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int HD, int G>
+__global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
+  constexpr int NKK = HD / 32;        // depth steps of the score product
+  constexpr int NDD = HD / 16;        // 16-dim blocks of the output
+  constexpr int NI = (G + 2 + 3) / 4;  // setup items per wave (q heads, new key, new value)
+  constexpr float LOG2E = 1.4426950408889634f;
+
+  __shared__ __align__(16) bf16 qs[16][HD];
+  __shared__ __align__(16) bf16 selfk[HD];
+  __shared__ __align__(16) bf16 selfv[HD];
+  __shared__ float wm[4][16], wl[4][16];
+  __shared__ float wacc[4][G][HD];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
+  const int t = *a.t_dev;  // position of the new key (device counter: graph-replayable)
+  const int lo = a.is_full ? 0 : max(0, t - a.window + 1);
+  const int T_lo = lo >> 5, T_hi = t >> 5;
+  const int ntiles = T_hi - T_lo + 1;
+  const int tps = (ntiles + a.n_split - 1) / a.n_split;
+  const int tb = T_lo + split * tps;                 // this split's tiles [tb, te)
+  const int te = min(T_hi + 1, tb + tps);
+  const bool has_self = tb <= T_hi && T_hi < te;
+  const int half = HD / 2;
+
+  // (1) projection values for q heads / new key / new value (L2), clamped and
+  // unconditional so the waits stay exact
+  const float* row = a.qkvg + (size_t)b * a.ld;
+  const int ln = min(lane, half - 1);
+  float x1[NI], x2[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = min(wave + 4 * it, G + 1);
+    const float* src = item < G ? row + (size_t)(kvh * G + item) * HD
+                                : row + (size_t)a.nq * HD + (size_t)(item - G) * a.nkv * HD + (size_t)kvh * HD;
+    x1[it] = src[ln];
+    x2[it] = src[ln + half];
+  }
+  const float2 cs = a.tab[(size_t)t * half + ln];
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
+
+  // (2) cache operands of the wave's first tile (HBM)
+  const bf16* kc = (const bf16*)a.kc;
+  const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * a.slots;  // V^T [hd][slots]
+  const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
+  auto slot_of = [&](int pos) { return a.is_full ? pos : pos % a.window; };
+  auto load = [&](int T, u32x4 (&ka)[2][NKK], u32x2_t (&va)[NDD][2]) {
+    const int p0 = T << 5;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = min(p0 + 16 * kb + c16, t);  // beyond t: any written slot, masked later
+      const bf16* kr = kc + (khead + slot_of(key)) * HD + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)(kr + kk * 32);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      // 4 consecutive positions, 4-aligned; runs past the last slot hold only
+      // positions > t (masked) and are clamped in bounds
+      const int g0 = p0 + 16 * h2 + 4 * g4;
+      const int s0 = min(a.is_full ? g0 : g0 % a.window, a.slots - 4);
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) va[dd][h2] = *(const u32x2_t*)(vt + (size_t)(16 * dd + c16) * a.slots + s0);
+    }
+  };
+  const int first = tb + wave;
+  u32x4 ka0[2][NKK];
+  u32x2_t va0[NDD][2];
+  if (first < te) load(first, ka0, va0);
+
+  // (3) RoPE at t, unit norm, bfloat16 storage of q and of the new key/value
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = wave + 4 * it;
+    const float y1 = lane < half ? x1[it] : 0.f, y2 = lane < half ? x2[it] : 0.f;
+    const float r1 = y1 * cs.x - y2 * cs.y;
+    const float r2 = y2 * cs.x + y1 * cs.y;
+    const float inv = inv_norm(wave_sum(r1 * r1 + r2 * r2));
+    const bool rot = item <= G;
+    const bf16 z1 = from_f<bf16>(rot ? r1 * inv : y1), z2 = from_f<bf16>(rot ? r2 * inv : y2);
+    if (lane < half && item < G + 2) {
+      if (item < G) {
+        qs[item][lane] = z1;
+        qs[item][lane + half] = z2;
+      } else if (has_self) {
+        bf16* dst = item == G ? selfk : selfv;
+        dst[lane] = z1;
+        dst[lane + half] = z2;
+      }
+    }
+  }
+  for (int e = tid; e < (16 - G) * HD; e += 256) qs[G + e / HD][e % HD] = 0;  // padded head columns
+  __syncthreads();
+  if (has_self && a.write_kv && tid < HD) {
+    // the slot of t held t - W (outside every window of this call) or nothing
+    const int slot = slot_of(t);
+    ((bf16*)a.kc)[(khead + slot) * HD + tid] = selfk[tid];
+    ((bf16*)a.vc)[(((size_t)b * a.nkv + kvh) * HD + tid) * a.slots + slot] = selfv[tid];
+  }
+
+  bf16x8_t qb[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qb[kk] = *(const bf16x8_t*)&qs[c16][kk * 32 + 8 * g4];
+
+  const float sl2 = a.scale * LOG2E;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[NDD];
+#pragma unroll
+  for (int dd = 0; dd < NDD; ++dd) acc[dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](int T, u32x4 (&ka)[2][NKK], u32x2_t (&va)[NDD][2]) {
+    const int p0 = T << 5;
+    const bool edge = p0 < lo || p0 + 31 >= t;  // wave-uniform: needs masks or the new key
+    // key of k-slot j of this lane: j < 4 -> p0 + 4*g4 + j, else p0 + 16 + 4*g4 + j - 4
+    if (edge) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (p0 + 16 * kb + c16 == t) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)&selfk[kk * 32 + 8 * g4];
+        }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = p0 + 16 * h2 + 4 * g4 + j;
+          const bool valid = key >= lo && key <= t;
+#pragma unroll
+          for (int dd = 0; dd < NDD; ++dd) {
+            uint32_t w = va[dd][h2][j >> 1];
+            const uint32_t sh = (j & 1) * 16;
+            uint32_t v = (w >> sh) & 0xffffu;
+            v = key == t ? (uint32_t)selfv[16 * dd + c16] : (valid ? v : 0u);
+            va[dd][h2][j >> 1] = (w & ~(0xffffu << sh)) | (v << sh);
+          }
+        }
+    }
+    // scores S^T[key][head] for both 16-key halves
+    f32x4_t sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(bf16x8_t*)&ka[kb][kk], qb[kk], sc[kb], 0, 0, 0);
+    }
+    float v8[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = p0 + 16 * kb + 4 * g4 + i;
+        const bool valid = !edge || (key >= lo && key <= t);
+        const float v = valid ? sc[kb][i] * sl2 : -INFINITY;
+        v8[kb * 4 + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    float ps = 0.f;
+    bf16x8_t pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = v8[j] == -INFINITY ? 0.f : exp2f(v8[j] - mn);
+      ps += p;
+      const bf16 pbits = from_f<bf16>(p);
+      pb[j] = *(const __bf16*)&pbits;
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+      acc[dd] *= alpha;
+      const u32x4 vv = u32x4{va[dd][0][0], va[dd][0][1], va[dd][1][0], va[dd][1][1]};
+      acc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pb, acc[dd], 0, 0, 0);
+    }
+  };
+
+  for (int T = first; T < te; T += 4) {
+    if (T != first) load(T, ka0, va0);
+    process(T, ka0, va0);
+  }
+
+  // this wave's result: head c16, dims 16*dd + 4*g4 + i
+  if (c16 < G) {
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wacc[wave][c16][16 * dd + 4 * g4 + i] = acc[dd][i];
+    if (g4 == 0) {
+      wm[wave][c16] = m;
+      wl[wave][c16] = l;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * HD; e += 256) {
+    const int g = e / HD, d = e % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
+    float Ls = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (wm[w][g] == -INFINITY) continue;
+        const float f = exp2f(wm[w][g] - M);
+        Ls = fmaf(wl[w][g], f, Ls);
+        A = fmaf(wacc[w][g][d], f, A);
+      }
+    }
+    float* out = a.part + (((size_t)b * a.nq + kvh * G + g) * a.n_split + split) * (HD + 2);
+    out[2 + d] = A;
+    if (d == 0) {
+      out[0] = M;
+      out[1] = Ls;
+    }
+  }
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void k_attn_merge(const float* __restrict__ part, const float* __restrict__ qkvg,
                                                   int64_t ld, int gate_off, int gate, T* __restrict__ ob, int nq,
@@ -542,8 +793,30 @@ static hipError_t attn_dec_hd(const AttnDecArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int HD>
+static hipError_t attn_dec_mfma(const AttnDecArgs& a, hipStream_t st) {
+  dim3 grid(a.n_split, a.B * a.nkv);
+  switch (a.nq / a.nkv) {
+    case 1: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 6>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 8>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full) {
+  // 4-position runs of V^T must be contiguous and 8-byte aligned
+  return dtype == 1 && (hd == 64 || hd == 128) && slots % 4 == 0 && slots >= 4 && (is_full || window % 4 == 0);
+}
+
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
+  if (attn_decode_uses_mfma(dtype, a.hd, a.slots, a.window, a.is_full))
+    return a.hd == 64 ? attn_dec_mfma<64>(a, st) : attn_dec_mfma<128>(a, st);
   if (dtype == 0) {
     if (a.hd == 64) return attn_dec_hd<float, 64>(a, st);
     if (a.hd == 128) return attn_dec_hd<float, 128>(a, st);

@@ -21,24 +21,26 @@ enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
 
 __device__ __forceinline__ float silu_(float v) { return v / (1.0f + expf(-v)); }
 
-__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const bf16*) {
-  float s = bf_lo(w.x) * bf_lo(x.x);
-  s = fmaf(bf_hi(w.x), bf_hi(x.x), s);
-  s = fmaf(bf_lo(w.y), bf_lo(x.y), s);
-  s = fmaf(bf_hi(w.y), bf_hi(x.y), s);
-  s = fmaf(bf_lo(w.z), bf_lo(x.z), s);
-  s = fmaf(bf_hi(w.z), bf_hi(x.z), s);
-  s = fmaf(bf_lo(w.w), bf_lo(x.w), s);
-  s = fmaf(bf_hi(w.w), bf_hi(x.w), s);
-  return s;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  // v_dot2c_f32_bf16: c + a.lo * b.lo + a.hi * b.hi in float32, no unpacking
+  return __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2_t*)&a, *(const bf16x2_t*)&b, c, false);
 }
 
-__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const float*) {
-  float s = __uint_as_float(w.x) * __uint_as_float(x.x);
-  s = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), s);
-  s = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), s);
-  s = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), s);
-  return s;
+// acc + <w, x> over 8 bfloat16 pairs
+__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const bf16*, float acc) {
+  acc = dot2bf(w.x, x.x, acc);
+  acc = dot2bf(w.y, x.y, acc);
+  acc = dot2bf(w.z, x.z, acc);
+  return dot2bf(w.w, x.w, acc);
+}
+
+__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const float*, float acc) {
+  acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+  acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+  acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+  return fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64
       if (m < M) {
         const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
 #pragma unroll
-        for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j], xv, (const T*)nullptr);
+        for (int j = 0; j < NR; ++j) acc[m][j] = dot16(wv[j], xv, (const T*)nullptr, acc[m][j]);
       }
     }
   }
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
         if (m < M) {
           const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
 #pragma unroll
-          for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j][c], xv, (const bf16*)nullptr);
+          for (int j = 0; j < NR; ++j) acc[m][j] = dot16(wv[j][c], xv, (const bf16*)nullptr, acc[m][j]);
         }
       }
     }
@@ -204,79 +206,93 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
 }
 
 // k_gemv_rows with the residual update in the prologue (see launch_linear_pro).
+// 1024-thread workgroups (16 waves) with kProOut outputs per wave: the
+// 36-layer shape's q|k|v|gate and up/gate projections become 256 workgroups,
+// one per CU, all resident at once, and the prologue runs once per CU. Each
+// wave streams the chunks of its rows through a rolling window of kProWin
+// 16-byte loads per lane: a CU keeps ~16 x kProWin KB in flight (enough to
+// cover HBM latency at its share of the bandwidth) with few registers.
+constexpr int kProThreads = 1024;
+constexpr int kProOut = 2;  // outputs per wave
+constexpr int kProWin = 8;  // chunk loads in flight per wave
+
 template <int MB, int CH, int EPI>
-__global__ __launch_bounds__(512) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W, void* __restrict__ y,
-                                                 int M, int N, int K, float scale) {
-  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
-  __shared__ float sh[8];
+__global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W,
+                                                      void* __restrict__ y, int M, int N, int K, float scale) {
+  constexpr int R = kProOut;
+  constexpr int NR = (EPI == EPI_SWIGLU ? 2 : 1) * R;  // weight rows per wave
+  constexpr int NC = NR * CH;                          // chunk loads per wave
+  constexpr int P = NC < kProWin ? NC : kProWin;
+  constexpr int NW = kProThreads / 64;
+  constexpr int EPT = (CH * 512 + kProThreads - 1) / kProThreads;  // prologue elements per thread
+  __shared__ float sh[NW];
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nv = K / 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const int o = blockIdx.x * 8 + wave;
-  const bool live = o < nout;
-  const int oc = live ? o : nout - 1;
+  const int o0 = (blockIdx.x * NW + wave) * R;  // outputs o0 .. o0+R-1
+  const bool live = o0 < nout;
+
+  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU
+  auto chunk_ptr = [&](int c) -> const u32x4* {
+    const int j = c / CH, cc = c % CH;
+    const int oc = min(o0 + j % R, nout - 1);
+    const int v = min(lane + 64 * cc, nv - 1);  // clamped: chunks past the row are ignored below
+    return (const u32x4*)(W + (size_t)(j >= R ? nout + oc : oc) * K) + v;
+  };
 
   // prologue inputs of row 0 first (vector loads complete in issue order),
-  // then the weights; element i = threadIdx.x + 512*c (CH*512 >= K)
-  constexpr int EPT = CH;
-  // e is read unconditionally (from y when there is no re-injection) so that
-  // no branch separates these loads
+  // then the first P weight chunks; element i = threadIdx.x + kProThreads*c.
+  // e is read from y when there is no re-injection so no branch separates loads.
   const float* ep = pr.e ? pr.e : pr.y;
-  float yv[EPT], hv[EPT], av[EPT], ev[EPT];
+  float yv[EPT], hv[EPT], ev[EPT];
 #pragma unroll
   for (int c = 0; c < EPT; ++c) {
-    const int i = min((int)threadIdx.x + 512 * c, K - 1);
-    const bool in = threadIdx.x + 512 * c < K;
-    const float y0 = pr.y[i], h0 = pr.h_in[i], a0 = pr.alpha[i], e0 = ep[i];
-    yv[c] = in ? y0 : 0.f;
-    hv[c] = in ? h0 : 0.f;
-    av[c] = in ? a0 : 0.f;
-    ev[c] = in ? e0 : 0.f;
+    const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
+    yv[c] = pr.y[i];
+    hv[c] = pr.h_in[i];
+    ev[c] = ep[i];
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
-  u32x4 wv[NR][CH];
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 buf[P];
 #pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    const u32x4* wr = (const u32x4*)(W + (size_t)(j ? nout + oc : oc) * K);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      // clamped, unconditional: straight-line loads keep exact wait counts;
-      // chunks past the row are ignored in the product below
-      const int v = min(lane + 64 * c, nv - 1);
-      wv[j][c] = __builtin_nontemporal_load(wr + v);
-    }
-  }
+  for (int c = 0; c < P; ++c) buf[c] = __builtin_nontemporal_load(chunk_ptr(c));
+  __builtin_amdgcn_sched_barrier(0);
 
   for (int m = 0; m < M; ++m) {
     const size_t ro = (size_t)m * K;
     if (m > 0) {
 #pragma unroll
       for (int c = 0; c < EPT; ++c) {
-        const int i = threadIdx.x + 512 * c;
-        yv[c] = i < K ? pr.y[ro + i] : 0.f;
-        hv[c] = i < K ? pr.h_in[ro + i] : 0.f;
-        ev[c] = i < K ? ep[ro + i] : 0.f;
+        const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
+        yv[c] = pr.y[ro + i];
+        hv[c] = pr.h_in[ro + i];
+        ev[c] = ep[ro + i];
       }
     }
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < EPT; ++c) ss += yv[c] * yv[c];
-    const float iy = inv_norm(block_sum<512>(ss, sh));
+    for (int c = 0; c < EPT; ++c) {
+      if ((int)threadIdx.x + kProThreads * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
+      ss += yv[c] * yv[c];
+    }
+    const float iy = inv_norm(block_sum<kProThreads>(ss, sh));
     float st = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      hv[c] = hv[c] + av[c] * (yv[c] * iy - hv[c]);
+      const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
+      const float al = (int)threadIdx.x + kProThreads * c < K ? pr.alpha[i] : 0.f;
+      hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
       st += hv[c] * hv[c];
     }
-    const float ih = inv_norm(block_sum<512>(st, sh));
+    const float ih = inv_norm(block_sum<kProThreads>(st, sh));
 #pragma unroll
     for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
     if (pr.e_out && blockIdx.x == 0) {
 #pragma unroll
       for (int c = 0; c < EPT; ++c) {
-        const int i = threadIdx.x + 512 * c;
+        const int i = threadIdx.x + kProThreads * c;
         if (i < K) pr.e_out[ro + i] = hv[c];
       }
     }
@@ -284,17 +300,16 @@ __global__ __launch_bounds__(512) void k_gemv_pro(GemvPro pr, const bf16* __rest
       float sv = 0.f;
 #pragma unroll
       for (int c = 0; c < EPT; ++c) {
-        const int i = threadIdx.x + 512 * c;
-        yv[c] = i < K ? pr.wh * hv[c] + pr.we * ev[c] : 0.f;
+        yv[c] = pr.wh * hv[c] + pr.we * ev[c];
         sv += yv[c] * yv[c];
       }
-      const float iv = inv_norm(block_sum<512>(sv, sh));
+      const float iv = inv_norm(block_sum<kProThreads>(sv, sh));
 #pragma unroll
       for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
     }
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      const int i = threadIdx.x + 512 * c;
+      const int i = threadIdx.x + kProThreads * c;
       if (i < K) {
         xs[ro + i] = from_f<bf16>(hv[c]);
         if (blockIdx.x == 0) pr.h_out[ro + i] = hv[c];
@@ -310,15 +325,16 @@ __global__ __launch_bounds__(512) void k_gemv_pro(GemvPro pr, const bf16* __rest
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int v = lane + 64 * c;
-    if (v < nv) {
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 w = buf[c % P];
+    if (c + P < NC) buf[c % P] = __builtin_nontemporal_load(chunk_ptr(c + P));
+    const int j = c / CH, cc = c % CH;
+    if (lane + 64 * cc < nv) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (m < M) {
-          const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[v];
-#pragma unroll
-          for (int j = 0; j < NR; ++j) acc[m][j] += dot16(wv[j][c], xv, (const bf16*)nullptr);
+          const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[lane + 64 * cc];
+          acc[m][j] = dot16(w, xv, (const bf16*)nullptr, acc[m][j]);
         }
       }
     }
@@ -326,12 +342,16 @@ __global__ __launch_bounds__(512) void k_gemv_pro(GemvPro pr, const bf16* __rest
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     if (m >= M) break;
-    const float s = wave_sum(acc[m][0]);
-    if (EPI == EPI_SWIGLU) {
-      const float g = wave_sum(acc[m][NR - 1]);
-      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
-    } else {
-      if (lane == 0) ((float*)y)[(size_t)m * N + o] = s * scale;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int o = o0 + r;
+      const float s = wave_sum(acc[m][r]);
+      if (EPI == EPI_SWIGLU) {
+        const float g = wave_sum(acc[m][R + r]);
+        if (lane == 0 && o < nout) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
+      } else {
+        if (lane == 0 && o < nout) ((float*)y)[(size_t)m * N + o] = s * scale;
+      }
     }
   }
 }
@@ -341,16 +361,23 @@ static hipError_t gemv_pro_launch(const GemvPro& p, const bf16* W, void* y, int 
                                   hipStream_t st) {
   const int ch = (K / 8 + 63) / 64;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const dim3 grid((nout + 7) / 8);
+  const int per_block = kProThreads / 64 * kProOut;
+  const dim3 grid((nout + per_block - 1) / per_block);
   const size_t lds = (size_t)M * K * 2;
 #define DORY_PRO(C) \
-  case C: hipLaunchKernelGGL((k_gemv_pro<MB, C, EPI>), grid, dim3(512), lds, st, p, W, y, M, N, K, scale); break;
+  case C: hipLaunchKernelGGL((k_gemv_pro<MB, C, EPI>), grid, dim3(kProThreads), lds, st, p, W, y, M, N, K, scale); break;
   switch (ch) {
-    DORY_PRO(4) DORY_PRO(5) DORY_PRO(6) DORY_PRO(8) DORY_PRO(12) DORY_PRO(16)
+    DORY_PRO(1) DORY_PRO(2) DORY_PRO(3) DORY_PRO(4) DORY_PRO(5) DORY_PRO(6) DORY_PRO(7) DORY_PRO(8)
+    DORY_PRO(12) DORY_PRO(16)
     default: return hipErrorInvalidValue;
   }
 #undef DORY_PRO
   return hipGetLastError();
+}
+
+bool linear_pro_supported(int M, int K) {
+  const int ch = (K / 8 + 63) / 64;
+  return M >= 1 && M <= 8 && K % 8 == 0 && (size_t)M * K * 2 <= 64 * 1024 && (ch <= 8 || ch == 12 || ch == 16);
 }
 
 hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, int N, int K, int epi, float scale,

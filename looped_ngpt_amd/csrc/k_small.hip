@@ -226,7 +226,14 @@ __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
     dst = (T*)(isk ? a.k_out : a.v_out) + ((size_t)r * a.nkv + kvh) * a.hd;
     if (a.kc) {
       const int slot = a.is_full ? pos : pos % a.window;
-      cdst = (T*)(isk ? a.kc : a.vc) + (((size_t)b * a.nkv + kvh) * a.slots + slot) * a.hd;
+      if (isk) {
+        cdst = (T*)a.kc + (((size_t)b * a.nkv + kvh) * a.slots + slot) * a.hd;
+      } else {
+        // V is stored transposed per head: [hd][slots]
+        T* vt = (T*)a.vc + ((size_t)b * a.nkv + kvh) * a.hd * a.slots + slot;
+        vt[(size_t)lane * a.slots] = from_f<T>(x1);
+        vt[(size_t)(lane + half) * a.slots] = from_f<T>(x2);
+      }
     }
   }
   const T y1 = from_f<T>(x1), y2 = from_f<T>(x2);
@@ -268,7 +275,10 @@ __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, cons
     const int x = isk ? e : e - kvd;
     const int kvh = x / hd, c = x % hd;
     const T val = (isk ? kw : vw)[(size_t)r * kvd + x];
-    (isk ? kc : vc)[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
+    if (isk)
+      kc[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
+    else  // V transposed per head: [hd][slots]
+      vc[(((size_t)b * nkv + kvh) * hd + c) * slots + slot] = val;
   }
 }
 
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(256) void k_argmax_part(const float* __restrict__ l
 }
 
 __global__ __launch_bounds__(256) void k_argmax_final(const float2* __restrict__ part, int nblk,
-                                                     int32_t* __restrict__ out) {
+                                                     int32_t* __restrict__ out, int* __restrict__ pos_dev) {
   const int b = blockIdx.x;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -340,13 +350,22 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float2* __restrict__
   }
   block_argmax(bv, bi);
   if (threadIdx.x == 0) out[b] = bi == 0x7fffffff ? 0 : bi;
+  if (pos_dev && b == 0 && threadIdx.x == 0) pos_dev[0] += 1;  // this step's position is done
 }
 
-hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st) {
+__global__ void k_set_pos(int* pos_dev, int value) { pos_dev[0] = value; }
+
+hipError_t launch_set_pos(int* pos_dev, int value, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_pos, dim3(1), dim3(1), 0, st, pos_dev, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st,
+                         int* pos_dev) {
   if (B <= 0) return hipSuccess;
   const int nblk = (V + kArgBlock - 1) / kArgBlock;
   hipLaunchKernelGGL(k_argmax_part, dim3(nblk, B), dim3(256), 0, st, logits, V, nblk, (float2*)scratch);
-  hipLaunchKernelGGL(k_argmax_final, dim3(B), dim3(256), 0, st, (const float2*)scratch, nblk, out);
+  hipLaunchKernelGGL(k_argmax_final, dim3(B), dim3(256), 0, st, (const float2*)scratch, nblk, out, pos_dev);
   return hipGetLastError();
 }
 

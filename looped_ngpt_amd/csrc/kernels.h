@@ -64,21 +64,29 @@ hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, 
 // workgroup whose split holds t also builds the new key/value (and writes
 // them to the cache slot of t when write_kv). Keys s < t come from the cache.
 // Writes partials (m in log2 units, l, acc[hd]) per (b, q head, split).
+// The position t of the new key is read from t_dev, so one recorded graph
+// serves every step; n_split is fixed by capacity and the kernel spreads the
+// actual key range over it (trailing splits may be empty).
 struct AttnDecArgs {
   const float* qkvg; int64_t ld;
   const float2* tab;
-  int t, B, nq, nkv, hd, slots, window, is_full, write_kv, n_split;
+  const int* t_dev;
+  int B, nq, nkv, hd, slots, window, is_full, write_kv, n_split;
   float scale;
   void* kc; void* vc;
   float* part;
 };
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st);
+// True when launch_attn_decode takes the matrix-core kernel, which splits the
+// keys in tiles of 32 positions (bfloat16, slots and window multiples of 4).
+bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full);
 
 // Merges the decode partials (log2 units), applies the sigmoid gate (gate 1
 // elementwise, 2 per head, 0 none; read at gate_off of the projection row),
 // stores the gated heads in ob [B][nq*hd]. One workgroup per (q head, row).
-// (A last-workgroup merge inside the attention kernel needs device-scope
-// fences, which cost far more than this launch on gfx950.)
+// (Merging inside the attention kernel by its last workgroup measured slower
+// on gfx950 than this separate launch, both with device-scope fences and with
+// coherent stores and loads of the partials.)
 hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off, int gate,
                              void* ob, int B, int nq, int hd, int n_split, hipStream_t st);
 
@@ -100,7 +108,14 @@ struct GemvPro {
 };
 hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, int N, int K, int epi, float scale,
                              hipStream_t st);
+bool linear_pro_supported(int M, int K);
 
-hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st);
+// Greedy argmax; if pos_dev is not NULL the final pass also advances the
+// device position counter by one (the end of a decode step).
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st,
+                         int* pos_dev = nullptr);
+
+// *pos_dev = value (one thread).
+hipError_t launch_set_pos(int* pos_dev, int value, hipStream_t st);
 
 }  // namespace dory

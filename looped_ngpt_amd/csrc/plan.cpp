@@ -127,6 +127,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.next = take((size_t)c.max_batch * 4);
   w.amax = take(argmax_partials(c.max_batch, c.vocab) * 8);
   w.flags = take(256);
+  w.pos = take(4);
   w.total = at;
   return w;
 }

@@ -33,6 +33,7 @@ struct WsLayout {
   size_t next = 0;                     // [max_batch] int32
   size_t amax = 0;                     // argmax partials
   size_t flags = 0;                    // device error flags
+  size_t pos = 0;                      // int: position counter read by decode kernels
   size_t total = 0;
 };
 

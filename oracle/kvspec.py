@@ -15,8 +15,10 @@ min(W, max_ctx) slots with slot = pos mod W.
 
 Buffer layout: caches are numbered layer by layer; a recurrent layer in
 per-loop mode owns `kv_loops` consecutive ids (loop j -> base + j - 1).
-Cache c occupies [K: batch x n_kv x slots_c x hd][V: same], in id order, with
-no padding. Offsets below are in elements of the cache dtype.
+Cache c occupies [K: batch x n_kv x slots_c x hd][V: batch x n_kv x hd x
+slots_c] in id order with no padding: V is stored transposed per head (keys
+contiguous for each dimension). Offsets below are in elements of the cache
+dtype.
 
 Pinned by tests/test_oracle_kv.py: the footprint the oracle actually touches,
 the pages' "independent of k" / "grows with k" statements, and closed forms.
@@ -79,11 +81,19 @@ def kv_bytes(cfg: ModelConfig, kv_mode: str, kv_loops: int, max_ctx: int, batch:
 
 def element_offset(cfg: ModelConfig, kv_mode: str, kv_loops: int, max_ctx: int, batch: int,
                    layer: int, loop: int, which: str, b: int, kvh: int, pos: int) -> int:
-    """Offset (elements) of element 0 of the head vector K or V of (b, kvh, pos)."""
+    """Offset (elements) of dimension 0 of K or V of (b, kvh, pos); dimension
+    d is at + d * dim_stride(...)."""
     cid = cache_id(cfg, kv_mode, kv_loops, layer, loop)
     lays = cache_layers(cfg, kv_mode, kv_loops)
     start = sum(cache_elems(cfg, max_ctx, batch, l) for l in lays[:cid])
     ns = slots(cfg, max_ctx, layer)
     half = batch * cfg.n_kv_heads * ns * cfg.head_dim
-    off = start + (half if which == "V" else 0)
-    return off + ((b * cfg.n_kv_heads + kvh) * ns + slot(cfg, max_ctx, layer, pos)) * cfg.head_dim
+    sl = slot(cfg, max_ctx, layer, pos)
+    if which == "V":
+        return start + half + (b * cfg.n_kv_heads + kvh) * cfg.head_dim * ns + sl
+    return start + ((b * cfg.n_kv_heads + kvh) * ns + sl) * cfg.head_dim
+
+
+def dim_stride(cfg: ModelConfig, max_ctx: int, layer: int, which: str) -> int:
+    """Distance (elements) between consecutive dimensions of one K or V vector."""
+    return slots(cfg, max_ctx, layer) if which == "V" else 1

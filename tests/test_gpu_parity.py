@@ -35,6 +35,8 @@ def model_and_weights(name):
             m = scaled_config(get_config("c36"), n_in=2, n_rec=2, n_out=2)
         elif name == "c72w":          # the 72-layer model's widths, 1/3/1 layers (layer 3 full)
             m = scaled_config(get_config("c72"), n_in=1, n_rec=3, n_out=1)
+        elif name == "tiny_bf16":     # the tiny shape in bfloat16 (64-key window, matrix-core decode)
+            m = get_config("tiny").replace(dtype="bf16", d_ff=688, name="tiny_bf16")
         else:
             raise KeyError(name)
         w = make_weights(m)
@@ -125,12 +127,14 @@ def test_tiny_kv_placement_bit_exact():
             live = range(ctx) if m.layer_is_full[l] else range(max(0, ctx - m.window), ctx)
             for p in live:
                 for which in "KV":
+                    st = kvspec.dim_stride(m, T, l, which)
                     for h in range(nkv):
                         off = kvspec.element_offset(m, "per_loop", k, T, 1, l, j, which, 0, h, p)
-                        got = kv[off:off + hd]
+                        idx = off + st * np.arange(hd)
+                        got = kv[idx]
                         ref = ora.cache[key][which][0, h, p]
                         np.testing.assert_allclose(got, ref, atol=2e-5, err_msg=f"L{l} loop{j} {which} pos{p}")
-                        written[off:off + hd] = True
+                        written[idx] = True
     # everything else (the full layers' slots >= ctx; the rings are all live
     # since ctx > W) still holds the sentinel
     assert np.all(kv[~written].view(np.uint32) == 0x7FC00001)
@@ -172,18 +176,64 @@ def test_state_errors_on_gpu():
 # ---------------------------------------------------------------------------
 # bfloat16 at the 4B-shaped widths (fewer layers so the oracle finishes)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name,k,mode,n,steps", [("c36w", 2, "last_loop", 64, 12),
-                                                 ("c36w", 2, "per_loop", 40, 8),
-                                                 ("c72w", 3, "per_loop", 33, 8)])
-def test_bf16_widths(name, k, mode, n, steps):
+@pytest.mark.parametrize("name,k,mode,n,steps,ctx", [("c36w", 2, "last_loop", 64, 12, 96),
+                                                     ("c36w", 2, "per_loop", 40, 8, 77),
+                                                     ("c72w", 3, "per_loop", 33, 8, 64),
+                                                     ("tiny_bf16", 2, "last_loop", 150, 24, 192),
+                                                     ("tiny_bf16", 3, "per_loop", 97, 20, 160)])
+def test_bf16_widths(name, k, mode, n, steps, ctx):
+    """ctx = max_ctx: multiples of 4 take the matrix-core decode attention,
+    77 the vector fallback; the tiny shape's 64-key rings wrap."""
     m, w, dw = model_and_weights(name)
     prompt = make_tokens(m, 6, (1, n))
-    ora = LoopedNGPT(m, w, max_ctx=n + steps + 1)
+    ora = LoopedNGPT(m, w, max_ctx=ctx)
     o_tok, o_log = ora.generate(prompt, steps, k, mode)
     margins = np.sort(o_log, axis=-1)
     print(f"{name}: min top1-top2 margin {np.min(margins[..., -1] - margins[..., -2]):.3e}", flush=True)
-    s = session(m, dw, batch=1, max_ctx=n + steps + 1, chunk=n, kv_mode=mode, k=k)
+    s = session(m, dw, batch=1, max_ctx=ctx, chunk=n, kv_mode=mode, k=k)
     g_tok, g_log, lib_next = generate(s, prompt, steps, k)
     assert _report(f"{name} {mode} k={k}", g_log, o_log) <= BF16_TOL
     np.testing.assert_array_equal(g_tok, o_tok)
     np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
+
+
+# ---------------------------------------------------------------------------
+# recorded decode steps: continued greedy decoding of a bfloat16 model is
+# recorded once per (loop count, batch) and replayed; each replay must equal
+# the same step launched kernel by kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
+def test_bf16_decode_graph_replays_match_eager(mode):
+    """Bit-identical logits and tokens at every replay, with eager torch work
+    and synchronisations between replays, loop counts switching between
+    recordings (last-loop mode), and a second sequence after a reset that
+    reuses the recordings (its position comes from the device counter)."""
+    m, w, dw = model_and_weights("tiny_bf16")
+    B, ctx = 2, 192
+    sched = [2, 2, 3, 1, 3, 2, 2, 1, 3, 3] if mode == "last_loop" else [3] * 10
+    runs = []
+    for graphs in (False, True):
+        s = session(m, dw, batch=B, max_ctx=ctx, chunk=64, kv_mode=mode, k=3)
+        s.set_graphs(graphs)
+        out = []
+        for seq in range(2):
+            k0 = 2 if mode == "last_loop" else 3
+            prompt = torch.from_numpy(make_tokens(m, 10 + seq, (B, 70 + 9 * seq))).cuda()
+            print(f"graphs={graphs} {mode} seq {seq}", flush=True)
+            s.prefill(prompt, k0)
+            for k in sched:
+                nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+                s.decode(None, k, next_tokens=nxt)
+                lg = s.logits()
+                junk = torch.randn(4096, device="cuda").sum()      # unrelated eager work between replays
+                torch.cuda.synchronize()
+                assert torch.isfinite(junk)
+                out.append((lg.cpu().numpy(), nxt.cpu().numpy()))
+            s.reset()
+        runs.append(out)
+    for i, ((la, ta), (lb, tb)) in enumerate(zip(*runs)):
+        np.testing.assert_array_equal(ta, tb, err_msg=f"step {i}")
+        np.testing.assert_array_equal(la, lb, err_msg=f"step {i}")
+    # the greedy tokens are the argmax of the logits they follow
+    for (la, ta) in runs[1]:
+        np.testing.assert_array_equal(np.argmax(la, axis=-1), ta)

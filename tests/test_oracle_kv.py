@@ -76,18 +76,21 @@ def test_slot_spec_ring_and_ids():
 
 
 def test_element_offsets_tile_the_buffer():
-    """Every (cache, K/V, b, head, slot) vector has its own place, and the
-    places exactly cover kv_bytes."""
+    """Every element of every (cache, K/V, b, head, slot) vector has its own
+    place, and the places exactly cover kv_bytes."""
     cfg = micro()
     B, T, kl = 2, 10, 2
-    seen = set()
+    seen = []
     for l in range(cfg.n_layers):
         loops = range(1, kl + 1) if cfg.is_recurrent(l) else [0]
         for j in loops:
             for which in "KV":
+                st = kvspec.dim_stride(cfg, T, l, which)
                 for b in range(B):
                     for h in range(cfg.n_kv_heads):
                         for p in range(kvspec.slots(cfg, T, l)):
-                            seen.add(kvspec.element_offset(cfg, PER_LOOP, kl, T, B, l, j, which, b, h, p))
-    assert len(seen) * cfg.head_dim * 4 == kvspec.kv_bytes(cfg, PER_LOOP, kl, T, B)
-    assert min(seen) == 0 and max(seen) == (len(seen) - 1) * cfg.head_dim
+                            o = kvspec.element_offset(cfg, PER_LOOP, kl, T, B, l, j, which, b, h, p)
+                            seen += [o + d * st for d in range(cfg.head_dim)]
+    assert len(seen) == len(set(seen))
+    assert len(seen) * 4 == kvspec.kv_bytes(cfg, PER_LOOP, kl, T, B)
+    assert sorted(seen) == list(range(len(seen)))
