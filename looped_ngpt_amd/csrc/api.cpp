@@ -145,6 +145,7 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
     ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
     ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
+    ra.vld = chunk_vld(n);
     ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
     ra.kc = nullptr; ra.vc = nullptr;
     ra.slots = slots; ra.window = C.window; ra.is_full = full;
@@ -155,18 +156,25 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     aa.B = B; aa.n = n; aa.p0 = c->pos; aa.nq = C.n_q_heads; aa.nkv = C.n_kv_heads; aa.hd = C.head_dim;
     aa.slots = slots; aa.window = C.window; aa.is_full = full;
     aa.n_split = 1;
+    aa.vld = ra.vld;
     aa.scale = P.attn_scale;
     aa.part = wsp<float>(c, W.part);
-    {
+    const int gate_off = P.q_dim + 2 * P.kv_dim;
+    if (attn_prefill_supported(dt, C.head_dim, C.n_q_heads, C.n_kv_heads)) {
       TimeScope ts(c, TIME_ATTN);
-      HIP_TRY(c, launch_attn_split(dt, aa, st));
+      HIP_TRY(c, launch_attn_prefill(aa, qkvg, P.qkvg_dim, gate_off, C.attn_gate, c->ws + W.ob, st));
+    } else {
+      {
+        TimeScope ts(c, TIME_ATTN);
+        HIP_TRY(c, launch_attn_split(dt, aa, st));
+      }
+      HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, gate_off, C.attn_gate, c->ws + W.ob, rows,
+                                     C.n_q_heads, C.head_dim, aa.n_split, st));
     }
-    HIP_TRY(c, launch_attn_combine(dt, aa.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
-                                   c->ws + W.ob, rows, C.n_q_heads, C.head_dim, aa.n_split, st));
     // after attention: the ring slots of this call's positions held keys it needed
     if (write_kv)
-      HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, kc, vc, B, n, c->pos, C.n_kv_heads, C.head_dim,
-                                 slots, C.window, full, st));
+      HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, ra.vld, kc, vc, B, n, c->pos, C.n_kv_heads,
+                                 C.head_dim, slots, C.window, full, st));
   }
 
   {

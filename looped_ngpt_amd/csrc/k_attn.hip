@@ -72,32 +72,36 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     __syncthreads();  // previous tile fully consumed (and q staged on the first pass)
     for (int e = tid; e < TK * VPK; e += 256) {
       const int kk = e / VPK, c = e % VPK;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      uint4 kv4 = make_uint4(0, 0, 0, 0);
       const int s = s0 + kk;
-      const bool cached = kk < nk && s < a.p0;  // its values come from the loop below
       if (kk < nk) {
         if (s >= a.p0) {
           const size_t o = ((size_t)(b * a.n + (s - a.p0)) * a.nkv + kvh) * HD;
           kv4 = ((const uint4*)(kw + o))[c];
-          vv4 = ((const uint4*)(vw + o))[c];
         } else {
           const int slot = a.is_full ? s : s % a.window;
           kv4 = ((const uint4*)(kc + (((size_t)b * a.nkv + kvh) * a.slots + slot) * HD))[c];
         }
       }
       *(uint4*)(Ks + kk * KLD + c * VEC) = kv4;
-      if (!cached) *(uint4*)(Vs + kk * HD + c * VEC) = vv4;
     }
-    // cached values are stored transposed ([hd][slots]): consecutive threads
-    // take consecutive keys of one dimension
+    // values are stored transposed ([hd][slots] in the cache, [hd][vld] for
+    // this call): consecutive threads take consecutive keys of one dimension
     const size_t vhead = ((size_t)b * a.nkv + kvh) * HD * a.slots;
+    const size_t vchunk = ((size_t)b * a.nkv + kvh) * HD * a.vld;
     for (int e = tid; e < TK * HD; e += 256) {
       const int d = e / TK, kk = e % TK;
       const int s = s0 + kk;
-      if (kk < nk && s < a.p0) {
-        const int slot = a.is_full ? s : s % a.window;
-        Vs[kk * HD + d] = vc[vhead + (size_t)d * a.slots + slot];
+      T v = from_f<T>(0.f);
+      if (kk < nk) {
+        if (s < a.p0) {
+          const int slot = a.is_full ? s : s % a.window;
+          v = vc[vhead + (size_t)d * a.slots + slot];
+        } else {
+          v = vw[vchunk + (size_t)d * a.vld + (s - a.p0)];
+        }
       }
+      Vs[kk * HD + d] = v;
     }
     __syncthreads();
 

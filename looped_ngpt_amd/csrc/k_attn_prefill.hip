@@ -1,0 +1,291 @@
+// Prefill attention of the looped nGPT on the matrix cores (bfloat16, head
+// dim 64 or 128): softmax(scale * q.k) v over the allowed keys of a sliding
+// window (t - W < s <= t) or full (s <= t) layer, grouped-query heads, then
+// the sigmoid output gate — the attention sublayer of the nGPT block
+// ("Dory1.0-4B" model summary, Architecture; the nGPT paper, Section 2.3).
+//
+// One workgroup takes 128 consecutive query positions of one query head; its
+// four waves own 32 positions each. Keys are visited in tiles of 64 positions
+// staged in LDS, K as rows [key][hd] and V transposed [hd][key]; the global
+// loads of the next tile are issued before the current tile is multiplied.
+// Per wave and 32-key half tile (v_mfma_f32_32x32x16_bf16):
+//   S^T[key][query] = K . Q^T            hd/16 steps
+//   online softmax per query column      a lane owns one query; the lane
+//                                        32 apart holds the other key rows
+//   O^T[d][query]  += V^T . P^T          P in bfloat16, 2 steps x hd/32 blocks
+// so the running max, sum and rescale of a query stay inside its two lanes.
+// The key order inside a 16-key step is permuted the same way on both
+// operands (lane half g supplies keys 4g..4g+3 and 8+4g..8+4g+3), which lets
+// P^T come straight from the score registers.
+//
+// Workgroup ids are spread over the eight XCDs so that the G query heads that
+// share a kv head (and so the same K/V tiles, through that XCD's L2) run on
+// one XCD back to back, and the query blocks with the most keys start first.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kQB = 128;  // query positions per workgroup
+constexpr int kKT = 64;   // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float* __restrict__ qkvg, int64_t ld,
+                                                      int gate_off, int gate, bf16* __restrict__ ob) {
+  constexpr int CPK = HD / 8;          // 16-byte chunks per key row
+  constexpr int NL = HD / 32;          // K chunks (and V runs) per thread per tile
+  constexpr int KLD = HD + 8;          // K tile row, padded 16 B (conflict-free 16-byte reads)
+  constexpr int VLD = kKT + 4;         // V^T tile row, padded 8 B (conflict-free 8-byte reads)
+  constexpr int NKS = HD / 16;         // S steps
+  constexpr int NMB = HD / 32;         // O^T row blocks
+  __shared__ __align__(16) bf16 Ks[kKT * KLD];
+  __shared__ __align__(16) bf16 Vt[HD * VLD];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, g = lane >> 5;
+  const int G = a.nq / a.nkv;
+
+  // ---- work item: (query block, sequence, kv head) group, head inside the group
+  const int nqb = (a.n + kQB - 1) / kQB;
+  const int per_blk = a.B * a.nkv;
+  const int ngroups = nqb * per_blk;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int grp = (j / G) * 8 + xcd;
+  if (grp >= ngroups) return;
+  const int qb = nqb - 1 - grp / per_blk;  // most keys first
+  const int b = (grp % per_blk) / a.nkv, kvh = grp % a.nkv;
+  const int hq = kvh * G + j % G;
+
+  const int p0 = a.p0, n = a.n, W = a.window, full = a.is_full;
+  const int i_blk = qb * kQB;
+  const int lo_blk = full ? 0 : max(0, p0 + i_blk - W + 1);  // keys any query of the block may see
+  const int hi_blk = p0 + min(i_blk + kQB - 1, n - 1);
+
+  // ---- this wave's queries
+  const int iw0 = i_blk + 32 * wave;
+  const bool wave_live = iw0 < n;
+  const int ta = p0 + iw0, tb = p0 + min(iw0 + 31, n - 1);
+  const int wlo = full ? 0 : max(0, ta - W + 1);
+  const int iq = min(iw0 + lq, n - 1);  // clamped: rows past n are computed and dropped
+  const int t = p0 + iq;
+
+  const bf16* q = (const bf16*)a.q;
+  const bf16* kw = (const bf16*)a.kw;
+  const bf16* vw = (const bf16*)a.vw;
+  const bf16* kc = (const bf16*)a.kc;
+  const bf16* vc = (const bf16*)a.vc;
+
+  // Q^T operand: lane (query lq, half g) holds dims 16*ks + 8*g .. +7
+  bf16x8_t qf[NKS];
+  {
+    const bf16* qr = q + ((size_t)(b * n + iq) * a.nq + hq) * HD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qr + 16 * ks);
+  }
+
+  // ---- tile loader: unconditional 16-byte loads from clamped addresses (so
+  // the waits stay exact); what must read as zero, or needs a per-key gather,
+  // is decided again when the registers go to LDS
+  const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
+  const size_t vhead_c = ((size_t)b * a.nkv + kvh) * HD * a.slots;  // cache V^T rows
+  const size_t vhead_w = ((size_t)b * a.nkv + kvh) * HD * a.vld;    // this call's V^T rows
+  const bool vec_chunk = (p0 & 7) == 0;
+  const bool vec_cache = (a.slots & 7) == 0 && (full || (W & 7) == 0);
+  auto slot_of = [&](int s) { return full ? s : s % W; };
+  auto key_src = [&](int s) -> const bf16* {  // K row of key s (clamped into the block's range)
+    s = min(max(s, lo_blk), hi_blk);
+    return s >= p0 ? kw + ((size_t)(b * n + (s - p0)) * a.nkv + kvh) * HD : kc + (khead + slot_of(s)) * HD;
+  };
+  // V run mode: 0 = vector (one source, contiguous), 1 = zero, 2 = per-key gather
+  auto run_mode = [&](int s) -> int {
+    if (s + 7 < lo_blk || s > hi_blk) return 1;
+    if (s < lo_blk || s + 7 > hi_blk) return 2;
+    if (s >= p0) return vec_chunk ? 0 : 2;
+    if (s + 7 < p0) return (vec_cache && (full || slot_of(s) + 8 <= W)) ? 0 : 2;
+    return 2;
+  };
+  auto v_src = [&](int d, int s) -> const bf16* {  // vector path source (or any aligned address)
+    if (run_mode(s) != 0) return vc;
+    return s >= p0 ? vw + vhead_w + (size_t)d * a.vld + (s - p0) : vc + vhead_c + (size_t)d * a.slots + slot_of(s);
+  };
+  auto v_elem = [&](int d, int s) -> bf16 {  // one value of key s (zero outside the block's range)
+    if (s < lo_blk || s > hi_blk) return 0;
+    return s >= p0 ? vw[vhead_w + (size_t)d * a.vld + (s - p0)] : vc[vhead_c + (size_t)d * a.slots + slot_of(s)];
+  };
+
+  u32x4 kr[NL], vr[NL];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + 256 * i;
+      kr[i] = *(const u32x4*)(key_src(s0 + e / CPK) + 8 * (e % CPK));
+      vr[i] = *(const u32x4*)v_src(e >> 3, s0 + 8 * (e & 7));
+    }
+  };
+  auto stage = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + 256 * i;
+      const int kk = e / CPK, c = e % CPK;
+      const int s = s0 + kk;
+      u32x4 kv = kr[i];
+      if (s < lo_blk || s > hi_blk) kv = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(Ks + kk * KLD + 8 * c) = kv;
+      const int d = e >> 3, run = e & 7;
+      const int sv = s0 + 8 * run;
+      const int mode = run_mode(sv);
+      u32x4 vv = vr[i];
+      if (mode == 1) {
+        vv = u32x4{0u, 0u, 0u, 0u};
+      } else if (mode == 2) {
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2)
+          vv[w2] = (uint32_t)v_elem(d, sv + 2 * w2) | ((uint32_t)v_elem(d, sv + 2 * w2 + 1) << 16);
+      }
+      u32x2_t* dst = (u32x2_t*)(Vt + d * VLD + 8 * run);
+      dst[0] = u32x2_t{vv[0], vv[1]};
+      dst[1] = u32x2_t{vv[2], vv[3]};
+    }
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x16_t acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+
+  const int T0 = lo_blk / kKT, T1 = hi_blk / kKT;
+  fetch(T0 * kKT);
+  for (int T = T0; T <= T1; ++T) {
+    const int s0 = T * kKT;
+    __syncthreads();  // the previous tile is consumed
+    stage(s0);
+    __syncthreads();
+    fetch(min(s0 + kKT, T1 * kKT));  // in flight while this tile is multiplied (the last refetches itself)
+
+    if (!wave_live || s0 > tb || s0 + kKT - 1 < wlo) continue;  // no allowed key for this wave
+    // masks needed unless every key of the tile is allowed for every query of the wave
+    const bool edge = s0 + kKT - 1 > ta || (!full && s0 < tb - W + 1);
+
+    f32x16_t sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
+      const bf16* kr0 = Ks + (kt * 32 + lq) * KLD + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(kr0 + 16 * ks), qf[ks], sc[kt], 0, 0,
+                                                         0);
+    }
+    // register r of half tile kt holds key s0 + 32 kt + 8 (r / 4) + 4 g + r % 4
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = sc[kt][r] * sl2;
+        if (edge) {
+          const int key = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key <= t && (full || key > t - W);
+          v = ok ? v : -INFINITY;
+        }
+        sc[kt][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    m = mn;
+    float ps = 0.f;
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = sc[kt][r] == -INFINITY ? 0.f : exp2f(sc[kt][r] - mn);
+        const bf16 bits = from_f<bf16>(p);
+        ps += to_f(bits);
+        pb[kt][r >> 3][r & 7] = *(const __bf16*)&bits;
+      }
+    l = l * alpha + ps;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const bf16* vrow = Vt + (mb * 32 + lq) * VLD + 32 * kt + 16 * h + 4 * g;
+          const u32x2_t lo = *(const u32x2_t*)vrow;
+          const u32x2_t hi = *(const u32x2_t*)(vrow + 8);
+          const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)&va, pb[kt][h], acc[mb], 0, 0, 0);
+        }
+  }
+
+  // ---- normalise, gate, store: register r of block mb holds dim
+  // 32 mb + 8 (r / 4) + 4 g + r % 4 of query lq
+  if (!wave_live || iw0 + lq >= n) return;
+  const float lt = l + __shfl_xor(l, 32, 64);
+  const float inv = 1.0f / lt;
+  const int row = b * n + iq;
+  const float* gr = qkvg + (size_t)row * ld + gate_off;
+  bf16* dst = ob + ((size_t)row * a.nq + hq) * HD;
+  const float gh = gate == 2 ? sigmoidf_(gr[hq]) : 1.f;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * mb + 8 * rq + 4 * g;
+      float gv[4] = {gh, gh, gh, gh};
+      if (gate == 1) {
+        const float4 g4 = *(const float4*)(gr + hq * HD + d0);
+        gv[0] = sigmoidf_(g4.x);
+        gv[1] = sigmoidf_(g4.y);
+        gv[2] = sigmoidf_(g4.z);
+        gv[3] = sigmoidf_(g4.w);
+      }
+      const bf16 o0 = from_f<bf16>(acc[mb][4 * rq + 0] * inv * gv[0]);
+      const bf16 o1 = from_f<bf16>(acc[mb][4 * rq + 1] * inv * gv[1]);
+      const bf16 o2 = from_f<bf16>(acc[mb][4 * rq + 2] * inv * gv[2]);
+      const bf16 o3 = from_f<bf16>(acc[mb][4 * rq + 3] * inv * gv[3]);
+      *(u32x2_t*)(dst + d0) = u32x2_t{(uint32_t)o0 | ((uint32_t)o1 << 16), (uint32_t)o2 | ((uint32_t)o3 << 16)};
+    }
+}
+
+}  // namespace
+
+// dtype 1 = bfloat16
+bool attn_prefill_supported(int dtype, int hd, int nq, int nkv) {
+  return dtype == 1 && (hd == 64 || hd == 128) && nkv > 0 && nq % nkv == 0;
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, const float* qkvg, int64_t ld, int gate_off, int gate, void* ob,
+                               hipStream_t st) {
+  if (a.B * a.n <= 0) return hipSuccess;
+  if (!attn_prefill_supported(1, a.hd, a.nq, a.nkv)) return hipErrorInvalidValue;
+  if ((gate_off & 3) || (ld & 3)) return hipErrorInvalidValue;  // float4 gate reads
+  const int G = a.nq / a.nkv;
+  const int64_t ngroups = (int64_t)((a.n + kQB - 1) / kQB) * a.B * a.nkv;
+  const int64_t blocks = (ngroups + 7) / 8 * 8 * G;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.hd == 64)
+    hipLaunchKernelGGL(k_attn_prefill<64>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
+                       (bf16*)ob);
+  else
+    hipLaunchKernelGGL(k_attn_prefill<128>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
+                       (bf16*)ob);
+  return hipGetLastError();
+}
+
+}  // namespace dory

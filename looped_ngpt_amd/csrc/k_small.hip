@@ -223,7 +223,15 @@ __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
   } else {
     const bool isk = head < a.nq + a.nkv;
     const int kvh = isk ? head - a.nq : head - a.nq - a.nkv;
-    dst = (T*)(isk ? a.k_out : a.v_out) + ((size_t)r * a.nkv + kvh) * a.hd;
+    if (isk) {
+      dst = (T*)a.k_out + ((size_t)r * a.nkv + kvh) * a.hd;
+    } else {
+      // values of the call transposed per head: [hd][vld], position i at column i
+      T* vt = (T*)a.v_out + ((size_t)b * a.nkv + kvh) * a.hd * a.vld + i;
+      vt[(size_t)lane * a.vld] = from_f<T>(x1);
+      vt[(size_t)(lane + half) * a.vld] = from_f<T>(x2);
+      dst = nullptr;
+    }
     if (a.kc) {
       const int slot = a.is_full ? pos : pos % a.window;
       if (isk) {
@@ -237,8 +245,10 @@ __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
     }
   }
   const T y1 = from_f<T>(x1), y2 = from_f<T>(x2);
-  dst[lane] = y1;
-  dst[lane + half] = y2;
+  if (dst) {
+    dst[lane] = y1;
+    dst[lane + half] = y2;
+  }
   if (cdst) {
     cdst[lane] = y1;
     cdst[lane + half] = y2;
@@ -261,7 +271,7 @@ hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
 // ring contents). Block = one row; copies k and v of all kv heads.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, const T* __restrict__ vw,
+__global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, const T* __restrict__ vw, int vld,
                                                  T* __restrict__ kc, T* __restrict__ vc, int n, int p0, int nkv,
                                                  int hd, int slots, int window, int is_full) {
   const int r = blockIdx.x;
@@ -274,7 +284,7 @@ __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, cons
     const bool isk = e < kvd;
     const int x = isk ? e : e - kvd;
     const int kvh = x / hd, c = x % hd;
-    const T val = (isk ? kw : vw)[(size_t)r * kvd + x];
+    const T val = isk ? kw[(size_t)r * kvd + x] : vw[((size_t)b * kvd + x) * vld + i];
     if (isk)
       kc[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
     else  // V transposed per head: [hd][slots]
@@ -282,14 +292,14 @@ __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, cons
   }
 }
 
-hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, void* kc, void* vc, int B, int n, int p0,
-                           int nkv, int hd, int slots, int window, int is_full, hipStream_t st) {
+hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, int vld, void* kc, void* vc, int B, int n,
+                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st) {
   if (B * n <= 0) return hipSuccess;
   if (dtype == 0)
-    hipLaunchKernelGGL(k_kv_write<float>, dim3(B * n), dim3(256), 0, st, (const float*)kw, (const float*)vw,
+    hipLaunchKernelGGL(k_kv_write<float>, dim3(B * n), dim3(256), 0, st, (const float*)kw, (const float*)vw, vld,
                        (float*)kc, (float*)vc, n, p0, nkv, hd, slots, window, is_full);
   else
-    hipLaunchKernelGGL(k_kv_write<bf16>, dim3(B * n), dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw,
+    hipLaunchKernelGGL(k_kv_write<bf16>, dim3(B * n), dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw, vld,
                        (bf16*)kc, (bf16*)vc, n, p0, nkv, hd, slots, window, is_full);
   return hipGetLastError();
 }

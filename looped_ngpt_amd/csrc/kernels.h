@@ -24,34 +24,45 @@ hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipS
 
 // Rows r = b*n + i at position p0 + i. Reads q|k|v of the fused projection
 // (float32, row stride ld); writes RoPE'd, per-head unit q and k and plain v
-// in the model dtype to q_out [rows][nq][hd], k_out / v_out [rows][nkv][hd].
+// in the model dtype to q_out [rows][nq][hd], k_out [rows][nkv][hd] and,
+// transposed, v_out [B][nkv][hd][vld] (position i at column i).
 // If kc is not NULL also writes k, v to the cache slot of each position
 // (only valid when no other position of the same launch maps to that slot).
 struct RopeArgs {
   const float* qkvg; int64_t ld;
   const float2* tab;
-  int p0, n, rows, nq, nkv, hd;
+  int p0, n, rows, nq, nkv, hd, vld;
   void* q_out; void* k_out; void* v_out;
   void* kc; void* vc; int slots, window, is_full;
 };
 hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st);
 
-// Copies this call's K/V rows into the cache: every row of a full layer, the
-// last min(n, slots) rows of a sliding-window ring.
-hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, void* kc, void* vc, int B, int n,
+// Copies this call's keys and values (kw rows, vw transposed with row length
+// vld) into the cache: every position of a full layer, the last
+// min(n, slots) positions of a sliding-window ring.
+hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, int vld, void* kc, void* vc, int B, int n,
                            int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st);
 
 // Split-K softmax attention. For query row r = b*n + i (position p0 + i) and
 // query head hq (kv head hq / G) the allowed keys are s <= t (and t - s <
-// window for sliding layers); keys s >= p0 come from kw/vw, earlier ones from
-// the cache. Writes (m, l, acc[hd]) per (r, hq, split) to part.
+// window for sliding layers); keys s >= p0 come from kw / vw (vw transposed,
+// row length vld), earlier ones from the cache. Writes (m, l, acc[hd]) per
+// (r, hq, split) to part.
 struct AttnArgs {
   const void* q; const void* kw; const void* vw; const void* kc; const void* vc;
-  int B, n, p0, nq, nkv, hd, slots, window, is_full, n_split;
+  int B, n, p0, nq, nkv, hd, slots, window, is_full, n_split, vld;
   float scale;
   float* part;
 };
 hipError_t launch_attn_split(int dtype, const AttnArgs& a, hipStream_t st);
+
+// Prefill attention on the matrix cores (bfloat16, hd 64 or 128): the same
+// keys and softmax as launch_attn_split with one split, followed by what
+// launch_attn_combine does (normalise, sigmoid gate read at gate_off of the
+// projection rows, store ob [rows][nq*hd]) in one launch.
+hipError_t launch_attn_prefill(const AttnArgs& a, const float* qkvg, int64_t ld, int gate_off, int gate, void* ob,
+                               hipStream_t st);
+bool attn_prefill_supported(int dtype, int hd, int nq, int nkv);
 
 // Merges the splits, applies the sigmoid gate (gate 1: elementwise, 2: per
 // head, 0: none) read from the fused projection, stores ob [rows][nq*hd] (dtype).

@@ -116,7 +116,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.qkvg = take(R * p.qkvg_dim * 4);
   w.q = take(R * p.q_dim * el);
   w.kw = take(R * p.kv_dim * el);
-  w.vw = take(R * p.kv_dim * el);
+  w.vw = take((size_t)c.max_batch * chunk_vld(c.max_chunk) * p.kv_dim * el);  // V^T rows of chunk_vld(n)
   const size_t dec = (size_t)c.max_batch * c.n_q_heads * kMaxSplits;
   const size_t pre = R * c.n_q_heads;
   w.part = take((dec > pre ? dec : pre) * (c.head_dim + 2) * 4);

@@ -18,13 +18,17 @@ constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+// Row length of a call's transposed values [B][n_kv][hd][vld]: n rounded up
+// to 8 positions, so that every row starts 16-byte aligned.
+inline int chunk_vld(int n) { return (n + 7) / 8 * 8; }
 
 struct WsLayout {
   size_t rope_swa = 0, rope_full = 0;  // float2 [max_ctx][hd/2]
   size_t h = 0, e = 0, xb = 0;         // [rows, d]   f32, f32, dtype
   size_t hb = 0;                       // [max_batch, d] f32: second residual buffer (decode ping-pong)
   size_t qkvg = 0;                     // [rows, qkvg_dim] f32
-  size_t q = 0, kw = 0, vw = 0;        // [rows, n_q|n_kv, hd] dtype
+  size_t q = 0, kw = 0;                // [rows, n_q|n_kv, hd] dtype
+  size_t vw = 0;                       // [B, n_kv, hd, chunk_vld(n)] dtype (values transposed)
   size_t part = 0;                     // attention partials f32
   size_t ob = 0;                       // [rows, q_dim] dtype
   size_t y = 0;                        // [rows, d] f32

@@ -37,6 +37,12 @@ def model_and_weights(name):
             m = scaled_config(get_config("c72"), n_in=1, n_rec=3, n_out=1)
         elif name == "tiny_bf16":     # the tiny shape in bfloat16 (64-key window, matrix-core decode)
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, name="tiny_bf16")
+        elif name == "tiny_bf16_w60":  # a window that is not a multiple of 8 (per-key value gathers)
+            m = get_config("tiny").replace(dtype="bf16", d_ff=688, window=60, name="tiny_bf16_w60")
+        elif name == "c36w_w192":     # the c36w weights with 192-key rings that wrap
+            m0, w, dw = model_and_weights("c36w")
+            _cache[name] = (m0.replace(window=192, name="c36w_w192"), w, dw)
+            return _cache[name]
         else:
             raise KeyError(name)
         w = make_weights(m)
@@ -193,6 +199,29 @@ def test_bf16_widths(name, k, mode, n, steps, ctx):
     s = session(m, dw, batch=1, max_ctx=ctx, chunk=n, kv_mode=mode, k=k)
     g_tok, g_log, lib_next = generate(s, prompt, steps, k)
     assert _report(f"{name} {mode} k={k}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
+
+
+# ---------------------------------------------------------------------------
+# chunked bfloat16 prefill (matrix-core prefill attention): keys from the
+# cache and from the call, ring wrap inside and across chunks, chunk starts
+# that are not multiples of 8 (per-key value gathers), ragged last chunks
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,B,n,chunk,k,mode,ctx,steps", [
+    ("tiny_bf16", 2, 300, 100, 2, "last_loop", 320, 8),     # p0 = 100 (gathers), 200; 64-key rings
+    ("tiny_bf16_w60", 1, 257, 64, 3, "per_loop", 272, 6),   # 60-key rings; last chunk is 1 position
+    ("c36w_w192", 1, 520, 256, 2, "last_loop", 544, 6),     # hd 128, 3 q heads per kv head
+])
+def test_bf16_prefill_chunked(name, B, n, chunk, k, mode, ctx, steps):
+    m, w, dw = model_and_weights(name)
+    prompt = make_tokens(m, 21, (B, n))
+    ora = LoopedNGPT(m, w, max_ctx=ctx, batch=B)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode, chunk=chunk)
+    print(f"{name}: oracle done", flush=True)
+    s = session(m, dw, batch=B, max_ctx=ctx, chunk=chunk, kv_mode=mode, k=k)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"{name} chunked prefill {mode} k={k}", g_log, o_log) <= BF16_TOL
     np.testing.assert_array_equal(g_tok, o_tok)
     np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
 
