@@ -70,18 +70,17 @@ P* wsp(dory_ctx* c, size_t off) { return (P*)(c->ws + off); }
 
 enum { TIME_NONE = 0, TIME_UG = 1, TIME_QKVG = 2, TIME_DOWN = 3, TIME_O = 4, TIME_ATTN = 5 };
 
-// Event bracket around one launch of the timed kernel class.
+// Hands a start/stop event pair to the first kernel launched inside the
+// scope (recorded as part of its dispatch, so the pair times that kernel
+// alone); counted only if a launch took it.
 struct TimeScope {
   dory_ctx* c;
   bool on;
   TimeScope(dory_ctx* ctx, int kind) : c(ctx), on(ctx->time_kind == kind && ctx->ev_used + 2 <= ctx->ev.size()) {
-    if (on) (void)hipEventRecord(c->ev[c->ev_used], c->st);
+    if (on) set_next_launch_events(c->ev[c->ev_used], c->ev[c->ev_used + 1]);
   }
   ~TimeScope() {
-    if (on) {
-      (void)hipEventRecord(c->ev[c->ev_used + 1], c->st);
-      c->ev_used += 2;
-    }
+    if (on && !take_next_launch_events().start) c->ev_used += 2;
   }
 };
 

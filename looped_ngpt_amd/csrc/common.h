@@ -2,8 +2,11 @@
 // workgroup reductions, 16-byte vector types.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "kernels.h"
 
 namespace dory {
 
@@ -57,5 +60,15 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 __device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / sqrtf(fmaxf(sumsq, 1e-30f)); }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Kernel launch that honours the timing tap's pending events.
+template <typename F, typename... Args>
+inline void dory_launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  const LaunchEvents e = take_next_launch_events();
+  if (e.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, e.start, e.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 }  // namespace dory

@@ -212,12 +212,12 @@ static hipError_t attn_hd(const AttnArgs& a, hipStream_t st) {
   const int G = a.nq / a.nkv;
   dim3 grid(a.n_split, a.B * a.nkv, a.n);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_split<T, HD, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_split<T, HD, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_split<T, HD, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_split<T, HD, 4>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_split<T, HD, 6>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_attn_split<T, HD, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: dory_launch((k_attn_split<T, HD, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: dory_launch((k_attn_split<T, HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: dory_launch((k_attn_split<T, HD, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: dory_launch((k_attn_split<T, HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 6: dory_launch((k_attn_split<T, HD, 6>), grid, dim3(256), 0, st, a); break;
+    case 8: dory_launch((k_attn_split<T, HD, 8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -240,7 +240,7 @@ hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, 
   if (rows <= 0) return hipSuccess;
   dim3 grid((nq + 3) / 4, rows);
 #define DORY_CMB(T, HDV)                                                                                   \
-  hipLaunchKernelGGL((k_attn_combine<T, HDV>), grid, dim3(256), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, \
+  dory_launch((k_attn_combine<T, HDV>), grid, dim3(256), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, \
                      rows, nq, n_split)
   if (dtype == 0) {
     if (hd == 64) DORY_CMB(float, 64); else if (hd == 128) DORY_CMB(float, 128); else return hipErrorInvalidValue;
@@ -786,12 +786,12 @@ template <typename T, int HD>
 static hipError_t attn_dec_hd(const AttnDecArgs& a, hipStream_t st) {
   dim3 grid(a.n_split, a.B * a.nkv);
   switch (a.nq / a.nkv) {
-    case 1: hipLaunchKernelGGL((k_attn_decode<T, HD, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_decode<T, HD, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_decode<T, HD, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_decode<T, HD, 4>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_decode<T, HD, 6>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_attn_decode<T, HD, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: dory_launch((k_attn_decode<T, HD, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: dory_launch((k_attn_decode<T, HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: dory_launch((k_attn_decode<T, HD, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: dory_launch((k_attn_decode<T, HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 6: dory_launch((k_attn_decode<T, HD, 6>), grid, dim3(256), 0, st, a); break;
+    case 8: dory_launch((k_attn_decode<T, HD, 8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -801,12 +801,12 @@ template <int HD>
 static hipError_t attn_dec_mfma(const AttnDecArgs& a, hipStream_t st) {
   dim3 grid(a.n_split, a.B * a.nkv);
   switch (a.nq / a.nkv) {
-    case 1: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 4>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 6>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_attn_decode_mfma<HD, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: dory_launch((k_attn_decode_mfma<HD, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: dory_launch((k_attn_decode_mfma<HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: dory_launch((k_attn_decode_mfma<HD, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: dory_launch((k_attn_decode_mfma<HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 6: dory_launch((k_attn_decode_mfma<HD, 6>), grid, dim3(256), 0, st, a); break;
+    case 8: dory_launch((k_attn_decode_mfma<HD, 8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -836,7 +836,7 @@ hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, in
   if (B <= 0) return hipSuccess;
   dim3 grid(nq, B);
 #define DORY_MRG(T, HDV)                                                                                  \
-  hipLaunchKernelGGL((k_attn_merge<T, HDV>), grid, dim3(HDV), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, nq, \
+  dory_launch((k_attn_merge<T, HDV>), grid, dim3(HDV), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, nq, \
                      n_split)
   if (dtype == 0) {
     if (hd == 64) DORY_MRG(float, 64); else if (hd == 128) DORY_MRG(float, 128); else return hipErrorInvalidValue;

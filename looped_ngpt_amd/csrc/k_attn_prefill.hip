@@ -280,10 +280,10 @@ hipError_t launch_attn_prefill(const AttnArgs& a, const float* qkvg, int64_t ld,
   const int64_t blocks = (ngroups + 7) / 8 * 8 * G;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.hd == 64)
-    hipLaunchKernelGGL(k_attn_prefill<64>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
+    dory_launch(k_attn_prefill<64>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
                        (bf16*)ob);
   else
-    hipLaunchKernelGGL(k_attn_prefill<128>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
+    dory_launch(k_attn_prefill<128>, dim3((unsigned)blocks), dim3(256), 0, st, a, qkvg, ld, gate_off, gate,
                        (bf16*)ob);
   return hipGetLastError();
 }

@@ -196,7 +196,7 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
   const dim3 grid((nout + 7) / 8);
   const size_t lds = (size_t)M * K * 2;
 #define DORY_ROWS(C) \
-  case C: hipLaunchKernelGGL((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale); return true;
+  case C: dory_launch((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale); return true;
   switch (ch) {
     DORY_ROWS(1) DORY_ROWS(2) DORY_ROWS(3) DORY_ROWS(4) DORY_ROWS(5) DORY_ROWS(6) DORY_ROWS(8) DORY_ROWS(12)
     DORY_ROWS(16)
@@ -365,7 +365,7 @@ static hipError_t gemv_pro_launch(const GemvPro& p, const bf16* W, void* y, int 
   const dim3 grid((nout + per_block - 1) / per_block);
   const size_t lds = (size_t)M * K * 2;
 #define DORY_PRO(C) \
-  case C: hipLaunchKernelGGL((k_gemv_pro<MB, C, EPI>), grid, dim3(kProThreads), lds, st, p, W, y, M, N, K, scale); break;
+  case C: dory_launch((k_gemv_pro<MB, C, EPI>), grid, dim3(kProThreads), lds, st, p, W, y, M, N, K, scale); break;
   switch (ch) {
     DORY_PRO(1) DORY_PRO(2) DORY_PRO(3) DORY_PRO(4) DORY_PRO(5) DORY_PRO(6) DORY_PRO(7) DORY_PRO(8)
     DORY_PRO(12) DORY_PRO(16)
@@ -614,7 +614,7 @@ static hipError_t gemv_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
   const int ostride = EPI == EPI_SWIGLU ? nout : N;
   if (!vec_ok) {
     dim3 grid((nout + 3) / 4, M);
-    hipLaunchKernelGGL((k_gemv_scalar<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
+    dory_launch((k_gemv_scalar<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
     return hipGetLastError();
   }
   if (sizeof(T) == 2) {
@@ -651,7 +651,7 @@ static hipError_t gemv_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     const int rows = (nout >= 4096) ? 2 : 1;
     const int grid = (nout + 4 * rows - 1) / (4 * rows);
 #define DORY_GEMV(MBV, RV) \
-  hipLaunchKernelGGL((k_gemv_vec<T, MBV, RV, EPI>), dim3(grid), dim3(256), lds, st, xm, ldx, W, ym, mm, N, K, scale)
+  dory_launch((k_gemv_vec<T, MBV, RV, EPI>), dim3(grid), dim3(256), lds, st, xm, ldx, W, ym, mm, N, K, scale)
     if (rows == 2) {
       if (mm == 1) DORY_GEMV(1, 2); else if (mm == 2) DORY_GEMV(2, 2); else if (mm <= 4) DORY_GEMV(4, 2); else DORY_GEMV(8, 2);
     } else {
@@ -671,11 +671,11 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
   if (sizeof(T) == 2 && K % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0)) {
     const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
     dim3 grid(nt, (M + GBM - 1) / GBM);
-    hipLaunchKernelGGL((k_gemm_mfma<EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+    dory_launch((k_gemm_mfma<EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
                        scale);
   } else {
     dim3 grid((nout + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
+    dory_launch((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
   }
   return hipGetLastError();
 }

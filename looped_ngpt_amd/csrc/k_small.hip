@@ -10,6 +10,14 @@
 
 namespace dory {
 
+static thread_local LaunchEvents g_next_events{nullptr, nullptr};
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop) { g_next_events = LaunchEvents{start, stop}; }
+LaunchEvents take_next_launch_events() {
+  const LaunchEvents e = g_next_events;
+  g_next_events = LaunchEvents{nullptr, nullptr};
+  return e;
+}
+
 constexpr int kRowThreads = 256;
 
 // ---------------------------------------------------------------------------

@@ -7,6 +7,13 @@
 
 namespace dory {
 
+// Timing tap: events that the next launch of a kernel wrapper on this host
+// thread records as part of its dispatch (hipExtLaunchKernel), so that the
+// pair brackets that kernel alone. Consumed by one launch.
+struct LaunchEvents { hipEvent_t start, stop; };
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop);
+LaunchEvents take_next_launch_events();  // and clears them
+
 // h = norm(E[tok]) per row; xb = h in the model dtype; h2 (optional) = h.
 hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, float* h2, void* xb,
                         int rows, int d, int vocab, int* err, hipStream_t st);
