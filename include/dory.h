@@ -117,11 +117,13 @@ dory_status dory_validate_config(const dory_config* cfg);
  * caches per recurrent layer (ignored in last-loop mode). Layout: caches
  * numbered layer by layer (a recurrent layer in per-loop mode owns kv_loops
  * consecutive ids, loop j -> base + j - 1); cache c holds K as
- * [max_batch][n_kv][slots_c][head_dim] and then V transposed per head as
- * [max_batch][n_kv][head_dim][slots_c] (keys contiguous for each dimension,
- * the operand order of the P.V matrix-core product), with slots = max_ctx
- * for full layers and min(window, max_ctx) for sliding layers (a ring,
- * slot = pos mod window). Returns 0 for an invalid config. */
+ * [max_batch][n_kv][slots_c][head_dim] and then V as
+ * [max_batch][n_kv][vslots_c / 32][head_dim][32]: blocks of 32 slots, each
+ * with the 32 values of one dimension contiguous (the operand order of the
+ * P.V matrix-core product; one block is one contiguous run), with slots =
+ * max_ctx for full layers and min(window, max_ctx) for sliding layers (a
+ * ring, slot = pos mod window) and vslots_c = slots_c rounded up to 32.
+ * Returns 0 for an invalid config. */
 size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops);
 
 /* Bytes of the workspace dory_create needs (activations for max_batch *
@@ -130,7 +132,7 @@ size_t dory_workspace_bytes(const dory_config* cfg);
 
 /* Where the KV of (layer, loop, pos) lives: cache id, slot, and the element
  * offsets of dimension 0 of K and of V for batch row 0, kv head 0 in the KV
- * buffer (K's dimensions follow contiguously, V's every slots_c elements).
+ * buffer (K's dimensions follow contiguously, V's every 32 elements).
  * loop is 1-based for recurrent layers and ignored for the others. */
 dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops,
                          int32_t layer, int32_t loop, int32_t pos,

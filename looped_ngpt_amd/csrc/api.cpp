@@ -515,7 +515,8 @@ dory_status dory_kv_slot(const dory_config* cfg, int32_t kv_mode, int32_t kv_loo
   if (cache_id) *cache_id = id;
   if (slot) *slot = sl;
   if (k_offset) *k_offset = kv.offset[id] + (int64_t)sl * p.cfg.head_dim;
-  if (v_offset) *v_offset = kv.offset[id] + half + sl;  // V is [hd][slots]: dim d at + d * slots
+  // values in 32-position blocks [hd][32]: dimension d at + 32 * d
+  if (v_offset) *v_offset = kv.offset[id] + half + (int64_t)(sl / 32 * 32) * p.cfg.head_dim + sl % 32;
   return DORY_OK;
 }
 

@@ -61,6 +61,15 @@ __device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / sqrtf(fma
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Value cache of one kv head: blocks of 32 positions, each stored [hd][32]
+// (the 32 values of one dimension contiguous), so the values of a 32-position
+// tile are one contiguous run of 32*hd elements. vslots = slots rounded up
+// to 32; vt_off = element offset of dimension d of the value in `slot`.
+__host__ __device__ __forceinline__ int vslots_of(int slots) { return (slots + 31) & ~31; }
+__host__ __device__ __forceinline__ size_t vt_off(int slot, int d, int hd) {
+  return (size_t)(slot & ~31) * hd + (size_t)d * 32 + (slot & 31);
+}
+
 // Kernel launch that honours the timing tap's pending events.
 template <typename F, typename... Args>
 inline void dory_launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {

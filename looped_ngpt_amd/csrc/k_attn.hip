@@ -85,9 +85,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       }
       *(uint4*)(Ks + kk * KLD + c * VEC) = kv4;
     }
-    // values are stored transposed ([hd][slots] in the cache, [hd][vld] for
-    // this call): consecutive threads take consecutive keys of one dimension
-    const size_t vhead = ((size_t)b * a.nkv + kvh) * HD * a.slots;
+    // values are stored transposed (blocks of [hd][32] in the cache, [hd][vld]
+    // for this call): consecutive threads take consecutive keys of one dimension
+    const size_t vhead = ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);
     const size_t vchunk = ((size_t)b * a.nkv + kvh) * HD * a.vld;
     for (int e = tid; e < TK * HD; e += 256) {
       const int d = e / TK, kk = e % TK;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       if (kk < nk) {
         if (s < a.p0) {
           const int slot = a.is_full ? s : s % a.window;
-          v = vc[vhead + (size_t)d * a.slots + slot];
+          v = vc[vhead + vt_off(slot, d, HD)];
         } else {
           v = vw[vchunk + (size_t)d * a.vld + (s - a.p0)];
         }
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
   const T* vc = (const T*)a.vc;
   const size_t head_base = ((size_t)b * a.nkv + kvh) * a.slots;
   u32x4 kv[U][NV], vv[U][NV];
-  const T* vt = vc + head_base * HD;  // this head's transposed values [hd][slots]
+  const T* vt = vc + ((size_t)b * a.nkv + kvh) * vslots_of(a.slots) * HD;  // this head's values (32-position blocks)
   auto issue = [&](int base0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
         kv[u][i] = *(const u32x4*)(kc + o + i * LPK * VEC);
         T tmp[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) tmp[j] = vt[(size_t)((i * LPK + sub) * VEC + j) * a.slots + slot];
+        for (int j = 0; j < VEC; ++j) tmp[j] = vt[vt_off(slot, (i * LPK + sub) * VEC + j, HD)];
         vv[u][i] = *(const u32x4*)tmp;
       }
     }
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
     // the slot of t held t - W (outside every window of this call) or nothing
     const int slot = a.is_full ? t : t % a.window;
     ((T*)a.kc)[(head_base + slot) * HD + tid] = selfk[tid];
-    ((T*)a.vc)[(head_base * HD) + (size_t)tid * a.slots + slot] = selfv[tid];  // V^T [hd][slots]
+    ((T*)a.vc)[((size_t)b * a.nkv + kvh) * vslots_of(a.slots) * HD + vt_off(slot, tid, HD)] = selfv[tid];
   }
 
   // this lane's dims: chunks sub, sub + 8, ... of VEC elements
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
 // the B operand of O^T = V^T . P^T once the 32 keys are taken in the order
 // {4g..4g+3, 16+4g..16+4g+3} for lane group g, so the P.V product needs no
 // shuffles: the A operand reads the transposed cache values V^T[dim][keys]
-// (two 8-byte runs per lane). Online softmax runs per head column; the only
+// (two 8-byte runs per lane, inside one 32-position block of the value cache). Online softmax runs per head column; the only
 // cross-lane steps are the 4-group max and sum (xor 16, 32).
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
 
   // (2) cache operands of the wave's first tile (HBM)
   const bf16* kc = (const bf16*)a.kc;
-  const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * a.slots;  // V^T [hd][slots]
+  const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);  // 32-position blocks
   const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
   auto slot_of = [&](int pos) { return a.is_full ? pos : pos % a.window; };
   auto load = [&](int T, u32x4 (&ka)[2][NKK], u32x2_t (&va)[NDD][2]) {
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       const int g0 = p0 + 16 * h2 + 4 * g4;
       const int s0 = min(a.is_full ? g0 : g0 % a.window, a.slots - 4);
 #pragma unroll
-      for (int dd = 0; dd < NDD; ++dd) va[dd][h2] = *(const u32x2_t*)(vt + (size_t)(16 * dd + c16) * a.slots + s0);
+      for (int dd = 0; dd < NDD; ++dd) va[dd][h2] = *(const u32x2_t*)(vt + vt_off(s0, 16 * dd + c16, HD));
     }
   };
   const int first = tb + wave;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     // the slot of t held t - W (outside every window of this call) or nothing
     const int slot = slot_of(t);
     ((bf16*)a.kc)[(khead + slot) * HD + tid] = selfk[tid];
-    ((bf16*)a.vc)[(((size_t)b * a.nkv + kvh) * HD + tid) * a.slots + slot] = selfv[tid];
+    ((bf16*)a.vc)[((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots) + vt_off(slot, tid, HD)] = selfv[tid];
   }
 
   bf16x8_t qb[NKK];

@@ -6,7 +6,9 @@
 //
 // One workgroup takes 128 consecutive query positions of one query head; its
 // four waves own 32 positions each. Keys are visited in tiles of 64 positions
-// staged in LDS, K as rows [key][hd] and V transposed [hd][key]; the global
+// staged in LDS, K as rows [key][hd] and V transposed [hd][key] (the cache
+// keeps values in 32-position blocks [hd][32], the call's own values as
+// [hd][n]); the global
 // loads of the next tile are issued before the current tile is multiplied.
 // Per wave and 32-key half tile (v_mfma_f32_32x32x16_bf16):
 //   S^T[key][query] = K . Q^T            hd/16 steps
@@ -93,10 +95,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
   // the waits stay exact); what must read as zero, or needs a per-key gather,
   // is decided again when the registers go to LDS
   const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
-  const size_t vhead_c = ((size_t)b * a.nkv + kvh) * HD * a.slots;  // cache V^T rows
+  const size_t vhead_c = ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);  // cache values (32-position blocks)
   const size_t vhead_w = ((size_t)b * a.nkv + kvh) * HD * a.vld;    // this call's V^T rows
   const bool vec_chunk = (p0 & 7) == 0;
-  const bool vec_cache = (a.slots & 7) == 0 && (full || (W & 7) == 0);
+  const bool vec_cache = full || (W & 7) == 0;  // 8-aligned runs stay inside one 32-position block
   auto slot_of = [&](int s) { return full ? s : s % W; };
   auto key_src = [&](int s) -> const bf16* {  // K row of key s (clamped into the block's range)
     s = min(max(s, lo_blk), hi_blk);
@@ -112,11 +114,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
   };
   auto v_src = [&](int d, int s) -> const bf16* {  // vector path source (or any aligned address)
     if (run_mode(s) != 0) return vc;
-    return s >= p0 ? vw + vhead_w + (size_t)d * a.vld + (s - p0) : vc + vhead_c + (size_t)d * a.slots + slot_of(s);
+    return s >= p0 ? vw + vhead_w + (size_t)d * a.vld + (s - p0) : vc + vhead_c + vt_off(slot_of(s), d, HD);
   };
   auto v_elem = [&](int d, int s) -> bf16 {  // one value of key s (zero outside the block's range)
     if (s < lo_blk || s > hi_blk) return 0;
-    return s >= p0 ? vw[vhead_w + (size_t)d * a.vld + (s - p0)] : vc[vhead_c + (size_t)d * a.slots + slot_of(s)];
+    return s >= p0 ? vw[vhead_w + (size_t)d * a.vld + (s - p0)] : vc[vhead_c + vt_off(slot_of(s), d, HD)];
   };
 
   u32x4 kr[NL], vr[NL];

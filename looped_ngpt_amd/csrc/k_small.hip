@@ -245,10 +245,10 @@ __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
       if (isk) {
         cdst = (T*)a.kc + (((size_t)b * a.nkv + kvh) * a.slots + slot) * a.hd;
       } else {
-        // V is stored transposed per head: [hd][slots]
-        T* vt = (T*)a.vc + ((size_t)b * a.nkv + kvh) * a.hd * a.slots + slot;
-        vt[(size_t)lane * a.slots] = from_f<T>(x1);
-        vt[(size_t)(lane + half) * a.slots] = from_f<T>(x2);
+        // values: 32-position blocks [hd][32] per kv head
+        T* vt = (T*)a.vc + ((size_t)b * a.nkv + kvh) * a.hd * vslots_of(a.slots);
+        vt[vt_off(slot, lane, a.hd)] = from_f<T>(x1);
+        vt[vt_off(slot, lane + half, a.hd)] = from_f<T>(x2);
       }
     }
   }
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, cons
     const T val = isk ? kw[(size_t)r * kvd + x] : vw[((size_t)b * kvd + x) * vld + i];
     if (isk)
       kc[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
-    else  // V transposed per head: [hd][slots]
-      vc[(((size_t)b * nkv + kvh) * hd + c) * slots + slot] = val;
+    else  // values: 32-position blocks [hd][32] per kv head
+      vc[((size_t)b * nkv + kvh) * hd * vslots_of(slots) + vt_off(slot, c, hd)] = val;
   }
 }
 

@@ -84,7 +84,7 @@ dory_status make_kv_layout(const Plan& p, int kv_mode, int kv_loops, KvLayout* k
     for (int j = 0; j < kv->n_ids[l]; ++j) {
       kv->offset.push_back(off);
       kv->id_layer.push_back(l);
-      off += 2 * per_slot * p.slots(l);
+      off += per_slot * ((int64_t)p.slots(l) + p.vslots(l));  // K rows, then value blocks
     }
   }
   kv->bytes = (size_t)off * p.elem;

@@ -50,6 +50,7 @@ struct Plan {
   WsLayout ws;
   bool recurrent(int l) const { return l >= cfg.n_in && l < cfg.n_in + cfg.n_rec; }
   int slots(int l) const;
+  int vslots(int l) const { return (slots(l) + 31) / 32 * 32; }  // value cache: 32-position blocks
 };
 
 // Fills `plan` from `cfg`; returns DORY_OK or DORY_E_ARG with `why` set.

@@ -15,10 +15,11 @@ min(W, max_ctx) slots with slot = pos mod W.
 
 Buffer layout: caches are numbered layer by layer; a recurrent layer in
 per-loop mode owns `kv_loops` consecutive ids (loop j -> base + j - 1).
-Cache c occupies [K: batch x n_kv x slots_c x hd][V: batch x n_kv x hd x
-slots_c] in id order with no padding: V is stored transposed per head (keys
-contiguous for each dimension). Offsets below are in elements of the cache
-dtype.
+Cache c occupies [K: batch x n_kv x slots_c x hd][V: batch x n_kv x
+(vslots_c / 32) x hd x 32] in id order: values are kept in blocks of 32 slots
+per head, each block holding the 32 values of one dimension contiguously
+(vslots_c = slots_c rounded up to 32; the pad slots of the last block are
+never written). Offsets below are in elements of the cache dtype.
 
 Pinned by tests/test_oracle_kv.py: the footprint the oracle actually touches,
 the pages' "independent of k" / "grows with k" statements, and closed forms.
@@ -41,6 +42,13 @@ def caches_of_layer(cfg: ModelConfig, kv_mode: str, kv_loops: int, layer: int) -
 
 def slots(cfg: ModelConfig, max_ctx: int, layer: int) -> int:
     return max_ctx if cfg.layer_is_full[layer] else min(cfg.window, max_ctx)
+
+
+VTILE = 32  # slots per value block
+
+
+def vslots(cfg: ModelConfig, max_ctx: int, layer: int) -> int:
+    return -(-slots(cfg, max_ctx, layer) // VTILE) * VTILE
 
 
 def slot(cfg: ModelConfig, max_ctx: int, layer: int, pos: int) -> int:
@@ -70,8 +78,8 @@ def elem_bytes(cfg: ModelConfig) -> int:
 
 
 def cache_elems(cfg: ModelConfig, max_ctx: int, batch: int, layer: int) -> int:
-    """Elements of one cache (K and V)."""
-    return 2 * batch * cfg.n_kv_heads * slots(cfg, max_ctx, layer) * cfg.head_dim
+    """Elements of one cache (K rows, then the value blocks)."""
+    return batch * cfg.n_kv_heads * cfg.head_dim * (slots(cfg, max_ctx, layer) + vslots(cfg, max_ctx, layer))
 
 
 def kv_bytes(cfg: ModelConfig, kv_mode: str, kv_loops: int, max_ctx: int, batch: int) -> int:
@@ -90,10 +98,11 @@ def element_offset(cfg: ModelConfig, kv_mode: str, kv_loops: int, max_ctx: int, 
     half = batch * cfg.n_kv_heads * ns * cfg.head_dim
     sl = slot(cfg, max_ctx, layer, pos)
     if which == "V":
-        return start + half + (b * cfg.n_kv_heads + kvh) * cfg.head_dim * ns + sl
+        nv = vslots(cfg, max_ctx, layer)
+        return start + half + ((b * cfg.n_kv_heads + kvh) * nv + sl // VTILE * VTILE) * cfg.head_dim + sl % VTILE
     return start + ((b * cfg.n_kv_heads + kvh) * ns + sl) * cfg.head_dim
 
 
 def dim_stride(cfg: ModelConfig, max_ctx: int, layer: int, which: str) -> int:
     """Distance (elements) between consecutive dimensions of one K or V vector."""
-    return slots(cfg, max_ctx, layer) if which == "V" else 1
+    return VTILE if which == "V" else 1

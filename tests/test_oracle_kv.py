@@ -19,10 +19,13 @@ def micro() -> ModelConfig:
 
 
 def touched_bytes(o: LoopedNGPT, max_ctx: int) -> int:
+    """Bytes of the caches the oracle created: keys for every slot, values in
+    32-slot blocks (the last block padded)."""
     c = o.cfg
     total = 0
     for (l, _j) in o.cache:
-        total += kvspec.slots(c, max_ctx, l) * 2 * c.n_kv_heads * c.head_dim * kvspec.elem_bytes(c) * o.batch
+        ns = kvspec.slots(c, max_ctx, l)
+        total += (ns + -(-ns // 32) * 32) * c.n_kv_heads * c.head_dim * kvspec.elem_bytes(c) * o.batch
     return total
 
 
@@ -77,20 +80,33 @@ def test_slot_spec_ring_and_ids():
 
 def test_element_offsets_tile_the_buffer():
     """Every element of every (cache, K/V, b, head, slot) vector has its own
-    place, and the places exactly cover kv_bytes."""
+    place inside kv_bytes; the only places left over are the pad slots of the
+    last value block of each head; and the values of the 32 slots of one
+    block (all dimensions) form one contiguous run."""
     cfg = micro()
-    B, T, kl = 2, 10, 2
+    B, T, kl = 2, 40, 2      # full layers: 40 slots (one full block + 8); sliding: 3 slots
     seen = []
+    pad = 0
     for l in range(cfg.n_layers):
         loops = range(1, kl + 1) if cfg.is_recurrent(l) else [0]
+        ns = kvspec.slots(cfg, T, l)
         for j in loops:
+            pad += B * cfg.n_kv_heads * cfg.head_dim * (-(-ns // 32) * 32 - ns)
             for which in "KV":
                 st = kvspec.dim_stride(cfg, T, l, which)
                 for b in range(B):
                     for h in range(cfg.n_kv_heads):
-                        for p in range(kvspec.slots(cfg, T, l)):
+                        blocks = {}
+                        for p in range(ns):
                             o = kvspec.element_offset(cfg, PER_LOOP, kl, T, B, l, j, which, b, h, p)
-                            seen += [o + d * st for d in range(cfg.head_dim)]
+                            run = [o + d * st for d in range(cfg.head_dim)]
+                            seen += run
+                            if which == "V":
+                                blocks.setdefault(p // 32, []).extend(run)
+                        for blk, offs in blocks.items():
+                            if len(offs) == 32 * cfg.head_dim:      # a full block is one contiguous run
+                                assert sorted(offs) == list(range(min(offs), min(offs) + len(offs)))
+    total = kvspec.kv_bytes(cfg, PER_LOOP, kl, T, B) // 4
     assert len(seen) == len(set(seen))
-    assert len(seen) * 4 == kvspec.kv_bytes(cfg, PER_LOOP, kl, T, B)
-    assert sorted(seen) == list(range(len(seen)))
+    assert min(seen) == 0 and max(seen) < total
+    assert total - len(seen) == pad and pad > 0
