@@ -746,40 +746,62 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   }
 }
 
+// One workgroup of 512 threads per (q head, row): thread (d, group) takes
+// dimension d of the splits group, group + NSG, ...; every load is issued at
+// once from a clamped address (one round of L2 latency), the first wave
+// turns the split maxima into weights meanwhile, and the groups are summed
+// through LDS.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeMaxSplits = 64;
+
 template <typename T, int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(const float* __restrict__ part, const float* __restrict__ qkvg,
-                                                  int64_t ld, int gate_off, int gate, T* __restrict__ ob, int nq,
-                                                  int n_split) {
-  __shared__ float wsh[64];
-  __shared__ float lsh[64];
-  __shared__ float red[HD / 64];
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __restrict__ part,
+                                                             const float* __restrict__ qkvg, int64_t ld, int gate_off,
+                                                             int gate, T* __restrict__ ob, int nq, int n_split) {
+  constexpr int NSG = kMergeThreads / HD;        // split groups
+  constexpr int PER = kMergeMaxSplits / NSG;     // splits per group at most
+  __shared__ float wsh[kMergeMaxSplits];
+  __shared__ float lsh;
+  __shared__ float red[NSG][HD];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = tid % HD, sg = tid / HD;
   const float* p = part + ((size_t)b * nq + hq) * n_split * (HD + 2);
-  // every split's max and sum at once (n_split <= 64)
-  const float ms = d < n_split ? p[(size_t)d * (HD + 2)] : -INFINITY;
-  const float ls = d < n_split ? p[(size_t)d * (HD + 2) + 1] : 0.f;
-  float M = wave_max(ms);
-  if (HD > 64) {
-    if ((d & 63) == 0) red[d >> 6] = M;
-    __syncthreads();
-    M = red[0];
-    for (int i = 1; i < HD / 64; ++i) M = fmaxf(M, red[i]);
+  const int last = n_split - 1;
+  // split maxima and sums first (they gate the weights), then the values
+  float ms = 0.f, ls = 0.f;
+  if (tid < kMergeMaxSplits) {
+    const float* ps = p + (size_t)min(tid, last) * (HD + 2);
+    ms = ps[0];
+    ls = ps[1];
   }
-  if (d < n_split) {
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    wsh[d] = w;
-    lsh[d] = ls * w;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = p[(size_t)min(sg + NSG * i, last) * (HD + 2) + 2 + d];
+  const float* gr = qkvg + (size_t)b * ld + gate_off;
+  const float gx = gate == 1 ? gr[hq * HD + d] : (gate == 2 ? gr[hq] : 0.f);
+  if (tid < kMergeMaxSplits) {  // wave 0: weights exp2(m_s - M), total sum
+    const bool ok = tid < n_split && ms != -INFINITY;
+    const float M = wave_max(ok ? ms : -INFINITY);
+    const float w = ok ? exp2f(ms - M) : 0.f;
+    wsh[tid] = w;
+    const float L = wave_sum(ok ? ls * w : 0.f);
+    if (tid == 0) lsh = L;
   }
   __syncthreads();
-  float L = 0.f, o = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < n_split; ++s) {
-    L += lsh[s];
-    o = fmaf(p[(size_t)s * (HD + 2) + 2 + d], wsh[s], o);
+  float o = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int sp = sg + NSG * i;
+    o = fmaf(v[i], sp < n_split ? wsh[sp] : 0.f, o);
   }
-  const float* gr = qkvg + (size_t)b * ld + gate_off;
-  const float g = gate == 1 ? sigmoidf_(gr[hq * HD + d]) : (gate == 2 ? sigmoidf_(gr[hq]) : 1.f);
-  ob[((size_t)b * nq + hq) * HD + d] = from_f<T>(o / L * g);
+  red[sg][d] = o;
+  __syncthreads();
+  if (sg == 0) {
+#pragma unroll
+    for (int k = 1; k < NSG; ++k) o += red[k][d];
+    const float g = gate == 0 ? 1.f : sigmoidf_(gx);
+    ob[((size_t)b * nq + hq) * HD + d] = from_f<T>(o / lsh * g);
+  }
 }
 
 template <typename T, int HD>
@@ -834,10 +856,11 @@ hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
 hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off, int gate,
                              void* ob, int B, int nq, int hd, int n_split, hipStream_t st) {
   if (B <= 0) return hipSuccess;
+  if (n_split < 1 || n_split > kMergeMaxSplits) return hipErrorInvalidValue;
   dim3 grid(nq, B);
-#define DORY_MRG(T, HDV)                                                                                  \
-  dory_launch((k_attn_merge<T, HDV>), grid, dim3(HDV), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, nq, \
-                     n_split)
+#define DORY_MRG(T, HDV)                                                                                   \
+  dory_launch((k_attn_merge<T, HDV>), grid, dim3(kMergeThreads), 0, st, part, qkvg, ld, gate_off, gate, (T*)ob, \
+              nq, n_split)
   if (dtype == 0) {
     if (hd == 64) DORY_MRG(float, 64); else if (hd == 128) DORY_MRG(float, 128); else return hipErrorInvalidValue;
   } else {
