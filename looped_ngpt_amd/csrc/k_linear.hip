@@ -246,13 +246,14 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   // then the first P weight chunks; element i = threadIdx.x + kProThreads*c.
   // e is read from y when there is no re-injection so no branch separates loads.
   const float* ep = pr.e ? pr.e : pr.y;
-  float yv[EPT], hv[EPT], ev[EPT];
+  float yv[EPT], hv[EPT], ev[EPT], av[EPT];
 #pragma unroll
   for (int c = 0; c < EPT; ++c) {
     const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
     yv[c] = pr.y[i];
     hv[c] = pr.h_in[i];
     ev[c] = ep[i];
+    av[c] = pr.alpha[i];  // before the weights: the update must not wait behind them
   }
   __builtin_amdgcn_sched_barrier(0);
   u32x4 buf[P];
@@ -281,8 +282,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
     float st = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
-      const float al = (int)threadIdx.x + kProThreads * c < K ? pr.alpha[i] : 0.f;
+      const float al = (int)threadIdx.x + kProThreads * c < K ? av[c] : 0.f;
       hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
       st += hv[c] * hv[c];
     }
