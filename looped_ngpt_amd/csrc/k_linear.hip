@@ -541,6 +541,145 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, i
 }
 
 // ---------------------------------------------------------------------------
+// Large-M prefill GEMM: 256x256 workgroup tiles, eight waves (two per SIMD)
+// of 128x64, K steps of 32 through a four-stage LDS ring that the tiles reach
+// by direct global->LDS loads (global_load_lds_dwordx4: lane l of a wave's
+// load writes bytes 16l..16l+15 of a 1 KB block, so a block is 16 tile rows
+// of 64 B). Inside a row the 16-byte chunks are XOR-swizzled by (row/4)%4,
+// which makes the 16-lane groups of the fragment reads hit distinct banks.
+// A stage is waited for with an explicit vmcnt (the loads of the two younger
+// stages stay in flight) and one workgroup barrier per K step; the ring slot
+// refilled at step kt was last read at step kt-1, before that barrier.
+// Workgroups are spread over the 8 XCDs in contiguous runs of tiles, grouped
+// two M tiles at a time, so concurrent tiles on one XCD share A and B rows in
+// its L2. Requires K % 32 == 0 and 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
+#define DORY_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+constexpr int kBigBK = 32;                          // K per stage
+constexpr int kBigHalf = 256 * kBigBK * 2;          // A (or B) bytes per stage: 16 KB
+constexpr int kBigStage = 2 * kBigHalf;             // 32 KB
+constexpr int kBigStages = 4;
+constexpr int kBigLoads = kBigStage / 8 / 1024;     // 1 KB loads per wave per stage (4)
+constexpr int kBigGroupM = 2;
+
+__device__ __forceinline__ int big_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, int64_t lda,
+                                                  const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
+                                                  int K, float scale) {
+  __shared__ __align__(1024) unsigned char smem[kBigStages * kBigStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;  // rows wm*128, columns wn*64 of the tile
+  const int F = N / 2;
+  const int nM = (M + 255) / 256;
+  const int nN = EPI == EPI_SWIGLU ? (F + 127) / 128 : (N + 255) / 256;
+  const int nt = nM * nN;
+  const int per = (nt + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= nt) return;
+  const int grp = t / (kBigGroupM * nN);
+  const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
+  const int loc = t - grp * kBigGroupM * nN;
+  const int m0 = (grp * kBigGroupM + loc % gs) * 256;
+  const int n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * 256;
+
+  // this lane's rows for its 2 A and 2 B loads per stage (clamped: rows past
+  // M or N load a valid row and are never stored). SwiGLU: B tile rows come
+  // in 32-row chunks u, v, u, v of the same outputs.
+  const int lr = lane >> 2, ls = lane & 3;
+  const bf16* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 2 + (i & 1)) * 16 + lr;
+    const int c = ls ^ ((r >> 2) & 3);
+    if (i < 2) {
+      src[i] = A + (size_t)min(m0 + r, M - 1) * lda + c * 8;
+    } else {
+      int wr;
+      if (EPI == EPI_SWIGLU) {
+        const int nb = r >> 5;
+        const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
+        wr = (nb & 1 ? F : 0) + o;
+      } else {
+        wr = min(n0 + r, N - 1);
+      }
+      src[i] = B + (size_t)wr * K + c * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % kBigStages) * kBigStage;
+    const int k0 = kt * kBigBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + k0,
+                                       (lds_void_t*)(st + (i >= 2 ? kBigHalf : 0) + (wave * 2 + (i & 1)) * 1024), 16,
+                                       0, 0);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nK = K / kBigBK;
+  const int l32 = lane & 31, lh = lane >> 5;
+  issue(0);
+  if (nK > 1) issue(1);
+  if (nK > 2) issue(2);
+  for (int kt = 0; kt < nK; ++kt) {
+    const int ahead = min(2, nK - 1 - kt);  // younger stages allowed in flight
+    if (ahead == 2) DORY_WAIT_VM(2 * kBigLoads); else if (ahead == 1) DORY_WAIT_VM(kBigLoads); else DORY_WAIT_VM(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 3 < nK) issue(kt + 3);
+    const unsigned char* sa = smem + (kt % kBigStages) * kBigStage;
+    const unsigned char* sb = sa + kBigHalf;
+#pragma unroll
+    for (int ks = 0; ks < kBigBK / 16; ++ks) {
+      bf16x8_t a[4], b[2];
+      const int c = ks * 2 + lh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(sa + big_off(wm * 128 + i * 32 + l32, c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(sb + big_off(wn * 64 + j * 32 + l32, c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (row >= M) continue;
+      if (EPI == EPI_SWIGLU) {
+        const int o = n0 + wn * 32 + l32;
+        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * silu_(acc[i][1][r]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + l32;
+          if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Simple tiled GEMM for float32 models and ragged shapes: 64x64 tiles, each
 // thread a 4x4 block, K in steps of 16 through LDS.
 // ---------------------------------------------------------------------------
@@ -668,7 +807,12 @@ template <typename T, int EPI>
 static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, int M, int N, int K, float scale,
                                 hipStream_t st) {
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  if (sizeof(T) == 2 && K % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0)) {
+  const bool al16 = ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0);
+  if (sizeof(T) == 2 && al16 && K % kBigBK == 0 && M >= 1024) {
+    const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + 255) / 256);
+    dory_launch((k_gemm_big<EPI>), dim3((tiles + 7) / 8 * 8), dim3(512), 0, st, (const bf16*)x, ldx,
+                (const bf16*)W, y, M, N, K, scale);
+  } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
     const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
     dim3 grid(nt, (M + GBM - 1) / GBM);
     dory_launch((k_gemm_mfma<EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,

@@ -1,5 +1,5 @@
 """Single-kernel GPU checks through the C ABI: the linear kernels (matrix-
-vector, MFMA and simple tiled paths, both epilogues) against a float64 numpy
+vector, the two MFMA GEMMs and the simple tiled path, both epilogues) against a float64 numpy
 product of the same stored values, and the greedy argmax bit for bit against
 numpy.argmax (lowest index on ties)."""
 import math
@@ -30,6 +30,9 @@ CASES = [
     ("bf16", 1, 2 * 8192, 3072, 1, 1), ("bf16", 5, 2 * 1000, 2304, 1, 1), ("bf16", 1, 3072, 2304, 0, 1),
     ("bf16", 130, 1000, 3072, 0, 2), ("bf16", 256, 8192, 3072, 0, 2), ("bf16", 200, 2 * 1000, 3072, 1, 2),
     ("bf16", 64, 3072, 8192, 0, 2), ("bf16", 33, 2304, 2304, 0, 2), ("bf16", 97, 2 * 6144, 2304, 1, 2),
+    # M >= 1024: the 256x256-tile kernel (ragged M and N tiles, both epilogues, K multiple of 32)
+    ("bf16", 1100, 1000, 3072, 0, 2), ("bf16", 1030, 2 * 1000, 2304, 1, 2), ("bf16", 2048, 3072, 1088, 0, 2),
+    ("bf16", 1024, 2 * 384, 3072, 1, 2),
 ]
 
 
