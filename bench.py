@@ -137,6 +137,173 @@ def cpu_baseline(model, dev_w, k_head: int, budget_s: float = 15.0):
             "wall_s": round(time.perf_counter() - t_start, 1)}
 
 
+def _timed_decode(sess, B, k, steps, warmup, first_tokens=None):
+    """warmup + steps decode calls; returns ms per step (HIP events on the session's stream)."""
+    import torch
+    st = sess.stream
+    if first_tokens is not None:
+        sess.decode(first_tokens, k)
+        warmup -= 1
+    for _ in range(max(warmup, 0)):
+        sess.decode(None, k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        sess.decode(None, k)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _line(workload, value, ms, B, steps, warmup, n, k, mode, extra):
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights, uniform random token ids)",
+        "config": {"workload": workload, "global_batch": B, "seq_len": n, "n_loops": k, "kv_mode": mode,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    res.update(extra)
+    print(json.dumps(res))
+
+
+def run_other(args, dev):
+    """The scope table's other measurement workloads (one JSON line each)."""
+    import torch
+    import looped_ngpt_amd as dory
+    from synth.configs import CONFIGS
+    from synth.device import make_weights_device
+    stream = torch.cuda.current_stream(dev)
+    log = lambda msg: print(f"[bench:{args.workload}] {msg}", file=sys.stderr, flush=True)
+    K, Wm = args.steps, args.warmup
+
+    if args.workload == "c72":
+        model = CONFIGS["c72"]["model"]
+        n = 16384
+        w = make_weights_device(model, dev)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(model.seed * 7 + 1)
+        prompt = torch.randint(0, model.vocab, (1, n), generator=g, dtype=torch.int32).to(dev)
+        max_ctx = (n + Wm + K + 2 + 255) // 256 * 256
+        table = {}
+        for mode in ("last_loop", "per_loop"):
+            for k in (1, 2, 3, 4):
+                sess = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=8192, kv_mode=mode,
+                                    kv_loops=k if mode == "per_loop" else 1, stream=stream, device=dev)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                sess.prefill(prompt, k)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                pms = e0.elapsed_time(e1)
+                ms = _timed_decode(sess, 1, k, K, Wm)
+                step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0)
+                table[f"{mode}/k={k}"] = {"tokens_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+                                         "hbm_frac": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4),
+                                         "kv_bytes": int(sess.kv.numel()), "prefill_ms": round(pms, 1),
+                                         "prefill_tokens_per_s": round(n / (pms / 1e3), 1)}
+                log(f"{mode} k={k}: {1e3 / ms:.1f} tok/s, KV {sess.kv.numel() / 1e9:.3f} GB, prefill {pms:.0f} ms")
+                del sess
+                torch.cuda.empty_cache()
+        hk = table["last_loop/k=2"]
+        _line(f"{model.name} bf16, batch 1, {n}-token random prompt (2 chunks of 8192), greedy decode, "
+              "k=1..4 in both KV modes (headline value: k=2, last-loop)",
+              hk["tokens_per_s"], hk["ms_per_step"], 1, K, Wm, n, 2, "last_loop", {"by_mode_k": table})
+        return
+
+    if args.workload == "long":
+        model = CONFIGS["c36_256k"]["model"]
+        n, k = 262144, 2
+        w = make_weights_device(model, dev)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(model.seed * 7 + 1)
+        prompt = torch.randint(0, model.vocab, (1, n), generator=g, dtype=torch.int32).to(dev)
+        max_ctx = (n + Wm + K + 2 + 255) // 256 * 256
+        sess = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=8192, kv_mode="last_loop",
+                            stream=stream, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c0 in range(0, n, 8192):   # one chunk per call, so the run reports progress
+            sess.prefill(prompt[:, c0:c0 + 8192].contiguous(), k)
+            if c0 % (8 * 8192) == 0:
+                torch.cuda.synchronize()
+                log(f"prefill {c0 + 8192} / {n}")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1)
+        ms = _timed_decode(sess, 1, k, K, Wm)
+        step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0)
+        fl = prefill_flops(model, k, n)
+        log(f"prefill {pms / 1e3:.2f} s ({n / (pms / 1e3):.0f} tok/s), decode {1e3 / ms:.1f} tok/s")
+        _line(f"{model.name} bf16, batch 1, {n}-token random prompt in 8192-token chunks, greedy decode at k=2, "
+              "last-loop KV", 1e3 / ms, ms, 1, K, Wm, n, k, "last_loop",
+              {"hbm_frac_step": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4), "kv_bytes": int(sess.kv.numel()),
+               "prefill": {"ms": round(pms, 1), "tokens_per_s": round(n / (pms / 1e3), 1),
+                           "mfma_frac_whole": round(fl / (pms / 1e3) / MFMA_PEAK, 4)}})
+        return
+
+    # b64: 64 sequences whose 32768 cached positions are synthetic: random
+    # bfloat16 values written straight into the caller-owned KV buffer, then
+    # dory_resume (decode throughput does not depend on cache contents)
+    model = CONFIGS["c36_b64"]["model"]
+    B, ctx, k = 64, 32768, 4
+    w = make_weights_device(model, dev)
+    max_ctx = (ctx + Wm + K + 2 + 255) // 256 * 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(model.seed * 7 + 3)
+    results = {}
+    for mode in ("last_loop", "per_loop"):
+        kv_loops = k if mode == "per_loop" else 1
+        probe = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=1, kv_mode=mode, kv_loops=kv_loops,
+                             stream=stream, device=dev)
+        per_seq = probe.kv.numel()
+        del probe
+        torch.cuda.empty_cache()
+        free = torch.cuda.mem_get_info(dev)[0]
+        fit = int((free - (4 << 30)) // per_seq)     # leave 4 GiB for the workspace and the allocator
+        Bm = min(B, fit)
+        entry = {"kv_bytes_at_batch_64": per_seq * B, "free_bytes": int(free)}
+        if Bm < 1:
+            entry["oom"] = True
+            results[mode] = entry
+            continue
+        if Bm < B:
+            entry["oom_at_batch_64"] = True
+            log(f"{mode}: KV for 64 sequences is {per_seq * B / 1e9:.1f} GB, {free / 1e9:.1f} GB free: "
+                f"largest batch that fits is {Bm}")
+        sess = dory.Session(model, w, max_batch=Bm, max_ctx=max_ctx, max_chunk=1, kv_mode=mode, kv_loops=kv_loops,
+                            stream=stream, device=dev)
+        kvv = sess.kv.view(torch.bfloat16)
+        step = 1 << 29
+        for i in range(0, kvv.numel(), step):
+            m = min(step, kvv.numel() - i)
+            kvv[i:i + m].normal_(0.0, 0.05, generator=g)
+            if (i // step) % 32 == 31:
+                torch.cuda.synchronize()
+                log(f"{mode}: filled {2 * (i + m) / 1e9:.0f} / {2 * kvv.numel() / 1e9:.0f} GB of synthetic cache")
+        torch.cuda.synchronize()
+        sess.resume(Bm, ctx, k)
+        first = torch.randint(0, model.vocab, (Bm,), generator=g, device=dev, dtype=torch.int32)
+        ms = _timed_decode(sess, Bm, k, K, Wm, first_tokens=first)
+        step_bytes = decode_bytes(model, k, ctx + Wm + (K - 1) / 2.0, B=Bm)
+        entry.update({"batch": Bm, "tokens_per_s": round(Bm * 1e3 / ms, 1), "ms_per_step": round(ms, 3),
+                      "hbm_frac": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4), "kv_bytes": int(sess.kv.numel()),
+                      "bytes_per_step": step_bytes})
+        results[mode] = entry
+        log(f"{mode} batch {Bm}: {Bm * 1e3 / ms:.1f} tok/s ({ms:.2f} ms/step), HBM {100 * entry['hbm_frac']:.1f}%")
+        del sess, kvv
+        torch.cuda.empty_cache()
+    ll = results["last_loop"]
+    _line(f"{model.name} bf16, batch 64, 32768 cached positions per sequence (synthetic caches, resumed), "
+          "greedy decode at k=4, both KV modes (headline value: last-loop)", ll["tokens_per_s"], ll["ms_per_step"],
+          ll["batch"], K, Wm, ctx, k, "last_loop", {"by_mode": results})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +318,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
+    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long"], default="c36",
+                    help="c36: the headline (default). c72: the 72-layer shape, 16384-token prompt, k=1..4 in "
+                         "both KV modes. b64: 64 sequences at 32768 cached positions (synthetic caches), k=4, "
+                         "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -166,6 +337,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "c36":
+        return run_other(args, dev)
     model = get_config("c36")
     ks = [int(x) for x in args.ks.split(",")]
     if args.headline_k not in ks:

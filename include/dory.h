@@ -158,6 +158,17 @@ void dory_destroy(dory_ctx* ctx);
  * Cache contents are not cleared; they are never read before rewritten. */
 dory_status dory_reset(dory_ctx* ctx);
 
+/* Continue sequences whose KV cache the caller has put in the KV buffer
+ * (for example a saved session copied back, laid out as dory_kv_slot
+ * describes): positions [0, pos) of `batch` sequences are taken as cached,
+ * written with kv_mode and, in per-loop mode, n_loops loops (the count the
+ * sequence must keep). The next call is a dory_prefill or a dory_decode_step
+ * with explicit tokens (there are no logits to take greedy tokens from).
+ * Enqueues the device-side position update on the stream.
+ * Errors: DORY_E_CAPACITY (batch outside [1, max_batch], pos outside
+ * [1, max_ctx - 1]), DORY_E_LOOPS, DORY_E_KV_MODE. */
+dory_status dory_resume(dory_ctx* ctx, int32_t batch, int32_t pos, int32_t n_loops, int32_t kv_mode);
+
 /* Process n prompt positions of `batch` sequences: tokens_dev is device
  * int32 [batch, n]. Prompts longer than max_chunk are cut into chunks of
  * max_chunk positions, processed in order. Afterwards the logits of the last
@@ -172,7 +183,8 @@ dory_status dory_prefill(dory_ctx* ctx, const int32_t* tokens_dev, int32_t batch
  * that receives the greedy argmax (lowest index on ties), or NULL. In
  * last-loop mode n_loops may change from call to call; in per-loop mode it
  * must stay the sequence's. Errors as dory_prefill, plus DORY_E_STATE before
- * any prefill. */
+ * any prefill or dory_resume, and for tokens_dev NULL when no logits are held
+ * (right after dory_resume). */
 dory_status dory_decode_step(dory_ctx* ctx, const int32_t* tokens_dev, int32_t n_loops,
                              int32_t kv_mode, int32_t* next_tokens_dev);
 

@@ -35,7 +35,7 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 # every function dory.h declares, for the export check
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
-           "dory_decode_step", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
+           "dory_decode_step", "dory_resume", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax"]
@@ -81,6 +81,7 @@ _sig = {
     "dory_last_error": (ctypes.c_char_p, [_P]),
     "dory_set_trace": (_I, [_P, _P, _I]),
     "dory_set_graphs": (_I, [_P, _I]),
+    "dory_resume": (_I, [_P, _I, _I, _I, _I]),
     "dory_set_kernel_timing": (_I, [_P, _I, _I]),
     "dory_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]),
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
@@ -241,6 +242,12 @@ class Session:
     def reset(self) -> None:
         self._check(_lib.dory_reset(self.h))
         self.batch = None
+
+    def resume(self, batch: int, pos: int, n_loops: int, kv_mode: Optional[str] = None) -> None:
+        """Take positions [0, pos) of `batch` sequences as already in the KV buffer."""
+        mode = self.kv_mode if kv_mode is None else KV_MODES[kv_mode]
+        self._check(_lib.dory_resume(self.h, batch, pos, n_loops, mode))
+        self.batch = batch
 
     def set_graphs(self, enable: bool) -> None:
         self._check(_lib.dory_set_graphs(self.h, 1 if enable else 0))

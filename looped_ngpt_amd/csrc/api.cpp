@@ -576,6 +576,28 @@ dory_status dory_reset(dory_ctx* c) {
   return DORY_OK;
 }
 
+dory_status dory_resume(dory_ctx* c, int32_t batch, int32_t pos, int32_t n_loops, int32_t kv_mode) {
+  if (!c) return DORY_E_ARG;
+  const dory_config& C = c->plan.cfg;
+  if (batch < 1 || batch > C.max_batch) return set_err(c, DORY_E_CAPACITY, "batch outside [1, max_batch]");
+  if (pos < 1 || pos >= C.max_ctx) return set_err(c, DORY_E_CAPACITY, "pos outside [1, max_ctx - 1]");
+  if (kv_mode != c->kv.kv_mode)
+    return set_err(c, DORY_E_KV_MODE, "kv mode differs from the one the KV buffer was laid out for");
+  if (n_loops < 1 || n_loops > C.max_loops) return set_err(c, DORY_E_LOOPS, "n_loops outside [1, max_loops]");
+  if (kv_mode == DORY_KV_PER_LOOP && n_loops > c->kv.kv_loops)
+    return set_err(c, DORY_E_LOOPS, "n_loops exceeds the allocated per-loop caches");
+  c->err.clear();
+  dory_status s = device_init(c);
+  if (s != DORY_OK) return s;
+  HIP_TRY(c, launch_set_pos(wsp<int>(c, c->plan.ws.pos), pos, c->st));
+  c->pos = pos;
+  c->batch = batch;
+  c->kv_mode_seq = kv_mode;
+  c->seq_loops = kv_mode == DORY_KV_PER_LOOP ? n_loops : 0;
+  c->has_logits = false;
+  return DORY_OK;
+}
+
 dory_status dory_prefill(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, int32_t n, int32_t n_loops,
                          int32_t kv_mode) {
   if (!c) return DORY_E_ARG;
@@ -602,7 +624,8 @@ dory_status dory_prefill(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, 
 dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_loops, int32_t kv_mode,
                              int32_t* next_tokens_dev) {
   if (!c) return DORY_E_ARG;
-  if (c->pos == 0 || !c->has_logits) return set_err(c, DORY_E_STATE, "decode before prefill");
+  if (c->pos == 0) return set_err(c, DORY_E_STATE, "decode before prefill");
+  if (!tokens_dev && !c->has_logits) return set_err(c, DORY_E_STATE, "no greedy tokens to continue from");
   dory_status s = check_call(c, c->batch, 1, n_loops, kv_mode);
   if (s != DORY_OK) return s;
   c->err.clear();

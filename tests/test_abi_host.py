@@ -156,6 +156,15 @@ def test_call_validation_codes():
     assert b"capacity" in L.dory_status_string(dory.DORY_E_CAPACITY)
     assert L.dory_reset(h) == dory.DORY_OK
     assert L.dory_reset(None) == dory.DORY_E_ARG
+    # resuming from a caller-filled cache: every bad argument is caught before any device work
+    assert L.dory_resume(h, 0, 4, 2, PL) == dory.DORY_E_CAPACITY             # batch
+    assert L.dory_resume(h, 3, 4, 2, PL) == dory.DORY_E_CAPACITY
+    assert L.dory_resume(h, 1, 0, 2, PL) == dory.DORY_E_CAPACITY             # pos
+    assert L.dory_resume(h, 1, 16, 2, PL) == dory.DORY_E_CAPACITY            # pos = max_ctx
+    assert L.dory_resume(h, 1, 4, 2, LL) == dory.DORY_E_KV_MODE
+    assert L.dory_resume(h, 1, 4, 3, PL) == dory.DORY_E_LOOPS                # > per-loop caches
+    assert L.dory_resume(h, 1, 4, 0, PL) == dory.DORY_E_LOOPS
+    assert L.dory_resume(None, 1, 4, 2, PL) == dory.DORY_E_ARG
 
 
 def test_op_validation():

@@ -227,6 +227,34 @@ def test_bf16_prefill_chunked(name, B, n, chunk, k, mode, ctx, steps):
 
 
 # ---------------------------------------------------------------------------
+# resuming from a caller-filled KV buffer: a copy of one context's cache,
+# resumed in a second context, decodes exactly like the first
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,mode", [("tiny_bf16", "last_loop"), ("tiny_bf16", "per_loop"), ("tiny", "last_loop")])
+def test_resume_from_copied_cache_bit_identical(name, mode):
+    m, w, dw = model_and_weights(name)
+    B, n, k, ctx = 2, 77, 2, 128
+    prompt = torch.from_numpy(make_tokens(m, 30, (B, n))).cuda()
+    a = session(m, dw, batch=B, max_ctx=ctx, chunk=64, kv_mode=mode, k=k)
+    b = session(m, dw, batch=B, max_ctx=ctx, chunk=64, kv_mode=mode, k=k)
+    a.prefill(prompt, k)
+    first = torch.argmax(a.logits(), dim=-1).to(torch.int32)
+    torch.cuda.synchronize()
+    b.kv.copy_(a.kv)
+    b.resume(B, n, k)
+    toks = [first] + [torch.tensor([(7 * i + 3) % m.vocab] * B, dtype=torch.int32, device="cuda") for i in range(4)]
+    for i, t in enumerate(toks):
+        a.decode(t.contiguous(), k)
+        b.decode(t.contiguous(), k)
+        la, lb = a.logits().cpu().numpy(), b.logits().cpu().numpy()
+        np.testing.assert_array_equal(la, lb, err_msg=f"step {i}")
+    # greedy continuation also works after the explicit first token
+    b.decode(None, k)
+    a.decode(None, k)
+    np.testing.assert_array_equal(a.logits().cpu().numpy(), b.logits().cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
 # recorded decode steps: continued greedy decoding of a bfloat16 model is
 # recorded once per (loop count, batch) and replayed; each replay must equal
 # the same step launched kernel by kernel
