@@ -188,6 +188,21 @@ dory_status dory_prefill(dory_ctx* ctx, const int32_t* tokens_dev, int32_t batch
 dory_status dory_decode_step(dory_ctx* ctx, const int32_t* tokens_dev, int32_t n_loops,
                              int32_t kv_mode, int32_t* next_tokens_dev);
 
+/* Per-sequence loop counts in one batched call: the loop count is a
+ * serve-time choice per request ("Dory1.0-4B: A Looped Normalized-GPT", AI
+ * summary, Key Contributions 1; broadside review, Why it matters here).
+ * Sequence b runs loops_host[b] passes of the recurrent block (host int32
+ * [batch], each in [1, max_loops]); while the batch runs on, sequence b's
+ * state stays as its own last pass left it, and its recurrent layers' K/V
+ * are written on that pass. Each sequence's result is the one it would get
+ * alone with its own count. Last-loop caching only (DORY_E_KV_MODE
+ * otherwise); loops_host NULL or a count outside [1, max_loops] ->
+ * DORY_E_ARG / DORY_E_LOOPS; the rest as dory_prefill / dory_decode_step. */
+dory_status dory_prefill_mixed(dory_ctx* ctx, const int32_t* tokens_dev, int32_t batch, int32_t n,
+                               const int32_t* loops_host, int32_t kv_mode);
+dory_status dory_decode_step_mixed(dory_ctx* ctx, const int32_t* tokens_dev, const int32_t* loops_host,
+                                   int32_t kv_mode, int32_t* next_tokens_dev);
+
 /* Copy the float32 logits [batch, vocab] of the last processed position to
  * out_dev (device). DORY_E_STATE before any prefill. */
 dory_status dory_logits(dory_ctx* ctx, float* out_dev);

@@ -35,7 +35,7 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 # every function dory.h declares, for the export check
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
-           "dory_decode_step", "dory_resume", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
+           "dory_decode_step", "dory_resume", "dory_prefill_mixed", "dory_decode_step_mixed", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax"]
@@ -82,6 +82,8 @@ _sig = {
     "dory_set_trace": (_I, [_P, _P, _I]),
     "dory_set_graphs": (_I, [_P, _I]),
     "dory_resume": (_I, [_P, _I, _I, _I, _I]),
+    "dory_prefill_mixed": (_I, [_P, _P, _I, _I, _P, _I]),
+    "dory_decode_step_mixed": (_I, [_P, _P, _P, _I, _P]),
     "dory_set_kernel_timing": (_I, [_P, _I, _I]),
     "dory_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]),
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
@@ -242,6 +244,22 @@ class Session:
     def reset(self) -> None:
         self._check(_lib.dory_reset(self.h))
         self.batch = None
+
+    def prefill_mixed(self, tokens, loops) -> None:
+        """Prefill with a loop count per sequence (last-loop caching)."""
+        import torch
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
+        arr = (ctypes.c_int32 * len(loops))(*[int(k) for k in loops])
+        self._check(_lib.dory_prefill_mixed(self.h, _ptr(tokens), tokens.shape[0], tokens.shape[1],
+                                            ctypes.cast(arr, ctypes.c_void_p), KV_MODES["last_loop"]))
+        self.batch = tokens.shape[0]
+
+    def decode_mixed(self, tokens, loops, next_tokens=None) -> None:
+        """One decode position with a loop count per sequence (last-loop caching)."""
+        arr = (ctypes.c_int32 * len(loops))(*[int(k) for k in loops])
+        self._check(_lib.dory_decode_step_mixed(self.h, _ptr(tokens) if tokens is not None else None,
+                                                ctypes.cast(arr, ctypes.c_void_p), KV_MODES["last_loop"],
+                                                _ptr(next_tokens) if next_tokens is not None else None))
 
     def resume(self, batch: int, pos: int, n_loops: int, kv_mode: Optional[str] = None) -> None:
         """Take positions [0, pos) of `batch` sequences as already in the KV buffer."""

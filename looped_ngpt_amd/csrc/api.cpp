@@ -28,6 +28,7 @@ struct dory_ctx {
   hipStream_t st = nullptr;
   // sequence state
   int pos = 0, batch = 0, seq_loops = 0, kv_mode_seq = -1;
+  bool mixed = false;  // inside a call with per-sequence loop counts (workspace rowk)
   bool has_logits = false;
   bool device_ready = false;  // RoPE tables built, flags cleared
   // test tap
@@ -130,6 +131,10 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
   float* qkvg = wsp<float>(c, W.qkvg);
   float* y = wsp<float>(c, W.y);
   hipStream_t st = c->st;
+  // mixed loop counts: rows past their count keep their state; K/V are
+  // written on each sequence's own last pass
+  const int* mix = (c->mixed && P.recurrent(l)) ? wsp<int>(c, W.rowk) : nullptr;
+  const RowGate gate{mix, loop, n};
 
   {
     TimeScope ts(c, TIME_QKVG);
@@ -173,14 +178,14 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     // after attention: the ring slots of this call's positions held keys it needed
     if (write_kv)
       HIP_TRY(c, launch_kv_write(dt, c->ws + W.kw, c->ws + W.vw, ra.vld, kc, vc, B, n, c->pos, C.n_kv_heads,
-                                 C.head_dim, slots, C.window, full, st));
+                                 C.head_dim, slots, C.window, full, st, mix, loop));
   }
 
   {
     TimeScope ts(c, TIME_O);
     HIP_TRY(c, launch_linear(dt, c->ws + W.ob, P.q_dim, c->o[l], y, rows, C.d_model, P.q_dim, 0, 1.f, 0, st));
   }
-  HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st, gate));
   {
     TimeScope ts(c, TIME_UG);
     HIP_TRY(c, launch_linear(dt, xb, C.d_model, c->ug[l], c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f, 0, st));
@@ -189,7 +194,7 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     TimeScope ts(c, TIME_DOWN);
     HIP_TRY(c, launch_linear(dt, c->ws + W.a, C.d_ff, c->down[l], y, rows, C.d_model, C.d_ff, 0, 1.f, 0, st));
   }
-  HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st, gate));
   if (c->trace)
     HIP_TRY(c, hipMemcpyAsync(c->trace + (size_t)app * rows * C.d_model, h, (size_t)rows * C.d_model * 4,
                               hipMemcpyDeviceToDevice, st));
@@ -223,6 +228,8 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
   da.scale = P.attn_scale;
   da.kc = kc; da.vc = vc;
   da.part = wsp<float>(c, W.part);
+  da.wloops = (c->mixed && P.recurrent(l)) ? wsp<int>(c, W.rowk) : nullptr;
+  da.loop = loop;
   {
     TimeScope ts(c, TIME_ATTN);
     HIP_TRY(c, launch_attn_decode(C.dtype, da, c->st));
@@ -240,7 +247,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
 // buffers so the workgroup writing the new one never races readers of the old.
 bool fused_decode_ok(const dory_ctx* c, int B) {
   const dory_config& C = c->plan.cfg;
-  return C.dtype == DORY_BF16 && !c->trace && C.n_rec >= 1 && linear_pro_supported(B, C.d_model);
+  return C.dtype == DORY_BF16 && !c->trace && !c->mixed && C.n_rec >= 1 && linear_pro_supported(B, C.d_model);
 }
 
 dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
@@ -364,8 +371,11 @@ dory_status run_forward(dory_ctx* c, const int32_t* tok, int64_t tok_ld, int B, 
     if (s != DORY_OK) return s;
   }
   for (int j = 1; j <= k; ++j) {
-    if (j >= 2) HIP_TRY(c, launch_combine(dt, h, e, C.combine_wh, C.combine_we, xb, rows, C.d_model, st));
-    const bool write_kv = c->kv.kv_mode == DORY_KV_PER_LOOP || j == k;
+    if (j >= 2)
+      HIP_TRY(c, launch_combine(dt, h, e, C.combine_wh, C.combine_we, xb, rows, C.d_model, st,
+                                RowGate{c->mixed ? wsp<int>(c, W.rowk) : nullptr, j, n}));
+    // mixed counts: every pass may be some sequence's last (per-row predicate in the writers)
+    const bool write_kv = c->mixed || c->kv.kv_mode == DORY_KV_PER_LOOP || j == k;
     for (int l = C.n_in; l < C.n_in + C.n_rec; ++l) {
       dory_status s = run_layer(c, l, j, B, n, nullptr, app++, write_kv);
       if (s != DORY_OK) return s;
@@ -643,6 +653,99 @@ dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_l
   if (next_tokens_dev)
     HIP_TRY(c, hipMemcpyAsync(next_tokens_dev, c->ws + P.ws.next, (size_t)c->batch * 4, hipMemcpyDeviceToDevice,
                               c->st));
+  return DORY_OK;
+}
+
+namespace {
+
+// Validates per-sequence loop counts (last-loop caches only) and stores them
+// in the workspace; returns the largest count.
+dory_status mixed_setup(dory_ctx* c, int B, const int32_t* loops_host, int kv_mode, int* kmax) {
+  const dory_config& C = c->plan.cfg;
+  if (!loops_host) return set_err(c, DORY_E_ARG, "loops is NULL");
+  if (kv_mode != DORY_KV_LAST_LOOP || c->kv.kv_mode != DORY_KV_LAST_LOOP)
+    return set_err(c, DORY_E_KV_MODE, "per-sequence loop counts need last-loop caching");
+  if (B < 1 || B > C.max_batch) return set_err(c, DORY_E_CAPACITY, "batch outside [1, max_batch]");
+  int km = 0;
+  for (int b = 0; b < B; ++b) {
+    if (loops_host[b] < 1 || loops_host[b] > C.max_loops)
+      return set_err(c, DORY_E_LOOPS, "a loop count is outside [1, max_loops]");
+    km = std::max(km, (int)loops_host[b]);
+  }
+  *kmax = km;
+  return DORY_OK;
+}
+
+dory_status mixed_upload(dory_ctx* c, int B, const int32_t* loops_host) {
+  int* dst = wsp<int>(c, c->plan.ws.rowk);
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    RowLoops a{};
+    a.n = std::min(64, B - b0);
+    for (int i = 0; i < a.n; ++i) a.k[i] = loops_host[b0 + i];
+    HIP_TRY(c, launch_set_rows(dst + b0, a, c->st));
+  }
+  return DORY_OK;
+}
+
+struct MixedScope {
+  dory_ctx* c;
+  explicit MixedScope(dory_ctx* ctx) : c(ctx) { c->mixed = true; }
+  ~MixedScope() { c->mixed = false; }
+};
+
+}  // namespace
+
+dory_status dory_prefill_mixed(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, int32_t n,
+                               const int32_t* loops_host, int32_t kv_mode) {
+  if (!c) return DORY_E_ARG;
+  if (!tokens_dev) return set_err(c, DORY_E_ARG, "tokens_dev is NULL");
+  if (n < 0) return set_err(c, DORY_E_ARG, "n < 0");
+  int kmax = 0;
+  dory_status s = mixed_setup(c, batch, loops_host, kv_mode, &kmax);
+  if (s != DORY_OK) return s;
+  if (n == 0) return DORY_OK;
+  s = check_call(c, batch, n, kmax, kv_mode);
+  if (s != DORY_OK) return s;
+  c->err.clear();
+  s = device_init(c);
+  if (s != DORY_OK) return s;
+  s = mixed_upload(c, batch, loops_host);
+  if (s != DORY_OK) return s;
+  MixedScope ms(c);
+  const int chunk = c->plan.cfg.max_chunk;
+  for (int s0 = 0; s0 < n; s0 += chunk) {
+    const int m = std::min(chunk, n - s0);
+    s = run_forward(c, tokens_dev + s0, n, batch, m, kmax, s0 + m >= n);
+    if (s != DORY_OK) return s;
+    commit_call(c, batch, m, kmax, kv_mode);
+  }
+  HIP_TRY(c, launch_set_pos(wsp<int>(c, c->plan.ws.pos), c->pos, c->st));
+  return DORY_OK;
+}
+
+dory_status dory_decode_step_mixed(dory_ctx* c, const int32_t* tokens_dev, const int32_t* loops_host,
+                                   int32_t kv_mode, int32_t* next_tokens_dev) {
+  if (!c) return DORY_E_ARG;
+  if (c->pos == 0) return set_err(c, DORY_E_STATE, "decode before prefill");
+  if (!tokens_dev && !c->has_logits) return set_err(c, DORY_E_STATE, "no greedy tokens to continue from");
+  int kmax = 0;
+  dory_status s = mixed_setup(c, c->batch, loops_host, kv_mode, &kmax);
+  if (s != DORY_OK) return s;
+  s = check_call(c, c->batch, 1, kmax, kv_mode);
+  if (s != DORY_OK) return s;
+  c->err.clear();
+  s = mixed_upload(c, c->batch, loops_host);
+  if (s != DORY_OK) return s;
+  {
+    MixedScope ms(c);
+    const int32_t* tok = tokens_dev ? tokens_dev : wsp<int32_t>(c, c->plan.ws.next);
+    s = run_forward(c, tok, 1, c->batch, 1, kmax, true, true);
+  }
+  if (s != DORY_OK) return s;
+  commit_call(c, c->batch, 1, kmax, kv_mode);
+  if (next_tokens_dev)
+    HIP_TRY(c, hipMemcpyAsync(next_tokens_dev, c->ws + c->plan.ws.next, (size_t)c->batch * 4,
+                              hipMemcpyDeviceToDevice, c->st));
   return DORY_OK;
 }
 

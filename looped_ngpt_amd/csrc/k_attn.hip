@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
     }
   }
   __syncthreads();
-  if (has_self && a.write_kv && tid < HD) {
+  if (has_self && a.write_kv && (!a.wloops || a.wloops[b] == a.loop) && tid < HD) {
     // the slot of t held t - W (outside every window of this call) or nothing
     const int slot = a.is_full ? t : t % a.window;
     ((T*)a.kc)[(head_base + slot) * HD + tid] = selfk[tid];
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   }
   for (int e = tid; e < (16 - G) * HD; e += 256) qs[G + e / HD][e % HD] = 0;  // padded head columns
   __syncthreads();
-  if (has_self && a.write_kv && tid < HD) {
+  if (has_self && a.write_kv && (!a.wloops || a.wloops[b] == a.loop) && tid < HD) {
     // the slot of t held t - W (outside every window of this call) or nothing
     const int slot = slot_of(t);
     ((bf16*)a.kc)[(khead + slot) * HD + tid] = selfk[tid];

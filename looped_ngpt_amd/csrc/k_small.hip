@@ -63,8 +63,9 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
 template <typename T, int EPT>
 __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, const float* __restrict__ y,
                                                        const float* __restrict__ alpha, T* __restrict__ xb,
-                                                       float* __restrict__ h2, int d) {
+                                                       float* __restrict__ h2, int d, RowGate gate) {
   __shared__ float sh[kRowThreads / 64];
+  if (gate.loops && gate.loop > gate.loops[blockIdx.x / gate.n]) return;  // row past its loop count
   const size_t o = (size_t)blockIdx.x * d;
   float yv[EPT], hv[EPT];
   float ss = 0.f;
@@ -102,8 +103,10 @@ __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, c
 // ---------------------------------------------------------------------------
 template <typename T, int EPT>
 __global__ __launch_bounds__(kRowThreads) void k_combine(float* __restrict__ h, const float* __restrict__ e,
-                                                        float wh, float we, T* __restrict__ xb, int d) {
+                                                        float wh, float we, T* __restrict__ xb, int d,
+                                                        RowGate gate) {
   __shared__ float sh[kRowThreads / 64];
+  if (gate.loops && gate.loop > gate.loops[blockIdx.x / gate.n]) return;  // row past its loop count
   const size_t o = (size_t)blockIdx.x * d;
   float v[EPT];
   float ss = 0.f;
@@ -151,22 +154,34 @@ hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, 
 }
 
 hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2, int rows,
-                         int d, hipStream_t st) {
+                         int d, hipStream_t st, RowGate gate) {
   if (rows <= 0) return hipSuccess;
+  if (gate.loops && gate.n < 1) return hipErrorInvalidValue;
   if (dtype == 0)
-    DORY_ROW_LAUNCH(k_update, float, d, rows, st, h, y, alpha, (float*)xb, h2, d);
+    DORY_ROW_LAUNCH(k_update, float, d, rows, st, h, y, alpha, (float*)xb, h2, d, gate);
   else
-    DORY_ROW_LAUNCH(k_update, bf16, d, rows, st, h, y, alpha, (bf16*)xb, h2, d);
+    DORY_ROW_LAUNCH(k_update, bf16, d, rows, st, h, y, alpha, (bf16*)xb, h2, d, gate);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(int dtype, float* h, const float* e, float wh, float we, void* xb, int rows, int d,
-                          hipStream_t st) {
+                          hipStream_t st, RowGate gate) {
   if (rows <= 0) return hipSuccess;
+  if (gate.loops && gate.n < 1) return hipErrorInvalidValue;
   if (dtype == 0)
-    DORY_ROW_LAUNCH(k_combine, float, d, rows, st, h, e, wh, we, (float*)xb, d);
+    DORY_ROW_LAUNCH(k_combine, float, d, rows, st, h, e, wh, we, (float*)xb, d, gate);
   else
-    DORY_ROW_LAUNCH(k_combine, bf16, d, rows, st, h, e, wh, we, (bf16*)xb, d);
+    DORY_ROW_LAUNCH(k_combine, bf16, d, rows, st, h, e, wh, we, (bf16*)xb, d, gate);
+  return hipGetLastError();
+}
+
+__global__ void k_set_rows(int* __restrict__ dst, RowLoops a) {
+  if ((int)threadIdx.x < a.n) dst[threadIdx.x] = a.k[threadIdx.x];
+}
+
+hipError_t launch_set_rows(int* dst, const RowLoops& a, hipStream_t st) {
+  if (a.n < 1 || a.n > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_set_rows, dim3(1), dim3(64), 0, st, dst, a);
   return hipGetLastError();
 }
 
@@ -281,10 +296,12 @@ hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, const T* __restrict__ vw, int vld,
                                                  T* __restrict__ kc, T* __restrict__ vc, int n, int p0, int nkv,
-                                                 int hd, int slots, int window, int is_full) {
+                                                 int hd, int slots, int window, int is_full,
+                                                 const int* __restrict__ wloops, int loop) {
   const int r = blockIdx.x;
   const int b = r / n, i = r % n;
   if (!is_full && i < n - slots) return;  // overwritten later in this call
+  if (wloops && wloops[b] != loop) return;  // not this sequence's last pass
   const int pos = p0 + i;
   const int slot = is_full ? pos : pos % window;
   const int kvd = nkv * hd;
@@ -301,14 +318,15 @@ __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, cons
 }
 
 hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, int vld, void* kc, void* vc, int B, int n,
-                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st) {
+                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st,
+                           const int* wloops, int loop) {
   if (B * n <= 0) return hipSuccess;
   if (dtype == 0)
     hipLaunchKernelGGL(k_kv_write<float>, dim3(B * n), dim3(256), 0, st, (const float*)kw, (const float*)vw, vld,
-                       (float*)kc, (float*)vc, n, p0, nkv, hd, slots, window, is_full);
+                       (float*)kc, (float*)vc, n, p0, nkv, hd, slots, window, is_full, wloops, loop);
   else
     hipLaunchKernelGGL(k_kv_write<bf16>, dim3(B * n), dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw, vld,
-                       (bf16*)kc, (bf16*)vc, n, p0, nkv, hd, slots, window, is_full);
+                       (bf16*)kc, (bf16*)vc, n, p0, nkv, hd, slots, window, is_full, wloops, loop);
   return hipGetLastError();
 }
 

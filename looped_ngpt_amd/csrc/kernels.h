@@ -14,17 +14,33 @@ struct LaunchEvents { hipEvent_t start, stop; };
 void set_next_launch_events(hipEvent_t start, hipEvent_t stop);
 LaunchEvents take_next_launch_events();  // and clears them
 
+// Mixed loop counts: row r of a launch belongs to sequence r / n, which runs
+// loops[r / n] passes of the recurrent block. At pass `loop` a row whose count
+// has passed is left untouched (its residual and bf16 copy keep the value of
+// its own last pass). loops == NULL: every row is active.
+struct RowGate {
+  const int* loops;
+  int loop, n;
+};
+
 // h = norm(E[tok]) per row; xb = h in the model dtype; h2 (optional) = h.
 hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, float* h2, void* xb,
                         int rows, int d, int vocab, int* err, hipStream_t st);
 
 // nGPT step per row: h = norm(h + alpha * (norm(y) - h)); xb = h (dtype); h2 (optional) = h.
 hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2,
-                         int rows, int d, hipStream_t st);
+                         int rows, int d, hipStream_t st, RowGate gate = RowGate{nullptr, 0, 1});
 
 // Loop re-injection per row: h = norm(wh * h + we * e); xb = h (dtype).
 hipError_t launch_combine(int dtype, float* h, const float* e, float wh, float we, void* xb, int rows,
-                          int d, hipStream_t st);
+                          int d, hipStream_t st, RowGate gate = RowGate{nullptr, 0, 1});
+
+// dst[i] = loops[i], i < n (n <= 64 per launch).
+struct RowLoops {
+  int n;
+  int k[64];
+};
+hipError_t launch_set_rows(int* dst, const RowLoops& a, hipStream_t st);
 
 // tab[pos][i] = (cos, sin)(pos * base^(-2i/hd)), angles in float64.
 hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipStream_t st);
@@ -46,9 +62,11 @@ hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st);
 
 // Copies this call's keys and values (kw rows, vw transposed with row length
 // vld) into the cache: every position of a full layer, the last
-// min(n, slots) positions of a sliding-window ring.
+// min(n, slots) positions of a sliding-window ring. wloops (optional, per
+// sequence): sequence b is written only when wloops[b] == loop (its last pass).
 hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, int vld, void* kc, void* vc, int B, int n,
-                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st);
+                           int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st,
+                           const int* wloops = nullptr, int loop = 0);
 
 // Split-K softmax attention. For query row r = b*n + i (position p0 + i) and
 // query head hq (kv head hq / G) the allowed keys are s <= t (and t - s <
@@ -85,6 +103,8 @@ hipError_t launch_attn_combine(int dtype, const float* part, const float* qkvg, 
 // The position t of the new key is read from t_dev, so one recorded graph
 // serves every step; n_split is fixed by capacity and the kernel spreads the
 // actual key range over it (trailing splits may be empty).
+// wloops (optional, per sequence): with write_kv, sequence b writes its new
+// key/value only when wloops[b] == loop (mixed loop counts, its last pass).
 struct AttnDecArgs {
   const float* qkvg; int64_t ld;
   const float2* tab;
@@ -93,6 +113,7 @@ struct AttnDecArgs {
   float scale;
   void* kc; void* vc;
   float* part;
+  const int* wloops; int loop;
 };
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st);
 // True when launch_attn_decode takes the matrix-core kernel, which splits the

@@ -128,6 +128,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.amax = take(argmax_partials(c.max_batch, c.vocab) * 8);
   w.flags = take(256);
   w.pos = take(4);
+  w.rowk = take((size_t)c.max_batch * 4);
   w.total = at;
   return w;
 }

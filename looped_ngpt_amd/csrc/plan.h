@@ -38,6 +38,7 @@ struct WsLayout {
   size_t amax = 0;                     // argmax partials
   size_t flags = 0;                    // device error flags
   size_t pos = 0;                      // int: position counter read by decode kernels
+  size_t rowk = 0;                     // int [max_batch]: per-sequence loop counts of a mixed call
   size_t total = 0;
 };
 

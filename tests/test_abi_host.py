@@ -167,6 +167,29 @@ def test_call_validation_codes():
     assert L.dory_resume(None, 1, 4, 2, PL) == dory.DORY_E_ARG
 
 
+def test_mixed_loop_validation_codes():
+    m = small()
+    L = dory.lib()
+    LL, PL = dory.DORY_KV_LAST_LOOP, dory.DORY_KV_PER_LOOP
+    tok = 1 << 14
+    arr = lambda *v: ctypes.cast((ctypes.c_int32 * len(v))(*v), ctypes.c_void_p)
+    f = FakeCtx(m, kv_mode="last_loop")
+    assert f.status == dory.DORY_OK
+    h = f.h
+    ok2 = arr(1, 3)
+    assert L.dory_prefill_mixed(h, tok, 2, 4, None, LL) == dory.DORY_E_ARG
+    assert L.dory_prefill_mixed(h, None, 2, 4, ok2, LL) == dory.DORY_E_ARG
+    assert L.dory_prefill_mixed(h, tok, 2, 4, ok2, PL) == dory.DORY_E_KV_MODE
+    assert L.dory_prefill_mixed(h, tok, 2, 4, arr(1, 5), LL) == dory.DORY_E_LOOPS   # > max_loops
+    assert L.dory_prefill_mixed(h, tok, 2, 4, arr(0, 1), LL) == dory.DORY_E_LOOPS
+    assert L.dory_prefill_mixed(h, tok, 3, 4, arr(1, 1, 1), LL) == dory.DORY_E_CAPACITY  # batch
+    assert L.dory_prefill_mixed(h, tok, 2, 17, ok2, LL) == dory.DORY_E_CAPACITY          # context
+    assert L.dory_prefill_mixed(h, tok, 2, 0, ok2, LL) == dory.DORY_OK                   # empty: no-op
+    assert L.dory_decode_step_mixed(h, tok, ok2, LL, None) == dory.DORY_E_STATE          # nothing prefilled
+    g = FakeCtx(m, kv_mode="per_loop", kv_loops=2)
+    assert L.dory_prefill_mixed(g.h, tok, 2, 4, ok2, PL) == dory.DORY_E_KV_MODE         # per-loop caches
+
+
 def test_op_validation():
     L = dory.lib()
     assert L.dory_op_linear(2, 1 << 12, 8, 1 << 12, 1 << 12, 1, 8, 8, 0, 1.0, 0, None) == dory.DORY_E_ARG

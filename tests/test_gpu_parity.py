@@ -227,6 +227,36 @@ def test_bf16_prefill_chunked(name, B, n, chunk, k, mode, ctx, steps):
 
 
 # ---------------------------------------------------------------------------
+# per-sequence loop counts in one batched call (last-loop caching): each
+# sequence must get what it gets alone with its own counts — the reference is
+# one single-sequence oracle per row
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,tol", [("tiny", F32_TOL), ("tiny_bf16", BF16_TOL)])
+def test_mixed_loop_counts_match_separate_sequences(name, tol):
+    m, w, dw = model_and_weights(name)
+    B, n, chunk, ctx = 3, 70, 64, 128
+    prompt = make_tokens(m, 40, (B, n))
+    pre_k = [1, 3, 2]
+    sched = [[1, 3, 2], [2, 2, 4], [1, 1, 1], [3, 1, 2], [4, 2, 1]]
+    forced = np.random.default_rng(5).integers(0, m.vocab, size=(len(sched), B)).astype(np.int32)
+    ref = np.zeros((len(sched) + 1, B, m.vocab))
+    for b in range(B):
+        o = LoopedNGPT(m, w, max_ctx=ctx, batch=1)
+        for s0 in range(0, n, chunk):
+            lg = o.call(prompt[b:b + 1, s0:s0 + chunk], pre_k[b], "last_loop")
+        ref[0, b] = lg[0]
+        for i, ks in enumerate(sched):
+            ref[i + 1, b] = o.call(forced[i:i + 1, b:b + 1], ks[b], "last_loop")[0]
+    s = session(m, dw, batch=B, max_ctx=ctx, chunk=chunk, kv_mode="last_loop", k=4)
+    s.prefill_mixed(torch.from_numpy(prompt).cuda(), pre_k)
+    got = [s.logits().cpu().numpy()]
+    for i, ks in enumerate(sched):
+        s.decode_mixed(torch.from_numpy(forced[i]).cuda(), ks)
+        got.append(s.logits().cpu().numpy())
+    assert _report(f"{name} mixed loop counts", np.stack(got), ref) <= tol
+
+
+# ---------------------------------------------------------------------------
 # resuming from a caller-filled KV buffer: a copy of one context's cache,
 # resumed in a second context, decodes exactly like the first
 # ---------------------------------------------------------------------------
