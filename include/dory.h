@@ -59,6 +59,16 @@ typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype;
  * by every loop; the footprint equals the one-loop size at any k. */
 typedef enum { DORY_KV_PER_LOOP = 0, DORY_KV_LAST_LOOP = 1 } dory_kv_mode;
 
+/* Storage of the layer projections (q|k|v|gate, o, up/gate, down).
+ * DORY_WEIGHTS_DTYPE: the config's dtype. DORY_WEIGHTS_MXFP8 (bfloat16
+ * models): the OCP Microscaling (MX) v1.0 MXFP8 format, our reading of the
+ * MXFP8 checkpoints the pages name ("Dory1.0-4B: A Looped Normalized-GPT", AI
+ * summary, Key Contributions 4): E4M3 element codes [N][K] (one byte each)
+ * and one E8M0 scale byte per block of 32 consecutive elements along K,
+ * [N][K/32]; element code q of block scale byte s stands for
+ * e4m3(q) * 2^(s - 127). The embedding / LM head stays in the dtype. */
+typedef enum { DORY_WEIGHTS_DTYPE = 0, DORY_WEIGHTS_MXFP8 = 1 } dory_weight_format;
+
 /* Model shape and capacity. Copied by dory_create (layer_is_full included). */
 typedef struct {
   int32_t d_model;        /* residual-stream width d                                  */
@@ -83,6 +93,8 @@ typedef struct {
                              the matrix cores when max_ctx and window are multiples of 4) */
   int32_t max_chunk;      /* positions per prefill chunk (longer prompts are chunked)  */
   int32_t max_loops;      /* largest n_loops accepted                                  */
+  int32_t weight_format;  /* dory_weight_format of the layer projections; MXFP8 needs
+                             bfloat16 and d_model, n_q*hd and d_ff multiples of 32      */
 } dory_config;
 
 /* Weights, all device pointers, row-major, of the config's dtype except alpha.
@@ -95,7 +107,10 @@ typedef struct {
  *   ug    [2*d_ff, d]                      rows 0..d_ff-1: u, rows d_ff..: v;
  *                                          the activation is u * silu(v)
  *   down  [d, d_ff]                        MLP down projection
- *   alpha_attn, alpha_mlp: float32 [d]     per-channel nGPT update weights   */
+ *   alpha_attn, alpha_mlp: float32 [d]     per-channel nGPT update weights
+ * With DORY_WEIGHTS_MXFP8, qkvg / o / ug / down hold the element codes and
+ * qkvg_scale / o_scale / ug_scale / down_scale the scale bytes (NULL
+ * otherwise); codes 16-byte aligned. */
 typedef struct {
   const void* embed;
   const void* const* qkvg;
@@ -104,6 +119,10 @@ typedef struct {
   const void* const* down;
   const float* const* alpha_attn;
   const float* const* alpha_mlp;
+  const void* const* qkvg_scale;
+  const void* const* o_scale;
+  const void* const* ug_scale;
+  const void* const* down_scale;
 } dory_weights;
 
 typedef struct dory_ctx dory_ctx;
@@ -258,6 +277,20 @@ dory_status dory_op_linear(int32_t dtype, const void* x, int64_t ldx, const void
 /* out[b] = argmax_v logits[b, v] (lowest index on ties); logits device float32
  * [B, V], out device int32 [B]. scratch_dev: device, >= dory_argmax_scratch_bytes. */
 size_t dory_argmax_scratch_bytes(int32_t B, int32_t V);
+
+/* MXFP8 encoding of a bfloat16 matrix w_dev [N][K] (K % 32 == 0, 16-byte
+ * aligned) into codes_dev [N][K] and scales_dev [N][K/32] (see
+ * dory_weight_format): block scale X = floor(log2(max |w|)) - 8 (an all-zero
+ * block takes X = -127), codes round w / 2^X to the nearest E4M3 value, ties
+ * to the even code, saturating at 448. Enqueued on stream. */
+dory_status dory_op_quant_mxfp8(const void* w_dev, int32_t N, int32_t K, void* codes_dev, void* scales_dev,
+                                void* stream);
+
+/* y = x . W^T with MXFP8 weights (codes, scales) for M <= 8 rows (the decode
+ * kernel); arguments as dory_op_linear (bfloat16 x, epilogue 0: float32 y * scale,
+ * 1: SwiGLU to bfloat16). K % 32 == 0; DORY_E_ARG otherwise. */
+dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, const void* scales, void* y,
+                              int32_t M, int32_t N, int32_t K, int32_t epilogue, float scale, void* stream);
 dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out,
                            void* scratch_dev, void* stream);
 

@@ -35,7 +35,8 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 # every function dory.h declares, for the export check
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
-           "dory_decode_step", "dory_resume", "dory_prefill_mixed", "dory_decode_step_mixed", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
+           "dory_decode_step", "dory_resume", "dory_prefill_mixed", "dory_decode_step_mixed", "dory_op_quant_mxfp8",
+           "dory_op_linear_mx", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax"]
@@ -51,14 +52,16 @@ class DoryConfig(ctypes.Structure):
                 ("attn_scale", ctypes.c_float), ("logit_scale", ctypes.c_float),
                 ("combine_wh", ctypes.c_float), ("combine_we", ctypes.c_float),
                 ("max_batch", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("max_chunk", ctypes.c_int32),
-                ("max_loops", ctypes.c_int32)]
+                ("max_loops", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 class DoryWeights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("qkvg", ctypes.POINTER(ctypes.c_void_p)),
                 ("o", ctypes.POINTER(ctypes.c_void_p)), ("ug", ctypes.POINTER(ctypes.c_void_p)),
                 ("down", ctypes.POINTER(ctypes.c_void_p)), ("alpha_attn", ctypes.POINTER(ctypes.c_void_p)),
-                ("alpha_mlp", ctypes.POINTER(ctypes.c_void_p))]
+                ("alpha_mlp", ctypes.POINTER(ctypes.c_void_p)),
+                ("qkvg_scale", ctypes.POINTER(ctypes.c_void_p)), ("o_scale", ctypes.POINTER(ctypes.c_void_p)),
+                ("ug_scale", ctypes.POINTER(ctypes.c_void_p)), ("down_scale", ctypes.POINTER(ctypes.c_void_p))]
 
 
 _P = ctypes.c_void_p
@@ -84,6 +87,8 @@ _sig = {
     "dory_resume": (_I, [_P, _I, _I, _I, _I]),
     "dory_prefill_mixed": (_I, [_P, _P, _I, _I, _P, _I]),
     "dory_decode_step_mixed": (_I, [_P, _P, _P, _I, _P]),
+    "dory_op_quant_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
+    "dory_op_linear_mx": (_I, [_P, ctypes.c_int64, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P]),
     "dory_set_kernel_timing": (_I, [_P, _I, _I]),
     "dory_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]),
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
@@ -107,7 +112,12 @@ def lib():
     return _lib
 
 
-def make_config(model, *, max_batch: int, max_ctx: int, max_chunk: int, max_loops: int = 8):
+WEIGHTS_DTYPE, WEIGHTS_MXFP8 = 0, 1
+PROJECTIONS = ("qkvg", "o", "ug", "down")
+
+
+def make_config(model, *, max_batch: int, max_ctx: int, max_chunk: int, max_loops: int = 8,
+                weight_format: int = 0):
     """dory_config for a synth.ModelConfig. Returns (struct, keepalive)."""
     full = (ctypes.c_uint8 * model.n_layers)(*[1 if f else 0 for f in model.layer_is_full])
     c = DoryConfig(
@@ -118,7 +128,8 @@ def make_config(model, *, max_batch: int, max_ctx: int, max_chunk: int, max_loop
         dtype=DORY_F32 if model.dtype == "f32" else DORY_BF16, attn_gate=model.attn_gate,
         attn_scale=float(model.attn_scale or 0.0), logit_scale=float(model.logit_scale or 0.0),
         combine_wh=model.combine_wh, combine_we=model.combine_we,
-        max_batch=max_batch, max_ctx=max_ctx, max_chunk=max_chunk, max_loops=max_loops)
+        max_batch=max_batch, max_ctx=max_ctx, max_chunk=max_chunk, max_loops=max_loops,
+        weight_format=weight_format)
     return c, full
 
 
@@ -171,17 +182,35 @@ def upload_weights(model, weights: Dict, device="cuda") -> Dict:
     return out
 
 
+def quantize_weights_mxfp8(model, dev_weights: Dict, stream=None) -> Dict:
+    """bfloat16 device weights -> a dict whose layer projections are MXFP8 codes
+    (uint8 [N, K]) with scales under "<name>_scale" (uint8 [N, K/32]); the rest is shared."""
+    import torch
+    out = dict(dev_weights)
+    for l in range(model.n_layers):
+        for p in PROJECTIONS:
+            w = dev_weights[f"L{l}.{p}"]
+            N, K = w.shape
+            q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+            s = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+            op_quant_mxfp8(w, N, K, q, s, stream=stream)
+            out[f"L{l}.{p}"] = q
+            out[f"L{l}.{p}_scale"] = s
+    return out
+
+
 class Session:
     """One dory_ctx with its KV buffer and workspace (torch-allocated)."""
 
     def __init__(self, model, dev_weights: Dict, *, max_batch: int = 1, max_ctx: int = 1024,
                  max_chunk: Optional[int] = None, max_loops: int = 8, kv_mode: str = "last_loop",
-                 kv_loops: int = 1, stream=None, device="cuda"):
+                 kv_loops: int = 1, stream=None, device="cuda", weight_format: int = 0):
         import torch
         self.model = model
         self.device = torch.device(device)
         self.cfg, self._keep = make_config(model, max_batch=max_batch, max_ctx=max_ctx,
-                                           max_chunk=max_chunk or max_ctx, max_loops=max_loops)
+                                           max_chunk=max_chunk or max_ctx, max_loops=max_loops,
+                                           weight_format=weight_format)
         s = validate_config(self.cfg)
         if s != DORY_OK:
             raise DoryError(s, "invalid config")
@@ -198,10 +227,15 @@ class Session:
         arr = lambda kind: (ctypes.c_void_p * L)(*[_ptr(dev_weights[f"L{l}.{kind}"]) for l in range(L)])
         self._arrays = {k: arr(k) for k in ("qkvg", "o", "ug", "down", "alpha_a", "alpha_m")}
         vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        if weight_format == WEIGHTS_MXFP8:
+            for k in PROJECTIONS:
+                self._arrays[k + "_scale"] = arr(k + "_scale")
+        sc = (lambda k: vp(self._arrays[k + "_scale"])) if weight_format == WEIGHTS_MXFP8 else (lambda k: None)
         self.wstruct = DoryWeights(embed=_ptr(dev_weights["embed"]), qkvg=vp(self._arrays["qkvg"]),
                                    o=vp(self._arrays["o"]), ug=vp(self._arrays["ug"]),
                                    down=vp(self._arrays["down"]), alpha_attn=vp(self._arrays["alpha_a"]),
-                                   alpha_mlp=vp(self._arrays["alpha_m"]))
+                                   alpha_mlp=vp(self._arrays["alpha_m"]), qkvg_scale=sc("qkvg"), o_scale=sc("o"),
+                                   ug_scale=sc("ug"), down_scale=sc("down"))
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
         s = _lib.dory_create(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _ptr(self.kv), kvb, self.kv_mode,
@@ -292,6 +326,20 @@ def op_linear(dtype: int, x, W, y, M: int, N: int, K: int, *, ldx: Optional[int]
                             scale, algo, _stream_handle(stream))
     if s != DORY_OK:
         raise DoryError(s, "dory_op_linear")
+
+
+def op_quant_mxfp8(w, N: int, K: int, codes, scales, stream=None) -> None:
+    s = _lib.dory_op_quant_mxfp8(_ptr(w), N, K, _ptr(codes), _ptr(scales), _stream_handle(stream))
+    if s != DORY_OK:
+        raise DoryError(s, "dory_op_quant_mxfp8")
+
+
+def op_linear_mx(x, codes, scales, y, M: int, N: int, K: int, *, ldx: Optional[int] = None, epilogue: int = 0,
+                 scale: float = 1.0, stream=None) -> None:
+    s = _lib.dory_op_linear_mx(_ptr(x), ldx if ldx is not None else K, _ptr(codes), _ptr(scales), _ptr(y), M, N, K,
+                               epilogue, scale, _stream_handle(stream))
+    if s != DORY_OK:
+        raise DoryError(s, "dory_op_linear_mx")
 
 
 def op_argmax(logits, out, scratch, stream=None) -> None:

@@ -14,19 +14,9 @@
 // and stores u * silu(v) in the model dtype.
 #include "common.h"
 #include "kernels.h"
+#include "linear_common.h"
 
 namespace dory {
-
-enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
-
-__device__ __forceinline__ float silu_(float v) { return v / (1.0f + expf(-v)); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-  // v_dot2c_f32_bf16: c + a.lo * b.lo + a.hi * b.hi in float32, no unpacking
-  return __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2_t*)&a, *(const bf16x2_t*)&b, c, false);
-}
 
 // acc + <w, x> over 8 bfloat16 pairs
 __device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, const bf16*, float acc) {

@@ -149,6 +149,20 @@ hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, in
                              hipStream_t st);
 bool linear_pro_supported(int M, int K);
 
+// MXFP8 weights (OCP MX, E4M3 elements, blocks of 32 along K, E8M0 scale
+// bytes): codes [N][K] bytes and scales [N][K/32] bytes per projection.
+// quant: bfloat16 [N][K] -> codes + scales; dequant: the reverse (exact).
+hipError_t launch_quant_mxfp8(const void* W_bf16, int N, int K, void* q, void* s, hipStream_t st);
+hipError_t launch_dequant_mxfp8(const void* q, const void* s, int N, int K, void* W_bf16, hipStream_t st);
+// Decode GEMV y = x . dequant(W)^T (M <= 8, K % 32 == 0), epilogues as launch_linear.
+hipError_t launch_linear_mx(const void* x, int64_t ldx, const void* Wq, const void* Ws, void* y, int M, int N, int K,
+                            int epi, float scale, hipStream_t st);
+bool linear_mx_supported(int M, int K);
+// launch_linear_pro for MXFP8 weights.
+hipError_t launch_linear_pro_mx(const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N, int K,
+                                int epi, float scale, hipStream_t st);
+bool linear_pro_mx_supported(int M, int K);
+
 // Greedy argmax; if pos_dev is not NULL the final pass also advances the
 // device position counter by one (the end of a decode step).
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st,

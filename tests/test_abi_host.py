@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "dory.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dory_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dory_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_match_header():
@@ -94,15 +94,32 @@ def test_capacity_configs():
     assert dory.kv_bytes(c, dory.DORY_KV_PER_LOOP, 3) == 0                 # more caches than max_loops
 
 
+def test_weight_format_configs():
+    """MXFP8 projections need a bfloat16 model whose contraction widths are
+    multiples of 32; the workspace grows by one expanded projection."""
+    m = small(dtype="bf16", d_ff=704)
+    base, _k1 = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16)
+    mx, _k2 = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, weight_format=dory.WEIGHTS_MXFP8)
+    assert dory.validate_config(base) == dory.DORY_OK and dory.validate_config(mx) == dory.DORY_OK
+    qkvg_dim = 2 * m.q_dim + 2 * m.kv_dim
+    biggest = max(qkvg_dim * m.d_model, m.d_model * m.q_dim, 2 * m.d_ff * m.d_model) * 2
+    assert biggest <= dory.workspace_bytes(mx) - dory.workspace_bytes(base) < biggest + 512
+    for bad in (small(dtype="bf16", d_ff=688), small(dtype="f32", d_ff=704)):
+        c, _k = dory.make_config(bad, max_batch=1, max_ctx=16, max_chunk=16, weight_format=dory.WEIGHTS_MXFP8)
+        assert dory.validate_config(c) == dory.DORY_E_ARG
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, weight_format=2)
+    assert dory.validate_config(c) == dory.DORY_E_ARG
+
+
 class FakeCtx:
     """A context bound to fake, aligned device addresses: only the validation
     paths (which return before any HIP call) may be exercised with it."""
 
     def __init__(self, model, *, kv_mode="last_loop", kv_loops=1, max_batch=2, max_ctx=16, max_loops=4,
-                 kv_bytes=None, ws_bytes=None, kv_addr=1 << 20, ws_addr=1 << 30):
+                 kv_bytes=None, ws_bytes=None, kv_addr=1 << 20, ws_addr=1 << 30, weight_format=0):
         L = model.n_layers
         self.c, self._k = dory.make_config(model, max_batch=max_batch, max_ctx=max_ctx, max_chunk=8,
-                                           max_loops=max_loops)
+                                           max_loops=max_loops, weight_format=weight_format)
         arrs = [(ctypes.c_void_p * L)(*[(1 << 16) * (l + 1) for l in range(L)]) for _ in range(6)]
         self._arrs = arrs
         vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
@@ -124,6 +141,8 @@ class FakeCtx:
 def test_create_validation():
     m = small()
     assert FakeCtx(m).status == dory.DORY_OK
+    # MXFP8 projections without their scale arrays
+    assert FakeCtx(small(dtype="bf16", d_ff=704), weight_format=dory.WEIGHTS_MXFP8).status == dory.DORY_E_ARG
     assert FakeCtx(m, kv_bytes=100).status == dory.DORY_E_ARG
     assert FakeCtx(m, ws_bytes=100).status == dory.DORY_E_ARG
     assert FakeCtx(m, kv_addr=(1 << 20) + 8).status == dory.DORY_E_ARG

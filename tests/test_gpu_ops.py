@@ -88,3 +88,69 @@ def test_argmax_ties_and_specials():
     dory.op_argmax(_dev(L), out, scratch)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), np.argmax(L, axis=1))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 weights: the device quantiser byte for byte against the oracle's
+# (OCP MX reading), and the decode GEMV against a float64 product with the
+# oracle's dequantised weights
+# ---------------------------------------------------------------------------
+def test_quant_mxfp8_bit_exact():
+    from oracle import mxfp8
+    rng = np.random.default_rng(21)
+    N, K = 96, 256
+    w = (rng.standard_normal((N, K)) * np.exp(rng.uniform(-9, 4, (N, 1)))).astype(np.float32)
+    w[3, 32:64] = 0.0                                           # zero block
+    w[4, :32] = -0.0                                            # negative zeros
+    w[5, :32] = 0.0
+    w[5, 0], w[5, 1] = 1e-30, -3e-31                            # tiny block scale
+    w[6, :32] = (1.0 + 1.0 / 16 + np.arange(32) % 7 / 8.0) / 256.0  # E4M3 ties after the 2^8 scaling
+    w[6, 31] = 1.0                                              # amax 1.0 -> X = -8
+    w[7, :32] = 0.01
+    w[7, 0] = 1.9375                                            # 496 after scaling: saturates
+    w[8, :32] = 0.0
+    w[8, 0] = 2.0 ** -130                                       # subnormal block max: X clamped to -127
+    wb = f32_to_bf16_bits(w)
+    q_ref, s_ref = mxfp8.quantize(bf16_bits_to_f32(wb).astype(np.float64))
+    q = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((N, K // 32), dtype=torch.uint8, device="cuda")
+    dory.op_quant_mxfp8(_dev(wb), N, K, q, sc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+MX_CASES = [(1, 8192, 3072, 0), (1, 2 * 8192, 3072, 1), (3, 1000, 2304, 0), (5, 2 * 1000, 2304, 1),
+            (1, 3072, 8192, 0), (8, 704, 256, 0), (2, 2 * 704, 256, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,epi", MX_CASES)
+def test_linear_mx(M, N, K, epi):
+    from oracle import mxfp8
+    rng = np.random.default_rng(M * 131 + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+    xs = f32_to_bf16_bits(x)
+    x64 = bf16_bits_to_f32(xs).astype(np.float64)
+    q, sc = mxfp8.quantize(bf16_bits_to_f32(f32_to_bf16_bits(W)).astype(np.float64))
+    W64 = mxfp8.dequantize(q, sc)
+    scale = 1.7 if epi == 0 else 1.0
+    ref = (x64 @ W64.T) * scale
+    if epi == 1:
+        F = N // 2
+        ref = ref[:, :F] * ref[:, F:] / (1.0 + np.exp(-ref[:, F:]))
+        y = torch.zeros((M, F), dtype=torch.int16, device="cuda")
+    else:
+        y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    print(f"linear mx M={M} N={N} K={K} epi={epi}", flush=True)
+    dory.op_linear_mx(_dev(xs), _dev(q), _dev(sc), y, M, N, K, epilogue=epi, scale=scale)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if epi == 1:
+        got = bf16_bits_to_f32(got.view(np.uint16)).astype(np.float64)
+        tol = np.abs(ref) * 2.0 ** -8 + 1e-4
+    else:
+        tol = 2e-5 * math.sqrt(K) * scale
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"max err {err.max()}"
+

@@ -39,6 +39,8 @@ def model_and_weights(name):
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, name="tiny_bf16")
         elif name == "tiny_bf16_w60":  # a window that is not a multiple of 8 (per-key value gathers)
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, window=60, name="tiny_bf16_w60")
+        elif name == "tiny_mx":       # the tiny shape in bfloat16 with MXFP8-compatible widths (multiples of 32)
+            m = get_config("tiny").replace(dtype="bf16", d_ff=704, name="tiny_mx")
         elif name == "c36w_w192":     # the c36w weights with 192-key rings that wrap
             m0, w, dw = model_and_weights("c36w")
             _cache[name] = (m0.replace(window=192, name="c36w_w192"), w, dw)
@@ -254,6 +256,40 @@ def test_mixed_loop_counts_match_separate_sequences(name, tol):
         s.decode_mixed(torch.from_numpy(forced[i]).cuda(), ks)
         got.append(s.logits().cpu().numpy())
     assert _report(f"{name} mixed loop counts", np.stack(got), ref) <= tol
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 layer projections: the oracle runs on its own quantise-dequantise of
+# the weights (exactly bfloat16 values); the library quantises on the device
+# and decodes with the MXFP8 GEMVs (prefill expands each projection to
+# bfloat16 and takes the GEMM)
+# ---------------------------------------------------------------------------
+def _mx_oracle_weights(m, w):
+    from oracle import mxfp8
+    from synth.gen import bf16_bits_to_f32, f32_to_bf16_bits
+    out = dict(w)
+    for l in range(m.n_layers):
+        for p in ("qkvg", "o", "ug", "down"):
+            q, sc = mxfp8.quantize(bf16_bits_to_f32(w[f"L{l}.{p}"]).astype(np.float64))
+            out[f"L{l}.{p}"] = f32_to_bf16_bits(mxfp8.dequantize(q, sc).astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("name,k,mode,n,steps,ctx", [("tiny_mx", 2, "last_loop", 100, 16, 160),
+                                                     ("tiny_mx", 3, "per_loop", 70, 8, 96),
+                                                     ("c36w", 2, "last_loop", 64, 8, 96)])
+def test_mxfp8_weights_generate(name, k, mode, n, steps, ctx):
+    m, w, dw = model_and_weights(name)
+    prompt = make_tokens(m, 50, (1, n))
+    ora = LoopedNGPT(m, _mx_oracle_weights(m, w), max_ctx=ctx)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode)
+    dq = dory.quantize_weights_mxfp8(m, dw)
+    s = dory.Session(m, dq, max_batch=1, max_ctx=ctx, max_chunk=n, max_loops=8, kv_mode=mode,
+                     kv_loops=k if mode == "per_loop" else 1, weight_format=dory.WEIGHTS_MXFP8)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"{name} MXFP8 {mode} k={k}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
 
 
 # ---------------------------------------------------------------------------
