@@ -29,10 +29,12 @@ MFMA_PEAK = 2.5e15         # FLOP/s, MI355X dense bf16 matrix cores
 METRIC = "decode tokens/s @ k=1,2,4 (last-loop KV) + % of HBM roofline, 1×MI355X"
 
 
-def decode_bytes(m, k, ctx_mean, B=1):
+def decode_bytes(m, k, ctx_mean, B=1, mxfp8=False):
     """Algorithmic HBM bytes of one decode step: every weight once (the
     recurrent block k times), the tied LM head, each layer application's K/V
-    reads over its window and its one-position K/V write, per sequence."""
+    reads over its window and its one-position K/V write, per sequence.
+    mxfp8: the layer projections are stored as one E4M3 byte per weight plus
+    one scale byte per 32 weights (the LM head stays bfloat16)."""
     el = 2
     apps_full, apps_swa = 0, 0
     for l in range(m.n_layers):
@@ -42,7 +44,8 @@ def decode_bytes(m, k, ctx_mean, B=1):
         else:
             apps_swa += reps
     per_key = 2 * m.n_kv_heads * m.head_dim * el
-    weights = (m.n_in + m.n_out + k * m.n_rec) * m.layer_bytes() + m.vocab * m.d_model * el
+    layer = m.layer_bytes() // 2 * 33 // 32 if mxfp8 else m.layer_bytes()
+    weights = (m.n_in + m.n_out + k * m.n_rec) * layer + m.vocab * m.d_model * el
     kv_read = B * per_key * (apps_full * ctx_mean + apps_swa * min(ctx_mean, m.window))
     kv_write = B * per_key * (apps_full + apps_swa)
     return weights + kv_read + kv_write
@@ -71,11 +74,13 @@ def ug_traffic():
                       + UG_TRAFFIC["write_kib"] * UG_TRAFFIC["write_factor"]) * 1024))
 
 
-def ug_bytes(m, B=1):
+def ug_bytes(m, B=1, mxfp8=False):
     """Algorithmic bytes of one SwiGLU up/gate projection launch (B rows): the
-    two weight matrices, the prologue's inputs (sublayer output y, residual h,
-    alpha; float32) and outputs (new residual, float32; activation, bf16)."""
-    return 2 * m.d_ff * m.d_model * 2 + B * m.d_model * 4 * 3 + B * m.d_model * 4 + B * m.d_ff * 2
+    two weight matrices (bfloat16, or E4M3 codes plus one scale byte per 32),
+    the prologue's inputs (sublayer output y, residual h, alpha; float32) and
+    outputs (new residual, float32; activation, bf16)."""
+    wb = 2 * m.d_ff * m.d_model * 33 // 32 if mxfp8 else 2 * m.d_ff * m.d_model * 2
+    return wb + B * m.d_model * 4 * 3 + B * m.d_model * 4 + B * m.d_ff * 2
 
 
 def attn_flops(m, k, n):
@@ -247,6 +252,59 @@ def run_other(args, dev):
                            "mfma_frac_whole": round(fl / (pms / 1e3) / MFMA_PEAK, 4)}})
         return
 
+    if args.workload == "mxfp8":
+        model = CONFIGS["c36"]["model"]
+        n = args.prompt
+        w = make_weights_device(model, dev)
+        wq = dory.quantize_weights_mxfp8(model, w, stream=stream)
+        for key in [x for x in w if x.split(".")[-1] in dory.PROJECTIONS]:
+            del w[key]                       # the bfloat16 projections are not used from here on
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        g = torch.Generator(device="cpu")
+        g.manual_seed(model.seed * 7 + 1)
+        prompt = torch.randint(0, model.vocab, (1, n), generator=g, dtype=torch.int32).to(dev)
+        max_ctx = (n + Wm + K + args.kernel_steps + 2 + 255) // 256 * 256
+        sess = dory.Session(model, wq, max_batch=1, max_ctx=max_ctx, max_chunk=n, kv_mode="last_loop",
+                            stream=stream, device=dev, weight_format=dory.WEIGHTS_MXFP8)
+        table, roof = {}, None
+        for k in (1, 2, 4):
+            sess.reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sess.prefill(prompt, k)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1)
+            ms = _timed_decode(sess, 1, k, K, Wm)
+            step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0, mxfp8=True)
+            table[f"k={k}"] = {"tokens_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+                               "hbm_frac": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4),
+                               "bytes_per_step": step_bytes, "prefill_ms": round(pms, 1)}
+            log(f"k={k}: {1e3 / ms:.1f} tok/s, HBM {100 * table[f'k={k}']['hbm_frac']:.1f}%, prefill {pms:.0f} ms")
+            if k == 2 and args.kernel_steps > 0:
+                apps = model.n_in + model.n_out + k * model.n_rec
+                sess.set_kernel_timing("ug", args.kernel_steps * apps)
+                for _ in range(args.kernel_steps):
+                    sess.decode(None, k)
+                tot, cnt = sess.kernel_time()
+                sess.set_kernel_timing(None)
+                ug_ms = tot / max(cnt, 1)
+                ach = ug_bytes(model, mxfp8=True) / (ug_ms / 1e3)
+                roof = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK, 4), "traffic": None,
+                        "kernel": "k_gemv_pro_mx<1,3,SwiGLU> (MXFP8 up/gate projection with the nGPT update "
+                                  "prologue, M=1, N=2x8192, K=3072)",
+                        "bytes_per_launch": ug_bytes(model, mxfp8=True), "avg_launch_us": round(ug_ms * 1e3, 2)}
+                log(f"MXFP8 up/gate GEMV: {cnt} launches, {ug_ms * 1e3:.1f} us avg, {100 * roof['frac']:.1f}% HBM")
+        hk = table["k=2"]
+        _line(f"{model.name} with MXFP8 layer projections (E4M3, 32-element blocks), batch 1, {n}-token random "
+              "prompt, greedy decode at k=1,2,4, last-loop KV (headline value: k=2)", hk["tokens_per_s"],
+              hk["ms_per_step"], 1, K, Wm, n, 2, "last_loop", {"by_k": table, "roofline": roof,
+                                                                "dtype": "bf16 activations, MXFP8 weights"})
+        return
+
     # b64: 64 sequences whose 32768 cached positions are synthetic: random
     # bfloat16 values written straight into the caller-owned KV buffer, then
     # dory_resume (decode throughput does not depend on cache contents)
@@ -318,10 +376,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
-    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long"], default="c36",
+    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8"], default="c36",
                     help="c36: the headline (default). c72: the 72-layer shape, 16384-token prompt, k=1..4 in "
                          "both KV modes. b64: 64 sequences at 32768 cached positions (synthetic caches), k=4, "
-                         "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2")
+                         "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2. mxfp8: the c36 shape with "
+                         "MXFP8 layer projections, decode at k=1,2,4")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
