@@ -60,14 +60,21 @@ typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype;
 typedef enum { DORY_KV_PER_LOOP = 0, DORY_KV_LAST_LOOP = 1 } dory_kv_mode;
 
 /* Storage of the layer projections (q|k|v|gate, o, up/gate, down).
- * DORY_WEIGHTS_DTYPE: the config's dtype. DORY_WEIGHTS_MXFP8 (bfloat16
- * models): the OCP Microscaling (MX) v1.0 MXFP8 format, our reading of the
- * MXFP8 checkpoints the pages name ("Dory1.0-4B: A Looped Normalized-GPT", AI
- * summary, Key Contributions 4): E4M3 element codes [N][K] (one byte each)
- * and one E8M0 scale byte per block of 32 consecutive elements along K,
- * [N][K/32]; element code q of block scale byte s stands for
- * e4m3(q) * 2^(s - 127). The embedding / LM head stays in the dtype. */
-typedef enum { DORY_WEIGHTS_DTYPE = 0, DORY_WEIGHTS_MXFP8 = 1 } dory_weight_format;
+ * DORY_WEIGHTS_DTYPE: the config's dtype. The low-bit formats (bfloat16
+ * models) are our readings of the MXFP8 and NVFP4 checkpoints the pages name
+ * ("Dory1.0-4B: A Looped Normalized-GPT", AI summary, Key Contributions 4 and
+ * Methodology in Plain English):
+ * DORY_WEIGHTS_MXFP8: the OCP Microscaling (MX) v1.0 MXFP8 format, E4M3
+ * element codes [N][K] (one byte each) and one E8M0 scale byte per block of
+ * 32 consecutive elements along K, [N][K/32]; element code q of block scale
+ * byte s stands for e4m3(q) * 2^(s - 127).
+ * DORY_WEIGHTS_NVFP4: E2M1 element codes, two per byte with the even element
+ * in the low nibble, [N][K/2]; one E4M3 scale byte (a positive finite E4M3
+ * value, codes 1..126) per block of 16 consecutive elements along K,
+ * [N][K/16]; one float32 scale g per tensor; code q of block scale s stands
+ * for e2m1(q) * e4m3(s) * g.
+ * The embedding / LM head stays in the dtype. */
+typedef enum { DORY_WEIGHTS_DTYPE = 0, DORY_WEIGHTS_MXFP8 = 1, DORY_WEIGHTS_NVFP4 = 2 } dory_weight_format;
 
 /* Model shape and capacity. Copied by dory_create (layer_is_full included). */
 typedef struct {
@@ -93,8 +100,9 @@ typedef struct {
                              the matrix cores when max_ctx and window are multiples of 4) */
   int32_t max_chunk;      /* positions per prefill chunk (longer prompts are chunked)  */
   int32_t max_loops;      /* largest n_loops accepted                                  */
-  int32_t weight_format;  /* dory_weight_format of the layer projections; MXFP8 needs
-                             bfloat16 and d_model, n_q*hd and d_ff multiples of 32      */
+  int32_t weight_format;  /* dory_weight_format of the layer projections; MXFP8 and NVFP4
+                             need bfloat16, d_model <= 8192 and d_model, n_q*hd and
+                             d_ff multiples of 32                                     */
 } dory_config;
 
 /* Weights, all device pointers, row-major, of the config's dtype except alpha.
@@ -108,9 +116,12 @@ typedef struct {
  *                                          the activation is u * silu(v)
  *   down  [d, d_ff]                        MLP down projection
  *   alpha_attn, alpha_mlp: float32 [d]     per-channel nGPT update weights
- * With DORY_WEIGHTS_MXFP8, qkvg / o / ug / down hold the element codes and
- * qkvg_scale / o_scale / ug_scale / down_scale the scale bytes (NULL
- * otherwise); codes 16-byte aligned. */
+ * With a low-bit weight_format, qkvg / o / ug / down hold the element codes
+ * (16-byte aligned) and qkvg_scale / o_scale / ug_scale / down_scale the
+ * block scale bytes (NULL otherwise; 2-byte aligned for NVFP4); with
+ * DORY_WEIGHTS_NVFP4, qkvg_tscale / o_tscale / ug_tscale / down_tscale are
+ * HOST arrays of n_layers float32 tensor scales (copied by dory_create;
+ * NULL otherwise). */
 typedef struct {
   const void* embed;
   const void* const* qkvg;
@@ -123,6 +134,10 @@ typedef struct {
   const void* const* o_scale;
   const void* const* ug_scale;
   const void* const* down_scale;
+  const float* qkvg_tscale;
+  const float* o_tscale;
+  const float* ug_tscale;
+  const float* down_tscale;
 } dory_weights;
 
 typedef struct dory_ctx dory_ctx;
@@ -266,8 +281,8 @@ dory_status dory_kernel_time(dory_ctx* ctx, double* total_ms, int32_t* launches)
 
 /* y = x . W^T on the stream. x [M, ldx-strided rows of K], W [N, K] (dtype),
  * epilogue 0: y float32 [M, N] scaled by `scale`;
- * epilogue 1: SwiGLU, N = 2*F: y (dtype) [M, F] = u * silu(v), u = cols 0..F-1,
- *             v = cols F..2F-1.
+ * epilogue 1: SwiGLU, N = 2*F: y (dtype) [M, F] = u * silu(v), u = scale times
+ *             cols 0..F-1, v = scale times cols F..2F-1.
  * algo 0 picks by M, 1 forces the matrix-vector kernel (M <= 8), 2 the tiled
  * matrix kernel. */
 dory_status dory_op_linear(int32_t dtype, const void* x, int64_t ldx, const void* W, void* y,
@@ -291,6 +306,25 @@ dory_status dory_op_quant_mxfp8(const void* w_dev, int32_t N, int32_t K, void* c
  * 1: SwiGLU to bfloat16). K % 32 == 0; DORY_E_ARG otherwise. */
 dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, const void* scales, void* y,
                               int32_t M, int32_t N, int32_t K, int32_t epilogue, float scale, void* stream);
+
+/* NVFP4 encoding (DORY_WEIGHTS_NVFP4) of a bfloat16 matrix w_dev [N][K]
+ * (K % 32 == 0, 16-byte aligned) into codes_dev [N][K/2] (8-byte aligned),
+ * scales_dev [N][K/16] and the tensor scale *tscale_dev (one device float32):
+ * g = float32(max |w| / 2688) (1 for an all-zero matrix); for every block the
+ * E4M3 scale 1..126 of least squared error (the pages' dynamic MSE scale
+ * selection, "Dory1.0-4B: A Looped Normalized-GPT", AI summary, Methodology in
+ * Plain English), computed in float64 in element order so that the choice is
+ * reproducible, the smallest code on equal errors; elements rounded to the
+ * nearest E2M1 magnitude of |w| / (e4m3 * g), ties to the even code,
+ * saturating at 6, sign from w. Enqueued on stream (four kernels). */
+dory_status dory_op_quant_nvfp4(const void* w_dev, int32_t N, int32_t K, void* codes_dev, void* scales_dev,
+                                float* tscale_dev, void* stream);
+
+/* y = x . W^T with NVFP4 weights (codes, block scales) for M <= 8 rows (the
+ * decode kernel); the tensor scale g is not read here: pass scale = g (times
+ * any other factor). Otherwise as dory_op_linear_mx; scales 2-byte aligned. */
+dory_status dory_op_linear_fp4(const void* x, int64_t ldx, const void* codes, const void* scales, void* y,
+                               int32_t M, int32_t N, int32_t K, int32_t epilogue, float scale, void* stream);
 dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out,
                            void* scratch_dev, void* stream);
 

@@ -36,7 +36,7 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
            "dory_decode_step", "dory_resume", "dory_prefill_mixed", "dory_decode_step_mixed", "dory_op_quant_mxfp8",
-           "dory_op_linear_mx", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
+           "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax"]
@@ -61,7 +61,9 @@ class DoryWeights(ctypes.Structure):
                 ("down", ctypes.POINTER(ctypes.c_void_p)), ("alpha_attn", ctypes.POINTER(ctypes.c_void_p)),
                 ("alpha_mlp", ctypes.POINTER(ctypes.c_void_p)),
                 ("qkvg_scale", ctypes.POINTER(ctypes.c_void_p)), ("o_scale", ctypes.POINTER(ctypes.c_void_p)),
-                ("ug_scale", ctypes.POINTER(ctypes.c_void_p)), ("down_scale", ctypes.POINTER(ctypes.c_void_p))]
+                ("ug_scale", ctypes.POINTER(ctypes.c_void_p)), ("down_scale", ctypes.POINTER(ctypes.c_void_p)),
+                ("qkvg_tscale", ctypes.POINTER(ctypes.c_float)), ("o_tscale", ctypes.POINTER(ctypes.c_float)),
+                ("ug_tscale", ctypes.POINTER(ctypes.c_float)), ("down_tscale", ctypes.POINTER(ctypes.c_float))]
 
 
 _P = ctypes.c_void_p
@@ -89,6 +91,8 @@ _sig = {
     "dory_decode_step_mixed": (_I, [_P, _P, _P, _I, _P]),
     "dory_op_quant_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
     "dory_op_linear_mx": (_I, [_P, ctypes.c_int64, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "dory_op_quant_nvfp4": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "dory_op_linear_fp4": (_I, [_P, ctypes.c_int64, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P]),
     "dory_set_kernel_timing": (_I, [_P, _I, _I]),
     "dory_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]),
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
@@ -112,7 +116,7 @@ def lib():
     return _lib
 
 
-WEIGHTS_DTYPE, WEIGHTS_MXFP8 = 0, 1
+WEIGHTS_DTYPE, WEIGHTS_MXFP8, WEIGHTS_NVFP4 = 0, 1, 2
 PROJECTIONS = ("qkvg", "o", "ug", "down")
 
 
@@ -199,6 +203,30 @@ def quantize_weights_mxfp8(model, dev_weights: Dict, stream=None) -> Dict:
     return out
 
 
+def quantize_weights_nvfp4(model, dev_weights: Dict, stream=None) -> Dict:
+    """bfloat16 device weights -> a dict whose layer projections are NVFP4
+    codes (uint8 [N, K/2]) with block scales under "<name>_scale" (uint8
+    [N, K/16]) and the tensor scale under "<name>_tscale" (a Python float, read
+    back from the device); the rest is shared."""
+    import torch
+    out = dict(dev_weights)
+    for l in range(model.n_layers):
+        for p in PROJECTIONS:
+            w = dev_weights[f"L{l}.{p}"]
+            N, K = w.shape
+            q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+            s = torch.empty((N, K // 16), dtype=torch.uint8, device=w.device)
+            g = torch.empty(1, dtype=torch.float32, device=w.device)
+            op_quant_nvfp4(w, N, K, q, s, g, stream=stream)
+            out[f"L{l}.{p}"] = q
+            out[f"L{l}.{p}_scale"] = s
+            out[f"L{l}.{p}_tscale"] = g
+    torch.cuda.synchronize()
+    for key in [k for k in out if k.endswith("_tscale")]:
+        out[key] = float(out[key].item())
+    return out
+
+
 class Session:
     """One dory_ctx with its KV buffer and workspace (torch-allocated)."""
 
@@ -227,15 +255,23 @@ class Session:
         arr = lambda kind: (ctypes.c_void_p * L)(*[_ptr(dev_weights[f"L{l}.{kind}"]) for l in range(L)])
         self._arrays = {k: arr(k) for k in ("qkvg", "o", "ug", "down", "alpha_a", "alpha_m")}
         vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
-        if weight_format == WEIGHTS_MXFP8:
+        lowbit = weight_format in (WEIGHTS_MXFP8, WEIGHTS_NVFP4)
+        if lowbit:
             for k in PROJECTIONS:
                 self._arrays[k + "_scale"] = arr(k + "_scale")
-        sc = (lambda k: vp(self._arrays[k + "_scale"])) if weight_format == WEIGHTS_MXFP8 else (lambda k: None)
+        if weight_format == WEIGHTS_NVFP4:
+            for k in PROJECTIONS:
+                self._arrays[k + "_tscale"] = (ctypes.c_float * L)(
+                    *[float(dev_weights[f"L{l}.{k}_tscale"]) for l in range(L)])
+        sc = (lambda k: vp(self._arrays[k + "_scale"])) if lowbit else (lambda k: None)
+        ts = ((lambda k: ctypes.cast(self._arrays[k + "_tscale"], ctypes.POINTER(ctypes.c_float)))
+              if weight_format == WEIGHTS_NVFP4 else (lambda k: None))
         self.wstruct = DoryWeights(embed=_ptr(dev_weights["embed"]), qkvg=vp(self._arrays["qkvg"]),
                                    o=vp(self._arrays["o"]), ug=vp(self._arrays["ug"]),
                                    down=vp(self._arrays["down"]), alpha_attn=vp(self._arrays["alpha_a"]),
                                    alpha_mlp=vp(self._arrays["alpha_m"]), qkvg_scale=sc("qkvg"), o_scale=sc("o"),
-                                   ug_scale=sc("ug"), down_scale=sc("down"))
+                                   ug_scale=sc("ug"), down_scale=sc("down"), qkvg_tscale=ts("qkvg"),
+                                   o_tscale=ts("o"), ug_tscale=ts("ug"), down_tscale=ts("down"))
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
         s = _lib.dory_create(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _ptr(self.kv), kvb, self.kv_mode,
@@ -332,6 +368,20 @@ def op_quant_mxfp8(w, N: int, K: int, codes, scales, stream=None) -> None:
     s = _lib.dory_op_quant_mxfp8(_ptr(w), N, K, _ptr(codes), _ptr(scales), _stream_handle(stream))
     if s != DORY_OK:
         raise DoryError(s, "dory_op_quant_mxfp8")
+
+
+def op_quant_nvfp4(w, N: int, K: int, codes, scales, tscale, stream=None) -> None:
+    s = _lib.dory_op_quant_nvfp4(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(tscale), _stream_handle(stream))
+    if s != DORY_OK:
+        raise DoryError(s, "dory_op_quant_nvfp4")
+
+
+def op_linear_fp4(x, codes, scales, y, M: int, N: int, K: int, *, ldx: Optional[int] = None, epilogue: int = 0,
+                  scale: float = 1.0, stream=None) -> None:
+    s = _lib.dory_op_linear_fp4(_ptr(x), ldx if ldx is not None else K, _ptr(codes), _ptr(scales), _ptr(y), M, N,
+                                K, epilogue, scale, _stream_handle(stream))
+    if s != DORY_OK:
+        raise DoryError(s, "dory_op_linear_fp4")
 
 
 def op_linear_mx(x, codes, scales, y, M: int, N: int, K: int, *, ldx: Optional[int] = None, epilogue: int = 0,

@@ -22,7 +22,8 @@ struct dory_ctx {
   KvLayout kv;
   const void* embed = nullptr;
   std::vector<const void*> qkvg, o, ug, down;
-  std::vector<const void*> qkvg_s, o_s, ug_s, down_s;  // MXFP8 scale bytes (nullptr otherwise)
+  std::vector<const void*> qkvg_s, o_s, ug_s, down_s;  // low-bit block scales (nullptr otherwise)
+  std::vector<float> qkvg_g, o_g, ug_g, down_g;         // NVFP4 tensor scales (1 otherwise)
   std::vector<const float*> alpha_attn, alpha_mlp;
   char* kvb = nullptr;
   char* ws = nullptr;
@@ -107,26 +108,29 @@ dory_status set_err(dory_ctx* c, dory_status s, const std::string& msg) {
 // y = x . W^T for one layer projection. MXFP8 weights: the decode GEMV for
 // M <= 8 rows, otherwise the projection is first expanded to bfloat16 in the
 // workspace and multiplied by the bfloat16 GEMM.
-dory_status proj(dory_ctx* c, const void* W, const void* S, const void* x, int64_t ldx, void* y, int M, int N, int K,
-                 int epi, float scale) {
+dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void* x, int64_t ldx, void* y, int M,
+                 int N, int K, int epi, float scale) {
   const Plan& P = c->plan;
   const int dt = P.cfg.dtype;
-  if (P.cfg.weight_format != DORY_WEIGHTS_MXFP8) {
+  const int fmt = P.cfg.weight_format;
+  if (fmt == DORY_WEIGHTS_DTYPE) {
     HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
-  } else if (linear_mx_supported(M, K)) {
-    HIP_TRY(c, launch_linear_mx(x, ldx, W, S, y, M, N, K, epi, scale, c->st));
+  } else if (linear_lowbit_supported(fmt, M, K)) {
+    HIP_TRY(c, launch_linear_lowbit(fmt, x, ldx, W, S, y, M, N, K, epi, scale * g, c->st));
   } else {
     void* wdq = c->ws + P.ws.wdq;
-    HIP_TRY(c, launch_dequant_mxfp8(W, S, N, K, wdq, c->st));
-    HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale, 0, c->st));
+    HIP_TRY(c, launch_dequant_lowbit(fmt, W, S, N, K, wdq, c->st));
+    HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale * g, 0, c->st));
   }
   return DORY_OK;
 }
 
-// The decode GEMV with the nGPT update in its prologue, for either weight format.
-dory_status proj_pro(dory_ctx* c, const GemvPro& p, const void* W, const void* S, void* y, int M, int N, int K, int epi) {
-  if (c->plan.cfg.weight_format == DORY_WEIGHTS_MXFP8)
-    HIP_TRY(c, launch_linear_pro_mx(p, W, S, y, M, N, K, epi, 1.f, c->st));
+// The decode GEMV with the nGPT update in its prologue, for any weight format.
+dory_status proj_pro(dory_ctx* c, const GemvPro& p, const void* W, const void* S, float g, void* y, int M, int N,
+                     int K, int epi) {
+  const int fmt = c->plan.cfg.weight_format;
+  if (fmt != DORY_WEIGHTS_DTYPE)
+    HIP_TRY(c, launch_linear_pro_lowbit(fmt, p, W, S, y, M, N, K, epi, g, c->st));
   else
     HIP_TRY(c, launch_linear_pro(p, W, y, M, N, K, epi, 1.f, c->st));
   return DORY_OK;
@@ -173,7 +177,7 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
 
   {
     TimeScope ts(c, TIME_QKVG);
-    DORY_TRY(proj(c, c->qkvg[l], c->qkvg_s[l], xb, C.d_model, qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f));
+    DORY_TRY(proj(c, c->qkvg[l], c->qkvg_s[l], c->qkvg_g[l], xb, C.d_model, qkvg, rows, P.qkvg_dim, C.d_model, 0, 1.f));
   }
 
   if (n == 1) {
@@ -218,16 +222,16 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
 
   {
     TimeScope ts(c, TIME_O);
-    DORY_TRY(proj(c, c->o[l], c->o_s[l], c->ws + W.ob, P.q_dim, y, rows, C.d_model, P.q_dim, 0, 1.f));
+    DORY_TRY(proj(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, rows, C.d_model, P.q_dim, 0, 1.f));
   }
   HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st, gate));
   {
     TimeScope ts(c, TIME_UG);
-    DORY_TRY(proj(c, c->ug[l], c->ug_s[l], xb, C.d_model, c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f));
+    DORY_TRY(proj(c, c->ug[l], c->ug_s[l], c->ug_g[l], xb, C.d_model, c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f));
   }
   {
     TimeScope ts(c, TIME_DOWN);
-    DORY_TRY(proj(c, c->down[l], c->down_s[l], c->ws + W.a, C.d_ff, y, rows, C.d_model, C.d_ff, 0, 1.f));
+    DORY_TRY(proj(c, c->down[l], c->down_s[l], c->down_g[l], c->ws + W.a, C.d_ff, y, rows, C.d_model, C.d_ff, 0, 1.f));
   }
   HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st, gate));
   if (c->trace)
@@ -282,8 +286,8 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
 // buffers so the workgroup writing the new one never races readers of the old.
 bool fused_decode_ok(const dory_ctx* c, int B) {
   const dory_config& C = c->plan.cfg;
-  const bool pro_ok = C.weight_format == DORY_WEIGHTS_MXFP8 ? linear_pro_mx_supported(B, C.d_model)
-                                                          : linear_pro_supported(B, C.d_model);
+  const bool pro_ok = C.weight_format != DORY_WEIGHTS_DTYPE ? linear_pro_lowbit_supported(C.weight_format, B, C.d_model)
+                                                           : linear_pro_supported(B, C.d_model);
   return C.dtype == DORY_BF16 && !c->trace && !c->mixed && C.n_rec >= 1 && pro_ok;
 }
 
@@ -313,29 +317,29 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
       pr.h_out = alt;
       pr.e_out = (first_rec && j == 1) ? e : nullptr;
       TimeScope ts(c, TIME_QKVG);
-      DORY_TRY(proj_pro(c, pr, c->qkvg[l], c->qkvg_s[l], qkvg, B, P.qkvg_dim, d, 0));
+      DORY_TRY(proj_pro(c, pr, c->qkvg[l], c->qkvg_s[l], c->qkvg_g[l], qkvg, B, P.qkvg_dim, d, 0));
       std::swap(cur, alt);
     } else {
       TimeScope ts(c, TIME_QKVG);
-      DORY_TRY(proj(c, c->qkvg[l], c->qkvg_s[l], xb, d, qkvg, B, P.qkvg_dim, d, 0, 1.f));
+      DORY_TRY(proj(c, c->qkvg[l], c->qkvg_s[l], c->qkvg_g[l], xb, d, qkvg, B, P.qkvg_dim, d, 0, 1.f));
     }
     dory_status s = decode_attention(c, l, j, B, write_kv);
     if (s != DORY_OK) return s;
     {
       TimeScope ts(c, TIME_O);
-      DORY_TRY(proj(c, c->o[l], c->o_s[l], c->ws + W.ob, P.q_dim, y, B, d, P.q_dim, 0, 1.f));
+      DORY_TRY(proj(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, B, d, P.q_dim, 0, 1.f));
     }
     {
       GemvPro pr{};
       pr.y = y; pr.h_in = cur; pr.alpha = c->alpha_attn[l];
       pr.h_out = alt;
       TimeScope ts(c, TIME_UG);
-      DORY_TRY(proj_pro(c, pr, c->ug[l], c->ug_s[l], c->ws + W.a, B, 2 * C.d_ff, d, 1));
+      DORY_TRY(proj_pro(c, pr, c->ug[l], c->ug_s[l], c->ug_g[l], c->ws + W.a, B, 2 * C.d_ff, d, 1));
       std::swap(cur, alt);
     }
     {
       TimeScope ts(c, TIME_DOWN);
-      DORY_TRY(proj(c, c->down[l], c->down_s[l], c->ws + W.a, C.d_ff, y, B, d, C.d_ff, 0, 1.f));
+      DORY_TRY(proj(c, c->down[l], c->down_s[l], c->down_g[l], c->ws + W.a, C.d_ff, y, B, d, C.d_ff, 0, 1.f));
     }
     pending_alpha = c->alpha_mlp[l];
     return DORY_OK;
@@ -600,11 +604,20 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, void* kv_
     c->o.push_back(w->o[l]);
     c->ug.push_back(w->ug[l]);
     c->down.push_back(w->down[l]);
-    if (P.cfg.weight_format == DORY_WEIGHTS_MXFP8) {
+    const int fmt = P.cfg.weight_format;
+    if (fmt != DORY_WEIGHTS_DTYPE) {
       const bool have = w->qkvg_scale && w->o_scale && w->ug_scale && w->down_scale;
-      const bool ok = have && w->qkvg_scale[l] && w->o_scale[l] && w->ug_scale[l] && w->down_scale[l] &&
-                      !((uintptr_t)w->qkvg[l] & 15) && !((uintptr_t)w->o[l] & 15) &&
-                      !((uintptr_t)w->ug[l] & 15) && !((uintptr_t)w->down[l] & 15);
+      bool ok = have && w->qkvg_scale[l] && w->o_scale[l] && w->ug_scale[l] && w->down_scale[l] &&
+                !((uintptr_t)w->qkvg[l] & 15) && !((uintptr_t)w->o[l] & 15) &&
+                !((uintptr_t)w->ug[l] & 15) && !((uintptr_t)w->down[l] & 15);
+      if (ok && fmt == DORY_WEIGHTS_NVFP4) {
+        ok = w->qkvg_tscale && w->o_tscale && w->ug_tscale && w->down_tscale &&
+             !((uintptr_t)w->qkvg_scale[l] & 1) && !((uintptr_t)w->o_scale[l] & 1) &&
+             !((uintptr_t)w->ug_scale[l] & 1) && !((uintptr_t)w->down_scale[l] & 1);
+        if (ok)
+          for (float g : {w->qkvg_tscale[l], w->o_tscale[l], w->ug_tscale[l], w->down_tscale[l]})
+            ok = ok && std::isfinite(g) && g > 0.f;
+      }
       if (!ok) {
         delete c;
         return DORY_E_ARG;
@@ -619,6 +632,11 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, void* kv_
       c->ug_s.push_back(nullptr);
       c->down_s.push_back(nullptr);
     }
+    const bool fp4 = fmt == DORY_WEIGHTS_NVFP4;
+    c->qkvg_g.push_back(fp4 ? w->qkvg_tscale[l] : 1.f);
+    c->o_g.push_back(fp4 ? w->o_tscale[l] : 1.f);
+    c->ug_g.push_back(fp4 ? w->ug_tscale[l] : 1.f);
+    c->down_g.push_back(fp4 ? w->down_tscale[l] : 1.f);
     c->alpha_attn.push_back(w->alpha_attn[l]);
     c->alpha_mlp.push_back(w->alpha_mlp[l]);
   }
@@ -896,8 +914,27 @@ dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, con
   if (!x || !codes || !scales || !y || M < 1 || M > 8 || N < 1 || K < 32 || K % 32 || ldx < K) return DORY_E_ARG;
   if (epilogue != 0 && epilogue != 1) return DORY_E_ARG;
   if (epilogue == 1 && N % 2) return DORY_E_ARG;
-  if (!linear_mx_supported(M, K)) return DORY_E_ARG;
-  hipError_t e = launch_linear_mx(x, ldx, codes, scales, y, M, N, K, epilogue, scale, (hipStream_t)stream);
+  if (!linear_lowbit_supported(DORY_WEIGHTS_MXFP8, M, K)) return DORY_E_ARG;
+  hipError_t e = launch_linear_lowbit(DORY_WEIGHTS_MXFP8, x, ldx, codes, scales, y, M, N, K, epilogue, scale,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? DORY_OK : (e == hipErrorInvalidValue ? DORY_E_ARG : DORY_E_HIP);
+}
+
+dory_status dory_op_quant_nvfp4(const void* w_dev, int32_t N, int32_t K, void* codes_dev, void* scales_dev,
+                                float* tscale_dev, void* stream) {
+  if (!w_dev || !codes_dev || !scales_dev || !tscale_dev || N < 0 || K < 32 || K % 32) return DORY_E_ARG;
+  hipError_t e = launch_quant_nvfp4(w_dev, N, K, codes_dev, scales_dev, tscale_dev, (hipStream_t)stream);
+  return e == hipSuccess ? DORY_OK : (e == hipErrorInvalidValue ? DORY_E_ARG : DORY_E_HIP);
+}
+
+dory_status dory_op_linear_fp4(const void* x, int64_t ldx, const void* codes, const void* scales, void* y,
+                               int32_t M, int32_t N, int32_t K, int32_t epilogue, float scale, void* stream) {
+  if (!x || !codes || !scales || !y || M < 1 || M > 8 || N < 1 || K < 32 || K % 32 || ldx < K) return DORY_E_ARG;
+  if (epilogue != 0 && epilogue != 1) return DORY_E_ARG;
+  if (epilogue == 1 && N % 2) return DORY_E_ARG;
+  if (!linear_lowbit_supported(DORY_WEIGHTS_NVFP4, M, K)) return DORY_E_ARG;
+  hipError_t e = launch_linear_lowbit(DORY_WEIGHTS_NVFP4, x, ldx, codes, scales, y, M, N, K, epilogue, scale,
+                                      (hipStream_t)stream);
   return e == hipSuccess ? DORY_OK : (e == hipErrorInvalidValue ? DORY_E_ARG : DORY_E_HIP);
 }
 

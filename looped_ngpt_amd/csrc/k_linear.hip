@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64
       const float s = wave_sum(acc[m][r]);
       if (EPI == EPI_SWIGLU) {
         const float g = wave_sum(acc[m][ROWS + r]);
-        if (lane == 0 && o0 + r < nout) ((T*)y)[(size_t)m * nout + o0 + r] = from_f<T>(s * silu_(g));
+        if (lane == 0 && o0 + r < nout) ((T*)y)[(size_t)m * nout + o0 + r] = from_f<T>(s * scale * silu_(g * scale));
       } else {
         if (lane == 0 && o0 + r < nout) ((float*)y)[(size_t)m * N + o0 + r] = s * scale;
       }
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
     const float s = wave_sum(acc[m][0]);
     if (EPI == EPI_SWIGLU) {
       const float g = wave_sum(acc[m][NR - 1]);
-      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
+      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * scale * silu_(g * scale));
     } else {
       if (lane == 0) ((float*)y)[(size_t)m * N + o] = s * scale;
     }
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
       const float s = wave_sum(acc[m][r]);
       if (EPI == EPI_SWIGLU) {
         const float g = wave_sum(acc[m][R + r]);
-        if (lane == 0 && o < nout) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * silu_(g));
+        if (lane == 0 && o < nout) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(s * scale * silu_(g * scale));
       } else {
         if (lane == 0 && o < nout) ((float*)y)[(size_t)m * N + o] = s * scale;
       }
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(256) void k_gemv_scalar(const T* __restrict__ x, in
   if (EPI == EPI_SWIGLU) s1 = wave_sum(s1);
   if (lane == 0) {
     if (EPI == EPI_SWIGLU)
-      ((T*)y)[(size_t)m * nout + o] = from_f<T>(s0 * silu_(s1));
+      ((T*)y)[(size_t)m * nout + o] = from_f<T>(s0 * scale * silu_(s1 * scale));
     else
       ((float*)y)[(size_t)m * N + o] = s0 * scale;
   }
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, i
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
         const int o = n0 + wn * 32 + lr;
-        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * silu_(acc[i][1][r]));
+        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * scale * silu_(acc[i][1][r] * scale));
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
         const int o = n0 + wn * 32 + l32;
-        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * silu_(acc[i][1][r]));
+        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * scale * silu_(acc[i][1][r] * scale));
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const T* __restrict__ A, in
       const int col = n0 + tx * 4 + j;
       if (col >= nout) continue;
       if (EPI == EPI_SWIGLU)
-        ((T*)C)[(size_t)row * nout + col] = from_f<T>(acc[0][i][j] * silu_(acc[1][i][j]));
+        ((T*)C)[(size_t)row * nout + col] = from_f<T>(acc[0][i][j] * scale * silu_(acc[1][i][j] * scale));
       else
         ((float*)C)[(size_t)row * N + col] = acc[0][i][j] * scale;
     }

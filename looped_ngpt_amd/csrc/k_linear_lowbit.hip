@@ -1,0 +1,710 @@
+// Low-bit weights for the layer projections, two formats.
+//
+// MXFP8: the OCP Microscaling (MX) v1.0 format with E4M3 elements, blocks of
+// 32 consecutive weights of an output row along the contraction dimension K,
+// one E8M0 scale byte per block (X + 127, the block standing for
+// e4m3(q) * 2^X). The pages name MXFP8 checkpoints of the model ("Dory1.0-4B:
+// A Looped Normalized-GPT", AI summary, Key Contributions 4) without defining
+// the format; this is the published definition.
+//
+// NVFP4-style: E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives), two
+// per byte with the even element in the low nibble, blocks of 16 along K with
+// one E4M3 scale byte each, and one float32 scale g per tensor: code q of
+// block scale s stands for e2m1(q) * e4m3(s) * g. The pages say the NVFP4
+// checkpoints choose each block scale by least squared error over the 126
+// positive E4M3 values (same page, Methodology in Plain English); the search
+// below tries all of them.
+//
+//  * k_quant_mxfp8: bfloat16 [N][K] -> codes [N][K] + scales [N][K/32];
+//    X = floor(log2(max |w|)) - 8, all-zero blocks X = -127; elements
+//    rounded to nearest, ties to the even code, saturating at 448.
+//  * k_absmax / k_quant_nvfp4 / k_tensor_scale: tensor amax, then per block
+//    the least-error E4M3 scale (float64, fixed order of operations, so the
+//    choice is reproducible), the codes, and g in place of the amax.
+//  * k_dequant: codes -> bfloat16 for the prefill GEMM (MXFP8: exact while
+//    X >= -124; NVFP4: e2m1 * e4m3 without g, always exact; the GEMM applies g).
+//  * k_gemv_rows_lb / k_gemv_pro_lb: the decode GEMVs of k_linear.hip for
+//    these weights. A lane takes 16-byte chunks of codes (16 E4M3 or 32 E2M1);
+//    the hardware converts them (v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly,
+//    v_perm_b32 repacks the floats' high halves into bfloat16 pairs;
+//    v_cvt_scalef32_pk_bf16_fp4 with scale 1 gives E2M1 pairs as bfloat16),
+//    v_dot2_f32_bf16 multiplies them with the activations, and each block's
+//    partial sum takes its scale once.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+#include "linear_common.h"
+
+namespace dory {
+namespace {
+
+// E8M0 byte -> 2^(byte - 127) as a float (byte 0 is the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// E4M3 code of v = w / 2^X (|v| < 512, exact), the sign taken from w
+__device__ __forceinline__ uint32_t e4m3_code(float w, float v) {
+  const uint32_t sign = (__float_as_uint(w) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;                                   // saturate
+  } else if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);              // subnormal steps of 2^-9; 8 is the smallest normal
+  } else {
+    int e;
+    (void)frexpf(a, &e);
+    const int E = e - 1;                            // floor(log2 a), -6..8
+    const float m = rintf((ldexpf(a, -E) - 1.f) * 8.f);
+    code = (uint32_t)((E + 7) << 3) + (uint32_t)m;  // m == 8 carries into the next binade
+  }
+  return code | sign;
+}
+
+__global__ __launch_bounds__(256) void k_quant_mxfp8(const bf16* __restrict__ W, uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ s, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4* src = (const u32x4*)(W + b * 32);
+  u32x4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = src[i];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[i][j])), fabsf(bf_hi(w[i][j]))));
+  int X = -127;
+  if (amax > 0.f) {
+    int e;
+    (void)frexpf(amax, &e);
+    X = min(max(e - 1 - 8, -127), 127);
+  }
+  uint32_t words[8];  // element 2k, 2k+1 of the block -> bytes 2k, 2k+1
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf_lo(w[i][j]), hi = bf_hi(w[i][j]);
+      const uint32_t pair = e4m3_code(lo, ldexpf(lo, -X)) | (e4m3_code(hi, ldexpf(hi, -X)) << 8);
+      const int k = 4 * i + j;  // pair index 0..15 inside the block
+      if (k & 1)
+        words[k >> 1] |= pair << 16;
+      else
+        words[k >> 1] = pair;
+    }
+  const u32x4 out[2] = {u32x4{words[0], words[1], words[2], words[3]}, u32x4{words[4], words[5], words[6], words[7]}};
+  u32x4* dst = (u32x4*)(q + b * 32);
+  dst[0] = out[0];
+  dst[1] = out[1];
+  s[b] = (uint8_t)(X + 127);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4-style quantiser
+// ---------------------------------------------------------------------------
+__global__ void k_zero_word(uint32_t* p) { *p = 0u; }
+
+// max |w| over n bfloat16 values into *amax_bits (float bits of a
+// non-negative value order like unsigned integers)
+__global__ __launch_bounds__(256) void k_absmax(const bf16* __restrict__ W, int64_t n, uint32_t* amax_bits) {
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(to_f(W[i])));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
+}
+
+// g = float32(amax / 2688), 1 for an all-zero tensor. The float64 quotient
+// rounded to float32 equals the correctly rounded float32 quotient: amax has
+// at most 24 significant bits and 2688 = 21 * 2^7, so the exact quotient is
+// either a float32 rounding midpoint itself or at least 2^-5 of a float32
+// half-step away from one, far more than the float64 rounding error.
+__device__ __forceinline__ float tensor_scale_of(uint32_t amax_bits) {
+  const float amax = __uint_as_float(amax_bits);
+  return amax > 0.f ? (float)((double)amax / 2688.0) : 1.0f;
+}
+
+// E4M3 value of a positive finite code 1..126 (exact in float64)
+__device__ __forceinline__ double e4m3_pos_value(int c) {
+  const int e = c >> 3, m = c & 7;
+  return e ? ldexp(1.0 + m * 0.125, e - 7) : ldexp((double)m, -9);
+}
+
+// One thread per block of 16 weights: every E4M3 scale 1..126 is tried with
+// S = e4m3 * g; each |w| rounds to the nearest E2M1 magnitude of |w| / S
+// (ties to the even code, saturating at 6) by comparing |w| with S times the
+// midpoints, all exact in float64; the error sum runs in element order with
+// separate multiply and add (no contraction), so the choice is reproducible.
+// The least error wins, the smallest code on equal errors.
+__global__ __launch_bounds__(256) void k_quant_nvfp4(const bf16* __restrict__ W, uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ s, const uint32_t* __restrict__ amax_bits,
+                                                     int64_t nblocks) {
+#pragma clang fp contract(off)
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const double g = (double)tensor_scale_of(*amax_bits);
+  const u32x4* src = (const u32x4*)(W + b * 16);
+  const u32x4 w0 = src[0], w1 = src[1];
+  uint32_t raw[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  double a[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[2 * i] = (double)fabsf(bf_lo(raw[i]));
+    a[2 * i + 1] = (double)fabsf(bf_hi(raw[i]));
+  }
+  constexpr double kMid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  constexpr double kMag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double best_err = 0.0;
+  int best = 1;
+  for (int c = 1; c <= 126; ++c) {
+    const double S = e4m3_pos_value(c) * g;
+    double T[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) T[j] = S * kMid[j];
+    double err = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      double m = 0.0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        const bool up = (j & 1) ? (a[i] >= T[j]) : (a[i] > T[j]);  // ties go to the even index
+        m = up ? kMag[j + 1] : m;
+      }
+      const double e = a[i] - m * S;
+      const double e2 = e * e;
+      err = err + e2;
+    }
+    if (c == 1 || err < best_err) {
+      best_err = err;
+      best = c;
+    }
+  }
+  const double S = e4m3_pos_value(best) * g;
+  uint32_t packed = 0, packed2 = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t idx = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const double t = S * kMid[j];
+      idx += (j & 1) ? (a[i] >= t) : (a[i] > t);
+    }
+    const uint32_t sign = ((i & 1) ? (raw[i >> 1] >> 31) : ((raw[i >> 1] >> 15) & 1u)) << 3;
+    const uint32_t code = idx | sign;
+    if (i < 8)
+      packed |= code << (4 * i);
+    else
+      packed2 |= code << (4 * (i - 8));
+  }
+  uint32_t* dst = (uint32_t*)(q + b * 8);
+  dst[0] = packed;
+  dst[1] = packed2;
+  s[b] = (uint8_t)best;
+}
+
+__global__ void k_tensor_scale(uint32_t* amax_bits) { *(float*)amax_bits = tensor_scale_of(*amax_bits); }
+
+// ---------------------------------------------------------------------------
+// Expansion to bfloat16 for the prefill GEMM
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dequant_mxfp8(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                       bf16* __restrict__ W, int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 codes per chunk
+  if (c >= nchunks) return;
+  const u32x4 v = ((const u32x4*)q)[c];
+  const float sc = e8m0_value(s[c >> 1]);
+  u32x4 out[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], true);
+    const uint32_t a = __float_as_uint(f01[0] * sc), b2 = __float_as_uint(f01[1] * sc);
+    const uint32_t c2 = __float_as_uint(f23[0] * sc), d = __float_as_uint(f23[1] * sc);
+    out[i >> 1][(i & 1) * 2] = (a >> 16) | (b2 & 0xffff0000u);
+    out[i >> 1][(i & 1) * 2 + 1] = (c2 >> 16) | (d & 0xffff0000u);
+  }
+  u32x4* dst = (u32x4*)(W + c * 16);
+  dst[0] = out[0];
+  dst[1] = out[1];
+}
+
+// E2M1 pairs of byte `sel` of w as bfloat16 pairs (exact)
+#define DORY_FP4_PAIR(w, sel) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((w), 1.0f, (sel)))
+
+__global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                       bf16* __restrict__ W, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 codes (8 bytes) per block
+  if (b >= nblocks) return;
+  const uint32_t* src = (const uint32_t*)(q + b * 8);
+  const float sc = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)s[b], false)[0];
+  u32x4 out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t v = src[h];
+    const uint32_t p[4] = {DORY_FP4_PAIR(v, 0), DORY_FP4_PAIR(v, 1), DORY_FP4_PAIR(v, 2), DORY_FP4_PAIR(v, 3)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // e2m1 * e4m3 has at most 6 significant bits: exact in bfloat16
+      out[h][j] = (__float_as_uint(bf_lo(p[j]) * sc) >> 16) | (__float_as_uint(bf_hi(p[j]) * sc) & 0xffff0000u);
+  }
+  u32x4* dst = (u32x4*)(W + b * 16);
+  dst[0] = out[0];
+  dst[1] = out[1];
+}
+
+// ---------------------------------------------------------------------------
+// Decode GEMVs
+// ---------------------------------------------------------------------------
+enum { LB_MX = 1, LB_FP4 = 2 };  // the dory_weight_format values
+
+template <int FMT> struct LowBit;
+
+template <> struct LowBit<LB_MX> {
+  static constexpr int kCodes = 16;  // weights per 16-byte chunk
+  __device__ static size_t row_bytes(int K) { return (size_t)K; }
+  // scale bits of chunk v of a row: its block's E8M0 byte
+  __device__ static uint32_t scale_bits(const uint8_t* Ws, size_t row, int K, int v) {
+    return Ws[row * (size_t)(K / 32) + v / 2];
+  }
+  // <16 E4M3 weights, 16 bfloat16 activations of xm> * 2^X + acc
+  __device__ static float dot(const u32x4& w, const u32x4* xm, int v, uint32_t sb, float acc) {
+    const u32x4 x0 = xm[2 * v], x1 = xm[2 * v + 1];
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+      // high halves of the floats are their exact bfloat16 values
+      const uint32_t p01 = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
+      const uint32_t p23 = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+      const u32x4& xv = i < 2 ? x0 : x1;
+      part = dot2bf(p01, xv[(i & 1) * 2], part);
+      part = dot2bf(p23, xv[(i & 1) * 2 + 1], part);
+    }
+    return fmaf(part, e8m0_value(sb), acc);
+  }
+};
+
+template <> struct LowBit<LB_FP4> {
+  static constexpr int kCodes = 32;
+  __device__ static size_t row_bytes(int K) { return (size_t)(K / 2); }
+  // the two E4M3 scale bytes of the chunk's blocks 2v, 2v+1
+  __device__ static uint32_t scale_bits(const uint8_t* Ws, size_t row, int K, int v) {
+    return *(const uint16_t*)(Ws + row * (size_t)(K / 16) + 2 * v);
+  }
+  // <32 E2M1 weights, 32 bfloat16 activations of xm>, block by block scaled, + acc
+  __device__ static float dot(const u32x4& w, const u32x4* xm, int v, uint32_t sb, float acc) {
+    const auto sc = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+    float p[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // word i: elements 8i..8i+7, block i / 2
+      const u32x4 xv = xm[4 * v + i];
+      float t = p[i >> 1];
+      t = dot2bf(DORY_FP4_PAIR(w[i], 0), xv[0], t);
+      t = dot2bf(DORY_FP4_PAIR(w[i], 1), xv[1], t);
+      t = dot2bf(DORY_FP4_PAIR(w[i], 2), xv[2], t);
+      t = dot2bf(DORY_FP4_PAIR(w[i], 3), xv[3], t);
+      p[i >> 1] = t;
+    }
+    return fmaf(p[1], sc[1], fmaf(p[0], sc[0], acc));
+  }
+};
+
+// One output (two rows for SwiGLU) per wave, activations staged in LDS, small
+// loads (activations, scale bits) issued before the weights.
+template <int FMT, int MB, int CQ, int EPI>
+__global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x, int64_t ldx,
+                                                     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
+                                                     void* __restrict__ y, int M, int N, int K, float scale) {
+  using F = LowBit<FMT>;
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* xs = (bf16*)smem;
+  const int nv = K / 8, nq = K / F::kCodes;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o = blockIdx.x * 8 + wave;
+  const bool live = o < nout;
+  const int oc = live ? o : nout - 1;
+
+  constexpr int XV = (MB * CQ * F::kCodes + 63) / 64;  // M rows x nv <= 8*CQ*kCodes vectors over 512 threads
+  u32x4 xr[XV];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + 512 * q;
+    const int ec = min(e, M * nv - 1);
+    xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
+  }
+  uint32_t sb[NR][CQ];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int row = j ? nout + oc : oc;
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) sb[j][c] = F::scale_bits(Ws, row, K, min(lane + 64 * c, nq - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  u32x4 wv[NR][CQ];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const u32x4* wr = (const u32x4*)(Wq + (size_t)(j ? nout + oc : oc) * F::row_bytes(K));
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) wv[j][c] = __builtin_nontemporal_load(wr + min(lane + 64 * c, nq - 1));
+  }
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + 512 * q;
+    if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float acc[MB][NR];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) {
+    const int v = lane + 64 * c;
+    if (v < nq) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < M) {
+          const u32x4* xm = (const u32x4*)(xs + (size_t)m * K);
+#pragma unroll
+          for (int j = 0; j < NR; ++j) acc[m][j] = F::dot(wv[j][c], xm, v, sb[j][c], acc[m][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= M) break;
+    const float sum = wave_sum(acc[m][0]) * scale;
+    if (EPI == EPI_SWIGLU) {
+      const float g = wave_sum(acc[m][NR - 1]) * scale;
+      if (lane == 0) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(sum * silu_(g));
+    } else {
+      if (lane == 0) ((float*)y)[(size_t)m * N + o] = sum;
+    }
+  }
+}
+
+// The GEMV with the nGPT update (and optional loop re-injection) in its
+// prologue, as k_gemv_pro of k_linear.hip: 1024-thread workgroups, two
+// outputs per wave, a rolling window of 8 weight chunks per lane.
+constexpr int kLbThreads = 1024;
+constexpr int kLbOut = 2;
+constexpr int kLbWin = 8;
+
+template <int FMT, int MB, int CQ, int EPI>
+__global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const uint8_t* __restrict__ Wq,
+                                                           const uint8_t* __restrict__ Ws, void* __restrict__ y,
+                                                           int M, int N, int K, float scale) {
+  using F = LowBit<FMT>;
+  constexpr int R = kLbOut;
+  constexpr int NR = (EPI == EPI_SWIGLU ? 2 : 1) * R;  // weight rows per wave
+  constexpr int NC = NR * CQ;                          // chunk loads per wave
+  constexpr int P = NC < kLbWin ? NC : kLbWin;
+  constexpr int NW = kLbThreads / 64;
+  constexpr int EPT = (CQ * F::kCodes * 64 + kLbThreads - 1) / kLbThreads;  // prologue elements per thread
+  __shared__ float sh[NW];
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* xs = (bf16*)smem;
+  const int nq = K / F::kCodes;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o0 = (blockIdx.x * NW + wave) * R;
+  const bool live = o0 < nout;
+
+  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU
+  auto wrow = [&](int j) { const int oc = min(o0 + j % R, nout - 1); return j >= R ? nout + oc : oc; };
+  auto chunk_ptr = [&](int c) -> const u32x4* {
+    const int v = min(lane + 64 * (c % CQ), nq - 1);  // clamped: chunks past the row are ignored below
+    return (const u32x4*)(Wq + (size_t)wrow(c / CQ) * F::row_bytes(K)) + v;
+  };
+
+  // prologue inputs of row 0 and the scale bits first, then the weight window
+  const float* ep = pr.e ? pr.e : pr.y;
+  float yv[EPT], hv[EPT], ev[EPT], av[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) {
+    const int i = min((int)threadIdx.x + kLbThreads * c, K - 1);
+    yv[c] = pr.y[i];
+    hv[c] = pr.h_in[i];
+    ev[c] = ep[i];
+    av[c] = pr.alpha[i];
+  }
+  uint32_t sb[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) sb[c] = F::scale_bits(Ws, wrow(c / CQ), K, min(lane + 64 * (c % CQ), nq - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 buf[P];
+#pragma unroll
+  for (int c = 0; c < P; ++c) buf[c] = __builtin_nontemporal_load(chunk_ptr(c));
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int m = 0; m < M; ++m) {
+    const size_t ro = (size_t)m * K;
+    if (m > 0) {
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        const int i = min((int)threadIdx.x + kLbThreads * c, K - 1);
+        yv[c] = pr.y[ro + i];
+        hv[c] = pr.h_in[ro + i];
+        ev[c] = ep[ro + i];
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      if ((int)threadIdx.x + kLbThreads * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
+      ss += yv[c] * yv[c];
+    }
+    const float iy = inv_norm(block_sum<kLbThreads>(ss, sh));
+    float st = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      const float al = (int)threadIdx.x + kLbThreads * c < K ? av[c] : 0.f;
+      hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
+      st += hv[c] * hv[c];
+    }
+    const float ih = inv_norm(block_sum<kLbThreads>(st, sh));
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
+    if (pr.e_out && blockIdx.x == 0) {
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        const int i = threadIdx.x + kLbThreads * c;
+        if (i < K) pr.e_out[ro + i] = hv[c];
+      }
+    }
+    if (pr.e) {
+      float sv = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) {
+        yv[c] = pr.wh * hv[c] + pr.we * ev[c];
+        sv += yv[c] * yv[c];
+      }
+      const float iv = inv_norm(block_sum<kLbThreads>(sv, sh));
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
+    }
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      const int i = threadIdx.x + kLbThreads * c;
+      if (i < K) {
+        xs[ro + i] = from_f<bf16>(hv[c]);
+        if (blockIdx.x == 0) pr.h_out[ro + i] = hv[c];
+      }
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float acc[MB][NR];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 w = buf[c % P];
+    if (c + P < NC) buf[c % P] = __builtin_nontemporal_load(chunk_ptr(c + P));
+    const int j = c / CQ, v = lane + 64 * (c % CQ);
+    if (v < nq) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < M) {
+          const u32x4* xm = (const u32x4*)(xs + (size_t)m * K);
+          acc[m][j] = F::dot(w, xm, v, sb[c], acc[m][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= M) break;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int o = o0 + r;
+      const float sum = wave_sum(acc[m][r]) * scale;
+      if (EPI == EPI_SWIGLU) {
+        const float g = wave_sum(acc[m][R + r]) * scale;
+        if (lane == 0 && o < nout) ((bf16*)y)[(size_t)m * nout + o] = from_f<bf16>(sum * silu_(g));
+      } else {
+        if (lane == 0 && o < nout) ((float*)y)[(size_t)m * N + o] = sum;
+      }
+    }
+  }
+}
+
+int chunks_per_lane(int fmt, int K) { return (K / (fmt == LB_MX ? 16 : 32) + 63) / 64; }
+
+// chunk counts per lane with an instantiation (rows: 1-6, 8, 12, 16; with the prologue: 1-6, 8)
+bool cq_ok(int cq, bool pro) { return (cq >= 1 && cq <= 6) || cq == 8 || (!pro && (cq == 12 || cq == 16)); }
+
+template <int FMT, int MB, int EPI>
+hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N,
+                          int K, float scale, hipStream_t st) {
+  const int cq = chunks_per_lane(FMT, K);
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const dim3 grid((nout + 7) / 8);
+  const size_t lds = (size_t)M * K * 2;
+  // M * K * 2 <= 64 KiB bounds K, hence the chunk counts worth instantiating
+  constexpr int kMaxCq = (32768 / MB / LowBit<FMT>::kCodes + 63) / 64;
+#define DORY_RLB(C)                                                                                                 \
+  case C:                                                                                                           \
+    if constexpr (C <= kMaxCq) {                                                                                    \
+      dory_launch((k_gemv_rows_lb<FMT, MB, C, EPI>), grid, dim3(512), (uint32_t)lds, st, x, ldx, Wq, Ws, y, M, N, K, \
+                  scale);                                                                                           \
+      break;                                                                                                        \
+    } else {                                                                                                        \
+      return hipErrorInvalidValue;                                                                                  \
+    }
+  switch (cq) {
+    DORY_RLB(1) DORY_RLB(2) DORY_RLB(3) DORY_RLB(4) DORY_RLB(5) DORY_RLB(6) DORY_RLB(8) DORY_RLB(12) DORY_RLB(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef DORY_RLB
+  return hipGetLastError();
+}
+
+template <int FMT, int MB, int EPI>
+hipError_t pro_lb_launch(const GemvPro& p, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N, int K,
+                         float scale, hipStream_t st) {
+  const int cq = chunks_per_lane(FMT, K);
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int per_block = kLbThreads / 64 * kLbOut;
+  const dim3 grid((nout + per_block - 1) / per_block);
+  const size_t lds = (size_t)M * K * 2;
+  constexpr int kMaxCq = (32768 / MB / LowBit<FMT>::kCodes + 63) / 64;
+#define DORY_PLB(C)                                                                                                  \
+  case C:                                                                                                            \
+    if constexpr (C <= kMaxCq) {                                                                                     \
+      dory_launch((k_gemv_pro_lb<FMT, MB, C, EPI>), grid, dim3(kLbThreads), (uint32_t)lds, st, p, Wq, Ws, y, M, N, K, \
+                  scale);                                                                                            \
+      break;                                                                                                         \
+    } else {                                                                                                         \
+      return hipErrorInvalidValue;                                                                                   \
+    }
+  switch (cq) {
+    DORY_PLB(1) DORY_PLB(2) DORY_PLB(3) DORY_PLB(4) DORY_PLB(5) DORY_PLB(6) DORY_PLB(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef DORY_PLB
+  return hipGetLastError();
+}
+
+bool lb_shape_ok(int fmt, int M, int K, const void* Wq, const void* Ws) {
+  if (fmt != LB_MX && fmt != LB_FP4) return false;
+  if (fmt == LB_FP4 && ((uintptr_t)Ws & 1)) return false;
+  return M >= 1 && M <= 8 && K % 32 == 0 && (size_t)M * K * 2 <= 64 * 1024 && ((uintptr_t)Wq & 15) == 0;
+}
+
+template <int FMT>
+hipError_t linear_lb(const void* x, int64_t ldx, const void* Wq, const void* Ws, void* y, int M, int N, int K,
+                     int epi, float scale, hipStream_t st) {
+  const bf16* xb = (const bf16*)x;
+  const uint8_t* q = (const uint8_t*)Wq;
+  const uint8_t* s = (const uint8_t*)Ws;
+#define DORY_LBM(E)                                                                         \
+  if (M == 1) return rows_lb_launch<FMT, 1, E>(xb, ldx, q, s, y, M, N, K, scale, st);       \
+  if (M == 2) return rows_lb_launch<FMT, 2, E>(xb, ldx, q, s, y, M, N, K, scale, st);       \
+  if (M <= 4) return rows_lb_launch<FMT, 4, E>(xb, ldx, q, s, y, M, N, K, scale, st);       \
+  return rows_lb_launch<FMT, 8, E>(xb, ldx, q, s, y, M, N, K, scale, st);
+  if (epi == EPI_SWIGLU) {
+    DORY_LBM(EPI_SWIGLU)
+  }
+  DORY_LBM(EPI_F32)
+#undef DORY_LBM
+}
+
+template <int FMT>
+hipError_t linear_pro_lb(const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N, int K, int epi,
+                         float scale, hipStream_t st) {
+  const uint8_t* q = (const uint8_t*)Wq;
+  const uint8_t* s = (const uint8_t*)Ws;
+#define DORY_PLM(E)                                                               \
+  if (M == 1) return pro_lb_launch<FMT, 1, E>(p, q, s, y, M, N, K, scale, st);    \
+  if (M == 2) return pro_lb_launch<FMT, 2, E>(p, q, s, y, M, N, K, scale, st);    \
+  if (M <= 4) return pro_lb_launch<FMT, 4, E>(p, q, s, y, M, N, K, scale, st);    \
+  return pro_lb_launch<FMT, 8, E>(p, q, s, y, M, N, K, scale, st);
+  if (epi == EPI_SWIGLU) {
+    DORY_PLM(EPI_SWIGLU)
+  }
+  DORY_PLM(EPI_F32)
+#undef DORY_PLM
+}
+
+}  // namespace
+
+hipError_t launch_quant_mxfp8(const void* W, int N, int K, void* q, void* s, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if (K % 32 || ((uintptr_t)W & 15) || ((uintptr_t)q & 15)) return hipErrorInvalidValue;
+  const int64_t nblocks = (int64_t)N * (K / 32);
+  hipLaunchKernelGGL(k_quant_mxfp8, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, (const bf16*)W,
+                     (uint8_t*)q, (uint8_t*)s, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const void* W, int N, int K, void* q, void* s, float* tscale, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if (K % 32 || ((uintptr_t)W & 15) || ((uintptr_t)q & 7) || ((uintptr_t)tscale & 3)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)N * K, nblocks = n / 16;
+  uint32_t* amax = (uint32_t*)tscale;  // holds the amax bits until k_tensor_scale turns them into g
+  hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, st, amax);
+  const int64_t groups = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_absmax, dim3((unsigned)groups), dim3(256), 0, st, (const bf16*)W, n, amax);
+  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, (const bf16*)W,
+                     (uint8_t*)q, (uint8_t*)s, (const uint32_t*)amax, nblocks);
+  hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1), 0, st, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_lowbit(int fmt, const void* q, const void* s, int N, int K, void* W, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if (K % 32 || ((uintptr_t)W & 15) || ((uintptr_t)q & 15)) return hipErrorInvalidValue;
+  // not timed kernels: plain launches, so a pending timing pair goes to the GEMM that follows
+  if (fmt == LB_MX) {
+    const int64_t nchunks = (int64_t)N * (K / 16);
+    hipLaunchKernelGGL(k_dequant_mxfp8, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
+                       (const uint8_t*)q, (const uint8_t*)s, (bf16*)W, nchunks);
+  } else if (fmt == LB_FP4) {
+    const int64_t nblocks = (int64_t)N * (K / 16);
+    hipLaunchKernelGGL(k_dequant_nvfp4, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st,
+                       (const uint8_t*)q, (const uint8_t*)s, (bf16*)W, nblocks);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool linear_lowbit_supported(int fmt, int M, int K) {
+  return (fmt == LB_MX || fmt == LB_FP4) && M >= 1 && M <= 8 && K % 32 == 0 && (size_t)M * K * 2 <= 64 * 1024 &&
+         cq_ok(chunks_per_lane(fmt, K), false);
+}
+
+bool linear_pro_lowbit_supported(int fmt, int M, int K) {
+  return (fmt == LB_MX || fmt == LB_FP4) && M >= 1 && M <= 8 && K % 32 == 0 && (size_t)M * K * 2 <= 64 * 1024 &&
+         cq_ok(chunks_per_lane(fmt, K), true);
+}
+
+hipError_t launch_linear_lowbit(int fmt, const void* x, int64_t ldx, const void* Wq, const void* Ws, void* y, int M,
+                                int N, int K, int epi, float scale, hipStream_t st) {
+  if (!lb_shape_ok(fmt, M, K, Wq, Ws) || !linear_lowbit_supported(fmt, M, K) || ldx % 8 || ((uintptr_t)x & 15))
+    return hipErrorInvalidValue;
+  return fmt == LB_MX ? linear_lb<LB_MX>(x, ldx, Wq, Ws, y, M, N, K, epi, scale, st)
+                      : linear_lb<LB_FP4>(x, ldx, Wq, Ws, y, M, N, K, epi, scale, st);
+}
+
+hipError_t launch_linear_pro_lowbit(int fmt, const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N,
+                                    int K, int epi, float scale, hipStream_t st) {
+  if (!lb_shape_ok(fmt, M, K, Wq, Ws) || !linear_pro_lowbit_supported(fmt, M, K)) return hipErrorInvalidValue;
+  return fmt == LB_MX ? linear_pro_lb<LB_MX>(p, Wq, Ws, y, M, N, K, epi, scale, st)
+                      : linear_pro_lb<LB_FP4>(p, Wq, Ws, y, M, N, K, epi, scale, st);
+}
+
+}  // namespace dory

@@ -149,19 +149,23 @@ hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, in
                              hipStream_t st);
 bool linear_pro_supported(int M, int K);
 
-// MXFP8 weights (OCP MX, E4M3 elements, blocks of 32 along K, E8M0 scale
-// bytes): codes [N][K] bytes and scales [N][K/32] bytes per projection.
-// quant: bfloat16 [N][K] -> codes + scales; dequant: the reverse (exact).
+// Low-bit weights of the layer projections; fmt is a dory_weight_format
+// (1: MXFP8 — E4M3 codes [N][K], E8M0 scales [N][K/32]; 2: NVFP4-style —
+// E2M1 codes [N][K/2], E4M3 scales [N][K/16], a float32 tensor scale applied
+// through `scale`).
 hipError_t launch_quant_mxfp8(const void* W_bf16, int N, int K, void* q, void* s, hipStream_t st);
-hipError_t launch_dequant_mxfp8(const void* q, const void* s, int N, int K, void* W_bf16, hipStream_t st);
-// Decode GEMV y = x . dequant(W)^T (M <= 8, K % 32 == 0), epilogues as launch_linear.
-hipError_t launch_linear_mx(const void* x, int64_t ldx, const void* Wq, const void* Ws, void* y, int M, int N, int K,
-                            int epi, float scale, hipStream_t st);
-bool linear_mx_supported(int M, int K);
-// launch_linear_pro for MXFP8 weights.
-hipError_t launch_linear_pro_mx(const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N, int K,
-                                int epi, float scale, hipStream_t st);
-bool linear_pro_mx_supported(int M, int K);
+// tscale: one device float, receives the tensor scale g
+hipError_t launch_quant_nvfp4(const void* W_bf16, int N, int K, void* q, void* s, float* tscale, hipStream_t st);
+// codes -> bfloat16 (MXFP8: the weights; NVFP4: e2m1 * e4m3, g left to the GEMM's scale)
+hipError_t launch_dequant_lowbit(int fmt, const void* q, const void* s, int N, int K, void* W_bf16, hipStream_t st);
+// decode GEMV (M <= 8): y = scale * x . W^T; SwiGLU: u = scale * x . W_u^T, v likewise
+hipError_t launch_linear_lowbit(int fmt, const void* x, int64_t ldx, const void* Wq, const void* Ws, void* y, int M,
+                                int N, int K, int epi, float scale, hipStream_t st);
+bool linear_lowbit_supported(int fmt, int M, int K);
+// launch_linear_pro for low-bit weights
+hipError_t launch_linear_pro_lowbit(int fmt, const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N,
+                                    int K, int epi, float scale, hipStream_t st);
+bool linear_pro_lowbit_supported(int fmt, int M, int K);
 
 // Greedy argmax; if pos_dev is not NULL the final pass also advances the
 // device position counter by one (the end of a decode step).

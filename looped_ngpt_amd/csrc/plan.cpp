@@ -44,12 +44,13 @@ dory_status make_plan(const dory_config* c, Plan* p, std::string* why) {
     return fail(why, "bfloat16 models need d_model, d_ff and head_dim multiples of 8");
   if ((int64_t)c->max_batch * c->max_chunk > (1 << 24)) return fail(why, "max_batch * max_chunk too large");
   if (!std::isfinite(c->combine_wh) || !std::isfinite(c->combine_we)) return fail(why, "combine weights must be finite");
-  if (c->weight_format != DORY_WEIGHTS_DTYPE && c->weight_format != DORY_WEIGHTS_MXFP8)
-    return fail(why, "weight_format must be DORY_WEIGHTS_DTYPE or DORY_WEIGHTS_MXFP8");
-  if (c->weight_format == DORY_WEIGHTS_MXFP8 &&
+  if (c->weight_format != DORY_WEIGHTS_DTYPE && c->weight_format != DORY_WEIGHTS_MXFP8 &&
+      c->weight_format != DORY_WEIGHTS_NVFP4)
+    return fail(why, "weight_format must be DORY_WEIGHTS_DTYPE, DORY_WEIGHTS_MXFP8 or DORY_WEIGHTS_NVFP4");
+  if (c->weight_format != DORY_WEIGHTS_DTYPE &&
       (c->dtype != DORY_BF16 || c->d_model % 32 || (c->n_q_heads * c->head_dim) % 32 || c->d_ff % 32 ||
        c->d_model > 8192))
-    return fail(why, "MXFP8 weights need bfloat16, d_model <= 8192 and d_model, n_q*hd, d_ff multiples of 32");
+    return fail(why, "low-bit weights need bfloat16, d_model <= 8192 and d_model, n_q*hd, d_ff multiples of 32");
 
   p->cfg = *c;
   p->n_layers = c->n_in + c->n_rec + c->n_out;
@@ -137,7 +138,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.flags = take(256);
   w.pos = take(4);
   w.rowk = take((size_t)c.max_batch * 4);
-  if (c.weight_format == DORY_WEIGHTS_MXFP8) {  // one projection expanded to bfloat16 for prefill GEMMs
+  if (c.weight_format != DORY_WEIGHTS_DTYPE) {  // one projection expanded to bfloat16 for prefill GEMMs
     const size_t d = c.d_model;
     size_t big = (size_t)p.qkvg_dim * d;
     big = std::max(big, d * (size_t)p.q_dim);

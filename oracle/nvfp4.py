@@ -37,7 +37,8 @@ element rounding at every midpoint and between them, the scale choice against
 exact rational squared errors (fractions) on small blocks, blocks that a
 known scale represents exactly (zero error, smallest such code), the tensor
 scale, that the choice is never worse than the amax/6 scale rounded to E4M3,
-bfloat16 exactness of e2m1 * e4m3, and the packing order.
+bfloat16 exactness of e2m1 * e4m3, and the packing order; the C search
+(choose_scales_c, oracle/c/nvfp4_search.c) against this numpy search.
 """
 from __future__ import annotations
 
@@ -115,10 +116,21 @@ def choose_scales(a: np.ndarray, g) -> np.ndarray:
     return best
 
 
-def quantize(w: np.ndarray, g=None):
+def choose_scales_c(a: np.ndarray, g) -> np.ndarray:
+    """choose_scales by the plain C loops of oracle/c/nvfp4_search.c (the
+    same definition; for tensors too large for numpy to finish in seconds)."""
+    from oracle import native
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.zeros(a.shape[0], dtype=np.int32)
+    native.lib().nvfp4_choose_scales(a.ctypes.data, a.shape[0], float(g), out.ctypes.data)
+    return out.astype(np.int64)
+
+
+def quantize(w: np.ndarray, g=None, use_c: bool = False):
     """w [N, K] (K % 16 == 0) -> (codes uint8 [N, K/2], scale codes uint8
     [N, K/16], tensor scale float32). g: the tensor scale to use (default:
-    from w; given when only some rows of a tensor are quantised)."""
+    from w; given when only some rows of a tensor are quantised). use_c: the
+    scale search in C (choose_scales_c)."""
     w = np.asarray(w, dtype=np.float64)
     N, K = w.shape
     if K % BLOCK:
@@ -127,7 +139,7 @@ def quantize(w: np.ndarray, g=None):
         g = tensor_scale(w)
     blocks = w.reshape(N * K // BLOCK, BLOCK)
     a = np.abs(blocks)
-    sc = choose_scales(a, g)
+    sc = choose_scales_c(a, g) if use_c else choose_scales(a, g)
     S = _E4M3_POS[sc - 1] * float(g)
     idx = magnitude_index(a, S)
     q = (idx | (np.signbit(blocks).astype(np.int64) << 3)).reshape(N, K)

@@ -107,7 +107,13 @@ def test_weight_format_configs():
     for bad in (small(dtype="bf16", d_ff=688), small(dtype="f32", d_ff=704)):
         c, _k = dory.make_config(bad, max_batch=1, max_ctx=16, max_chunk=16, weight_format=dory.WEIGHTS_MXFP8)
         assert dory.validate_config(c) == dory.DORY_E_ARG
-    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, weight_format=2)
+    fp4, _k3 = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, weight_format=dory.WEIGHTS_NVFP4)
+    assert dory.validate_config(fp4) == dory.DORY_OK
+    assert dory.workspace_bytes(fp4) == dory.workspace_bytes(mx)
+    for bad in (small(dtype="bf16", d_ff=688), small(dtype="f32", d_ff=704)):
+        c, _k = dory.make_config(bad, max_batch=1, max_ctx=16, max_chunk=16, weight_format=dory.WEIGHTS_NVFP4)
+        assert dory.validate_config(c) == dory.DORY_E_ARG
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16, weight_format=3)
     assert dory.validate_config(c) == dory.DORY_E_ARG
 
 
@@ -116,7 +122,8 @@ class FakeCtx:
     paths (which return before any HIP call) may be exercised with it."""
 
     def __init__(self, model, *, kv_mode="last_loop", kv_loops=1, max_batch=2, max_ctx=16, max_loops=4,
-                 kv_bytes=None, ws_bytes=None, kv_addr=1 << 20, ws_addr=1 << 30, weight_format=0):
+                 kv_bytes=None, ws_bytes=None, kv_addr=1 << 20, ws_addr=1 << 30, weight_format=0,
+                 scales=False, tscales=None):
         L = model.n_layers
         self.c, self._k = dory.make_config(model, max_batch=max_batch, max_ctx=max_ctx, max_chunk=8,
                                            max_loops=max_loops, weight_format=weight_format)
@@ -125,6 +132,15 @@ class FakeCtx:
         vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
         self.w = binding.DoryWeights(embed=1 << 12, qkvg=vp(arrs[0]), o=vp(arrs[1]), ug=vp(arrs[2]),
                                      down=vp(arrs[3]), alpha_attn=vp(arrs[4]), alpha_mlp=vp(arrs[5]))
+        if scales:   # fake block-scale arrays (even addresses)
+            sarrs = [(ctypes.c_void_p * L)(*[(1 << 24) + 64 * (l + 1) for l in range(L)]) for _ in range(4)]
+            self._arrs += sarrs
+            self.w.qkvg_scale, self.w.o_scale, self.w.ug_scale, self.w.down_scale = [vp(a) for a in sarrs]
+        if tscales is not None:
+            tarr = (ctypes.c_float * L)(*tscales)
+            self._arrs.append(tarr)
+            fp = ctypes.cast(tarr, ctypes.POINTER(ctypes.c_float))
+            self.w.qkvg_tscale = self.w.o_tscale = self.w.ug_tscale = self.w.down_tscale = fp
         code = dory.KV_MODES[kv_mode]
         kvb = dory.kv_bytes(self.c, code, kv_loops) if kv_bytes is None else kv_bytes
         wsb = dory.workspace_bytes(self.c) if ws_bytes is None else ws_bytes
@@ -142,7 +158,18 @@ def test_create_validation():
     m = small()
     assert FakeCtx(m).status == dory.DORY_OK
     # MXFP8 projections without their scale arrays
-    assert FakeCtx(small(dtype="bf16", d_ff=704), weight_format=dory.WEIGHTS_MXFP8).status == dory.DORY_E_ARG
+    mb = small(dtype="bf16", d_ff=704)
+    assert FakeCtx(mb, weight_format=dory.WEIGHTS_MXFP8).status == dory.DORY_E_ARG
+    assert FakeCtx(mb, weight_format=dory.WEIGHTS_MXFP8, scales=True).status == dory.DORY_OK
+    # NVFP4 projections need block scales and positive finite tensor scales
+    L = mb.n_layers
+    assert FakeCtx(mb, weight_format=dory.WEIGHTS_NVFP4, scales=True).status == dory.DORY_E_ARG
+    assert FakeCtx(mb, weight_format=dory.WEIGHTS_NVFP4, tscales=[0.01] * L).status == dory.DORY_E_ARG
+    assert FakeCtx(mb, weight_format=dory.WEIGHTS_NVFP4, scales=True, tscales=[0.01] * L).status == dory.DORY_OK
+    for badg in (0.0, -1.0, float("inf"), float("nan")):
+        t = [0.01] * L
+        t[L - 1] = badg
+        assert FakeCtx(mb, weight_format=dory.WEIGHTS_NVFP4, scales=True, tscales=t).status == dory.DORY_E_ARG
     assert FakeCtx(m, kv_bytes=100).status == dory.DORY_E_ARG
     assert FakeCtx(m, ws_bytes=100).status == dory.DORY_E_ARG
     assert FakeCtx(m, kv_addr=(1 << 20) + 8).status == dory.DORY_E_ARG

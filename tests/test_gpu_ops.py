@@ -154,3 +154,105 @@ def test_linear_mx(M, N, K, epi):
     err = np.abs(got - ref)
     assert np.all(err <= tol), f"max err {err.max()}"
 
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-style weights: the device quantiser code for code against the oracle,
+# at moderate and at full size (sampled blocks), and the decode GEMV on
+# arbitrary codes against a float64 product with the oracle's dequantisation
+# ---------------------------------------------------------------------------
+def _quant_fp4_gpu(wb, N, K):
+    q = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((N, K // 16), dtype=torch.uint8, device="cuda")
+    g = torch.zeros(1, dtype=torch.float32, device="cuda")
+    dory.op_quant_nvfp4(_dev(wb), N, K, q, sc, g)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sc.cpu().numpy(), g.cpu().numpy()[0]
+
+
+def test_quant_nvfp4_bit_exact():
+    from oracle import mxfp8, nvfp4
+    rng = np.random.default_rng(31)
+    N, K = 64, 512
+    w = (rng.standard_normal((N, K)) * np.exp(rng.uniform(-7, -1.5, (N, 1)))).astype(np.float32)
+    w = np.clip(w, -2.5, 2.5)
+    w[0, 0] = 2688.0 * 2.0 ** -10                       # amax: g = 2^-10 exactly
+    S = 2.0 ** -10
+    w[1, :16] = 0.0                                     # zero block
+    w[1, 16:32] = -0.0                                  # negative zeros
+    for r, s in zip(range(2, 8), (0x38, 0x30, 0x28, 0x3C, 0x44, 0x10)):
+        e = mxfp8.e4m3_value(s) * S
+        w[r, :16] = np.array([0, .5, 1, 1.5, 2, 3, 4, 6] * 2) * e             # exact at scale s
+        w[r, 16:23] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * e  # ties at scale s
+        w[r, 23:32] = -w[r, 16:25]
+    wb = f32_to_bf16_bits(w)
+    w64 = bf16_bits_to_f32(wb).astype(np.float64)
+    q_ref, s_ref, g_ref = nvfp4.quantize(w64)
+    q, sc, g = _quant_fp4_gpu(wb, N, K)
+    assert g == g_ref == np.float32(2.0 ** -10)
+    np.testing.assert_array_equal(sc, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+    # an all-zero matrix: g = 1, every block scale code 1, codes 0 / 8 (sign of -0)
+    z = np.zeros((4, 64), dtype=np.uint16)
+    z[1] = 0x8000
+    q, sc, g = _quant_fp4_gpu(z, 4, 64)
+    assert g == 1.0 and np.all(sc == 1) and np.all(q[0] == 0) and np.all(q[1] == 0x88)
+
+
+def test_quant_nvfp4_full_size_sampled():
+    """16384 x 3072 (the 36-layer up/gate shape): the tensor scale exactly,
+    2048 random blocks code for code."""
+    from oracle import nvfp4
+    rng = np.random.default_rng(32)
+    N, K = 16384, 3072
+    w = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    w[123, 456] = 0.5
+    wb = f32_to_bf16_bits(w)
+    q, sc, g = _quant_fp4_gpu(wb, N, K)
+    g_ref = nvfp4.tensor_scale(bf16_bits_to_f32(wb))
+    assert g == g_ref
+    idx = rng.choice(N * K // 16, size=2048, replace=False)
+    blocks = bf16_bits_to_f32(wb.reshape(-1, 16)[idx]).astype(np.float64)
+    qb, sb, _ = nvfp4.quantize(blocks, g_ref)
+    np.testing.assert_array_equal(sc.reshape(-1)[idx], sb.reshape(-1))
+    np.testing.assert_array_equal(q.reshape(-1, 8)[idx], qb)
+
+
+FP4_CASES = [(1, 8192, 3072, 0), (1, 2 * 8192, 3072, 1), (3, 1000, 2304, 0), (5, 2 * 1000, 2304, 1),
+             (1, 3072, 8192, 0), (8, 704, 256, 0), (2, 2 * 704, 256, 1), (4, 512, 8192, 0), (1, 64, 16384, 0),
+             (2, 2 * 96, 6144, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,epi", FP4_CASES)
+def test_linear_fp4(M, N, K, epi):
+    """Arbitrary codes (every E2M1 code, -0 included) and block scales over a
+    wide range; scale = g times an extra factor."""
+    from oracle import nvfp4
+    rng = np.random.default_rng(M * 977 + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    xs = f32_to_bf16_bits(x)
+    x64 = bf16_bits_to_f32(xs).astype(np.float64)
+    q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sc = rng.integers(20, 100, size=(N, K // 16), dtype=np.uint8)
+    g = np.float32(0.37 / math.sqrt(K))
+    W64 = nvfp4.dequantize(q, sc, g)
+    extra = 1.3 if epi == 0 else 1.0
+    ref = (x64 @ W64.T) * extra
+    absref = (np.abs(x64) @ np.abs(W64).T) * extra
+    if epi == 1:
+        F = N // 2
+        ref = ref[:, :F] * ref[:, F:] / (1.0 + np.exp(-ref[:, F:]))
+        y = torch.zeros((M, F), dtype=torch.int16, device="cuda")
+    else:
+        y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    print(f"linear fp4 M={M} N={N} K={K} epi={epi}", flush=True)
+    dory.op_linear_fp4(_dev(xs), _dev(q), _dev(sc), y, M, N, K, epilogue=epi, scale=float(g) * extra)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if epi == 1:
+        got = bf16_bits_to_f32(got.view(np.uint16)).astype(np.float64)
+        tol = np.abs(ref) * 2.0 ** -8 + 1e-4 * (1 + np.abs(ref))
+    else:
+        tol = 2e-5 * absref + 1e-7
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"max err {err.max()} (tol at argmax {tol.reshape(-1)[np.argmax(err)]})"

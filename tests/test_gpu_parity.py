@@ -41,6 +41,9 @@ def model_and_weights(name):
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, window=60, name="tiny_bf16_w60")
         elif name == "tiny_mx":       # the tiny shape in bfloat16 with MXFP8-compatible widths (multiples of 32)
             m = get_config("tiny").replace(dtype="bf16", d_ff=704, name="tiny_mx")
+        elif name == "wide_fp4":      # the 36-layer model's d_model (3072) with one head and a narrow MLP, 1/1/1
+            m = scaled_config(get_config("c36"), n_in=1, n_rec=1, n_out=1).replace(
+                n_q_heads=1, n_kv_heads=1, d_ff=64, vocab=2048, window=64, name="wide_fp4")
         elif name == "c36w_w192":     # the c36w weights with 192-key rings that wrap
             m0, w, dw = model_and_weights("c36w")
             _cache[name] = (m0.replace(window=192, name="c36w_w192"), w, dw)
@@ -288,6 +291,45 @@ def test_mxfp8_weights_generate(name, k, mode, n, steps, ctx):
                      kv_loops=k if mode == "per_loop" else 1, weight_format=dory.WEIGHTS_MXFP8)
     g_tok, g_log, lib_next = generate(s, prompt, steps, k)
     assert _report(f"{name} MXFP8 {mode} k={k}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-style layer projections: the oracle runs on its own quantisation (the
+# least-error block scales, dequantised exactly in float64); the library
+# quantises on the device and decodes with the 4-bit GEMVs (prefill expands
+# e2m1 * e4m3 to bfloat16 and applies the tensor scale in the GEMM)
+# ---------------------------------------------------------------------------
+_fp4_cache = {}
+
+
+def _fp4_oracle_weights(name, m, w):
+    from oracle import nvfp4
+    from synth.gen import bf16_bits_to_f32
+    if name not in _fp4_cache:
+        out = dict(w)
+        for l in range(m.n_layers):
+            for p in ("qkvg", "o", "ug", "down"):
+                q, sc, g = nvfp4.quantize(bf16_bits_to_f32(w[f"L{l}.{p}"]).astype(np.float64), use_c=True)
+                out[f"L{l}.{p}"] = nvfp4.dequantize(q, sc, g)
+        _fp4_cache[name] = out
+    return _fp4_cache[name]
+
+
+@pytest.mark.parametrize("name,k,mode,n,steps,ctx", [("tiny_mx", 2, "last_loop", 100, 16, 160),
+                                                     ("tiny_mx", 3, "per_loop", 70, 8, 96),
+                                                     ("wide_fp4", 2, "last_loop", 96, 8, 128)])
+def test_nvfp4_weights_generate(name, k, mode, n, steps, ctx):
+    m, w, dw = model_and_weights(name)
+    prompt = make_tokens(m, 60, (1, n))
+    ora = LoopedNGPT(m, _fp4_oracle_weights(name, m, w), max_ctx=ctx)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode)
+    dq = dory.quantize_weights_nvfp4(m, dw)
+    s = dory.Session(m, dq, max_batch=1, max_ctx=ctx, max_chunk=n, max_loops=8, kv_mode=mode,
+                     kv_loops=k if mode == "per_loop" else 1, weight_format=dory.WEIGHTS_NVFP4)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"{name} NVFP4 {mode} k={k}", g_log, o_log) <= BF16_TOL
     np.testing.assert_array_equal(g_tok, o_tok)
     np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
 

@@ -149,3 +149,26 @@ def test_round_trip_error_bound():
     sat = x > 6
     assert np.all((np.abs(np.abs(d) - np.abs(w)) <= step * S / 2 * (1 + 1e-12)) | sat)
     assert np.all(np.sign(d) * np.sign(w) >= 0)
+
+
+def test_c_search_equals_numpy_search():
+    """The C loops (oracle/c/nvfp4_search.c) choose the same codes as the numpy
+    definition: random blocks over many binades, exact ties for several
+    candidates, zero and single-element blocks."""
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 3, (64, 1)))
+    w = bf16_bits_to_f32(f32_to_bf16_bits(w.astype(np.float32))).astype(np.float64)
+    w[0, :16] = 0.0
+    w[1, :16] = 0.0
+    w[1, 5] = -3.0
+    for r, s in zip(range(2, 10), (0x38, 0x30, 0x3C, 0x20, 0x04, 0x41, 0x7E, 0x01)):
+        w[r, :16] = np.array(GRID * 2)[:16] * mxfp8.e4m3_value(s)        # exact for scale s
+        w[r, 16:23] = nvfp4._MIDS * mxfp8.e4m3_value(s)                   # ties for scale s
+    for g in (nvfp4.tensor_scale(w), np.float32(1.0), np.float32(3e-3)):
+        a = np.abs(w).reshape(-1, 16)
+        np.testing.assert_array_equal(nvfp4.choose_scales_c(a, g), nvfp4.choose_scales(a, g))
+    q1, s1, g1 = nvfp4.quantize(w)
+    q2, s2, g2 = nvfp4.quantize(w, use_c=True)
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s1, s2)
+    assert g1 == g2
