@@ -29,12 +29,17 @@ MFMA_PEAK = 2.5e15         # FLOP/s, MI355X dense bf16 matrix cores
 METRIC = "decode tokens/s @ k=1,2,4 (last-loop KV) + % of HBM roofline, 1×MI355X"
 
 
-def decode_bytes(m, k, ctx_mean, B=1, mxfp8=False):
+# bytes per projection weight of each storage format: bfloat16; MXFP8 (one
+# E4M3 byte + one scale byte per 32); NVFP4 (half a byte + one scale byte per 16)
+WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16}
+
+
+def decode_bytes(m, k, ctx_mean, B=1, fmt="bf16"):
     """Algorithmic HBM bytes of one decode step: every weight once (the
     recurrent block k times), the tied LM head, each layer application's K/V
     reads over its window and its one-position K/V write, per sequence.
-    mxfp8: the layer projections are stored as one E4M3 byte per weight plus
-    one scale byte per 32 weights (the LM head stays bfloat16)."""
+    fmt: storage of the layer projections (WEIGHT_BYTES); the LM head stays
+    bfloat16."""
     el = 2
     apps_full, apps_swa = 0, 0
     for l in range(m.n_layers):
@@ -44,7 +49,7 @@ def decode_bytes(m, k, ctx_mean, B=1, mxfp8=False):
         else:
             apps_swa += reps
     per_key = 2 * m.n_kv_heads * m.head_dim * el
-    layer = m.layer_bytes() // 2 * 33 // 32 if mxfp8 else m.layer_bytes()
+    layer = int(m.layer_bytes() // 2 * WEIGHT_BYTES[fmt])
     weights = (m.n_in + m.n_out + k * m.n_rec) * layer + m.vocab * m.d_model * el
     kv_read = B * per_key * (apps_full * ctx_mean + apps_swa * min(ctx_mean, m.window))
     kv_write = B * per_key * (apps_full + apps_swa)
@@ -74,12 +79,12 @@ def ug_traffic():
                       + UG_TRAFFIC["write_kib"] * UG_TRAFFIC["write_factor"]) * 1024))
 
 
-def ug_bytes(m, B=1, mxfp8=False):
+def ug_bytes(m, B=1, fmt="bf16"):
     """Algorithmic bytes of one SwiGLU up/gate projection launch (B rows): the
-    two weight matrices (bfloat16, or E4M3 codes plus one scale byte per 32),
-    the prologue's inputs (sublayer output y, residual h, alpha; float32) and
-    outputs (new residual, float32; activation, bf16)."""
-    wb = 2 * m.d_ff * m.d_model * 33 // 32 if mxfp8 else 2 * m.d_ff * m.d_model * 2
+    two weight matrices (WEIGHT_BYTES per weight: bfloat16, or codes plus
+    block-scale bytes), the prologue's inputs (sublayer output y, residual h,
+    alpha; float32) and outputs (new residual, float32; activation, bf16)."""
+    wb = int(2 * m.d_ff * m.d_model * WEIGHT_BYTES[fmt])
     return wb + B * m.d_model * 4 * 3 + B * m.d_model * 4 + B * m.d_ff * 2
 
 
@@ -252,11 +257,19 @@ def run_other(args, dev):
                            "mfma_frac_whole": round(fl / (pms / 1e3) / MFMA_PEAK, 4)}})
         return
 
-    if args.workload == "mxfp8":
+    if args.workload in ("mxfp8", "nvfp4"):
+        fmt = args.workload
         model = CONFIGS["c36"]["model"]
         n = args.prompt
         w = make_weights_device(model, dev)
-        wq = dory.quantize_weights_mxfp8(model, w, stream=stream)
+        torch.cuda.synchronize()
+        tq = time.perf_counter()
+        if fmt == "mxfp8":
+            wq = dory.quantize_weights_mxfp8(model, w, stream=stream)
+        else:
+            wq = dory.quantize_weights_nvfp4(model, w, stream=stream)
+        torch.cuda.synchronize()
+        log(f"quantised {4 * model.n_layers} projections in {time.perf_counter() - tq:.2f} s")
         for key in [x for x in w if x.split(".")[-1] in dory.PROJECTIONS]:
             del w[key]                       # the bfloat16 projections are not used from here on
         torch.cuda.synchronize()
@@ -266,7 +279,8 @@ def run_other(args, dev):
         prompt = torch.randint(0, model.vocab, (1, n), generator=g, dtype=torch.int32).to(dev)
         max_ctx = (n + Wm + K + args.kernel_steps + 2 + 255) // 256 * 256
         sess = dory.Session(model, wq, max_batch=1, max_ctx=max_ctx, max_chunk=n, kv_mode="last_loop",
-                            stream=stream, device=dev, weight_format=dory.WEIGHTS_MXFP8)
+                            stream=stream, device=dev,
+                            weight_format=dory.WEIGHTS_MXFP8 if fmt == "mxfp8" else dory.WEIGHTS_NVFP4)
         table, roof = {}, None
         for k in (1, 2, 4):
             sess.reset()
@@ -278,7 +292,7 @@ def run_other(args, dev):
             torch.cuda.synchronize()
             pms = e0.elapsed_time(e1)
             ms = _timed_decode(sess, 1, k, K, Wm)
-            step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0, mxfp8=True)
+            step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0, fmt=fmt)
             table[f"k={k}"] = {"tokens_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
                                "hbm_frac": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4),
                                "bytes_per_step": step_bytes, "prefill_ms": round(pms, 1)}
@@ -291,18 +305,21 @@ def run_other(args, dev):
                 tot, cnt = sess.kernel_time()
                 sess.set_kernel_timing(None)
                 ug_ms = tot / max(cnt, 1)
-                ach = ug_bytes(model, mxfp8=True) / (ug_ms / 1e3)
+                ach = ug_bytes(model, fmt=fmt) / (ug_ms / 1e3)
+                kname = ("k_gemv_pro_lb<MXFP8,1,3,SwiGLU>" if fmt == "mxfp8" else "k_gemv_pro_lb<NVFP4,1,2,SwiGLU>")
                 roof = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK, 4), "traffic": None,
-                        "kernel": "k_gemv_pro_mx<1,3,SwiGLU> (MXFP8 up/gate projection with the nGPT update "
-                                  "prologue, M=1, N=2x8192, K=3072)",
-                        "bytes_per_launch": ug_bytes(model, mxfp8=True), "avg_launch_us": round(ug_ms * 1e3, 2)}
-                log(f"MXFP8 up/gate GEMV: {cnt} launches, {ug_ms * 1e3:.1f} us avg, {100 * roof['frac']:.1f}% HBM")
+                        "kernel": f"{kname} ({fmt.upper()} up/gate projection with the nGPT update prologue, "
+                                  "M=1, N=2x8192, K=3072)",
+                        "bytes_per_launch": ug_bytes(model, fmt=fmt), "avg_launch_us": round(ug_ms * 1e3, 2)}
+                log(f"{fmt} up/gate GEMV: {cnt} launches, {ug_ms * 1e3:.1f} us avg, {100 * roof['frac']:.1f}% HBM")
         hk = table["k=2"]
-        _line(f"{model.name} with MXFP8 layer projections (E4M3, 32-element blocks), batch 1, {n}-token random "
-              "prompt, greedy decode at k=1,2,4, last-loop KV (headline value: k=2)", hk["tokens_per_s"],
-              hk["ms_per_step"], 1, K, Wm, n, 2, "last_loop", {"by_k": table, "roofline": roof,
-                                                                "dtype": "bf16 activations, MXFP8 weights"})
+        desc = ("MXFP8 layer projections (E4M3, 32-element blocks, E8M0 scales)" if fmt == "mxfp8" else
+                "NVFP4-style layer projections (E2M1, 16-element blocks, least-error E4M3 scales, float32 "
+                "tensor scale)")
+        _line(f"{model.name} with {desc}, batch 1, {n}-token random prompt, greedy decode at k=1,2,4, last-loop "
+              "KV (headline value: k=2)", hk["tokens_per_s"], hk["ms_per_step"], 1, K, Wm, n, 2, "last_loop",
+              {"by_k": table, "roofline": roof, "dtype": f"bf16 activations, {fmt.upper()} weights"})
         return
 
     # b64: 64 sequences whose 32768 cached positions are synthetic: random
@@ -376,11 +393,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
-    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8"], default="c36",
+    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8", "nvfp4"], default="c36",
                     help="c36: the headline (default). c72: the 72-layer shape, 16384-token prompt, k=1..4 in "
                          "both KV modes. b64: 64 sequences at 32768 cached positions (synthetic caches), k=4, "
-                         "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2. mxfp8: the c36 shape with "
-                         "MXFP8 layer projections, decode at k=1,2,4")
+                         "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2. mxfp8 / nvfp4: the c36 shape "
+                         "with MXFP8 / NVFP4-style layer projections, decode at k=1,2,4")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
