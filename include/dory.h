@@ -328,6 +328,41 @@ dory_status dory_op_linear_fp4(const void* x, int64_t ldx, const void* codes, co
 dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out,
                            void* scratch_dev, void* stream);
 
+/* ---- depth-1 truncated backward of the last recurrent invocation -------- */
+
+/* The pages train the looped stage with backpropagation truncated to depth
+ * one: only the final invocation of the recurrent block receives gradients
+ * ("Dory1.0-4B: A Looped Normalized-GPT", AI summary, Methodology in Plain
+ * English). For a training chunk of `batch` sequences of n positions starting
+ * at position 0: x_dev [batch, n, d] float32 is that invocation's input (the
+ * re-injected input, a constant for the truncated backward), h_out =
+ * norm(R(x)) with R the recurrent layers in order and attention over the
+ * chunk's own positions (causal; t - s < window in sliding-window layers).
+ * Given grad_out_dev = dL/dh_out [batch, n, d] float32, writes dL/dW of the
+ * four projections and dL/dalpha of both updates of every recurrent layer
+ * into `grads` (overwritten, not accumulated) and dL/dx into grad_x_dev (may
+ * be NULL). Projections in the context's dtype (bfloat16 operands on the
+ * matrix cores with float32 accumulation), everything else float32. Needs a
+ * DORY_WEIGHTS_DTYPE context, n <= max_ctx, head_dim 64 or 128; independent
+ * of the sequence state (no cache is read or written). ws_dev: device,
+ * 256-byte aligned, >= dory_backward_workspace_bytes(cfg, batch, n).
+ * Enqueued on the context's stream. DORY_E_ARG on bad arguments (nothing
+ * enqueued), DORY_E_HIP on a launch failure. */
+typedef struct {            /* host arrays of n_rec device float32 pointers; entry i is
+                               global layer n_in + i                                    */
+  float* const* qkvg;       /* [qkvg_dim, d] */
+  float* const* o;          /* [d, q_dim]    */
+  float* const* ug;         /* [2*d_ff, d]   */
+  float* const* down;       /* [d, d_ff]     */
+  float* const* alpha_attn; /* [d]           */
+  float* const* alpha_mlp;  /* [d]           */
+} dory_grads;
+
+size_t dory_backward_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t n);
+dory_status dory_backward_last_loop(dory_ctx* ctx, const float* x_dev, const float* grad_out_dev, int32_t batch,
+                                    int32_t n, const dory_grads* grads, float* grad_x_dev, void* ws_dev,
+                                    size_t ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dor
            "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
-           "dory_argmax_scratch_bytes", "dory_op_argmax"]
+           "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_backward_workspace_bytes", "dory_backward_last_loop"]
 
 
 class DoryConfig(ctypes.Structure):
@@ -64,6 +64,10 @@ class DoryWeights(ctypes.Structure):
                 ("ug_scale", ctypes.POINTER(ctypes.c_void_p)), ("down_scale", ctypes.POINTER(ctypes.c_void_p)),
                 ("qkvg_tscale", ctypes.POINTER(ctypes.c_float)), ("o_tscale", ctypes.POINTER(ctypes.c_float)),
                 ("ug_tscale", ctypes.POINTER(ctypes.c_float)), ("down_tscale", ctypes.POINTER(ctypes.c_float))]
+
+
+class DoryGrads(ctypes.Structure):
+    _fields_ = [(k, ctypes.POINTER(ctypes.c_void_p)) for k in ("qkvg", "o", "ug", "down", "alpha_attn", "alpha_mlp")]
 
 
 _P = ctypes.c_void_p
@@ -98,6 +102,8 @@ _sig = {
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
     "dory_argmax_scratch_bytes": (ctypes.c_size_t, [_I, _I]),
     "dory_op_argmax": (_I, [_P, _I, _I, _P, _P, _P]),
+    "dory_backward_workspace_bytes": (ctypes.c_size_t, [_C, _I, _I]),
+    "dory_backward_last_loop": (_I, [_P, _P, _P, _I, _I, ctypes.POINTER(DoryGrads), _P, _P, ctypes.c_size_t]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -147,6 +153,10 @@ def kv_bytes(c: DoryConfig, kv_mode: int, kv_loops: int) -> int:
 
 def workspace_bytes(c: DoryConfig) -> int:
     return _lib.dory_workspace_bytes(ctypes.byref(c))
+
+
+def backward_workspace_bytes(c: DoryConfig, batch: int, n: int) -> int:
+    return _lib.dory_backward_workspace_bytes(ctypes.byref(c), batch, n)
 
 
 def kv_slot(c: DoryConfig, kv_mode: int, kv_loops: int, layer: int, loop: int, pos: int):
@@ -336,6 +346,40 @@ class Session:
         mode = self.kv_mode if kv_mode is None else KV_MODES[kv_mode]
         self._check(_lib.dory_resume(self.h, batch, pos, n_loops, mode))
         self.batch = batch
+
+    def backward_last_loop(self, x, grad_out, *, ws=None, grads=None, stream_sync: bool = False):
+        """Depth-1 backward of the last recurrent invocation (dory_backward_last_loop).
+        x, grad_out: float32 [B, n, d] device tensors. Returns a dict of float32
+        gradients keyed like the weights ("L{l}.qkvg", ..., "L{l}.alpha_a",
+        "L{l}.alpha_m" for the recurrent layers) plus "x"."""
+        import torch
+        m = self.model
+        B, n, d = x.shape
+        wsb = backward_workspace_bytes(self.cfg, B, n)
+        if wsb == 0:
+            raise DoryError(DORY_E_ARG, "backward workspace size")
+        if ws is None or ws.numel() < wsb:
+            ws = torch.empty(wsb, dtype=torch.uint8, device=self.device)
+        rec = list(range(m.n_in, m.n_in + m.n_rec))
+        if grads is None:
+            grads = {}
+            for l in rec:
+                for key in ("qkvg", "o", "ug", "down"):
+                    grads[f"L{l}.{key}"] = torch.empty(tuple(self.weights[f"L{l}.{key}"].shape), dtype=torch.float32,
+                                                       device=self.device)
+                grads[f"L{l}.alpha_a"] = torch.empty(d, dtype=torch.float32, device=self.device)
+                grads[f"L{l}.alpha_m"] = torch.empty(d, dtype=torch.float32, device=self.device)
+            grads["x"] = torch.empty((B, n, d), dtype=torch.float32, device=self.device)
+        arr = lambda key: (ctypes.c_void_p * len(rec))(*[_ptr(grads[f"L{l}.{key}"]) for l in rec])
+        keep = {k: arr(k) for k in ("qkvg", "o", "ug", "down", "alpha_a", "alpha_m")}
+        vp = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        g = DoryGrads(qkvg=vp(keep["qkvg"]), o=vp(keep["o"]), ug=vp(keep["ug"]), down=vp(keep["down"]),
+                      alpha_attn=vp(keep["alpha_a"]), alpha_mlp=vp(keep["alpha_m"]))
+        self._check(_lib.dory_backward_last_loop(self.h, _ptr(x), _ptr(grad_out), B, n, ctypes.byref(g),
+                                                 _ptr(grads["x"]) if "x" in grads else None, _ptr(ws), wsb))
+        if stream_sync:
+            torch.cuda.synchronize(self.device)
+        return grads
 
     def set_graphs(self, enable: bool) -> None:
         self._check(_lib.dory_set_graphs(self.h, 1 if enable else 0))

@@ -511,6 +511,129 @@ void commit_call(dory_ctx* c, int B, int n, int n_loops, int kv_mode) {
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// depth-1 truncated backward
+// ---------------------------------------------------------------------------
+struct Bw {
+  dory_ctx* c;
+  BwLayout L;
+  char* ws;
+  int B, n, M;
+  template <typename P>
+  P* f(size_t off) const { return (P*)(ws + off); }
+  float* h_at(int i) const { return f<float>(L.hin) + (size_t)i * M * c->plan.cfg.d_model; }
+};
+
+// y[M][N] = x[M][K] . W[N][K]^T, float32 out, operands in the model dtype
+dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K) {
+  HIP_TRY(c, launch_linear(c->plan.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
+  return DORY_OK;
+}
+
+// forward of recurrent layer l on h_in -> h_out, keeping what its backward reads
+dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
+  dory_ctx* c = b.c;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const int dt = C.dtype, M = b.M, d = C.d_model, F = C.d_ff, Q = P.qkvg_dim, qd = P.q_dim;
+  const BwLayout& L = b.L;
+  hipStream_t st = c->st;
+  const bool full = P.is_full[l];
+  const float2* tab = wsp<float2>(c, full ? P.ws.rope_full : P.ws.rope_swa);
+  HIP_TRY(c, launch_bw_cast(dt, h_in, b.ws + L.xb, (int64_t)M * d, st));
+  DORY_TRY(bw_gemm(c, b.ws + L.xb, d, c->qkvg[l], b.f<float>(L.P1), M, Q, d));
+  HIP_TRY(c, launch_bw_rope_norm_fwd(b.f<float>(L.P1), Q, tab, b.n, C.n_q_heads, C.n_kv_heads, C.head_dim, M,
+                                     b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.rq), b.f<float>(L.rk), st));
+  BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
+           C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
+  HIP_TRY(c, launch_bw_attn_fwd(a, M, b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst), st));
+  HIP_TRY(c, launch_bw_gate_fwd(dt, b.f<float>(L.o), b.f<float>(L.P1), Q, qd + 2 * P.kv_dim, C.attn_gate,
+                                C.head_dim, qd, M, b.f<float>(L.oh), b.ws + L.ohb, b.f<float>(L.rc), st));
+  DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd));
+  HIP_TRY(c, launch_bw_update_fwd(dt, h_in, b.f<float>(L.y), c->alpha_attn[l], M, d, b.f<float>(L.yh),
+                                  b.f<float>(L.ry), b.f<float>(L.rz), b.f<float>(L.h1), b.ws + L.h1b, st));
+  DORY_TRY(bw_gemm(c, b.ws + L.h1b, d, c->ug[l], b.f<float>(L.P2), M, 2 * F, d));
+  HIP_TRY(c, launch_bw_swiglu_fwd(dt, b.f<float>(L.P2), F, M, b.f<float>(L.a32), b.ws + L.ab, b.f<float>(L.rs),
+                                  st));
+  DORY_TRY(bw_gemm(c, b.ws + L.ab, F, c->down[l], b.f<float>(L.y), M, d, F));
+  HIP_TRY(c, launch_bw_update_fwd(dt, b.f<float>(L.h1), b.f<float>(L.y), c->alpha_mlp[l], M, d, b.f<float>(L.y2h),
+                                  b.f<float>(L.ry2), b.f<float>(L.rz2), h_out, nullptr, st));
+  return DORY_OK;
+}
+
+// dW [N][K] = dY^T X from dY [M][N] and X [M][K] (model dtype): both
+// transposed into TA / TB, then one GEMM over the M rows
+dory_status bw_wgrad(const Bw& b, const void* dY, int N, const void* X, int K, float* dW) {
+  dory_ctx* c = b.c;
+  const int dt = c->plan.cfg.dtype;
+  HIP_TRY(c, launch_bw_transpose(dt, dY, N, b.ws + b.L.TA, b.M, N, c->st));
+  HIP_TRY(c, launch_bw_transpose(dt, X, K, b.ws + b.L.TB, b.M, K, c->st));
+  return bw_gemm(c, b.ws + b.L.TA, b.M, b.ws + b.L.TB, dW, N, K, b.M);
+}
+
+// dX [M][K] = dY [M][N] . W [N][K]: W transposed into WT, then one GEMM
+dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX) {
+  dory_ctx* c = b.c;
+  HIP_TRY(c, launch_bw_transpose(c->plan.cfg.dtype, W, K, b.ws + b.L.WT, N, K, c->st));
+  return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N);
+}
+
+// backward of recurrent layer l (its forward values in the workspace):
+// dho = dL/d(output) -> dhi = dL/d(input); gradients into g (index i)
+dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const float* h_out, const float* dho,
+                         float* dhi, const dory_grads* g) {
+  dory_ctx* c = b.c;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const int dt = C.dtype, M = b.M, d = C.d_model, F = C.d_ff, Q = P.qkvg_dim, qd = P.q_dim;
+  const BwLayout& L = b.L;
+  hipStream_t st = c->st;
+  const bool full = P.is_full[l];
+  const float2* tab = wsp<float2>(c, full ? P.ws.rope_full : P.ws.rope_swa);
+  float* tmp = b.f<float>(L.tmp);
+
+  // MLP sublayer
+  HIP_TRY(c, launch_bw_update_bwd(dt, dho, h_out, b.f<float>(L.rz2), b.f<float>(L.y2h), b.f<float>(L.ry2),
+                                  b.f<float>(L.h1), c->alpha_mlp[l], M, d, b.f<float>(L.dres), b.ws + L.dyb,
+                                  b.f<float>(L.contrib), st));
+  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_mlp[i], st));
+  DORY_TRY(bw_wgrad(b, b.ws + L.dyb, d, b.ws + L.ab, F, g->down[i]));
+  DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->down[l], d, F, tmp));                     // da [M][F]
+  HIP_TRY(c, launch_bw_swiglu_bwd(dt, tmp, b.f<float>(L.a32), b.f<float>(L.rs), b.f<float>(L.P2), F, M,
+                                  b.ws + L.dP2b, st));
+  DORY_TRY(bw_wgrad(b, b.ws + L.dP2b, 2 * F, b.ws + L.h1b, d, g->ug[i]));
+  DORY_TRY(bw_xgrad(b, b.ws + L.dP2b, c->ug[l], 2 * F, d, tmp));                  // [M][d]
+  float* dh1 = b.f<float>(L.dh2);
+  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dh1, (int64_t)M * d, st));
+
+  // attention sublayer
+  HIP_TRY(c, launch_bw_update_bwd(dt, dh1, b.f<float>(L.h1), b.f<float>(L.rz), b.f<float>(L.yh), b.f<float>(L.ry),
+                                  h_in, c->alpha_attn[l], M, d, b.f<float>(L.dres), b.ws + L.dyb,
+                                  b.f<float>(L.contrib), st));
+  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_attn[i], st));
+  DORY_TRY(bw_wgrad(b, b.ws + L.dyb, d, b.ws + L.ohb, qd, g->o[i]));
+  DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->o[l], d, qd, tmp));                       // doh [M][qd]
+  HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
+                                qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
+                                b.f<float>(L.dP1), st));
+  BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
+           C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
+  HIP_TRY(c, launch_bw_attn_bwd(a, M, b.f<float>(L.dO), b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst),
+                                b.f<float>(L.D), b.f<float>(L.dqn), b.f<float>(L.dkn), b.f<float>(L.dv), st));
+  HIP_TRY(c, launch_bw_rope_norm_bwd(b.f<float>(L.dqn), b.f<float>(L.qn), b.f<float>(L.rq), b.f<float>(L.dkn),
+                                     b.f<float>(L.kn), b.f<float>(L.rk), b.f<float>(L.dv), tab, b.n, C.n_q_heads,
+                                     C.n_kv_heads, C.head_dim, M, b.f<float>(L.dP1), Q, st));
+  HIP_TRY(c, launch_bw_cast(dt, b.f<float>(L.dP1), b.ws + L.dP1b, (int64_t)M * Q, st));
+  DORY_TRY(bw_wgrad(b, b.ws + L.dP1b, Q, b.ws + L.xb, d, g->qkvg[i]));
+  DORY_TRY(bw_xgrad(b, b.ws + L.dP1b, c->qkvg[l], Q, d, tmp));                    // [M][d]
+  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dhi, (int64_t)M * d, st));
+  return DORY_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* dory_status_string(dory_status s) {
@@ -918,6 +1041,44 @@ dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, con
   hipError_t e = launch_linear_lowbit(DORY_WEIGHTS_MXFP8, x, ldx, codes, scales, y, M, N, K, epilogue, scale,
                                       (hipStream_t)stream);
   return e == hipSuccess ? DORY_OK : (e == hipErrorInvalidValue ? DORY_E_ARG : DORY_E_HIP);
+}
+
+size_t dory_backward_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t n) {
+  Plan p;
+  if (!cfg || batch < 1 || n < 1 || make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  return make_bw_layout(p, batch, n).total;
+}
+
+dory_status dory_backward_last_loop(dory_ctx* c, const float* x, const float* grad_out, int32_t batch, int32_t n,
+                                    const dory_grads* g, float* grad_x, void* ws_dev, size_t ws_bytes) {
+  if (!c) return DORY_E_ARG;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  if (!x || !grad_out || !g || !ws_dev || batch < 1 || n < 1 || n > C.max_ctx)
+    return set_err(c, DORY_E_ARG, "backward: bad arguments");
+  if (C.weight_format != DORY_WEIGHTS_DTYPE || (C.head_dim != 64 && C.head_dim != 128) || C.n_rec < 1)
+    return set_err(c, DORY_E_ARG, "backward: needs dtype weights, head_dim 64 or 128 and a recurrent block");
+  if ((int64_t)batch * n > (1 << 21)) return set_err(c, DORY_E_ARG, "backward: batch * n too large");
+  if (!g->qkvg || !g->o || !g->ug || !g->down || !g->alpha_attn || !g->alpha_mlp)
+    return set_err(c, DORY_E_ARG, "backward: null gradient array");
+  for (int i = 0; i < C.n_rec; ++i)
+    if (!g->qkvg[i] || !g->o[i] || !g->ug[i] || !g->down[i] || !g->alpha_attn[i] || !g->alpha_mlp[i])
+      return set_err(c, DORY_E_ARG, "backward: null gradient pointer");
+  Bw b{c, make_bw_layout(P, batch, n), (char*)ws_dev, batch, n, batch * n};
+  if (ws_bytes < b.L.total || ((uintptr_t)ws_dev & (kAlign - 1)))
+    return set_err(c, DORY_E_ARG, "backward: workspace too small or misaligned");
+  DORY_TRY(device_init(c));
+  const size_t rows = (size_t)b.M * C.d_model;
+  HIP_TRY(c, hipMemcpyAsync(b.h_at(0), x, rows * 4, hipMemcpyDeviceToDevice, c->st));
+  for (int i = 0; i < C.n_rec; ++i) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));
+  float* dh = b.f<float>(b.L.dh);
+  HIP_TRY(c, launch_bw_final(b.h_at(C.n_rec), grad_out, b.M, C.d_model, dh, c->st));
+  for (int i = C.n_rec - 1; i >= 0; --i) {
+    if (i < C.n_rec - 1) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));  // recompute
+    DORY_TRY(bw_layer_bwd(b, C.n_in + i, i, b.h_at(i), b.h_at(i + 1), dh, dh, g));
+  }
+  if (grad_x) HIP_TRY(c, hipMemcpyAsync(grad_x, dh, rows * 4, hipMemcpyDeviceToDevice, c->st));
+  return DORY_OK;
 }
 
 dory_status dory_op_quant_nvfp4(const void* w_dev, int32_t N, int32_t K, void* codes_dev, void* scales_dev,

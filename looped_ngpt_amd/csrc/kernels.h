@@ -175,4 +175,44 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* 
 // *pos_dev = value (one thread).
 hipError_t launch_set_pos(int* pos_dev, int value, hipStream_t st);
 
+
+// ---- depth-1 truncated backward (k_backward.hip); float32 unless a dtype
+// `dt` (0 float32, 1 bfloat16) names the GEMM operand copies ----
+struct BwAttn {
+  const float* qn;   // [M][nq*hd] normalised, rotated queries
+  const float* kn;   // [M][nkv*hd]
+  const float* v;    // values: row r at v + r*ldv
+  int ldv;
+  int n, nq, nkv, hd;
+  int window;        // 0: full causal
+  float scale;
+};
+hipError_t launch_bw_cast(int dt_out, const float* in, void* out, int64_t n, hipStream_t st);
+hipError_t launch_bw_transpose(int dt, const void* in, int64_t ld, void* out, int R, int C, hipStream_t st);
+hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
+hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, hipStream_t st);
+hipError_t launch_bw_update_fwd(int dt, const float* h, const float* y, const float* alpha, int M, int d, float* yh,
+                                float* ry, float* rz, float* hout, void* hout_t, hipStream_t st);
+hipError_t launch_bw_rope_norm_fwd(const float* P1, int ldp, const float2* tab, int n, int nq, int nkv, int hd, int M,
+                                   float* qn, float* kn, float* rq, float* rk, hipStream_t st);
+hipError_t launch_bw_attn_fwd(const BwAttn& a, int M, float* o, float* mst, float* lst, hipStream_t st);
+hipError_t launch_bw_gate_fwd(int dt, const float* o, const float* P1, int ldp, int goff, int mode, int hd, int qd,
+                              int M, float* oh, void* oh_t, float* rc, hipStream_t st);
+hipError_t launch_bw_swiglu_fwd(int dt, const float* P2, int F, int M, float* a32, void* a_t, float* rs,
+                                hipStream_t st);
+hipError_t launch_bw_final(const float* h, const float* G, int M, int d, float* dh, hipStream_t st);
+hipError_t launch_bw_update_bwd(int dt, const float* dho, const float* ho, const float* rz, const float* yh,
+                                const float* ry, const float* h, const float* alpha, int M, int d, float* dres,
+                                void* dy_t, float* contrib, hipStream_t st);
+hipError_t launch_bw_swiglu_bwd(int dt, const float* da, const float* a32, const float* rs, const float* P2, int F,
+                                int M, void* dP2, hipStream_t st);
+hipError_t launch_bw_gate_bwd(const float* doh, const float* oh, const float* rc, const float* o, const float* P1,
+                              int ldp, int goff, int mode, int hd, int qd, int M, float* dO, float* dP1,
+                              hipStream_t st);
+hipError_t launch_bw_attn_bwd(const BwAttn& a, int M, const float* dO, const float* o, const float* mst,
+                              const float* lst, float* D, float* dqn, float* dkn, float* dv, hipStream_t st);
+hipError_t launch_bw_rope_norm_bwd(const float* dqn, const float* qn, const float* rq, const float* dkn,
+                                   const float* kn, const float* rk, const float* dv, const float2* tab, int n, int nq,
+                                   int nkv, int hd, int M, float* dP1, int ldp, hipStream_t st);
+
 }  // namespace dory

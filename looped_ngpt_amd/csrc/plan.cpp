@@ -149,4 +149,62 @@ WsLayout make_ws_layout(const Plan& p) {
   return w;
 }
 
+BwLayout make_bw_layout(const Plan& p, int B, int n) {
+  BwLayout w;
+  const auto& c = p.cfg;
+  const size_t M = (size_t)B * n, d = c.d_model, F = c.d_ff, Q = p.qkvg_dim, qd = p.q_dim, kvd = p.kv_dim;
+  const size_t nq = c.n_q_heads, el = p.elem;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = at;
+    at = align_up(at + (bytes ? bytes : 1));
+    return o;
+  };
+  w.hin = take((size_t)(c.n_rec + 1) * M * d * 4);
+  w.P1 = take(M * Q * 4);
+  w.qn = take(M * qd * 4);
+  w.kn = take(M * kvd * 4);
+  w.rq = take(M * nq * 4);
+  w.rk = take(M * c.n_kv_heads * 4);
+  w.o = take(M * qd * 4);
+  w.mst = take(M * nq * 4);
+  w.lst = take(M * nq * 4);
+  w.oh = take(M * qd * 4);
+  w.rc = take(M * 4);
+  w.y = take(M * d * 4);
+  w.yh = take(M * d * 4);
+  w.ry = take(M * 4);
+  w.rz = take(M * 4);
+  w.h1 = take(M * d * 4);
+  w.P2 = take(M * 2 * F * 4);
+  w.a32 = take(M * F * 4);
+  w.rs = take(M * 4);
+  w.y2h = take(M * d * 4);
+  w.ry2 = take(M * 4);
+  w.rz2 = take(M * 4);
+  w.dres = take(M * d * 4);
+  w.contrib = take(M * d * 4);
+  w.tmp = take(M * std::max(d, std::max(F, qd)) * 4);
+  w.dh = take(M * d * 4);
+  w.dh2 = take(M * d * 4);
+  w.dO = take(M * qd * 4);
+  w.D = take(M * nq * 4);
+  w.dqn = take(M * qd * 4);
+  w.dkn = take(M * kvd * 4);
+  w.dv = take(M * kvd * 4);
+  w.dP1 = take(M * Q * 4);
+  w.xb = take(M * d * el);
+  w.ohb = take(M * qd * el);
+  w.h1b = take(M * d * el);
+  w.ab = take(M * F * el);
+  w.dyb = take(M * d * el);
+  w.dP2b = take(M * 2 * F * el);
+  w.dP1b = take(M * Q * el);
+  w.TA = take(M * std::max(Q, std::max(2 * F, d)) * el);
+  w.TB = take(M * std::max(d, std::max(F, qd)) * el);
+  w.WT = take(std::max(std::max(Q * d, 2 * F * d), std::max(d * qd, d * F)) * el);
+  w.total = at;
+  return w;
+}
+
 }  // namespace dory

@@ -71,6 +71,26 @@ dory_status make_kv_layout(const Plan& p, int kv_mode, int kv_loops, KvLayout* k
 
 WsLayout make_ws_layout(const Plan& p);
 
+// Workspace of the depth-1 backward for B sequences of n positions (M = B*n
+// rows): byte offsets. float32 unless marked; "T" arrays are GEMM operand
+// copies in the model dtype.
+struct BwLayout {
+  size_t hin = 0;                                   // [n_rec + 1][M][d]: layer inputs, then the block output
+  size_t P1 = 0, qn = 0, kn = 0, rq = 0, rk = 0;    // fused projection; rotated normalised q / k and their norms
+  size_t o = 0, mst = 0, lst = 0;                   // attention output; softmax max / sum per (row, head)
+  size_t oh = 0, rc = 0;                            // gated normalised attention output, |c|
+  size_t y = 0, yh = 0, ry = 0, rz = 0, h1 = 0;     // output projection / update of the attention sublayer
+  size_t P2 = 0, a32 = 0, rs = 0;                   // up/gate projection, activation, |s|
+  size_t y2h = 0, ry2 = 0, rz2 = 0;                 // update of the MLP sublayer
+  size_t dres = 0, contrib = 0, tmp = 0, dh = 0, dh2 = 0;
+  size_t dO = 0, D = 0, dqn = 0, dkn = 0, dv = 0, dP1 = 0;
+  size_t xb = 0, ohb = 0, h1b = 0, ab = 0, dyb = 0, dP2b = 0, dP1b = 0;  // T
+  size_t TA = 0, TB = 0, WT = 0;                    // T: transposed operands of the gradient GEMMs
+  size_t total = 0;
+};
+
+BwLayout make_bw_layout(const Plan& p, int B, int n);
+
 size_t argmax_partials(int32_t B, int32_t V);
 
 }  // namespace dory

@@ -243,3 +243,38 @@ def test_op_validation():
     assert L.dory_op_linear(1, 1 << 12, 8, 1 << 12, 1 << 12, 1, 7, 8, 1, 1.0, 0, None) == dory.DORY_E_ARG  # odd SwiGLU N
     assert L.dory_op_argmax(None, 1, 8, 1 << 12, 1 << 12, None) == dory.DORY_E_ARG
     assert dory.argmax_scratch_bytes(2, 3000) == 2 * 3 * 8
+
+
+def test_backward_workspace_and_validation():
+    """dory_backward_workspace_bytes grows with the rows; dory_backward_last_loop
+    rejects bad arguments on the host, before anything is enqueued."""
+    m = small(dtype="bf16", d_ff=704)
+    c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16)
+    a = dory.backward_workspace_bytes(c, 1, 8)
+    b = dory.backward_workspace_bytes(c, 2, 8)
+    assert 0 < a < b and dory.backward_workspace_bytes(c, 0, 8) == 0
+    # the checkpointed layer inputs alone: (n_rec + 1) * rows * d float32
+    assert a >= (m.n_rec + 1) * 8 * m.d_model * 4
+    lib = dory.lib()
+    L = m.n_rec
+    fake = (ctypes.c_void_p * L)(*[(1 << 20) * (i + 1) for i in range(L)])
+    vp = ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p))
+    g = binding.DoryGrads(qkvg=vp, o=vp, ug=vp, down=vp, alpha_attn=vp, alpha_mlp=vp)
+    ctx = FakeCtx(m, max_ctx=16)
+    assert ctx.status == dory.DORY_OK
+    ws = 1 << 30
+    call = lambda n, grads, wsb, x=1 << 12: lib.dory_backward_last_loop(ctx.h, x, 1 << 12, 1, n,
+                                                                       ctypes.byref(grads) if grads else None,
+                                                                       None, ws, wsb)
+    assert call(17, g, 1 << 40) == dory.DORY_E_ARG          # n > max_ctx
+    assert call(8, None, 1 << 40) == dory.DORY_E_ARG        # no gradient arrays
+    assert call(8, g, 100) == dory.DORY_E_ARG               # workspace too small
+    assert call(8, g, 1 << 40, x=0) == dory.DORY_E_ARG      # no input
+    zero = (ctypes.c_void_p * L)(*([0] * L))
+    g0 = binding.DoryGrads(qkvg=vp, o=vp, ug=vp, down=vp, alpha_attn=ctypes.cast(zero, ctypes.POINTER(ctypes.c_void_p)),
+                           alpha_mlp=vp)
+    assert call(8, g0, 1 << 40) == dory.DORY_E_ARG          # a null gradient pointer
+    mx = FakeCtx(m, weight_format=dory.WEIGHTS_MXFP8, scales=True, max_ctx=16)
+    assert mx.status == dory.DORY_OK
+    assert lib.dory_backward_last_loop(mx.h, 1 << 12, 1 << 12, 1, 8, ctypes.byref(g), None, ws,
+                                       1 << 40) == dory.DORY_E_ARG   # low-bit weights

@@ -1,0 +1,113 @@
+"""Depth-1 truncated backward of the last recurrent invocation on the GPU
+(dory_backward_last_loop) against the float64 oracle (oracle/backward.py):
+every gradient of every recurrent layer and the gradient of the input.
+
+float32 models: max |difference| <= 2e-4 of the tensor's largest entry (float32
+arithmetic against float64). bfloat16 models: the projections take bfloat16
+operands (activations and gradients rounded once per GEMM), so the bar is
+norm-wise: |g - g_ref| / |g_ref| <= 3e-2 (Frobenius) for every tensor."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import looped_ngpt_amd as dory  # noqa: E402
+from oracle import backward as bw  # noqa: E402
+from synth.configs import ModelConfig, get_config, scaled_config  # noqa: E402
+from synth.gen import make_weights  # noqa: E402
+
+
+def _small(gate: int, dtype: str) -> ModelConfig:
+    # 1 input, 2 recurrent (one sliding with a 5-key window, one full), 1 output layer; hd 64
+    return ModelConfig(name=f"bwg_{dtype}_{gate}", d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=96,
+                       vocab=256, n_in=1, n_rec=2, n_out=1, window=5,
+                       layer_is_full=(False, False, True, False), rope_base_swa=1.0e4, rope_base_full=1.0e6,
+                       dtype=dtype, attn_gate=gate, seed=11 + gate)
+
+
+def _alphas(cfg, w, seed):
+    rng = np.random.default_rng(seed)
+    for l in range(cfg.n_layers):
+        w[f"L{l}.alpha_a"] = rng.uniform(0.1, 0.6, cfg.d_model).astype(np.float32)
+        w[f"L{l}.alpha_m"] = rng.uniform(0.1, 0.6, cfg.d_model).astype(np.float32)
+    return w
+
+
+def _inputs(cfg, B, n, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, n, cfg.d_model))
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    G = rng.standard_normal((B, n, cfg.d_model))
+    return x.astype(np.float32), G.astype(np.float32)
+
+
+def _run(cfg, w, x, G):
+    dw = dory.upload_weights(cfg, w)
+    s = dory.Session(cfg, dw, max_batch=1, max_ctx=max(64, x.shape[1]), max_chunk=8, kv_mode="last_loop")
+    xt = torch.from_numpy(x).cuda()
+    gt = torch.from_numpy(G).cuda()
+    print(f"backward {cfg.name} B={x.shape[0]} n={x.shape[1]}", flush=True)
+    out = s.backward_last_loop(xt, gt)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def _compare(cfg, got, ref, x_shape, bar, normwise):
+    worst = 0.0
+    for l in range(cfg.n_in, cfg.n_in + cfg.n_rec):
+        for p in ("qkvg", "o", "ug", "down", "alpha_a", "alpha_m"):
+            key = f"L{l}.{p}"
+            assert got[key].shape == ref[key].shape, key
+            worst = max(worst, _err(key, got[key], ref[key], bar, normwise))
+    worst = max(worst, _err("x", got["x"].reshape(x_shape), ref["x"], bar, normwise))
+    print(f"{cfg.name}: worst {'relative Frobenius' if normwise else 'max/|max|'} error {worst:.3e}", flush=True)
+
+
+def _err(key, g, r, bar, normwise):
+    if normwise:
+        e = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    else:
+        e = np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30)
+    assert e <= bar, f"{key}: error {e:.3e} > {bar}"
+    return e
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_backward_f32_small(gate):
+    cfg = _small(gate, "f32")
+    w = _alphas(cfg, make_weights(cfg), 70 + gate)
+    x, G = _inputs(cfg, 2, 24, 80 + gate)
+    ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
+    got = _run(cfg, w, x, G)
+    _compare(cfg, got, ref, x.shape, 2e-4, normwise=False)
+
+
+def test_backward_bf16_small():
+    cfg = _small(1, "bf16")
+    w = _alphas(cfg, make_weights(cfg), 90)
+    x, G = _inputs(cfg, 2, 40, 91)
+    ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
+    got = _run(cfg, w, x, G)
+    _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
+
+
+def test_backward_bf16_36layer_widths():
+    """d 3072, 24 / 8 heads of 128, d_ff 8192: 1 input, 2 recurrent (one full), 1 output layer; 160 positions."""
+    cfg = scaled_config(get_config("c36"), n_in=1, n_rec=2, n_out=1).replace(vocab=512, name="c36w_bw")
+    cfg = cfg.replace(layer_is_full=(False, False, True, False))
+    w = _alphas(cfg, make_weights(cfg), 92)
+    x, G = _inputs(cfg, 1, 160, 93)
+    ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
+    got = _run(cfg, w, x, G)
+    _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
+
+
+def test_backward_argument_errors():
+    cfg = _small(1, "f32")
+    w = make_weights(cfg)
+    dw = dory.upload_weights(cfg, w)
+    s = dory.Session(cfg, dw, max_batch=1, max_ctx=32, max_chunk=8, kv_mode="last_loop")
+    x = torch.zeros((1, 40, cfg.d_model), dtype=torch.float32, device="cuda")
+    with pytest.raises(dory.DoryError):
+        s.backward_last_loop(x, x)            # n > max_ctx
