@@ -322,6 +322,61 @@ def run_other(args, dev):
               {"by_k": table, "roofline": roof, "dtype": f"bf16 activations, {fmt.upper()} weights"})
         return
 
+    if args.workload == "backward":
+        # depth-1 truncated backward of the last recurrent invocation: the
+        # 20 recurrent layers of the 36-layer shape on one training chunk
+        model = CONFIGS["c36"]["model"]
+        B, n = 1, args.bw_tokens
+        K = min(K, 10)                                       # a call takes a good fraction of a second
+        w = make_weights_device(model, dev)
+        sess = dory.Session(model, w, max_batch=1, max_ctx=max(n, 256), max_chunk=256, kv_mode="last_loop",
+                            stream=stream, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(model.seed * 7 + 5)
+        x = torch.randn((B, n, model.d_model), generator=g, device=dev, dtype=torch.float32)
+        x /= x.norm(dim=-1, keepdim=True)
+        G = torch.randn((B, n, model.d_model), generator=g, device=dev, dtype=torch.float32)
+        wsb = dory.backward_workspace_bytes(sess.cfg, B, n)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        grads = sess.backward_last_loop(x, G, ws=ws)       # allocates the gradients once
+        torch.cuda.synchronize()
+        for _ in range(max(Wm - 1, 0)):
+            sess.backward_last_loop(x, G, ws=ws, grads=grads)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            sess.backward_last_loop(x, G, ws=ws, grads=grads)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        M = B * n
+        params = model.layer_bytes() // 2
+        pairs_full = n * (n + 1) // 2
+        Wn = model.window
+        pairs_swa = Wn * (Wn + 1) // 2 + (n - Wn) * Wn if n > Wn else pairs_full
+        attn_fwd = sum(4 * model.q_dim * (pairs_full if model.layer_is_full[l] else pairs_swa)
+                       for l in range(model.n_in, model.n_in + model.n_rec))
+        # training FLOPs of the block: forward 2 M P + backward 4 M P per layer, attention forward + 2x backward
+        flops = model.n_rec * 6 * M * params + 3 * attn_fwd
+        log(f"backward of {model.n_rec} layers on {M} positions: {ms:.2f} ms, "
+            f"{M / (ms / 1e3):.0f} tokens/s, {flops / (ms / 1e3) / 1e12:.0f} TFLOP/s, workspace {wsb / 1e9:.2f} GB")
+        res = {
+            "metric": "depth-1 truncated backward of the last recurrent invocation, tokens/s, 1xMI355X",
+            "value": round(M / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+            "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded random-init weights, random unit inputs and gradients)",
+            "config": {"workload": f"{model.name}: backward through the {model.n_rec} recurrent layers, batch {B}, "
+                                   f"{n} positions (causal, window {model.window})", "global_batch": B,
+                       "seq_len": n, "parallelism": "none (1 GPU)"},
+            "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 1), "peak": MFMA_PEAK / 1e12,
+                         "unit": "TFLOP/s", "frac": round(flops / (ms / 1e3) / MFMA_PEAK, 4), "traffic": None,
+                         "kernel": "whole call (gradient GEMMs, attention, row kernels)", "flops": flops},
+            "workspace_bytes": wsb, "cpu_baseline": None,
+        }
+        print(json.dumps(res))
+        return
+
     # b64: 64 sequences whose 32768 cached positions are synthetic: random
     # bfloat16 values written straight into the caller-owned KV buffer, then
     # dory_resume (decode throughput does not depend on cache contents)
@@ -393,11 +448,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
-    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8", "nvfp4"], default="c36",
+    ap.add_argument("--bw-tokens", type=int, default=2048, help="positions of the backward workload")
+    ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8", "nvfp4", "backward"],
+                    default="c36",
                     help="c36: the headline (default). c72: the 72-layer shape, 16384-token prompt, k=1..4 in "
                          "both KV modes. b64: 64 sequences at 32768 cached positions (synthetic caches), k=4, "
                          "both KV modes. long: a 262144-token prompt in 8192-token chunks, k=2. mxfp8 / nvfp4: the c36 shape "
-                         "with MXFP8 / NVFP4-style layer projections, decode at k=1,2,4")
+                         "with MXFP8 / NVFP4-style layer projections, decode at k=1,2,4. backward: the depth-1 "
+                         "truncated backward of the c36 recurrent block on --bw-tokens positions")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
