@@ -146,7 +146,7 @@ int choose_splits_decode(int keys, int B, int nkv) {
   return s < 1 ? 1 : s;
 }
 
-dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv);
+dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv, bool to_acc = false);
 
 // One layer application (attention sublayer + MLP sublayer) on `rows` rows.
 // write_kv: store this application's K/V in the cache. In last-loop mode the
@@ -242,7 +242,7 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
 
 // Decode attention of layer l (loop j) on the fused projection rows: RoPE,
 // q/k norm, split-K attention, new key/value into the cache, merge and gate.
-dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv) {
+dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv, bool to_acc) {
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
   const WsLayout& W = P.ws;
@@ -269,12 +269,42 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv)
   da.part = wsp<float>(c, W.part);
   da.wloops = (c->mixed && P.recurrent(l)) ? wsp<int>(c, W.rowk) : nullptr;
   da.loop = loop;
+  da.acc = to_acc ? wsp<unsigned long long>(c, W.attn_acc) : nullptr;
+  da.gate_off = P.q_dim + 2 * P.kv_dim;
+  da.gate = C.attn_gate;
   {
     TimeScope ts(c, TIME_ATTN);
     HIP_TRY(c, launch_attn_decode(C.dtype, da, c->st));
   }
-  HIP_TRY(c, launch_attn_merge(C.dtype, da.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
-                                 c->ws + W.ob, B, C.n_q_heads, C.head_dim, da.n_split, c->st));
+  if (!to_acc)
+    HIP_TRY(c, launch_attn_merge(C.dtype, da.part, qkvg, P.qkvg_dim, P.q_dim + 2 * P.kv_dim, C.attn_gate,
+                                   c->ws + W.ob, B, C.n_q_heads, C.head_dim, da.n_split, c->st));
+  return DORY_OK;
+}
+
+// Decode attention summed into the workspace accumulators and the output
+// projection built from them (no merge launch): bfloat16 activations, at
+// most 8 rows, the matrix-core attention kernel for this layer, and an
+// output GEMV that can stage its input from the accumulators.
+bool attn_to_acc_ok(const dory_ctx* c, int l, int B) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  if (C.dtype != DORY_BF16 || B > 8 || C.head_dim % 8) return false;
+  if (!attn_decode_uses_mfma(C.dtype, C.head_dim, P.slots(l), C.window, P.is_full[l])) return false;
+  return C.weight_format == DORY_WEIGHTS_DTYPE ? linear_attn_supported(B, P.q_dim)
+                                               : linear_lowbit_supported(C.weight_format, B, P.q_dim);
+}
+
+// y = W_o . gate(attention) with the attention read from the accumulators
+dory_status proj_attn_o(dory_ctx* c, int l, int B, float* y) {
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  AttnX ax{wsp<unsigned long long>(c, P.ws.attn_acc), C.head_dim, C.n_q_heads};
+  if (C.weight_format == DORY_WEIGHTS_DTYPE)
+    HIP_TRY(c, launch_linear_attn(ax, c->o[l], y, B, C.d_model, P.q_dim, 1.f, c->st));
+  else
+    HIP_TRY(c, launch_linear_lowbit_attn(C.weight_format, ax, c->o[l], c->o_s[l], y, B, C.d_model, P.q_dim,
+                                         c->o_g[l], c->st));
   return DORY_OK;
 }
 
@@ -306,6 +336,13 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
   void* xb = c->ws + W.xb;
   HIP_TRY(c, launch_embed(dt, tok, c->embed, cur, C.n_in == 0 ? e : nullptr, xb, B, d, C.vocab,
                           wsp<int>(c, W.flags), st));
+  // attention accumulators: cleared here for the first layer application,
+  // then by each q|k|v|gate GEMV (after the previous output GEMV read them)
+  bool any_acc = false;
+  for (int l = 0; l < P.n_layers; ++l) any_acc = any_acc || attn_to_acc_ok(c, l, B);
+  unsigned long long* acc = wsp<unsigned long long>(c, W.attn_acc);
+  const int acc_n = B * C.n_q_heads * (C.head_dim + kAttnAccPad);
+  if (any_acc) HIP_TRY(c, launch_zero_u64(acc, acc_n, st));
   const float* pending_alpha = nullptr;  // MLP update not yet applied to the residual
   auto app = [&](int l, int j, bool write_kv) -> dory_status {
     if (pending_alpha) {
@@ -316,6 +353,8 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
       pr.wh = C.combine_wh; pr.we = C.combine_we;
       pr.h_out = alt;
       pr.e_out = (first_rec && j == 1) ? e : nullptr;
+      pr.zero = any_acc ? acc : nullptr;
+      pr.zero_n = acc_n;
       TimeScope ts(c, TIME_QKVG);
       DORY_TRY(proj_pro(c, pr, c->qkvg[l], c->qkvg_s[l], c->qkvg_g[l], qkvg, B, P.qkvg_dim, d, 0));
       std::swap(cur, alt);
@@ -323,11 +362,15 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
       TimeScope ts(c, TIME_QKVG);
       DORY_TRY(proj(c, c->qkvg[l], c->qkvg_s[l], c->qkvg_g[l], xb, d, qkvg, B, P.qkvg_dim, d, 0, 1.f));
     }
-    dory_status s = decode_attention(c, l, j, B, write_kv);
+    const bool to_acc = attn_to_acc_ok(c, l, B);
+    dory_status s = decode_attention(c, l, j, B, write_kv, to_acc);
     if (s != DORY_OK) return s;
     {
       TimeScope ts(c, TIME_O);
-      DORY_TRY(proj(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, B, d, P.q_dim, 0, 1.f));
+      if (to_acc)
+        DORY_TRY(proj_attn_o(c, l, B, y));
+      else
+        DORY_TRY(proj(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, B, d, P.q_dim, 0, 1.f));
     }
     {
       GemvPro pr{};

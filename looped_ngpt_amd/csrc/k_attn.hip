@@ -722,6 +722,28 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     }
   }
   __syncthreads();
+  if (a.acc) {
+    // sums referenced to the largest possible score sl2 (unit q and k), the
+    // value sums gated (linear in the sums), then 2^36 fixed point; integer
+    // adds are order-independent
+    const float* grow = a.qkvg + (size_t)b * a.ld + a.gate_off;
+    for (int e = tid; e < G * (HD + 1); e += 256) {
+      const int g = e / (HD + 1), d = e % (HD + 1);
+      const int hq = kvh * G + g;
+      float S = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (wm[w][g] == -INFINITY) continue;
+        const float f = exp2f(wm[w][g] - sl2);
+        S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], f, S);
+      }
+      if (d < HD && a.gate) S *= sigmoidf_(a.gate == 1 ? grow[hq * HD + d] : grow[hq]);
+      if (S != 0.f)
+        atomicAdd(a.acc + ((size_t)b * a.nq + hq) * (HD + kAttnAccPad) + d,
+                  (unsigned long long)llrint((double)S * 68719476736.0));
+    }
+    return;
+  }
   for (int e = tid; e < G * HD; e += 256) {
     const int g = e / HD, d = e % HD;
     float M = -INFINITY;
@@ -841,7 +863,9 @@ bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full
 
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
-  if (attn_decode_uses_mfma(dtype, a.hd, a.slots, a.window, a.is_full))
+  const bool mfma = attn_decode_uses_mfma(dtype, a.hd, a.slots, a.window, a.is_full);
+  if (a.acc && !mfma) return hipErrorInvalidValue;  // accumulators only from the matrix-core kernel
+  if (mfma)
     return a.hd == 64 ? attn_dec_mfma<64>(a, st) : attn_dec_mfma<128>(a, st);
   if (dtype == 0) {
     if (a.hd == 64) return attn_dec_hd<float, 64>(a, st);

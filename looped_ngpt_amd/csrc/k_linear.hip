@@ -102,10 +102,12 @@ __global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64
 // so the HBM latency of the weights overlaps the activation staging and the
 // workgroup barrier; then each lane multiplies its chunks and a wave
 // reduction closes the dot products.
-template <int MB, int CH, int EPI>
+// XM 1: the activations are built from decode attention accumulators (AttnX)
+// instead of read from x.
+template <int MB, int CH, int EPI, int XM = 0>
 __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, int64_t ldx,
                                                   const bf16* __restrict__ W, void* __restrict__ y, int M, int N,
-                                                  int K, float scale) {
+                                                  int K, float scale, AttnX ax) {
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
@@ -119,11 +121,15 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
   // activations first (vector loads complete in issue order), then weights
   constexpr int XV = (MB * CH + 7) / 8;  // MB rows x nv <= 64*CH vectors over 512 threads
   u32x4 xr[XV];
+  AttnXRaw xa[XM ? XV : 1];
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
     const int e = threadIdx.x + 512 * q;
     const int ec = min(e, M * nv - 1);
-    xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
+    if (XM)
+      attn_x_load(ax, ec / nv, 8 * (ec % nv), xa[XM ? q : 0]);
+    else
+      xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
   u32x4 wv[NR][CH];
@@ -141,6 +147,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
     const int e = threadIdx.x + 512 * q;
+    if (XM) xr[q] = attn_x_make(xa[XM ? q : 0]);
     if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
   }
   __syncthreads();
@@ -185,8 +192,10 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
   const dim3 grid((nout + 7) / 8);
   const size_t lds = (size_t)M * K * 2;
-#define DORY_ROWS(C) \
-  case C: dory_launch((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale); return true;
+#define DORY_ROWS(C)                                                                                         \
+  case C:                                                                                                    \
+    dory_launch((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale, AttnX{}); \
+    return true;
   switch (ch) {
     DORY_ROWS(1) DORY_ROWS(2) DORY_ROWS(3) DORY_ROWS(4) DORY_ROWS(5) DORY_ROWS(6) DORY_ROWS(8) DORY_ROWS(12)
     DORY_ROWS(16)
@@ -245,6 +254,8 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
     ev[c] = ep[i];
     av[c] = pr.alpha[i];  // before the weights: the update must not wait behind them
   }
+  if (pr.zero)
+    for (int i = blockIdx.x * kProThreads + threadIdx.x; i < pr.zero_n; i += gridDim.x * kProThreads) pr.zero[i] = 0ull;
   __builtin_amdgcn_sched_barrier(0);
   u32x4 buf[P];
 #pragma unroll
@@ -812,6 +823,42 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     dory_launch((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
   }
   return hipGetLastError();
+}
+
+bool linear_attn_supported(int M, int K) {
+  const int ch = (K / 8 + 63) / 64;
+  return M >= 1 && M <= 8 && K % 8 == 0 && (size_t)M * K * 2 <= 64 * 1024 &&
+         ((ch >= 1 && ch <= 6) || ch == 8 || ch == 12 || ch == 16);
+}
+
+template <int MB>
+static hipError_t linear_attn_mb(const AttnX& ax, const bf16* W, float* y, int M, int N, int K, float scale,
+                                 hipStream_t st) {
+  const int ch = (K / 8 + 63) / 64;
+  const dim3 grid((N + 7) / 8);
+  const size_t lds = (size_t)M * K * 2;
+#define DORY_AROWS(C)                                                                                       \
+  case C:                                                                                                   \
+    dory_launch((k_gemv_rows<MB, C, EPI_F32, 1>), grid, dim3(512), lds, st, (const bf16*)nullptr, (int64_t)K, \
+                W, (void*)y, M, N, K, scale, ax);                                                           \
+    break;
+  switch (ch) {
+    DORY_AROWS(1) DORY_AROWS(2) DORY_AROWS(3) DORY_AROWS(4) DORY_AROWS(5) DORY_AROWS(6) DORY_AROWS(8)
+    DORY_AROWS(12) DORY_AROWS(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef DORY_AROWS
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_attn(const AttnX& ax, const void* W, float* y, int M, int N, int K, float scale,
+                              hipStream_t st) {
+  if (!linear_attn_supported(M, K) || ax.hd % 8 || K != ax.nq * ax.hd || ((uintptr_t)W & 15)) return hipErrorInvalidValue;
+  const bf16* w = (const bf16*)W;
+  if (M == 1) return linear_attn_mb<1>(ax, w, y, M, N, K, scale, st);
+  if (M == 2) return linear_attn_mb<2>(ax, w, y, M, N, K, scale, st);
+  if (M <= 4) return linear_attn_mb<4>(ax, w, y, M, N, K, scale, st);
+  return linear_attn_mb<8>(ax, w, y, M, N, K, scale, st);
 }
 
 hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K, int epi,

@@ -314,10 +314,11 @@ template <> struct LowBit<LB_FP4> {
 
 // One output (two rows for SwiGLU) per wave, activations staged in LDS, small
 // loads (activations, scale bits) issued before the weights.
-template <int FMT, int MB, int CQ, int EPI>
+template <int FMT, int MB, int CQ, int EPI, int XM = 0>
 __global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x, int64_t ldx,
                                                      const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
-                                                     void* __restrict__ y, int M, int N, int K, float scale) {
+                                                     void* __restrict__ y, int M, int N, int K, float scale,
+                                                     AttnX ax) {
   using F = LowBit<FMT>;
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -331,11 +332,15 @@ __global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x
 
   constexpr int XV = (MB * CQ * F::kCodes + 63) / 64;  // M rows x nv <= 8*CQ*kCodes vectors over 512 threads
   u32x4 xr[XV];
+  AttnXRaw xa[XM ? XV : 1];
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
     const int e = threadIdx.x + 512 * q;
     const int ec = min(e, M * nv - 1);
-    xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
+    if (XM)
+      attn_x_load(ax, ec / nv, 8 * (ec % nv), xa[XM ? q : 0]);
+    else
+      xr[q] = ((const u32x4*)(x + (size_t)(ec / nv) * ldx))[ec % nv];
   }
   uint32_t sb[NR][CQ];
 #pragma unroll
@@ -355,6 +360,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
     const int e = threadIdx.x + 512 * q;
+    if (XM) xr[q] = attn_x_make(xa[XM ? q : 0]);
     if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
   }
   __syncthreads();
@@ -437,6 +443,8 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
     ev[c] = ep[i];
     av[c] = pr.alpha[i];
   }
+  if (pr.zero)
+    for (int i = blockIdx.x * kLbThreads + threadIdx.x; i < pr.zero_n; i += gridDim.x * kLbThreads) pr.zero[i] = 0ull;
   uint32_t sb[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) sb[c] = F::scale_bits(Ws, wrow(c / CQ), K, min(lane + 64 * (c % CQ), nq - 1));
@@ -546,9 +554,9 @@ int chunks_per_lane(int fmt, int K) { return (K / (fmt == LB_MX ? 16 : 32) + 63)
 // chunk counts per lane with an instantiation (rows: 1-6, 8, 12, 16; with the prologue: 1-6, 8)
 bool cq_ok(int cq, bool pro) { return (cq >= 1 && cq <= 6) || cq == 8 || (!pro && (cq == 12 || cq == 16)); }
 
-template <int FMT, int MB, int EPI>
+template <int FMT, int MB, int EPI, int XM = 0>
 hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N,
-                          int K, float scale, hipStream_t st) {
+                          int K, float scale, hipStream_t st, const AttnX& ax = AttnX{}) {
   const int cq = chunks_per_lane(FMT, K);
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
   const dim3 grid((nout + 7) / 8);
@@ -558,8 +566,8 @@ hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const u
 #define DORY_RLB(C)                                                                                                 \
   case C:                                                                                                           \
     if constexpr (C <= kMaxCq) {                                                                                    \
-      dory_launch((k_gemv_rows_lb<FMT, MB, C, EPI>), grid, dim3(512), (uint32_t)lds, st, x, ldx, Wq, Ws, y, M, N, K, \
-                  scale);                                                                                           \
+      dory_launch((k_gemv_rows_lb<FMT, MB, C, EPI, XM>), grid, dim3(512), (uint32_t)lds, st, x, ldx, Wq, Ws, y, M, N, \
+                  K, scale, ax);                                                                                    \
       break;                                                                                                        \
     } else {                                                                                                        \
       return hipErrorInvalidValue;                                                                                  \
@@ -698,6 +706,24 @@ hipError_t launch_linear_lowbit(int fmt, const void* x, int64_t ldx, const void*
     return hipErrorInvalidValue;
   return fmt == LB_MX ? linear_lb<LB_MX>(x, ldx, Wq, Ws, y, M, N, K, epi, scale, st)
                       : linear_lb<LB_FP4>(x, ldx, Wq, Ws, y, M, N, K, epi, scale, st);
+}
+
+hipError_t launch_linear_lowbit_attn(int fmt, const AttnX& ax, const void* Wq, const void* Ws, float* y, int M, int N,
+                                     int K, float scale, hipStream_t st) {
+  if (!lb_shape_ok(fmt, M, K, Wq, Ws) || !linear_lowbit_supported(fmt, M, K) || ax.hd % 8 || K != ax.nq * ax.hd)
+    return hipErrorInvalidValue;
+  const uint8_t* q = (const uint8_t*)Wq;
+  const uint8_t* s = (const uint8_t*)Ws;
+#define DORY_ALB(F)                                                                                      \
+  if (M == 1) return rows_lb_launch<F, 1, EPI_F32, 1>(nullptr, K, q, s, y, M, N, K, scale, st, ax);     \
+  if (M == 2) return rows_lb_launch<F, 2, EPI_F32, 1>(nullptr, K, q, s, y, M, N, K, scale, st, ax);     \
+  if (M <= 4) return rows_lb_launch<F, 4, EPI_F32, 1>(nullptr, K, q, s, y, M, N, K, scale, st, ax);     \
+  return rows_lb_launch<F, 8, EPI_F32, 1>(nullptr, K, q, s, y, M, N, K, scale, st, ax);
+  if (fmt == LB_MX) {
+    DORY_ALB(LB_MX)
+  }
+  DORY_ALB(LB_FP4)
+#undef DORY_ALB
 }
 
 hipError_t launch_linear_pro_lowbit(int fmt, const GemvPro& p, const void* Wq, const void* Ws, void* y, int M, int N,

@@ -5,6 +5,8 @@
 // Row kernels use one 256-thread workgroup per row of d_model elements, each
 // thread holding EPT elements in registers, so a row is read from memory once
 // and the two L2 norms are workgroup reductions.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -402,6 +404,20 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* 
   const int nblk = (V + kArgBlock - 1) / kArgBlock;
   hipLaunchKernelGGL(k_argmax_part, dim3(nblk, B), dim3(256), 0, st, logits, V, nblk, (float2*)scratch);
   hipLaunchKernelGGL(k_argmax_final, dim3(B), dim3(256), 0, st, (const float2*)scratch, nblk, out, pos_dev);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// clearing of 64-bit words (a kernel, so that recorded graphs hold no memset)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_zero_u64(unsigned long long* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0ull;
+}
+
+hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_zero_u64, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

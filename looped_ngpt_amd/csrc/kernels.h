@@ -114,7 +114,17 @@ struct AttnDecArgs {
   void* kc; void* vc;
   float* part;
   const int* wloops; int loop;
+  // optional (matrix-core kernel): instead of per-split partials, add the
+  // split's sums, referenced to the largest possible score (q and k are unit
+  // vectors, so a score never exceeds `scale`), as 2^36 fixed point with
+  // 64-bit integer atomics (order-independent, hence deterministic) into
+  // acc [B][nq][hd + 8]: sum p v times the sigmoid gate (read at gate_off of
+  // the projection row; gate 1 elementwise, 2 per head, 0 none), then sum p
+  // (7 words of padding keep rows 16-byte aligned). acc must start at zero.
+  unsigned long long* acc;
+  int gate_off, gate;
 };
+constexpr int kAttnAccPad = 8;  // words per (row, head) beyond hd
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st);
 // True when launch_attn_decode takes the matrix-core kernel, which splits the
 // keys in tiles of 32 positions (bfloat16, slots and window multiples of 4).
@@ -128,6 +138,24 @@ bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full
 // coherent stores and loads of the partials.)
 hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, int64_t ld, int gate_off, int gate,
                              void* ob, int B, int nq, int hd, int n_split, hipStream_t st);
+
+// The output projection fed straight from the decode attention accumulators
+// (AttnDecArgs::acc): input element (row m, head h, dim d) = (gated sum p v)
+// / (sum p), rounded to bfloat16 — the merge folded into the GEMV's
+// activation staging. (The concat norm before W_o is left out: the update
+// only sees norm(y), and norm(c W x) = norm(W x).)
+struct AttnX {
+  const unsigned long long* acc;
+  int hd; int nq;
+};
+hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st);
+// bfloat16 weights W [N][K = nq*hd], M <= 8 rows, y float32 [M][N] * scale
+hipError_t launch_linear_attn(const AttnX& ax, const void* W, float* y, int M, int N, int K, float scale,
+                              hipStream_t st);
+bool linear_attn_supported(int M, int K);
+// the same for low-bit weights (fmt as launch_linear_lowbit)
+hipError_t launch_linear_lowbit_attn(int fmt, const AttnX& ax, const void* Wq, const void* Ws, float* y, int M, int N,
+                                     int K, float scale, hipStream_t st);
 
 // y = x . W^T (see dory_op_linear).
 hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K,
@@ -144,6 +172,7 @@ struct GemvPro {
   const float* y; const float* h_in; const float* alpha; const float* e;
   float wh, we;
   float* h_out; float* e_out;
+  unsigned long long* zero; int zero_n;  // optional: cleared by the workgroups (decode attention accumulators)
 };
 hipError_t launch_linear_pro(const GemvPro& p, const void* W, void* y, int M, int N, int K, int epi, float scale,
                              hipStream_t st);

@@ -39,7 +39,8 @@ struct WsLayout {
   size_t flags = 0;                    // device error flags
   size_t pos = 0;                      // int: position counter read by decode kernels
   size_t rowk = 0;                     // int [max_batch]: per-sequence loop counts of a mixed call
-  size_t wdq = 0;                      // bf16: one MXFP8 projection expanded for a prefill GEMM
+  size_t wdq = 0;                      // bf16: one low-bit projection expanded for a prefill GEMM
+  size_t attn_acc = 0;                 // uint64 [min(max_batch, 8)][n_q][hd + 8]: decode attention sums
   size_t total = 0;
 };
 
