@@ -10,6 +10,8 @@
 
 namespace dory {
 
+constexpr int kNumCUs = 256;  // MI355X compute units (the grids of the decode GEMVs are sized to it)
+
 typedef uint16_t bf16;  // bfloat16 stored as its bit pattern
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte vector
 

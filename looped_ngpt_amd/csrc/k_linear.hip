@@ -104,27 +104,30 @@ __global__ __launch_bounds__(256) void k_gemv_vec(const T* __restrict__ x, int64
 // reduction closes the dot products.
 // XM 1: the activations are built from decode attention accumulators (AttnX)
 // instead of read from x.
-template <int MB, int CH, int EPI, int XM = 0>
-__global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, int64_t ldx,
-                                                  const bf16* __restrict__ W, void* __restrict__ y, int M, int N,
-                                                  int K, float scale, AttnX ax) {
+// NW waves per workgroup (one output each): 8, or nout / 256 so that the
+// grid is exactly one workgroup per CU (3072 outputs: 12 waves).
+template <int MB, int CH, int EPI, int XM = 0, int NW = 8>
+__global__ __launch_bounds__(NW * 64) void k_gemv_rows(const bf16* __restrict__ x, int64_t ldx,
+                                                      const bf16* __restrict__ W, void* __restrict__ y, int M, int N,
+                                                      int K, float scale, AttnX ax) {
+  constexpr int NT = NW * 64;
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nv = K / 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const int o = blockIdx.x * 8 + wave;
+  const int o = blockIdx.x * NW + wave;
   const bool live = o < nout;
   const int oc = live ? o : nout - 1;
 
   // activations first (vector loads complete in issue order), then weights
-  constexpr int XV = (MB * CH + 7) / 8;  // MB rows x nv <= 64*CH vectors over 512 threads
+  constexpr int XV = (MB * CH * 64 + NT - 1) / NT;  // MB rows x nv <= 64*CH vectors over NT threads
   u32x4 xr[XV];
   AttnXRaw xa[XM ? XV : 1];
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
-    const int e = threadIdx.x + 512 * q;
+    const int e = threadIdx.x + NT * q;
     const int ec = min(e, M * nv - 1);
     if (XM)
       attn_x_load(ax, ec / nv, 8 * (ec % nv), xa[XM ? q : 0]);
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
   }
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
-    const int e = threadIdx.x + 512 * q;
+    const int e = threadIdx.x + NT * q;
     if (XM) xr[q] = attn_x_make(xa[XM ? q : 0]);
     if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
   }
@@ -185,16 +188,25 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const bf16* __restrict__ x, i
   }
 }
 
-template <int MB, int EPI>
-static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
-                             hipStream_t st) {
+// waves per workgroup of the rows kernels: one workgroup per CU when the
+// outputs split evenly that way (12 for 3072 outputs, 9 for 2304), else 8
+int rows_waves(int nout) {
+  if (nout % kNumCUs == 0 && (nout / kNumCUs == 9 || nout / kNumCUs == 12 || nout / kNumCUs == 16))
+    return nout / kNumCUs;
+  return 8;
+}
+
+template <int MB, int EPI, int NW>
+static bool gemv_rows_launch_nw(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                                hipStream_t st) {
   const int ch = (K / 8 + 63) / 64;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const dim3 grid((nout + 7) / 8);
+  const dim3 grid((nout + NW - 1) / NW);
   const size_t lds = (size_t)M * K * 2;
-#define DORY_ROWS(C)                                                                                         \
-  case C:                                                                                                    \
-    dory_launch((k_gemv_rows<MB, C, EPI>), grid, dim3(512), lds, st, x, ldx, W, y, M, N, K, scale, AttnX{}); \
+#define DORY_ROWS(C)                                                                                          \
+  case C:                                                                                                     \
+    dory_launch((k_gemv_rows<MB, C, EPI, 0, NW>), grid, dim3(NW * 64), lds, st, x, ldx, W, y, M, N, K, scale, \
+                AttnX{});                                                                                     \
     return true;
   switch (ch) {
     DORY_ROWS(1) DORY_ROWS(2) DORY_ROWS(3) DORY_ROWS(4) DORY_ROWS(5) DORY_ROWS(6) DORY_ROWS(8) DORY_ROWS(12)
@@ -202,6 +214,17 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
     default: return false;
   }
 #undef DORY_ROWS
+}
+
+template <int MB, int EPI>
+static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                             hipStream_t st) {
+  switch (rows_waves(EPI == EPI_SWIGLU ? N / 2 : N)) {
+    case 9: return gemv_rows_launch_nw<MB, EPI, 9>(x, ldx, W, y, M, N, K, scale, st);
+    case 12: return gemv_rows_launch_nw<MB, EPI, 12>(x, ldx, W, y, M, N, K, scale, st);
+    case 16: return gemv_rows_launch_nw<MB, EPI, 16>(x, ldx, W, y, M, N, K, scale, st);
+    default: return gemv_rows_launch_nw<MB, EPI, 8>(x, ldx, W, y, M, N, K, scale, st);
+  }
 }
 
 // k_gemv_rows with the residual update in the prologue (see launch_linear_pro).
@@ -831,16 +854,16 @@ bool linear_attn_supported(int M, int K) {
          ((ch >= 1 && ch <= 6) || ch == 8 || ch == 12 || ch == 16);
 }
 
-template <int MB>
-static hipError_t linear_attn_mb(const AttnX& ax, const bf16* W, float* y, int M, int N, int K, float scale,
+template <int MB, int NW>
+static hipError_t linear_attn_nw(const AttnX& ax, const bf16* W, float* y, int M, int N, int K, float scale,
                                  hipStream_t st) {
   const int ch = (K / 8 + 63) / 64;
-  const dim3 grid((N + 7) / 8);
+  const dim3 grid((N + NW - 1) / NW);
   const size_t lds = (size_t)M * K * 2;
 #define DORY_AROWS(C)                                                                                       \
   case C:                                                                                                   \
-    dory_launch((k_gemv_rows<MB, C, EPI_F32, 1>), grid, dim3(512), lds, st, (const bf16*)nullptr, (int64_t)K, \
-                W, (void*)y, M, N, K, scale, ax);                                                           \
+    dory_launch((k_gemv_rows<MB, C, EPI_F32, 1, NW>), grid, dim3(NW * 64), lds, st, (const bf16*)nullptr,   \
+                (int64_t)K, W, (void*)y, M, N, K, scale, ax);                                               \
     break;
   switch (ch) {
     DORY_AROWS(1) DORY_AROWS(2) DORY_AROWS(3) DORY_AROWS(4) DORY_AROWS(5) DORY_AROWS(6) DORY_AROWS(8)
@@ -849,6 +872,17 @@ static hipError_t linear_attn_mb(const AttnX& ax, const bf16* W, float* y, int M
   }
 #undef DORY_AROWS
   return hipGetLastError();
+}
+
+template <int MB>
+static hipError_t linear_attn_mb(const AttnX& ax, const bf16* W, float* y, int M, int N, int K, float scale,
+                                 hipStream_t st) {
+  switch (rows_waves(N)) {
+    case 9: return linear_attn_nw<MB, 9>(ax, W, y, M, N, K, scale, st);
+    case 12: return linear_attn_nw<MB, 12>(ax, W, y, M, N, K, scale, st);
+    case 16: return linear_attn_nw<MB, 16>(ax, W, y, M, N, K, scale, st);
+    default: return linear_attn_nw<MB, 8>(ax, W, y, M, N, K, scale, st);
+  }
 }
 
 hipError_t launch_linear_attn(const AttnX& ax, const void* W, float* y, int M, int N, int K, float scale,

@@ -314,28 +314,29 @@ template <> struct LowBit<LB_FP4> {
 
 // One output (two rows for SwiGLU) per wave, activations staged in LDS, small
 // loads (activations, scale bits) issued before the weights.
-template <int FMT, int MB, int CQ, int EPI, int XM = 0>
-__global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x, int64_t ldx,
-                                                     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
-                                                     void* __restrict__ y, int M, int N, int K, float scale,
-                                                     AttnX ax) {
+template <int FMT, int MB, int CQ, int EPI, int XM = 0, int NW = 8>
+__global__ __launch_bounds__(NW * 64) void k_gemv_rows_lb(const bf16* __restrict__ x, int64_t ldx,
+                                                         const uint8_t* __restrict__ Wq,
+                                                         const uint8_t* __restrict__ Ws, void* __restrict__ y, int M,
+                                                         int N, int K, float scale, AttnX ax) {
   using F = LowBit<FMT>;
+  constexpr int NT = NW * 64;
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nv = K / 8, nq = K / F::kCodes;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const int o = blockIdx.x * 8 + wave;
+  const int o = blockIdx.x * NW + wave;
   const bool live = o < nout;
   const int oc = live ? o : nout - 1;
 
-  constexpr int XV = (MB * CQ * F::kCodes + 63) / 64;  // M rows x nv <= 8*CQ*kCodes vectors over 512 threads
+  constexpr int XV = (MB * CQ * F::kCodes * 8 + NT - 1) / NT;  // M rows x nv <= 8*CQ*kCodes vectors over NT threads
   u32x4 xr[XV];
   AttnXRaw xa[XM ? XV : 1];
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
-    const int e = threadIdx.x + 512 * q;
+    const int e = threadIdx.x + NT * q;
     const int ec = min(e, M * nv - 1);
     if (XM)
       attn_x_load(ax, ec / nv, 8 * (ec % nv), xa[XM ? q : 0]);
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows_lb(const bf16* __restrict__ x
   }
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
-    const int e = threadIdx.x + 512 * q;
+    const int e = threadIdx.x + NT * q;
     if (XM) xr[q] = attn_x_make(xa[XM ? q : 0]);
     if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
   }
@@ -554,20 +555,20 @@ int chunks_per_lane(int fmt, int K) { return (K / (fmt == LB_MX ? 16 : 32) + 63)
 // chunk counts per lane with an instantiation (rows: 1-6, 8, 12, 16; with the prologue: 1-6, 8)
 bool cq_ok(int cq, bool pro) { return (cq >= 1 && cq <= 6) || cq == 8 || (!pro && (cq == 12 || cq == 16)); }
 
-template <int FMT, int MB, int EPI, int XM = 0>
-hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N,
-                          int K, float scale, hipStream_t st, const AttnX& ax = AttnX{}) {
+template <int FMT, int MB, int EPI, int XM, int NW>
+hipError_t rows_lb_launch_nw(const bf16* x, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N,
+                             int K, float scale, hipStream_t st, const AttnX& ax) {
   const int cq = chunks_per_lane(FMT, K);
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const dim3 grid((nout + 7) / 8);
+  const dim3 grid((nout + NW - 1) / NW);
   const size_t lds = (size_t)M * K * 2;
   // M * K * 2 <= 64 KiB bounds K, hence the chunk counts worth instantiating
   constexpr int kMaxCq = (32768 / MB / LowBit<FMT>::kCodes + 63) / 64;
 #define DORY_RLB(C)                                                                                                 \
   case C:                                                                                                           \
     if constexpr (C <= kMaxCq) {                                                                                    \
-      dory_launch((k_gemv_rows_lb<FMT, MB, C, EPI, XM>), grid, dim3(512), (uint32_t)lds, st, x, ldx, Wq, Ws, y, M, N, \
-                  K, scale, ax);                                                                                    \
+      dory_launch((k_gemv_rows_lb<FMT, MB, C, EPI, XM, NW>), grid, dim3(NW * 64), (uint32_t)lds, st, x, ldx, Wq, Ws, \
+                  y, M, N, K, scale, ax);                                                                           \
       break;                                                                                                        \
     } else {                                                                                                        \
       return hipErrorInvalidValue;                                                                                  \
@@ -578,6 +579,17 @@ hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const u
   }
 #undef DORY_RLB
   return hipGetLastError();
+}
+
+template <int FMT, int MB, int EPI, int XM = 0>
+hipError_t rows_lb_launch(const bf16* x, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, void* y, int M, int N,
+                          int K, float scale, hipStream_t st, const AttnX& ax = AttnX{}) {
+  switch (rows_waves(EPI == EPI_SWIGLU ? N / 2 : N)) {
+    case 9: return rows_lb_launch_nw<FMT, MB, EPI, XM, 9>(x, ldx, Wq, Ws, y, M, N, K, scale, st, ax);
+    case 12: return rows_lb_launch_nw<FMT, MB, EPI, XM, 12>(x, ldx, Wq, Ws, y, M, N, K, scale, st, ax);
+    case 16: return rows_lb_launch_nw<FMT, MB, EPI, XM, 16>(x, ldx, Wq, Ws, y, M, N, K, scale, st, ax);
+    default: return rows_lb_launch_nw<FMT, MB, EPI, XM, 8>(x, ldx, Wq, Ws, y, M, N, K, scale, st, ax);
+  }
 }
 
 template <int FMT, int MB, int EPI>

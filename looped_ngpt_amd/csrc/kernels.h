@@ -144,6 +144,9 @@ hipError_t launch_attn_merge(int dtype, const float* part, const float* qkvg, in
 // / (sum p), rounded to bfloat16 — the merge folded into the GEMV's
 // activation staging. (The concat norm before W_o is left out: the update
 // only sees norm(y), and norm(c W x) = norm(W x).)
+// waves per workgroup of the one-output-per-wave GEMVs for `nout` outputs
+int rows_waves(int nout);
+
 struct AttnX {
   const unsigned long long* acc;
   int hd; int nq;
