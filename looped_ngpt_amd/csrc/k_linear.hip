@@ -256,9 +256,14 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   const int o0 = (blockIdx.x * NW + wave) * R;  // outputs o0 .. o0+R-1
   const bool live = o0 < nout;
 
-  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU
+  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU.
+  // Chunk c: with few rows M the order is position-major (c = cc * NR + j) so
+  // that a position's activations are read from LDS once for all NR rows.
+  constexpr bool kReuse = MB <= 2;
+  auto cj = [](int c) { return kReuse ? c % NR : c / CH; };
+  auto ccq = [](int c) { return kReuse ? c / NR : c % CH; };
   auto chunk_ptr = [&](int c) -> const u32x4* {
-    const int j = c / CH, cc = c % CH;
+    const int j = cj(c), cc = ccq(c);
     const int oc = min(o0 + j % R, nout - 1);
     const int v = min(lane + 64 * cc, nv - 1);  // clamped: chunks past the row are ignored below
     return (const u32x4*)(W + (size_t)(j >= R ? nout + oc : oc) * K) + v;
@@ -348,16 +353,22 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+  u32x4 xq[kReuse ? MB : 1];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const u32x4 w = buf[c % P];
     if (c + P < NC) buf[c % P] = __builtin_nontemporal_load(chunk_ptr(c + P));
-    const int j = c / CH, cc = c % CH;
+    const int j = cj(c), cc = ccq(c);
+    if (kReuse && j == 0) {
+#pragma unroll
+      for (int m = 0; m < (kReuse ? MB : 1); ++m)
+        if (m < M) xq[m] = ((const u32x4*)(xs + (size_t)m * K))[min(lane + 64 * cc, nv - 1)];
+    }
     if (lane + 64 * cc < nv) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (m < M) {
-          const u32x4 xv = ((const u32x4*)(xs + (size_t)m * K))[lane + 64 * cc];
+          const u32x4 xv = kReuse ? xq[kReuse ? m : 0] : ((const u32x4*)(xs + (size_t)m * K))[lane + 64 * cc];
           acc[m][j] = dot16(w, xv, (const bf16*)nullptr, acc[m][j]);
         }
       }

@@ -268,9 +268,19 @@ template <> struct LowBit<LB_MX> {
   __device__ static uint32_t scale_bits(const uint8_t* Ws, size_t row, int K, int v) {
     return Ws[row * (size_t)(K / 32) + v / 2];
   }
-  // <16 E4M3 weights, 16 bfloat16 activations of xm> * 2^X + acc
+  static constexpr int kXV = 2;  // activation vectors (8 bfloat16) per chunk
+  __device__ static void load_x(const u32x4* xm, int v, u32x4 (&x)[kXV]) {
+    x[0] = xm[2 * v];
+    x[1] = xm[2 * v + 1];
+  }
   __device__ static float dot(const u32x4& w, const u32x4* xm, int v, uint32_t sb, float acc) {
-    const u32x4 x0 = xm[2 * v], x1 = xm[2 * v + 1];
+    u32x4 x[kXV];
+    load_x(xm, v, x);
+    return dot_x(w, x, sb, acc);
+  }
+  // <16 E4M3 weights, 16 bfloat16 activations> * 2^X + acc
+  __device__ static float dot_x(const u32x4& w, const u32x4 (&x)[kXV], uint32_t sb, float acc) {
+    const u32x4 x0 = x[0], x1 = x[1];
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -294,13 +304,23 @@ template <> struct LowBit<LB_FP4> {
   __device__ static uint32_t scale_bits(const uint8_t* Ws, size_t row, int K, int v) {
     return *(const uint16_t*)(Ws + row * (size_t)(K / 16) + 2 * v);
   }
-  // <32 E2M1 weights, 32 bfloat16 activations of xm>, block by block scaled, + acc
+  static constexpr int kXV = 4;
+  __device__ static void load_x(const u32x4* xm, int v, u32x4 (&x)[kXV]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = xm[4 * v + i];
+  }
   __device__ static float dot(const u32x4& w, const u32x4* xm, int v, uint32_t sb, float acc) {
+    u32x4 x[kXV];
+    load_x(xm, v, x);
+    return dot_x(w, x, sb, acc);
+  }
+  // <32 E2M1 weights, 32 bfloat16 activations>, block by block scaled, + acc
+  __device__ static float dot_x(const u32x4& w, const u32x4 (&x)[kXV], uint32_t sb, float acc) {
     const auto sc = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
     float p[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // word i: elements 8i..8i+7, block i / 2
-      const u32x4 xv = xm[4 * v + i];
+      const u32x4 xv = x[i];
       float t = p[i >> 1];
       t = dot2bf(DORY_FP4_PAIR(w[i], 0), xv[0], t);
       t = dot2bf(DORY_FP4_PAIR(w[i], 1), xv[1], t);
@@ -426,11 +446,16 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
   const int o0 = (blockIdx.x * NW + wave) * R;
   const bool live = o0 < nout;
 
-  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU
+  // row j of this wave: output o0 + j % R; the u row (j < R) or the v row of SwiGLU.
+  // Chunk c: with few rows M the order is position-major (c = cc * NR + j) so
+  // that a position's activations are read from LDS once for all NR rows.
+  constexpr bool kReuse = MB <= 2;
+  auto cj = [](int c) { return kReuse ? c % NR : c / CQ; };
+  auto ccq = [](int c) { return kReuse ? c / NR : c % CQ; };
   auto wrow = [&](int j) { const int oc = min(o0 + j % R, nout - 1); return j >= R ? nout + oc : oc; };
   auto chunk_ptr = [&](int c) -> const u32x4* {
-    const int v = min(lane + 64 * (c % CQ), nq - 1);  // clamped: chunks past the row are ignored below
-    return (const u32x4*)(Wq + (size_t)wrow(c / CQ) * F::row_bytes(K)) + v;
+    const int v = min(lane + 64 * ccq(c), nq - 1);  // clamped: chunks past the row are ignored below
+    return (const u32x4*)(Wq + (size_t)wrow(cj(c)) * F::row_bytes(K)) + v;
   };
 
   // prologue inputs of row 0 and the scale bits first, then the weight window
@@ -448,7 +473,7 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
     for (int i = blockIdx.x * kLbThreads + threadIdx.x; i < pr.zero_n; i += gridDim.x * kLbThreads) pr.zero[i] = 0ull;
   uint32_t sb[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) sb[c] = F::scale_bits(Ws, wrow(c / CQ), K, min(lane + 64 * (c % CQ), nq - 1));
+  for (int c = 0; c < NC; ++c) sb[c] = F::scale_bits(Ws, wrow(cj(c)), K, min(lane + 64 * ccq(c), nq - 1));
   __builtin_amdgcn_sched_barrier(0);
   u32x4 buf[P];
 #pragma unroll
@@ -518,17 +543,25 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[m][j] = 0.f;
+  u32x4 xq[kReuse ? MB : 1][F::kXV];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const u32x4 w = buf[c % P];
     if (c + P < NC) buf[c % P] = __builtin_nontemporal_load(chunk_ptr(c + P));
-    const int j = c / CQ, v = lane + 64 * (c % CQ);
+    const int j = cj(c), v = lane + 64 * ccq(c);
+    if (kReuse && j == 0) {
+#pragma unroll
+      for (int m = 0; m < (kReuse ? MB : 1); ++m)
+        if (m < M) F::load_x((const u32x4*)(xs + (size_t)m * K), min(v, nq - 1), xq[m]);
+    }
     if (v < nq) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (m < M) {
-          const u32x4* xm = (const u32x4*)(xs + (size_t)m * K);
-          acc[m][j] = F::dot(w, xm, v, sb[c], acc[m][j]);
+          if (kReuse)
+            acc[m][j] = F::dot_x(w, xq[kReuse ? m : 0], sb[c], acc[m][j]);
+          else
+            acc[m][j] = F::dot(w, (const u32x4*)(xs + (size_t)m * K), v, sb[c], acc[m][j]);
         }
       }
     }
