@@ -335,6 +335,34 @@ def test_nvfp4_weights_generate(name, k, mode, n, steps, ctx):
 
 
 # ---------------------------------------------------------------------------
+# batched decode across the row-count boundaries of the decode kernels: up to
+# 8 rows take the GEMVs (sums by atomics into the output GEMV), more rows the
+# split merge and the tiled GEMMs (low-bit weights expanded to bfloat16)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,fmt,B", [("tiny_bf16", "bf16", 10), ("tiny_bf16", "bf16", 7),
+                                        ("tiny_mx", "mxfp8", 10), ("tiny_mx", "mxfp8", 5),
+                                        ("tiny_mx", "nvfp4", 3), ("tiny_mx", "nvfp4", 9)])
+def test_batched_decode_row_paths(name, fmt, B):
+    m, w, dw = model_and_weights(name)
+    k, n, steps, ctx = 2, 40, 6, 64
+    prompt = make_tokens(m, 70 + B, (B, n))
+    if fmt == "bf16":
+        ow, gw, wf = w, dw, dory.WEIGHTS_DTYPE
+    elif fmt == "mxfp8":
+        ow, gw, wf = _mx_oracle_weights(m, w), dory.quantize_weights_mxfp8(m, dw), dory.WEIGHTS_MXFP8
+    else:
+        ow, gw, wf = _fp4_oracle_weights(name, m, w), dory.quantize_weights_nvfp4(m, dw), dory.WEIGHTS_NVFP4
+    ora = LoopedNGPT(m, ow, max_ctx=ctx, batch=B)
+    o_tok, o_log = ora.generate(prompt, steps, k, "last_loop")
+    s = dory.Session(m, gw, max_batch=B, max_ctx=ctx, max_chunk=n, max_loops=8, kv_mode="last_loop",
+                     weight_format=wf)
+    g_tok, g_log, lib_next = generate(s, prompt, steps, k)
+    assert _report(f"{name} {fmt} batch {B}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+    np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
+
+
+# ---------------------------------------------------------------------------
 # resuming from a caller-filled KV buffer: a copy of one context's cache,
 # resumed in a second context, decodes exactly like the first
 # ---------------------------------------------------------------------------
