@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "blaslt.h"
 #include "dory.h"
 #include "kernels.h"
 #include "plan.h"
@@ -45,6 +46,7 @@ struct dory_ctx {
   std::vector<Graph> graphs;
   hipStream_t gst = nullptr;
   hipEvent_t gev[2] = {nullptr, nullptr};
+  BlasLt* blas = nullptr;  // hipBLASLt for the plain prefill GEMMs (nullptr without a device)
   // timing tap
   int time_kind = 0;
   std::vector<hipEvent_t> ev;
@@ -58,6 +60,7 @@ struct dory_ctx {
     graphs.clear();
   }
   ~dory_ctx() {
+    blaslt_destroy(blas);
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     drop_graphs();
     for (hipEvent_t e : gev)
@@ -113,14 +116,19 @@ dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void*
   const Plan& P = c->plan;
   const int dt = P.cfg.dtype;
   const int fmt = P.cfg.weight_format;
+  // plain bfloat16 GEMMs at prefill row counts: hipBLASLt (its own algorithm per shape)
+  auto library = [&](const void* w, float s) {
+    return epi == 0 && dt == DORY_BF16 && M >= kBlasMinRows && c->blas &&
+           blaslt_gemm(c->blas, x, ldx, w, (float*)y, M, N, K, s, c->ws + P.ws.blas, kBlasWsBytes, c->st);
+  };
   if (fmt == DORY_WEIGHTS_DTYPE) {
-    HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
+    if (!library(W, scale)) HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
   } else if (linear_lowbit_supported(fmt, M, K)) {
     HIP_TRY(c, launch_linear_lowbit(fmt, x, ldx, W, S, y, M, N, K, epi, scale * g, c->st));
   } else {
     void* wdq = c->ws + P.ws.wdq;
     HIP_TRY(c, launch_dequant_lowbit(fmt, W, S, N, K, wdq, c->st));
-    HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale * g, 0, c->st));
+    if (!library(wdq, scale * g)) HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale * g, 0, c->st));
   }
   return DORY_OK;
 }
@@ -570,8 +578,13 @@ struct Bw {
 };
 
 // y[M][N] = x[M][K] . W[N][K]^T, float32 out, operands in the model dtype
+// (bfloat16 with enough rows: hipBLASLt)
 dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K) {
-  HIP_TRY(c, launch_linear(c->plan.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
+  const Plan& P = c->plan;
+  if (P.cfg.dtype == DORY_BF16 && M >= kBlasMinRows && c->blas &&
+      blaslt_gemm(c->blas, x, ldx, W, y, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st))
+    return DORY_OK;
+  HIP_TRY(c, launch_linear(P.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
   return DORY_OK;
 }
 
@@ -809,6 +822,7 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, void* kv_
   c->kvb = (char*)kv_dev;
   c->ws = (char*)ws_dev;
   c->st = (hipStream_t)stream;
+  if (P.cfg.dtype == DORY_BF16) c->blas = blaslt_create();  // needs a device; none: our GEMM throughout
   *out = c;
   return DORY_OK;
 }

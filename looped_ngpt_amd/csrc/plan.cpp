@@ -140,6 +140,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.flags = take(256);
   w.pos = take(4);
   w.rowk = take((size_t)c.max_batch * 4);
+  w.blas = take(kBlasWsBytes);
   w.attn_acc = take((size_t)std::min(c.max_batch, 8) * c.n_q_heads * (c.head_dim + kAttnAccPad) * 8);
   if (c.weight_format != DORY_WEIGHTS_DTYPE) {  // one projection expanded to bfloat16 for prefill GEMMs
     const size_t d = c.d_model;

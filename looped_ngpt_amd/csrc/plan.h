@@ -16,6 +16,8 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kMaxSplits = 64;        // split-K pieces per (row, kv head) in decode attention
 constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
 constexpr size_t kAlign = 256;
+constexpr size_t kBlasWsBytes = 32u << 20;  // workspace handed to hipBLASLt for prefill GEMMs
+constexpr int kBlasMinRows = 256;           // prefill rows from which plain GEMMs go to hipBLASLt
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 // Row length of a call's transposed values [B][n_kv][hd][vld]: n rounded up
@@ -40,6 +42,7 @@ struct WsLayout {
   size_t pos = 0;                      // int: position counter read by decode kernels
   size_t rowk = 0;                     // int [max_batch]: per-sequence loop counts of a mixed call
   size_t wdq = 0;                      // bf16: one low-bit projection expanded for a prefill GEMM
+  size_t blas = 0;                     // hipBLASLt workspace (kBlasWsBytes)
   size_t attn_acc = 0;                 // uint64 [min(max_batch, 8)][n_q][hd + 8]: decode attention sums
   size_t total = 0;
 };
