@@ -559,9 +559,12 @@ def main():
                 sess.prefill(prompt, k)
                 tot, cnt = sess.kernel_time()
                 sess.set_kernel_timing(None)
+                if cnt == 0 or tot <= 0:
+                    continue
                 if kind == "ug":
                     fl = 2.0 * n * 2 * model.d_ff * model.d_model * cnt
-                    name = "up/gate GEMM with SwiGLU (M=%d, N=%d, K=%d)" % (n, 2 * model.d_ff, model.d_model)
+                    name = ("up/gate projection + SwiGLU (M=%d, N=%d, K=%d; hipBLASLt GEMM to bfloat16, then the "
+                            "activation kernel)" % (n, 2 * model.d_ff, model.d_model))
                 else:
                     fl = float(attn_flops(model, k, n))
                     name = "attention (flash, causal + window %d)" % model.window

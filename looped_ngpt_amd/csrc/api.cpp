@@ -116,10 +116,32 @@ dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void*
   const Plan& P = c->plan;
   const int dt = P.cfg.dtype;
   const int fmt = P.cfg.weight_format;
-  // plain bfloat16 GEMMs at prefill row counts: hipBLASLt (its own algorithm per shape)
-  auto library = [&](const void* w, float s) {
-    return epi == 0 && dt == DORY_BF16 && M >= kBlasMinRows && c->blas &&
-           blaslt_gemm(c->blas, x, ldx, w, (float*)y, M, N, K, s, c->ws + P.ws.blas, kBlasWsBytes, c->st);
+  // bfloat16 GEMMs at prefill row counts: hipBLASLt (its own algorithm per
+  // shape). SwiGLU: the library writes u | v in bfloat16 into the fused
+  // projection's buffer (free once attention has run) and a row kernel
+  // applies the activation — u and v are rounded to bfloat16 on this path.
+  auto library = [&](const void* w, float s) -> bool {
+    if (dt != DORY_BF16 || M < kBlasMinRows || !c->blas) return false;
+    const size_t need = (size_t)M * N * 2, have = (size_t)P.max_rows * P.qkvg_dim * 4;
+    if (epi != 0 && (need > have || (N / 2) % 8)) return false;
+    // a pending timing pair brackets the library call(s) on the stream
+    const LaunchEvents ev = take_next_launch_events();
+    if (ev.start) (void)hipEventRecord(ev.start, c->st);
+    bool ok;
+    if (epi == 0) {
+      ok = blaslt_gemm(c->blas, x, ldx, w, y, false, M, N, K, s, c->ws + P.ws.blas, kBlasWsBytes, c->st);
+    } else {
+      void* uv = c->ws + P.ws.qkvg;
+      ok = blaslt_gemm(c->blas, x, ldx, w, uv, true, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st) &&
+           launch_swiglu_rows(uv, M, N / 2, s, y, c->st) == hipSuccess;
+    }
+    if (ev.start) {
+      if (ok)
+        (void)hipEventRecord(ev.stop, c->st);
+      else
+        set_next_launch_events(ev.start, ev.stop);  // hand the pair on to our GEMM
+    }
+    return ok;
   };
   if (fmt == DORY_WEIGHTS_DTYPE) {
     if (!library(W, scale)) HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
@@ -582,7 +604,7 @@ struct Bw {
 dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K) {
   const Plan& P = c->plan;
   if (P.cfg.dtype == DORY_BF16 && M >= kBlasMinRows && c->blas &&
-      blaslt_gemm(c->blas, x, ldx, W, y, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st))
+      blaslt_gemm(c->blas, x, ldx, W, y, false, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st))
     return DORY_OK;
   HIP_TRY(c, launch_linear(P.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
   return DORY_OK;

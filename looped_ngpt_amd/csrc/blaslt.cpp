@@ -1,4 +1,4 @@
-// Plain prefill projections on hipBLASLt: y[M][N] (float32) = scale *
+// Plain prefill projections on hipBLASLt: y[M][N] (float32 or bfloat16) = scale *
 // x[M][K] (bfloat16, row stride ldx) . W[N][K]^T (bfloat16). These are
 // library GEMMs with no fused epilogue (q|k|v|gate, output, down at prefill
 // row counts); the fused ones (SwiGLU, decode GEMVs) stay on our kernels.
@@ -23,7 +23,7 @@ struct BlasLt {
     size_t ws = 0;
     bool ok = false;
   };
-  std::map<std::tuple<int, int, int, int64_t>, Plan> plans;
+  std::map<std::tuple<int, int, int, int64_t, int>, Plan> plans;
   ~BlasLt() {
     for (auto& kv : plans) {
       Plan& p = kv.second;
@@ -53,8 +53,8 @@ BlasLt* blaslt_create() {
 
 void blaslt_destroy(BlasLt* b) { delete b; }
 
-static BlasLt::Plan* plan_for(BlasLt* b, int M, int N, int K, int64_t ldx, size_t ws_bytes) {
-  auto key = std::make_tuple(M, N, K, ldx);
+static BlasLt::Plan* plan_for(BlasLt* b, int M, int N, int K, int64_t ldx, bool bf16_out, size_t ws_bytes) {
+  auto key = std::make_tuple(M, N, K, ldx, bf16_out ? 1 : 0);
   auto it = b->plans.find(key);
   if (it != b->plans.end()) return it->second.ok ? &it->second : nullptr;
   BlasLt::Plan& p = b->plans[key];
@@ -66,7 +66,7 @@ static BlasLt::Plan* plan_for(BlasLt* b, int M, int N, int K, int64_t ldx, size_
                  HIPBLAS_STATUS_SUCCESS;
   ok = ok && hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
   ok = ok && hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, K, M, ldx) == HIPBLAS_STATUS_SUCCESS;
-  ok = ok && hipblasLtMatrixLayoutCreate(&p.c, HIP_R_32F, N, M, N) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&p.c, bf16_out ? HIP_R_16BF : HIP_R_32F, N, M, N) == HIPBLAS_STATUS_SUCCESS;
   hipblasLtMatmulPreference_t pref = nullptr;
   ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
   const uint64_t wsb = ws_bytes;
@@ -86,10 +86,10 @@ static BlasLt::Plan* plan_for(BlasLt* b, int M, int N, int K, int64_t ldx, size_
   return ok ? &p : nullptr;
 }
 
-bool blaslt_gemm(BlasLt* b, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K, float scale,
-                 void* ws, size_t ws_bytes, hipStream_t st) {
+bool blaslt_gemm(BlasLt* b, const void* x, int64_t ldx, const void* W, void* y, bool bf16_out, int M, int N, int K,
+                 float scale, void* ws, size_t ws_bytes, hipStream_t st) {
   if (!b || M <= 0 || N <= 0 || K <= 0) return false;
-  BlasLt::Plan* p = plan_for(b, M, N, K, ldx, ws_bytes);
+  BlasLt::Plan* p = plan_for(b, M, N, K, ldx, bf16_out, ws_bytes);
   if (!p) return false;
   const float alpha = scale, beta = 0.f;
   return hipblasLtMatmul(b->h, p->desc, &alpha, W, p->a, x, p->b, &beta, y, p->c, y, p->c, &p->algo, ws, p->ws,

@@ -421,4 +421,35 @@ hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// SwiGLU of a bfloat16 projection [M][2F] (u then v per row): a[M][F] =
+// (scale u) silu(scale v), 8 outputs per thread (16-byte loads and stores)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_swiglu_rows(const bf16* __restrict__ p, int F, float scale,
+                                                     bf16* __restrict__ a, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 outputs
+  if (i >= n8) return;
+  const int64_t e = i * 8, r = e / F, c = e % F;
+  const u32x4 u = *(const u32x4*)(p + r * 2 * F + c);
+  const u32x4 v = *(const u32x4*)(p + r * 2 * F + F + c);
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float u0 = bf_lo(u[k]) * scale, u1 = bf_hi(u[k]) * scale;
+    const float v0 = bf_lo(v[k]) * scale, v1 = bf_hi(v[k]) * scale;
+    o[k] = (uint32_t)from_f<bf16>(u0 * v0 / (1.f + expf(-v0))) |
+           ((uint32_t)from_f<bf16>(u1 * v1 / (1.f + expf(-v1))) << 16);
+  }
+  *(u32x4*)(a + e) = o;
+}
+
+hipError_t launch_swiglu_rows(const void* p, int M, int F, float scale, void* a, hipStream_t st) {
+  if (F % 8) return hipErrorInvalidValue;
+  const int64_t n8 = (int64_t)M * F / 8;
+  if (n8 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_rows, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, (const bf16*)p, F, scale,
+                     (bf16*)a, n8);
+  return hipGetLastError();
+}
+
 }  // namespace dory

@@ -152,6 +152,8 @@ struct AttnX {
   int hd; int nq;
 };
 hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st);
+// a[M][F] = (scale u) silu(scale v) from a bfloat16 projection [M][2F] (u | v per row); F % 8 == 0
+hipError_t launch_swiglu_rows(const void* p, int M, int F, float scale, void* a, hipStream_t st);
 // bfloat16 weights W [N][K = nq*hd], M <= 8 rows, y float32 [M][N] * scale
 hipError_t launch_linear_attn(const AttnX& ax, const void* W, float* y, int M, int N, int K, float scale,
                               hipStream_t st);
