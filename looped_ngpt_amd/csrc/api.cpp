@@ -610,6 +610,76 @@ dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, floa
   return DORY_OK;
 }
 
+// Attention of the backward through strided-batched GEMMs (bfloat16 models
+// with hipBLASLt): one batch entry per (sequence, kv head), its q heads'
+// queries stacked as G*n rows (head-major copies), so that dK and dV sum over
+// the group's heads inside the products. The scores are computed in full and
+// masked in the softmax rows.
+bool bw_attn_gemm(const Bw& b) { return b.c->plan.cfg.dtype == DORY_BF16 && b.c->blas != nullptr; }
+
+dory_status bw_rm(const Bw& b, bool tA, bool tB, int M, int N, int K, const void* A, int ta, int64_t lda, int64_t sA,
+                  const void* B, int tb, int64_t ldb, int64_t sB, void* C, int tc, int64_t ldc, int64_t sC, int batch,
+                  float alpha) {
+  dory_ctx* c = b.c;
+  if (!blaslt_rm(c->blas, tA, tB, M, N, K, A, ta, lda, sA, B, tb, ldb, sB, C, tc, ldc, sC, batch, alpha,
+                 c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
+    return set_err(c, DORY_E_HIP, "backward: hipBLASLt has no algorithm for an attention product");
+  return DORY_OK;
+}
+
+dory_status bw_attn_fwd_gemm(const Bw& b, bool full) {
+  dory_ctx* c = b.c;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const BwLayout& L = b.L;
+  const int n = b.n, hd = C.head_dim, nq = C.n_q_heads, nkv = C.n_kv_heads, G = nq / nkv;
+  const int R = G * n, batch = b.B * nkv;
+  hipStream_t st = c->st;
+  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.qn), (int64_t)nq * hd, 0, nq, hd, n, b.B, b.ws + L.Qh, st));
+  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.kn), (int64_t)nkv * hd, 0, nkv, hd, n, b.B, b.ws + L.Kh, st));
+  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.P1), P.qkvg_dim, P.q_dim + P.kv_dim, nkv, hd, n, b.B, b.ws + L.Vh,
+                                st));
+  // S = scale Q K^T
+  DORY_TRY(bw_rm(b, false, true, R, n, hd, b.ws + L.Qh, 1, hd, (int64_t)R * hd, b.ws + L.Kh, 1, hd, (int64_t)n * hd,
+                 b.ws + L.S, 0, n, (int64_t)R * n, batch, P.attn_scale));
+  HIP_TRY(c, launch_bw_softmax_rows(b.f<float>(L.S), (int64_t)batch * R, n, full ? 0 : C.window, b.ws + L.Pb, st));
+  // O = P V
+  DORY_TRY(bw_rm(b, false, false, R, hd, n, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Vh, 1, hd, (int64_t)n * hd,
+                 b.ws + L.Oh, 0, hd, (int64_t)R * hd, batch, 1.f));
+  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.Oh), nq, hd, n, b.B, b.f<float>(L.o), st));
+  return DORY_OK;
+}
+
+// given dO (float32 rows): dqn, dkn, dv (float32 rows)
+dory_status bw_attn_bwd_gemm(const Bw& b) {
+  dory_ctx* c = b.c;
+  const Plan& P = c->plan;
+  const dory_config& C = P.cfg;
+  const BwLayout& L = b.L;
+  const int n = b.n, hd = C.head_dim, nq = C.n_q_heads, nkv = C.n_kv_heads, G = nq / nkv;
+  const int R = G * n, batch = b.B * nkv;
+  hipStream_t st = c->st;
+  HIP_TRY(c, launch_bw_attn_D(b.f<float>(L.dO), b.f<float>(L.o), nq, hd, b.M, b.f<float>(L.D), st));
+  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.dO), (int64_t)nq * hd, 0, nq, hd, n, b.B, b.ws + L.dOh, st));
+  // dV = P^T dO (sums the group's heads)
+  DORY_TRY(bw_rm(b, true, false, n, hd, R, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.dOh, 1, hd, (int64_t)R * hd,
+                 b.ws + L.dVh, 0, hd, (int64_t)n * hd, batch, 1.f));
+  // dP = dO V^T (into the score buffer), then dS = P (dP - D) over P
+  DORY_TRY(bw_rm(b, false, true, R, n, hd, b.ws + L.dOh, 1, hd, (int64_t)R * hd, b.ws + L.Vh, 1, hd,
+                 (int64_t)n * hd, b.ws + L.S, 0, n, (int64_t)R * n, batch, 1.f));
+  HIP_TRY(c, launch_bw_dsoft_rows(b.f<float>(L.S), b.ws + L.Pb, b.f<float>(L.D), (int64_t)batch * R, n, G, nq, nkv,
+                                  st));
+  // dQ = scale dS K, dK = scale dS^T Q
+  DORY_TRY(bw_rm(b, false, false, R, hd, n, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Kh, 1, hd, (int64_t)n * hd,
+                 b.ws + L.dQh, 0, hd, (int64_t)R * hd, batch, P.attn_scale));
+  DORY_TRY(bw_rm(b, true, false, n, hd, R, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Qh, 1, hd, (int64_t)R * hd,
+                 b.ws + L.dKh, 0, hd, (int64_t)n * hd, batch, P.attn_scale));
+  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dQh), nq, hd, n, b.B, b.f<float>(L.dqn), st));
+  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dKh), nkv, hd, n, b.B, b.f<float>(L.dkn), st));
+  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dVh), nkv, hd, n, b.B, b.f<float>(L.dv), st));
+  return DORY_OK;
+}
+
 // forward of recurrent layer l on h_in -> h_out, keeping what its backward reads
 dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   dory_ctx* c = b.c;
@@ -624,9 +694,13 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   DORY_TRY(bw_gemm(c, b.ws + L.xb, d, c->qkvg[l], b.f<float>(L.P1), M, Q, d));
   HIP_TRY(c, launch_bw_rope_norm_fwd(b.f<float>(L.P1), Q, tab, b.n, C.n_q_heads, C.n_kv_heads, C.head_dim, M,
                                      b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.rq), b.f<float>(L.rk), st));
-  BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
-           C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
-  HIP_TRY(c, launch_bw_attn_fwd(a, M, b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst), st));
+  if (bw_attn_gemm(b)) {
+    DORY_TRY(bw_attn_fwd_gemm(b, full));
+  } else {
+    BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
+             C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
+    HIP_TRY(c, launch_bw_attn_fwd(a, M, b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst), st));
+  }
   HIP_TRY(c, launch_bw_gate_fwd(dt, b.f<float>(L.o), b.f<float>(L.P1), Q, qd + 2 * P.kv_dim, C.attn_gate,
                                 C.head_dim, qd, M, b.f<float>(L.oh), b.ws + L.ohb, b.f<float>(L.rc), st));
   DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd));
@@ -696,10 +770,14 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
                                 qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
                                 b.f<float>(L.dP1), st));
-  BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
-           C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
-  HIP_TRY(c, launch_bw_attn_bwd(a, M, b.f<float>(L.dO), b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst),
-                                b.f<float>(L.D), b.f<float>(L.dqn), b.f<float>(L.dkn), b.f<float>(L.dv), st));
+  if (bw_attn_gemm(b)) {
+    DORY_TRY(bw_attn_bwd_gemm(b));
+  } else {
+    BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
+             C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
+    HIP_TRY(c, launch_bw_attn_bwd(a, M, b.f<float>(L.dO), b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst),
+                                  b.f<float>(L.D), b.f<float>(L.dqn), b.f<float>(L.dkn), b.f<float>(L.dv), st));
+  }
   HIP_TRY(c, launch_bw_rope_norm_bwd(b.f<float>(L.dqn), b.f<float>(L.qn), b.f<float>(L.rq), b.f<float>(L.dkn),
                                      b.f<float>(L.kn), b.f<float>(L.rk), b.f<float>(L.dv), tab, b.n, C.n_q_heads,
                                      C.n_kv_heads, C.head_dim, M, b.f<float>(L.dP1), Q, st));

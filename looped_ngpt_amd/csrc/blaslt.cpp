@@ -11,9 +11,20 @@
 
 #include <map>
 #include <tuple>
+#include <utility>
 
 namespace dory {
 
+struct RmKey {
+  bool tA, tB;
+  int M, N, K, batch;
+  int64_t lda, ldb, ldc, sA, sB, sC;
+  int ta, tb, tc;
+  bool operator<(const RmKey& o) const {
+    return std::tie(tA, tB, M, N, K, batch, lda, ldb, ldc, sA, sB, sC, ta, tb, tc) <
+           std::tie(o.tA, o.tB, o.M, o.N, o.K, o.batch, o.lda, o.ldb, o.ldc, o.sA, o.sB, o.sC, o.ta, o.tb, o.tc);
+  }
+};
 struct BlasLt {
   hipblasLtHandle_t h = nullptr;
   struct Plan {
@@ -24,14 +35,16 @@ struct BlasLt {
     bool ok = false;
   };
   std::map<std::tuple<int, int, int, int64_t, int>, Plan> plans;
+  std::map<RmKey, Plan> rm_plans;
+  static void drop(Plan& p) {
+    if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
+    if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
+    if (p.c) hipblasLtMatrixLayoutDestroy(p.c);
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+  }
   ~BlasLt() {
-    for (auto& kv : plans) {
-      Plan& p = kv.second;
-      if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
-      if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
-      if (p.c) hipblasLtMatrixLayoutDestroy(p.c);
-      if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
-    }
+    for (auto& kv : plans) drop(kv.second);
+    for (auto& kv : rm_plans) drop(kv.second);
     if (h) hipblasLtDestroy(h);
   }
 };
@@ -84,6 +97,74 @@ static BlasLt::Plan* plan_for(BlasLt* b, int M, int N, int K, int64_t ldx, bool 
   }
   p.ok = ok;
   return ok ? &p : nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// general row-major strided-batched product (the backward's attention):
+// C[M][N] = alpha opA(A) opB(B), A stored [M][K] (or [K][M] when tA), B
+// stored [K][N] (or [N][K] when tB), row strides lda/ldb/ldc, batch strides
+// in elements. Column-major: C^T (N x M) = opB(B view) . opA(A view).
+// ---------------------------------------------------------------------------
+
+
+static hipDataType dtype_of(int t) { return t == 1 ? HIP_R_16BF : HIP_R_32F; }
+
+static bool layout(hipblasLtMatrixLayout_t* L, int t, uint64_t rows, uint64_t cols, int64_t ld, int batch,
+                   int64_t stride) {
+  if (hipblasLtMatrixLayoutCreate(L, dtype_of(t), rows, cols, ld) != HIPBLAS_STATUS_SUCCESS) return false;
+  if (batch > 1) {
+    const int32_t bc = batch;
+    const int64_t so = stride;
+    if (hipblasLtMatrixLayoutSetAttribute(*L, HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &bc, sizeof(bc)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutSetAttribute(*L, HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET, &so, sizeof(so)) !=
+            HIPBLAS_STATUS_SUCCESS)
+      return false;
+  }
+  return true;
+}
+
+bool blaslt_rm(BlasLt* b, bool tA, bool tB, int M, int N, int K, const void* A, int ta, int64_t lda, int64_t sA,
+               const void* B, int tb, int64_t ldb, int64_t sB, void* C, int tc, int64_t ldc, int64_t sC, int batch,
+               float alpha, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!b || M <= 0 || N <= 0 || K <= 0 || batch <= 0) return false;
+  const RmKey key{tA, tB, M, N, K, batch, lda, ldb, ldc, sA, sB, sC, ta, tb, tc};
+  auto it = b->rm_plans.find(key);
+  if (it == b->rm_plans.end()) {
+    BlasLt::Plan& p = b->rm_plans[key];
+    const hipblasOperation_t op1 = tB ? HIPBLAS_OP_T : HIPBLAS_OP_N, op2 = tA ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+    bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op1, sizeof(op1)) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op2, sizeof(op2)) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    // first operand: the column-major view of B; second: of A
+    ok = ok && (tB ? layout(&p.a, tb, K, N, ldb, batch, sB) : layout(&p.a, tb, N, K, ldb, batch, sB));
+    ok = ok && (tA ? layout(&p.b, ta, M, K, lda, batch, sA) : layout(&p.b, ta, K, M, lda, batch, sA));
+    ok = ok && layout(&p.c, tc, N, M, ldc, batch, sC);
+    hipblasLtMatmulPreference_t pref = nullptr;
+    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+    const uint64_t wsb = ws_bytes;
+    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
+                                                     sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int got = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(b->h, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &got) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    ok = ok && got >= 1 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= ws_bytes;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (ok) {
+      p.algo = res[0].algo;
+      p.ws = res[0].workspaceSize;
+    }
+    p.ok = ok;
+    it = b->rm_plans.find(key);
+  }
+  BlasLt::Plan* p = &it->second;
+  if (!p->ok) return false;
+  const float beta = 0.f;
+  return hipblasLtMatmul(b->h, p->desc, &alpha, B, p->a, A, p->b, &beta, C, p->c, C, p->c, &p->algo, ws, p->ws,
+                         st) == HIPBLAS_STATUS_SUCCESS;
 }
 
 bool blaslt_gemm(BlasLt* b, const void* x, int64_t ldx, const void* W, void* y, bool bf16_out, int M, int N, int K,

@@ -538,9 +538,127 @@ __global__ __launch_bounds__(256) void k_bw_rope_norm_bwd(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// attention through batched GEMMs (bfloat16 models): head-major layouts,
+// masked softmax rows and the softmax backward rows
+// ---------------------------------------------------------------------------
+// dst [B][H][n][hd] (model dtype) from src rows [B*n][ld] at column off + h*hd
+template <typename T>
+__global__ __launch_bounds__(256) void k_bw_to_heads(const float* __restrict__ src, int64_t ld, int off, int H,
+                                                     int hd, int n, int64_t total, T* __restrict__ dst) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int d = (int)(e % hd);
+  const int64_t r = e / hd;  // (b, h, t)
+  const int t = (int)(r % n);
+  const int64_t bh = r / n;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  dst[e] = from_f<T>(src[(b * n + t) * ld + off + (int64_t)h * hd + d]);
+}
+
+// dst rows [B*n][H*hd] from src [B][H][n][hd]
+__global__ __launch_bounds__(256) void k_bw_from_heads(const float* __restrict__ src, int H, int hd, int n,
+                                                       int64_t total, float* __restrict__ dst) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int d = (int)(e % hd);
+  const int64_t r = e / hd;
+  const int t = (int)(r % n);
+  const int64_t bh = r / n;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  dst[(b * n + t) * ((int64_t)H * hd) + (int64_t)h * hd + d] = src[e];
+}
+
+// row r of the scores (query position t = r % n): allowed keys lo..t;
+// P = softmax over them, 0 elsewhere (bfloat16)
+__global__ __launch_bounds__(256) void k_bw_softmax_rows(const float* __restrict__ S, int n, int window,
+                                                         bf16* __restrict__ P) {
+  __shared__ float sh[4];
+  const int64_t r = blockIdx.x;
+  const int t = (int)(r % n);
+  const int lo = window > 0 ? max(0, t - window + 1) : 0;
+  const float* row = S + r * n;
+  float m = -INFINITY;
+  for (int s = lo + threadIdx.x; s <= t; s += 256) m = fmaxf(m, row[s]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  float l = 0.f;
+  for (int s = lo + threadIdx.x; s <= t; s += 256) l += expf(row[s] - m);
+  const float il = 1.f / block_sum<256>(l, sh);
+  bf16* out = P + r * n;
+  for (int s = threadIdx.x; s < n; s += 256) out[s] = from_f<bf16>(s >= lo && s <= t ? expf(row[s] - m) * il : 0.f);
+}
+
+// softmax backward rows: dS = P (dP - D) in place over P; row r of batch
+// block (b, kv head g) is (q head g*G + i, position t)
+__global__ __launch_bounds__(256) void k_bw_dsoft_rows(const float* __restrict__ dP, bf16* __restrict__ P,
+                                                       const float* __restrict__ D, int n, int G, int nq, int nkv) {
+  const int64_t r = blockIdx.x;
+  const int64_t blk = r / ((int64_t)G * n);
+  const int within = (int)(r % ((int64_t)G * n));
+  const int i = within / n, t = within % n;
+  const int64_t b = blk / nkv;
+  const int g = (int)(blk % nkv);
+  const float Dv = D[(b * n + t) * nq + g * G + i];
+  const float* dp = dP + r * n;
+  bf16* p = P + r * n;
+  for (int s = threadIdx.x; s < n; s += 256) p[s] = from_f<bf16>(to_f(p[s]) * (dp[s] - Dv));
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
+
+hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int H, int hd, int n, int B, void* dst,
+                              hipStream_t st) {
+  const int64_t total = (int64_t)B * H * n * hd;
+  if (total <= 0) return hipSuccess;
+  if (dt == 1)
+    hipLaunchKernelGGL((k_bw_to_heads<bf16>), dim3(blocks_for(total)), dim3(256), 0, st, src, ld, off, H, hd, n,
+                       total, (bf16*)dst);
+  else
+    hipLaunchKernelGGL((k_bw_to_heads<float>), dim3(blocks_for(total)), dim3(256), 0, st, src, ld, off, H, hd, n,
+                       total, (float*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, float* dst, hipStream_t st) {
+  const int64_t total = (int64_t)B * H * n * hd;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_from_heads, dim3(blocks_for(total)), dim3(256), 0, st, src, H, hd, n, total, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bw_softmax_rows, dim3((unsigned)rows), dim3(256), 0, st, S, n, window, (bf16*)P);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int G, int nq, int nkv,
+                                hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bw_dsoft_rows, dim3((unsigned)rows), dim3(256), 0, st, dP, (bf16*)P, D, n, G, nq, nkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_attn_D(const float* dO, const float* o, int nq, int hd, int M, float* D, hipStream_t st) {
+  const dim3 g((nq + 3) / 4, M);
+  if (hd == 64)
+    hipLaunchKernelGGL((k_bw_attn_D<64>), g, dim3(256), 0, st, dO, o, nq, M, D);
+  else if (hd == 128)
+    hipLaunchKernelGGL((k_bw_attn_D<128>), g, dim3(256), 0, st, dO, o, nq, M, D);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // launchers

@@ -245,6 +245,14 @@ hipError_t launch_bw_gate_bwd(const float* doh, const float* oh, const float* rc
                               hipStream_t st);
 hipError_t launch_bw_attn_bwd(const BwAttn& a, int M, const float* dO, const float* o, const float* mst,
                               const float* lst, float* D, float* dqn, float* dkn, float* dv, hipStream_t st);
+// attention of the backward through batched GEMMs (bfloat16): layouts and rows
+hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int H, int hd, int n, int B, void* dst,
+                              hipStream_t st);
+hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, float* dst, hipStream_t st);
+hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st);
+hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int G, int nq, int nkv,
+                                hipStream_t st);
+hipError_t launch_bw_attn_D(const float* dO, const float* o, int nq, int hd, int M, float* D, hipStream_t st);
 hipError_t launch_bw_rope_norm_bwd(const float* dqn, const float* qn, const float* rq, const float* dkn,
                                    const float* kn, const float* rk, const float* dv, const float2* tab, int n, int nq,
                                    int nkv, int hd, int M, float* dP1, int ldp, hipStream_t st);

@@ -207,6 +207,20 @@ BwLayout make_bw_layout(const Plan& p, int B, int n) {
   w.TA = take(M * std::max(Q, std::max(2 * F, d)) * el);
   w.TB = take(M * std::max(d, std::max(F, qd)) * el);
   w.WT = take(std::max(std::max(Q * d, 2 * F * d), std::max(d * qd, d * F)) * el);
+  if (c.dtype == DORY_BF16) {
+    const size_t hq = (size_t)B * nq * n * c.head_dim, hk = (size_t)B * c.n_kv_heads * n * c.head_dim;
+    const size_t sq = (size_t)B * nq * n * n;
+    w.Qh = take(hq * el);
+    w.dOh = take(hq * el);
+    w.Kh = take(hk * el);
+    w.Vh = take(hk * el);
+    w.Oh = take(hq * 4);
+    w.dQh = take(hq * 4);
+    w.dKh = take(hk * 4);
+    w.dVh = take(hk * 4);
+    w.S = take(sq * 4);
+    w.Pb = take(sq * el);
+  }
   w.total = at;
   return w;
 }

@@ -90,6 +90,10 @@ struct BwLayout {
   size_t dO = 0, D = 0, dqn = 0, dkn = 0, dv = 0, dP1 = 0;
   size_t xb = 0, ohb = 0, h1b = 0, ab = 0, dyb = 0, dP2b = 0, dP1b = 0;  // T
   size_t TA = 0, TB = 0, WT = 0;                    // T: transposed operands of the gradient GEMMs
+  // attention through batched GEMMs (bfloat16 models): head-major copies
+  // [B][heads][n][hd] (T: Qh, Kh, Vh, dOh; float32: Oh, dQh, dKh, dVh), the
+  // scores / dP [B][n_q][n][n] (float32) and P / dS [B][n_q][n][n] (T)
+  size_t Qh = 0, Kh = 0, Vh = 0, dOh = 0, Oh = 0, dQh = 0, dKh = 0, dVh = 0, S = 0, Pb = 0;
   size_t total = 0;
 };
 
