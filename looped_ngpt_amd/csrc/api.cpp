@@ -651,7 +651,7 @@ dory_status bw_attn_fwd_gemm(const Bw& b, bool full) {
 }
 
 // given dO (float32 rows): dqn, dkn, dv (float32 rows)
-dory_status bw_attn_bwd_gemm(const Bw& b) {
+dory_status bw_attn_bwd_gemm(const Bw& b, bool full) {
   dory_ctx* c = b.c;
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
@@ -667,8 +667,8 @@ dory_status bw_attn_bwd_gemm(const Bw& b) {
   // dP = dO V^T (into the score buffer), then dS = P (dP - D) over P
   DORY_TRY(bw_rm(b, false, true, R, n, hd, b.ws + L.dOh, 1, hd, (int64_t)R * hd, b.ws + L.Vh, 1, hd,
                  (int64_t)n * hd, b.ws + L.S, 0, n, (int64_t)R * n, batch, 1.f));
-  HIP_TRY(c, launch_bw_dsoft_rows(b.f<float>(L.S), b.ws + L.Pb, b.f<float>(L.D), (int64_t)batch * R, n, G, nq, nkv,
-                                  st));
+  HIP_TRY(c, launch_bw_dsoft_rows(b.f<float>(L.S), b.ws + L.Pb, b.f<float>(L.D), (int64_t)batch * R, n,
+                                  full ? 0 : C.window, G, nq, nkv, st));
   // dQ = scale dS K, dK = scale dS^T Q
   DORY_TRY(bw_rm(b, false, false, R, hd, n, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Kh, 1, hd, (int64_t)n * hd,
                  b.ws + L.dQh, 0, hd, (int64_t)R * hd, batch, P.attn_scale));
@@ -715,19 +715,29 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   return DORY_OK;
 }
 
-// dW [N][K] = dY^T X from dY [M][N] and X [M][K] (model dtype): both
-// transposed into TA / TB, then one GEMM over the M rows
+// dW [N][K] = dY^T X from dY [M][N] and X [M][K] (model dtype). hipBLASLt
+// reads dY transposed in place; otherwise both are transposed into TA / TB,
+// then one GEMM over the M rows
 dory_status bw_wgrad(const Bw& b, const void* dY, int N, const void* X, int K, float* dW) {
   dory_ctx* c = b.c;
   const int dt = c->plan.cfg.dtype;
+  if (dt == DORY_BF16 && c->blas && b.M >= kBlasMinRows &&
+      blaslt_rm(c->blas, true, false, N, K, b.M, dY, 1, N, 0, X, 1, K, 0, dW, 0, K, 0, 1, 1.f,
+                c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
+    return DORY_OK;
   HIP_TRY(c, launch_bw_transpose(dt, dY, N, b.ws + b.L.TA, b.M, N, c->st));
   HIP_TRY(c, launch_bw_transpose(dt, X, K, b.ws + b.L.TB, b.M, K, c->st));
   return bw_gemm(c, b.ws + b.L.TA, b.M, b.ws + b.L.TB, dW, N, K, b.M);
 }
 
-// dX [M][K] = dY [M][N] . W [N][K]: W transposed into WT, then one GEMM
+// dX [M][K] = dY [M][N] . W [N][K]: hipBLASLt reads W as stored; otherwise
+// W is transposed into WT, then one GEMM
 dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX) {
   dory_ctx* c = b.c;
+  if (c->plan.cfg.dtype == DORY_BF16 && c->blas && b.M >= kBlasMinRows &&
+      blaslt_rm(c->blas, false, false, b.M, K, N, dY, 1, N, 0, W, 1, K, 0, dX, 0, K, 0, 1, 1.f,
+                c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
+    return DORY_OK;
   HIP_TRY(c, launch_bw_transpose(c->plan.cfg.dtype, W, K, b.ws + b.L.WT, N, K, c->st));
   return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N);
 }
@@ -750,7 +760,7 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_update_bwd(dt, dho, h_out, b.f<float>(L.rz2), b.f<float>(L.y2h), b.f<float>(L.ry2),
                                   b.f<float>(L.h1), c->alpha_mlp[l], M, d, b.f<float>(L.dres), b.ws + L.dyb,
                                   b.f<float>(L.contrib), st));
-  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_mlp[i], st));
+  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_mlp[i], tmp, st));
   DORY_TRY(bw_wgrad(b, b.ws + L.dyb, d, b.ws + L.ab, F, g->down[i]));
   DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->down[l], d, F, tmp));                     // da [M][F]
   HIP_TRY(c, launch_bw_swiglu_bwd(dt, tmp, b.f<float>(L.a32), b.f<float>(L.rs), b.f<float>(L.P2), F, M,
@@ -764,14 +774,14 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_update_bwd(dt, dh1, b.f<float>(L.h1), b.f<float>(L.rz), b.f<float>(L.yh), b.f<float>(L.ry),
                                   h_in, c->alpha_attn[l], M, d, b.f<float>(L.dres), b.ws + L.dyb,
                                   b.f<float>(L.contrib), st));
-  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_attn[i], st));
+  HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_attn[i], tmp, st));
   DORY_TRY(bw_wgrad(b, b.ws + L.dyb, d, b.ws + L.ohb, qd, g->o[i]));
   DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->o[l], d, qd, tmp));                       // doh [M][qd]
   HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
                                 qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
                                 b.f<float>(L.dP1), st));
   if (bw_attn_gemm(b)) {
-    DORY_TRY(bw_attn_bwd_gemm(b));
+    DORY_TRY(bw_attn_bwd_gemm(b, full));
   } else {
     BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
              C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};

@@ -311,6 +311,20 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
     x2[it] = src[ln + half];
   }
   const float2 cs = a.tab[(size_t)t * half + ln];
+  // gate values of this thread's entries of the sums, fetched with the setup
+  // values rather than at the end of the kernel; always in bounds (without a
+  // gate the unused index points into q)
+  constexpr int NE = (G * (HD + 1) + 255) / 256;
+  float gx[NE];
+  {
+    const float* gp = a.gate ? row + a.gate_off : row;
+#pragma unroll
+    for (int it = 0; it < NE; ++it) {
+      const int e = min(tid + 256 * it, G * (HD + 1) - 1);
+      const int hq = kvh * G + e / (HD + 1), d = min(e % (HD + 1), HD - 1);
+      gx[it] = gp[a.gate == 2 ? hq : hq * HD + d];
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
 
   // (2) cache rows of the first U steps (HBM); out-of-range keys and the new
@@ -561,6 +575,20 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     x2[it] = src[ln + half];
   }
   const float2 cs = a.tab[(size_t)t * half + ln];
+  // gate values of this thread's entries of the sums, fetched with the setup
+  // values rather than at the end of the kernel; always in bounds (without a
+  // gate the unused index points into q)
+  constexpr int NE = (G * (HD + 1) + 255) / 256;
+  float gx[NE];
+  {
+    const float* gp = a.gate ? row + a.gate_off : row;
+#pragma unroll
+    for (int it = 0; it < NE; ++it) {
+      const int e = min(tid + 256 * it, G * (HD + 1) - 1);
+      const int hq = kvh * G + e / (HD + 1), d = min(e % (HD + 1), HD - 1);
+      gx[it] = gp[a.gate == 2 ? hq : hq * HD + d];
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
 
   // (2) cache operands of the wave's first tile (HBM)
@@ -587,10 +615,13 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       for (int dd = 0; dd < NDD; ++dd) va[dd][h2] = *(const u32x2_t*)(vt + vt_off(s0, 16 * dd + c16, HD));
     }
   };
+  // issued unconditionally (a tile past te is clamped in bounds and never
+  // processed): loads under a branch make the compiler wait for all of them
+  // where the paths join, before the setup arithmetic below
   const int first = tb + wave;
   u32x4 ka0[2][NKK];
   u32x2_t va0[NDD][2];
-  if (first < te) load(first, ka0, va0);
+  load(first, ka0, va0);
 
   // (3) RoPE at t, unit norm, bfloat16 storage of q and of the new key/value
 #pragma unroll
@@ -726,8 +757,10 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     // sums referenced to the largest possible score sl2 (unit q and k), the
     // value sums gated (linear in the sums), then 2^36 fixed point; integer
     // adds are order-independent
-    const float* grow = a.qkvg + (size_t)b * a.ld + a.gate_off;
-    for (int e = tid; e < G * (HD + 1); e += 256) {
+#pragma unroll
+    for (int it = 0; it < NE; ++it) {
+      const int e = tid + 256 * it;
+      if (e >= G * (HD + 1)) break;
       const int g = e / (HD + 1), d = e % (HD + 1);
       const int hq = kvh * G + g;
       float S = 0.f;
@@ -737,7 +770,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
         const float f = exp2f(wm[w][g] - sl2);
         S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], f, S);
       }
-      if (d < HD && a.gate) S *= sigmoidf_(a.gate == 1 ? grow[hq * HD + d] : grow[hq]);
+      if (d < HD && a.gate) S *= sigmoidf_(gx[it]);
       if (S != 0.f)
         atomicAdd(a.acc + ((size_t)b * a.nq + hq) * (HD + kAttnAccPad) + d,
                   (unsigned long long)llrint((double)S * 68719476736.0));

@@ -53,13 +53,17 @@ __global__ __launch_bounds__(256) void k_bw_add(const float* __restrict__ a, con
   if (i < n) out[i] = a[i] + b[i];
 }
 
-// out[j] = sum over rows of in[r][j] (rows in order: deterministic)
-__global__ __launch_bounds__(256) void k_bw_colsum(const float* __restrict__ in, int M, int d, float* __restrict__ out) {
+// out[c][j] = sum of in[r][j] over the rows r of chunk c (blockIdx.y, rc rows
+// each), in row order: a fixed summation order, so deterministic
+constexpr int kColRows = 64;
+__global__ __launch_bounds__(256) void k_bw_colsum(const float* __restrict__ in, int M, int d, int rc,
+                                                   float* __restrict__ out) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= d) return;
+  const int r0 = blockIdx.y * rc, r1 = min(M, r0 + rc);
   float s = 0.f;
-  for (int r = 0; r < M; ++r) s += in[(size_t)r * d + j];
-  out[j] = s;
+  for (int r = r0; r < r1; ++r) s += in[(size_t)r * d + j];
+  out[(size_t)blockIdx.y * d + j] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -610,7 +614,94 @@ __global__ __launch_bounds__(256) void k_bw_dsoft_rows(const float* __restrict__
   for (int s = threadIdx.x; s < n; s += 256) p[s] = from_f<bf16>(to_f(p[s]) * (dp[s] - Dv));
 }
 
+// The same two row operations with one wave per row (4 rows per workgroup)
+// for n a multiple of 4 up to 256 J: lane l holds the float4 groups l + 64 j
+// of its row in registers, so the scores are read once; groups wholly outside
+// the allowed keys lo..t are neither read nor (for dS, whose P is already 0
+// there) written.
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)from_f<bf16>(a) | ((uint32_t)from_f<bf16>(b) << 16),
+                    (uint32_t)from_f<bf16>(c) | ((uint32_t)from_f<bf16>(d) << 16));
+}
+
+template <int J>
+__global__ __launch_bounds__(256) void k_bw_softmax_rows_v(const float* __restrict__ S, int64_t rows, int n,
+                                                           int window, bf16* __restrict__ P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int t = (int)(r % n);
+  const int lo = window > 0 ? max(0, t - window + 1) : 0;
+  const float4* row = reinterpret_cast<const float4*>(S + r * n);
+  float v[J][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 4 * (lane + 64 * j);
+    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (e < n && e + 3 >= lo && e <= t) x = row[e >> 2];
+    v[j][0] = (e >= lo && e <= t) ? x.x : -INFINITY;
+    v[j][1] = (e + 1 >= lo && e + 1 <= t) ? x.y : -INFINITY;
+    v[j][2] = (e + 2 >= lo && e + 2 <= t) ? x.z : -INFINITY;
+    v[j][3] = (e + 3 >= lo && e + 3 <= t) ? x.w : -INFINITY;
+    m = fmaxf(m, fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
+  }
+  m = wave_max(m);  // finite: key t is always allowed
+  float l = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[j][c] = expf(v[j][c] - m);
+      l += v[j][c];
+    }
+  const float il = 1.f / wave_sum(l);
+  uint2* out = reinterpret_cast<uint2*>(P + r * n);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 4 * (lane + 64 * j);
+    if (e < n) out[e >> 2] = pack4_bf16(v[j][0] * il, v[j][1] * il, v[j][2] * il, v[j][3] * il);
+  }
+}
+
+// dS = P (dP - D) over the allowed keys of each row
+template <int J>
+__global__ __launch_bounds__(256) void k_bw_dsoft_rows_v(const float* __restrict__ dP, bf16* __restrict__ P,
+                                                         const float* __restrict__ D, int64_t rows, int n, int window,
+                                                         int G, int nq, int nkv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int64_t blk = r / ((int64_t)G * n);
+  const int within = (int)(r % ((int64_t)G * n));
+  const int i = within / n, t = within % n;
+  const int lo = window > 0 ? max(0, t - window + 1) : 0;
+  const int64_t b = blk / nkv;
+  const int g = (int)(blk % nkv);
+  const float Dv = D[(b * n + t) * nq + g * G + i];
+  const float4* dp = reinterpret_cast<const float4*>(dP + r * n);
+  uint2* p = reinterpret_cast<uint2*>(P + r * n);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 4 * (lane + 64 * j);
+    if (e < n && e + 3 >= lo && e <= t) {
+      const float4 x = dp[e >> 2];
+      const uint2 pv = p[e >> 2];
+      p[e >> 2] = pack4_bf16(to_f((bf16)(pv.x & 0xffffu)) * (x.x - Dv), to_f((bf16)(pv.x >> 16)) * (x.y - Dv),
+                             to_f((bf16)(pv.y & 0xffffu)) * (x.z - Dv), to_f((bf16)(pv.y >> 16)) * (x.w - Dv));
+    }
+  }
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+// groups of 4 per lane: J = ceil(n / 256) rounded up to a power of two, at most 16
+inline int rows_v_groups(int n) {
+  if (n % 4 != 0) return 0;
+  for (int J = 1; J <= 16; J *= 2)
+    if (n <= 256 * J) return J;
+  return 0;
+}
 
 }  // namespace
 
@@ -637,14 +728,34 @@ hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, f
 hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 gv((unsigned)((rows + 3) / 4));
+  switch (rows_v_groups(n)) {
+#define SOFT_V(J)                                                                                           \
+  case J:                                                                                                   \
+    hipLaunchKernelGGL((k_bw_softmax_rows_v<J>), gv, dim3(256), 0, st, S, rows, n, window, (bf16*)P);      \
+    return hipGetLastError();
+    SOFT_V(1) SOFT_V(2) SOFT_V(4) SOFT_V(8) SOFT_V(16)
+#undef SOFT_V
+    default: break;
+  }
   hipLaunchKernelGGL(k_bw_softmax_rows, dim3((unsigned)rows), dim3(256), 0, st, S, n, window, (bf16*)P);
   return hipGetLastError();
 }
 
-hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int G, int nq, int nkv,
-                                hipStream_t st) {
+hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int window, int G,
+                                int nq, int nkv, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 gv((unsigned)((rows + 3) / 4));
+  switch (rows_v_groups(n)) {
+#define DSOFT_V(J)                                                                                               \
+  case J:                                                                                                        \
+    hipLaunchKernelGGL((k_bw_dsoft_rows_v<J>), gv, dim3(256), 0, st, dP, (bf16*)P, D, rows, n, window, G, nq, nkv); \
+    return hipGetLastError();
+    DSOFT_V(1) DSOFT_V(2) DSOFT_V(4) DSOFT_V(8) DSOFT_V(16)
+#undef DSOFT_V
+    default: break;
+  }
   hipLaunchKernelGGL(k_bw_dsoft_rows, dim3((unsigned)rows), dim3(256), 0, st, dP, (bf16*)P, D, n, G, nq, nkv);
   return hipGetLastError();
 }
@@ -690,8 +801,17 @@ hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, 
   return hipGetLastError();
 }
 
-hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_bw_colsum, dim3(blocks_for(d)), dim3(256), 0, st, in, M, d, out);
+hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, float* part, hipStream_t st) {
+  if (M <= 0 || d <= 0) return hipSuccess;
+  const int chunks = (M + kColRows - 1) / kColRows;
+  if (chunks == 1) {
+    hipLaunchKernelGGL(k_bw_colsum, dim3(blocks_for(d), 1), dim3(256), 0, st, in, M, d, M, out);
+    return hipGetLastError();
+  }
+  // chunk sums into part [chunks][d], then the sum of the chunks in order
+  hipLaunchKernelGGL(k_bw_colsum, dim3(blocks_for(d), chunks), dim3(256), 0, st, in, M, d, kColRows, part);
+  hipLaunchKernelGGL(k_bw_colsum, dim3(blocks_for(d), 1), dim3(256), 0, st, (const float*)part, chunks, d, chunks,
+                     out);
   return hipGetLastError();
 }
 

@@ -224,7 +224,8 @@ struct BwAttn {
 hipError_t launch_bw_cast(int dt_out, const float* in, void* out, int64_t n, hipStream_t st);
 hipError_t launch_bw_transpose(int dt, const void* in, int64_t ld, void* out, int R, int C, hipStream_t st);
 hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
-hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, hipStream_t st);
+// out[j] = sum over the M rows of in[r][j]; part: scratch of ceil(M/64) * d floats
+hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, float* part, hipStream_t st);
 hipError_t launch_bw_update_fwd(int dt, const float* h, const float* y, const float* alpha, int M, int d, float* yh,
                                 float* ry, float* rz, float* hout, void* hout_t, hipStream_t st);
 hipError_t launch_bw_rope_norm_fwd(const float* P1, int ldp, const float2* tab, int n, int nq, int nkv, int hd, int M,
@@ -250,8 +251,9 @@ hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int
                               hipStream_t st);
 hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, float* dst, hipStream_t st);
 hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st);
-hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int G, int nq, int nkv,
-                                hipStream_t st);
+// dS = P (dP - D) over P; window 0: causal only (P is 0 outside the allowed keys)
+hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int window, int G,
+                                int nq, int nkv, hipStream_t st);
 hipError_t launch_bw_attn_D(const float* dO, const float* o, int nq, int hd, int M, float* D, hipStream_t st);
 hipError_t launch_bw_rope_norm_bwd(const float* dqn, const float* qn, const float* rq, const float* dkn,
                                    const float* kn, const float* rk, const float* dv, const float2* tab, int n, int nq,

@@ -83,21 +83,25 @@ def test_backward_f32_small(gate):
     _compare(cfg, got, ref, x.shape, 2e-4, normwise=False)
 
 
-def test_backward_bf16_small():
+@pytest.mark.parametrize("n", [40, 23])
+def test_backward_bf16_small(n):
+    """n 40: the one-wave-per-row softmax kernels; 23 (not a multiple of 4): the per-row-workgroup ones."""
     cfg = _small(1, "bf16")
     w = _alphas(cfg, make_weights(cfg), 90)
-    x, G = _inputs(cfg, 2, 40, 91)
+    x, G = _inputs(cfg, 2, n, 91)
     ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
     got = _run(cfg, w, x, G)
     _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
 
 
 def test_backward_bf16_36layer_widths():
-    """d 3072, 24 / 8 heads of 128, d_ff 8192: 1 input, 2 recurrent (one full), 1 output layer; 160 positions."""
+    """d 3072, 24 / 8 heads of 128, d_ff 8192: 1 input, 2 recurrent (one sliding with a 100-key window, one
+    full), 1 output layer; 300 positions: 300 rows take the library GEMMs for the projections and their
+    gradients, and the softmax rows hold two float4 groups per lane."""
     cfg = scaled_config(get_config("c36"), n_in=1, n_rec=2, n_out=1).replace(vocab=512, name="c36w_bw")
-    cfg = cfg.replace(layer_is_full=(False, False, True, False))
+    cfg = cfg.replace(layer_is_full=(False, False, True, False), window=100)
     w = _alphas(cfg, make_weights(cfg), 92)
-    x, G = _inputs(cfg, 1, 160, 93)
+    x, G = _inputs(cfg, 1, 300, 93)
     ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
     got = _run(cfg, w, x, G)
     _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
