@@ -311,20 +311,6 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
     x2[it] = src[ln + half];
   }
   const float2 cs = a.tab[(size_t)t * half + ln];
-  // gate values of this thread's entries of the sums, fetched with the setup
-  // values rather than at the end of the kernel; always in bounds (without a
-  // gate the unused index points into q)
-  constexpr int NE = (G * (HD + 1) + 255) / 256;
-  float gx[NE];
-  {
-    const float* gp = a.gate ? row + a.gate_off : row;
-#pragma unroll
-    for (int it = 0; it < NE; ++it) {
-      const int e = min(tid + 256 * it, G * (HD + 1) - 1);
-      const int hq = kvh * G + e / (HD + 1), d = min(e % (HD + 1), HD - 1);
-      gx[it] = gp[a.gate == 2 ? hq : hq * HD + d];
-    }
-  }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
 
   // (2) cache rows of the first U steps (HBM); out-of-range keys and the new

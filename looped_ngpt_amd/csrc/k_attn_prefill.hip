@@ -30,6 +30,7 @@ namespace dory {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
   };
 
   const float sl2 = a.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;
+  float m = -1e30f, l = 0.f;
   f32x16_t acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
@@ -188,39 +189,52 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(kr0 + 16 * ks), qf[ks], sc[kt], 0, 0,
                                                          0);
     }
-    // register r of half tile kt holds key s0 + 32 kt + 8 (r / 4) + 4 g + r % 4
+    // register r of half tile kt holds key s0 + 32 kt + 8 (r / 4) + 4 g + r % 4.
+    // Masks only on edge tiles (a wave-uniform branch), as selects; the max
+    // is taken on the raw scores (sl2 > 0) and the running max m stays finite
+    // (starts at -1e30), so a masked score (-inf) gives p = 2^-inf = 0.
     float tmax = -INFINITY;
+    if (edge) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sc[kt][r] * sl2;
-        if (edge) {
+        for (int r = 0; r < 16; ++r) {
           const int key = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key <= t && (full || key > t - W);
-          v = ok ? v : -INFINITY;
+          const bool ok = (key <= t) & (full | (key > t - W));
+          sc[kt][r] = ok ? sc[kt][r] : -INFINITY;
+          tmax = fmaxf(tmax, sc[kt][r]);
         }
-        sc[kt][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[kt][r]);
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float mn = fmaxf(m, tmax * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
+    // p = 2^(s sl2 - m) in bfloat16 (the P.V operand); the row sum adds the
+    // rounded values two at a time
     float ps = 0.f;
     bf16x8_t pb[2][2];
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = sc[kt][r] == -INFINITY ? 0.f : exp2f(sc[kt][r] - mn);
-        const bf16 bits = from_f<bf16>(p);
-        ps += to_f(bits);
-        pb[kt][r >> 3][r & 7] = *(const __bf16*)&bits;
+      for (int r = 0; r < 16; r += 2) {
+        bf16x2_t pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kt][r], sl2, -mn));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kt][r + 1], sl2, -mn));
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
+        pb[kt][r >> 3][r & 7] = pr[0];
+        pb[kt][r >> 3][(r & 7) + 1] = pr[1];
       }
     l = l * alpha + ps;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the max moved for some query of the wave
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
