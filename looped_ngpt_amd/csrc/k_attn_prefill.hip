@@ -122,28 +122,63 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
     return s >= p0 ? vw[vhead_w + (size_t)d * a.vld + (s - p0)] : vc[vhead_c + vt_off(slot_of(s), d, HD)];
   };
 
+  // A plain tile (every key inside the block's range, and all from the cache
+  // without a ring wrap, or all from this call with 8-aligned value runs)
+  // has every address as a wave-uniform base plus a per-thread constant.
+  // fetch always issues those loads (clamped in bounds, no branch around
+  // them, so the waits stay exact); stage writes them to LDS for a plain
+  // tile and otherwise re-reads the tile through the per-key path above
+  // (edge tiles only: the block's first and last, the one holding p0).
+  const int slots = a.slots, vslots = vslots_of(a.slots);
+  const bool cache_plain = vec_cache && (full || W % kKT == 0);
+  auto plain = [&](int s0) {
+    if (s0 < lo_blk || s0 + kKT - 1 > hi_blk) return false;
+    if (s0 >= p0) return vec_chunk;
+    return s0 + kKT - 1 < p0 && cache_plain;
+  };
   u32x4 kr[NL], vr[NL];
   auto fetch = [&](int s0) {
+    const bool chunk = s0 >= p0;
+    const int r0 = s0 - p0;
+    const int slot0 = slot_of(s0);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int e = tid + 256 * i;
-      kr[i] = *(const u32x4*)(key_src(s0 + e / CPK) + 8 * (e % CPK));
-      vr[i] = *(const u32x4*)v_src(e >> 3, s0 + 8 * (e & 7));
+      const int kk = e / CPK, c = e % CPK, d = e >> 3, run = e & 7;
+      const bf16* kp = chunk ? kw + ((size_t)(b * n + min(r0 + kk, n - 1)) * a.nkv + kvh) * HD + 8 * c
+                             : kc + (khead + min(slot0 + kk, slots - 1)) * HD + 8 * c;
+      // value runs rounded down to 8 positions: 16-byte aligned (they are
+      // used as loaded only when already aligned, i.e. in a plain tile)
+      const bf16* vp = chunk ? vw + vhead_w + (size_t)d * a.vld + (min(r0 + 8 * run, a.vld - 8) & ~7)
+                             : vc + vhead_c + vt_off(min(slot0 + 8 * run, vslots - 8) & ~7, d, HD);
+      kr[i] = *(const u32x4*)kp;
+      vr[i] = *(const u32x4*)vp;
     }
   };
   auto stage = [&](int s0) {
+    if (plain(s0)) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int e = tid + 256 * i;
+        *(u32x4*)(Ks + (e / CPK) * KLD + 8 * (e % CPK)) = kr[i];
+        u32x2_t* dst = (u32x2_t*)(Vt + (e >> 3) * VLD + 8 * (e & 7));
+        dst[0] = u32x2_t{vr[i][0], vr[i][1]};
+        dst[1] = u32x2_t{vr[i][2], vr[i][3]};
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int e = tid + 256 * i;
       const int kk = e / CPK, c = e % CPK;
       const int s = s0 + kk;
-      u32x4 kv = kr[i];
+      u32x4 kv = *(const u32x4*)(key_src(s) + 8 * c);
       if (s < lo_blk || s > hi_blk) kv = u32x4{0u, 0u, 0u, 0u};
       *(u32x4*)(Ks + kk * KLD + 8 * c) = kv;
       const int d = e >> 3, run = e & 7;
       const int sv = s0 + 8 * run;
       const int mode = run_mode(sv);
-      u32x4 vv = vr[i];
+      u32x4 vv = *(const u32x4*)v_src(d, sv);
       if (mode == 1) {
         vv = u32x4{0u, 0u, 0u, 0u};
       } else if (mode == 2) {
