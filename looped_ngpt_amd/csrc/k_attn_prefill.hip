@@ -192,8 +192,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
     }
   };
 
+  // q and k are unit vectors, so no score exceeds the scale: with sl2 at most
+  // 40 the exponents are referenced to that bound (softmax is unchanged by
+  // the shift, and 2^(-2 sl2) is still a normal bfloat16), which needs no
+  // running max and no rescaling; above it, the usual online max.
   const float sl2 = a.scale * kLog2e;
-  float m = -1e30f, l = 0.f;
+  const bool fixed_ref = sl2 <= 40.f;
+  float m = fixed_ref ? sl2 : -1e30f, l = 0.f;
   f32x16_t acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
@@ -225,9 +230,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
                                                          0);
     }
     // register r of half tile kt holds key s0 + 32 kt + 8 (r / 4) + 4 g + r % 4.
-    // Masks only on edge tiles (a wave-uniform branch), as selects; the max
-    // is taken on the raw scores (sl2 > 0) and the running max m stays finite
-    // (starts at -1e30), so a masked score (-inf) gives p = 2^-inf = 0.
+    // Masks only on edge tiles (a wave-uniform branch), as selects; a masked
+    // score (-inf) gives p = 2^-inf = 0 since the reference m is finite (the
+    // bound sl2, or a running max that starts at -1e30 and is taken on the
+    // raw scores, sl2 > 0).
     float tmax = -INFINITY;
     if (edge) {
 #pragma unroll
@@ -239,14 +245,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(AttnArgs a, const float
           sc[kt][r] = ok ? sc[kt][r] : -INFINITY;
           tmax = fmaxf(tmax, sc[kt][r]);
         }
-    } else {
+    } else if (!fixed_ref) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[kt][r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax * sl2);
+    float mn = m;
+    if (!fixed_ref) {
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      mn = fmaxf(m, tmax * sl2);
+    }
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     // p = 2^(s sl2 - m) in bfloat16 (the P.V operand); the row sum adds the
