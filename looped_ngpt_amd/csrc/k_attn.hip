@@ -537,7 +537,9 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   const int c16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x;
   const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
-  const int t = *a.t_dev;  // position of the new key (device counter: graph-replayable)
+  // position of the new key (device counter: graph-replayable), read through
+  // the scalar cache (it is not written by this kernel)
+  const int t = *(const __attribute__((address_space(4))) int*)a.t_dev;
   const int lo = a.is_full ? 0 : max(0, t - a.window + 1);
   const int T_lo = lo >> 5, T_hi = t >> 5;
   const int ntiles = T_hi - T_lo + 1;
@@ -582,31 +584,33 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);  // 32-position blocks
   const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
   auto slot_of = [&](int pos) { return a.is_full ? pos : pos % a.window; };
-  auto load = [&](int T, u32x4 (&ka)[2][NKK], u32x2_t (&va)[NDD][2]) {
+  // Key order inside a 32-position tile: A row r of 16-key half kb holds key
+  // 8 (r / 4) + 4 kb + r % 4, so the score lane (head, g4) ends up with keys
+  // 8 g4 .. 8 g4 + 7 (half 0: +0..3, half 1: +4..7) — the k order of the P.V
+  // product, whose V^T operand is then one 16-byte run of 8 positions.
+  auto load = [&](int T, u32x4 (&ka)[2][NKK], u32x4 (&va)[NDD]) {
     const int p0 = T << 5;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(p0 + 16 * kb + c16, t);  // beyond t: any written slot, masked later
+      const int key = min(p0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), t);  // beyond t: any written slot, masked later
       const bf16* kr = kc + (khead + slot_of(key)) * HD + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)(kr + kk * 32);
     }
+    // 8 consecutive positions, 8-aligned (slot and window counts are multiples
+    // of 8); runs past the last slot hold only positions > t (masked) and are
+    // clamped in bounds
+    const int g0 = p0 + 8 * g4;
+    const int s0 = min(a.is_full ? g0 : g0 % a.window, a.slots - 8);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      // 4 consecutive positions, 4-aligned; runs past the last slot hold only
-      // positions > t (masked) and are clamped in bounds
-      const int g0 = p0 + 16 * h2 + 4 * g4;
-      const int s0 = min(a.is_full ? g0 : g0 % a.window, a.slots - 4);
-#pragma unroll
-      for (int dd = 0; dd < NDD; ++dd) va[dd][h2] = *(const u32x2_t*)(vt + vt_off(s0, 16 * dd + c16, HD));
-    }
+    for (int dd = 0; dd < NDD; ++dd) va[dd] = *(const u32x4*)(vt + vt_off(s0, 16 * dd + c16, HD));
   };
   // issued unconditionally (a tile past te is clamped in bounds and never
   // processed): loads under a branch make the compiler wait for all of them
   // where the paths join, before the setup arithmetic below
   const int first = tb + wave;
   u32x4 ka0[2][NKK];
-  u32x2_t va0[NDD][2];
+  u32x4 va0[NDD];
   load(first, ka0, va0);
 
   // (3) RoPE at t, unit norm, bfloat16 storage of q and of the new key/value
@@ -643,38 +647,41 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qb[kk] = *(const bf16x8_t*)&qs[c16][kk * 32 + 8 * g4];
 
+  // q and k are unit vectors, so no score exceeds the scale: while
+  // sl2 = scale log2(e) is at most 40 the exponents are referenced to that
+  // bound (no running max or rescale; 2^(-2 sl2) is still a normal float),
+  // above it to a running max.
   const float sl2 = a.scale * LOG2E;
-  float m = -INFINITY, l = 0.f;
+  const bool fixed_ref = sl2 <= 40.f;
+  float m = fixed_ref ? sl2 : -INFINITY, l = 0.f;
   f32x4_t acc[NDD];
 #pragma unroll
   for (int dd = 0; dd < NDD; ++dd) acc[dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](int T, u32x4 (&ka)[2][NKK], u32x2_t (&va)[NDD][2]) {
+  auto process = [&](int T, u32x4 (&ka)[2][NKK], u32x4 (&va)[NDD]) {
     const int p0 = T << 5;
     const bool edge = p0 < lo || p0 + 31 >= t;  // wave-uniform: needs masks or the new key
-    // key of k-slot j of this lane: j < 4 -> p0 + 4*g4 + j, else p0 + 16 + 4*g4 + j - 4
+    // k-slot j of this lane (score register i of half kb: j = 4 kb + i) is key p0 + 8 g4 + j
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (p0 + 16 * kb + c16 == t) {
+        if (p0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3) == t) {
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)&selfk[kk * 32 + 8 * g4];
         }
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int j = 0; j < 8; ++j) {
+        const int key = p0 + 8 * g4 + j;
+        const bool valid = key >= lo && key <= t;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = p0 + 16 * h2 + 4 * g4 + j;
-          const bool valid = key >= lo && key <= t;
-#pragma unroll
-          for (int dd = 0; dd < NDD; ++dd) {
-            uint32_t w = va[dd][h2][j >> 1];
-            const uint32_t sh = (j & 1) * 16;
-            uint32_t v = (w >> sh) & 0xffffu;
-            v = key == t ? (uint32_t)selfv[16 * dd + c16] : (valid ? v : 0u);
-            va[dd][h2][j >> 1] = (w & ~(0xffffu << sh)) | (v << sh);
-          }
+        for (int dd = 0; dd < NDD; ++dd) {
+          uint32_t w = va[dd][j >> 1];
+          const uint32_t sh = (j & 1) * 16;
+          uint32_t v = (w >> sh) & 0xffffu;
+          v = key == t ? (uint32_t)selfv[16 * dd + c16] : (valid ? v : 0u);
+          va[dd][j >> 1] = (w & ~(0xffffu << sh)) | (v << sh);
         }
+      }
     }
     // scores S^T[key][head] for both 16-key halves
     f32x4_t sc[2];
@@ -691,16 +698,19 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = p0 + 16 * kb + 4 * g4 + i;
+        const int key = p0 + 8 * g4 + 4 * kb + i;
         const bool valid = !edge || (key >= lo && key <= t);
         const float v = valid ? sc[kb][i] * sl2 : -INFINITY;
         v8[kb * 4 + i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    float mn = m, alpha = 1.f;
+    if (!fixed_ref) {
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      mn = fmaxf(m, tmax);
+      alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    }
     float ps = 0.f;
     bf16x8_t pb;
 #pragma unroll
@@ -716,9 +726,8 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     m = mn;
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) {
-      acc[dd] *= alpha;
-      const u32x4 vv = u32x4{va[dd][0][0], va[dd][0][1], va[dd][1][0], va[dd][1][1]};
-      acc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pb, acc[dd], 0, 0, 0);
+      if (!fixed_ref) acc[dd] *= alpha;
+      acc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&va[dd], pb, acc[dd], 0, 0, 0);
     }
   };
 
@@ -876,8 +885,8 @@ static hipError_t attn_dec_mfma(const AttnDecArgs& a, hipStream_t st) {
 }
 
 bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full) {
-  // 4-position runs of V^T must be contiguous and 8-byte aligned
-  return dtype == 1 && (hd == 64 || hd == 128) && slots % 4 == 0 && slots >= 4 && (is_full || window % 4 == 0);
+  // 8-position runs of V^T must be contiguous and 16-byte aligned
+  return dtype == 1 && (hd == 64 || hd == 128) && slots % 8 == 0 && slots >= 8 && (is_full || window % 8 == 0);
 }
 
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
