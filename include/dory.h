@@ -97,7 +97,7 @@ typedef struct {
   float combine_we;
   int32_t max_batch;      /* sequences per call                                        */
   int32_t max_ctx;        /* positions per sequence (bfloat16 decode attention runs on
-                             the matrix cores when max_ctx and window are multiples of 4) */
+                             the matrix cores when max_ctx and window are multiples of 8) */
   int32_t max_chunk;      /* positions per prefill chunk (longer prompts are chunked)  */
   int32_t max_loops;      /* largest n_loops accepted                                  */
   int32_t weight_format;  /* dory_weight_format of the layer projections; MXFP8 and NVFP4

@@ -193,7 +193,7 @@ def test_state_errors_on_gpu():
                                                      ("tiny_bf16", 2, "last_loop", 150, 24, 192),
                                                      ("tiny_bf16", 3, "per_loop", 97, 20, 160)])
 def test_bf16_widths(name, k, mode, n, steps, ctx):
-    """ctx = max_ctx: multiples of 4 take the matrix-core decode attention,
+    """ctx = max_ctx: multiples of 8 take the matrix-core decode attention,
     77 the vector fallback; the tiny shape's 64-key rings wrap."""
     m, w, dw = model_and_weights(name)
     prompt = make_tokens(m, 6, (1, n))
