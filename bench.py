@@ -479,8 +479,8 @@ def main():
     if args.headline_k not in ks:
         ks.append(args.headline_k)
     n, K, Wm = args.prompt, args.steps, args.warmup
-    # positions needed, rounded to 256 (a multiple of 4 keeps the cached
-    # values' 4-position runs aligned for the matrix-core decode attention)
+    # positions needed, rounded to 256 (a multiple of 8 keeps the cached
+    # values' 8-position runs aligned for the matrix-core decode attention)
     max_ctx = (n + Wm + K + args.kernel_steps + 2 + 255) // 256 * 256
 
     if args.copy_calibration:

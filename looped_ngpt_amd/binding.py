@@ -298,7 +298,7 @@ class Session:
 
     def __del__(self):
         h = getattr(self, "h", None)
-        if h:
+        if h and _lib is not None:  # at interpreter exit the module globals may be gone
             _lib.dory_destroy(h)
             self.h = None
 
