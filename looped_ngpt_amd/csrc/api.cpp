@@ -217,11 +217,10 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
     RopeArgs ra{};
     ra.qkvg = qkvg; ra.ld = P.qkvg_dim;
     ra.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
-    ra.p0 = c->pos; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads; ra.hd = C.head_dim;
+    ra.p0 = c->pos; ra.B = B; ra.n = n; ra.rows = rows; ra.nq = C.n_q_heads; ra.nkv = C.n_kv_heads;
+    ra.hd = C.head_dim;
     ra.vld = chunk_vld(n);
     ra.q_out = c->ws + W.q; ra.k_out = c->ws + W.kw; ra.v_out = c->ws + W.vw;
-    ra.kc = nullptr; ra.vc = nullptr;
-    ra.slots = slots; ra.window = C.window; ra.is_full = full;
     HIP_TRY(c, launch_rope_qk(dt, ra, st));
 
     AttnArgs aa{};

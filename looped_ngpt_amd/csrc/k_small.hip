@@ -210,112 +210,120 @@ hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipS
 }
 
 // ---------------------------------------------------------------------------
-// RoPE + per-head L2 norm of q and k, plain copy of v, optional cache write.
-// One wave per (row, head); lane l owns the rotation pair (l, l + hd/2).
+// RoPE + per-head L2 norm of q and k. One wave per (row, head); lane l owns
+// the rotation pair (l, l + hd/2).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int head = blockIdx.x * 4 + wave;
   const int r = blockIdx.y;
-  const int nh = a.nq + 2 * a.nkv;
-  if (head >= nh) return;
+  if (head >= a.nq + a.nkv) return;
   const int half = a.hd / 2;
-  const int b = r / a.n, i = r % a.n;
-  const int pos = a.p0 + i;
+  const int pos = a.p0 + r % a.n;
   const float* src = a.qkvg + (size_t)r * a.ld + (size_t)head * a.hd;
   if (lane >= half) return;
-  float x1 = src[lane], x2 = src[lane + half];
-  T* dst;
-  T* cdst = nullptr;
-  if (head < a.nq + a.nkv) {
-    const float2 cs = a.tab[(size_t)pos * half + lane];
-    const float r1 = x1 * cs.x - x2 * cs.y;
-    const float r2 = x2 * cs.x + x1 * cs.y;
-    // lanes >= half returned early; the wave sum below only sees active lanes
-    float ss = r1 * r1 + r2 * r2;
+  const float x1 = src[lane], x2 = src[lane + half];
+  const float2 cs = a.tab[(size_t)pos * half + lane];
+  const float r1 = x1 * cs.x - x2 * cs.y;
+  const float r2 = x2 * cs.x + x1 * cs.y;
+  // lanes >= half returned early; the wave sum below only sees active lanes
+  float ss = r1 * r1 + r2 * r2;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float other = __shfl_xor(ss, o, 64);
-      if ((lane ^ o) < half) ss += other;
-    }
-    const float inv = inv_norm(ss);
-    x1 = r1 * inv;
-    x2 = r2 * inv;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float other = __shfl_xor(ss, o, 64);
+    if ((lane ^ o) < half) ss += other;
   }
-  if (head < a.nq) {
-    dst = (T*)a.q_out + ((size_t)r * a.nq + head) * a.hd;
-  } else {
-    const bool isk = head < a.nq + a.nkv;
-    const int kvh = isk ? head - a.nq : head - a.nq - a.nkv;
-    if (isk) {
-      dst = (T*)a.k_out + ((size_t)r * a.nkv + kvh) * a.hd;
-    } else {
-      // values of the call transposed per head: [hd][vld], position i at column i
-      T* vt = (T*)a.v_out + ((size_t)b * a.nkv + kvh) * a.hd * a.vld + i;
-      vt[(size_t)lane * a.vld] = from_f<T>(x1);
-      vt[(size_t)(lane + half) * a.vld] = from_f<T>(x2);
-      dst = nullptr;
-    }
-    if (a.kc) {
-      const int slot = a.is_full ? pos : pos % a.window;
-      if (isk) {
-        cdst = (T*)a.kc + (((size_t)b * a.nkv + kvh) * a.slots + slot) * a.hd;
-      } else {
-        // values: 32-position blocks [hd][32] per kv head
-        T* vt = (T*)a.vc + ((size_t)b * a.nkv + kvh) * a.hd * vslots_of(a.slots);
-        vt[vt_off(slot, lane, a.hd)] = from_f<T>(x1);
-        vt[vt_off(slot, lane + half, a.hd)] = from_f<T>(x2);
-      }
-    }
+  const float inv = inv_norm(ss);
+  T* dst = head < a.nq ? (T*)a.q_out + ((size_t)r * a.nq + head) * a.hd
+                       : (T*)a.k_out + ((size_t)r * a.nkv + head - a.nq) * a.hd;
+  dst[lane] = from_f<T>(r1 * inv);
+  dst[lane + half] = from_f<T>(r2 * inv);
+}
+
+// The call's values transposed per kv head, [B][n_kv][hd][vld] with position
+// i at column i (zeros from n to vld): a workgroup takes 64 positions of one
+// kv head, reads them as rows through LDS and writes each dimension's run of
+// positions contiguously.
+constexpr int kVtPos = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_v_transpose(RopeArgs a) {
+  __shared__ float tile[kVtPos][129];
+  const int i0 = blockIdx.x * kVtPos, kvh = blockIdx.y, b = blockIdx.z;
+  const int hd = a.hd;  // <= 128
+  const size_t col = (size_t)(a.nq + a.nkv + kvh) * hd;
+  for (int e = threadIdx.x; e < kVtPos * hd; e += 256) {
+    const int p = e / hd, d = e % hd, i = i0 + p;
+    tile[p][d] = i < a.n ? a.qkvg[(size_t)(b * a.n + i) * a.ld + col + d] : 0.f;
   }
-  const T y1 = from_f<T>(x1), y2 = from_f<T>(x2);
-  if (dst) {
-    dst[lane] = y1;
-    dst[lane + half] = y2;
-  }
-  if (cdst) {
-    cdst[lane] = y1;
-    cdst[lane + half] = y2;
+  __syncthreads();
+  T* out = (T*)a.v_out + ((size_t)b * a.nkv + kvh) * hd * a.vld;
+  for (int e = threadIdx.x; e < kVtPos * hd; e += 256) {
+    const int d = e / kVtPos, p = e % kVtPos, i = i0 + p;
+    if (i < a.vld) out[(size_t)d * a.vld + i] = from_f<T>(tile[p][d]);
   }
 }
 
 hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  const int nh = a.nq + 2 * a.nkv;
-  dim3 grid((nh + 3) / 4, a.rows);
-  if (dtype == 0)
+  if (a.hd > 128 || a.rows != a.B * a.n) return hipErrorInvalidValue;
+  const dim3 grid((a.nq + a.nkv + 3) / 4, a.rows);
+  const dim3 vgrid((a.vld + kVtPos - 1) / kVtPos, a.nkv, a.B);
+  if (dtype == 0) {
     hipLaunchKernelGGL(k_rope_qk<float>, grid, dim3(256), 0, st, a);
-  else
+    hipLaunchKernelGGL(k_v_transpose<float>, vgrid, dim3(256), 0, st, a);
+  } else {
     hipLaunchKernelGGL(k_rope_qk<bf16>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_v_transpose<bf16>, vgrid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // KV writer after a multi-position call (attention has already read the old
-// ring contents). Block = one row; copies k and v of all kv heads.
+// ring contents): every position of a full layer, the last min(n, slots)
+// positions of a sliding-window ring. A workgroup takes 32 consecutive
+// positions of one (sequence, kv head): keys row by row, values as runs of
+// positions (the call's V^T rows and the cache's 32-slot blocks both keep a
+// dimension's positions contiguous), 16 bytes at a time where a run of 8
+// positions lands on 8 consecutive slots of one block, else one by one.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_kv_write(const T* __restrict__ kw, const T* __restrict__ vw, int vld,
                                                  T* __restrict__ kc, T* __restrict__ vc, int n, int p0, int nkv,
                                                  int hd, int slots, int window, int is_full,
                                                  const int* __restrict__ wloops, int loop) {
-  const int r = blockIdx.x;
-  const int b = r / n, i = r % n;
-  if (!is_full && i < n - slots) return;  // overwritten later in this call
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte vector
+  const int i0 = blockIdx.x * 32, kvh = blockIdx.y, b = blockIdx.z;
   if (wloops && wloops[b] != loop) return;  // not this sequence's last pass
-  const int pos = p0 + i;
-  const int slot = is_full ? pos : pos % window;
-  const int kvd = nkv * hd;
-  for (int e = threadIdx.x; e < 2 * kvd; e += blockDim.x) {
-    const bool isk = e < kvd;
-    const int x = isk ? e : e - kvd;
-    const int kvh = x / hd, c = x % hd;
-    const T val = isk ? kw[(size_t)r * kvd + x] : vw[((size_t)b * kvd + x) * vld + i];
-    if (isk)
-      kc[(((size_t)b * nkv + kvh) * slots + slot) * hd + c] = val;
-    else  // values: 32-position blocks [hd][32] per kv head
-      vc[((size_t)b * nkv + kvh) * hd * vslots_of(slots) + vt_off(slot, c, hd)] = val;
+  const int i_first = is_full ? 0 : max(0, n - slots);  // earlier positions are overwritten later in this call
+  auto slot_of = [&](int i) { return is_full ? p0 + i : (p0 + i) % window; };
+  const size_t head = (size_t)b * nkv + kvh;
+  // keys: 32 rows of hd, E elements per thread and step
+  const int kv_per_row = hd / E;
+  for (int e = threadIdx.x; e < 32 * kv_per_row; e += 256) {
+    const int p = e / kv_per_row, c = e % kv_per_row, i = i0 + p;
+    if (i < n && i >= i_first)
+      *(u32x4*)(kc + (head * slots + slot_of(i)) * hd + c * E) =
+          *(const u32x4*)(kw + ((size_t)(b * n + i) * nkv + kvh) * hd + c * E);
+  }
+  // values: per dimension, runs of E positions
+  const T* vsrc = vw + head * hd * vld;
+  T* vdst = vc + head * hd * vslots_of(slots);
+  for (int e = threadIdx.x; e < hd * (32 / E); e += 256) {
+    const int d = e / (32 / E), ia = i0 + E * (e % (32 / E));
+    const int sa = slot_of(ia);
+    const bool vec = ia >= i_first && ia + E <= n && (sa % E) == 0 && (sa % 32) + E <= 32 &&
+                     slot_of(ia + E - 1) == sa + E - 1 && ((size_t)d * vld + ia) % E == 0;
+    if (vec) {
+      *(u32x4*)(vdst + vt_off(sa, d, hd)) = *(const u32x4*)(vsrc + (size_t)d * vld + ia);
+    } else {
+      for (int q = 0; q < E; ++q) {
+        const int i = ia + q;
+        if (i < n && i >= i_first) vdst[vt_off(slot_of(i), d, hd)] = vsrc[(size_t)d * vld + i];
+      }
+    }
   }
 }
 
@@ -323,11 +331,13 @@ hipError_t launch_kv_write(int dtype, const void* kw, const void* vw, int vld, v
                            int p0, int nkv, int hd, int slots, int window, int is_full, hipStream_t st,
                            const int* wloops, int loop) {
   if (B * n <= 0) return hipSuccess;
+  if (hd % 8) return hipErrorInvalidValue;
+  const dim3 grid((n + 31) / 32, nkv, B);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_kv_write<float>, dim3(B * n), dim3(256), 0, st, (const float*)kw, (const float*)vw, vld,
+    hipLaunchKernelGGL(k_kv_write<float>, grid, dim3(256), 0, st, (const float*)kw, (const float*)vw, vld,
                        (float*)kc, (float*)vc, n, p0, nkv, hd, slots, window, is_full, wloops, loop);
   else
-    hipLaunchKernelGGL(k_kv_write<bf16>, dim3(B * n), dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw, vld,
+    hipLaunchKernelGGL(k_kv_write<bf16>, grid, dim3(256), 0, st, (const bf16*)kw, (const bf16*)vw, vld,
                        (bf16*)kc, (bf16*)vc, n, p0, nkv, hd, slots, window, is_full, wloops, loop);
   return hipGetLastError();
 }

@@ -51,12 +51,14 @@ hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipS
 // transposed, v_out [B][nkv][hd][vld] (position i at column i).
 // If kc is not NULL also writes k, v to the cache slot of each position
 // (only valid when no other position of the same launch maps to that slot).
+// a multi-position call's q / k (RoPE + per-head norm) into q_out / k_out
+// (rows of [heads][hd]) and its values into v_out ([B][nkv][hd][vld], V^T per
+// kv head, zeros from n to vld); rows = B * n, hd <= 128
 struct RopeArgs {
   const float* qkvg; int64_t ld;
   const float2* tab;
-  int p0, n, rows, nq, nkv, hd, vld;
+  int p0, B, n, rows, nq, nkv, hd, vld;
   void* q_out; void* k_out; void* v_out;
-  void* kc; void* vc; int slots, window, is_full;
 };
 hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st);
 
