@@ -350,9 +350,13 @@ dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* o
  * matrix cores with float32 accumulation), everything else float32. Needs a
  * DORY_WEIGHTS_DTYPE context, n <= max_ctx, head_dim 64 or 128; independent
  * of the sequence state (no cache is read or written). ws_dev: device,
- * 256-byte aligned, >= dory_backward_workspace_bytes(cfg, batch, n).
- * Enqueued on the context's stream. DORY_E_ARG on bad arguments (nothing
- * enqueued), DORY_E_HIP on a launch failure. */
+ * 256-byte aligned, caller-owned; with ws_bytes >= dory_backward_workspace_bytes
+ * the forward values of every recurrent layer are kept from the forward sweep
+ * (fastest), with ws_bytes >= dory_backward_workspace_min_bytes only each
+ * layer's input is kept and its forward runs again during the backward (the
+ * same results, bit for bit). Enqueued on the context's stream. DORY_E_ARG on
+ * bad arguments or a smaller workspace (nothing enqueued), DORY_E_HIP on a
+ * launch failure. */
 typedef struct {            /* host arrays of n_rec device float32 pointers; entry i is
                                global layer n_in + i                                    */
   float* const* qkvg;       /* [qkvg_dim, d] */
@@ -363,7 +367,10 @@ typedef struct {            /* host arrays of n_rec device float32 pointers; ent
   float* const* alpha_mlp;  /* [d]           */
 } dory_grads;
 
+/* workspace of the backward keeping every layer's forward values / of the one
+ * recomputing them; 0 on a bad configuration or size */
 size_t dory_backward_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t n);
+size_t dory_backward_workspace_min_bytes(const dory_config* cfg, int32_t batch, int32_t n);
 dory_status dory_backward_last_loop(dory_ctx* ctx, const float* x_dev, const float* grad_out_dev, int32_t batch,
                                     int32_t n, const dory_grads* grads, float* grad_x_dev, void* ws_dev,
                                     size_t ws_bytes);

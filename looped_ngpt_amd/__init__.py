@@ -9,7 +9,7 @@ _NAMES = (
     "DoryError", "Session", "make_config", "validate_config", "kv_bytes", "workspace_bytes", "kv_slot",
     "upload_weights", "op_linear", "op_argmax", "argmax_scratch_bytes", "lib", "EXPORTS",
     "quantize_weights_mxfp8", "op_quant_mxfp8", "op_linear_mx", "WEIGHTS_DTYPE", "WEIGHTS_MXFP8", "PROJECTIONS",
-    "WEIGHTS_NVFP4", "quantize_weights_nvfp4", "op_quant_nvfp4", "op_linear_fp4", "backward_workspace_bytes",
+    "WEIGHTS_NVFP4", "quantize_weights_nvfp4", "op_quant_nvfp4", "op_linear_fp4", "backward_workspace_bytes", "backward_workspace_min_bytes",
     "DORY_OK", "DORY_E_ARG", "DORY_E_CAPACITY", "DORY_E_LOOPS", "DORY_E_KV_MODE", "DORY_E_STATE", "DORY_E_HIP",
     "DORY_F32", "DORY_BF16", "DORY_KV_PER_LOOP", "DORY_KV_LAST_LOOP", "KV_MODES",
 )

@@ -39,7 +39,8 @@ EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dor
            "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
-           "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_backward_workspace_bytes", "dory_backward_last_loop"]
+           "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_backward_workspace_bytes", "dory_backward_workspace_min_bytes",
+           "dory_backward_last_loop"]
 
 
 class DoryConfig(ctypes.Structure):
@@ -103,6 +104,7 @@ _sig = {
     "dory_argmax_scratch_bytes": (ctypes.c_size_t, [_I, _I]),
     "dory_op_argmax": (_I, [_P, _I, _I, _P, _P, _P]),
     "dory_backward_workspace_bytes": (ctypes.c_size_t, [_C, _I, _I]),
+    "dory_backward_workspace_min_bytes": (ctypes.c_size_t, [_C, _I, _I]),
     "dory_backward_last_loop": (_I, [_P, _P, _P, _I, _I, ctypes.POINTER(DoryGrads), _P, _P, ctypes.c_size_t]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -156,7 +158,13 @@ def workspace_bytes(c: DoryConfig) -> int:
 
 
 def backward_workspace_bytes(c: DoryConfig, batch: int, n: int) -> int:
+    """workspace that keeps every recurrent layer's forward values"""
     return _lib.dory_backward_workspace_bytes(ctypes.byref(c), batch, n)
+
+
+def backward_workspace_min_bytes(c: DoryConfig, batch: int, n: int) -> int:
+    """workspace of the backward that recomputes each layer's forward"""
+    return _lib.dory_backward_workspace_min_bytes(ctypes.byref(c), batch, n)
 
 
 def kv_slot(c: DoryConfig, kv_mode: int, kv_loops: int, layer: int, loop: int, pos: int):
@@ -347,15 +355,17 @@ class Session:
         self._check(_lib.dory_resume(self.h, batch, pos, n_loops, mode))
         self.batch = batch
 
-    def backward_last_loop(self, x, grad_out, *, ws=None, grads=None, stream_sync: bool = False):
+    def backward_last_loop(self, x, grad_out, *, ws=None, grads=None, stream_sync: bool = False,
+                           recompute: bool = False):
         """Depth-1 backward of the last recurrent invocation (dory_backward_last_loop).
         x, grad_out: float32 [B, n, d] device tensors. Returns a dict of float32
         gradients keyed like the weights ("L{l}.qkvg", ..., "L{l}.alpha_a",
-        "L{l}.alpha_m" for the recurrent layers) plus "x"."""
+        "L{l}.alpha_m" for the recurrent layers) plus "x". recompute: pass the
+        smaller workspace, with which each layer's forward runs again."""
         import torch
         m = self.model
         B, n, d = x.shape
-        wsb = backward_workspace_bytes(self.cfg, B, n)
+        wsb = (backward_workspace_min_bytes if recompute else backward_workspace_bytes)(self.cfg, B, n)
         if wsb == 0:
             raise DoryError(DORY_E_ARG, "backward workspace size")
         if ws is None or ws.numel() < wsb:

@@ -1212,7 +1212,13 @@ dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, con
 size_t dory_backward_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t n) {
   Plan p;
   if (!cfg || batch < 1 || n < 1 || make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
-  return make_bw_layout(p, batch, n).total;
+  return make_bw_layout(p, batch, n, true).total;
+}
+
+size_t dory_backward_workspace_min_bytes(const dory_config* cfg, int32_t batch, int32_t n) {
+  Plan p;
+  if (!cfg || batch < 1 || n < 1 || make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  return make_bw_layout(p, batch, n, false).total;
 }
 
 dory_status dory_backward_last_loop(dory_ctx* c, const float* x, const float* grad_out, int32_t batch, int32_t n,
@@ -1230,18 +1236,22 @@ dory_status dory_backward_last_loop(dory_ctx* c, const float* x, const float* gr
   for (int i = 0; i < C.n_rec; ++i)
     if (!g->qkvg[i] || !g->o[i] || !g->ug[i] || !g->down[i] || !g->alpha_attn[i] || !g->alpha_mlp[i])
       return set_err(c, DORY_E_ARG, "backward: null gradient pointer");
-  Bw b{c, make_bw_layout(P, batch, n), (char*)ws_dev, batch, n, batch * n};
+  // every layer's forward values kept when the workspace holds them, else
+  // each layer's forward runs again just before its backward
+  const bool stored = ws_bytes >= make_bw_layout(P, batch, n, true).total;
+  Bw b{c, make_bw_layout(P, batch, n, stored), (char*)ws_dev, batch, n, batch * n};
   if (ws_bytes < b.L.total || ((uintptr_t)ws_dev & (kAlign - 1)))
     return set_err(c, DORY_E_ARG, "backward: workspace too small or misaligned");
   DORY_TRY(device_init(c));
+  auto at = [&](int i) { return Bw{b.c, bw_layer_view(b.L, i), b.ws, b.B, b.n, b.M}; };
   const size_t rows = (size_t)b.M * C.d_model;
   HIP_TRY(c, hipMemcpyAsync(b.h_at(0), x, rows * 4, hipMemcpyDeviceToDevice, c->st));
-  for (int i = 0; i < C.n_rec; ++i) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));
+  for (int i = 0; i < C.n_rec; ++i) DORY_TRY(bw_layer_fwd(at(i), C.n_in + i, b.h_at(i), b.h_at(i + 1)));
   float* dh = b.f<float>(b.L.dh);
   HIP_TRY(c, launch_bw_final(b.h_at(C.n_rec), grad_out, b.M, C.d_model, dh, c->st));
   for (int i = C.n_rec - 1; i >= 0; --i) {
-    if (i < C.n_rec - 1) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));  // recompute
-    DORY_TRY(bw_layer_bwd(b, C.n_in + i, i, b.h_at(i), b.h_at(i + 1), dh, dh, g));
+    if (!stored && i < C.n_rec - 1) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));  // recompute
+    DORY_TRY(bw_layer_bwd(at(i), C.n_in + i, i, b.h_at(i), b.h_at(i + 1), dh, dh, g));
   }
   if (grad_x) HIP_TRY(c, hipMemcpyAsync(grad_x, dh, rows * 4, hipMemcpyDeviceToDevice, c->st));
   return DORY_OK;

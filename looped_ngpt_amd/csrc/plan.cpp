@@ -153,39 +153,23 @@ WsLayout make_ws_layout(const Plan& p) {
   return w;
 }
 
-BwLayout make_bw_layout(const Plan& p, int B, int n) {
+BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   BwLayout w;
   const auto& c = p.cfg;
   const size_t M = (size_t)B * n, d = c.d_model, F = c.d_ff, Q = p.qkvg_dim, qd = p.q_dim, kvd = p.kv_dim;
   const size_t nq = c.n_q_heads, el = p.elem;
+  const bool bf = c.dtype == DORY_BF16;
+  const size_t hq = (size_t)B * nq * n * c.head_dim, hk = (size_t)B * c.n_kv_heads * n * c.head_dim;
+  const size_t sq = (size_t)B * nq * n * n;
   size_t at = 0;
   auto take = [&](size_t bytes) {
     size_t o = at;
     at = align_up(at + (bytes ? bytes : 1));
     return o;
   };
+  // scratch shared by the layers
   w.hin = take((size_t)(c.n_rec + 1) * M * d * 4);
-  w.P1 = take(M * Q * 4);
-  w.qn = take(M * qd * 4);
-  w.kn = take(M * kvd * 4);
-  w.rq = take(M * nq * 4);
-  w.rk = take(M * c.n_kv_heads * 4);
-  w.o = take(M * qd * 4);
-  w.mst = take(M * nq * 4);
-  w.lst = take(M * nq * 4);
-  w.oh = take(M * qd * 4);
-  w.rc = take(M * 4);
   w.y = take(M * d * 4);
-  w.yh = take(M * d * 4);
-  w.ry = take(M * 4);
-  w.rz = take(M * 4);
-  w.h1 = take(M * d * 4);
-  w.P2 = take(M * 2 * F * 4);
-  w.a32 = take(M * F * 4);
-  w.rs = take(M * 4);
-  w.y2h = take(M * d * 4);
-  w.ry2 = take(M * 4);
-  w.rz2 = take(M * 4);
   w.dres = take(M * d * 4);
   w.contrib = take(M * d * 4);
   w.tmp = take(M * std::max(d, std::max(F, qd)) * 4);
@@ -197,32 +181,72 @@ BwLayout make_bw_layout(const Plan& p, int B, int n) {
   w.dkn = take(M * kvd * 4);
   w.dv = take(M * kvd * 4);
   w.dP1 = take(M * Q * 4);
-  w.xb = take(M * d * el);
-  w.ohb = take(M * qd * el);
-  w.h1b = take(M * d * el);
-  w.ab = take(M * F * el);
   w.dyb = take(M * d * el);
   w.dP2b = take(M * 2 * F * el);
   w.dP1b = take(M * Q * el);
   w.TA = take(M * std::max(Q, std::max(2 * F, d)) * el);
   w.TB = take(M * std::max(d, std::max(F, qd)) * el);
   w.WT = take(std::max(std::max(Q * d, 2 * F * d), std::max(d * qd, d * F)) * el);
-  if (c.dtype == DORY_BF16) {
-    const size_t hq = (size_t)B * nq * n * c.head_dim, hk = (size_t)B * c.n_kv_heads * n * c.head_dim;
-    const size_t sq = (size_t)B * nq * n * n;
-    w.Qh = take(hq * el);
+  if (bf) {
     w.dOh = take(hq * el);
-    w.Kh = take(hk * el);
-    w.Vh = take(hk * el);
     w.Oh = take(hq * 4);
     w.dQh = take(hq * 4);
     w.dKh = take(hk * 4);
     w.dVh = take(hk * 4);
     w.S = take(sq * 4);
+  }
+  // one layer's forward values
+  const size_t g0 = at;
+  w.P1 = take(M * Q * 4);
+  w.qn = take(M * qd * 4);
+  w.kn = take(M * kvd * 4);
+  w.rq = take(M * nq * 4);
+  w.rk = take(M * c.n_kv_heads * 4);
+  w.o = take(M * qd * 4);
+  w.mst = take(M * nq * 4);
+  w.lst = take(M * nq * 4);
+  w.oh = take(M * qd * 4);
+  w.rc = take(M * 4);
+  w.yh = take(M * d * 4);
+  w.ry = take(M * 4);
+  w.rz = take(M * 4);
+  w.h1 = take(M * d * 4);
+  w.P2 = take(M * 2 * F * 4);
+  w.a32 = take(M * F * 4);
+  w.rs = take(M * 4);
+  w.y2h = take(M * d * 4);
+  w.ry2 = take(M * 4);
+  w.rz2 = take(M * 4);
+  w.xb = take(M * d * el);
+  w.ohb = take(M * qd * el);
+  w.h1b = take(M * d * el);
+  w.ab = take(M * F * el);
+  if (bf) {
+    w.Qh = take(hq * el);
+    w.Kh = take(hk * el);
+    w.Vh = take(hk * el);
     w.Pb = take(sq * el);
   }
-  w.total = at;
+  w.layer_bytes = at - g0;
+  w.stored = stored;
+  w.total = at + (stored ? (size_t)(c.n_rec - 1) * w.layer_bytes : 0);
   return w;
+}
+
+BwLayout bw_layer_view(const BwLayout& L, int i) {
+  BwLayout v = L;
+  if (!L.stored || i == 0) return v;
+  const size_t s = (size_t)i * L.layer_bytes;
+  for (size_t* f : {&v.P1, &v.qn, &v.kn, &v.rq, &v.rk, &v.o, &v.mst, &v.lst, &v.oh, &v.rc, &v.yh, &v.ry, &v.rz,
+                    &v.h1, &v.P2, &v.a32, &v.rs, &v.y2h, &v.ry2, &v.rz2, &v.xb, &v.ohb, &v.h1b, &v.ab})
+    *f += s;
+  if (L.Pb) {
+    v.Qh += s;
+    v.Kh += s;
+    v.Vh += s;
+    v.Pb += s;
+  }
+  return v;
 }
 
 }  // namespace dory

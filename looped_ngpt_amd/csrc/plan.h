@@ -94,10 +94,21 @@ struct BwLayout {
   // [B][heads][n][hd] (T: Qh, Kh, Vh, dOh; float32: Oh, dQh, dKh, dVh), the
   // scores / dP [B][n_q][n][n] (float32) and P / dS [B][n_q][n][n] (T)
   size_t Qh = 0, Kh = 0, Vh = 0, dOh = 0, Oh = 0, dQh = 0, dKh = 0, dVh = 0, S = 0, Pb = 0;
+  // The values a layer's backward reads from its forward (P1 .. rz2 above
+  // but y, the T copies xb .. ab, Qh, Kh, Vh, Pb) sit in one group at the end
+  // of the layout, layer_bytes long; with every layer's group kept
+  // (stored = true: n_rec groups) the backward reads them instead of running
+  // each layer's forward again.
+  size_t layer_bytes = 0;
+  bool stored = false;
   size_t total = 0;
 };
 
-BwLayout make_bw_layout(const Plan& p, int B, int n);
+// stored: one group of forward values per recurrent layer (else one, refilled
+// by recomputing each layer's forward during the backward)
+BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored);
+// the layout with the forward-value group of recurrent layer i (stored layouts)
+BwLayout bw_layer_view(const BwLayout& L, int i);
 
 size_t argmax_partials(int32_t B, int32_t V);
 

@@ -250,11 +250,15 @@ def test_backward_workspace_and_validation():
     rejects bad arguments on the host, before anything is enqueued."""
     m = small(dtype="bf16", d_ff=704)
     c, _k = dory.make_config(m, max_batch=1, max_ctx=16, max_chunk=16)
-    a = dory.backward_workspace_bytes(c, 1, 8)
-    b = dory.backward_workspace_bytes(c, 2, 8)
-    assert 0 < a < b and dory.backward_workspace_bytes(c, 0, 8) == 0
+    a = dory.backward_workspace_min_bytes(c, 1, 8)
+    b = dory.backward_workspace_min_bytes(c, 2, 8)
+    assert 0 < a < b and dory.backward_workspace_min_bytes(c, 0, 8) == 0
     # the checkpointed layer inputs alone: (n_rec + 1) * rows * d float32
     assert a >= (m.n_rec + 1) * 8 * m.d_model * 4
+    # keeping every recurrent layer's forward values: one more group per layer
+    s1, s2 = dory.backward_workspace_bytes(c, 1, 8), dory.backward_workspace_bytes(c, 2, 8)
+    assert a < s1 < s2 and dory.backward_workspace_bytes(c, 1, 0) == 0
+    assert m.n_rec == 1 or (s1 - a) % (m.n_rec - 1) == 0
     lib = dory.lib()
     L = m.n_rec
     fake = (ctypes.c_void_p * L)(*[(1 << 20) * (i + 1) for i in range(L)])

@@ -115,3 +115,22 @@ def test_backward_argument_errors():
     x = torch.zeros((1, 40, cfg.d_model), dtype=torch.float32, device="cuda")
     with pytest.raises(dory.DoryError):
         s.backward_last_loop(x, x)            # n > max_ctx
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_kept_forward_equals_recompute(dtype):
+    """The full workspace keeps every layer's forward values; the minimum one
+    recomputes each layer's forward during the backward: the same kernels on
+    the same inputs, so the gradients agree bit for bit."""
+    cfg = _small(2, dtype)
+    w = _alphas(cfg, make_weights(cfg), 95)
+    x, G = _inputs(cfg, 2, 32, 96)
+    dw = dory.upload_weights(cfg, w)
+    s = dory.Session(cfg, dw, max_batch=1, max_ctx=64, max_chunk=8, kv_mode="last_loop")
+    xt, gt = torch.from_numpy(x).cuda(), torch.from_numpy(G).cuda()
+    print(f"backward kept vs recomputed forward, {dtype}", flush=True)
+    kept = {k: v.cpu().numpy() for k, v in s.backward_last_loop(xt, gt).items()}
+    again = {k: v.cpu().numpy() for k, v in s.backward_last_loop(xt, gt, recompute=True).items()}
+    assert kept.keys() == again.keys()
+    for k in kept:
+        np.testing.assert_array_equal(kept[k], again[k], err_msg=k)
