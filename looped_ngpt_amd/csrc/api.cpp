@@ -116,7 +116,7 @@ dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void*
   const Plan& P = c->plan;
   const int dt = P.cfg.dtype;
   const int fmt = P.cfg.weight_format;
-  // bfloat16 GEMMs at prefill row counts: hipBLASLt (its own algorithm per
+  // bfloat16 GEMMs above the GEMV row counts: hipBLASLt (its own algorithm per
   // shape). SwiGLU: the library writes u | v in bfloat16 into the fused
   // projection's buffer (free once attention has run) and a row kernel
   // applies the activation — u and v are rounded to bfloat16 on this path.

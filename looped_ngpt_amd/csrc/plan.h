@@ -17,7 +17,7 @@ constexpr int kMaxSplits = 64;        // split-K pieces per (row, kv head) in de
 constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
 constexpr size_t kAlign = 256;
 constexpr size_t kBlasWsBytes = 32u << 20;  // workspace handed to hipBLASLt for prefill GEMMs
-constexpr int kBlasMinRows = 256;           // prefill rows from which plain GEMMs go to hipBLASLt
+constexpr int kBlasMinRows = 9;  // rows from which bfloat16 GEMMs go to hipBLASLt (up to 8: our GEMVs)
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 // Row length of a call's transposed values [B][n_kv][hd][vld]: n rounded up
