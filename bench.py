@@ -460,8 +460,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (sequences are "
+              "independent, so batches would split across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch
