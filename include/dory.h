@@ -179,10 +179,11 @@ const char* dory_status_string(dory_status s);
 /* ---- context ------------------------------------------------------------ */
 
 /* Binds caller memory. For bfloat16 models with a device present it also
- * creates the context's hipBLASLt handle (the plain prefill projections run
- * on hipBLASLt; the library allocates its own small state there, the only
- * allocation this API makes, and none after); otherwise it makes no HIP call
- * and everything runs on this library's kernels. The first dory_prefill on
+ * creates the context's hipBLASLt handle: every bfloat16 GEMM above 8 rows
+ * (prefill, batched decode, the backward's products) runs on hipBLASLt; the library
+ * allocates its own small state there, the only allocation this API makes,
+ * and none after; otherwise it makes no HIP call and everything runs on this
+ * library's kernels. The first dory_prefill on
  * the context builds the RoPE tables (angles in float64, stored float32) in
  * the workspace on the stream. kv_dev must hold dory_kv_bytes(cfg, kv_mode,
  * kv_loops) bytes and ws_dev dory_workspace_bytes(cfg); both 256-byte
