@@ -32,16 +32,68 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Butterfly steps of a 64-lane wave without the LDS crossbar (a ds_bpermute
+// round trip costs ~4x a whole DPP reduction): xsum<K>(v) = v + v[lane ^ K]
+// and xmax<K> likewise, bit for bit, since each lane adds the same two values
+// as its partner (float addition is commutative). K = 1, 2: DPP quad_perm;
+// 4: row_shl:4 into banks 0 and 2, row_shr:4 into banks 1 and 3; 8:
+// row_ror:8; 16, 32: gfx950's v_permlane16_swap / v_permlane32_swap, whose
+// two results are the even and odd rows (lower and upper halves) of v. Every
+// lane of the wave must be active.
+template <int CTRL, int BANKS = 0xF>
+__device__ __forceinline__ float dpp_mov(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xF, BANKS, false));
+}
+
+template <int K>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8 || K == 16 || K == 32, "power of two below 64");
+  if constexpr (K == 32 || K == 16) {
+    const auto r = K == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    a = v;
+    if constexpr (K == 1) b = dpp_mov<0xB1>(0.f, v);       // quad_perm [1,0,3,2]
+    else if constexpr (K == 2) b = dpp_mov<0x4E>(0.f, v);  // quad_perm [2,3,0,1]
+    else if constexpr (K == 4) b = dpp_mov<0x104, 0x5>(dpp_mov<0x114, 0xA>(0.f, v), v);
+    else b = dpp_mov<0x128>(0.f, v);                       // row_ror:8
+  }
+}
+
+template <int K>
+__device__ __forceinline__ float xsum(float v) {
+  float a, b;
+  lane_pair<K>(v, a, b);
+  return a + b;
+}
+
+template <int K>
+__device__ __forceinline__ float xmax(float v) {
+  float a, b;
+  lane_pair<K>(v, a, b);
+  return fmaxf(a, b);
+}
+
+// Sum / max over the wave, every lane gets the result; the pairing (32, 16,
+// 8, 4, 2, 1) is the classic butterfly's, so the rounding is too.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = xsum<32>(v);
+  v = xsum<16>(v);
+  v = xsum<8>(v);
+  v = xsum<4>(v);
+  v = xsum<2>(v);
+  return xsum<1>(v);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = xmax<32>(v);
+  v = xmax<16>(v);
+  v = xmax<8>(v);
+  v = xmax<4>(v);
+  v = xmax<2>(v);
+  return xmax<1>(v);
 }
 
 // Sum over a workgroup of NT threads (NT a multiple of 64). `sh` holds at

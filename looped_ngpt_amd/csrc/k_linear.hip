@@ -290,7 +290,10 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   for (int c = 0; c < P; ++c) buf[c] = __builtin_nontemporal_load(chunk_ptr(c));
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int m = 0; m < M; ++m) {
+  // one row: a single pass the compiler sees whole (a runtime trip count with
+  // loads inside makes its wait counts at the loop joins wait for the weights)
+  const int Mp = MB == 1 ? 1 : M;
+  for (int m = 0; m < Mp; ++m) {
     const size_t ro = (size_t)m * K;
     if (m > 0) {
 #pragma unroll
