@@ -112,8 +112,12 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       float dsum = 0.f;
 #pragma unroll
       for (int d = 0; d < DP; ++d) dsum = fmaf(qs[g][part * DP + d], to_f(Ks[key * KLD + part * DP + d]), dsum);
-#pragma unroll
-      for (int o = 1; o < NPART; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
+      if constexpr (NPART > 1) dsum = xsum<1>(dsum);
+      if constexpr (NPART > 2) dsum = xsum<2>(dsum);
+      if constexpr (NPART > 4) dsum = xsum<4>(dsum);
+      if constexpr (NPART > 8) dsum = xsum<8>(dsum);
+      if constexpr (NPART > 16) dsum = xsum<16>(dsum);
+      if constexpr (NPART > 32) dsum = xsum<32>(dsum);
       sc[g] = key < nk ? a.scale * dsum : -INFINITY;
     }
     // tile max per head
@@ -431,19 +435,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) d = fmaf(qr[g][i], kf[i], d);
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        d += __shfl_xor(d, 4, 64);
+        d = xsum<4>(xsum<2>(xsum<1>(d)));
         const float sc = valid ? d : -INFINITY;
-        float mt = fmaxf(sc, __shfl_xor(sc, 8, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mt = xmax<32>(xmax<16>(xmax<8>(sc)));
         const float mn = fmaxf(m[g], mt);
         const float alpha = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mn);
         const float p = valid ? exp2f(sc - mn) : 0.f;
-        float ps = p + __shfl_xor(p, 8, 64);
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        const float ps = xsum<32>(xsum<16>(xsum<8>(p)));
         l[g] = l[g] * alpha + ps;
         m[g] = mn;
 #pragma unroll
@@ -458,10 +456,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecArgs a) {
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
       float v = acc[g][i];
-      v += __shfl_xor(v, 8, 64);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[g][i] = v;
+      acc[g][i] = xsum<32>(xsum<16>(xsum<8>(v)));
     }
   if (kg == 0) {
 #pragma unroll
@@ -706,8 +701,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       }
     float mn = m, alpha = 1.f;
     if (!fixed_ref) {
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = xmax<32>(xmax<16>(tmax));
       mn = fmaxf(m, tmax);
       alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
     }
@@ -720,9 +714,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       const bf16 pbits = from_f<bf16>(p);
       pb[j] = *(const __bf16*)&pbits;
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
+    l = l * alpha + ps;  // this lane's keys; summed over the key groups after the loop
     m = mn;
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) {
@@ -736,6 +728,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     process(T, ka0, va0);
   }
 
+  l = xsum<32>(xsum<16>(l));  // the four key groups (g4) of head c16
   // this wave's result: head c16, dims 16*dd + 4*g4 + i
   if (c16 < G) {
 #pragma unroll
