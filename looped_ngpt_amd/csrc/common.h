@@ -111,6 +111,20 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return r;
 }
 
+// As block_sum, without the leading barrier: for a slot `sh` that no wave can
+// still be reading (a barrier has passed since its last read, as when the
+// slots of consecutive sums rotate). Same arithmetic, same result.
+template <int NT>
+__device__ __forceinline__ float block_sum_slot(float v, float* sh) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r += sh[i];
+  return r;
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / sqrtf(fmaxf(sumsq, 1e-30f)); }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   constexpr int P = NC < kProWin ? NC : kProWin;
   constexpr int NW = kProThreads / 64;
   constexpr int EPT = (CH * 512 + kProThreads - 1) / kProThreads;  // prologue elements per thread
-  __shared__ float sh[NW];
+  __shared__ float sh[3][NW];  // one slot per workgroup sum of a row: each reuse follows a barrier
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nv = K / 8;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
       if ((int)threadIdx.x + kProThreads * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
       ss += yv[c] * yv[c];
     }
-    const float iy = inv_norm(block_sum<kProThreads>(ss, sh));
+    const float iy = inv_norm(block_sum_slot<kProThreads>(ss, sh[0]));
     float st = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
       hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
       st += hv[c] * hv[c];
     }
-    const float ih = inv_norm(block_sum<kProThreads>(st, sh));
+    const float ih = inv_norm(block_sum_slot<kProThreads>(st, sh[1]));
 #pragma unroll
     for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
     if (pr.e_out && blockIdx.x == 0) {
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
         yv[c] = pr.wh * hv[c] + pr.we * ev[c];
         sv += yv[c] * yv[c];
       }
-      const float iv = inv_norm(block_sum<kProThreads>(sv, sh));
+      const float iv = inv_norm(block_sum_slot<kProThreads>(sv, sh[2]));
 #pragma unroll
       for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
     }

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
   constexpr int P = NC < kLbWin ? NC : kLbWin;
   constexpr int NW = kLbThreads / 64;
   constexpr int EPT = (CQ * F::kCodes * 64 + kLbThreads - 1) / kLbThreads;  // prologue elements per thread
-  __shared__ float sh[NW];
+  __shared__ float sh[3][NW];  // one slot per workgroup sum of a row: each reuse follows a barrier
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nq = K / F::kCodes;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
       if ((int)threadIdx.x + kLbThreads * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
       ss += yv[c] * yv[c];
     }
-    const float iy = inv_norm(block_sum<kLbThreads>(ss, sh));
+    const float iy = inv_norm(block_sum_slot<kLbThreads>(ss, sh[0]));
     float st = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
       hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
       st += hv[c] * hv[c];
     }
-    const float ih = inv_norm(block_sum<kLbThreads>(st, sh));
+    const float ih = inv_norm(block_sum_slot<kLbThreads>(st, sh[1]));
 #pragma unroll
     for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
     if (pr.e_out && blockIdx.x == 0) {
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
         yv[c] = pr.wh * hv[c] + pr.we * ev[c];
         sv += yv[c] * yv[c];
       }
-      const float iv = inv_norm(block_sum<kLbThreads>(sv, sh));
+      const float iv = inv_norm(block_sum_slot<kLbThreads>(sv, sh[2]));
 #pragma unroll
       for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
     }

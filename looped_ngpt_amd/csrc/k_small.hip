@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
     v[j] = i < d ? to_f(e[i]) : 0.f;
     ss += v[j] * v[j];
   }
-  const float inv = inv_norm(block_sum<kRowThreads>(ss, sh));
+  const float inv = inv_norm(block_sum_slot<kRowThreads>(ss, sh));  // first use of sh
   const size_t o = (size_t)r * d;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -66,7 +66,7 @@ template <typename T, int EPT>
 __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, const float* __restrict__ y,
                                                        const float* __restrict__ alpha, T* __restrict__ xb,
                                                        float* __restrict__ h2, int d, RowGate gate) {
-  __shared__ float sh[kRowThreads / 64];
+  __shared__ float sh[2][kRowThreads / 64];  // one slot per sum: no barrier before either
   if (gate.loops && gate.loop > gate.loops[blockIdx.x / gate.n]) return;  // row past its loop count
   const size_t o = (size_t)blockIdx.x * d;
   float yv[EPT], hv[EPT];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, c
     hv[j] = i < d ? h[o + i] : 0.f;
     ss += yv[j] * yv[j];
   }
-  const float iy = inv_norm(block_sum<kRowThreads>(ss, sh));
+  const float iy = inv_norm(block_sum_slot<kRowThreads>(ss, sh[0]));
   float st = 0.f;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, c
     hv[j] = hv[j] + a * (yv[j] * iy - hv[j]);
     st += hv[j] * hv[j];
   }
-  const float ih = inv_norm(block_sum<kRowThreads>(st, sh));
+  const float ih = inv_norm(block_sum_slot<kRowThreads>(st, sh[1]));
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int i = threadIdx.x + j * kRowThreads;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(float* __restrict__ h, 
     v[j] = i < d ? wh * h[o + i] + we * e[o + i] : 0.f;
     ss += v[j] * v[j];
   }
-  const float inv = inv_norm(block_sum<kRowThreads>(ss, sh));
+  const float inv = inv_norm(block_sum_slot<kRowThreads>(ss, sh));  // first use of sh
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int i = threadIdx.x + j * kRowThreads;
