@@ -188,6 +188,50 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_rows(const bf16* __restrict__ 
   }
 }
 
+// Batch 1, float32 out, long rows (the down projection, K = d_ff): the K
+// range of each output is split over two waves of CH chunks, 12 waves (6
+// outputs) per workgroup, and the two halves' wave sums are added through
+// LDS. Shorter load chains and twice the waves of k_gemv_rows: 9.6 us
+// against 10.3 us on the 36-layer shape (3072 x 8192).
+template <int CH>
+__global__ __launch_bounds__(768) void k_gemv_rows_k2(const bf16* __restrict__ x, const bf16* __restrict__ W,
+                                                     float* __restrict__ y, int N, int K, float scale) {
+  constexpr int NW = 12, NT = NW * 64, OPW = NW / 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float part[NW];
+  bf16* xs = (bf16*)smem;
+  const int nv = K / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int o = blockIdx.x * OPW + (wave >> 1), half = wave & 1;
+  const bool live = o < N;
+  const int oc = live ? o : N - 1;
+  constexpr int XV = (CH * 2 * 64 + NT - 1) / NT;
+  u32x4 xr[XV];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) xr[q] = ((const u32x4*)x)[min((int)threadIdx.x + NT * q, nv - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  u32x4 wv[CH];
+  const u32x4* wr = (const u32x4*)(W + (size_t)oc * K);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) wv[c] = __builtin_nontemporal_load(wr + min(half * CH * 64 + lane + 64 * c, nv - 1));
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + NT * q;
+    if (e < nv) ((u32x4*)xs)[e] = xr[q];
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int v = half * CH * 64 + lane + 64 * c;
+    if (v < nv) acc = dot16(wv[c], ((const u32x4*)xs)[v], (const bf16*)nullptr, acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (half == 0 && lane == 0 && live) y[o] = (part[wave] + part[wave + 1]) * scale;
+}
+
 // waves per workgroup of the rows kernels: one workgroup per CU when the
 // outputs split evenly that way (12 for 3072 outputs, 9 for 2304), else 8
 int rows_waves(int nout) {
@@ -219,6 +263,18 @@ static bool gemv_rows_launch_nw(const bf16* x, int64_t ldx, const bf16* W, void*
 template <int MB, int EPI>
 static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
                              hipStream_t st) {
+  if constexpr (MB == 1 && EPI == EPI_F32) {
+    const int ch = (K / 8 + 63) / 64;  // chunks per lane of the one-wave-per-row kernel
+    const dim3 grid((N + 5) / 6);
+    if (ch == 16) {
+      dory_launch(k_gemv_rows_k2<8>, grid, dim3(768), (uint32_t)K * 2, st, x, W, (float*)y, N, K, scale);
+      return true;
+    }
+    if (ch == 12) {
+      dory_launch(k_gemv_rows_k2<6>, grid, dim3(768), (uint32_t)K * 2, st, x, W, (float*)y, N, K, scale);
+      return true;
+    }
+  }
   switch (rows_waves(EPI == EPI_SWIGLU ? N / 2 : N)) {
     case 9: return gemv_rows_launch_nw<MB, EPI, 9>(x, ldx, W, y, M, N, K, scale, st);
     case 12: return gemv_rows_launch_nw<MB, EPI, 12>(x, ldx, W, y, M, N, K, scale, st);

@@ -28,6 +28,8 @@ CASES = [
     ("f32", 2, 2 * 683, 256, 1, 1), ("f32", 130, 683, 256, 0, 2), ("f32", 70, 2 * 683, 256, 1, 2),
     ("bf16", 1, 8192, 3072, 0, 1), ("bf16", 1, 3072, 8192, 0, 1), ("bf16", 4, 1000, 3072, 0, 1),
     ("bf16", 1, 2 * 8192, 3072, 1, 1), ("bf16", 5, 2 * 1000, 2304, 1, 1), ("bf16", 1, 3072, 2304, 0, 1),
+    # batch 1, long rows: each output's K range on two waves (8 or 6 chunks), a ragged last workgroup
+    ("bf16", 1, 2304, 6144, 0, 1), ("bf16", 1, 1001, 8192, 0, 1), ("bf16", 1, 7, 5640, 0, 1),
     ("bf16", 130, 1000, 3072, 0, 2), ("bf16", 256, 8192, 3072, 0, 2), ("bf16", 200, 2 * 1000, 3072, 1, 2),
     ("bf16", 64, 3072, 8192, 0, 2), ("bf16", 33, 2304, 2304, 0, 2), ("bf16", 97, 2 * 6144, 2304, 1, 2),
     # M >= 1024: the 256x256-tile kernel (ragged M and N tiles, both epilogues, K multiple of 32)
