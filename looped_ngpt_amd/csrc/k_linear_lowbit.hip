@@ -586,9 +586,10 @@ __global__ __launch_bounds__(kLbThreads) void k_gemv_pro_lb(GemvPro pr, const ui
   }
 }
 
-// Batch 1: the same GEMV and update on the skeleton of k_gemv_rows_lb. One
-// output per wave, 8 waves per workgroup; each thread takes the update of one
-// group of 8 consecutive elements with 16-byte loads (K <= 8 * 512). A bare
+// Batch 1: the same GEMV and update (without re-injection, e_out or clearing)
+// on the skeleton of k_gemv_rows_lb. One output per wave, 8 waves per
+// workgroup; each thread takes the update of one group of 8 consecutive
+// elements with 16-byte loads (K <= 8 * 512). A bare
 // barrier after the small loads (inputs, scale bits) queues every wave's
 // before any weight load, so the update does not wait behind the weight
 // stream. The activations of a chunk position are read from LDS once for the
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(kLb1Waves * 64) void k_gemv_pro1_lb(GemvPro pr, con
   using F = LowBit<FMT>;
   constexpr int NW = kLb1Waves, NT = NW * 64;
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
-  __shared__ float sh[3][NW];  // one slot per workgroup sum: each is used once
+  __shared__ float sh[2][NW];  // one slot per workgroup sum: each is used once
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
   const int nv = K / 8, nq = K / F::kCodes;
@@ -618,18 +619,14 @@ __global__ __launch_bounds__(kLb1Waves * 64) void k_gemv_pro1_lb(GemvPro pr, con
   const bool gv = g < nv;
   const int gc = gv ? g : nv - 1;
 
-  // inputs first (e is read from y without re-injection: no branch between loads)
-  const float* ep = pr.e ? pr.e : pr.y;
-  float4 y4[2], h4[2], e4[2], a4[2];
+  // inputs first
+  float4 y4[2], h4[2], a4[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     y4[i] = ((const float4*)pr.y)[2 * gc + i];
     h4[i] = ((const float4*)pr.h_in)[2 * gc + i];
-    e4[i] = ((const float4*)ep)[2 * gc + i];
     a4[i] = ((const float4*)pr.alpha)[2 * gc + i];
   }
-  if (pr.zero)
-    for (int i = blockIdx.x * NT + threadIdx.x; i < pr.zero_n; i += gridDim.x * NT) pr.zero[i] = 0ull;
   uint32_t sb[NR][CQ];
 #pragma unroll
   for (int j = 0; j < NR; ++j)
@@ -647,12 +644,11 @@ __global__ __launch_bounds__(kLb1Waves * 64) void k_gemv_pro1_lb(GemvPro pr, con
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  float yv[8], hv[8], ev[8], av[8];
+  float yv[8], hv[8], av[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     yv[i] = gv ? y4[i >> 2][i & 3] : 0.f;
     hv[i] = gv ? h4[i >> 2][i & 3] : 0.f;
-    ev[i] = gv ? e4[i >> 2][i & 3] : 0.f;
     av[i] = gv ? a4[i >> 2][i & 3] : 0.f;
   }
   float ss = 0.f;
@@ -668,21 +664,6 @@ __global__ __launch_bounds__(kLb1Waves * 64) void k_gemv_pro1_lb(GemvPro pr, con
   const float ih = inv_norm(block_sum_slot<NT>(st, sh[1]));
 #pragma unroll
   for (int i = 0; i < 8; ++i) hv[i] *= ih;  // u
-  if (pr.e_out && blockIdx.x == 0 && gv) {
-    ((float4*)pr.e_out)[2 * g] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-    ((float4*)pr.e_out)[2 * g + 1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
-  }
-  if (pr.e) {
-    float sv = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      yv[i] = pr.wh * hv[i] + pr.we * ev[i];
-      sv += yv[i] * yv[i];
-    }
-    const float iv = inv_norm(block_sum_slot<NT>(sv, sh[2]));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hv[i] = yv[i] * iv;
-  }
   if (gv) {
     u32x4 w;
 #pragma unroll
@@ -811,13 +792,14 @@ hipError_t linear_lb(const void* x, int64_t ldx, const void* Wq, const void* Ws,
 #undef DORY_LBM
 }
 
-// k_gemv_pro1_lb covers K <= 8 x 512 (one element group per thread) with
-// 16-byte aligned update vectors; other shapes take k_gemv_pro_lb.
+// k_gemv_pro1_lb covers the plain update (no re-injection, no e_out, nothing
+// to clear) at K <= 8 x 512 (one element group per thread) with 16-byte
+// aligned vectors; everything else takes k_gemv_pro_lb.
 bool pro1_ok(int fmt, const GemvPro& p, int K) {
   auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
   const int cq = chunks_per_lane(fmt, K);
-  return K % 8 == 0 && K / 8 <= kLb1Waves * 64 && cq >= 1 && cq <= 4 && al(p.y) && al(p.h_in) && al(p.alpha) &&
-         al(p.h_out) && (!p.e || al(p.e)) && (!p.e_out || al(p.e_out));
+  return !p.e && !p.e_out && !p.zero && K % 8 == 0 && K / 8 <= kLb1Waves * 64 && cq >= 1 && cq <= 4 && al(p.y) &&
+         al(p.h_in) && al(p.alpha) && al(p.h_out);
 }
 
 template <int FMT, int EPI>
