@@ -210,35 +210,48 @@ hipError_t launch_rope_table(float2* tab, int max_ctx, int hd, double base, hipS
 }
 
 // ---------------------------------------------------------------------------
-// RoPE + per-head L2 norm of q and k. One wave per (row, head); lane l owns
-// the rotation pair (l, l + hd/2).
+// RoPE + per-head L2 norm of q and k. One wave per (head, kRopeRows
+// consecutive rows); lane l owns the rotation pair (l, l + hd/2).
 // ---------------------------------------------------------------------------
+constexpr int kRopeRows = 4;  // rows (positions) per wave of k_rope_qk
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int head = blockIdx.x * 4 + wave;
-  const int r = blockIdx.y;
-  if (head >= a.nq + a.nkv) return;
+  if (head >= a.nq + a.nkv) return;  // wave-uniform
   const int half = a.hd / 2;
-  const int pos = a.p0 + r % a.n;
-  const float* src = a.qkvg + (size_t)r * a.ld + (size_t)head * a.hd;
-  if (lane >= half) return;
-  const float x1 = src[lane], x2 = src[lane + half];
-  const float2 cs = a.tab[(size_t)pos * half + lane];
-  const float r1 = x1 * cs.x - x2 * cs.y;
-  const float r2 = x2 * cs.x + x1 * cs.y;
-  // lanes >= half returned early; the wave sum below only sees active lanes
-  float ss = r1 * r1 + r2 * r2;
+  const int r0 = blockIdx.y * kRopeRows;
+  // every row's loads first (rows past the end and lanes past half read a
+  // clamped address and are masked below), so each lane keeps 3 x kRopeRows
+  // loads in flight
+  const int ln = min(lane, half - 1);
+  float x1[kRopeRows], x2[kRopeRows];
+  float2 cs[kRopeRows];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float other = __shfl_xor(ss, o, 64);
-    if ((lane ^ o) < half) ss += other;
+  for (int i = 0; i < kRopeRows; ++i) {
+    const int r = min(r0 + i, a.rows - 1);
+    const float* src = a.qkvg + (size_t)r * a.ld + (size_t)head * a.hd;
+    x1[i] = src[ln];
+    x2[i] = src[ln + half];
+    cs[i] = a.tab[(size_t)(a.p0 + r % a.n) * half + ln];
   }
-  const float inv = inv_norm(ss);
-  T* dst = head < a.nq ? (T*)a.q_out + ((size_t)r * a.nq + head) * a.hd
-                       : (T*)a.k_out + ((size_t)r * a.nkv + head - a.nq) * a.hd;
-  dst[lane] = from_f<T>(r1 * inv);
-  dst[lane + half] = from_f<T>(r2 * inv);
+#pragma unroll
+  for (int i = 0; i < kRopeRows; ++i) {
+    const int r = r0 + i;
+    if (r >= a.rows) break;  // wave-uniform
+    const bool on = lane < half;
+    const float r1 = on ? x1[i] * cs[i].x - x2[i] * cs[i].y : 0.f;
+    const float r2 = on ? x2[i] * cs[i].x + x1[i] * cs[i].y : 0.f;
+    // lanes past half add zeros: the same sums as a butterfly over the active lanes
+    const float inv = inv_norm(wave_sum(r1 * r1 + r2 * r2));
+    if (on) {
+      T* dst = head < a.nq ? (T*)a.q_out + ((size_t)r * a.nq + head) * a.hd
+                           : (T*)a.k_out + ((size_t)r * a.nkv + head - a.nq) * a.hd;
+      dst[lane] = from_f<T>(r1 * inv);
+      dst[lane + half] = from_f<T>(r2 * inv);
+    }
+  }
 }
 
 // The call's values transposed per kv head, [B][n_kv][hd][vld] with position
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(256) void k_v_transpose(RopeArgs a) {
 hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   if (a.hd > 128 || a.rows != a.B * a.n) return hipErrorInvalidValue;
-  const dim3 grid((a.nq + a.nkv + 3) / 4, a.rows);
+  const dim3 grid((a.nq + a.nkv + 3) / 4, (a.rows + kRopeRows - 1) / kRopeRows);
   const dim3 vgrid((a.vld + kVtPos - 1) / kVtPos, a.nkv, a.B);
   if (dtype == 0) {
     hipLaunchKernelGGL(k_rope_qk<float>, grid, dim3(256), 0, st, a);
