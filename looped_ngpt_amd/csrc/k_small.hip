@@ -446,8 +446,16 @@ hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // SwiGLU of a bfloat16 projection [M][2F] (u then v per row): a[M][F] =
-// (scale u) silu(scale v), 8 outputs per thread (16-byte loads and stores)
+// (scale u) silu(scale v), 8 outputs per thread (16-byte loads and stores).
+// silu(v) = v / (1 + e^-v) with the hardware exp2 and reciprocal (each about
+// 1 ulp; the precise expf and division had made the kernel VALU-bound): for
+// v -> -inf e^-v overflows to inf and the reciprocal to 0, for v -> +inf the
+// quotient tends to v, as it should.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_hw(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
+
 __global__ __launch_bounds__(256) void k_swiglu_rows(const bf16* __restrict__ p, int F, float scale,
                                                      bf16* __restrict__ a, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 outputs
@@ -460,8 +468,7 @@ __global__ __launch_bounds__(256) void k_swiglu_rows(const bf16* __restrict__ p,
   for (int k = 0; k < 4; ++k) {
     const float u0 = bf_lo(u[k]) * scale, u1 = bf_hi(u[k]) * scale;
     const float v0 = bf_lo(v[k]) * scale, v1 = bf_hi(v[k]) * scale;
-    o[k] = (uint32_t)from_f<bf16>(u0 * v0 / (1.f + expf(-v0))) |
-           ((uint32_t)from_f<bf16>(u1 * v1 / (1.f + expf(-v1))) << 16);
+    o[k] = (uint32_t)from_f<bf16>(u0 * silu_hw(v0)) | ((uint32_t)from_f<bf16>(u1 * silu_hw(v1)) << 16);
   }
   *(u32x4*)(a + e) = o;
 }
