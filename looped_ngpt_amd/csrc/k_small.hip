@@ -278,6 +278,53 @@ __global__ __launch_bounds__(256) void k_v_transpose(RopeArgs a) {
   }
 }
 
+// Same transpose for head sizes 64 / 128 with 16-byte reads (4 dimensions of
+// a position) and 4-position stores (one group of a dimension's run), no
+// integer division by a runtime size: the generic kernel moved 2-4 bytes per
+// instruction and divided by hd for every element.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_v_transpose4(RopeArgs a) {
+  __shared__ float tile[kVtPos][HD + 1];
+  constexpr int D4 = HD / 4, G = kVtPos / 4;
+  const int i0 = blockIdx.x * kVtPos, kvh = blockIdx.y, b = blockIdx.z;
+  const size_t col = (size_t)(a.nq + a.nkv + kvh) * HD;
+  for (int e = threadIdx.x; e < kVtPos * D4; e += 256) {
+    const int p = e / D4, d = 4 * (e % D4), i = i0 + p;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < a.n) v = *(const float4*)(a.qkvg + (size_t)(b * a.n + i) * a.ld + col + d);
+    tile[p][d] = v.x;
+    tile[p][d + 1] = v.y;
+    tile[p][d + 2] = v.z;
+    tile[p][d + 3] = v.w;
+  }
+  __syncthreads();
+  T* out = (T*)a.v_out + ((size_t)b * a.nkv + kvh) * HD * a.vld;
+  for (int e = threadIdx.x; e < HD * G; e += 256) {
+    const int d = e / G, g = e % G, i = i0 + 4 * g;
+    if (i >= a.vld) continue;  // vld % 4 == 0: a group is wholly inside or outside
+    const float v0 = tile[4 * g][d], v1 = tile[4 * g + 1][d], v2 = tile[4 * g + 2][d], v3 = tile[4 * g + 3][d];
+    if constexpr (sizeof(T) == 2) {
+      *(uint2*)(out + (size_t)d * a.vld + i) =
+          make_uint2((uint32_t)from_f<bf16>(v0) | ((uint32_t)from_f<bf16>(v1) << 16),
+                     (uint32_t)from_f<bf16>(v2) | ((uint32_t)from_f<bf16>(v3) << 16));
+    } else {
+      *(float4*)(out + (size_t)d * a.vld + i) = make_float4(v0, v1, v2, v3);
+    }
+  }
+}
+
+template <typename T>
+static void launch_v_transpose(const RopeArgs& a, dim3 vgrid, hipStream_t st) {
+  const bool vec = a.ld % 4 == 0 && a.vld % 4 == 0 && ((uintptr_t)a.qkvg & 15) == 0 &&
+                   ((uintptr_t)a.v_out & (sizeof(T) == 2 ? 7 : 15)) == 0;
+  if (vec && a.hd == 128)
+    hipLaunchKernelGGL((k_v_transpose4<T, 128>), vgrid, dim3(256), 0, st, a);
+  else if (vec && a.hd == 64)
+    hipLaunchKernelGGL((k_v_transpose4<T, 64>), vgrid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_v_transpose<T>, vgrid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   if (a.hd > 128 || a.rows != a.B * a.n) return hipErrorInvalidValue;
@@ -285,10 +332,10 @@ hipError_t launch_rope_qk(int dtype, const RopeArgs& a, hipStream_t st) {
   const dim3 vgrid((a.vld + kVtPos - 1) / kVtPos, a.nkv, a.B);
   if (dtype == 0) {
     hipLaunchKernelGGL(k_rope_qk<float>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_v_transpose<float>, vgrid, dim3(256), 0, st, a);
+    launch_v_transpose<float>(a, vgrid, st);
   } else {
     hipLaunchKernelGGL(k_rope_qk<bf16>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_v_transpose<bf16>, vgrid, dim3(256), 0, st, a);
+    launch_v_transpose<bf16>(a, vgrid, st);
   }
   return hipGetLastError();
 }
