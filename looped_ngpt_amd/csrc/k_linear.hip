@@ -286,7 +286,8 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
 // k_gemv_rows with the residual update in the prologue (see launch_linear_pro).
 // 1024-thread workgroups (16 waves) with kProOut outputs per wave: the
 // 36-layer shape's q|k|v|gate and up/gate projections become 256 workgroups,
-// one per CU, all resident at once, and the prologue runs once per CU. Each
+// one per CU, all resident at once, and the prologue runs once per CU (the
+// 72-layer shape's 6144 outputs take 12-wave workgroups for the same count). Each
 // wave streams the chunks of its rows through a rolling window of kProWin
 // 16-byte loads per lane: a CU keeps ~16 x kProWin KB in flight (enough to
 // cover HBM latency at its share of the bandwidth) with few registers.
@@ -294,15 +295,15 @@ constexpr int kProThreads = 1024;
 constexpr int kProOut = 2;  // outputs per wave
 constexpr int kProWin = 8;  // chunk loads in flight per wave
 
-template <int MB, int CH, int EPI>
-__global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W,
+template <int MB, int CH, int EPI, int NTH = kProThreads>
+__global__ __launch_bounds__(NTH) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W,
                                                       void* __restrict__ y, int M, int N, int K, float scale) {
   constexpr int R = kProOut;
   constexpr int NR = (EPI == EPI_SWIGLU ? 2 : 1) * R;  // weight rows per wave
   constexpr int NC = NR * CH;                          // chunk loads per wave
   constexpr int P = NC < kProWin ? NC : kProWin;
-  constexpr int NW = kProThreads / 64;
-  constexpr int EPT = (CH * 512 + kProThreads - 1) / kProThreads;  // prologue elements per thread
+  constexpr int NW = NTH / 64;
+  constexpr int EPT = (CH * 512 + NTH - 1) / NTH;  // prologue elements per thread
   __shared__ float sh[3][NW];  // one slot per workgroup sum of a row: each reuse follows a barrier
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* xs = (bf16*)smem;
@@ -326,20 +327,20 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
   };
 
   // prologue inputs of row 0 first (vector loads complete in issue order),
-  // then the first P weight chunks; element i = threadIdx.x + kProThreads*c.
+  // then the first P weight chunks; element i = threadIdx.x + NTH*c.
   // e is read from y when there is no re-injection so no branch separates loads.
   const float* ep = pr.e ? pr.e : pr.y;
   float yv[EPT], hv[EPT], ev[EPT], av[EPT];
 #pragma unroll
   for (int c = 0; c < EPT; ++c) {
-    const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
+    const int i = min((int)threadIdx.x + NTH * c, K - 1);
     yv[c] = pr.y[i];
     hv[c] = pr.h_in[i];
     ev[c] = ep[i];
     av[c] = pr.alpha[i];  // before the weights: the update must not wait behind them
   }
   if (pr.zero)
-    for (int i = blockIdx.x * kProThreads + threadIdx.x; i < pr.zero_n; i += gridDim.x * kProThreads) pr.zero[i] = 0ull;
+    for (int i = blockIdx.x * NTH + threadIdx.x; i < pr.zero_n; i += gridDim.x * NTH) pr.zero[i] = 0ull;
   __builtin_amdgcn_sched_barrier(0);
   u32x4 buf[P];
 #pragma unroll
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
     if (m > 0) {
 #pragma unroll
       for (int c = 0; c < EPT; ++c) {
-        const int i = min((int)threadIdx.x + kProThreads * c, K - 1);
+        const int i = min((int)threadIdx.x + NTH * c, K - 1);
         yv[c] = pr.y[ro + i];
         hv[c] = pr.h_in[ro + i];
         ev[c] = ep[ro + i];
@@ -363,24 +364,24 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      if ((int)threadIdx.x + kProThreads * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
+      if ((int)threadIdx.x + NTH * c >= K) yv[c] = 0.f, hv[c] = 0.f, ev[c] = 0.f;
       ss += yv[c] * yv[c];
     }
-    const float iy = inv_norm(block_sum_slot<kProThreads>(ss, sh[0]));
+    const float iy = inv_norm(block_sum_slot<NTH>(ss, sh[0]));
     float st = 0.f;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      const float al = (int)threadIdx.x + kProThreads * c < K ? av[c] : 0.f;
+      const float al = (int)threadIdx.x + NTH * c < K ? av[c] : 0.f;
       hv[c] = hv[c] + al * (yv[c] * iy - hv[c]);
       st += hv[c] * hv[c];
     }
-    const float ih = inv_norm(block_sum_slot<kProThreads>(st, sh[1]));
+    const float ih = inv_norm(block_sum_slot<NTH>(st, sh[1]));
 #pragma unroll
     for (int c = 0; c < EPT; ++c) hv[c] *= ih;  // u
     if (pr.e_out && blockIdx.x == 0) {
 #pragma unroll
       for (int c = 0; c < EPT; ++c) {
-        const int i = threadIdx.x + kProThreads * c;
+        const int i = threadIdx.x + NTH * c;
         if (i < K) pr.e_out[ro + i] = hv[c];
       }
     }
@@ -391,13 +392,13 @@ __global__ __launch_bounds__(kProThreads) void k_gemv_pro(GemvPro pr, const bf16
         yv[c] = pr.wh * hv[c] + pr.we * ev[c];
         sv += yv[c] * yv[c];
       }
-      const float iv = inv_norm(block_sum_slot<kProThreads>(sv, sh[2]));
+      const float iv = inv_norm(block_sum_slot<NTH>(sv, sh[2]));
 #pragma unroll
       for (int c = 0; c < EPT; ++c) hv[c] = yv[c] * iv;
     }
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-      const int i = threadIdx.x + kProThreads * c;
+      const int i = threadIdx.x + NTH * c;
       if (i < K) {
         xs[ro + i] = from_f<bf16>(hv[c]);
         if (blockIdx.x == 0) pr.h_out[ro + i] = hv[c];
@@ -455,9 +456,24 @@ static hipError_t gemv_pro_launch(const GemvPro& p, const bf16* W, void* y, int 
                                   hipStream_t st) {
   const int ch = (K / 8 + 63) / 64;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const size_t lds = (size_t)M * K * 2;
+  // batch 1, 12 x 2 outputs per CU: 12-wave workgroups keep one per CU (16
+  // waves would leave a quarter of the CUs idle)
+  if (MB == 1 && nout == 12 * kProOut * kNumCUs && ch <= 8) {
+    const dim3 grid12(kNumCUs);
+#define DORY_PRO12(C)                                                                                          \
+  case C:                                                                                                      \
+    dory_launch((k_gemv_pro<MB, C, EPI, 768>), grid12, dim3(768), lds, st, p, W, y, M, N, K, scale); \
+    return hipGetLastError();
+    switch (ch) {
+      DORY_PRO12(1) DORY_PRO12(2) DORY_PRO12(3) DORY_PRO12(4) DORY_PRO12(5) DORY_PRO12(6) DORY_PRO12(7)
+      DORY_PRO12(8)
+      default: break;
+    }
+#undef DORY_PRO12
+  }
   const int per_block = kProThreads / 64 * kProOut;
   const dim3 grid((nout + per_block - 1) / per_block);
-  const size_t lds = (size_t)M * K * 2;
 #define DORY_PRO(C) \
   case C: dory_launch((k_gemv_pro<MB, C, EPI>), grid, dim3(kProThreads), lds, st, p, W, y, M, N, K, scale); break;
   switch (ch) {
