@@ -65,7 +65,7 @@ def decode_bytes(m, k, ctx_mean, B=1, fmt="bf16"):
 UG_TRAFFIC = {"fetch_kib": 49348.5, "fetch_factor": 2.0, "write_kib": 28.0, "write_factor": 1.0,
               "sources": ("looped_ngpt_amd/csrc/k_linear.hip", "looped_ngpt_amd/csrc/common.h",
                           "looped_ngpt_amd/csrc/linear_common.h"),
-              "sha256_16": "46e5aa5c9c1c4fc6"}
+              "sha256_16": "cc311759ebf37616"}
 
 
 def ug_traffic():
