@@ -419,6 +419,53 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_rows_lb(const bf16* __restrict
   }
 }
 
+// Batch 1, float32 out, long rows (the down projection): each output's K
+// range on two waves of CQ chunks, 12 waves (6 outputs) per workgroup, the
+// halves' wave sums added through LDS (as k_gemv_rows_k2 of k_linear.hip).
+template <int FMT, int CQ>
+__global__ __launch_bounds__(768) void k_gemv_rows_lb_k2(const bf16* __restrict__ x, const uint8_t* __restrict__ Wq,
+                                                        const uint8_t* __restrict__ Ws, float* __restrict__ y, int N,
+                                                        int K, float scale) {
+  using F = LowBit<FMT>;
+  constexpr int NW = 12, NT = NW * 64, OPW = NW / 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float part[NW];
+  bf16* xs = (bf16*)smem;
+  const int nv = K / 8, nq = K / F::kCodes;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int o = blockIdx.x * OPW + (wave >> 1), half = wave & 1;
+  const bool live = o < N;
+  const int oc = live ? o : N - 1;
+  constexpr int XV = (2 * CQ * F::kCodes * 8 + NT - 1) / NT;  // 8-element groups over the whole row
+  u32x4 xr[XV];
+#pragma unroll
+  for (int q = 0; q < XV; ++q) xr[q] = ((const u32x4*)x)[min((int)threadIdx.x + NT * q, nv - 1)];
+  uint32_t sb[CQ];
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) sb[c] = F::scale_bits(Ws, oc, K, min(half * CQ * 64 + lane + 64 * c, nq - 1));
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  u32x4 wv[CQ];
+  const u32x4* wr = (const u32x4*)(Wq + (size_t)oc * F::row_bytes(K));
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) wv[c] = __builtin_nontemporal_load(wr + min(half * CQ * 64 + lane + 64 * c, nq - 1));
+#pragma unroll
+  for (int q = 0; q < XV; ++q) {
+    const int e = threadIdx.x + NT * q;
+    if (e < nv) ((u32x4*)xs)[e] = xr[q];
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) {
+    const int v = half * CQ * 64 + lane + 64 * c;
+    if (v < nq) acc = F::dot(wv[c], (const u32x4*)xs, v, sb[c], acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (half == 0 && lane == 0 && live) y[o] = (part[wave] + part[wave + 1]) * scale;
+}
+
 // The GEMV with the nGPT update (and optional loop re-injection) in its
 // prologue, as k_gemv_pro of k_linear.hip: 1024-thread workgroups, two
 // outputs per wave, a rolling window of 8 weight chunks per lane.
@@ -780,6 +827,19 @@ hipError_t linear_lb(const void* x, int64_t ldx, const void* Wq, const void* Ws,
   const bf16* xb = (const bf16*)x;
   const uint8_t* q = (const uint8_t*)Wq;
   const uint8_t* s = (const uint8_t*)Ws;
+  // batch 1, long rows (8 or 4 chunks per lane on one wave): two waves per row
+  if (M == 1 && epi == EPI_F32 && (uintptr_t)xb % 16 == 0) {
+    const int cq = chunks_per_lane(FMT, K);
+    const dim3 grid((N + 5) / 6);
+    if (cq == 8) {
+      dory_launch((k_gemv_rows_lb_k2<FMT, 4>), grid, dim3(768), (uint32_t)K * 2, st, xb, q, s, (float*)y, N, K, scale);
+      return hipGetLastError();
+    }
+    if (cq == 4 && K / LowBit<FMT>::kCodes > 192) {
+      dory_launch((k_gemv_rows_lb_k2<FMT, 2>), grid, dim3(768), (uint32_t)K * 2, st, xb, q, s, (float*)y, N, K, scale);
+      return hipGetLastError();
+    }
+  }
 #define DORY_LBM(E)                                                                         \
   if (M == 1) return rows_lb_launch<FMT, 1, E>(xb, ldx, q, s, y, M, N, K, scale, st);       \
   if (M == 2) return rows_lb_launch<FMT, 2, E>(xb, ldx, q, s, y, M, N, K, scale, st);       \
