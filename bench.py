@@ -307,7 +307,7 @@ def run_other(args, dev):
                 sess.set_kernel_timing(None)
                 ug_ms = tot / max(cnt, 1)
                 ach = ug_bytes(model, fmt=fmt) / (ug_ms / 1e3)
-                kname = ("k_gemv_pro_lb<MXFP8,1,3,SwiGLU>" if fmt == "mxfp8" else "k_gemv_pro_lb<NVFP4,1,2,SwiGLU>")
+                kname = ("k_gemv_pro_lb<MXFP8,1,3,SwiGLU>" if fmt == "mxfp8" else "k_gemv_pro1_lb<NVFP4,2,SwiGLU>")
                 roof = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK, 4), "traffic": None,
                         "kernel": f"{kname} ({fmt.upper()} up/gate projection with the nGPT update prologue, "
