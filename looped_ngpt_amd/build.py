@@ -43,11 +43,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def _stale(src: str) -> bool:
+    """The object is missing or older than its source or any header."""
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    heads += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    return any(os.path.getmtime(f) > t for f in [src, *heads])
+
+
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compiles every source (incremental: only those whose object is stale)
+    and links libdory.so."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    todo = [s for s in srcs if _stale(s)] if incremental else srcs
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
            "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
@@ -65,4 +80,4 @@ def clean() -> None:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="-i" in sys.argv[1:])

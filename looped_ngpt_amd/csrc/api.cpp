@@ -299,6 +299,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv,
   da.wloops = (c->mixed && P.recurrent(l)) ? wsp<int>(c, W.rowk) : nullptr;
   da.loop = loop;
   da.acc = to_acc ? wsp<unsigned long long>(c, W.attn_acc) : nullptr;
+  da.acc_nb = attn_acc_bins(P.attn_scale);
   da.gate_off = P.q_dim + 2 * P.kv_dim;
   da.gate = C.attn_gate;
   {
@@ -319,6 +320,7 @@ bool attn_to_acc_ok(const dory_ctx* c, int l, int B) {
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
   if (C.dtype != DORY_BF16 || B > 8 || C.head_dim % 8) return false;
+  if (attn_acc_bins(P.attn_scale) == 0) return false;  // scale too large for the fixed-point bins
   if (!attn_decode_uses_mfma(C.dtype, C.head_dim, P.slots(l), C.window, P.is_full[l])) return false;
   return C.weight_format == DORY_WEIGHTS_DTYPE ? linear_attn_supported(B, P.q_dim)
                                                : linear_lowbit_supported(C.weight_format, B, P.q_dim);
@@ -328,7 +330,7 @@ bool attn_to_acc_ok(const dory_ctx* c, int l, int B) {
 dory_status proj_attn_o(dory_ctx* c, int l, int B, float* y) {
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
-  AttnX ax{wsp<unsigned long long>(c, P.ws.attn_acc), C.head_dim, C.n_q_heads};
+  AttnX ax{wsp<unsigned long long>(c, P.ws.attn_acc), C.head_dim, C.n_q_heads, attn_acc_bins(P.attn_scale)};
   if (C.weight_format == DORY_WEIGHTS_DTYPE)
     HIP_TRY(c, launch_linear_attn(ax, c->o[l], y, B, C.d_model, P.q_dim, 1.f, c->st));
   else
@@ -370,7 +372,7 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
   bool any_acc = false;
   for (int l = 0; l < P.n_layers; ++l) any_acc = any_acc || attn_to_acc_ok(c, l, B);
   unsigned long long* acc = wsp<unsigned long long>(c, W.attn_acc);
-  const int acc_n = B * C.n_q_heads * (C.head_dim + kAttnAccPad);
+  const int acc_n = B * C.n_q_heads * attn_acc_stride(C.head_dim, attn_acc_bins(P.attn_scale));
   if (any_acc) HIP_TRY(c, launch_zero_u64(acc, acc_n, st));
   const float* pending_alpha = nullptr;  // MLP update not yet applied to the residual
   auto app = [&](int l, int j, bool write_kv) -> dory_status {

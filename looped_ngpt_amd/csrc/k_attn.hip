@@ -10,6 +10,8 @@
 // call) come from the call's own K/V rows, earlier ones from the cache (ring
 // slot pos mod W for sliding layers). k_attn_combine merges the partials with
 // a log-sum-exp, applies the gate and stores the gated output.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -743,25 +745,33 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   __syncthreads();
   if (a.acc) {
     // sums referenced to the largest possible score sl2 (unit q and k), the
-    // value sums gated (linear in the sums), then 2^36 fixed point; integer
-    // adds are order-independent
+    // value sums gated (linear in the sums), then fixed point in the bin that
+    // this workgroup's sum p of the head selects; integer adds are
+    // order-independent
+    const int stride = attn_acc_stride(HD, a.acc_nb);
 #pragma unroll
     for (int it = 0; it < NE; ++it) {
       const int e = tid + 256 * it;
       if (e >= G * (HD + 1)) break;
       const int g = e / (HD + 1), d = e % (HD + 1);
       const int hq = kvh * G + g;
-      float S = 0.f;
+      float S = 0.f, L = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if (wm[w][g] == -INFINITY) continue;
         const float f = exp2f(wm[w][g] - sl2);
         S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], f, S);
+        L = fmaf(wl[w][g], f, L);  // the same for every d of head g: one bin per (workgroup, head)
       }
       if (d < HD && a.gate) S *= sigmoidf_(gx[it]);
-      if (S != 0.f)
-        atomicAdd(a.acc + ((size_t)b * a.nq + hq) * (HD + kAttnAccPad) + d,
-                  (unsigned long long)llrint((double)S * 68719476736.0));
+      if (S == 0.f) continue;
+      // L in [2^ex, 2^(ex+1)) (normal: L >= 2^(-2 sl2) > 2^-126); bin b keeps
+      // L 2^(16b) in [2^-15, 2)
+      const int ex = (int)((__float_as_uint(L) >> 23) & 0xff) - 127;
+      const int bin = ex < 0 ? min(-ex / kAttnAccBinBits, a.acc_nb - 1) : 0;
+      unsigned long long* ap = a.acc + ((size_t)b * a.nq + hq) * stride;
+      atomicAdd(d < HD ? ap + bin * HD + d : ap + a.acc_nb * HD + bin,
+                (unsigned long long)llrint(ldexp((double)S, 36 + kAttnAccBinBits * bin)));
     }
     return;
   }
@@ -882,10 +892,19 @@ bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full
   return dtype == 1 && (hd == 64 || hd == 128) && slots % 8 == 0 && slots >= 8 && (is_full || window % 8 == 0);
 }
 
+int attn_acc_bins(float scale) {
+  const double sl2 = (double)scale * 1.4426950408889634;
+  if (!(sl2 > 0.0)) return 0;
+  const double nb = std::floor(2.0 * sl2 / kAttnAccBinBits) + 1.0;  // -log2(sum p) <= 2 sl2 < 16 nb
+  return nb <= kAttnAccBinsMax ? (int)nb : 0;
+}
+
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
   const bool mfma = attn_decode_uses_mfma(dtype, a.hd, a.slots, a.window, a.is_full);
-  if (a.acc && !mfma) return hipErrorInvalidValue;  // accumulators only from the matrix-core kernel
+  // accumulators only from the matrix-core kernel, with enough bins for the scale
+  if (a.acc && (!mfma || a.acc_nb < attn_acc_bins(a.scale) || a.acc_nb < 1 || a.acc_nb > kAttnAccBinsMax))
+    return hipErrorInvalidValue;
   if (mfma)
     return a.hd == 64 ? attn_dec_mfma<64>(a, st) : attn_dec_mfma<128>(a, st);
   if (dtype == 0) {

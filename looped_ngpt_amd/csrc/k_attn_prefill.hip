@@ -2,7 +2,8 @@
 // dim 64 or 128): softmax(scale * q.k) v over the allowed keys of a sliding
 // window (t - W < s <= t) or full (s <= t) layer, grouped-query heads, then
 // the sigmoid output gate — the attention sublayer of the nGPT block
-// ("Dory1.0-4B" model summary, Architecture; the nGPT paper, Section 2.3).
+// ("Dory1.0-4B: A Looped Normalized-GPT", ai.info AI summary, Methodology in
+// Plain English).
 //
 // One workgroup takes 128 consecutive query positions of one query head; its
 // four waves own 32 positions each. Keys are visited in tiles of 64 positions

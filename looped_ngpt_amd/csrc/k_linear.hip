@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_rows(const bf16* __restrict__ 
 #pragma unroll
   for (int q = 0; q < XV; ++q) {
     const int e = threadIdx.x + NT * q;
-    if (XM) xr[q] = attn_x_make(xa[XM ? q : 0]);
+    if (XM) xr[q] = attn_x_make(ax, xa[XM ? q : 0]);
     if (e / nv < M) ((u32x4*)xs)[e] = xr[q];
   }
   __syncthreads();

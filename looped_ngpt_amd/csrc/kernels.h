@@ -117,16 +117,30 @@ struct AttnDecArgs {
   float* part;
   const int* wloops; int loop;
   // optional (matrix-core kernel): instead of per-split partials, add the
-  // split's sums, referenced to the largest possible score (q and k are unit
-  // vectors, so a score never exceeds `scale`), as 2^36 fixed point with
-  // 64-bit integer atomics (order-independent, hence deterministic) into
-  // acc [B][nq][hd + 8]: sum p v times the sigmoid gate (read at gate_off of
-  // the projection row; gate 1 elementwise, 2 per head, 0 none), then sum p
-  // (7 words of padding keep rows 16-byte aligned). acc must start at zero.
+  // split's sums as fixed point with 64-bit integer atomics (order-
+  // independent, hence deterministic) into acc. The sums are referenced to
+  // the largest possible score (q and k are unit vectors, so a score never
+  // exceeds `scale`); a workgroup whose sum p lies in [2^(-16(b+1)),
+  // 2^(-16b)) takes bin b (b < acc_nb; b = 0 from 2^-16 up), where one unit
+  // is 2^-(36 + 16b), so its largest term keeps at least 21 bits however far
+  // below the bound every score lies. Layout per (row, q head):
+  // acc_nb x hd words of sum p v times the sigmoid gate (read at gate_off of
+  // the projection row; gate 1 elementwise, 2 per head, 0 none), bin-major,
+  // then 8 words whose first acc_nb hold sum p per bin (the rest stay zero).
+  // acc must start at zero.
   unsigned long long* acc;
+  int acc_nb;
   int gate_off, gate;
 };
-constexpr int kAttnAccPad = 8;  // words per (row, head) beyond hd
+constexpr int kAttnAccPad = 8;       // words per (row, head) beyond the bins' value words
+constexpr int kAttnAccBinsMax = 4;   // sum-p words fit in the pad; covers scale log2(e) < 32
+constexpr int kAttnAccBinBits = 16;  // binary orders of magnitude per bin
+// words per (row, q head) of the accumulators
+__host__ __device__ inline int attn_acc_stride(int hd, int nb) { return nb * hd + kAttnAccPad; }
+// bins the accumulators need for the softmax scale `scale` (every sum p of a
+// workgroup is >= its largest term >= 2^(-2 scale log2 e)); 0 when more than
+// kAttnAccBinsMax would be needed (the float split + merge path then runs)
+int attn_acc_bins(float scale);
 hipError_t launch_attn_decode(int dtype, const AttnDecArgs& a, hipStream_t st);
 // True when launch_attn_decode takes the matrix-core kernel, which splits the
 // keys in tiles of 32 positions (bfloat16, slots and window multiples of 4).
@@ -151,7 +165,7 @@ int rows_waves(int nout);
 
 struct AttnX {
   const unsigned long long* acc;
-  int hd; int nq;
+  int hd; int nq; int nb;  // accumulators as AttnDecArgs::acc with acc_nb = nb
 };
 hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t st);
 // a[M][F] = (scale u) silu(scale v) from a bfloat16 projection [M][2F] (u | v per row); F % 8 == 0

@@ -141,7 +141,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.pos = take(4);
   w.rowk = take((size_t)c.max_batch * 4);
   w.blas = take(kBlasWsBytes);
-  w.attn_acc = take((size_t)std::min(c.max_batch, 8) * c.n_q_heads * (c.head_dim + kAttnAccPad) * 8);
+  w.attn_acc = take((size_t)std::min(c.max_batch, 8) * c.n_q_heads * attn_acc_stride(c.head_dim, kAttnAccBinsMax) * 8);
   if (c.weight_format != DORY_WEIGHTS_DTYPE) {  // one projection expanded to bfloat16 for prefill GEMMs
     const size_t d = c.d_model;
     size_t big = (size_t)p.qkvg_dim * d;

@@ -2,10 +2,12 @@
 (dory_backward_last_loop) against the float64 oracle (oracle/backward.py):
 every gradient of every recurrent layer and the gradient of the input.
 
-float32 models: max |difference| <= 2e-4 of the tensor's largest entry (float32
-arithmetic against float64). bfloat16 models: the projections take bfloat16
-operands (activations and gradients rounded once per GEMM), so the bar is
-norm-wise: |g - g_ref| / |g_ref| <= 3e-2 (Frobenius) for every tensor."""
+Every tensor is compared element by element: max |g - g_ref| <= bar x
+max |g_ref|. float32 models: bar 2e-4 (float32 arithmetic against float64).
+bfloat16 models: bar 3e-2 — the products take bfloat16 operands (activations
+and gradients rounded once per GEMM, about 2^-9 relative each, a few such
+roundings on every path) against the oracle's exact float64; the relative
+Frobenius error is printed beside it."""
 import numpy as np
 import pytest
 
@@ -53,24 +55,24 @@ def _run(cfg, w, x, G):
     return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
 
 
-def _compare(cfg, got, ref, x_shape, bar, normwise):
-    worst = 0.0
+def _compare(cfg, got, ref, x_shape, bar):
+    worst, worst_fro = 0.0, 0.0
     for l in range(cfg.n_in, cfg.n_in + cfg.n_rec):
         for p in ("qkvg", "o", "ug", "down", "alpha_a", "alpha_m"):
             key = f"L{l}.{p}"
             assert got[key].shape == ref[key].shape, key
-            worst = max(worst, _err(key, got[key], ref[key], bar, normwise))
-    worst = max(worst, _err("x", got["x"].reshape(x_shape), ref["x"], bar, normwise))
-    print(f"{cfg.name}: worst {'relative Frobenius' if normwise else 'max/|max|'} error {worst:.3e}", flush=True)
+            e, f = _err(key, got[key], ref[key], bar)
+            worst, worst_fro = max(worst, e), max(worst_fro, f)
+    e, f = _err("x", got["x"].reshape(x_shape), ref["x"], bar)
+    worst, worst_fro = max(worst, e), max(worst_fro, f)
+    print(f"{cfg.name}: worst max|diff|/max|ref| {worst:.3e} (relative Frobenius {worst_fro:.3e})", flush=True)
 
 
-def _err(key, g, r, bar, normwise):
-    if normwise:
-        e = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
-    else:
-        e = np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30)
-    assert e <= bar, f"{key}: error {e:.3e} > {bar}"
-    return e
+def _err(key, g, r, bar):
+    e = np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30)
+    f = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    assert e <= bar, f"{key}: element error {e:.3e} of the largest entry > {bar}"
+    return e, f
 
 
 @pytest.mark.parametrize("gate", [0, 1, 2])
@@ -80,7 +82,7 @@ def test_backward_f32_small(gate):
     x, G = _inputs(cfg, 2, 24, 80 + gate)
     ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
     got = _run(cfg, w, x, G)
-    _compare(cfg, got, ref, x.shape, 2e-4, normwise=False)
+    _compare(cfg, got, ref, x.shape, 2e-4)
 
 
 @pytest.mark.parametrize("n", [40, 23])
@@ -91,7 +93,7 @@ def test_backward_bf16_small(n):
     x, G = _inputs(cfg, 2, n, 91)
     ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
     got = _run(cfg, w, x, G)
-    _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
+    _compare(cfg, got, ref, x.shape, 3e-2)
 
 
 def test_backward_bf16_36layer_widths():
@@ -104,7 +106,7 @@ def test_backward_bf16_36layer_widths():
     x, G = _inputs(cfg, 1, 300, 93)
     ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
     got = _run(cfg, w, x, G)
-    _compare(cfg, got, ref, x.shape, 3e-2, normwise=True)
+    _compare(cfg, got, ref, x.shape, 3e-2)
 
 
 def test_backward_argument_errors():
