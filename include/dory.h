@@ -334,6 +334,19 @@ dory_status dory_op_linear_fp4(const void* x, int64_t ldx, const void* codes, co
 dory_status dory_op_argmax(const float* logits, int32_t B, int32_t V, int32_t* out,
                            void* scratch_dev, void* stream);
 
+/* dory_op_argmax for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and result, with the partials in a 64 KiB device array
+ * that the library holds, one copy per GPU, kept until the process ends. The
+ * caller passes only the logits (device float32 [B, V]) and out (device
+ * int32 [B]). Limit: B * ceil(V / 1024) <= 8192 (batch 64 at vocabulary
+ * 131,072), else DORY_E_CAPACITY and nothing is enqueued; DORY_E_ARG for a
+ * NULL pointer or B, V < 1; DORY_E_HIP if the array's address cannot be
+ * found on the current device. Calls no allocator. Every call on one GPU
+ * uses that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+dory_status dory_op_argmax_noalloc(const float* logits, int32_t B, int32_t V, int32_t* out, void* stream);
+
 /* ---- depth-1 truncated backward of the last recurrent invocation -------- */
 
 /* The pages train the looped stage with backpropagation truncated to depth

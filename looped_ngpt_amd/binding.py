@@ -39,7 +39,7 @@ EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dor
            "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
-           "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_backward_workspace_bytes", "dory_backward_workspace_min_bytes",
+           "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_op_argmax_noalloc", "dory_backward_workspace_bytes", "dory_backward_workspace_min_bytes",
            "dory_backward_last_loop"]
 
 
@@ -103,6 +103,7 @@ _sig = {
     "dory_op_linear": (_I, [_I, _P, ctypes.c_int64, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
     "dory_argmax_scratch_bytes": (ctypes.c_size_t, [_I, _I]),
     "dory_op_argmax": (_I, [_P, _I, _I, _P, _P, _P]),
+    "dory_op_argmax_noalloc": (_I, [_P, _I, _I, _P, _P]),
     "dory_backward_workspace_bytes": (ctypes.c_size_t, [_C, _I, _I]),
     "dory_backward_workspace_min_bytes": (ctypes.c_size_t, [_C, _I, _I]),
     "dory_backward_last_loop": (_I, [_P, _P, _P, _I, _I, ctypes.POINTER(DoryGrads), _P, _P, ctypes.c_size_t]),
@@ -451,6 +452,14 @@ def op_argmax(logits, out, scratch, stream=None) -> None:
     s = _lib.dory_op_argmax(_ptr(logits), B, V, _ptr(out), _ptr(scratch), _stream_handle(stream))
     if s != DORY_OK:
         raise DoryError(s, "dory_op_argmax")
+
+
+def op_argmax_noalloc(logits, out, stream=None) -> None:
+    """op_argmax with the library's own partials (no scratch argument)."""
+    B, V = logits.shape
+    s = _lib.dory_op_argmax_noalloc(_ptr(logits), B, V, _ptr(out), _stream_handle(stream))
+    if s != DORY_OK:
+        raise DoryError(s, "dory_op_argmax_noalloc")
 
 
 def argmax_scratch_bytes(B: int, V: int) -> int:

@@ -6,8 +6,10 @@
 // thread holding EPT elements in registers, so a row is read from memory once
 // and the two L2 norms are workgroup reductions.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
+#include "dory.h"
 #include "kernels.h"
 
 namespace dory {
@@ -476,6 +478,53 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* 
   hipLaunchKernelGGL(k_argmax_final, dim3(B), dim3(256), 0, st, (const float2*)scratch, nblk, out, pos_dev);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// argmax with library-held partials (dory_op_argmax_noalloc): for callers
+// that cannot allocate. The partials live in a fixed device array, one copy
+// per GPU; its address on a device is looked up once, with that device
+// current, and kept. Pass 1 writes every partial pass 2 reads, so nothing
+// needs clearing between calls; calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float2 scratch[kArgmaxNoAllocPartials];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float2* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t argmax_noalloc_scratch(float2** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float2*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace dory
+
+extern "C" dory_status dory_op_argmax_noalloc(const float* logits, int32_t B, int32_t V, int32_t* out,
+                                              void* stream) {
+  if (!logits || !out || B < 1 || V < 1) return DORY_E_ARG;
+  const int64_t nblk = ((int64_t)V + dory::kArgBlock - 1) / dory::kArgBlock;
+  if ((int64_t)B * nblk > dory::kArgmaxNoAllocPartials) return DORY_E_CAPACITY;
+  float2* part = nullptr;
+  if (dory::argmax_noalloc_scratch(&part) != hipSuccess) return DORY_E_HIP;
+  const hipError_t e = dory::launch_argmax(logits, B, V, out, part, (hipStream_t)stream);
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
+namespace dory {
 
 // ---------------------------------------------------------------------------
 // clearing of 64-bit words (a kernel, so that recorded graphs hold no memset)

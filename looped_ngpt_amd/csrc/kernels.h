@@ -217,6 +217,9 @@ hipError_t launch_linear_pro_lowbit(int fmt, const GemvPro& p, const void* Wq, c
                                     int K, int epi, float scale, hipStream_t st);
 bool linear_pro_lowbit_supported(int fmt, int M, int K);
 
+// partials (float2) held by the library for dory_op_argmax_noalloc: 64 KiB
+// per GPU, batch x ceil(V / 1024) <= 8192 (batch 64 at a 131,072 vocabulary)
+constexpr int kArgmaxNoAllocPartials = 8192;
 // Greedy argmax; if pos_dev is not NULL the final pass also advances the
 // device position counter by one (the end of a decode step).
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, void* scratch, hipStream_t st,
