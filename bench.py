@@ -564,8 +564,8 @@ def main():
                     continue
                 if kind == "ug":
                     fl = 2.0 * n * 2 * model.d_ff * model.d_model * cnt
-                    name = ("up/gate projection + SwiGLU (M=%d, N=%d, K=%d; hipBLASLt GEMM to bfloat16, then the "
-                            "activation kernel)" % (n, 2 * model.d_ff, model.d_model))
+                    name = ("k_gemm_big up/gate projection with the SwiGLU epilogue (M=%d, N=%d, K=%d)"
+                            % (n, 2 * model.d_ff, model.d_model))
                 else:
                     fl = float(attn_flops(model, k, n))
                     name = "attention (flash, causal + window %d)" % model.window

@@ -161,8 +161,8 @@ dory_status dory_validate_config(const dory_config* cfg);
 size_t dory_kv_bytes(const dory_config* cfg, int32_t kv_mode, int32_t kv_loops);
 
 /* Bytes of the workspace dory_create needs (activations for max_batch *
- * max_chunk rows, attention partials and sums, RoPE tables, logits, 32 MiB
- * for hipBLASLt). 0 if invalid. */
+ * max_chunk rows, attention partials and sums, RoPE tables, logits). 0 if
+ * invalid. */
 size_t dory_workspace_bytes(const dory_config* cfg);
 
 /* Where the KV of (layer, loop, pos) lives: cache id, slot, and the element
@@ -178,12 +178,9 @@ const char* dory_status_string(dory_status s);
 
 /* ---- context ------------------------------------------------------------ */
 
-/* Binds caller memory. For bfloat16 models with a device present it also
- * creates the context's hipBLASLt handle: every bfloat16 GEMM above 8 rows
- * (prefill, batched decode, the backward's products) runs on hipBLASLt; the library
- * allocates its own small state there, the only allocation this API makes,
- * and none after; otherwise it makes no HIP call and everything runs on this
- * library's kernels. The first dory_prefill on
+/* Binds caller memory; makes no HIP call and allocates nothing on the
+ * device (every computation runs on this library's kernels, in memory the
+ * caller owns). The first dory_prefill on
  * the context builds the RoPE tables (angles in float64, stored float32) in
  * the workspace on the stream. kv_dev must hold dory_kv_bytes(cfg, kv_mode,
  * kv_loops) bytes and ws_dev dory_workspace_bytes(cfg); both 256-byte

@@ -64,8 +64,10 @@ def build(verbose: bool = True, incremental: bool = False) -> str:
         list(ex.map(_compile, todo))
     objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     tmp = LIB + ".tmp"
+    # --no-undefined: a symbol that a source failed to emit is a build error,
+    # not a load-time one
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
-           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+           "-Wl,--no-undefined"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

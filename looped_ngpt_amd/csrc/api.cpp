@@ -11,7 +11,6 @@
 #include <string>
 #include <vector>
 
-#include "blaslt.h"
 #include "dory.h"
 #include "kernels.h"
 #include "plan.h"
@@ -46,7 +45,6 @@ struct dory_ctx {
   std::vector<Graph> graphs;
   hipStream_t gst = nullptr;
   hipEvent_t gev[2] = {nullptr, nullptr};
-  BlasLt* blas = nullptr;  // hipBLASLt for the plain prefill GEMMs (nullptr without a device)
   // timing tap
   int time_kind = 0;
   std::vector<hipEvent_t> ev;
@@ -60,7 +58,6 @@ struct dory_ctx {
     graphs.clear();
   }
   ~dory_ctx() {
-    blaslt_destroy(blas);
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     drop_graphs();
     for (hipEvent_t e : gev)
@@ -108,49 +105,23 @@ dory_status set_err(dory_ctx* c, dory_status s, const std::string& msg) {
     if (s_ != DORY_OK) return s_; \
   } while (0)
 
-// y = x . W^T for one layer projection. MXFP8 weights: the decode GEMV for
-// M <= 8 rows, otherwise the projection is first expanded to bfloat16 in the
-// workspace and multiplied by the bfloat16 GEMM.
+// y = x . W^T for one layer projection: the GEMV kernels up to 8 rows, the
+// tiled matrix-core GEMMs above (SwiGLU in their epilogue). Low-bit weights:
+// the decode GEMV for M <= 8 rows, otherwise the projection is first expanded
+// to bfloat16 in the workspace and multiplied by the bfloat16 GEMM.
 dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void* x, int64_t ldx, void* y, int M,
                  int N, int K, int epi, float scale) {
   const Plan& P = c->plan;
   const int dt = P.cfg.dtype;
   const int fmt = P.cfg.weight_format;
-  // bfloat16 GEMMs above the GEMV row counts: hipBLASLt (its own algorithm per
-  // shape). SwiGLU: the library writes u | v in bfloat16 into the fused
-  // projection's buffer (free once attention has run) and a row kernel
-  // applies the activation — u and v are rounded to bfloat16 on this path.
-  auto library = [&](const void* w, float s) -> bool {
-    if (dt != DORY_BF16 || M < kBlasMinRows || !c->blas) return false;
-    const size_t need = (size_t)M * N * 2, have = (size_t)P.max_rows * P.qkvg_dim * 4;
-    if (epi != 0 && (need > have || (N / 2) % 8)) return false;
-    // a pending timing pair brackets the library call(s) on the stream
-    const LaunchEvents ev = take_next_launch_events();
-    if (ev.start) (void)hipEventRecord(ev.start, c->st);
-    bool ok;
-    if (epi == 0) {
-      ok = blaslt_gemm(c->blas, x, ldx, w, y, false, M, N, K, s, c->ws + P.ws.blas, kBlasWsBytes, c->st);
-    } else {
-      void* uv = c->ws + P.ws.qkvg;
-      ok = blaslt_gemm(c->blas, x, ldx, w, uv, true, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st) &&
-           launch_swiglu_rows(uv, M, N / 2, s, y, c->st) == hipSuccess;
-    }
-    if (ev.start) {
-      if (ok)
-        (void)hipEventRecord(ev.stop, c->st);
-      else
-        set_next_launch_events(ev.start, ev.stop);  // hand the pair on to our GEMM
-    }
-    return ok;
-  };
   if (fmt == DORY_WEIGHTS_DTYPE) {
-    if (!library(W, scale)) HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
+    HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, epi, scale, 0, c->st));
   } else if (linear_lowbit_supported(fmt, M, K)) {
     HIP_TRY(c, launch_linear_lowbit(fmt, x, ldx, W, S, y, M, N, K, epi, scale * g, c->st));
   } else {
     void* wdq = c->ws + P.ws.wdq;
     HIP_TRY(c, launch_dequant_lowbit(fmt, W, S, N, K, wdq, c->st));
-    if (!library(wdq, scale * g)) HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale * g, 0, c->st));
+    HIP_TRY(c, launch_linear(dt, x, ldx, wdq, y, M, N, K, epi, scale * g, 0, c->st));
   }
   return DORY_OK;
 }
@@ -601,83 +572,8 @@ struct Bw {
 };
 
 // y[M][N] = x[M][K] . W[N][K]^T, float32 out, operands in the model dtype
-// (bfloat16 with enough rows: hipBLASLt)
 dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K) {
-  const Plan& P = c->plan;
-  if (P.cfg.dtype == DORY_BF16 && M >= kBlasMinRows && c->blas &&
-      blaslt_gemm(c->blas, x, ldx, W, y, false, M, N, K, 1.f, c->ws + P.ws.blas, kBlasWsBytes, c->st))
-    return DORY_OK;
-  HIP_TRY(c, launch_linear(P.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
-  return DORY_OK;
-}
-
-// Attention of the backward through strided-batched GEMMs (bfloat16 models
-// with hipBLASLt): one batch entry per (sequence, kv head), its q heads'
-// queries stacked as G*n rows (head-major copies), so that dK and dV sum over
-// the group's heads inside the products. The scores are computed in full and
-// masked in the softmax rows.
-bool bw_attn_gemm(const Bw& b) { return b.c->plan.cfg.dtype == DORY_BF16 && b.c->blas != nullptr; }
-
-dory_status bw_rm(const Bw& b, bool tA, bool tB, int M, int N, int K, const void* A, int ta, int64_t lda, int64_t sA,
-                  const void* B, int tb, int64_t ldb, int64_t sB, void* C, int tc, int64_t ldc, int64_t sC, int batch,
-                  float alpha) {
-  dory_ctx* c = b.c;
-  if (!blaslt_rm(c->blas, tA, tB, M, N, K, A, ta, lda, sA, B, tb, ldb, sB, C, tc, ldc, sC, batch, alpha,
-                 c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
-    return set_err(c, DORY_E_HIP, "backward: hipBLASLt has no algorithm for an attention product");
-  return DORY_OK;
-}
-
-dory_status bw_attn_fwd_gemm(const Bw& b, bool full) {
-  dory_ctx* c = b.c;
-  const Plan& P = c->plan;
-  const dory_config& C = P.cfg;
-  const BwLayout& L = b.L;
-  const int n = b.n, hd = C.head_dim, nq = C.n_q_heads, nkv = C.n_kv_heads, G = nq / nkv;
-  const int R = G * n, batch = b.B * nkv;
-  hipStream_t st = c->st;
-  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.qn), (int64_t)nq * hd, 0, nq, hd, n, b.B, b.ws + L.Qh, st));
-  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.kn), (int64_t)nkv * hd, 0, nkv, hd, n, b.B, b.ws + L.Kh, st));
-  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.P1), P.qkvg_dim, P.q_dim + P.kv_dim, nkv, hd, n, b.B, b.ws + L.Vh,
-                                st));
-  // S = scale Q K^T
-  DORY_TRY(bw_rm(b, false, true, R, n, hd, b.ws + L.Qh, 1, hd, (int64_t)R * hd, b.ws + L.Kh, 1, hd, (int64_t)n * hd,
-                 b.ws + L.S, 0, n, (int64_t)R * n, batch, P.attn_scale));
-  HIP_TRY(c, launch_bw_softmax_rows(b.f<float>(L.S), (int64_t)batch * R, n, full ? 0 : C.window, b.ws + L.Pb, st));
-  // O = P V
-  DORY_TRY(bw_rm(b, false, false, R, hd, n, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Vh, 1, hd, (int64_t)n * hd,
-                 b.ws + L.Oh, 0, hd, (int64_t)R * hd, batch, 1.f));
-  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.Oh), nq, hd, n, b.B, b.f<float>(L.o), st));
-  return DORY_OK;
-}
-
-// given dO (float32 rows): dqn, dkn, dv (float32 rows)
-dory_status bw_attn_bwd_gemm(const Bw& b, bool full) {
-  dory_ctx* c = b.c;
-  const Plan& P = c->plan;
-  const dory_config& C = P.cfg;
-  const BwLayout& L = b.L;
-  const int n = b.n, hd = C.head_dim, nq = C.n_q_heads, nkv = C.n_kv_heads, G = nq / nkv;
-  const int R = G * n, batch = b.B * nkv;
-  hipStream_t st = c->st;
-  HIP_TRY(c, launch_bw_attn_D(b.f<float>(L.dO), b.f<float>(L.o), nq, hd, b.M, b.f<float>(L.D), st));
-  HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.dO), (int64_t)nq * hd, 0, nq, hd, n, b.B, b.ws + L.dOh, st));
-  // dV = P^T dO (sums the group's heads)
-  DORY_TRY(bw_rm(b, true, false, n, hd, R, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.dOh, 1, hd, (int64_t)R * hd,
-                 b.ws + L.dVh, 0, hd, (int64_t)n * hd, batch, 1.f));
-  // dP = dO V^T (into the score buffer), then dS = P (dP - D) over P
-  DORY_TRY(bw_rm(b, false, true, R, n, hd, b.ws + L.dOh, 1, hd, (int64_t)R * hd, b.ws + L.Vh, 1, hd,
-                 (int64_t)n * hd, b.ws + L.S, 0, n, (int64_t)R * n, batch, 1.f));
-  HIP_TRY(c, launch_bw_dsoft_rows(b.f<float>(L.S), b.ws + L.Pb, b.f<float>(L.D), (int64_t)batch * R, n,
-                                  full ? 0 : C.window, G, nq, nkv, st));
-  // dQ = scale dS K, dK = scale dS^T Q
-  DORY_TRY(bw_rm(b, false, false, R, hd, n, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Kh, 1, hd, (int64_t)n * hd,
-                 b.ws + L.dQh, 0, hd, (int64_t)R * hd, batch, P.attn_scale));
-  DORY_TRY(bw_rm(b, true, false, n, hd, R, b.ws + L.Pb, 1, n, (int64_t)R * n, b.ws + L.Qh, 1, hd, (int64_t)R * hd,
-                 b.ws + L.dKh, 0, hd, (int64_t)n * hd, batch, P.attn_scale));
-  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dQh), nq, hd, n, b.B, b.f<float>(L.dqn), st));
-  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dKh), nkv, hd, n, b.B, b.f<float>(L.dkn), st));
-  HIP_TRY(c, launch_bw_from_heads(b.f<float>(L.dVh), nkv, hd, n, b.B, b.f<float>(L.dv), st));
+  HIP_TRY(c, launch_linear(c->plan.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
   return DORY_OK;
 }
 
@@ -695,9 +591,7 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   DORY_TRY(bw_gemm(c, b.ws + L.xb, d, c->qkvg[l], b.f<float>(L.P1), M, Q, d));
   HIP_TRY(c, launch_bw_rope_norm_fwd(b.f<float>(L.P1), Q, tab, b.n, C.n_q_heads, C.n_kv_heads, C.head_dim, M,
                                      b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.rq), b.f<float>(L.rk), st));
-  if (bw_attn_gemm(b)) {
-    DORY_TRY(bw_attn_fwd_gemm(b, full));
-  } else {
+  {
     BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
              C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
     HIP_TRY(c, launch_bw_attn_fwd(a, M, b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst), st));
@@ -716,29 +610,19 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   return DORY_OK;
 }
 
-// dW [N][K] = dY^T X from dY [M][N] and X [M][K] (model dtype). hipBLASLt
-// reads dY transposed in place; otherwise both are transposed into TA / TB,
-// then one GEMM over the M rows
+// dW [N][K] = dY^T X from dY [M][N] and X [M][K] (model dtype): both are
+// transposed into TA / TB, then one GEMM over the M rows
 dory_status bw_wgrad(const Bw& b, const void* dY, int N, const void* X, int K, float* dW) {
   dory_ctx* c = b.c;
   const int dt = c->plan.cfg.dtype;
-  if (dt == DORY_BF16 && c->blas && b.M >= kBlasMinRows &&
-      blaslt_rm(c->blas, true, false, N, K, b.M, dY, 1, N, 0, X, 1, K, 0, dW, 0, K, 0, 1, 1.f,
-                c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
-    return DORY_OK;
   HIP_TRY(c, launch_bw_transpose(dt, dY, N, b.ws + b.L.TA, b.M, N, c->st));
   HIP_TRY(c, launch_bw_transpose(dt, X, K, b.ws + b.L.TB, b.M, K, c->st));
   return bw_gemm(c, b.ws + b.L.TA, b.M, b.ws + b.L.TB, dW, N, K, b.M);
 }
 
-// dX [M][K] = dY [M][N] . W [N][K]: hipBLASLt reads W as stored; otherwise
-// W is transposed into WT, then one GEMM
+// dX [M][K] = dY [M][N] . W [N][K]: W is transposed into WT, then one GEMM
 dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX) {
   dory_ctx* c = b.c;
-  if (c->plan.cfg.dtype == DORY_BF16 && c->blas && b.M >= kBlasMinRows &&
-      blaslt_rm(c->blas, false, false, b.M, K, N, dY, 1, N, 0, W, 1, K, 0, dX, 0, K, 0, 1, 1.f,
-                c->ws + c->plan.ws.blas, kBlasWsBytes, c->st))
-    return DORY_OK;
   HIP_TRY(c, launch_bw_transpose(c->plan.cfg.dtype, W, K, b.ws + b.L.WT, N, K, c->st));
   return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N);
 }
@@ -781,9 +665,7 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
                                 qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
                                 b.f<float>(L.dP1), st));
-  if (bw_attn_gemm(b)) {
-    DORY_TRY(bw_attn_bwd_gemm(b, full));
-  } else {
+  {
     BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
              C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
     HIP_TRY(c, launch_bw_attn_bwd(a, M, b.f<float>(L.dO), b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst),
@@ -933,7 +815,6 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, void* kv_
   c->kvb = (char*)kv_dev;
   c->ws = (char*)ws_dev;
   c->st = (hipStream_t)stream;
-  if (P.cfg.dtype == DORY_BF16) c->blas = blaslt_create();  // needs a device; none: our GEMM throughout
   *out = c;
   return DORY_OK;
 }

@@ -651,42 +651,78 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, i
 }
 
 // ---------------------------------------------------------------------------
-// Large-M prefill GEMM: 256x256 workgroup tiles, eight waves (two per SIMD)
-// of 128x64, K steps of 32 through a four-stage LDS ring that the tiles reach
-// by direct global->LDS loads (global_load_lds_dwordx4: lane l of a wave's
-// load writes bytes 16l..16l+15 of a 1 KB block, so a block is 16 tile rows
-// of 64 B). Inside a row the 16-byte chunks are XOR-swizzled by (row/4)%4,
-// which makes the 16-lane groups of the fragment reads hit distinct banks.
-// A stage is waited for with an explicit vmcnt (the loads of the two younger
-// stages stay in flight) and one workgroup barrier per K step; the ring slot
-// refilled at step kt was last read at step kt-1, before that barrier.
+// Large-M prefill GEMM: 256 x BN workgroup tiles (BN = 256, or 192 where 256
+// would leave the last round of workgroups half empty, e.g. N = 3072), four
+// waves (one per SIMD) in a 2 x 2 grid of 128 x BN/2, so every LDS fragment
+// feeds BN/64 (A) or 4 (B) matrix-core products. The 4 x BN/64 accumulator
+// blocks of v_mfma_f32_32x32x16_bf16 (256 floats per lane at BN = 256) live
+// in the accumulation registers.
+//
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4:
+// lane l of a wave's load writes bytes 16l..16l+15 of a 1 KB block). A stage
+// is 64 deep in K, so a load covers 8 tile rows x 128 B — whole cache lines
+// (16 rows x 64 B per load, a 32-deep stage, streamed measurably slower).
+// Inside a row the 16-byte chunks are XOR-swizzled by (row/2)%8, which makes
+// the 16-lane groups of the fragment reads hit distinct banks (no bank
+// conflicts by the counters). The 160 KB of LDS hold A in a three-slot ring
+// and B in a two-slot ring: the loads of A for stage kt+2 go out in three
+// pieces during stage kt, those of B for stage kt+2 right after the barrier
+// that ends stage kt (the slot that stage kt's B used is then free: its last
+// 16-deep slice is already in registers), so every load has one to two
+// stages of matrix work to land. One workgroup barrier per stage, after an
+// explicit vmcnt wait for stage kt+1 (A of stage kt+2 stays in flight).
+// Within a stage the fragments of the next 16-deep slice are read while the
+// current one is multiplied, one LDS read (or global load) issued after each
+// product (sched_group_barrier), so neither unit sees bursts.
+//
 // Workgroups are spread over the 8 XCDs in contiguous runs of tiles, grouped
-// two M tiles at a time, so concurrent tiles on one XCD share A and B rows in
-// its L2. Requires K % 32 == 0 and 16-byte aligned rows.
+// four M tiles at a time, so the tiles that run together on one XCD share A
+// and B rows in its L2. SwiGLU (BN = 256 only): B tile rows come in 32-row
+// chunks u, v, u, v of the same outputs, and a wave's blocks (0, 1) and
+// (2, 3) are (u, v) pairs. Requires K % 64 == 0 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 #define DORY_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt lgkmcnt(0) and no wait on the other counters
+#define DORY_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
+// sched_group_barrier masks
+#define DORY_SG_MFMA 0x008
+#define DORY_SG_VMEM_RD 0x020
+#define DORY_SG_DS_RD 0x100
 
-constexpr int kBigBK = 32;                          // K per stage
-constexpr int kBigHalf = 256 * kBigBK * 2;          // A (or B) bytes per stage: 16 KB
-constexpr int kBigStage = 2 * kBigHalf;             // 32 KB
-constexpr int kBigStages = 4;
-constexpr int kBigLoads = kBigStage / 8 / 1024;     // 1 KB loads per wave per stage (4)
-constexpr int kBigGroupM = 2;
+constexpr int kBigBK = 64;      // K per stage
+constexpr int kBigGroupM = 4;
+constexpr int kBigLds = 160 * 1024;
 
-__device__ __forceinline__ int big_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// 16 bytes per lane from global memory straight into LDS (a wave fills dst ..
+// dst + 1023). A plain device function: called directly from a lambda of a
+// kernel template, the builtin made host compilation drop its callers.
+__device__ __forceinline__ void lds_load16(const bf16* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
 
-template <int EPI>
-__global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, int64_t lda,
+// byte offset of 16-byte chunk c (K elements 8c..8c+7) of tile row r in a stage
+__device__ __forceinline__ int big_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) void k_gemm_big(const bf16* __restrict__ A, int64_t lda,
                                                   const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
                                                   int K, float scale) {
-  __shared__ __align__(1024) unsigned char smem[kBigStages * kBigStage];
+  static_assert(BN == 256 || (BN == 192 && EPI == EPI_F32), "tile widths");
+  constexpr int NJ = BN / 64;          // 32-column blocks per wave
+  constexpr int kHA = 256 * 128;       // A bytes per stage (32 KB)
+  constexpr int kHB = BN * 128;        // B bytes per stage (32 or 24 KB)
+  constexpr int kLA = kHA / 4096;      // 1 KB loads per wave per stage: A 8, B 8 or 6
+  constexpr int kLB = kHB / 4096;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  unsigned char* const sA = smem;             // 3 x kHA
+  unsigned char* const sB = smem + 3 * kHA;   // 2 x kHB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;  // rows wm*128, columns wn*64 of the tile
+  const int wm = wave >> 1, wn = wave & 1;  // rows wm*128, columns wn*BN/2 of the tile
   const int F = N / 2;
   const int nM = (M + 255) / 256;
-  const int nN = EPI == EPI_SWIGLU ? (F + 127) / 128 : (N + 255) / 256;
+  const int nN = EPI == EPI_SWIGLU ? (F + 127) / 128 : (N + BN - 1) / BN;
   const int nt = nM * nN;
   const int per = (nt + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -695,78 +731,133 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
   const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
   const int loc = t - grp * kBigGroupM * nN;
   const int m0 = (grp * kBigGroupM + loc % gs) * 256;
-  const int n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * 256;
+  const int n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * BN;
 
-  // this lane's rows for its 2 A and 2 B loads per stage (clamped: rows past
-  // M or N load a valid row and are never stored). SwiGLU: B tile rows come
-  // in 32-row chunks u, v, u, v of the same outputs.
-  const int lr = lane >> 2, ls = lane & 3;
-  const bf16* src[4];
+  // this lane's source rows (clamped: rows past M or N load a valid row and
+  // are never stored); load i of a wave fills tile rows 8 (wave kL + i) + 0..7
+  const int lr = lane >> 3, ls = lane & 7;
+  const bf16* srcA[kLA];
+  const bf16* srcB[kLB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 2 + (i & 1)) * 16 + lr;
-    const int c = ls ^ ((r >> 2) & 3);
-    if (i < 2) {
-      src[i] = A + (size_t)min(m0 + r, M - 1) * lda + c * 8;
-    } else {
-      int wr;
-      if (EPI == EPI_SWIGLU) {
-        const int nb = r >> 5;
-        const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
-        wr = (nb & 1 ? F : 0) + o;
-      } else {
-        wr = min(n0 + r, N - 1);
-      }
-      src[i] = B + (size_t)wr * K + c * 8;
-    }
+  for (int i = 0; i < kLA; ++i) {
+    const int r = (wave * kLA + i) * 8 + lr;
+    srcA[i] = A + (size_t)min(m0 + r, M - 1) * lda + (ls ^ ((r >> 1) & 7)) * 8;
   }
-  auto issue = [&](int kt) {
-    unsigned char* st = smem + (kt % kBigStages) * kBigStage;
-    const int k0 = kt * kBigBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + k0,
-                                       (lds_void_t*)(st + (i >= 2 ? kBigHalf : 0) + (wave * 2 + (i & 1)) * 1024), 16,
-                                       0, 0);
+  for (int i = 0; i < kLB; ++i) {
+    const int r = (wave * kLB + i) * 8 + lr;
+    int wr;
+    if (EPI == EPI_SWIGLU) {
+      const int nb = r >> 5;
+      const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
+      wr = (nb & 1 ? F : 0) + o;
+    } else {
+      wr = min(n0 + r, N - 1);
+    }
+    srcB[i] = B + (size_t)wr * K + (ls ^ ((r >> 1) & 7)) * 8;
+  }
+  auto issueA = [&](int kt, int i0, int i1) {
+    unsigned char* st = sA + (kt % 3) * kHA;
+#pragma unroll
+    for (int i = i0; i < i1; ++i) lds_load16(srcA[i] + kt * kBigBK, st + (wave * kLA + i) * 1024);
+  };
+  auto issueB = [&](int kt) {
+    unsigned char* st = sB + (kt & 1) * kHB;
+#pragma unroll
+    for (int i = 0; i < kLB; ++i) lds_load16(srcB[i] + kt * kBigBK, st + (wave * kLB + i) * 1024);
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nK = K / kBigBK;
   const int l32 = lane & 31, lh = lane >> 5;
-  issue(0);
-  if (nK > 1) issue(1);
-  if (nK > 2) issue(2);
-  for (int kt = 0; kt < nK; ++kt) {
-    const int ahead = min(2, nK - 1 - kt);  // younger stages allowed in flight
-    if (ahead == 2) DORY_WAIT_VM(2 * kBigLoads); else if (ahead == 1) DORY_WAIT_VM(kBigLoads); else DORY_WAIT_VM(0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 3 < nK) issue(kt + 3);
-    const unsigned char* sa = smem + (kt % kBigStages) * kBigStage;
-    const unsigned char* sb = sa + kBigHalf;
+  // fragments of 16-deep K slice ks (0..3) of stage kt
+  auto frag = [&](int kt, int ks, bf16x8_t (&fa)[4], bf16x8_t (&fb)[NJ]) {
+    const unsigned char* a = sA + (kt % 3) * kHA;
+    const unsigned char* b = sB + (kt & 1) * kHB;
+    const int c = ks * 2 + lh;
 #pragma unroll
-    for (int ks = 0; ks < kBigBK / 16; ++ks) {
-      bf16x8_t a[4], b[2];
-      const int c = ks * 2 + lh;
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(a + big_off(wm * 128 + i * 32 + l32, c));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(sa + big_off(wm * 128 + i * 32 + l32, c));
+    for (int j = 0; j < NJ; ++j) fb[j] = *(const bf16x8_t*)(b + big_off(wn * (BN / 2) + j * 32 + l32, c));
+  };
+  auto mma = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NJ]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(sb + big_off(wn * 64 + j * 32 + l32, c));
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  bf16x8_t fa[2][4], fb[2][NJ];
+  // prologue: A and B of stages 0 and 1
+  issueA(0, 0, kLA);
+  issueB(0);
+  if (nK > 1) {
+    issueA(1, 0, kLA);
+    issueB(1);
+    DORY_WAIT_VM(kLA + kLB);
+  } else {
+    DORY_WAIT_VM(0);
   }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  frag(0, 0, fa[0], fb[0]);
+  DORY_WAIT_LGKM0();
+  for (int kt = 0; kt < nK; ++kt) {
+    const bool moreA = kt + 2 < nK;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) {
+        // a third of A(kt+2) into the A slot stage kt-1 used; fragments of slice s+1
+        constexpr int c0[3] = {0, kLA / 3, 2 * kLA / 3}, c1[3] = {kLA / 3, 2 * kLA / 3, kLA};
+        if (moreA) issueA(kt + 2, c0[s], c1[s]);
+        frag(kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        mma(fa[s & 1], fb[s & 1]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_VMEM_RD, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4 + NJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 4 * NJ - 7 - NJ, 0);
+      } else {
+        // stage kt+1 complete (A of stage kt+2 may stay in flight), then B of
+        // stage kt+2 into the B slot stage kt used, fragments of stage kt+1
+        if (moreA) DORY_WAIT_VM(kLA); else DORY_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 2 < nK) issueB(kt + 2);
+        frag(kt + 1, 0, fa[0], fb[0]);  // unconditional (past the last stage: a stale slot, unused): exact waits
+        mma(fa[1], fb[1]);
+#pragma unroll
+        for (int q = 0; q < kLB; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_VMEM_RD, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4 + NJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_DS_RD, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the fragment reads are done long before the products are: waiting
+      // here lets the next slice's products start without a wait
+      DORY_WAIT_LGKM0();
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
@@ -776,17 +867,48 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
       const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
-        const int o = n0 + wn * 32 + l32;
-        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * scale * silu_(acc[i][1][r] * scale));
+#pragma unroll
+        for (int jp = 0; jp < NJ / 2; ++jp) {
+          const int o = n0 + wn * 64 + jp * 32 + l32;
+          if (o < F)
+            ((bf16*)C)[(size_t)row * F + o] =
+                from_f<bf16>(acc[i][2 * jp][r] * scale * silu_(acc[i][2 * jp + 1][r] * scale));
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < NJ; ++j) {
+          const int col = n0 + wn * (BN / 2) + j * 32 + l32;
           if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
         }
       }
     }
   }
+}
+
+// LDS bytes of k_gemm_big (three A slots and two B slots of one stage)
+static constexpr uint32_t big_lds(int bn) { return 3 * 256 * 128 + 2 * bn * 128; }
+
+// k_gemm_big<EPI, BN> with its dynamic LDS above the 64 KB default allowed
+// (set once per process)
+template <int EPI, int BN>
+static void big_launch(dim3 grid, const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                       hipStream_t st) {
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_big<EPI, BN>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)big_lds(BN));
+  (void)attr;
+  dory_launch((k_gemm_big<EPI, BN>), grid, dim3(256), big_lds(BN), st, x, ldx, W, y, M, N, K, scale);
+}
+
+// tile width for a large-M GEMM with N outputs: 192 when 256-wide tiles would
+// leave the last round of workgroups (one per CU) at most half full and
+// 192-wide ones do better
+static int big_tile_n(int M, int N) {
+  auto eff = [&](int bn) {
+    const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+    const long rounds = (tiles + kNumCUs - 1) / kNumCUs;
+    return (double)tiles / (double)(rounds * kNumCUs) * (bn == 256 ? 1.0 : 0.93);  // 192: more LDS reads per FLOP
+  };
+  return eff(192) > eff(256) ? 192 : 256;
 }
 
 // ---------------------------------------------------------------------------
@@ -919,9 +1041,12 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
   const bool al16 = ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0);
   if (sizeof(T) == 2 && al16 && K % kBigBK == 0 && M >= 1024) {
-    const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + 255) / 256);
-    dory_launch((k_gemm_big<EPI>), dim3((tiles + 7) / 8 * 8), dim3(512), 0, st, (const bf16*)x, ldx,
-                (const bf16*)W, y, M, N, K, scale);
+    const int bn = EPI == EPI_SWIGLU ? 256 : big_tile_n(M, N);
+    const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + bn - 1) / bn);
+    if (bn == 192)
+      big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+    else
+      big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
   } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
     const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
     dim3 grid(nt, (M + GBM - 1) / GBM);

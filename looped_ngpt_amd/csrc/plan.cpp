@@ -140,7 +140,6 @@ WsLayout make_ws_layout(const Plan& p) {
   w.flags = take(256);
   w.pos = take(4);
   w.rowk = take((size_t)c.max_batch * 4);
-  w.blas = take(kBlasWsBytes);
   w.attn_acc = take((size_t)std::min(c.max_batch, 8) * c.n_q_heads * attn_acc_stride(c.head_dim, kAttnAccBinsMax) * 8);
   if (c.weight_format != DORY_WEIGHTS_DTYPE) {  // one projection expanded to bfloat16 for prefill GEMMs
     const size_t d = c.d_model;
@@ -158,9 +157,6 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   const auto& c = p.cfg;
   const size_t M = (size_t)B * n, d = c.d_model, F = c.d_ff, Q = p.qkvg_dim, qd = p.q_dim, kvd = p.kv_dim;
   const size_t nq = c.n_q_heads, el = p.elem;
-  const bool bf = c.dtype == DORY_BF16;
-  const size_t hq = (size_t)B * nq * n * c.head_dim, hk = (size_t)B * c.n_kv_heads * n * c.head_dim;
-  const size_t sq = (size_t)B * nq * n * n;
   size_t at = 0;
   auto take = [&](size_t bytes) {
     size_t o = at;
@@ -187,14 +183,6 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   w.TA = take(M * std::max(Q, std::max(2 * F, d)) * el);
   w.TB = take(M * std::max(d, std::max(F, qd)) * el);
   w.WT = take(std::max(std::max(Q * d, 2 * F * d), std::max(d * qd, d * F)) * el);
-  if (bf) {
-    w.dOh = take(hq * el);
-    w.Oh = take(hq * 4);
-    w.dQh = take(hq * 4);
-    w.dKh = take(hk * 4);
-    w.dVh = take(hk * 4);
-    w.S = take(sq * 4);
-  }
   // one layer's forward values
   const size_t g0 = at;
   w.P1 = take(M * Q * 4);
@@ -221,12 +209,6 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   w.ohb = take(M * qd * el);
   w.h1b = take(M * d * el);
   w.ab = take(M * F * el);
-  if (bf) {
-    w.Qh = take(hq * el);
-    w.Kh = take(hk * el);
-    w.Vh = take(hk * el);
-    w.Pb = take(sq * el);
-  }
   w.layer_bytes = at - g0;
   w.stored = stored;
   w.total = at + (stored ? (size_t)(c.n_rec - 1) * w.layer_bytes : 0);
@@ -240,12 +222,6 @@ BwLayout bw_layer_view(const BwLayout& L, int i) {
   for (size_t* f : {&v.P1, &v.qn, &v.kn, &v.rq, &v.rk, &v.o, &v.mst, &v.lst, &v.oh, &v.rc, &v.yh, &v.ry, &v.rz,
                     &v.h1, &v.P2, &v.a32, &v.rs, &v.y2h, &v.ry2, &v.rz2, &v.xb, &v.ohb, &v.h1b, &v.ab})
     *f += s;
-  if (L.Pb) {
-    v.Qh += s;
-    v.Kh += s;
-    v.Vh += s;
-    v.Pb += s;
-  }
   return v;
 }
 

@@ -16,8 +16,6 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kMaxSplits = 64;        // split-K pieces per (row, kv head) in decode attention
 constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
 constexpr size_t kAlign = 256;
-constexpr size_t kBlasWsBytes = 32u << 20;  // workspace handed to hipBLASLt for prefill GEMMs
-constexpr int kBlasMinRows = 9;  // rows from which bfloat16 GEMMs go to hipBLASLt (up to 8: our GEMVs)
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 // Row length of a call's transposed values [B][n_kv][hd][vld]: n rounded up
@@ -42,7 +40,6 @@ struct WsLayout {
   size_t pos = 0;                      // int: position counter read by decode kernels
   size_t rowk = 0;                     // int [max_batch]: per-sequence loop counts of a mixed call
   size_t wdq = 0;                      // bf16: one low-bit projection expanded for a prefill GEMM
-  size_t blas = 0;                     // hipBLASLt workspace (kBlasWsBytes)
   size_t attn_acc = 0;                 // uint64 [min(max_batch, 8)][n_q][hd + 8]: decode attention sums
   size_t total = 0;
 };
@@ -90,12 +87,8 @@ struct BwLayout {
   size_t dO = 0, D = 0, dqn = 0, dkn = 0, dv = 0, dP1 = 0;
   size_t xb = 0, ohb = 0, h1b = 0, ab = 0, dyb = 0, dP2b = 0, dP1b = 0;  // T
   size_t TA = 0, TB = 0, WT = 0;                    // T: transposed operands of the gradient GEMMs
-  // attention through batched GEMMs (bfloat16 models): head-major copies
-  // [B][heads][n][hd] (T: Qh, Kh, Vh, dOh; float32: Oh, dQh, dKh, dVh), the
-  // scores / dP [B][n_q][n][n] (float32) and P / dS [B][n_q][n][n] (T)
-  size_t Qh = 0, Kh = 0, Vh = 0, dOh = 0, Oh = 0, dQh = 0, dKh = 0, dVh = 0, S = 0, Pb = 0;
   // The values a layer's backward reads from its forward (P1 .. rz2 above
-  // but y, the T copies xb .. ab, Qh, Kh, Vh, Pb) sit in one group at the end
+  // but y, and the T copies xb .. ab) sit in one group at the end
   // of the layout, layer_bytes long; with every layer's group kept
   // (stored = true: n_rec groups) the backward reads them instead of running
   // each layer's forward again.
