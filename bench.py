@@ -110,28 +110,62 @@ def prefill_flops(m, k, n):
     return apps * 2 * n * (m.layer_bytes() // 2) + attn_flops(m, k, n) + 2 * m.vocab * m.d_model
 
 
-def cpu_baseline(model, dev_w, k_head: int, budget_s: float = 15.0):
-    """The oracle (numpy, float32 compute, bfloat16 storage points) on the
-    host, on the full 36-layer model with the benchmark's weights: greedy
-    decode calls at k = k_head after an 8-token prompt, timed over as many
-    calls as fit in about budget_s (at least 3). The context is short (the
-    oracle cannot prefill 8192 positions in seconds), so attention over the
-    benchmark's 8K context is not part of the sample."""
-    import numpy as np
+def _host_info():
+    """CPU model and the BLAS library numpy calls (threadpoolctl), for the report."""
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
+            threads = max(int(i.get("num_threads", 1)) for i in libs)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    from oracle.ngpt import LoopedNGPT
+        pass
+    return cpu, blas, threads
+
+
+def cpu_baseline(model, dev_w, k_head: int, ctx: int = 8192, budget_s: float = 15.0):
+    """The oracle (numpy, float32 compute, bfloat16 storage points) on the
+    host, on the full 36-layer model with the benchmark's weights, decoding
+    at the benchmark's context: its KV caches are filled for positions
+    0..ctx-1 with synthetic bfloat16 keys (unit vectors per head) and values
+    (N(0, 1/d) entries, the scale of a unit row times unit weight rows), as
+    the GPU run's caches hold prefilled keys, and greedy decode calls at
+    k = k_head are timed over as many calls as fit in about budget_s (at
+    least 3). The sample therefore includes the attention over ctx cached
+    positions (full layers) and the 4096-key windows (sliding layers)."""
+    import numpy as np
+    from oracle.ngpt import LoopedNGPT, round_bf16
+    cpu_model, blas, threads = _host_info()
     t_start = time.perf_counter()
     w = {}
     for name, t in dev_w.items():
         a = t.cpu().numpy()
         w[name] = a.view(np.uint16) if a.dtype == np.int16 else a
-    o = LoopedNGPT(model, w, compute="f32", bf16_points=True, max_ctx=64)
-    prompt = (np.arange(8, dtype=np.int64)[None, :] * 997 % model.vocab).astype(np.int32)
-    logits = o.call(prompt, k_head, "last_loop")        # also widens every weight once
+    o = LoopedNGPT(model, w, compute="f32", bf16_points=True, max_ctx=ctx + 64)
+    rng = np.random.default_rng(12345)
+    hd, nkv = model.head_dim, model.n_kv_heads
+    kk = rng.standard_normal((1, nkv, ctx, hd), dtype=np.float32)
+    kk /= np.linalg.norm(kk, axis=-1, keepdims=True)
+    vv = rng.standard_normal((1, nkv, ctx, hd), dtype=np.float32) / np.float32(np.sqrt(model.d_model))
+    kk, vv = round_bf16(kk), round_bf16(vv)
+    o.kv_mode = "last_loop"
+    for l in range(model.n_layers):
+        c = o._cache(o.cache_key(l, 0))
+        c["K"][:, :, :ctx, :] = kk
+        c["V"][:, :, :ctx, :] = vv
+    o.pos = ctx
+    tok = 17
+    logits = o.call(np.array([[tok]], dtype=np.int32), k_head, "last_loop")  # also widens every weight once
     t_setup = time.perf_counter() - t_start
     tok = int(np.argmax(logits[0]))
     calls, t0 = 0, time.perf_counter()
@@ -141,10 +175,12 @@ def cpu_baseline(model, dev_w, k_head: int, budget_s: float = 15.0):
         calls += 1
     sec = (time.perf_counter() - t0) / calls
     return {"value": round(1.0 / sec, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": (f"numpy oracle (float32 compute, bfloat16 storage points), full {model.n_layers}-layer model, "
-                       f"{calls} greedy decode calls at k={k_head} after an 8-token prompt "
-                       f"({sec * 1e3:.0f} ms/token; context <= {8 + calls} positions, so the 8K-context "
-                       f"attention of the GPU run is not included; weight widening {t_setup:.0f} s excluded)"),
+                       f"{calls} greedy decode calls at k={k_head} at context {ctx + 1}..{ctx + calls + 1} "
+                       f"(KV caches filled with synthetic bf16 keys/values for positions 0..{ctx - 1}, so the "
+                       f"attention over the {ctx}-position context is included; {sec * 1e3:.0f} ms/token; "
+                       f"weight widening and cache fill, {t_setup:.0f} s, excluded)"),
             "wall_s": round(time.perf_counter() - t_start, 1)}
 
 
@@ -449,6 +485,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
+    ap.add_argument("--no-per-loop", action="store_true", help="skip the per-loop KV decode timings")
     ap.add_argument("--bw-tokens", type=int, default=2048, help="positions of the backward workload")
     ap.add_argument("--workload", choices=["c36", "c72", "b64", "long", "mxfp8", "nvfp4", "backward"],
                     default="c36",
@@ -537,7 +574,8 @@ def main():
         ctx_mean = n + Wm + (K - 1) / 2.0
         step_bytes = decode_bytes(model, k, ctx_mean)
         by_k[k] = {"tokens_per_s": K / (ms / 1e3), "ms_per_step": ms / K,
-                   "hbm_frac": step_bytes / (ms / 1e3 / K) / HBM_PEAK, "bytes_per_step": step_bytes}
+                   "hbm_frac": step_bytes / (ms / 1e3 / K) / HBM_PEAK, "bytes_per_step": step_bytes,
+                   "kv_bytes": int(sess.kv.numel())}
         print(f"[bench] k={k} decode: {ms / K:.3f} ms/step, {K / (ms / 1e3):.1f} tok/s, "
               f"HBM {100 * by_k[k]['hbm_frac']:.1f}%", file=sys.stderr, flush=True)
         if k == args.headline_k and args.kernel_steps > 0:
@@ -554,7 +592,12 @@ def main():
         if k == args.headline_k and not args.no_prefill_taps:
             # prefill kernel-timing passes: the up/gate GEMM and the attention
             apps = model.n_in + model.n_out + k * model.n_rec
-            for kind in ("ug", "attn"):
+            d, qd = model.d_model, model.q_dim
+            shapes = {"qkvg": (model.qkvg_dim, d, "q|k|v|gate projection"),
+                      "o": (d, qd, "output projection"),
+                      "ug": (2 * model.d_ff, d, "up/gate projection with the SwiGLU epilogue"),
+                      "down": (d, model.d_ff, "down projection")}
+            for kind in ("qkvg", "o", "ug", "down", "attn"):
                 sess.reset()
                 sess.set_kernel_timing(kind, apps)
                 sess.prefill(prompt, k)
@@ -562,10 +605,10 @@ def main():
                 sess.set_kernel_timing(None)
                 if cnt == 0 or tot <= 0:
                     continue
-                if kind == "ug":
-                    fl = 2.0 * n * 2 * model.d_ff * model.d_model * cnt
-                    name = ("k_gemm_big up/gate projection with the SwiGLU epilogue (M=%d, N=%d, K=%d)"
-                            % (n, 2 * model.d_ff, model.d_model))
+                if kind in shapes:
+                    N_, K_, what = shapes[kind]
+                    fl = 2.0 * n * N_ * K_ * cnt
+                    name = "k_gemm_big %s (M=%d, N=%d, K=%d)" % (what, n, N_, K_)
                 else:
                     fl = float(attn_flops(model, k, n))
                     name = "attention (flash, causal + window %d)" % model.window
@@ -575,6 +618,26 @@ def main():
                                   "mfma_frac": round(fl / (tot / 1e3) / MFMA_PEAK, 4)}
                 print(f"[bench] prefill {name}: {cnt} launches, {tot:.2f} ms, "
                       f"{pre_taps[kind]['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+
+    # per-loop KV mode at the same loop counts: one cache per loop of every
+    # recurrent layer (KV bytes grow with k), same prompt, same timed steps
+    per_loop = {}
+    if not args.no_per_loop:
+        del sess
+        torch.cuda.empty_cache()
+        for k in ks:
+            sp = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=n, kv_mode="per_loop", kv_loops=k,
+                              stream=stream, device=dev)
+            sp.prefill(prompt, k)
+            ms = _timed_decode(sp, 1, k, K, Wm)
+            step_bytes = decode_bytes(model, k, n + Wm + (K - 1) / 2.0)
+            per_loop[str(k)] = {"tokens_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+                                "hbm_frac": round(step_bytes / (ms / 1e3) / HBM_PEAK, 4),
+                                "kv_bytes": int(sp.kv.numel())}
+            print(f"[bench] per-loop k={k} decode: {ms:.3f} ms/step, {1e3 / ms:.1f} tok/s, "
+                  f"KV {sp.kv.numel() / 1e9:.3f} GB", file=sys.stderr, flush=True)
+            del sp
+            torch.cuda.empty_cache()
 
     hk = args.headline_k
     roof = None
@@ -601,6 +664,7 @@ def main():
         "hbm_frac_step": round(by_k[hk]["hbm_frac"], 4),
         "by_k": {str(k): {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in d.items()}
                  for k, d in by_k.items()},
+        "per_loop": per_loop or None,
         "prefill": {str(k): {kk: round(v, 4) for kk, v in d.items()} for k, d in prefill.items()},
         "prefill_kernels": pre_taps or None,
         "roofline": roof,

@@ -912,6 +912,85 @@ static int big_tile_n(int M, int N) {
 }
 
 // ---------------------------------------------------------------------------
+// Batched-decode GEMM (9..64 rows): weight-stream bound. A workgroup owns 16
+// outputs (16 weight rows; SwiGLU: those 16 u rows and the 16 matching v
+// rows) and all M rows; its four waves split K in quarters. With
+// v_mfma_f32_16x16x32_bf16 lane l supplies row l%16 of a 16-row block and K
+// elements 8(l/16)..8(l/16)+7 of each 32-deep step, so every operand
+// fragment is one 16-byte load straight from global memory (the weights
+// stream once, the activations come from L2); four steps of loads are issued
+// before their products. The quarters are summed through LDS. Rows past M
+// and outputs past N are clamped loads whose results are dropped. Requires
+// K % 128 == 0 and 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSkU = 4;  // K steps of 32 whose loads are issued together
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X, int64_t ldx,
+                                                     const bf16* __restrict__ W, void* __restrict__ C, int M, int N,
+                                                     int K, float scale) {
+  constexpr int NB = MB / 16;                  // 16-row blocks of X
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;  // weight blocks (u, v)
+  __shared__ f32x4_t part[4][NR][NB][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o0 = blockIdx.x * 16;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int kper = K / 4, kb = wave * kper;
+  const bf16* wp[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) wp[j] = W + (size_t)((j ? nout : 0) + min(o0 + r16, nout - 1)) * K + kb + kq;
+  const bf16* xp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) xp[b] = X + (size_t)min(b * 16 + r16, M - 1) * ldx + kb + kq;
+  f32x4_t acc[NR][NB];
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kper; k += 32 * kSkU) {
+    bf16x8_t wf[kSkU][NR], xf[kSkU][NB];
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      const int kk = min(k + 32 * u, kper - 32);  // past the quarter: a re-read, not multiplied
+#pragma unroll
+      for (int j = 0; j < NR; ++j) wf[u][j] = __builtin_nontemporal_load((const bf16x8_t*)(wp[j] + kk));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xf[u][b] = *(const bf16x8_t*)(xp[b] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      if (k + 32 * u >= kper) break;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][b], wf[u][j], acc[j][b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part[wave][j][b][lane] = acc[j][b];
+  __syncthreads();
+  // output (row m, column n) of block b: lane n + 16 (m%16 / 4), register m % 4
+  for (int e = tid; e < MB * 16; e += 256) {
+    const int m = e >> 4, n = e & 15;
+    const int b = m >> 4, ln = n + 16 * ((m & 15) >> 2), r = m & 3;
+    float s[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) s[j] = part[0][j][b][ln][r] + part[1][j][b][ln][r] + part[2][j][b][ln][r] +
+                                        part[3][j][b][ln][r];
+    if (m >= M || o0 + n >= nout) continue;
+    if (EPI == EPI_SWIGLU)
+      ((bf16*)C)[(size_t)m * nout + o0 + n] = from_f<bf16>(s[0] * scale * silu_(s[1] * scale));
+    else
+      ((float*)C)[(size_t)m * N + o0 + n] = s[0] * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Simple tiled GEMM for float32 models and ragged shapes: 64x64 tiles, each
 // thread a 4x4 block, K in steps of 16 through LDS.
 // ---------------------------------------------------------------------------
@@ -1047,6 +1126,17 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
       big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
     else
       big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+  } else if (sizeof(T) == 2 && al16 && K % 128 == 0 && M <= 64) {
+    const dim3 grid((nout + 15) / 16);
+    if (M <= 16)
+      dory_launch((k_gemm_skinny<16, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
+    else if (M <= 32)
+      dory_launch((k_gemm_skinny<32, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
+    else
+      dory_launch((k_gemm_skinny<64, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
   } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
     const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
     dim3 grid(nt, (M + GBM - 1) / GBM);
