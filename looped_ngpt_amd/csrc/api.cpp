@@ -577,6 +577,23 @@ dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, floa
   return DORY_OK;
 }
 
+// arguments of the matrix-core backward attention on this layer's buffers
+BwFlash bw_flash_args(const Bw& b, bool full) {
+  const Plan& P = b.c->plan;
+  const dory_config& C = P.cfg;
+  const BwLayout& L = b.L;
+  BwFlash fa{};
+  fa.Q = b.f<uint16_t>(L.fQ); fa.K = b.f<uint16_t>(L.fK); fa.V = b.f<uint16_t>(L.fV); fa.dO = b.f<uint16_t>(L.fdO);
+  fa.QT = b.f<uint16_t>(L.fQT); fa.KT = b.f<uint16_t>(L.fKT); fa.VT = b.f<uint16_t>(L.fVT);
+  fa.dOT = b.f<uint16_t>(L.fdOT);
+  fa.B = b.B; fa.n = b.n; fa.nT = L.nT; fa.nq = C.n_q_heads; fa.nkv = C.n_kv_heads; fa.hd = C.head_dim;
+  fa.window = full ? 0 : C.window;
+  fa.scale = P.attn_scale;
+  fa.mst = b.f<float>(L.mst); fa.lst = b.f<float>(L.lst); fa.D = b.f<float>(L.D);
+  fa.o = b.f<float>(L.o); fa.dq = b.f<float>(L.dqn); fa.dk = b.f<float>(L.dkn); fa.dv = b.f<float>(L.dv);
+  return fa;
+}
+
 // forward of recurrent layer l on h_in -> h_out, keeping what its backward reads
 dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   dory_ctx* c = b.c;
@@ -591,7 +608,15 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   DORY_TRY(bw_gemm(c, b.ws + L.xb, d, c->qkvg[l], b.f<float>(L.P1), M, Q, d));
   HIP_TRY(c, launch_bw_rope_norm_fwd(b.f<float>(L.P1), Q, tab, b.n, C.n_q_heads, C.n_kv_heads, C.head_dim, M,
                                      b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.rq), b.f<float>(L.rk), st));
-  {
+  if (bw_flash_supported(dt, C.head_dim, C.n_q_heads, C.n_kv_heads)) {
+    BwFlash fa = bw_flash_args(b, full);
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.qn), qd, 0, C.n_q_heads, C.head_dim, b.n, b.B, b.ws + L.fQ, st));
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.kn), P.kv_dim, 0, C.n_kv_heads, C.head_dim, b.n, b.B, b.ws + L.fK,
+                                  st));
+    HIP_TRY(c, launch_bw_heads_t(b.f<float>(L.P1), Q, qd + P.kv_dim, C.n_kv_heads, C.head_dim, b.n, b.B, L.nT,
+                                 b.ws + L.fVT, st));
+    HIP_TRY(c, launch_bw_flash_fwd(fa, st));
+  } else {
     BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
              C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
     HIP_TRY(c, launch_bw_attn_fwd(a, M, b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst), st));
@@ -665,7 +690,19 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
                                 qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
                                 b.f<float>(L.dP1), st));
-  {
+  if (bw_flash_supported(dt, C.head_dim, C.n_q_heads, C.n_kv_heads)) {
+    // operand copies of this layer (the forward's may belong to another layer)
+    const int nq = C.n_q_heads, nkv = C.n_kv_heads, hd = C.head_dim, kvd = P.kv_dim;
+    HIP_TRY(c, launch_bw_attn_D(b.f<float>(L.dO), b.f<float>(L.o), nq, hd, M, b.f<float>(L.D), st));
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.qn), qd, 0, nq, hd, b.n, b.B, b.ws + L.fQ, st));
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.dO), qd, 0, nq, hd, b.n, b.B, b.ws + L.fdO, st));
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.kn), kvd, 0, nkv, hd, b.n, b.B, b.ws + L.fK, st));
+    HIP_TRY(c, launch_bw_to_heads(1, b.f<float>(L.P1), Q, qd + kvd, nkv, hd, b.n, b.B, b.ws + L.fV, st));
+    HIP_TRY(c, launch_bw_heads_t(b.f<float>(L.qn), qd, 0, nq, hd, b.n, b.B, L.nT, b.ws + L.fQT, st));
+    HIP_TRY(c, launch_bw_heads_t(b.f<float>(L.dO), qd, 0, nq, hd, b.n, b.B, L.nT, b.ws + L.fdOT, st));
+    HIP_TRY(c, launch_bw_heads_t(b.f<float>(L.kn), kvd, 0, nkv, hd, b.n, b.B, L.nT, b.ws + L.fKT, st));
+    HIP_TRY(c, launch_bw_flash_bwd(bw_flash_args(b, full), st));
+  } else {
     BwAttn a{b.f<float>(L.qn), b.f<float>(L.kn), b.f<float>(L.P1) + qd + P.kv_dim, Q, b.n, C.n_q_heads,
              C.n_kv_heads, C.head_dim, full ? 0 : C.window, P.attn_scale};
     HIP_TRY(c, launch_bw_attn_bwd(a, M, b.f<float>(L.dO), b.f<float>(L.o), b.f<float>(L.mst), b.f<float>(L.lst),

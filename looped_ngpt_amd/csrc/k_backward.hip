@@ -543,8 +543,7 @@ __global__ __launch_bounds__(256) void k_bw_rope_norm_bwd(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// attention through batched GEMMs (bfloat16 models): head-major layouts,
-// masked softmax rows and the softmax backward rows
+// head-major operand copies of the matrix-core attention (k_bw_flash.hip)
 // ---------------------------------------------------------------------------
 // dst [B][H][n][hd] (model dtype) from src rows [B*n][ld] at column off + h*hd
 template <typename T>
@@ -561,147 +560,7 @@ __global__ __launch_bounds__(256) void k_bw_to_heads(const float* __restrict__ s
   dst[e] = from_f<T>(src[(b * n + t) * ld + off + (int64_t)h * hd + d]);
 }
 
-// dst rows [B*n][H*hd] from src [B][H][n][hd]
-__global__ __launch_bounds__(256) void k_bw_from_heads(const float* __restrict__ src, int H, int hd, int n,
-                                                       int64_t total, float* __restrict__ dst) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int d = (int)(e % hd);
-  const int64_t r = e / hd;
-  const int t = (int)(r % n);
-  const int64_t bh = r / n;
-  const int h = (int)(bh % H);
-  const int64_t b = bh / H;
-  dst[(b * n + t) * ((int64_t)H * hd) + (int64_t)h * hd + d] = src[e];
-}
-
-// row r of the scores (query position t = r % n): allowed keys lo..t;
-// P = softmax over them, 0 elsewhere (bfloat16)
-__global__ __launch_bounds__(256) void k_bw_softmax_rows(const float* __restrict__ S, int n, int window,
-                                                         bf16* __restrict__ P) {
-  __shared__ float sh[4];
-  const int64_t r = blockIdx.x;
-  const int t = (int)(r % n);
-  const int lo = window > 0 ? max(0, t - window + 1) : 0;
-  const float* row = S + r * n;
-  float m = -INFINITY;
-  for (int s = lo + threadIdx.x; s <= t; s += 256) m = fmaxf(m, row[s]);
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  __syncthreads();
-  float l = 0.f;
-  for (int s = lo + threadIdx.x; s <= t; s += 256) l += expf(row[s] - m);
-  const float il = 1.f / block_sum<256>(l, sh);
-  bf16* out = P + r * n;
-  for (int s = threadIdx.x; s < n; s += 256) out[s] = from_f<bf16>(s >= lo && s <= t ? expf(row[s] - m) * il : 0.f);
-}
-
-// softmax backward rows: dS = P (dP - D) in place over P; row r of batch
-// block (b, kv head g) is (q head g*G + i, position t)
-__global__ __launch_bounds__(256) void k_bw_dsoft_rows(const float* __restrict__ dP, bf16* __restrict__ P,
-                                                       const float* __restrict__ D, int n, int G, int nq, int nkv) {
-  const int64_t r = blockIdx.x;
-  const int64_t blk = r / ((int64_t)G * n);
-  const int within = (int)(r % ((int64_t)G * n));
-  const int i = within / n, t = within % n;
-  const int64_t b = blk / nkv;
-  const int g = (int)(blk % nkv);
-  const float Dv = D[(b * n + t) * nq + g * G + i];
-  const float* dp = dP + r * n;
-  bf16* p = P + r * n;
-  for (int s = threadIdx.x; s < n; s += 256) p[s] = from_f<bf16>(to_f(p[s]) * (dp[s] - Dv));
-}
-
-// The same two row operations with one wave per row (4 rows per workgroup)
-// for n a multiple of 4 up to 256 J: lane l holds the float4 groups l + 64 j
-// of its row in registers, so the scores are read once; groups wholly outside
-// the allowed keys lo..t are neither read nor (for dS, whose P is already 0
-// there) written.
-__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  return make_uint2((uint32_t)from_f<bf16>(a) | ((uint32_t)from_f<bf16>(b) << 16),
-                    (uint32_t)from_f<bf16>(c) | ((uint32_t)from_f<bf16>(d) << 16));
-}
-
-template <int J>
-__global__ __launch_bounds__(256) void k_bw_softmax_rows_v(const float* __restrict__ S, int64_t rows, int n,
-                                                           int window, bf16* __restrict__ P) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int t = (int)(r % n);
-  const int lo = window > 0 ? max(0, t - window + 1) : 0;
-  const float4* row = reinterpret_cast<const float4*>(S + r * n);
-  float v[J][4];
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int e = 4 * (lane + 64 * j);
-    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (e < n && e + 3 >= lo && e <= t) x = row[e >> 2];
-    v[j][0] = (e >= lo && e <= t) ? x.x : -INFINITY;
-    v[j][1] = (e + 1 >= lo && e + 1 <= t) ? x.y : -INFINITY;
-    v[j][2] = (e + 2 >= lo && e + 2 <= t) ? x.z : -INFINITY;
-    v[j][3] = (e + 3 >= lo && e + 3 <= t) ? x.w : -INFINITY;
-    m = fmaxf(m, fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
-  }
-  m = wave_max(m);  // finite: key t is always allowed
-  float l = 0.f;
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[j][c] = expf(v[j][c] - m);
-      l += v[j][c];
-    }
-  const float il = 1.f / wave_sum(l);
-  uint2* out = reinterpret_cast<uint2*>(P + r * n);
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int e = 4 * (lane + 64 * j);
-    if (e < n) out[e >> 2] = pack4_bf16(v[j][0] * il, v[j][1] * il, v[j][2] * il, v[j][3] * il);
-  }
-}
-
-// dS = P (dP - D) over the allowed keys of each row
-template <int J>
-__global__ __launch_bounds__(256) void k_bw_dsoft_rows_v(const float* __restrict__ dP, bf16* __restrict__ P,
-                                                         const float* __restrict__ D, int64_t rows, int n, int window,
-                                                         int G, int nq, int nkv) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int64_t blk = r / ((int64_t)G * n);
-  const int within = (int)(r % ((int64_t)G * n));
-  const int i = within / n, t = within % n;
-  const int lo = window > 0 ? max(0, t - window + 1) : 0;
-  const int64_t b = blk / nkv;
-  const int g = (int)(blk % nkv);
-  const float Dv = D[(b * n + t) * nq + g * G + i];
-  const float4* dp = reinterpret_cast<const float4*>(dP + r * n);
-  uint2* p = reinterpret_cast<uint2*>(P + r * n);
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int e = 4 * (lane + 64 * j);
-    if (e < n && e + 3 >= lo && e <= t) {
-      const float4 x = dp[e >> 2];
-      const uint2 pv = p[e >> 2];
-      p[e >> 2] = pack4_bf16(to_f((bf16)(pv.x & 0xffffu)) * (x.x - Dv), to_f((bf16)(pv.x >> 16)) * (x.y - Dv),
-                             to_f((bf16)(pv.y & 0xffffu)) * (x.z - Dv), to_f((bf16)(pv.y >> 16)) * (x.w - Dv));
-    }
-  }
-}
-
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
-
-// groups of 4 per lane: J = ceil(n / 256) rounded up to a power of two, at most 16
-inline int rows_v_groups(int n) {
-  if (n % 4 != 0) return 0;
-  for (int J = 1; J <= 16; J *= 2)
-    if (n <= 256 * J) return J;
-  return 0;
-}
 
 }  // namespace
 
@@ -715,48 +574,6 @@ hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int
   else
     hipLaunchKernelGGL((k_bw_to_heads<float>), dim3(blocks_for(total)), dim3(256), 0, st, src, ld, off, H, hd, n,
                        total, (float*)dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, float* dst, hipStream_t st) {
-  const int64_t total = (int64_t)B * H * n * hd;
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bw_from_heads, dim3(blocks_for(total)), dim3(256), 0, st, src, H, hd, n, total, dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  if (rows > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 gv((unsigned)((rows + 3) / 4));
-  switch (rows_v_groups(n)) {
-#define SOFT_V(J)                                                                                           \
-  case J:                                                                                                   \
-    hipLaunchKernelGGL((k_bw_softmax_rows_v<J>), gv, dim3(256), 0, st, S, rows, n, window, (bf16*)P);      \
-    return hipGetLastError();
-    SOFT_V(1) SOFT_V(2) SOFT_V(4) SOFT_V(8) SOFT_V(16)
-#undef SOFT_V
-    default: break;
-  }
-  hipLaunchKernelGGL(k_bw_softmax_rows, dim3((unsigned)rows), dim3(256), 0, st, S, n, window, (bf16*)P);
-  return hipGetLastError();
-}
-
-hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int window, int G,
-                                int nq, int nkv, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  if (rows > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 gv((unsigned)((rows + 3) / 4));
-  switch (rows_v_groups(n)) {
-#define DSOFT_V(J)                                                                                               \
-  case J:                                                                                                        \
-    hipLaunchKernelGGL((k_bw_dsoft_rows_v<J>), gv, dim3(256), 0, st, dP, (bf16*)P, D, rows, n, window, G, nq, nkv); \
-    return hipGetLastError();
-    DSOFT_V(1) DSOFT_V(2) DSOFT_V(4) DSOFT_V(8) DSOFT_V(16)
-#undef DSOFT_V
-    default: break;
-  }
-  hipLaunchKernelGGL(k_bw_dsoft_rows, dim3((unsigned)rows), dim3(256), 0, st, dP, (bf16*)P, D, n, G, nq, nkv);
   return hipGetLastError();
 }
 

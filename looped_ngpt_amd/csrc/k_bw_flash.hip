@@ -1,0 +1,427 @@
+// Attention of the depth-1 truncated backward on the matrix cores (bfloat16
+// models, head dim 64 or 128): the forward with its softmax statistics, dQ,
+// and dK / dV summed over the query heads of each kv head. Scores are never
+// stored: every kernel recomputes its score tiles from q and k, so the
+// workspace stays O(n d) ("Dory1.0-4B: A Looped Normalized-GPT", ai.info AI
+// summary, Methodology in Plain English: backpropagation is truncated to the
+// last invocation of the recurrent block; the attention is the causal /
+// sliding-window grouped-query attention of the forward).
+//
+// Math (one head, queries t, keys s, unit q and k): S = scale q.k,
+// P = exp(S - m_t) / l_t over the allowed keys (s <= t, t - s < window),
+// O = P V;  given dO:  D_t = dO_t . O_t,  dP = dO V^T,  dS = P (dP - D),
+// dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+//
+// Operands are bfloat16 head-major copies [B][H][n][hd] and transposed ones
+// [B][H][hd][nT] (nT = n rounded up to 8, zero past n), made once per layer.
+// Matrix products use v_mfma_f32_32x32x16_bf16 as the prefill attention
+// does: the product whose rows are the workgroup's own positions is taken
+// transposed (S^T = K Q^T in the query kernels, S = Q K^T in the key kernel)
+// so that each position's softmax terms sit in its two lanes, and the 16
+// inner positions of every step are permuted identically on both operands
+// (lane half g supplies positions 4g..4g+3 and 8+4g..8+4g+3), which lets
+// the second product take P or dS straight from the score registers.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kFR = 128;  // own positions per workgroup (4 waves x 32)
+constexpr int kFT = 64;   // inner positions per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bool allowed(int t, int s, int window) {
+  return s <= t && (window == 0 || t - s < window);
+}
+
+// Stage a [kFT rows][HD] tile of a head-major array (rows r0.., clamped to
+// n-1) into LDS rows of ld elements.
+template <int HD>
+__device__ __forceinline__ void stage_rows(const bf16* __restrict__ src, int n, int r0, bf16* dst, int ld) {
+  constexpr int CPK = HD / 8;
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int rr = e / CPK, c = e % CPK;
+    *(u32x4*)(dst + rr * ld + 8 * c) = *(const u32x4*)(src + (size_t)min(r0 + rr, n - 1) * HD + 8 * c);
+  }
+}
+
+// Stage the [HD][kFT] transposed tile (columns c0.., the source has nT
+// columns, zero past n) into LDS rows of ld elements, as 8-byte pieces.
+template <int HD>
+__device__ __forceinline__ void stage_cols(const bf16* __restrict__ srcT, int nT, int c0, bf16* dst, int ld) {
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int d = e >> 3, run = e & 7;
+    const int c = min(c0 + 8 * run, nT - 8);  // past the last column: zeros / unused
+    const u32x4 v = *(const u32x4*)(srcT + (size_t)d * nT + c);
+    u32x2_t* p = (u32x2_t*)(dst + d * ld + 8 * run);
+    p[0] = u32x2_t{v[0], v[1]};
+    p[1] = u32x2_t{v[2], v[3]};
+  }
+}
+
+// A operand of the second product: rows = 32 dims of block mb, the 16 inner
+// positions of step (kt, h) in the permuted order, from a transposed tile
+template <int LD>
+__device__ __forceinline__ bf16x8_t perm_frag(const bf16* tT, int mb, int kt, int h, int lr, int g) {
+  const bf16* row = tT + (mb * 32 + lr) * LD + 32 * kt + 16 * h + 4 * g;
+  const u32x2_t lo = *(const u32x2_t*)row;
+  const u32x2_t hi = *(const u32x2_t*)(row + 8);
+  const u32x4 v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  return *(const bf16x8_t*)&v;
+}
+
+// ---------------------------------------------------------------------------
+// forward: O and the softmax statistics (mst in natural-log units, lst the sum)
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
+  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32;
+  __shared__ __align__(16) bf16 Ks[kFT * KLD];
+  __shared__ __align__(16) bf16 Vt[HD * VLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+  const int nqb = (a.n + kFR - 1) / kFR;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);  // most keys first
+  const int bh = blockIdx.x / nqb, b = bh / a.nq, hq = bh % a.nq, kvh = hq * a.nkv / a.nq;
+  const int i0 = qb * kFR, iw0 = i0 + 32 * wave;
+  const int t = min(iw0 + lq, a.n - 1);
+  const bf16* Q = a.Q + ((size_t)b * a.nq + hq) * a.n * HD;
+  const bf16* K = a.K + ((size_t)b * a.nkv + kvh) * a.n * HD;
+  const bf16* VT = a.VT + ((size_t)b * a.nkv + kvh) * HD * a.nT;
+  bf16x8_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(Q + (size_t)t * HD + 16 * ks + 8 * g);
+
+  const float sl2 = a.scale * kLog2e;
+  const bool fixed_ref = sl2 <= 40.f;  // unit q, k: no score exceeds scale
+  float m = fixed_ref ? sl2 : -1e30f, l = 0.f;
+  f32x16_t acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const int hi = min(i0 + kFR - 1, a.n - 1);
+  const int lo = a.window ? max(0, i0 - a.window + 1) : 0;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  for (int s0 = lo / kFT * kFT; s0 <= hi; s0 += kFT) {
+    __syncthreads();
+    stage_rows<HD>(K, a.n, s0, Ks, KLD);
+    stage_cols<HD>(VT, a.nT, s0, Vt, VLD);
+    __syncthreads();
+    if (iw0 >= a.n || s0 > iw0 + 31) continue;
+    f32x16_t sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8_t*)(Ks + (kt * 32 + lq) * KLD + 16 * ks + 8 * g), qf[ks], sc[kt], 0, 0, 0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        sc[kt][r] = allowed(t, s, a.window) && s < a.n ? sc[kt][r] * sl2 : -INFINITY;
+        tmax = fmaxf(tmax, sc[kt][r]);
+      }
+    float mn = m;
+    if (!fixed_ref) mn = fmaxf(m, fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    float ps = 0.f;
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        bf16x2_t pr;
+        pr[0] = (__bf16)exp2f(sc[kt][r] - mn);
+        pr[1] = (__bf16)exp2f(sc[kt][r + 1] - mn);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
+        pb[kt][r >> 3][r & 7] = pr[0];
+        pb[kt][r >> 3][(r & 7) + 1] = pr[1];
+      }
+    l = l * alpha + ps;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      if (alpha != 1.f) acc[mb] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(Vt, mb, kt, h, lq, g), pb[kt][h],
+                                                            acc[mb], 0, 0, 0);
+    }
+  }
+  if (iw0 >= a.n || iw0 + lq >= a.n) return;
+  const float lt = l + __shfl_xor(l, 32, 64);
+  const float inv = 1.f / lt;
+  const size_t row = (size_t)b * a.n + t;
+  float* o = a.o + row * a.nq * HD + (size_t)hq * HD;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = acc[mb][r] * inv;
+  if (g == 0) {
+    a.mst[row * a.nq + hq] = m * 0.6931471805599453f;  // log2 -> natural units
+    a.lst[row * a.nq + hq] = lt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 128 queries of one (sequence, q head)
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256, 1) void k_bwf_dq(BwFlash a) {
+  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32;
+  __shared__ __align__(16) bf16 Ks[kFT * KLD];
+  __shared__ __align__(16) bf16 Vs[kFT * KLD];
+  __shared__ __align__(16) bf16 KTs[HD * VLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, g = lane >> 5;
+  const int nqb = (a.n + kFR - 1) / kFR;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+  const int bh = blockIdx.x / nqb, b = bh / a.nq, hq = bh % a.nq, kvh = hq * a.nkv / a.nq;
+  const int i0 = qb * kFR, iw0 = i0 + 32 * wave;
+  const int t = min(iw0 + lq, a.n - 1);
+  const size_t qoff = ((size_t)b * a.nq + hq) * a.n * HD;
+  const bf16* K = a.K + ((size_t)b * a.nkv + kvh) * a.n * HD;
+  const bf16* V = a.V + ((size_t)b * a.nkv + kvh) * a.n * HD;
+  const bf16* KT = a.KT + ((size_t)b * a.nkv + kvh) * HD * a.nT;
+  bf16x8_t qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = *(const bf16x8_t*)(a.Q + qoff + (size_t)t * HD + 16 * ks + 8 * g);
+    df[ks] = *(const bf16x8_t*)(a.dO + qoff + (size_t)t * HD + 16 * ks + 8 * g);
+  }
+  const size_t row = (size_t)b * a.n + t;
+  const float sl2 = a.scale * kLog2e;
+  const float m2 = a.mst[row * a.nq + hq] * kLog2e, il = 1.f / a.lst[row * a.nq + hq];
+  const float Dt = a.D[row * a.nq + hq];
+  f32x16_t acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const int hi = min(i0 + kFR - 1, a.n - 1);
+  const int lo = a.window ? max(0, i0 - a.window + 1) : 0;
+  for (int s0 = lo / kFT * kFT; s0 <= hi; s0 += kFT) {
+    __syncthreads();
+    stage_rows<HD>(K, a.n, s0, Ks, KLD);
+    stage_rows<HD>(V, a.n, s0, Vs, KLD);
+    stage_cols<HD>(KT, a.nT, s0, KTs, VLD);
+    __syncthreads();
+    if (iw0 >= a.n || s0 > iw0 + 31) continue;
+    f32x16_t sc[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kt][r] = dp[kt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (kt * 32 + lq) * KLD + 16 * ks + 8 * g;
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ks + o), qf[ks], sc[kt], 0, 0, 0);
+        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Vs + o), df[ks], dp[kt], 0, 0, 0);
+      }
+    }
+    bf16x8_t db[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float p = allowed(t, s, a.window) && s < a.n ? exp2f(fmaf(sc[kt][r], sl2, -m2)) * il : 0.f;
+        db[kt][r >> 3][r & 7] = (__bf16)(p * (dp[kt][r] - Dt));
+      }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(KTs, mb, kt, h, lq, g), db[kt][h],
+                                                            acc[mb], 0, 0, 0);
+  }
+  if (iw0 >= a.n || iw0 + lq >= a.n) return;
+  float* dq = a.dq + row * a.nq * HD + (size_t)hq * HD;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = a.scale * acc[mb][r];
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys of one (sequence, kv head), summed over
+// the G query heads of the group and every query that sees those keys
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
+  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32;
+  __shared__ __align__(16) bf16 Qs[kFT * KLD];
+  __shared__ __align__(16) bf16 Ds_[kFT * KLD];
+  __shared__ __align__(16) bf16 QTs[HD * VLD];
+  __shared__ __align__(16) bf16 DTs[HD * VLD];
+  __shared__ float m2s[kFT], ils[kFT], Dq[kFT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lk = lane & 31, g = lane >> 5;
+  const int nkb = (a.n + kFR - 1) / kFR;
+  const int kb = (int)(blockIdx.x % nkb);
+  const int bh = blockIdx.x / nkb, b = bh / a.nkv, kvh = bh % a.nkv;
+  const int G = a.nq / a.nkv;
+  const int k0 = kb * kFR, kw0 = k0 + 32 * wave;
+  const int s = min(kw0 + lk, a.n - 1);
+  const size_t koff = ((size_t)b * a.nkv + kvh) * a.n * HD;
+  bf16x8_t kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kf[ks] = *(const bf16x8_t*)(a.K + koff + (size_t)s * HD + 16 * ks + 8 * g);
+    vf[ks] = *(const bf16x8_t*)(a.V + koff + (size_t)s * HD + 16 * ks + 8 * g);
+  }
+  const float sl2 = a.scale * kLog2e;
+  f32x16_t ak[NMB], av[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ak[mb][r] = av[mb][r] = 0.f;
+  const int khi = min(k0 + kFR - 1, a.n - 1);
+  const int qlo = k0, qhi = a.window ? min(a.n - 1, khi + a.window - 1) : a.n - 1;
+  for (int h = 0; h < G; ++h) {
+    const int hq = kvh * G + h;
+    const size_t qoff = ((size_t)b * a.nq + hq) * a.n * HD;
+    const bf16* QT = a.QT + ((size_t)b * a.nq + hq) * HD * a.nT;
+    const bf16* DT = a.dOT + ((size_t)b * a.nq + hq) * HD * a.nT;
+    for (int q0 = qlo / kFT * kFT; q0 <= qhi; q0 += kFT) {
+      __syncthreads();
+      stage_rows<HD>(a.Q + qoff, a.n, q0, Qs, KLD);
+      stage_rows<HD>(a.dO + qoff, a.n, q0, Ds_, KLD);
+      stage_cols<HD>(QT, a.nT, q0, QTs, VLD);
+      stage_cols<HD>(DT, a.nT, q0, DTs, VLD);
+      if (tid < kFT) {
+        const size_t r = (size_t)b * a.n + min(q0 + tid, a.n - 1);
+        m2s[tid] = a.mst[r * a.nq + hq] * kLog2e;
+        ils[tid] = 1.f / a.lst[r * a.nq + hq];
+        Dq[tid] = a.D[r * a.nq + hq];
+      }
+      __syncthreads();
+      // queries of the tile that see some key of this wave
+      if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
+      f32x16_t sc[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qt][r] = dp[qt][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int o = (qt * 32 + lk) * KLD + 16 * ks + 8 * g;
+          sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Qs + o), kf[ks], sc[qt], 0, 0, 0);
+          dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ds_ + o), vf[ks], dp[qt], 0, 0, 0);
+        }
+      }
+      bf16x8_t pb[2][2], db[2][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int t = q0 + qi;
+          const float p =
+              allowed(t, s, a.window) && t < a.n ? exp2f(fmaf(sc[qt][r], sl2, -m2s[qi])) * ils[qi] : 0.f;
+          pb[qt][r >> 3][r & 7] = (__bf16)p;
+          db[qt][r >> 3][r & 7] = (__bf16)(p * (dp[qt][r] - Dq[qi]));
+        }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            av[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(DTs, mb, qt, hh, lk, g), pb[qt][hh],
+                                                             av[mb], 0, 0, 0);
+            ak[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(QTs, mb, qt, hh, lk, g), db[qt][hh],
+                                                             ak[mb], 0, 0, 0);
+          }
+    }
+  }
+  if (kw0 >= a.n || kw0 + lk >= a.n) return;
+  const size_t row = (size_t)b * a.n + s;
+  float* dk = a.dk + row * a.nkv * HD + (size_t)kvh * HD;
+  float* dv = a.dv + row * a.nkv * HD + (size_t)kvh * HD;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+      dk[d] = a.scale * ak[mb][r];
+      dv[d] = av[mb][r];
+    }
+}
+
+// bfloat16 transposed head copies: dst[b][h][d][t] (nT columns, zero past n)
+// from float32 rows src[(b n + t) ld + off + h hd + d]; one thread per element,
+// t fastest
+__global__ __launch_bounds__(256) void k_bwf_heads_t(const float* __restrict__ src, int64_t ld, int off, int H,
+                                                     int hd, int n, int nT, int64_t total, bf16* __restrict__ dst) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int t = (int)(e % nT);
+  const int64_t r = e / nT;  // (b, h, d)
+  const int d = (int)(r % hd);
+  const int64_t bh = r / hd;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  dst[e] = t < n ? from_f<bf16>(src[(b * n + t) * ld + off + (int64_t)h * hd + d]) : (bf16)0;
+}
+
+}  // namespace
+
+bool bw_flash_supported(int dtype, int hd, int nq, int nkv) {
+  return dtype == 1 && (hd == 64 || hd == 128) && nkv > 0 && nq % nkv == 0;
+}
+
+hipError_t launch_bw_heads_t(const float* src, int64_t ld, int off, int H, int hd, int n, int B, int nT, void* dst,
+                             hipStream_t st) {
+  const int64_t total = (int64_t)B * H * hd * nT;
+  if (total <= 0) return hipSuccess;
+  if (nT < n || nT % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwf_heads_t, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, ld, off, H, hd, n,
+                     nT, total, (bf16*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_flash_fwd(const BwFlash& a, hipStream_t st) {
+  if (a.B * a.n <= 0) return hipSuccess;
+  if (!bw_flash_supported(1, a.hd, a.nq, a.nkv) || a.nT < a.n || a.nT % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n + kFR - 1) / kFR * a.B * a.nq));
+  if (a.hd == 64)
+    hipLaunchKernelGGL(k_bwf_fwd<64>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_bwf_fwd<128>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_flash_bwd(const BwFlash& a, hipStream_t st) {
+  if (a.B * a.n <= 0) return hipSuccess;
+  if (!bw_flash_supported(1, a.hd, a.nq, a.nkv) || a.nT < a.n || a.nT % 8) return hipErrorInvalidValue;
+  const dim3 gq((unsigned)((a.n + kFR - 1) / kFR * a.B * a.nq)), gk((unsigned)((a.n + kFR - 1) / kFR * a.B * a.nkv));
+  if (a.hd == 64) {
+    hipLaunchKernelGGL(k_bwf_dq<64>, gq, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_bwf_dkv<64>, gk, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_bwf_dq<128>, gq, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_bwf_dkv<128>, gk, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dory

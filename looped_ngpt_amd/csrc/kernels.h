@@ -240,6 +240,27 @@ struct BwAttn {
   int window;        // 0: full causal
   float scale;
 };
+// Matrix-core attention of the backward (bfloat16 models, hd 64 / 128):
+// head-major bfloat16 operand copies Q, K, V, dO [B][H][n][hd] and
+// transposed ones QT, KT, VT, dOT [B][H][hd][nT] (nT = n rounded up to 8,
+// zero past n); softmax statistics mst / lst and D [B*n][nq] (float32); o,
+// dq [B*n][nq*hd] and dk, dv [B*n][nkv*hd] float32 rows.
+struct BwFlash {
+  const uint16_t *Q, *K, *V, *dO, *QT, *KT, *VT, *dOT;
+  int B, n, nT, nq, nkv, hd, window;  // window 0: full causal
+  float scale;
+  float *mst, *lst;
+  const float* D;
+  float *o, *dq, *dk, *dv;
+};
+bool bw_flash_supported(int dtype, int hd, int nq, int nkv);
+// dst [B][H][hd][nT] bfloat16 (zero past n) from float32 rows src[(b n + t) ld + off + h hd + d]
+hipError_t launch_bw_heads_t(const float* src, int64_t ld, int off, int H, int hd, int n, int B, int nT, void* dst,
+                             hipStream_t st);
+// o, mst, lst from Q, K, VT
+hipError_t launch_bw_flash_fwd(const BwFlash& a, hipStream_t st);
+// dq from Q, dO, K, V, KT; dk, dv from K, V, Q, dO, QT, dOT (and mst, lst, D)
+hipError_t launch_bw_flash_bwd(const BwFlash& a, hipStream_t st);
 hipError_t launch_bw_cast(int dt_out, const float* in, void* out, int64_t n, hipStream_t st);
 hipError_t launch_bw_transpose(int dt, const void* in, int64_t ld, void* out, int R, int C, hipStream_t st);
 hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
@@ -265,14 +286,9 @@ hipError_t launch_bw_gate_bwd(const float* doh, const float* oh, const float* rc
                               hipStream_t st);
 hipError_t launch_bw_attn_bwd(const BwAttn& a, int M, const float* dO, const float* o, const float* mst,
                               const float* lst, float* D, float* dqn, float* dkn, float* dv, hipStream_t st);
-// attention of the backward through batched GEMMs (bfloat16): layouts and rows
+// dst [B][H][n][hd] (dt: 0 float32, 1 bfloat16) from float32 rows src[(b n + t) ld + off + h hd + d]
 hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int H, int hd, int n, int B, void* dst,
                               hipStream_t st);
-hipError_t launch_bw_from_heads(const float* src, int H, int hd, int n, int B, float* dst, hipStream_t st);
-hipError_t launch_bw_softmax_rows(const float* S, int64_t rows, int n, int window, void* P, hipStream_t st);
-// dS = P (dP - D) over P; window 0: causal only (P is 0 outside the allowed keys)
-hipError_t launch_bw_dsoft_rows(const float* dP, void* P, const float* D, int64_t rows, int n, int window, int G,
-                                int nq, int nkv, hipStream_t st);
 hipError_t launch_bw_attn_D(const float* dO, const float* o, int nq, int hd, int M, float* D, hipStream_t st);
 hipError_t launch_bw_rope_norm_bwd(const float* dqn, const float* qn, const float* rq, const float* dkn,
                                    const float* kn, const float* rk, const float* dv, const float2* tab, int n, int nq,

@@ -183,6 +183,18 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   w.TA = take(M * std::max(Q, std::max(2 * F, d)) * el);
   w.TB = take(M * std::max(d, std::max(F, qd)) * el);
   w.WT = take(std::max(std::max(Q * d, 2 * F * d), std::max(d * qd, d * F)) * el);
+  if (c.dtype == DORY_BF16) {
+    w.nT = (n + 7) / 8 * 8;
+    const size_t rowsT = (size_t)B * w.nT;
+    w.fQ = take(M * qd * 2);
+    w.fdO = take(M * qd * 2);
+    w.fK = take(M * kvd * 2);
+    w.fV = take(M * kvd * 2);
+    w.fQT = take(rowsT * qd * 2);
+    w.fdOT = take(rowsT * qd * 2);
+    w.fKT = take(rowsT * kvd * 2);
+    w.fVT = take(rowsT * kvd * 2);
+  }
   // one layer's forward values
   const size_t g0 = at;
   w.P1 = take(M * Q * 4);

@@ -87,6 +87,10 @@ struct BwLayout {
   size_t dO = 0, D = 0, dqn = 0, dkn = 0, dv = 0, dP1 = 0;
   size_t xb = 0, ohb = 0, h1b = 0, ab = 0, dyb = 0, dP2b = 0, dP1b = 0;  // T
   size_t TA = 0, TB = 0, WT = 0;                    // T: transposed operands of the gradient GEMMs
+  // matrix-core attention (bfloat16 models): head-major operand copies
+  // [B][H][n][hd] and transposed [B][H][hd][nT] (bfloat16), remade per layer
+  size_t fQ = 0, fK = 0, fV = 0, fdO = 0, fQT = 0, fKT = 0, fVT = 0, fdOT = 0;
+  int nT = 0;
   // The values a layer's backward reads from its forward (P1 .. rz2 above
   // but y, and the T copies xb .. ab) sit in one group at the end
   // of the layout, layer_bytes long; with every layer's group kept
