@@ -1,0 +1,581 @@
+// Matrix-core GEMMs y = x . W^T for the projections of the looped nGPT at
+// more than 8 rows (prefill chunks, batched decode, the backward's gradient
+// products). x is [M][K] (row stride ldx), W is [N][K] (row-major, the
+// nn.Linear layout), y is [M][N] float32, or [M][N/2] in the model dtype with
+// the SwiGLU epilogue (rows o and N/2 + o of W are the up and gate rows of
+// output o; y = u * silu(v)).
+//
+//  * k_gemm_big: M >= 1024, bfloat16, K % 64 == 0. 256 x BN workgroup tiles
+//    (BN 256 or 192) on v_mfma_f32_32x32x16_bf16, direct global->LDS loads
+//    into a three / two slot ring, XCD-aware tile order.
+//  * k_gemm_skinny: 9..64 rows (batched decode), weight-stream bound.
+//  * k_gemm_mfma: the remaining bfloat16 shapes, 128 x 128 tiles.
+//  * k_gemm_simple: float32 models and unaligned shapes.
+#include "common.h"
+#include "kernels.h"
+#include "linear_common.h"
+
+namespace dory {
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM (bfloat16 in, float32 accumulate)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;  // 144-byte LDS rows
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, int64_t lda,
+                                                  const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
+                                                  int K, float scale) {
+  __shared__ __align__(16) bf16 As[GBM * GLD];
+  __shared__ __align__(16) bf16 Bs[GBN * GLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * GBM;
+  const int F = N / 2;
+  const int n0 = EPI == EPI_SWIGLU ? blockIdx.x * (GBN / 2) : blockIdx.x * GBN;
+
+  // each thread moves 4 x 16 B of A and of B per K tile
+  int arow[4], brow[4], col8[4];
+  bool aok[4], bok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3;
+    col8[i] = (c & 7) * 8;
+    arow[i] = m0 + r;
+    aok[i] = arow[i] < M;
+    int br;
+    if (EPI == EPI_SWIGLU) {
+      const int nb = r >> 5;
+      const int o = n0 + (nb >> 1) * 32 + (r & 31);
+      bok[i] = o < F;
+      br = (nb & 1 ? F : 0) + o;
+    } else {
+      br = n0 + r;
+      bok[i] = br < N;
+    }
+    brow[i] = br;
+  }
+  uint4 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + col8[i];
+      const bool kin = k < K;
+      ra[i] = (aok[i] && kin) ? *(const uint4*)(A + (size_t)arow[i] * lda + k) : make_uint4(0, 0, 0, 0);
+      rb[i] = (bok[i] && kin) ? *(const uint4*)(B + (size_t)brow[i] * K + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid + 256 * i) >> 3;
+      *(uint4*)(As + r * GLD + col8[i]) = ra[i];
+      *(uint4*)(Bs + r * GLD + col8[i]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  for (int k0 = 0; k0 < K; k0 += GBK) {
+    const bool more = k0 + GBK < K;
+    if (more) gload(k0 + GBK);
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8_t*)(As + (wm * 64 + i * 32 + lr) * GLD + ks * 16 + lk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(Bs + (wn * 64 + j * 32 + lr) * GLD + ks * 16 + lk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= M) continue;
+      if (EPI == EPI_SWIGLU) {
+        const int o = n0 + wn * 32 + lr;
+        if (o < F) ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * scale * silu_(acc[i][1][r] * scale));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + lr;
+          if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large-M prefill GEMM: 256 x BN workgroup tiles (BN = 256, or 192 where 256
+// would leave the last round of workgroups half empty, e.g. N = 3072), four
+// waves (one per SIMD) in a 2 x 2 grid of 128 x BN/2, so every LDS fragment
+// feeds BN/64 (A) or 4 (B) matrix-core products. The 4 x BN/64 accumulator
+// blocks of v_mfma_f32_32x32x16_bf16 (256 floats per lane at BN = 256) live
+// in the accumulation registers.
+//
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4:
+// lane l of a wave's load writes bytes 16l..16l+15 of a 1 KB block). A stage
+// is 64 deep in K, so a load covers 8 tile rows x 128 B — whole cache lines
+// (16 rows x 64 B per load, a 32-deep stage, streamed measurably slower).
+// Inside a row the 16-byte chunks are XOR-swizzled by (row/2)%8, which makes
+// the 16-lane groups of the fragment reads hit distinct banks (no bank
+// conflicts by the counters). The 160 KB of LDS hold A in a three-slot ring
+// and B in a two-slot ring: the loads of A for stage kt+2 go out in three
+// pieces during stage kt, those of B for stage kt+2 right after the barrier
+// that ends stage kt (the slot that stage kt's B used is then free: its last
+// 16-deep slice is already in registers), so every load has one to two
+// stages of matrix work to land. One workgroup barrier per stage, after an
+// explicit vmcnt wait for stage kt+1 (A of stage kt+2 stays in flight).
+// Within a stage the fragments of the next 16-deep slice are read while the
+// current one is multiplied, one LDS read (or global load) issued after each
+// product (sched_group_barrier), so neither unit sees bursts.
+//
+// Workgroups are spread over the 8 XCDs in contiguous runs of tiles, grouped
+// four M tiles at a time, so the tiles that run together on one XCD share A
+// and B rows in its L2. SwiGLU (BN = 256 only): B tile rows come in 32-row
+// chunks u, v, u, v of the same outputs, and a wave's blocks (0, 1) and
+// (2, 3) are (u, v) pairs. Requires K % 64 == 0 and 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
+#define DORY_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt lgkmcnt(0) and no wait on the other counters
+#define DORY_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
+// sched_group_barrier masks
+#define DORY_SG_MFMA 0x008
+#define DORY_SG_VMEM_RD 0x020
+#define DORY_SG_DS_RD 0x100
+
+constexpr int kBigBK = 64;      // K per stage
+constexpr int kBigGroupM = 4;
+constexpr int kBigLds = 160 * 1024;
+
+// 16 bytes per lane from global memory straight into LDS (a wave fills dst ..
+// dst + 1023). A plain device function: called directly from a lambda of a
+// kernel template, the builtin made host compilation drop its callers.
+__device__ __forceinline__ void lds_load16(const bf16* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// byte offset of 16-byte chunk c (K elements 8c..8c+7) of tile row r in a stage
+__device__ __forceinline__ int big_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) void k_gemm_big(const bf16* __restrict__ A, int64_t lda,
+                                                  const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
+                                                  int K, float scale) {
+  static_assert(BN == 256 || (BN == 192 && EPI == EPI_F32), "tile widths");
+  constexpr int NJ = BN / 64;          // 32-column blocks per wave
+  constexpr int kHA = 256 * 128;       // A bytes per stage (32 KB)
+  constexpr int kHB = BN * 128;        // B bytes per stage (32 or 24 KB)
+  constexpr int kLA = kHA / 4096;      // 1 KB loads per wave per stage: A 8, B 8 or 6
+  constexpr int kLB = kHB / 4096;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  unsigned char* const sA = smem;             // 3 x kHA
+  unsigned char* const sB = smem + 3 * kHA;   // 2 x kHB
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;  // rows wm*128, columns wn*BN/2 of the tile
+  const int F = N / 2;
+  const int nM = (M + 255) / 256;
+  const int nN = EPI == EPI_SWIGLU ? (F + 127) / 128 : (N + BN - 1) / BN;
+  const int nt = nM * nN;
+  const int per = (nt + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= nt) return;
+  const int grp = t / (kBigGroupM * nN);
+  const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
+  const int loc = t - grp * kBigGroupM * nN;
+  const int m0 = (grp * kBigGroupM + loc % gs) * 256;
+  const int n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * BN;
+
+  // this lane's source rows (clamped: rows past M or N load a valid row and
+  // are never stored); load i of a wave fills tile rows 8 (wave kL + i) + 0..7
+  const int lr = lane >> 3, ls = lane & 7;
+  const bf16* srcA[kLA];
+  const bf16* srcB[kLB];
+#pragma unroll
+  for (int i = 0; i < kLA; ++i) {
+    const int r = (wave * kLA + i) * 8 + lr;
+    srcA[i] = A + (size_t)min(m0 + r, M - 1) * lda + (ls ^ ((r >> 1) & 7)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < kLB; ++i) {
+    const int r = (wave * kLB + i) * 8 + lr;
+    int wr;
+    if (EPI == EPI_SWIGLU) {
+      const int nb = r >> 5;
+      const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
+      wr = (nb & 1 ? F : 0) + o;
+    } else {
+      wr = min(n0 + r, N - 1);
+    }
+    srcB[i] = B + (size_t)wr * K + (ls ^ ((r >> 1) & 7)) * 8;
+  }
+  auto issueA = [&](int kt, int i0, int i1) {
+    unsigned char* st = sA + (kt % 3) * kHA;
+#pragma unroll
+    for (int i = i0; i < i1; ++i) lds_load16(srcA[i] + kt * kBigBK, st + (wave * kLA + i) * 1024);
+  };
+  auto issueB = [&](int kt) {
+    unsigned char* st = sB + (kt & 1) * kHB;
+#pragma unroll
+    for (int i = 0; i < kLB; ++i) lds_load16(srcB[i] + kt * kBigBK, st + (wave * kLB + i) * 1024);
+  };
+
+  f32x16_t acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nK = K / kBigBK;
+  const int l32 = lane & 31, lh = lane >> 5;
+  // fragments of 16-deep K slice ks (0..3) of stage kt
+  auto frag = [&](int kt, int ks, bf16x8_t (&fa)[4], bf16x8_t (&fb)[NJ]) {
+    const unsigned char* a = sA + (kt % 3) * kHA;
+    const unsigned char* b = sB + (kt & 1) * kHB;
+    const int c = ks * 2 + lh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(a + big_off(wm * 128 + i * 32 + l32, c));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[j] = *(const bf16x8_t*)(b + big_off(wn * (BN / 2) + j * 32 + l32, c));
+  };
+  auto mma = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  bf16x8_t fa[2][4], fb[2][NJ];
+  // prologue: A and B of stages 0 and 1
+  issueA(0, 0, kLA);
+  issueB(0);
+  if (nK > 1) {
+    issueA(1, 0, kLA);
+    issueB(1);
+    DORY_WAIT_VM(kLA + kLB);
+  } else {
+    DORY_WAIT_VM(0);
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  frag(0, 0, fa[0], fb[0]);
+  DORY_WAIT_LGKM0();
+  for (int kt = 0; kt < nK; ++kt) {
+    const bool moreA = kt + 2 < nK;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) {
+        // a third of A(kt+2) into the A slot stage kt-1 used; fragments of slice s+1
+        constexpr int c0[3] = {0, kLA / 3, 2 * kLA / 3}, c1[3] = {kLA / 3, 2 * kLA / 3, kLA};
+        if (moreA) issueA(kt + 2, c0[s], c1[s]);
+        frag(kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        mma(fa[s & 1], fb[s & 1]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_VMEM_RD, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4 + NJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 4 * NJ - 7 - NJ, 0);
+      } else {
+        // stage kt+1 complete (A of stage kt+2 may stay in flight), then B of
+        // stage kt+2 into the B slot stage kt used, fragments of stage kt+1
+        if (moreA) DORY_WAIT_VM(kLA); else DORY_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 2 < nK) issueB(kt + 2);
+        frag(kt + 1, 0, fa[0], fb[0]);  // unconditional (past the last stage: a stale slot, unused): exact waits
+        mma(fa[1], fb[1]);
+#pragma unroll
+        for (int q = 0; q < kLB; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_VMEM_RD, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4 + NJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(DORY_SG_DS_RD, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the fragment reads are done long before the products are: waiting
+      // here lets the next slice's products start without a wait
+      DORY_WAIT_LGKM0();
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (row >= M) continue;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int jp = 0; jp < NJ / 2; ++jp) {
+          const int o = n0 + wn * 64 + jp * 32 + l32;
+          if (o < F)
+            ((bf16*)C)[(size_t)row * F + o] =
+                from_f<bf16>(acc[i][2 * jp][r] * scale * silu_(acc[i][2 * jp + 1][r] * scale));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int col = n0 + wn * (BN / 2) + j * 32 + l32;
+          if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
+        }
+      }
+    }
+  }
+}
+
+// LDS bytes of k_gemm_big (three A slots and two B slots of one stage)
+static constexpr uint32_t big_lds(int bn) { return 3 * 256 * 128 + 2 * bn * 128; }
+
+// k_gemm_big<EPI, BN> with its dynamic LDS above the 64 KB default allowed
+// (set once per process)
+template <int EPI, int BN>
+static void big_launch(dim3 grid, const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                       hipStream_t st) {
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_big<EPI, BN>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)big_lds(BN));
+  (void)attr;
+  dory_launch((k_gemm_big<EPI, BN>), grid, dim3(256), big_lds(BN), st, x, ldx, W, y, M, N, K, scale);
+}
+
+// tile width for a large-M GEMM with N outputs: 192 when 256-wide tiles would
+// leave the last round of workgroups (one per CU) at most half full and
+// 192-wide ones do better
+static int big_tile_n(int M, int N) {
+  auto eff = [&](int bn) {
+    const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+    const long rounds = (tiles + kNumCUs - 1) / kNumCUs;
+    return (double)tiles / (double)(rounds * kNumCUs) * (bn == 256 ? 1.0 : 0.93);  // 192: more LDS reads per FLOP
+  };
+  return eff(192) > eff(256) ? 192 : 256;
+}
+
+// ---------------------------------------------------------------------------
+// Batched-decode GEMM (9..64 rows): weight-stream bound. A workgroup owns 16
+// outputs (16 weight rows; SwiGLU: those 16 u rows and the 16 matching v
+// rows) and all M rows; its four waves split K in quarters. With
+// v_mfma_f32_16x16x32_bf16 lane l supplies row l%16 of a 16-row block and K
+// elements 8(l/16)..8(l/16)+7 of each 32-deep step, so every operand
+// fragment is one 16-byte load straight from global memory (the weights
+// stream once, the activations come from L2); four steps of loads are issued
+// before their products. The quarters are summed through LDS. Rows past M
+// and outputs past N are clamped loads whose results are dropped. Requires
+// K % 128 == 0 and 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSkU = 4;  // K steps of 32 whose loads are issued together
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X, int64_t ldx,
+                                                     const bf16* __restrict__ W, void* __restrict__ C, int M, int N,
+                                                     int K, float scale) {
+  constexpr int NB = MB / 16;                  // 16-row blocks of X
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;  // weight blocks (u, v)
+  __shared__ f32x4_t part[4][NR][NB][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int o0 = blockIdx.x * 16;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int kper = K / 4, kb = wave * kper;
+  const bf16* wp[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) wp[j] = W + (size_t)((j ? nout : 0) + min(o0 + r16, nout - 1)) * K + kb + kq;
+  const bf16* xp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) xp[b] = X + (size_t)min(b * 16 + r16, M - 1) * ldx + kb + kq;
+  f32x4_t acc[NR][NB];
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kper; k += 32 * kSkU) {
+    bf16x8_t wf[kSkU][NR], xf[kSkU][NB];
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      const int kk = min(k + 32 * u, kper - 32);  // past the quarter: a re-read, not multiplied
+#pragma unroll
+      for (int j = 0; j < NR; ++j) wf[u][j] = __builtin_nontemporal_load((const bf16x8_t*)(wp[j] + kk));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xf[u][b] = *(const bf16x8_t*)(xp[b] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      if (k + 32 * u >= kper) break;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][b], wf[u][j], acc[j][b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part[wave][j][b][lane] = acc[j][b];
+  __syncthreads();
+  // output (row m, column n) of block b: lane n + 16 (m%16 / 4), register m % 4
+  for (int e = tid; e < MB * 16; e += 256) {
+    const int m = e >> 4, n = e & 15;
+    const int b = m >> 4, ln = n + 16 * ((m & 15) >> 2), r = m & 3;
+    float s[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) s[j] = part[0][j][b][ln][r] + part[1][j][b][ln][r] + part[2][j][b][ln][r] +
+                                        part[3][j][b][ln][r];
+    if (m >= M || o0 + n >= nout) continue;
+    if (EPI == EPI_SWIGLU)
+      ((bf16*)C)[(size_t)m * nout + o0 + n] = from_f<bf16>(s[0] * scale * silu_(s[1] * scale));
+    else
+      ((float*)C)[(size_t)m * N + o0 + n] = s[0] * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Simple tiled GEMM for float32 models and ragged shapes: 64x64 tiles, each
+// thread a 4x4 block, K in steps of 16 through LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_simple(const T* __restrict__ A, int64_t lda, const T* __restrict__ B,
+                                                    void* __restrict__ C, int M, int N, int K, float scale) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[2][16][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  float acc[2][4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int rr = e >> 4, kk = e & 15;
+      const int gm = m0 + rr, gn = n0 + rr, gk = k0 + kk;
+      As[kk][rr] = (gm < M && gk < K) ? to_f(A[(size_t)gm * lda + gk]) : 0.f;
+      Bs[0][kk][rr] = (gn < nout && gk < K) ? to_f(B[(size_t)gn * K + gk]) : 0.f;
+      if (EPI == EPI_SWIGLU) Bs[1][kk][rr] = (gn < nout && gk < K) ? to_f(B[(size_t)(nout + gn) * K + gk]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b0[j] = Bs[0][kk][tx * 4 + j];
+        b1[j] = EPI == EPI_SWIGLU ? Bs[1][kk][tx * 4 + j] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[0][i][j] = fmaf(a[i], b0[j], acc[0][i][j]);
+          if (EPI == EPI_SWIGLU) acc[1][i][j] = fmaf(a[i], b1[j], acc[1][i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= nout) continue;
+      if (EPI == EPI_SWIGLU)
+        ((T*)C)[(size_t)row * nout + col] = from_f<T>(acc[0][i][j] * scale * silu_(acc[1][i][j] * scale));
+      else
+        ((float*)C)[(size_t)row * N + col] = acc[0][i][j] * scale;
+    }
+  }
+}
+
+template <typename T, int EPI>
+static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, int M, int N, int K, float scale,
+                                hipStream_t st) {
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const bool al16 = ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0);
+  if (sizeof(T) == 2 && al16 && K % kBigBK == 0 && M >= 1024) {
+    const int bn = EPI == EPI_SWIGLU ? 256 : big_tile_n(M, N);
+    const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + bn - 1) / bn);
+    if (bn == 192)
+      big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+    else
+      big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+  } else if (sizeof(T) == 2 && al16 && K % 128 == 0 && M <= 64) {
+    const dim3 grid((nout + 15) / 16);
+    if (M <= 16)
+      dory_launch((k_gemm_skinny<16, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
+    else if (M <= 32)
+      dory_launch((k_gemm_skinny<32, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
+    else
+      dory_launch((k_gemm_skinny<64, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                  scale);
+  } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
+    const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
+    dim3 grid(nt, (M + GBM - 1) / GBM);
+    dory_launch((k_gemm_mfma<EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
+                       scale);
+  } else {
+    dim3 grid((nout + 63) / 64, (M + 63) / 64);
+    dory_launch((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K, int epi,
+                       float scale, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (dtype == 0)
+    return epi == EPI_SWIGLU ? gemm_dispatch<float, EPI_SWIGLU>((const float*)x, ldx, (const float*)W, y, M, N, K, scale, st)
+                             : gemm_dispatch<float, EPI_F32>((const float*)x, ldx, (const float*)W, y, M, N, K, scale, st);
+  return epi == EPI_SWIGLU ? gemm_dispatch<bf16, EPI_SWIGLU>((const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st)
+                           : gemm_dispatch<bf16, EPI_F32>((const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+}
+
+}  // namespace dory

@@ -178,9 +178,12 @@ bool linear_attn_supported(int M, int K);
 hipError_t launch_linear_lowbit_attn(int fmt, const AttnX& ax, const void* Wq, const void* Ws, float* y, int M, int N,
                                      int K, float scale, hipStream_t st);
 
-// y = x . W^T (see dory_op_linear).
+// y = x . W^T (see dory_op_linear): GEMVs up to 8 rows (algo 0), else launch_gemm.
 hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K,
                          int epi, float scale, int algo, hipStream_t st);
+// the matrix-core GEMMs of launch_linear (any M; meant for M > 8)
+hipError_t launch_gemm(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K, int epi,
+                       float scale, hipStream_t st);
 
 // Decode GEMV whose input row is produced in its own prologue: every
 // workgroup first issues its weight loads, then computes for each of the M
