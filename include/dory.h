@@ -144,7 +144,12 @@ typedef struct dory_ctx dory_ctx;
 
 /* ---- host-only queries (no HIP call; usable without a GPU) -------------- */
 
-/* DORY_OK if the config is consistent and within the kernels' limits. */
+/* DORY_OK if the config is consistent and within the kernels' limits:
+ * d_model <= 65536, d_ff <= 262144, n_q_heads <= 1024, vocab <= 2^26, at most
+ * 4096 layers per block, max_batch <= 2^20, max_ctx <= 2^26, max_loops <= 64,
+ * max_batch * n_kv_heads * head_dim * 2 * (max_ctx + 32) <= 2^40 (one cache),
+ * finite attn_scale, logit_scale and combine weights. The layer_is_full array
+ * is read only after the layer counts have passed these checks. */
 dory_status dory_validate_config(const dory_config* cfg);
 
 /* Bytes of the KV buffer for a kv mode. kv_loops is the number of per-loop

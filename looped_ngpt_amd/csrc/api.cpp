@@ -1131,13 +1131,15 @@ dory_status dory_op_linear_mx(const void* x, int64_t ldx, const void* codes, con
 
 size_t dory_backward_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t n) {
   Plan p;
-  if (!cfg || batch < 1 || n < 1 || make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  if (!cfg || batch < 1 || n < 1 || (int64_t)batch * n > kMaxBwRows || make_plan(cfg, &p, nullptr) != DORY_OK)
+    return 0;
   return make_bw_layout(p, batch, n, true).total;
 }
 
 size_t dory_backward_workspace_min_bytes(const dory_config* cfg, int32_t batch, int32_t n) {
   Plan p;
-  if (!cfg || batch < 1 || n < 1 || make_plan(cfg, &p, nullptr) != DORY_OK) return 0;
+  if (!cfg || batch < 1 || n < 1 || (int64_t)batch * n > kMaxBwRows || make_plan(cfg, &p, nullptr) != DORY_OK)
+    return 0;
   return make_bw_layout(p, batch, n, false).total;
 }
 
@@ -1150,7 +1152,7 @@ dory_status dory_backward_last_loop(dory_ctx* c, const float* x, const float* gr
     return set_err(c, DORY_E_ARG, "backward: bad arguments");
   if (C.weight_format != DORY_WEIGHTS_DTYPE || (C.head_dim != 64 && C.head_dim != 128) || C.n_rec < 1)
     return set_err(c, DORY_E_ARG, "backward: needs dtype weights, head_dim 64 or 128 and a recurrent block");
-  if ((int64_t)batch * n > (1 << 21)) return set_err(c, DORY_E_ARG, "backward: batch * n too large");
+  if ((int64_t)batch * n > kMaxBwRows) return set_err(c, DORY_E_ARG, "backward: batch * n too large");
   if (!g->qkvg || !g->o || !g->ug || !g->down || !g->alpha_attn || !g->alpha_mlp)
     return set_err(c, DORY_E_ARG, "backward: null gradient array");
   for (int i = 0; i < C.n_rec; ++i)

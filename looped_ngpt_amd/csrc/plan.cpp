@@ -25,8 +25,12 @@ dory_status make_plan(const dory_config* c, Plan* p, std::string* why) {
   if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
       c->d_ff <= 0 || c->vocab <= 0)
     return fail(why, "model sizes must be positive");
-  if (c->n_in < 0 || c->n_rec < 0 || c->n_out < 0 || c->n_in + c->n_rec + c->n_out < 1)
+  if (c->d_model > kMaxDModel || c->d_ff > kMaxDFF || c->n_q_heads > kMaxHeads || c->vocab > kMaxVocab)
+    return fail(why, "model sizes beyond the library's limits (d_model, d_ff, heads, vocab)");
+  if (c->n_in < 0 || c->n_rec < 0 || c->n_out < 0 || (int64_t)c->n_in + c->n_rec + c->n_out < 1)
     return fail(why, "layer split must be non-negative with at least one layer");
+  if (c->n_in > kMaxLayers || c->n_rec > kMaxLayers || c->n_out > kMaxLayers)
+    return fail(why, "more layers per block than the library's limit");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(why, "head_dim must be 64 or 128");
   if (c->n_q_heads % c->n_kv_heads != 0) return fail(why, "n_q_heads must be a multiple of n_kv_heads");
   {
@@ -38,14 +42,24 @@ dory_status make_plan(const dory_config* c, Plan* p, std::string* why) {
   if (!c->layer_is_full) return fail(why, "layer_is_full is NULL");
   if (c->dtype != DORY_F32 && c->dtype != DORY_BF16) return fail(why, "dtype must be DORY_F32 or DORY_BF16");
   if (c->attn_gate < 0 || c->attn_gate > 2) return fail(why, "attn_gate must be 0, 1 or 2");
-  if (!(c->rope_base_swa > 1.0) || !(c->rope_base_full > 1.0)) return fail(why, "RoPE bases must be > 1");
+  if (!(c->rope_base_swa > 1.0) || !(c->rope_base_full > 1.0) || !std::isfinite(c->rope_base_swa) ||
+      !std::isfinite(c->rope_base_full))
+    return fail(why, "RoPE bases must be finite and > 1");
   if (c->max_batch < 1 || c->max_ctx < 1 || c->max_chunk < 1 || c->max_loops < 1)
     return fail(why, "capacities must be >= 1");
+  if (c->max_batch > kMaxBatch || c->max_ctx > kMaxCtx || c->max_loops > kMaxLoops)
+    return fail(why, "capacities beyond the library's limits (max_batch, max_ctx, max_loops)");
+  // elements of one cache (keys and value blocks) within 2^40, so that every
+  // KV offset and byte count stays far inside 64 bits
+  if ((int64_t)c->max_batch * c->n_kv_heads * c->head_dim * 2 * ((int64_t)c->max_ctx + 32) > ((int64_t)1 << 40))
+    return fail(why, "KV cache too large");
   if (c->max_chunk > c->max_ctx) return fail(why, "max_chunk must not exceed max_ctx");
   if (c->dtype == DORY_BF16 && (c->d_model % 8 || c->d_ff % 8 || c->head_dim % 8))
     return fail(why, "bfloat16 models need d_model, d_ff and head_dim multiples of 8");
   if ((int64_t)c->max_batch * c->max_chunk > (1 << 24)) return fail(why, "max_batch * max_chunk too large");
   if (!std::isfinite(c->combine_wh) || !std::isfinite(c->combine_we)) return fail(why, "combine weights must be finite");
+  if (!std::isfinite(c->attn_scale) || !std::isfinite(c->logit_scale))
+    return fail(why, "attn_scale and logit_scale must be finite (<= 0 selects the default)");
   if (c->weight_format != DORY_WEIGHTS_DTYPE && c->weight_format != DORY_WEIGHTS_MXFP8 &&
       c->weight_format != DORY_WEIGHTS_NVFP4)
     return fail(why, "weight_format must be DORY_WEIGHTS_DTYPE, DORY_WEIGHTS_MXFP8 or DORY_WEIGHTS_NVFP4");
@@ -103,7 +117,7 @@ dory_status make_kv_layout(const Plan& p, int kv_mode, int kv_loops, KvLayout* k
 }
 
 size_t argmax_partials(int32_t B, int32_t V) {
-  return (size_t)B * ((V + kArgmaxBlock - 1) / kArgmaxBlock);
+  return (size_t)B * (size_t)(((int64_t)V + kArgmaxBlock - 1) / kArgmaxBlock);
 }
 
 WsLayout make_ws_layout(const Plan& p) {

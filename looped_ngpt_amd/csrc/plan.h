@@ -16,6 +16,17 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kMaxSplits = 64;        // split-K pieces per (row, kv head) in decode attention
 constexpr int kArgmaxBlock = 1024;    // logits per argmax partial
 constexpr size_t kAlign = 256;
+// Shape and capacity limits of a config: every size the plan derives stays
+// far inside 64-bit arithmetic (and every per-row count inside int32).
+constexpr int kMaxDModel = 1 << 16;
+constexpr int kMaxDFF = 1 << 18;
+constexpr int kMaxHeads = 1024;
+constexpr int kMaxVocab = 1 << 26;
+constexpr int kMaxLayers = 4096;       // per block (input, recurrent, output)
+constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxCtx = 1 << 26;
+constexpr int kMaxLoops = 64;
+constexpr int64_t kMaxBwRows = 1 << 21;  // batch * positions of one backward call
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 // Row length of a call's transposed values [B][n_kv][hd][vld]: n rounded up
