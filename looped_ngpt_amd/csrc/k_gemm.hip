@@ -397,80 +397,171 @@ static int big_tile_n(int M, int N) {
 // ---------------------------------------------------------------------------
 // Batched-decode GEMM (9..64 rows): weight-stream bound. A workgroup owns 16
 // outputs (16 weight rows; SwiGLU: those 16 u rows and the 16 matching v
-// rows) and all M rows; its four waves split K in quarters. With
-// v_mfma_f32_16x16x32_bf16 lane l supplies row l%16 of a 16-row block and K
-// elements 8(l/16)..8(l/16)+7 of each 32-deep step, so every operand
-// fragment is one 16-byte load straight from global memory (the weights
-// stream once, the activations come from L2); four steps of loads are issued
-// before their products. The quarters are summed through LDS. Rows past M
-// and outputs past N are clamped loads whose results are dropped. Requires
-// K % 128 == 0 and 16-byte aligned rows.
+// rows) and all M rows (MB = 16, 32 or 64 staged, rows past M clamped). K
+// goes in windows of 64: each window's X rows and weight rows are copied
+// into LDS by direct global->LDS loads laid out like k_gemm_big's stages
+// (one 1 KB load covers 8 rows x 128 B, whole cache lines, chunks
+// XOR-swizzled by (row/2) % 8), in a ring of D windows so that D - 1
+// windows are in flight while one is multiplied (one barrier per window).
+// The loads of a window are spread over the four waves; each 16-row block of
+// X is one wave's 16 x 16 output block (v_mfma_f32_16x16x32_bf16, two
+// 32-deep steps per window), written straight from its accumulators.
+// Every workgroup streams all of X (M x K) from L2 beside its 16 weight rows;
+// operand loads taken straight from global memory in the MFMA layout (16
+// rows per 16-lane group) ran the wide projections at about half this rate.
+// Requires K % 64 == 0 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kSkU = 4;  // K steps of 32 whose loads are issued together
+constexpr int kStrBK = 64;
 
-template <int MB, int EPI>
+// s_waitcnt vmcnt(n) for a wave-uniform runtime n in [0, 63]
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n) {
+#define DORY_WV(i) \
+  case i: DORY_WAIT_VM(i); break;
+    DORY_WV(0) DORY_WV(1) DORY_WV(2) DORY_WV(3) DORY_WV(4) DORY_WV(5) DORY_WV(6) DORY_WV(7) DORY_WV(8)
+    DORY_WV(9) DORY_WV(10) DORY_WV(11) DORY_WV(12) DORY_WV(13) DORY_WV(14) DORY_WV(15) DORY_WV(16)
+    DORY_WV(17) DORY_WV(18) DORY_WV(19) DORY_WV(20) DORY_WV(21) DORY_WV(22) DORY_WV(23) DORY_WV(24)
+    DORY_WV(25) DORY_WV(26) DORY_WV(27) DORY_WV(28) DORY_WV(29) DORY_WV(30) DORY_WV(31) DORY_WV(32)
+    DORY_WV(33) DORY_WV(34) DORY_WV(35) DORY_WV(36) DORY_WV(37) DORY_WV(38) DORY_WV(39) DORY_WV(40)
+    DORY_WV(41) DORY_WV(42) DORY_WV(43) DORY_WV(44) DORY_WV(45) DORY_WV(46) DORY_WV(47) DORY_WV(48)
+#undef DORY_WV
+    default: DORY_WAIT_VM(0); break;
+  }
+}
+
+template <int MB, int EPI, int D>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X, int64_t ldx,
                                                      const bf16* __restrict__ W, void* __restrict__ C, int M, int N,
                                                      int K, float scale) {
-  constexpr int NB = MB / 16;                  // 16-row blocks of X
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;  // weight blocks (u, v)
-  __shared__ f32x4_t part[4][NR][NB][64];
+  constexpr int ROWS = MB + 16 * NR;             // window rows: X, then weights
+  constexpr int NL = ROWS / 8;                   // 1 KB loads per window
+  constexpr int LMAX = (NL + 3) / 4;             // loads per wave at most
+  constexpr int WIN = ROWS * 128;                // window bytes
+  static_assert(D >= 2 && (D - 2) * LMAX <= 48, "ring depth");
+  extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
   const int o0 = blockIdx.x * 16;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int kper = K / 4, kb = wave * kper;
-  const bf16* wp[NR];
+  const int nl = wave < NL ? (NL - wave + 3) / 4 : 0;  // this wave's loads per window (wave-uniform)
+
+  // load i of this wave fills window rows 8 (wave + 4 i) + 0..7
+  const int lr = lane >> 3, ls = lane & 7;
+  const bf16* src[LMAX];
 #pragma unroll
-  for (int j = 0; j < NR; ++j) wp[j] = W + (size_t)((j ? nout : 0) + min(o0 + r16, nout - 1)) * K + kb + kq;
-  const bf16* xp[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) xp[b] = X + (size_t)min(b * 16 + r16, M - 1) * ldx + kb + kq;
-  f32x4_t acc[NR][NB];
-#pragma unroll
-  for (int j = 0; j < NR; ++j)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < kper; k += 32 * kSkU) {
-    bf16x8_t wf[kSkU][NR], xf[kSkU][NB];
-#pragma unroll
-    for (int u = 0; u < kSkU; ++u) {
-      const int kk = min(k + 32 * u, kper - 32);  // past the quarter: a re-read, not multiplied
-#pragma unroll
-      for (int j = 0; j < NR; ++j) wf[u][j] = __builtin_nontemporal_load((const bf16x8_t*)(wp[j] + kk));
-#pragma unroll
-      for (int b = 0; b < NB; ++b) xf[u][b] = *(const bf16x8_t*)(xp[b] + kk);
+  for (int i = 0; i < LMAX; ++i) {
+    const int r = min(8 * (wave + 4 * i) + lr, ROWS - 1);
+    const bf16* base;
+    if (r < MB) {
+      base = X + (size_t)min(r, M - 1) * ldx;
+    } else {
+      const int wr = r - MB;
+      const int o = min(o0 + (wr & 15), nout - 1);
+      base = W + (size_t)((wr >= 16 ? nout : 0) + o) * K;
     }
-#pragma unroll
-    for (int u = 0; u < kSkU; ++u) {
-      if (k + 32 * u >= kper) break;
-#pragma unroll
-      for (int j = 0; j < NR; ++j)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][b], wf[u][j], acc[j][b], 0, 0, 0);
-    }
+    src[i] = base + (ls ^ ((r >> 1) & 7)) * 8;
   }
+  const int nK = K / kStrBK;
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % D) * WIN;
 #pragma unroll
-  for (int j = 0; j < NR; ++j)
+    for (int i = 0; i < LMAX; ++i)
+      if (i < nl) lds_load16(src[i] + kt * kStrBK, st + (wave + 4 * i) * 1024);
+  };
+
+  // wave w multiplies X rows 16w..16w+15 (waves past MB/16 only load)
+  const bool active = wave < MB / 16;
+  const int r16 = lane & 15, cq = lane >> 4;
+  f32x4_t acc[NR];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) part[wave][j][b][lane] = acc[j][b];
-  __syncthreads();
-  // output (row m, column n) of block b: lane n + 16 (m%16 / 4), register m % 4
-  for (int e = tid; e < MB * 16; e += 256) {
-    const int m = e >> 4, n = e & 15;
-    const int b = m >> 4, ln = n + 16 * ((m & 15) >> 2), r = m & 3;
-    float s[NR];
+  for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mul = [&](int kt) {
+    const unsigned char* st = smem + (kt % D) * WIN;
 #pragma unroll
-    for (int j = 0; j < NR; ++j) s[j] = part[0][j][b][ln][r] + part[1][j][b][ln][r] + part[2][j][b][ln][r] +
-                                        part[3][j][b][ln][r];
-    if (m >= M || o0 + n >= nout) continue;
+    for (int s = 0; s < 2; ++s) {
+      const int c = 4 * s + cq;  // 16-byte chunk: K elements 32 s + 8 (lane / 16) ..
+      const bf16x8_t a = *(const bf16x8_t*)(st + big_off(16 * wave + r16, c));
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const bf16x8_t w = *(const bf16x8_t*)(st + big_off(MB + 16 * j + r16, c));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j], 0, 0, 0);
+      }
+    }
+  };
+
+  const int pre = min(D - 1, nK);
+  for (int kt = 0; kt < pre; ++kt) issue(kt);
+  // steady state: window kt + D - 1 goes out while window kt is multiplied
+  int kt = 0;
+  for (; kt + D - 1 < nK; ++kt) {
+    wait_vm_dyn(nl * (D - 2));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + D - 1);  // into the slot window kt - 1 used (every wave is past it)
+    if (active) mul(kt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // tail: no more loads
+  for (; kt < nK; ++kt) {
+    wait_vm_dyn(nl * (nK - 1 - kt));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (active) mul(kt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!active) return;
+  // D layout of a 16x16 block: register i of lane l -> row 4 (l / 16) + i, column l % 16
+  const int o = o0 + r16;
+  if (o >= nout) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 16 * wave + 4 * cq + i;
+    if (m >= M) continue;
     if (EPI == EPI_SWIGLU)
-      ((bf16*)C)[(size_t)m * nout + o0 + n] = from_f<bf16>(s[0] * scale * silu_(s[1] * scale));
+      ((bf16*)C)[(size_t)m * nout + o] = from_f<bf16>(acc[0][i] * scale * silu_(acc[1][i] * scale));
     else
-      ((float*)C)[(size_t)m * N + o0 + n] = s[0] * scale;
+      ((float*)C)[(size_t)m * N + o] = acc[0][i] * scale;
   }
+}
+
+template <int MB, int EPI, int D>
+static void skinny_launch_mb(dim3 grid, const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K,
+                             float scale, hipStream_t st) {
+  constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr uint32_t lds = D * (MB + 16 * NR) * 128;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_skinny<MB, EPI, D>,
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)attr;
+  dory_launch((k_gemm_skinny<MB, EPI, D>), grid, dim3(256), lds, st, x, ldx, W, y, M, N, K, scale);
+}
+
+// Ring depth in windows: 16 (one workgroup per CU) or 8 (two per CU) at 16 and
+// 32 rows, 12 or 6 at 64 rows. Deeper rings measured slower (18-36 windows:
+// -10 to -30%).
+template <int MB, bool ONE>
+constexpr int skinny_depth() {
+  return MB == 64 ? (ONE ? 12 : 6) : (ONE ? 16 : 8);
+}
+
+template <int EPI>
+static void skinny_launch(const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
+                          hipStream_t st) {
+  const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
+  const dim3 grid((nout + 15) / 16);
+  // one workgroup per CU (a deep ring) below 512 workgroups, else two per CU
+  const bool one = grid.x < 512;
+#define DORY_SK(MB)                                                                                      \
+  if (one) skinny_launch_mb<MB, EPI, skinny_depth<MB, true>()>(grid, x, ldx, W, y, M, N, K, scale, st); \
+  else skinny_launch_mb<MB, EPI, skinny_depth<MB, false>()>(grid, x, ldx, W, y, M, N, K, scale, st);
+  if (M <= 16) {
+    DORY_SK(16)
+  } else if (M <= 32) {
+    DORY_SK(32)
+  } else {
+    DORY_SK(64)
+  }
+#undef DORY_SK
 }
 
 // ---------------------------------------------------------------------------
@@ -545,17 +636,8 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
       big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
     else
       big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
-  } else if (sizeof(T) == 2 && al16 && K % 128 == 0 && M <= 64) {
-    const dim3 grid((nout + 15) / 16);
-    if (M <= 16)
-      dory_launch((k_gemm_skinny<16, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
-                  scale);
-    else if (M <= 32)
-      dory_launch((k_gemm_skinny<32, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
-                  scale);
-    else
-      dory_launch((k_gemm_skinny<64, EPI>), grid, dim3(256), 0, st, (const bf16*)x, ldx, (const bf16*)W, y, M, N, K,
-                  scale);
+  } else if (sizeof(T) == 2 && al16 && K % kStrBK == 0 && M <= 64) {
+    skinny_launch<EPI>((const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
   } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
     const int nt = EPI == EPI_SWIGLU ? (nout + GBN / 2 - 1) / (GBN / 2) : (N + GBN - 1) / GBN;
     dim3 grid(nt, (M + GBM - 1) / GBM);

@@ -32,6 +32,10 @@ CASES = [
     ("bf16", 1, 2304, 6144, 0, 1), ("bf16", 1, 1001, 8192, 0, 1), ("bf16", 1, 7, 5640, 0, 1),
     ("bf16", 130, 1000, 3072, 0, 2), ("bf16", 256, 8192, 3072, 0, 2), ("bf16", 200, 2 * 1000, 3072, 1, 2),
     ("bf16", 64, 3072, 8192, 0, 2), ("bf16", 33, 2304, 2304, 0, 2), ("bf16", 97, 2 * 6144, 2304, 1, 2),
+    # 9..64 rows: the weight-streaming GEMM (eight waves below 512 workgroups, four from there; the
+    # SwiGLU epilogue; a K range of one 128-deep batch per wave; ragged M and N)
+    ("bf16", 64, 2 * 8192, 3072, 1, 2), ("bf16", 40, 8192, 3072, 0, 2), ("bf16", 9, 2 * 1000, 3072, 1, 2),
+    ("bf16", 17, 1000, 1024, 0, 2), ("bf16", 64, 3072, 3072, 0, 2),
     # M >= 1024: the 256x256-tile kernel (ragged M and N tiles, both epilogues, K multiple of 32)
     ("bf16", 1100, 1000, 3072, 0, 2), ("bf16", 1030, 2 * 1000, 2304, 1, 2), ("bf16", 2048, 3072, 1088, 0, 2),
     ("bf16", 1024, 2 * 384, 3072, 1, 2),
