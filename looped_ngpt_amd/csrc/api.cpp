@@ -261,7 +261,9 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv,
   // replays at every step; the kernel spreads the actual keys over the splits
   const int key_cap = full ? C.max_ctx : std::min(C.window, C.max_ctx);
   if (attn_decode_uses_mfma(C.dtype, C.head_dim, slots, C.window, full))
-    da.n_split = choose_splits_decode(((key_cap + 31) / 32 + 1) * 32, B, C.n_kv_heads);  // 32-position tiles
+    // 32-slot tiles: a ring's tiles are fixed, positions 0..t of a full layer
+    // may straddle one tile more
+    da.n_split = choose_splits_decode(full ? ((key_cap + 31) / 32 + 1) * 32 : (slots + 31) / 32 * 32, B, C.n_kv_heads);
   else
     da.n_split = choose_splits_decode(key_cap, B, C.n_kv_heads);
   da.scale = P.attn_scale;

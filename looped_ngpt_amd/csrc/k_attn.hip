@@ -517,7 +517,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int HD, int G>
+template <int HD, int G, bool FULL>
 __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   constexpr int NKK = HD / 32;        // depth steps of the score product
   constexpr int NDD = HD / 16;        // 16-dim blocks of the output
@@ -534,20 +534,17 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   const int c16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x;
   const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
-  // position of the new key (device counter: graph-replayable), read through
-  // the scalar cache (it is not written by this kernel)
-  const int t = *(const __attribute__((address_space(4))) int*)a.t_dev;
-  const int lo = a.is_full ? 0 : max(0, t - a.window + 1);
-  const int T_lo = lo >> 5, T_hi = t >> 5;
-  const int ntiles = T_hi - T_lo + 1;
-  const int tps = (ntiles + a.n_split - 1) / a.n_split;
-  const int tb = T_lo + split * tps;                 // this split's tiles [tb, te)
-  const int te = min(T_hi + 1, tb + tps);
-  const bool has_self = tb <= T_hi && T_hi < te;
   const int half = HD / 2;
 
+  // (0) position of the new key: a device counter (graph-replayable), read by
+  // a vector (buffer) load so that waiting for it does not wait for anything
+  // issued after it: vector loads return in order, while a scalar load would
+  // share its wait with the kernel-argument loads that the addresses below need
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)a.t_dev, (short)0, 4, 0x00020000);
+  const int t_v = __builtin_amdgcn_raw_buffer_load_b32(trs, 0, 0, 0);
+
   // (1) projection values for q heads / new key / new value (L2), clamped and
-  // unconditional so the waits stay exact
+  // unconditional so the waits stay exact; they do not depend on the position
   const float* row = a.qkvg + (size_t)b * a.ld;
   const int ln = min(lane, half - 1);
   float x1[NI], x2[NI];
@@ -559,10 +556,8 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     x1[it] = src[ln];
     x2[it] = src[ln + half];
   }
-  const float2 cs = a.tab[(size_t)t * half + ln];
-  // gate values of this thread's entries of the sums, fetched with the setup
-  // values rather than at the end of the kernel; always in bounds (without a
-  // gate the unused index points into q)
+  // gate values of this thread's entries of the sums (without a gate the
+  // unused index points into q)
   constexpr int NE = (G * (HD + 1) + 255) / 256;
   float gx[NE];
   {
@@ -574,41 +569,77 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       gx[it] = gp[a.gate == 2 ? hq : hq * HD + d];
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the cache stream
+  __builtin_amdgcn_sched_barrier(0);  // keep these small loads ahead of the cache stream
 
-  // (2) cache operands of the wave's first tile (HBM)
+  // (2) cache operands. Tiles of 32 slots. Sliding layers (a ring of
+  // `slots` slots, slot = pos mod window) walk the ring by slot, so a split's
+  // tiles are fixed and their loads go out before the position is known;
+  // which position a slot holds (and whether it is in the window) is worked
+  // out afterwards. Full layers spread the tiles of positions 0..t over the
+  // splits.
   const bf16* kc = (const bf16*)a.kc;
-  const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);  // 32-position blocks
+  const bf16* vt = (const bf16*)a.vc + ((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots);
   const size_t khead = ((size_t)b * a.nkv + kvh) * a.slots;
-  auto slot_of = [&](int pos) { return a.is_full ? pos : pos % a.window; };
-  // Key order inside a 32-position tile: A row r of 16-key half kb holds key
-  // 8 (r / 4) + 4 kb + r % 4, so the score lane (head, g4) ends up with keys
-  // 8 g4 .. 8 g4 + 7 (half 0: +0..3, half 1: +4..7) — the k order of the P.V
-  // product, whose V^T operand is then one 16-byte run of 8 positions.
-  auto load = [&](int T, u32x4 (&ka)[2][NKK], u32x4 (&va)[NDD]) {
-    const int p0 = T << 5;
+  // Key order inside a tile: A row r of 16-key half kb holds key 8 (r / 4) +
+  // 4 kb + r % 4, so the score lane (head, g4) ends up with keys 8 g4 .. 8 g4
+  // + 7 (half 0: +0..3, half 1: +4..7) — the k order of the P.V product,
+  // whose V^T operand is then one 16-byte run of 8 slots.
+  auto loadK = [&](int T, int smax, u32x4 (&ka)[2][NKK]) {
+    const int s0t = T << 5;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(p0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), t);  // beyond t: any written slot, masked later
-      const bf16* kr = kc + (khead + slot_of(key)) * HD + 8 * g4;
+      const int sl = min(s0t + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), smax);  // past smax: masked later
+      const bf16* kr = kc + (khead + sl) * HD + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)(kr + kk * 32);
     }
-    // 8 consecutive positions, 8-aligned (slot and window counts are multiples
-    // of 8); runs past the last slot hold only positions > t (masked) and are
-    // clamped in bounds
-    const int g0 = p0 + 8 * g4;
-    const int s0 = min(a.is_full ? g0 : g0 % a.window, a.slots - 8);
+  };
+  // 8 consecutive slots, 8-aligned (slot and window counts are multiples of
+  // 8), clamped in bounds
+  auto loadV = [&](int T, u32x4 (&va)[NDD]) {
+    const int s0 = min((T << 5) + 8 * g4, a.slots - 8);
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) va[dd] = *(const u32x4*)(vt + vt_off(s0, 16 * dd + c16, HD));
   };
-  // issued unconditionally (a tile past te is clamped in bounds and never
-  // processed): loads under a branch make the compiler wait for all of them
-  // where the paths join, before the setup arithmetic below
-  const int first = tb + wave;
+  const int ntiles_ring = vslots_of(a.slots) >> 5;
+  const int half_ln = ln;
+  int tb, te, t;
+  float2 cs;
   u32x4 ka0[2][NKK];
   u32x4 va0[NDD];
-  load(first, ka0, va0);
+  if (!FULL) {
+    const int tps = (ntiles_ring + a.n_split - 1) / a.n_split;
+    tb = split * tps;
+    te = min(ntiles_ring, tb + tps);
+    // issued unconditionally (a tile past te is clamped in bounds and never
+    // processed): loads under a branch make the compiler wait for all of
+    // them where the paths join. The keys go out before the position is
+    // known; the rotation row (which needs it) before the values, so that
+    // waiting for it does not wait for them.
+    const int T0 = min(tb + wave, ntiles_ring - 1);
+    loadK(T0, a.slots - 1, ka0);
+    __builtin_amdgcn_sched_barrier(0);
+    t = __builtin_amdgcn_readfirstlane(t_v);
+    cs = a.tab[(size_t)t * half + half_ln];
+    __builtin_amdgcn_sched_barrier(0);
+    loadV(T0, va0);
+  } else {
+    t = __builtin_amdgcn_readfirstlane(t_v);
+    cs = a.tab[(size_t)t * half + half_ln];
+    const int ntiles = (t >> 5) + 1;
+    const int tps = (ntiles + a.n_split - 1) / a.n_split;
+    tb = split * tps;
+    te = min(ntiles, tb + tps);
+    loadK(tb + wave, t, ka0);
+    loadV(tb + wave, va0);
+  }
+  // position -> slot; ring: slot s holds position base + s (s <= tm) or
+  // base + s - window (s > tm), base = t - tm, tm = t mod window
+  const int tm = FULL ? t : t % a.window;
+  const int base = t - tm;
+  const int lo = FULL ? 0 : max(0, t - a.window + 1);
+  const int tself = tm >> 5;  // tile holding the new key (by slot)
+  const bool has_self = tb <= tself && tself < te;
 
   // (3) RoPE at t, unit norm, bfloat16 storage of q and of the new key/value
 #pragma unroll
@@ -633,12 +664,16 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   }
   for (int e = tid; e < (16 - G) * HD; e += 256) qs[G + e / HD][e % HD] = 0;  // padded head columns
   __syncthreads();
-  if (has_self && a.write_kv && (!a.wloops || a.wloops[b] == a.loop) && tid < HD) {
-    // the slot of t held t - W (outside every window of this call) or nothing
-    const int slot = slot_of(t);
-    ((bf16*)a.kc)[(khead + slot) * HD + tid] = selfk[tid];
-    ((bf16*)a.vc)[((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots) + vt_off(slot, tid, HD)] = selfv[tid];
-  }
+  // The new key and value go to the cache at the end of the kernel (nothing
+  // in it reads that slot from memory): stores count in the same wait counter
+  // as loads, so stores issued here would hold up every later wait for a tile.
+  auto write_self = [&]() {
+    if (has_self && a.write_kv && (!a.wloops || a.wloops[b] == a.loop) && tid < HD) {
+      // the slot of t held t - window (outside every window of this call) or nothing
+      ((bf16*)a.kc)[(khead + tm) * HD + tid] = selfk[tid];
+      ((bf16*)a.vc)[((size_t)b * a.nkv + kvh) * HD * vslots_of(a.slots) + vt_off(tm, tid, HD)] = selfv[tid];
+    }
+  };
 
   bf16x8_t qb[NKK];
 #pragma unroll
@@ -655,27 +690,41 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
 #pragma unroll
   for (int dd = 0; dd < NDD; ++dd) acc[dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // position held by slot s (ring) or slot = position (full); valid: in the
+  // window and written
+  auto pos_of = [&](int s) { return FULL ? s : (s <= tm ? base + s : base + s - a.window); };
   auto process = [&](int T, u32x4 (&ka)[2][NKK], u32x4 (&va)[NDD]) {
-    const int p0 = T << 5;
-    const bool edge = p0 < lo || p0 + 31 >= t;  // wave-uniform: needs masks or the new key
-    // k-slot j of this lane (score register i of half kb: j = 4 kb + i) is key p0 + 8 g4 + j
+    const int s0t = T << 5;
+    // wave-uniform: the tile needs masks (slots outside the window, past the
+    // written ones or past the ring) or holds the new key
+    const bool edge = FULL ? s0t + 31 >= t : (T == tself || t < a.window - 1 || s0t + 32 > a.slots);
     if (edge) {
+      // branch-free: the new key's operands from LDS, selected per lane
+      u32x4 sk[NKK];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (p0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3) == t) {
+      for (int kk = 0; kk < NKK; ++kk) sk[kk] = *(const u32x4*)&selfk[kk * 32 + 8 * g4];
+      uint32_t sv[NDD];
 #pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = *(const u32x4*)&selfk[kk * 32 + 8 * g4];
-        }
+      for (int dd = 0; dd < NDD; ++dd) sv[dd] = (uint32_t)selfv[16 * dd + c16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool me = s0t + 8 * (c16 >> 2) + 4 * kb + (c16 & 3) == tm;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ka[kb][kk][q] = me ? sk[kk][q] : ka[kb][kk][q];
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int key = p0 + 8 * g4 + j;
-        const bool valid = key >= lo && key <= t;
+        const int s = s0t + 8 * g4 + j;
+        const int p = pos_of(s);
+        const bool valid = s < a.slots && p >= lo && p <= t;
+        const bool me = s == tm;
+        const uint32_t sh = (j & 1) * 16;
 #pragma unroll
         for (int dd = 0; dd < NDD; ++dd) {
-          uint32_t w = va[dd][j >> 1];
-          const uint32_t sh = (j & 1) * 16;
-          uint32_t v = (w >> sh) & 0xffffu;
-          v = key == t ? (uint32_t)selfv[16 * dd + c16] : (valid ? v : 0u);
+          const uint32_t w = va[dd][j >> 1];
+          const uint32_t v = me ? sv[dd] : (valid ? (w >> sh) & 0xffffu : 0u);
           va[dd][j >> 1] = (w & ~(0xffffu << sh)) | (v << sh);
         }
       }
@@ -695,8 +744,12 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = p0 + 8 * g4 + 4 * kb + i;
-        const bool valid = !edge || (key >= lo && key <= t);
+        const int s = s0t + 8 * g4 + 4 * kb + i;
+        bool valid = true;
+        if (edge) {
+          const int p = pos_of(s);
+          valid = s < a.slots && p >= lo && p <= t;
+        }
         const float v = valid ? sc[kb][i] * sl2 : -INFINITY;
         v8[kb * 4 + i] = v;
         tmax = fmaxf(tmax, v);
@@ -711,10 +764,10 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     bf16x8_t pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = v8[j] == -INFINITY ? 0.f : exp2f(v8[j] - mn);
+      // arguments >= -2 sl2 >= -80: the raw v_exp_f32 is exact enough
+      const float p = v8[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v8[j] - mn);
       ps += p;
-      const bf16 pbits = from_f<bf16>(p);
-      pb[j] = *(const __bf16*)&pbits;
+      pb[j] = (__bf16)p;
     }
     l = l * alpha + ps;  // this lane's keys; summed over the key groups after the loop
     m = mn;
@@ -725,8 +778,13 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     }
   };
 
+  const int first = tb + wave;
+  const int smax = FULL ? t : a.slots - 1;
   for (int T = first; T < te; T += 4) {
-    if (T != first) load(T, ka0, va0);
+    if (T != first) {
+      loadK(T, smax, ka0);
+      loadV(T, va0);
+    }
     process(T, ka0, va0);
   }
 
@@ -748,6 +806,23 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
     // value sums gated (linear in the sums), then fixed point in the bin that
     // this workgroup's sum p of the head selects; integer adds are
     // order-independent
+    // per head, once: each wave's factor to the bound, the workgroup's sum p
+    // L and its bin (L in [2^ex, 2^(ex+1)), normal: L >= 2^(-2 sl2) > 2^-126;
+    // bin b keeps L 2^(16b) in [2^-15, 2))
+    __shared__ float fw[4][16];
+    __shared__ int binh[16];
+    if (tid < G) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = wm[w][tid] == -INFINITY ? 0.f : exp2f(wm[w][tid] - sl2);
+        fw[w][tid] = f;
+        L = fmaf(wl[w][tid], f, L);
+      }
+      const int ex = (int)((__float_as_uint(L) >> 23) & 0xff) - 127;
+      binh[tid] = ex < 0 ? min(-ex / kAttnAccBinBits, a.acc_nb - 1) : 0;
+    }
+    __syncthreads();
     const int stride = attn_acc_stride(HD, a.acc_nb);
 #pragma unroll
     for (int it = 0; it < NE; ++it) {
@@ -755,24 +830,17 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       if (e >= G * (HD + 1)) break;
       const int g = e / (HD + 1), d = e % (HD + 1);
       const int hq = kvh * G + g;
-      float S = 0.f, L = 0.f;
+      float S = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (wm[w][g] == -INFINITY) continue;
-        const float f = exp2f(wm[w][g] - sl2);
-        S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], f, S);
-        L = fmaf(wl[w][g], f, L);  // the same for every d of head g: one bin per (workgroup, head)
-      }
+      for (int w = 0; w < 4; ++w) S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], fw[w][g], S);
       if (d < HD && a.gate) S *= sigmoidf_(gx[it]);
       if (S == 0.f) continue;
-      // L in [2^ex, 2^(ex+1)) (normal: L >= 2^(-2 sl2) > 2^-126); bin b keeps
-      // L 2^(16b) in [2^-15, 2)
-      const int ex = (int)((__float_as_uint(L) >> 23) & 0xff) - 127;
-      const int bin = ex < 0 ? min(-ex / kAttnAccBinBits, a.acc_nb - 1) : 0;
+      const int bin = binh[g];
       unsigned long long* ap = a.acc + ((size_t)b * a.nq + hq) * stride;
       atomicAdd(d < HD ? ap + bin * HD + d : ap + a.acc_nb * HD + bin,
                 (unsigned long long)llrint(ldexp((double)S, 36 + kAttnAccBinBits * bin)));
     }
+    write_self();
     return;
   }
   for (int e = tid; e < G * HD; e += 256) {
@@ -797,6 +865,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       out[1] = Ls;
     }
   }
+  write_self();
 }
 
 // One workgroup of 512 threads per (q head, row): thread (d, group) takes
@@ -872,19 +941,24 @@ static hipError_t attn_dec_hd(const AttnDecArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int HD>
-static hipError_t attn_dec_mfma(const AttnDecArgs& a, hipStream_t st) {
+template <int HD, bool FULL>
+static hipError_t attn_dec_mfma_f(const AttnDecArgs& a, hipStream_t st) {
   dim3 grid(a.n_split, a.B * a.nkv);
   switch (a.nq / a.nkv) {
-    case 1: dory_launch((k_attn_decode_mfma<HD, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: dory_launch((k_attn_decode_mfma<HD, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: dory_launch((k_attn_decode_mfma<HD, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: dory_launch((k_attn_decode_mfma<HD, 4>), grid, dim3(256), 0, st, a); break;
-    case 6: dory_launch((k_attn_decode_mfma<HD, 6>), grid, dim3(256), 0, st, a); break;
-    case 8: dory_launch((k_attn_decode_mfma<HD, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: dory_launch((k_attn_decode_mfma<HD, 1, FULL>), grid, dim3(256), 0, st, a); break;
+    case 2: dory_launch((k_attn_decode_mfma<HD, 2, FULL>), grid, dim3(256), 0, st, a); break;
+    case 3: dory_launch((k_attn_decode_mfma<HD, 3, FULL>), grid, dim3(256), 0, st, a); break;
+    case 4: dory_launch((k_attn_decode_mfma<HD, 4, FULL>), grid, dim3(256), 0, st, a); break;
+    case 6: dory_launch((k_attn_decode_mfma<HD, 6, FULL>), grid, dim3(256), 0, st, a); break;
+    case 8: dory_launch((k_attn_decode_mfma<HD, 8, FULL>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t attn_dec_mfma(const AttnDecArgs& a, hipStream_t st) {
+  return a.is_full ? attn_dec_mfma_f<HD, true>(a, st) : attn_dec_mfma_f<HD, false>(a, st);
 }
 
 bool attn_decode_uses_mfma(int dtype, int hd, int slots, int window, int is_full) {
