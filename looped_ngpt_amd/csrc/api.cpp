@@ -41,6 +41,9 @@ struct dory_ctx {
   // stream, which cannot be recorded), ordered after and before the caller's
   // stream by two events.
   bool graphs_on = false;
+  // position of the decode step's new key, passed by value to the decode
+  // attention on eager, uncaptured calls; -1: kernels read the device counter
+  int t_now = -1;
   struct Graph { int k, B; hipGraph_t g; hipGraphExec_t x; };
   std::vector<Graph> graphs;
   hipStream_t gst = nullptr;
@@ -255,7 +258,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv,
   AttnDecArgs da{};
   da.qkvg = qkvg; da.ld = P.qkvg_dim;
   da.tab = wsp<float2>(c, full ? W.rope_full : W.rope_swa);
-  da.t_dev = wsp<int>(c, W.pos); da.B = B; da.nq = C.n_q_heads; da.nkv = C.n_kv_heads; da.hd = C.head_dim;
+  da.t_dev = wsp<int>(c, W.pos); da.t_now = c->t_now; da.B = B; da.nq = C.n_q_heads; da.nkv = C.n_kv_heads; da.hd = C.head_dim;
   da.slots = slots; da.window = C.window; da.is_full = full; da.write_kv = write_kv ? 1 : 0;
   // split count from the capacity (not the position), so a recorded graph
   // replays at every step; the kernel spreads the actual keys over the splits
@@ -524,6 +527,15 @@ dory_status decode_graph(dory_ctx* c, int k) {
   HIP_TRY(c, hipStreamWaitEvent(c->st, c->gev[1], 0));
   c->has_logits = true;
   return DORY_OK;
+}
+
+// The new key's position for the decode attention: c->pos on an eager call;
+// -1 (read the device counter) while the caller's stream is being captured,
+// so that a graph recorded around dory_decode_step stays step-invariant.
+int eager_position(dory_ctx* c) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(c->st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return -1;
+  return c->pos;
 }
 
 dory_status check_call(dory_ctx* c, int B, int n, int n_loops, int kv_mode) {
@@ -930,8 +942,10 @@ dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_l
   if (fused && c->graphs_on && !tokens_dev && c->time_kind == 0) {
     s = decode_graph(c, n_loops);
   } else {
+    c->t_now = eager_position(c);
     s = fused ? run_decode_fused(c, tok, c->batch, n_loops)
               : run_forward(c, tok, 1, c->batch, 1, n_loops, true, true);
+    c->t_now = -1;
   }
   if (s != DORY_OK) return s;
   commit_call(c, c->batch, 1, n_loops, kv_mode);

@@ -536,12 +536,15 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   const int b = blockIdx.y / a.nkv, kvh = blockIdx.y % a.nkv;
   const int half = HD / 2;
 
-  // (0) position of the new key: a device counter (graph-replayable), read by
-  // a vector (buffer) load so that waiting for it does not wait for anything
-  // issued after it: vector loads return in order, while a scalar load would
-  // share its wait with the kernel-argument loads that the addresses below need
-  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)a.t_dev, (short)0, 4, 0x00020000);
-  const int t_v = __builtin_amdgcn_raw_buffer_load_b32(trs, 0, 0, 0);
+  // (0) position of the new key: passed by value on eager calls; recorded
+  // graphs read the device counter (every argument step-invariant)
+  int t;
+  if (a.t_now >= 0) {
+    t = a.t_now;
+  } else {
+    const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)a.t_dev, (short)0, 4, 0x00020000);
+    t = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(trs, 0, 0, 0));
+  }
 
   // (1) projection values for q heads / new key / new value (L2), clamped and
   // unconditional so the waits stay exact; they do not depend on the position
@@ -601,38 +604,31 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) va[dd] = *(const u32x4*)(vt + vt_off(s0, 16 * dd + c16, HD));
   };
-  const int ntiles_ring = vslots_of(a.slots) >> 5;
-  const int half_ln = ln;
-  int tb, te, t;
-  float2 cs;
-  u32x4 ka0[2][NKK];
-  u32x4 va0[NDD];
+  // rotation row at t, issued before the cache stream so that waiting for it
+  // does not wait for the stream (vector loads return in order)
+  const float2 cs = a.tab[(size_t)t * half + ln];
+  __builtin_amdgcn_sched_barrier(0);
+  int tb, te;
   if (!FULL) {
-    const int tps = (ntiles_ring + a.n_split - 1) / a.n_split;
+    const int ntiles = vslots_of(a.slots) >> 5;
+    const int tps = (ntiles + a.n_split - 1) / a.n_split;
     tb = split * tps;
-    te = min(ntiles_ring, tb + tps);
-    // issued unconditionally (a tile past te is clamped in bounds and never
-    // processed): loads under a branch make the compiler wait for all of
-    // them where the paths join. The keys go out before the position is
-    // known; the rotation row (which needs it) before the values, so that
-    // waiting for it does not wait for them.
-    const int T0 = min(tb + wave, ntiles_ring - 1);
-    loadK(T0, a.slots - 1, ka0);
-    __builtin_amdgcn_sched_barrier(0);
-    t = __builtin_amdgcn_readfirstlane(t_v);
-    cs = a.tab[(size_t)t * half + half_ln];
-    __builtin_amdgcn_sched_barrier(0);
-    loadV(T0, va0);
+    te = min(ntiles, tb + tps);
   } else {
-    t = __builtin_amdgcn_readfirstlane(t_v);
-    cs = a.tab[(size_t)t * half + half_ln];
     const int ntiles = (t >> 5) + 1;
     const int tps = (ntiles + a.n_split - 1) / a.n_split;
     tb = split * tps;
     te = min(ntiles, tb + tps);
-    loadK(tb + wave, t, ka0);
-    loadV(tb + wave, va0);
   }
+  // issued unconditionally (a tile past te is clamped in bounds and never
+  // processed): loads under a branch make the compiler wait for all of them
+  // where the paths join
+  const int smax = FULL ? t : a.slots - 1;
+  const int T0 = FULL ? tb + wave : min(tb + wave, (vslots_of(a.slots) >> 5) - 1);
+  u32x4 ka0[2][NKK];
+  u32x4 va0[NDD];
+  loadK(T0, smax, ka0);
+  loadV(T0, va0);
   // position -> slot; ring: slot s holds position base + s (s <= tm) or
   // base + s - window (s > tm), base = t - tm, tm = t mod window
   const int tm = FULL ? t : t % a.window;
@@ -779,7 +775,6 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   };
 
   const int first = tb + wave;
-  const int smax = FULL ? t : a.slots - 1;
   for (int T = first; T < te; T += 4) {
     if (T != first) {
       loadK(T, smax, ka0);

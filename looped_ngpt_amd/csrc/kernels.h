@@ -111,6 +111,7 @@ struct AttnDecArgs {
   const float* qkvg; int64_t ld;
   const float2* tab;
   const int* t_dev;
+  int t_now;  // position of the new key if >= 0 (eager calls), else read *t_dev
   int B, nq, nkv, hd, slots, window, is_full, write_kv, n_split;
   float scale;
   void* kc; void* vc;
