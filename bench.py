@@ -482,6 +482,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-steps", type=int, default=16, help="decode steps of the kernel-timing pass")
     ap.add_argument("--graphs", action="store_true", help="replay decode steps as recorded HIP graphs")
+    ap.add_argument("--markers", action="store_true",
+                    help="roctx ranges around calls and layer applications (rocprofv3 --marker-trace)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB on the device 3 times (reference for the HBM byte counters)")
     ap.add_argument("--no-prefill-taps", action="store_true", help="skip the prefill kernel-timing passes")
@@ -543,6 +545,8 @@ def main():
     sess = dory.Session(model, w, max_batch=1, max_ctx=max_ctx, max_chunk=n, kv_mode="last_loop",
                         stream=stream, device=dev)
     sess.set_graphs(args.graphs)
+    if args.markers:
+        sess.set_markers(True)
     # warm-up prefill (untimed) at the timed shapes: first-use costs of the
     # code objects and of the GEMM library (its per-shape algorithm choice)
     sess.prefill(prompt, ks[0])

@@ -273,6 +273,15 @@ dory_status dory_set_trace(dory_ctx* ctx, float* trace_dev, int32_t max_apps);
  * bottleneck. */
 dory_status dory_set_graphs(dory_ctx* ctx, int32_t enable);
 
+/* Profiler ranges. With enable != 0, every dory_prefill, dory_decode_step
+ * and dory_backward_last_loop call, and each layer application inside it
+ * ("layer l loop j"; j = 0 outside the recurrent block), is bracketed by a
+ * roctx range, host side (rocprofv3 --marker-trace shows them beside the
+ * kernels they enqueue). The ROCm marker library (librocprofiler-sdk-roctx,
+ * else libroctx64) is loaded on first use; DORY_E_ARG if neither loads. Off
+ * by default; a switched-off context makes no marker call. */
+dory_status dory_set_markers(dory_ctx* ctx, int32_t enable);
+
 /* Kernel timing tap. When kind is not 0, every launch of one kernel class is
  * bracketed by HIP events recorded on the context's stream:
  *   1 SwiGLU up/gate projection   2 fused q|k|v|gate projection

@@ -36,7 +36,7 @@ KV_MODES = {"per_loop": DORY_KV_PER_LOOP, "last_loop": DORY_KV_LAST_LOOP}
 EXPORTS = ["dory_validate_config", "dory_kv_bytes", "dory_workspace_bytes", "dory_kv_slot",
            "dory_status_string", "dory_create", "dory_destroy", "dory_reset", "dory_prefill",
            "dory_decode_step", "dory_resume", "dory_prefill_mixed", "dory_decode_step_mixed", "dory_op_quant_mxfp8",
-           "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs",
+           "dory_op_linear_mx", "dory_op_quant_nvfp4", "dory_op_linear_fp4", "dory_logits", "dory_last_error", "dory_set_trace", "dory_set_graphs", "dory_set_markers",
            "dory_set_kernel_timing",
            "dory_kernel_time", "dory_op_linear",
            "dory_argmax_scratch_bytes", "dory_op_argmax", "dory_op_argmax_noalloc", "dory_backward_workspace_bytes", "dory_backward_workspace_min_bytes",
@@ -91,6 +91,7 @@ _sig = {
     "dory_last_error": (ctypes.c_char_p, [_P]),
     "dory_set_trace": (_I, [_P, _P, _I]),
     "dory_set_graphs": (_I, [_P, _I]),
+    "dory_set_markers": (_I, [_P, _I]),
     "dory_resume": (_I, [_P, _I, _I, _I, _I]),
     "dory_prefill_mixed": (_I, [_P, _P, _I, _I, _P, _I]),
     "dory_decode_step_mixed": (_I, [_P, _P, _P, _I, _P]),
@@ -394,6 +395,10 @@ class Session:
 
     def set_graphs(self, enable: bool) -> None:
         self._check(_lib.dory_set_graphs(self.h, 1 if enable else 0))
+
+    def set_markers(self, enable: bool) -> None:
+        """roctx ranges around calls and layer applications (rocprofv3 --marker-trace)."""
+        self._check(_lib.dory_set_markers(self.h, 1 if enable else 0))
 
     TIME_KINDS = {"ug": 1, "qkvg": 2, "down": 3, "o": 4, "attn": 5}
 

@@ -3,11 +3,13 @@
 // controller that runs the input block once, the shared recurrent block
 // n_loops times with the input block's output re-injected before every pass,
 // and the output block once.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -41,6 +43,7 @@ struct dory_ctx {
   // stream, which cannot be recorded), ordered after and before the caller's
   // stream by two events.
   bool graphs_on = false;
+  bool markers = false;  // profiler ranges around calls, loop passes and layer applications
   // position of the decode step's new key, passed by value to the decode
   // attention on eager, uncaptured calls; -1: kernels read the device counter
   int t_now = -1;
@@ -142,6 +145,46 @@ dory_status proj_pro(dory_ctx* c, const GemvPro& p, const void* W, const void* S
 
 // Key splits of decode attention: about 128 keys per workgroup, at most
 // kMaxSplits, and no more than ~4 workgroups per CU over all (row, kv head).
+// Profiler ranges (roctx), resolved from the ROCm marker library on first
+// use; a no-op unless the context has them switched on.
+struct RoctxApi {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+const RoctxApi& roctx_api() {
+  static RoctxApi api;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"}) {
+      void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (!h) continue;
+      auto push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+      auto pop = (int (*)())dlsym(h, "roctxRangePop");
+      if (push && pop) {
+        api.push = push;
+        api.pop = pop;
+        return;
+      }
+    }
+  });
+  return api;
+}
+
+struct Range {
+  bool on;
+  Range(const dory_ctx* c, const char* fmt, int x = 0, int y = 0) : on(c->markers && roctx_api().push) {
+    if (!on) return;
+    char buf[96];
+    std::snprintf(buf, sizeof buf, fmt, x, y);
+    roctx_api().push(buf);
+  }
+  ~Range() {
+    if (on) roctx_api().pop();
+  }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
 int choose_splits_decode(int keys, int B, int nkv) {
   int s = (keys + 127) / 128;
   const int cap = (1024 + B * nkv - 1) / (B * nkv);
@@ -159,6 +202,7 @@ dory_status decode_attention(dory_ctx* c, int l, int loop, int B, bool write_kv,
 // which must still hold the previous calls' entries (a ring slot overwritten
 // by loop 1 would lose keys that loop 2 still needs).
 dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int app, bool write_kv) {
+  Range range(c, "layer %d loop %d", l, loop);
   const Plan& P = c->plan;
   const dory_config& C = P.cfg;
   const WsLayout& W = P.ws;
@@ -352,6 +396,7 @@ dory_status run_decode_fused(dory_ctx* c, const int32_t* tok, int B, int k) {
   if (any_acc) HIP_TRY(c, launch_zero_u64(acc, acc_n, st));
   const float* pending_alpha = nullptr;  // MLP update not yet applied to the residual
   auto app = [&](int l, int j, bool write_kv) -> dory_status {
+    Range range(c, "layer %d loop %d", l, j);
     if (pending_alpha) {
       const bool first_rec = l == C.n_in;
       GemvPro pr{};
@@ -916,6 +961,7 @@ dory_status dory_prefill(dory_ctx* c, const int32_t* tokens_dev, int32_t batch, 
   c->err.clear();
   s = device_init(c);
   if (s != DORY_OK) return s;
+  Range range(c, "dory_prefill n=%d k=%d", n, n_loops);
   const int chunk = c->plan.cfg.max_chunk;
   for (int s0 = 0; s0 < n; s0 += chunk) {
     const int m = std::min(chunk, n - s0);
@@ -939,6 +985,7 @@ dory_status dory_decode_step(dory_ctx* c, const int32_t* tokens_dev, int32_t n_l
   const Plan& P = c->plan;
   const int32_t* tok = tokens_dev ? tokens_dev : wsp<int32_t>(c, P.ws.next);
   const bool fused = fused_decode_ok(c, c->batch);
+  Range range(c, "dory_decode_step k=%d batch=%d", n_loops, c->batch);
   if (fused && c->graphs_on && !tokens_dev && c->time_kind == 0) {
     s = decode_graph(c, n_loops);
   } else {
@@ -1066,6 +1113,13 @@ dory_status dory_set_trace(dory_ctx* c, float* trace_dev, int32_t max_apps) {
   return DORY_OK;
 }
 
+dory_status dory_set_markers(dory_ctx* c, int32_t enable) {
+  if (!c) return DORY_E_ARG;
+  if (enable && !roctx_api().push) return set_err(c, DORY_E_ARG, "no ROCm marker (roctx) library could be loaded");
+  c->markers = enable != 0;
+  return DORY_OK;
+}
+
 dory_status dory_set_graphs(dory_ctx* c, int32_t enable) {
   if (!c) return DORY_E_ARG;
   c->graphs_on = enable != 0;
@@ -1183,11 +1237,16 @@ dory_status dory_backward_last_loop(dory_ctx* c, const float* x, const float* gr
   DORY_TRY(device_init(c));
   auto at = [&](int i) { return Bw{b.c, bw_layer_view(b.L, i), b.ws, b.B, b.n, b.M}; };
   const size_t rows = (size_t)b.M * C.d_model;
+  Range range(c, "dory_backward_last_loop rows=%d", b.M);
   HIP_TRY(c, hipMemcpyAsync(b.h_at(0), x, rows * 4, hipMemcpyDeviceToDevice, c->st));
-  for (int i = 0; i < C.n_rec; ++i) DORY_TRY(bw_layer_fwd(at(i), C.n_in + i, b.h_at(i), b.h_at(i + 1)));
+  for (int i = 0; i < C.n_rec; ++i) {
+    Range r(c, "forward layer %d", C.n_in + i);
+    DORY_TRY(bw_layer_fwd(at(i), C.n_in + i, b.h_at(i), b.h_at(i + 1)));
+  }
   float* dh = b.f<float>(b.L.dh);
   HIP_TRY(c, launch_bw_final(b.h_at(C.n_rec), grad_out, b.M, C.d_model, dh, c->st));
   for (int i = C.n_rec - 1; i >= 0; --i) {
+    Range r(c, "backward layer %d", C.n_in + i);
     if (!stored && i < C.n_rec - 1) DORY_TRY(bw_layer_fwd(b, C.n_in + i, b.h_at(i), b.h_at(i + 1)));  // recompute
     DORY_TRY(bw_layer_bwd(at(i), C.n_in + i, i, b.h_at(i), b.h_at(i + 1), dh, dh, g));
   }

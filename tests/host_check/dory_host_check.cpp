@@ -306,6 +306,12 @@ void check_context_errors() {
   CHECK(dory_prefill_mixed(ctx, tok, 2, 4, loops_ok, DORY_KV_PER_LOOP) == DORY_E_KV_MODE, "mixed per-loop");
   CHECK(dory_decode_step_mixed(ctx, tok, loops_ok, DORY_KV_LAST_LOOP, out) == DORY_E_STATE,
         "mixed decode before prefill");
+  {
+    const dory_status m = dory_set_markers(ctx, 1);  // the marker library may be absent: then an argument error
+    CHECK(m == DORY_OK || m == DORY_E_ARG, "set_markers status %d", (int)m);
+    CHECK(dory_set_markers(ctx, 0) == DORY_OK, "markers off");
+    CHECK(dory_set_markers(nullptr, 1) == DORY_E_ARG, "markers on a NULL context");
+  }
   CHECK(dory_set_trace(ctx, (float*)dummy, 0) == DORY_E_ARG, "trace of 0 entries");
   CHECK(dory_set_trace(ctx, nullptr, 0) == DORY_OK, "trace off");
   CHECK(dory_reset(ctx) == DORY_OK && std::strlen(dory_last_error(ctx)) == 0, "reset clears the error");

@@ -430,3 +430,59 @@ def test_bf16_decode_graph_replays_match_eager(mode):
     # the greedy tokens are the argmax of the logits they follow
     for (la, ta) in runs[1]:
         np.testing.assert_array_equal(np.argmax(la, axis=-1), ta)
+
+
+# ---------------------------------------------------------------------------
+# a decode step captured into the caller's own graph: the library sees the
+# capture and has the decode attention read the position from the device
+# counter (on eager calls it passes the position by value), so every replay
+# continues the sequence
+# ---------------------------------------------------------------------------
+def test_bf16_decode_captured_by_caller_replays_match_eager():
+    m, w, dw = model_and_weights("tiny_bf16")
+    B, ctx, k, steps = 2, 192, 2, 6
+    prompt = torch.from_numpy(make_tokens(m, 31, (B, 50))).cuda()
+    stream = torch.cuda.Stream()
+    ref = []
+    s = dory.Session(m, dw, max_batch=B, max_ctx=ctx, max_chunk=64, kv_mode="last_loop", stream=stream)
+    with torch.cuda.stream(stream):
+        s.prefill(prompt, k)
+        for _ in range(steps):
+            s.decode(None, k)
+            ref.append(s.logits().clone())
+    torch.cuda.synchronize()
+    s2 = dory.Session(m, dw, max_batch=B, max_ctx=ctx, max_chunk=64, kv_mode="last_loop", stream=stream)
+    with torch.cuda.stream(stream):
+        s2.prefill(prompt, k)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("capturing one decode step", flush=True)
+    with torch.cuda.graph(g, stream=stream):
+        s2.decode(None, k)           # recorded, not run: replays advance the device position
+    got = []
+    for i in range(steps):
+        with torch.cuda.stream(stream):                     # the replay and the copy on the session's stream
+            g.replay()
+            got.append(s2.logits().clone())
+        junk = torch.randn(4096, device="cuda").sum()      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+    for i, (a, b) in enumerate(zip(ref, got)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy(), err_msg=f"replay {i}")
+
+
+def test_markers_leave_results_unchanged():
+    """roctx ranges around calls and layer applications are host-side only."""
+    m, w, dw = model_and_weights("tiny_bf16")
+    prompt = make_tokens(m, 32, (1, 40))
+    outs = []
+    for markers in (False, True):
+        s = session(m, dw, batch=1, max_ctx=128, chunk=64, kv_mode="per_loop", k=2)
+        try:
+            s.set_markers(markers)
+        except dory.DoryError:
+            pytest.skip("no ROCm marker library on this machine")
+        toks, logits, _ = generate(s, prompt, 5, 2)
+        outs.append((toks, logits))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
