@@ -565,11 +565,17 @@ dory_status decode_graph(dory_ctx* c, int k) {
     c->graphs.push_back(g);
     x = g.x;
   }
-  HIP_TRY(c, hipEventRecord(c->gev[0], c->st));
-  HIP_TRY(c, hipStreamWaitEvent(c->gst, c->gev[0], 0));
-  HIP_TRY(c, hipGraphLaunch(x, c->gst));
-  HIP_TRY(c, hipEventRecord(c->gev[1], c->gst));
-  HIP_TRY(c, hipStreamWaitEvent(c->st, c->gev[1], 0));
+  if (c->st) {
+    // straight onto the caller's stream (a graph recorded on one stream runs on any)
+    HIP_TRY(c, hipGraphLaunch(x, c->st));
+  } else {
+    // the legacy null stream: on the private stream, ordered after and before it by events
+    HIP_TRY(c, hipEventRecord(c->gev[0], c->st));
+    HIP_TRY(c, hipStreamWaitEvent(c->gst, c->gev[0], 0));
+    HIP_TRY(c, hipGraphLaunch(x, c->gst));
+    HIP_TRY(c, hipEventRecord(c->gev[1], c->gst));
+    HIP_TRY(c, hipStreamWaitEvent(c->st, c->gev[1], 0));
+  }
   c->has_logits = true;
   return DORY_OK;
 }
