@@ -517,6 +517,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// llrint(S * 2^e) in float32 and integer arithmetic (S * 2^e is exact in
+// float32 here, so rounding it to the nearest integer, ties to even, then
+// splitting off the high 32 bits gives the float64 route's result bit for bit)
+__device__ __forceinline__ long long fixed_point(float S, int e) {
+  const float r = rintf(ldexpf(S, e));
+  const float mag = fabsf(r);
+  const float hi = floorf(mag * 0x1p-32f);
+  const float lo = mag - hi * 0x1p32f;  // exact: < 2^32, at most 24 significant bits
+  const unsigned long long u = ((unsigned long long)(unsigned)hi << 32) | (unsigned long long)(unsigned)lo;
+  return r < 0.f ? -(long long)u : (long long)u;
+}
+
 template <int HD, int G, bool FULL>
 __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   constexpr int NKK = HD / 32;        // depth steps of the score product
@@ -674,6 +686,11 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
   bf16x8_t qb[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qb[kk] = *(const bf16x8_t*)&qs[c16][kk * 32 + 8 * g4];
+  // the output gate's sigmoid, while the tiles are still arriving
+  if (a.acc && a.gate) {
+#pragma unroll
+    for (int it = 0; it < NE; ++it) gx[it] = sigmoidf_(gx[it]);
+  }
 
   // q and k are unit vectors, so no score exceeds the scale: while
   // sl2 = scale log2(e) is at most 40 the exponents are referenced to that
@@ -828,12 +845,12 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(AttnDecArgs a) {
       float S = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) S = fmaf(d < HD ? wacc[w][g][d] : wl[w][g], fw[w][g], S);
-      if (d < HD && a.gate) S *= sigmoidf_(gx[it]);
+      if (d < HD && a.gate) S *= gx[it];  // the sigmoid, taken during the set-up
       if (S == 0.f) continue;
       const int bin = binh[g];
       unsigned long long* ap = a.acc + ((size_t)b * a.nq + hq) * stride;
       atomicAdd(d < HD ? ap + bin * HD + d : ap + a.acc_nb * HD + bin,
-                (unsigned long long)llrint(ldexp((double)S, 36 + kAttnAccBinBits * bin)));
+                (unsigned long long)fixed_point(S, 36 + kAttnAccBinBits * bin));
     }
     write_self();
     return;
