@@ -40,6 +40,12 @@ def _model(name):
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, name="tiny_bf16")
         elif name == "tiny_bf16_s30":  # softmax scale 30: too large for the fixed-point bins
             m = get_config("tiny").replace(dtype="bf16", d_ff=688, attn_scale=30.0, name="tiny_bf16_s30")
+        elif name == "tiny_bf16_w40":  # hd 64, a 40-key ring: a multiple of 8 but not of 32
+            m = get_config("tiny").replace(dtype="bf16", d_ff=688, window=40, name="tiny_bf16_w40")
+        elif name == "c36w_w40":       # the c36w weights (hd 128) with 40-key rings
+            m0, w, dw = _model("c36w")
+            _cache[name] = (m0.replace(window=40, name="c36w_w40"), w, dw)
+            return _cache[name]
         else:
             raise KeyError(name)
         w = make_weights(m)
@@ -210,4 +216,23 @@ def test_large_softmax_scale_takes_float_merge():
     g_tok, g_log, _ = generate(s, prompt, steps, k)
     assert np.all(np.isfinite(g_log))
     assert _report("tiny bf16 attn_scale 30", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+
+
+# ---------------------------------------------------------------------------
+# ring layers whose window is a multiple of 8 but not of 32: the ring's last
+# 32-slot tile runs past the ring; decode from before the ring fills (every
+# slot above t unwritten) through several wraps
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,k,mode", [("tiny_bf16_w40", 2, "last_loop"), ("c36w_w40", 2, "per_loop")])
+def test_decode_ring_window_not_multiple_of_32(name, k, mode):
+    m, w, dw = _model(name)
+    n, steps, ctx = 24, 64, 96
+    prompt = make_tokens(m, 90, (1, n))
+    print(f"{name} k={k} {mode}: oracle", flush=True)
+    ora = LoopedNGPT(m, w, max_ctx=ctx)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode)
+    s = session(m, dw, batch=1, max_ctx=ctx, chunk=n, kv_mode=mode, k=k)
+    g_tok, g_log, _ = generate(s, prompt, steps, k)
+    assert _report(f"{name} ring decode {mode} k={k}", g_log, o_log) <= BF16_TOL
     np.testing.assert_array_equal(g_tok, o_tok)
