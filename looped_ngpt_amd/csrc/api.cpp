@@ -637,8 +637,18 @@ struct Bw {
 };
 
 // y[M][N] = x[M][K] . W[N][K]^T, float32 out, operands in the model dtype
-dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K) {
-  HIP_TRY(c, launch_linear(c->plan.cfg.dtype, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
+// y [M][N] = x . W^T in float32. With `part` (room for M x N floats), a
+// product whose output tiles would leave half of the CUs idle runs the two
+// halves of its contraction side by side, then y = (first half) + (second)
+dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K,
+                    float* part = nullptr) {
+  const int dt = c->plan.cfg.dtype;
+  if (part && gemm_split2_pays(dt, M, N, K)) {
+    HIP_TRY(c, launch_gemm_split2(x, ldx, W, y, part, M, N, K, 1.f, c->st));
+    HIP_TRY(c, launch_bw_add(y, part, y, (int64_t)M * N, c->st));
+    return DORY_OK;
+  }
+  HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
   return DORY_OK;
 }
 
@@ -688,13 +698,13 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   }
   HIP_TRY(c, launch_bw_gate_fwd(dt, b.f<float>(L.o), b.f<float>(L.P1), Q, qd + 2 * P.kv_dim, C.attn_gate,
                                 C.head_dim, qd, M, b.f<float>(L.oh), b.ws + L.ohb, b.f<float>(L.rc), st));
-  DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd));
+  DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd, b.f<float>(L.part)));
   HIP_TRY(c, launch_bw_update_fwd(dt, h_in, b.f<float>(L.y), c->alpha_attn[l], M, d, b.f<float>(L.yh),
                                   b.f<float>(L.ry), b.f<float>(L.rz), b.f<float>(L.h1), b.ws + L.h1b, st));
   DORY_TRY(bw_gemm(c, b.ws + L.h1b, d, c->ug[l], b.f<float>(L.P2), M, 2 * F, d));
   HIP_TRY(c, launch_bw_swiglu_fwd(dt, b.f<float>(L.P2), F, M, b.f<float>(L.a32), b.ws + L.ab, b.f<float>(L.rs),
                                   st));
-  DORY_TRY(bw_gemm(c, b.ws + L.ab, F, c->down[l], b.f<float>(L.y), M, d, F));
+  DORY_TRY(bw_gemm(c, b.ws + L.ab, F, c->down[l], b.f<float>(L.y), M, d, F, b.f<float>(L.part)));
   HIP_TRY(c, launch_bw_update_fwd(dt, b.f<float>(L.h1), b.f<float>(L.y), c->alpha_mlp[l], M, d, b.f<float>(L.y2h),
                                   b.f<float>(L.ry2), b.f<float>(L.rz2), h_out, nullptr, st));
   return DORY_OK;
@@ -714,7 +724,9 @@ dory_status bw_wgrad(const Bw& b, const void* dY, int N, const void* X, int K, f
 dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX) {
   dory_ctx* c = b.c;
   HIP_TRY(c, launch_bw_transpose(c->plan.cfg.dtype, W, K, b.ws + b.L.WT, N, K, c->st));
-  return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N);
+  const Plan& P = c->plan;
+  float* part = K <= std::max(P.cfg.d_model, P.q_dim) ? b.f<float>(b.L.part) : nullptr;
+  return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N, part);
 }
 
 // backward of recurrent layer l (its forward values in the workspace):

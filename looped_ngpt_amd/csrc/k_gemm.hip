@@ -194,7 +194,7 @@ __device__ __forceinline__ int big_off(int r, int c) { return r * 128 + ((c ^ ((
 template <int EPI, int BN>
 __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, int64_t lda,
                                                    const bf16* __restrict__ B, void* __restrict__ C, int M, int N,
-                                                   int K, float scale) {
+                                                   int K, float scale, int64_t ldb, void* __restrict__ C1) {
   static_assert(BN == 256 || (BN == 192 && EPI == EPI_F32), "tile widths");
   constexpr int WM = BN == 256 ? 2 : 4;  // waves along M
   constexpr int WN = 8 / WM;             // waves along N
@@ -216,6 +216,13 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
   const int per = (nt + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (t >= nt) return;
+  // split of the contraction (blockIdx.y): columns y K .. y K + K - 1 of A
+  // and B, partial sums into C (y = 0) or C1 (y = 1)
+  if (blockIdx.y) {
+    A += (size_t)blockIdx.y * K;
+    B += (size_t)blockIdx.y * K;
+    C = C1;
+  }
   const int grp = t / (kBigGroupM * nN);
   const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
   const int loc = t - grp * kBigGroupM * nN;
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
     } else {
       wr = min(n0 + r, N - 1);
     }
-    srcB[i] = B + (size_t)wr * K + (ls ^ ((r >> 1) & 7)) * 8;
+    srcB[i] = B + (size_t)wr * ldb + (ls ^ ((r >> 1) & 7)) * 8;
   }
   auto issueA = [&](int kt, int i0, int i1) {
     unsigned char* st = sA + (kt % 3) * kHA;
@@ -368,19 +375,19 @@ static constexpr uint32_t big_lds(int bn) { return 3 * 256 * 128 + 2 * bn * 128;
 // (set once per process)
 template <int EPI, int BN>
 static void big_launch(dim3 grid, const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K, float scale,
-                       hipStream_t st) {
+                       hipStream_t st, int64_t ldw, void* y1 = nullptr) {
   static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_big<EPI, BN>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)big_lds(BN));
   (void)attr;
-  dory_launch((k_gemm_big<EPI, BN>), grid, dim3(512), big_lds(BN), st, x, ldx, W, y, M, N, K, scale);
+  dory_launch((k_gemm_big<EPI, BN>), grid, dim3(512), big_lds(BN), st, x, ldx, W, y, M, N, K, scale, ldw, y1);
 }
 
-// tile width for a large-M GEMM with N outputs: 192 when 256-wide tiles would
-// leave the last round of workgroups (one per CU) at most half full and
-// 192-wide ones do better
-static int big_tile_n(int M, int N) {
+// tile width for a large-M GEMM with N outputs (run `splits` times over, one
+// per part of the contraction): 192 when 256-wide tiles would leave the last
+// round of workgroups (one per CU) at most half full and 192-wide ones do better
+static int big_tile_n(int M, int N, int splits = 1) {
   auto eff = [&](int bn) {
-    const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+    const long tiles = (long)splits * ((M + 255) / 256) * ((N + bn - 1) / bn);
     const long rounds = (tiles + kNumCUs - 1) / kNumCUs;
     return (double)tiles / (double)(rounds * kNumCUs) * (bn == 256 ? 1.0 : 0.93);  // 192: more LDS reads per FLOP
   };
@@ -626,9 +633,9 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     const int bn = EPI == EPI_SWIGLU ? 256 : big_tile_n(M, N);
     const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + bn - 1) / bn);
     if (bn == 192)
-      big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+      big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
     else
-      big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
+      big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
   } else if (sizeof(T) == 2 && al16 && K % kStrBK == 0 && M <= 64) {
     skinny_launch<EPI>((const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
   } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
@@ -640,6 +647,28 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     dim3 grid((nout + 63) / 64, (M + 63) / 64);
     dory_launch((k_gemm_simple<T, EPI>), grid, dim3(256), 0, st, x, ldx, W, y, M, N, K, scale);
   }
+  return hipGetLastError();
+}
+
+bool gemm_split2_pays(int dtype, int M, int N, int K) {
+  if (dtype != 1 || M < 1024 || N <= 0 || K % (2 * kBigBK) != 0 || K / 2 < 16 * kBigBK) return false;
+  const int bn = big_tile_n(M, N);
+  const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+  return 2 * tiles <= kNumCUs;
+}
+
+hipError_t launch_gemm_split2(const void* x, int64_t ldx, const void* W, float* y0, float* y1, int M, int N, int K,
+                              float scale, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const bool al16 = ldx % 8 == 0 && (((uintptr_t)x & 15) == 0) && (((uintptr_t)W & 15) == 0);
+  if (!al16 || K % (2 * kBigBK) != 0 || y0 == nullptr || y1 == nullptr) return hipErrorInvalidValue;
+  const int bn = big_tile_n(M, N, 2);
+  const int tiles = ((M + 255) / 256) * ((N + bn - 1) / bn);
+  const dim3 grid((tiles + 7) / 8 * 8, 2);
+  if (bn == 192)
+    big_launch<EPI_F32, 192>(grid, (const bf16*)x, ldx, (const bf16*)W, y0, M, N, K / 2, scale, st, K, y1);
+  else
+    big_launch<EPI_F32, 256>(grid, (const bf16*)x, ldx, (const bf16*)W, y0, M, N, K / 2, scale, st, K, y1);
   return hipGetLastError();
 }
 

@@ -185,6 +185,14 @@ hipError_t launch_linear(int dtype, const void* x, int64_t ldx, const void* W, v
 // the matrix-core GEMMs of launch_linear (any M; meant for M > 8)
 hipError_t launch_gemm(int dtype, const void* x, int64_t ldx, const void* W, void* y, int M, int N, int K, int epi,
                        float scale, hipStream_t st);
+// The contraction of a float32-output bfloat16 GEMM in two halves that one
+// launch runs side by side: y0 = x[:, :K/2] . W[:, :K/2]^T and
+// y1 = x[:, K/2:] . W[:, K/2:]^T (y0 + y1 is the product). For large-M shapes
+// whose output tiles alone fill at most half of the CUs (gemm_split2_pays).
+// Needs K % 128 == 0 and 16-byte aligned operands, else hipErrorInvalidValue.
+bool gemm_split2_pays(int dtype, int M, int N, int K);
+hipError_t launch_gemm_split2(const void* x, int64_t ldx, const void* W, float* y0, float* y1, int M, int N, int K,
+                              float scale, hipStream_t st);
 
 // Decode GEMV whose input row is produced in its own prologue: every
 // workgroup first issues its weight loads, then computes for each of the M

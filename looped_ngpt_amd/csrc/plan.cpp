@@ -183,6 +183,7 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
   w.dres = take(M * d * 4);
   w.contrib = take(M * d * 4);
   w.tmp = take(M * std::max(d, std::max(F, qd)) * 4);
+  w.part = take(M * std::max(d, qd) * 4);
   w.dh = take(M * d * 4);
   w.dh2 = take(M * d * 4);
   w.dO = take(M * qd * 4);

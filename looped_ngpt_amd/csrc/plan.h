@@ -95,6 +95,7 @@ struct BwLayout {
   size_t P2 = 0, a32 = 0, rs = 0;                   // up/gate projection, activation, |s|
   size_t y2h = 0, ry2 = 0, rz2 = 0;                 // update of the MLP sublayer
   size_t dres = 0, contrib = 0, tmp = 0, dh = 0, dh2 = 0;
+  size_t part = 0;  // second partial sum of a GEMM whose contraction is split in two ([M][max(d, qd)])
   size_t dO = 0, D = 0, dqn = 0, dkn = 0, dv = 0, dP1 = 0;
   size_t xb = 0, ohb = 0, h1b = 0, ab = 0, dyb = 0, dP2b = 0, dP1b = 0;  // T
   size_t TA = 0, TB = 0, WT = 0;                    // T: transposed operands of the gradient GEMMs

@@ -109,6 +109,22 @@ def test_backward_bf16_36layer_widths():
     _compare(cfg, got, ref, x.shape, 3e-2)
 
 
+def test_backward_bf16_split_contraction():
+    """d 256, d_ff 2048, 2 x 520 positions (1040 rows, a ragged last row tile): the output projections of
+    the MLP (contraction 2048) and the input gradient through up/gate (contraction 4096) have too few
+    output tiles to fill the chip, so each runs the two halves of its contraction side by side and adds
+    the partial sums afterwards."""
+    cfg = ModelConfig(name="bw_split", d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=2048,
+                      vocab=256, n_in=1, n_rec=2, n_out=1, window=37,
+                      layer_is_full=(False, False, True, False), rope_base_swa=1.0e4, rope_base_full=1.0e6,
+                      dtype="bf16", attn_gate=1, seed=17)
+    w = _alphas(cfg, make_weights(cfg), 94)
+    x, G = _inputs(cfg, 2, 520, 95)
+    ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
+    got = _run(cfg, w, x, G)
+    _compare(cfg, got, ref, x.shape, 3e-2)
+
+
 def test_backward_argument_errors():
     cfg = _small(1, "f32")
     w = make_weights(cfg)
