@@ -639,13 +639,16 @@ struct Bw {
 // y[M][N] = x[M][K] . W[N][K]^T, float32 out, operands in the model dtype
 // y [M][N] = x . W^T in float32. With `part` (room for M x N floats), a
 // product whose output tiles would leave half of the CUs idle runs the two
-// halves of its contraction side by side, then y = (first half) + (second)
+// halves of its contraction side by side: the first half's sums land in y,
+// the second's in part, and *y2 = part tells the caller to read y + part;
+// otherwise *y2 = nullptr and y holds the product
 dory_status bw_gemm(dory_ctx* c, const void* x, int64_t ldx, const void* W, float* y, int M, int N, int K,
-                    float* part = nullptr) {
+                    float* part = nullptr, const float** y2 = nullptr) {
   const int dt = c->plan.cfg.dtype;
-  if (part && gemm_split2_pays(dt, M, N, K)) {
+  if (y2) *y2 = nullptr;
+  if (part && y2 && gemm_split2_pays(dt, M, N, K)) {
     HIP_TRY(c, launch_gemm_split2(x, ldx, W, y, part, M, N, K, 1.f, c->st));
-    HIP_TRY(c, launch_bw_add(y, part, y, (int64_t)M * N, c->st));
+    *y2 = part;
     return DORY_OK;
   }
   HIP_TRY(c, launch_linear(dt, x, ldx, W, y, M, N, K, 0, 1.f, 0, c->st));
@@ -698,15 +701,16 @@ dory_status bw_layer_fwd(const Bw& b, int l, const float* h_in, float* h_out) {
   }
   HIP_TRY(c, launch_bw_gate_fwd(dt, b.f<float>(L.o), b.f<float>(L.P1), Q, qd + 2 * P.kv_dim, C.attn_gate,
                                 C.head_dim, qd, M, b.f<float>(L.oh), b.ws + L.ohb, b.f<float>(L.rc), st));
-  DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd, b.f<float>(L.part)));
+  const float* y2 = nullptr;
+  DORY_TRY(bw_gemm(c, b.ws + L.ohb, qd, c->o[l], b.f<float>(L.y), M, d, qd, b.f<float>(L.part), &y2));
   HIP_TRY(c, launch_bw_update_fwd(dt, h_in, b.f<float>(L.y), c->alpha_attn[l], M, d, b.f<float>(L.yh),
-                                  b.f<float>(L.ry), b.f<float>(L.rz), b.f<float>(L.h1), b.ws + L.h1b, st));
+                                  b.f<float>(L.ry), b.f<float>(L.rz), b.f<float>(L.h1), b.ws + L.h1b, st, y2));
   DORY_TRY(bw_gemm(c, b.ws + L.h1b, d, c->ug[l], b.f<float>(L.P2), M, 2 * F, d));
   HIP_TRY(c, launch_bw_swiglu_fwd(dt, b.f<float>(L.P2), F, M, b.f<float>(L.a32), b.ws + L.ab, b.f<float>(L.rs),
                                   st));
-  DORY_TRY(bw_gemm(c, b.ws + L.ab, F, c->down[l], b.f<float>(L.y), M, d, F, b.f<float>(L.part)));
+  DORY_TRY(bw_gemm(c, b.ws + L.ab, F, c->down[l], b.f<float>(L.y), M, d, F, b.f<float>(L.part), &y2));
   HIP_TRY(c, launch_bw_update_fwd(dt, b.f<float>(L.h1), b.f<float>(L.y), c->alpha_mlp[l], M, d, b.f<float>(L.y2h),
-                                  b.f<float>(L.ry2), b.f<float>(L.rz2), h_out, nullptr, st));
+                                  b.f<float>(L.ry2), b.f<float>(L.rz2), h_out, nullptr, st, y2));
   return DORY_OK;
 }
 
@@ -721,12 +725,15 @@ dory_status bw_wgrad(const Bw& b, const void* dY, int N, const void* X, int K, f
 }
 
 // dX [M][K] = dY [M][N] . W [N][K]: W is transposed into WT, then one GEMM
-dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX) {
+// (split as bw_gemm says when dX2 is given and M x K floats fit its buffer:
+// then dX + *dX2 is the gradient)
+dory_status bw_xgrad(const Bw& b, const void* dY, const void* W, int N, int K, float* dX,
+                     const float** dX2 = nullptr) {
   dory_ctx* c = b.c;
   HIP_TRY(c, launch_bw_transpose(c->plan.cfg.dtype, W, K, b.ws + b.L.WT, N, K, c->st));
   const Plan& P = c->plan;
   float* part = K <= std::max(P.cfg.d_model, P.q_dim) ? b.f<float>(b.L.part) : nullptr;
-  return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N, part);
+  return bw_gemm(c, dY, N, b.ws + b.L.WT, dX, b.M, K, N, part, dX2);
 }
 
 // backward of recurrent layer l (its forward values in the workspace):
@@ -753,9 +760,10 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
   HIP_TRY(c, launch_bw_swiglu_bwd(dt, tmp, b.f<float>(L.a32), b.f<float>(L.rs), b.f<float>(L.P2), F, M,
                                   b.ws + L.dP2b, st));
   DORY_TRY(bw_wgrad(b, b.ws + L.dP2b, 2 * F, b.ws + L.h1b, d, g->ug[i]));
-  DORY_TRY(bw_xgrad(b, b.ws + L.dP2b, c->ug[l], 2 * F, d, tmp));                  // [M][d]
+  const float* tmp2 = nullptr;
+  DORY_TRY(bw_xgrad(b, b.ws + L.dP2b, c->ug[l], 2 * F, d, tmp, &tmp2));           // [M][d]
   float* dh1 = b.f<float>(L.dh2);
-  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dh1, (int64_t)M * d, st));
+  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dh1, (int64_t)M * d, st, tmp2));
 
   // attention sublayer
   HIP_TRY(c, launch_bw_update_bwd(dt, dh1, b.f<float>(L.h1), b.f<float>(L.rz), b.f<float>(L.yh), b.f<float>(L.ry),
@@ -763,10 +771,10 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
                                   b.f<float>(L.contrib), st));
   HIP_TRY(c, launch_bw_colsum(b.f<float>(L.contrib), M, d, g->alpha_attn[i], tmp, st));
   DORY_TRY(bw_wgrad(b, b.ws + L.dyb, d, b.ws + L.ohb, qd, g->o[i]));
-  DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->o[l], d, qd, tmp));                       // doh [M][qd]
+  DORY_TRY(bw_xgrad(b, b.ws + L.dyb, c->o[l], d, qd, tmp, &tmp2));                // doh [M][qd]
   HIP_TRY(c, launch_bw_gate_bwd(tmp, b.f<float>(L.oh), b.f<float>(L.rc), b.f<float>(L.o), b.f<float>(L.P1), Q,
                                 qd + 2 * P.kv_dim, C.attn_gate, C.head_dim, qd, M, b.f<float>(L.dO),
-                                b.f<float>(L.dP1), st));
+                                b.f<float>(L.dP1), st, tmp2));
   if (bw_flash_supported(dt, C.head_dim, C.n_q_heads, C.n_kv_heads)) {
     // operand copies of this layer (the forward's may belong to another layer)
     const int nq = C.n_q_heads, nkv = C.n_kv_heads, hd = C.head_dim, kvd = P.kv_dim;
@@ -790,8 +798,8 @@ dory_status bw_layer_bwd(const Bw& b, int l, int i, const float* h_in, const flo
                                      C.n_kv_heads, C.head_dim, M, b.f<float>(L.dP1), Q, st));
   HIP_TRY(c, launch_bw_cast(dt, b.f<float>(L.dP1), b.ws + L.dP1b, (int64_t)M * Q, st));
   DORY_TRY(bw_wgrad(b, b.ws + L.dP1b, Q, b.ws + L.xb, d, g->qkvg[i]));
-  DORY_TRY(bw_xgrad(b, b.ws + L.dP1b, c->qkvg[l], Q, d, tmp));                    // [M][d]
-  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dhi, (int64_t)M * d, st));
+  DORY_TRY(bw_xgrad(b, b.ws + L.dP1b, c->qkvg[l], Q, d, tmp, &tmp2));             // [M][d]
+  HIP_TRY(c, launch_bw_add(b.f<float>(L.dres), tmp, dhi, (int64_t)M * d, st, tmp2));
   return DORY_OK;
 }
 

@@ -47,10 +47,63 @@ __global__ __launch_bounds__(256) void k_bw_transpose(const TI* __restrict__ in,
   }
 }
 
+// bfloat16 out [C][R] = in [R][C] (row stride ld) in 64 x 64 tiles: 16-byte
+// loads of 8 consecutive columns, 2-byte scatter into an LDS tile (rows of 66
+// elements: consecutive rows start 33 banks apart), 2-byte gathers of 8
+// consecutive rows and 16-byte stores. vin / vout: the 16-byte accesses are
+// aligned (ld a multiple of 8 and a 16-byte aligned base for the loads; R a
+// multiple of 8 and an aligned base for the stores); chunks that run past the
+// matrix edge, or any chunk without them, go element by element.
+__global__ __launch_bounds__(256) void k_bw_transpose16(const bf16* __restrict__ in, int64_t ld,
+                                                        bf16* __restrict__ out, int R, int C, int vin, int vout) {
+  __shared__ uint16_t tile[64][66];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const uint16_t* src = (const uint16_t*)in;
+  uint16_t* dst = (uint16_t*)out;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    uint16_t v[8];
+    if (vin && r < R && c + 8 <= C) {
+      const uint4 u = *(const uint4*)(src + (size_t)r * ld + c);
+      v[0] = u.x & 0xffff; v[1] = u.x >> 16; v[2] = u.y & 0xffff; v[3] = u.y >> 16;
+      v[4] = u.z & 0xffff; v[5] = u.z >> 16; v[6] = u.w & 0xffff; v[7] = u.w >> 16;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (r < R && c + e < C) ? src[(size_t)r * ld + c + e] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[rr][cc + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int cc = q >> 3, rr = (q & 7) * 8;  // output row c0 + cc, columns r0 + rr ..
+    const int c = c0 + cc, r = r0 + rr;
+    if (c >= C) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[rr + e][cc];
+    if (vout && r + 8 <= R) {
+      uint4 u;
+      u.x = v[0] | ((uint32_t)v[1] << 16); u.y = v[2] | ((uint32_t)v[3] << 16);
+      u.z = v[4] | ((uint32_t)v[5] << 16); u.w = v[6] | ((uint32_t)v[7] << 16);
+      *(uint4*)(dst + (size_t)c * R + r) = u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r + e < R) dst[(size_t)c * R + r + e] = v[e];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_bw_add(const float* __restrict__ a, const float* __restrict__ b,
-                                                float* __restrict__ out, int64_t n) {
+                                                const float* __restrict__ b2, float* __restrict__ out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = a[i] + b[i];
+  if (i < n) out[i] = a[i] + (b2 ? b[i] + b2[i] : b[i]);
 }
 
 // out[c][j] = sum of in[r][j] over the rows r of chunk c (blockIdx.y, rc rows
@@ -70,8 +123,10 @@ __global__ __launch_bounds__(256) void k_bw_colsum(const float* __restrict__ in,
 // forward with the values the backward needs
 // ---------------------------------------------------------------------------
 // h' = norm(h + alpha (norm(y) - h)); keeps norm(y), |y|, |z| and h'
+// (y2: optional second partial sum of y)
 template <typename T>
 __global__ __launch_bounds__(256) void k_bw_update_fwd(const float* __restrict__ h, const float* __restrict__ y,
+                                                       const float* __restrict__ y2,
                                                        const float* __restrict__ alpha, int d,
                                                        float* __restrict__ yh, float* __restrict__ ry,
                                                        float* __restrict__ rz, float* __restrict__ hout,
@@ -80,12 +135,17 @@ __global__ __launch_bounds__(256) void k_bw_update_fwd(const float* __restrict__
   const size_t r = blockIdx.x;
   const float* hr = h + r * d;
   const float* yr = y + r * d;
+  const float* y2r = y2 ? y2 + r * d : nullptr;
+  auto yv = [&](int j) { return y2r ? yr[j] + y2r[j] : yr[j]; };
   float ss = 0.f;
-  for (int j = threadIdx.x; j < d; j += 256) ss += yr[j] * yr[j];
+  for (int j = threadIdx.x; j < d; j += 256) {
+    const float v = yv(j);
+    ss += v * v;
+  }
   const float ny = guard_norm(block_sum<256>(ss, sh));
   float sz = 0.f;
   for (int j = threadIdx.x; j < d; j += 256) {
-    const float yn = yr[j] / ny;
+    const float yn = yv(j) / ny;
     const float z = hr[j] + alpha[j] * (yn - hr[j]);
     yh[r * d + j] = yn;
     hout[r * d + j] = z;
@@ -321,17 +381,18 @@ __global__ __launch_bounds__(256) void k_bw_gate_bwd(const float* __restrict__ d
                                                      const float* __restrict__ rc, const float* __restrict__ o,
                                                      const float* __restrict__ P1, int ldp, int goff, int mode,
                                                      int hd, int qd, float* __restrict__ dO,
-                                                     float* __restrict__ dP1) {
+                                                     float* __restrict__ dP1, const float* __restrict__ doh2) {
   __shared__ float sh[4];
   const size_t r = blockIdx.x;
+  auto dv = [&](int j) { return doh2 ? doh[r * qd + j] + doh2[r * qd + j] : doh[r * qd + j]; };
   float s = 0.f;
-  for (int j = threadIdx.x; j < qd; j += 256) s += oh[r * qd + j] * doh[r * qd + j];
+  for (int j = threadIdx.x; j < qd; j += 256) s += oh[r * qd + j] * dv(j);
   const float od = block_sum<256>(s, sh);
   const float ic = 1.f / rc[r];
   const float* g = P1 + r * ldp + goff;
   float* dg = dP1 + r * ldp + goff;
   for (int j = threadIdx.x; j < qd; j += 256) {
-    const float dc = (doh[r * qd + j] - oh[r * qd + j] * od) * ic;
+    const float dc = (dv(j) - oh[r * qd + j] * od) * ic;
     if (mode == 1) {
       const float sg = sigmoidf_(g[j]);
       dO[r * qd + j] = dc * sg;
@@ -350,7 +411,7 @@ __global__ __launch_bounds__(256) void k_bw_gate_bwd(const float* __restrict__ d
       float acc = 0.f;
       for (int e = lane; e < hd; e += 64) {
         const int j = hh * hd + e;
-        acc += (doh[r * qd + j] - oh[r * qd + j] * od) * ic * o[r * qd + j];
+        acc += (dv(j) - oh[r * qd + j] * od) * ic * o[r * qd + j];
       }
       acc = wave_sum(acc);
       if (lane == 0) dg[hh] = acc * sg * (1.f - sg);
@@ -604,17 +665,20 @@ hipError_t launch_bw_transpose(int dt, const void* in, int64_t ld, void* out, in
   if (R <= 0 || C <= 0) return hipSuccess;
   if ((R + 31) / 32 > 65535) return hipErrorInvalidValue;
   const dim3 grid((C + 31) / 32, (R + 31) / 32);
-  if (dt == 1)
-    hipLaunchKernelGGL((k_bw_transpose<bf16, bf16>), grid, dim3(256), 0, st, (const bf16*)in, ld, (bf16*)out, R, C);
-  else
+  if (dt == 1) {
+    const int vin = ld % 8 == 0 && ((uintptr_t)in & 15) == 0;
+    const int vout = R % 8 == 0 && ((uintptr_t)out & 15) == 0;
+    hipLaunchKernelGGL(k_bw_transpose16, dim3((C + 63) / 64, (R + 63) / 64), dim3(256), 0, st, (const bf16*)in, ld,
+                       (bf16*)out, R, C, vin, vout);
+  } else
     hipLaunchKernelGGL((k_bw_transpose<float, float>), grid, dim3(256), 0, st, (const float*)in, ld, (float*)out, R,
                        C);
   return hipGetLastError();
 }
 
-hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st) {
+hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st, const float* b2) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bw_add, dim3(blocks_for(n)), dim3(256), 0, st, a, b, out, n);
+  hipLaunchKernelGGL(k_bw_add, dim3(blocks_for(n)), dim3(256), 0, st, a, b, b2, out, n);
   return hipGetLastError();
 }
 
@@ -633,12 +697,12 @@ hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, float* pa
 }
 
 hipError_t launch_bw_update_fwd(int dt, const float* h, const float* y, const float* alpha, int M, int d, float* yh,
-                                float* ry, float* rz, float* hout, void* hout_t, hipStream_t st) {
+                                float* ry, float* rz, float* hout, void* hout_t, hipStream_t st, const float* y2) {
   if (dt == 1)
-    hipLaunchKernelGGL((k_bw_update_fwd<bf16>), dim3(M), dim3(256), 0, st, h, y, alpha, d, yh, ry, rz, hout,
+    hipLaunchKernelGGL((k_bw_update_fwd<bf16>), dim3(M), dim3(256), 0, st, h, y, y2, alpha, d, yh, ry, rz, hout,
                        (bf16*)hout_t);
   else
-    hipLaunchKernelGGL((k_bw_update_fwd<float>), dim3(M), dim3(256), 0, st, h, y, alpha, d, yh, ry, rz, hout,
+    hipLaunchKernelGGL((k_bw_update_fwd<float>), dim3(M), dim3(256), 0, st, h, y, y2, alpha, d, yh, ry, rz, hout,
                        (float*)hout_t);
   return hipGetLastError();
 }
@@ -710,8 +774,9 @@ hipError_t launch_bw_swiglu_bwd(int dt, const float* da, const float* a32, const
 
 hipError_t launch_bw_gate_bwd(const float* doh, const float* oh, const float* rc, const float* o, const float* P1,
                               int ldp, int goff, int mode, int hd, int qd, int M, float* dO, float* dP1,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_bw_gate_bwd, dim3(M), dim3(256), 0, st, doh, oh, rc, o, P1, ldp, goff, mode, hd, qd, dO, dP1);
+                              hipStream_t st, const float* doh2) {
+  hipLaunchKernelGGL(k_bw_gate_bwd, dim3(M), dim3(256), 0, st, doh, oh, rc, o, P1, ldp, goff, mode, hd, qd, dO, dP1,
+                     doh2);
   return hipGetLastError();
 }
 

@@ -275,11 +275,15 @@ hipError_t launch_bw_flash_fwd(const BwFlash& a, hipStream_t st);
 hipError_t launch_bw_flash_bwd(const BwFlash& a, hipStream_t st);
 hipError_t launch_bw_cast(int dt_out, const float* in, void* out, int64_t n, hipStream_t st);
 hipError_t launch_bw_transpose(int dt, const void* in, int64_t ld, void* out, int R, int C, hipStream_t st);
-hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
+// out = a + b, or a + (b + b2) with b2 (the two partial sums of a split product)
+hipError_t launch_bw_add(const float* a, const float* b, float* out, int64_t n, hipStream_t st,
+                         const float* b2 = nullptr);
 // out[j] = sum over the M rows of in[r][j]; part: scratch of ceil(M/64) * d floats
 hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, float* part, hipStream_t st);
+// y2: optional second partial sum of y (y + y2 is the sublayer output)
 hipError_t launch_bw_update_fwd(int dt, const float* h, const float* y, const float* alpha, int M, int d, float* yh,
-                                float* ry, float* rz, float* hout, void* hout_t, hipStream_t st);
+                                float* ry, float* rz, float* hout, void* hout_t, hipStream_t st,
+                                const float* y2 = nullptr);
 hipError_t launch_bw_rope_norm_fwd(const float* P1, int ldp, const float2* tab, int n, int nq, int nkv, int hd, int M,
                                    float* qn, float* kn, float* rq, float* rk, hipStream_t st);
 hipError_t launch_bw_attn_fwd(const BwAttn& a, int M, float* o, float* mst, float* lst, hipStream_t st);
@@ -293,9 +297,10 @@ hipError_t launch_bw_update_bwd(int dt, const float* dho, const float* ho, const
                                 void* dy_t, float* contrib, hipStream_t st);
 hipError_t launch_bw_swiglu_bwd(int dt, const float* da, const float* a32, const float* rs, const float* P2, int F,
                                 int M, void* dP2, hipStream_t st);
+// doh2: optional second partial sum of doh
 hipError_t launch_bw_gate_bwd(const float* doh, const float* oh, const float* rc, const float* o, const float* P1,
                               int ldp, int goff, int mode, int hd, int qd, int M, float* dO, float* dP1,
-                              hipStream_t st);
+                              hipStream_t st, const float* doh2 = nullptr);
 hipError_t launch_bw_attn_bwd(const BwAttn& a, int M, const float* dO, const float* o, const float* mst,
                               const float* lst, float* D, float* dqn, float* dkn, float* dv, hipStream_t st);
 // dst [B][H][n][hd] (dt: 0 float32, 1 bfloat16) from float32 rows src[(b n + t) ld + off + h hd + d]
