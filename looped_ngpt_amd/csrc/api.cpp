@@ -669,6 +669,7 @@ BwFlash bw_flash_args(const Bw& b, bool full) {
   fa.scale = P.attn_scale;
   fa.mst = b.f<float>(L.mst); fa.lst = b.f<float>(L.lst); fa.D = b.f<float>(L.D);
   fa.o = b.f<float>(L.o); fa.dq = b.f<float>(L.dqn); fa.dk = b.f<float>(L.dkn); fa.dv = b.f<float>(L.dv);
+  fa.dkh = b.f<float>(L.fdkh); fa.dvh = b.f<float>(L.fdvh);
   return fa;
 }
 

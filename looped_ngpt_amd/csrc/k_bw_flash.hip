@@ -1,6 +1,7 @@
 // Attention of the depth-1 truncated backward on the matrix cores (bfloat16
 // models, head dim 64 or 128): the forward with its softmax statistics, dQ,
-// and dK / dV summed over the query heads of each kv head. Scores are never
+// and dK / dV per query head, then summed over the query heads of each kv
+// head. Scores are never
 // stored: every kernel recomputes its score tiles from q and k, so the
 // workspace stays O(n d) ("Dory1.0-4B: A Looped Normalized-GPT", ai.info AI
 // summary, Methodology in Plain English: backpropagation is truncated to the
@@ -40,32 +41,50 @@ __device__ __forceinline__ bool allowed(int t, int s, int window) {
   return s <= t && (window == 0 || t - s < window);
 }
 
-// Stage a [kFT rows][HD] tile of a head-major array (rows r0.., clamped to
-// n-1) into LDS rows of ld elements.
+// Staging of a tile in two halves, so that the global loads of the next tile
+// are in flight while the current one is multiplied: fetch_* loads into
+// registers (every thread HD/32 16-byte pieces), put_* writes them to LDS.
+//
+// [kFT rows][HD] of a head-major array (rows r0.., clamped to n-1), LDS rows
+// of ld elements
 template <int HD>
-__device__ __forceinline__ void stage_rows(const bf16* __restrict__ src, int n, int r0, bf16* dst, int ld) {
+__device__ __forceinline__ void fetch_rows(const bf16* __restrict__ src, int n, int r0, u32x4* v) {
   constexpr int CPK = HD / 8;
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) {
     const int e = threadIdx.x + 256 * i;
-    const int rr = e / CPK, c = e % CPK;
-    *(u32x4*)(dst + rr * ld + 8 * c) = *(const u32x4*)(src + (size_t)min(r0 + rr, n - 1) * HD + 8 * c);
+    v[i] = *(const u32x4*)(src + (size_t)min(r0 + e / CPK, n - 1) * HD + 8 * (e % CPK));
   }
 }
-
-// Stage the [HD][kFT] transposed tile (columns c0.., the source has nT
-// columns, zero past n) into LDS rows of ld elements, as 8-byte pieces.
 template <int HD>
-__device__ __forceinline__ void stage_cols(const bf16* __restrict__ srcT, int nT, int c0, bf16* dst, int ld) {
+__device__ __forceinline__ void put_rows(const u32x4* v, bf16* dst, int ld) {
+  constexpr int CPK = HD / 8;
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) {
     const int e = threadIdx.x + 256 * i;
-    const int d = e >> 3, run = e & 7;
-    const int c = min(c0 + 8 * run, nT - 8);  // past the last column: zeros / unused
-    const u32x4 v = *(const u32x4*)(srcT + (size_t)d * nT + c);
-    u32x2_t* p = (u32x2_t*)(dst + d * ld + 8 * run);
-    p[0] = u32x2_t{v[0], v[1]};
-    p[1] = u32x2_t{v[2], v[3]};
+    *(u32x4*)(dst + (e / CPK) * ld + 8 * (e % CPK)) = v[i];
+  }
+}
+
+// [HD][kFT] of a transposed array (columns c0.., nT columns, zero past n;
+// runs past nT clamped: their positions are masked), LDS rows of ld
+// elements written as 8-byte pieces
+template <int HD>
+__device__ __forceinline__ void fetch_cols(const bf16* __restrict__ srcT, int nT, int c0, u32x4* v) {
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    v[i] = *(const u32x4*)(srcT + (size_t)(e >> 3) * nT + min(c0 + 8 * (e & 7), nT - 8));
+  }
+}
+template <int HD>
+__device__ __forceinline__ void put_cols(const u32x4* v, bf16* dst, int ld) {
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    u32x2_t* p = (u32x2_t*)(dst + (e >> 3) * ld + 8 * (e & 7));
+    p[0] = u32x2_t{v[i][0], v[i][1]};
+    p[1] = u32x2_t{v[i][2], v[i][3]};
   }
 }
 
@@ -112,11 +131,18 @@ __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
   const int hi = min(i0 + kFR - 1, a.n - 1);
   const int lo = a.window ? max(0, i0 - a.window + 1) : 0;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  for (int s0 = lo / kFT * kFT; s0 <= hi; s0 += kFT) {
+  const int sfirst = lo / kFT * kFT, slast = hi / kFT * kFT;
+  u32x4 kr[HD / 32], vr[HD / 32];
+  fetch_rows<HD>(K, a.n, sfirst, kr);
+  fetch_cols<HD>(VT, a.nT, sfirst, vr);
+  for (int s0 = sfirst; s0 <= slast; s0 += kFT) {
+    __syncthreads();  // the previous tile is consumed
+    put_rows<HD>(kr, Ks, KLD);
+    put_cols<HD>(vr, Vt, VLD);
     __syncthreads();
-    stage_rows<HD>(K, a.n, s0, Ks, KLD);
-    stage_cols<HD>(VT, a.nT, s0, Vt, VLD);
-    __syncthreads();
+    const int s1 = min(s0 + kFT, slast);  // in flight during this tile (the last refetches itself)
+    fetch_rows<HD>(K, a.n, s1, kr);
+    fetch_cols<HD>(VT, a.nT, s1, vr);
     if (iw0 >= a.n || s0 > iw0 + 31) continue;
     f32x16_t sc[2];
 #pragma unroll
@@ -217,12 +243,21 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dq(BwFlash a) {
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   const int hi = min(i0 + kFR - 1, a.n - 1);
   const int lo = a.window ? max(0, i0 - a.window + 1) : 0;
-  for (int s0 = lo / kFT * kFT; s0 <= hi; s0 += kFT) {
+  const int sfirst = lo / kFT * kFT, slast = hi / kFT * kFT;
+  u32x4 kr[HD / 32], vr[HD / 32], ktr[HD / 32];
+  fetch_rows<HD>(K, a.n, sfirst, kr);
+  fetch_rows<HD>(V, a.n, sfirst, vr);
+  fetch_cols<HD>(KT, a.nT, sfirst, ktr);
+  for (int s0 = sfirst; s0 <= slast; s0 += kFT) {
     __syncthreads();
-    stage_rows<HD>(K, a.n, s0, Ks, KLD);
-    stage_rows<HD>(V, a.n, s0, Vs, KLD);
-    stage_cols<HD>(KT, a.nT, s0, KTs, VLD);
+    put_rows<HD>(kr, Ks, KLD);
+    put_rows<HD>(vr, Vs, KLD);
+    put_cols<HD>(ktr, KTs, VLD);
     __syncthreads();
+    const int s1 = min(s0 + kFT, slast);
+    fetch_rows<HD>(K, a.n, s1, kr);
+    fetch_rows<HD>(V, a.n, s1, vr);
+    fetch_cols<HD>(KT, a.nT, s1, ktr);
     if (iw0 >= a.n || s0 > iw0 + 31) continue;
     f32x16_t sc[2], dp[2];
 #pragma unroll
@@ -263,12 +298,16 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dq(BwFlash a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys of one (sequence, kv head), summed over
-// the G query heads of the group and every query that sees those keys
+// dK, dV of one query head: one workgroup per 128 keys of one (sequence, q
+// head), over every query that sees those keys; the G query heads of a kv
+// head write separate partial sums (dkh, dvh [B n][nq][HD]) that
+// k_bwf_sum_heads adds in head order. Workgroup ids: the eight XCDs take
+// every eighth head, and inside an XCD the key blocks with the most queries
+// start first.
 // ---------------------------------------------------------------------------
 template <int HD>
 __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
-  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32;
+  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32, NL = HD / 32;
   __shared__ __align__(16) bf16 Qs[kFT * KLD];
   __shared__ __align__(16) bf16 Ds_[kFT * KLD];
   __shared__ __align__(16) bf16 QTs[HD * VLD];
@@ -276,9 +315,11 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
   __shared__ float m2s[kFT], ils[kFT], Dq[kFT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lk = lane & 31, g = lane >> 5;
   const int nkb = (a.n + kFR - 1) / kFR;
-  const int kb = (int)(blockIdx.x % nkb);
-  const int bh = blockIdx.x / nkb, b = bh / a.nkv, kvh = bh % a.nkv;
-  const int G = a.nq / a.nkv;
+  const int BH = a.B * a.nq, hpx = (BH + 7) / 8;
+  const int j = (int)(blockIdx.x >> 3), bhq = (j % hpx) * 8 + (int)(blockIdx.x & 7);
+  const int kb = j / hpx;
+  if (bhq >= BH || kb >= nkb) return;
+  const int b = bhq / a.nq, hq = bhq % a.nq, kvh = hq / (a.nq / a.nkv);
   const int k0 = kb * kFR, kw0 = k0 + 32 * wave;
   const int s = min(kw0 + lk, a.n - 1);
   const size_t koff = ((size_t)b * a.nkv + kvh) * a.n * HD;
@@ -296,67 +337,86 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
     for (int r = 0; r < 16; ++r) ak[mb][r] = av[mb][r] = 0.f;
   const int khi = min(k0 + kFR - 1, a.n - 1);
   const int qlo = k0, qhi = a.window ? min(a.n - 1, khi + a.window - 1) : a.n - 1;
-  for (int h = 0; h < G; ++h) {
-    const int hq = kvh * G + h;
-    const size_t qoff = ((size_t)b * a.nq + hq) * a.n * HD;
-    const bf16* QT = a.QT + ((size_t)b * a.nq + hq) * HD * a.nT;
-    const bf16* DT = a.dOT + ((size_t)b * a.nq + hq) * HD * a.nT;
-    for (int q0 = qlo / kFT * kFT; q0 <= qhi; q0 += kFT) {
-      __syncthreads();
-      stage_rows<HD>(a.Q + qoff, a.n, q0, Qs, KLD);
-      stage_rows<HD>(a.dO + qoff, a.n, q0, Ds_, KLD);
-      stage_cols<HD>(QT, a.nT, q0, QTs, VLD);
-      stage_cols<HD>(DT, a.nT, q0, DTs, VLD);
-      if (tid < kFT) {
-        const size_t r = (size_t)b * a.n + min(q0 + tid, a.n - 1);
-        m2s[tid] = a.mst[r * a.nq + hq] * kLog2e;
-        ils[tid] = 1.f / a.lst[r * a.nq + hq];
-        Dq[tid] = a.D[r * a.nq + hq];
+  const size_t qoff = ((size_t)b * a.nq + hq) * a.n * HD;
+  const bf16* QT = a.QT + ((size_t)b * a.nq + hq) * HD * a.nT;
+  const bf16* DT = a.dOT + ((size_t)b * a.nq + hq) * HD * a.nT;
+  // per-query softmax terms of a tile: threads 0..63 hold one query each
+  auto fetch_stats = [&](int q0, float& m2, float& il, float& dd) {
+    if (tid < kFT) {
+      const size_t r = (size_t)b * a.n + min(q0 + tid, a.n - 1);
+      m2 = a.mst[r * a.nq + hq];
+      il = a.lst[r * a.nq + hq];
+      dd = a.D[r * a.nq + hq];
+    }
+  };
+  const int qfirst = qlo / kFT * kFT, qlast = qhi / kFT * kFT;
+  u32x4 qr[NL], dr[NL], qtr[NL], dtr[NL];
+  float m2r = 0.f, ilr = 1.f, ddr = 0.f;
+  fetch_rows<HD>(a.Q + qoff, a.n, qfirst, qr);
+  fetch_rows<HD>(a.dO + qoff, a.n, qfirst, dr);
+  fetch_cols<HD>(QT, a.nT, qfirst, qtr);
+  fetch_cols<HD>(DT, a.nT, qfirst, dtr);
+  fetch_stats(qfirst, m2r, ilr, ddr);
+  for (int q0 = qfirst; q0 <= qlast; q0 += kFT) {
+    __syncthreads();
+    put_rows<HD>(qr, Qs, KLD);
+    put_rows<HD>(dr, Ds_, KLD);
+    put_cols<HD>(qtr, QTs, VLD);
+    put_cols<HD>(dtr, DTs, VLD);
+    if (tid < kFT) {
+      m2s[tid] = m2r * kLog2e;
+      ils[tid] = 1.f / ilr;
+      Dq[tid] = ddr;
+    }
+    __syncthreads();
+    const int q1 = min(q0 + kFT, qlast);
+    fetch_rows<HD>(a.Q + qoff, a.n, q1, qr);
+    fetch_rows<HD>(a.dO + qoff, a.n, q1, dr);
+    fetch_cols<HD>(QT, a.nT, q1, qtr);
+    fetch_cols<HD>(DT, a.nT, q1, dtr);
+    fetch_stats(q1, m2r, ilr, ddr);
+    // queries of the tile that see some key of this wave
+    if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
+    f32x16_t sc[2], dp[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[qt][r] = dp[qt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (qt * 32 + lk) * KLD + 16 * ks + 8 * g;
+        sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Qs + o), kf[ks], sc[qt], 0, 0, 0);
+        dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ds_ + o), vf[ks], dp[qt], 0, 0, 0);
       }
-      __syncthreads();
-      // queries of the tile that see some key of this wave
-      if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
-      f32x16_t sc[2], dp[2];
+    }
+    bf16x8_t pb[2][2], db[2][2];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qt][r] = dp[qt][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int o = (qt * 32 + lk) * KLD + 16 * ks + 8 * g;
-          sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Qs + o), kf[ks], sc[qt], 0, 0, 0);
-          dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ds_ + o), vf[ks], dp[qt], 0, 0, 0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int t = q0 + qi;
+        const float p =
+            allowed(t, s, a.window) && t < a.n ? exp2f(fmaf(sc[qt][r], sl2, -m2s[qi])) * ils[qi] : 0.f;
+        pb[qt][r >> 3][r & 7] = (__bf16)p;
+        db[qt][r >> 3][r & 7] = (__bf16)(p * (dp[qt][r] - Dq[qi]));
       }
-      bf16x8_t pb[2][2], db[2][2];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int t = q0 + qi;
-          const float p =
-              allowed(t, s, a.window) && t < a.n ? exp2f(fmaf(sc[qt][r], sl2, -m2s[qi])) * ils[qi] : 0.f;
-          pb[qt][r >> 3][r & 7] = (__bf16)p;
-          db[qt][r >> 3][r & 7] = (__bf16)(p * (dp[qt][r] - Dq[qi]));
+        for (int hh = 0; hh < 2; ++hh) {
+          av[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(DTs, mb, qt, hh, lk, g), pb[qt][hh],
+                                                           av[mb], 0, 0, 0);
+          ak[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(QTs, mb, qt, hh, lk, g), db[qt][hh],
+                                                           ak[mb], 0, 0, 0);
         }
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            av[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(DTs, mb, qt, hh, lk, g), pb[qt][hh],
-                                                             av[mb], 0, 0, 0);
-            ak[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(QTs, mb, qt, hh, lk, g), db[qt][hh],
-                                                             ak[mb], 0, 0, 0);
-          }
-    }
   }
   if (kw0 >= a.n || kw0 + lk >= a.n) return;
   const size_t row = (size_t)b * a.n + s;
-  float* dk = a.dk + row * a.nkv * HD + (size_t)kvh * HD;
-  float* dv = a.dv + row * a.nkv * HD + (size_t)kvh * HD;
+  float* dk = a.dkh + row * a.nq * HD + (size_t)hq * HD;
+  float* dv = a.dvh + row * a.nq * HD + (size_t)hq * HD;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -365,6 +425,26 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
       dk[d] = a.scale * ak[mb][r];
       dv[d] = av[mb][r];
     }
+}
+
+// dk [B n][nkv][hd] = sum over the G query heads h of kv head k, in head
+// order, of dkh [B n][k G + h][hd] (the same for dv); one thread per output
+__global__ __launch_bounds__(256) void k_bwf_sum_heads(const float* __restrict__ dkh, const float* __restrict__ dvh,
+                                                       int G, int hd, int nkv, int64_t total, float* __restrict__ dk,
+                                                       float* __restrict__ dv) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int kvd = nkv * hd;
+  const int64_t row = e / kvd;
+  const int c = (int)(e % kvd), kvh = c / hd, d = c % hd;
+  const size_t src = (size_t)row * G * kvd + ((size_t)kvh * G) * hd + d;
+  float sk = dkh[src], sv = dvh[src];
+  for (int h = 1; h < G; ++h) {
+    sk += dkh[src + (size_t)h * hd];
+    sv += dvh[src + (size_t)h * hd];
+  }
+  dk[e] = sk;
+  dv[e] = sv;
 }
 
 // bfloat16 transposed head copies: dst[b][h][d][t] (nT columns, zero past n)
@@ -413,7 +493,9 @@ hipError_t launch_bw_flash_fwd(const BwFlash& a, hipStream_t st) {
 hipError_t launch_bw_flash_bwd(const BwFlash& a, hipStream_t st) {
   if (a.B * a.n <= 0) return hipSuccess;
   if (!bw_flash_supported(1, a.hd, a.nq, a.nkv) || a.nT < a.n || a.nT % 8) return hipErrorInvalidValue;
-  const dim3 gq((unsigned)((a.n + kFR - 1) / kFR * a.B * a.nq)), gk((unsigned)((a.n + kFR - 1) / kFR * a.B * a.nkv));
+  if (!a.dkh || !a.dvh) return hipErrorInvalidValue;
+  const int nkb = (a.n + kFR - 1) / kFR, hpx = (a.B * a.nq + 7) / 8;
+  const dim3 gq((unsigned)(nkb * a.B * a.nq)), gk((unsigned)((int64_t)nkb * hpx * 8));
   if (a.hd == 64) {
     hipLaunchKernelGGL(k_bwf_dq<64>, gq, dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_bwf_dkv<64>, gk, dim3(256), 0, st, a);
@@ -421,6 +503,9 @@ hipError_t launch_bw_flash_bwd(const BwFlash& a, hipStream_t st) {
     hipLaunchKernelGGL(k_bwf_dq<128>, gq, dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_bwf_dkv<128>, gk, dim3(256), 0, st, a);
   }
+  const int64_t total = (int64_t)a.B * a.n * a.nkv * a.hd;
+  hipLaunchKernelGGL(k_bwf_sum_heads, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const float*)a.dkh,
+                     (const float*)a.dvh, a.nq / a.nkv, a.hd, a.nkv, total, a.dk, a.dv);
   return hipGetLastError();
 }
 

@@ -264,6 +264,7 @@ struct BwFlash {
   float *mst, *lst;
   const float* D;
   float *o, *dq, *dk, *dv;
+  float *dkh, *dvh;  // [B n][nq][hd] per-query-head partial dk, dv (scratch of the backward pass)
 };
 bool bw_flash_supported(int dtype, int hd, int nq, int nkv);
 // dst [B][H][hd][nT] bfloat16 (zero past n) from float32 rows src[(b n + t) ld + off + h hd + d]

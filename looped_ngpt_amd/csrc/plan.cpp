@@ -209,6 +209,8 @@ BwLayout make_bw_layout(const Plan& p, int B, int n, bool stored) {
     w.fdOT = take(rowsT * qd * 2);
     w.fKT = take(rowsT * kvd * 2);
     w.fVT = take(rowsT * kvd * 2);
+    w.fdkh = take(M * qd * 4);
+    w.fdvh = take(M * qd * 4);
   }
   // one layer's forward values
   const size_t g0 = at;

@@ -102,6 +102,7 @@ struct BwLayout {
   // matrix-core attention (bfloat16 models): head-major operand copies
   // [B][H][n][hd] and transposed [B][H][hd][nT] (bfloat16), remade per layer
   size_t fQ = 0, fK = 0, fV = 0, fdO = 0, fQT = 0, fKT = 0, fVT = 0, fdOT = 0;
+  size_t fdkh = 0, fdvh = 0;  // per-query-head dk, dv (float32 [M][qd])
   int nT = 0;
   // The values a layer's backward reads from its forward (P1 .. rz2 above
   // but y, and the T copies xb .. ab) sit in one group at the end
