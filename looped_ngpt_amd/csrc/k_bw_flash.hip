@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
 // dQ: one workgroup per 128 queries of one (sequence, q head)
 // ---------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(256, 1) void k_bwf_dq(BwFlash a) {
+__global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
   constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32;
   __shared__ __align__(16) bf16 Ks[kFT * KLD];
   __shared__ __align__(16) bf16 Vs[kFT * KLD];
@@ -244,50 +244,52 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dq(BwFlash a) {
   const int hi = min(i0 + kFR - 1, a.n - 1);
   const int lo = a.window ? max(0, i0 - a.window + 1) : 0;
   const int sfirst = lo / kFT * kFT, slast = hi / kFT * kFT;
-  u32x4 kr[HD / 32], vr[HD / 32], ktr[HD / 32];
+  // K and V rows of the next tile are prefetched; K^T is loaded at staging
+  // (registers for two workgroups per CU)
+  u32x4 kr[HD / 32], vr[HD / 32];
   fetch_rows<HD>(K, a.n, sfirst, kr);
   fetch_rows<HD>(V, a.n, sfirst, vr);
-  fetch_cols<HD>(KT, a.nT, sfirst, ktr);
   for (int s0 = sfirst; s0 <= slast; s0 += kFT) {
     __syncthreads();
-    put_rows<HD>(kr, Ks, KLD);
-    put_rows<HD>(vr, Vs, KLD);
-    put_cols<HD>(ktr, KTs, VLD);
+    {
+      u32x4 ktr[HD / 32];
+      fetch_cols<HD>(KT, a.nT, s0, ktr);
+      put_rows<HD>(kr, Ks, KLD);
+      put_rows<HD>(vr, Vs, KLD);
+      put_cols<HD>(ktr, KTs, VLD);
+    }
     __syncthreads();
     const int s1 = min(s0 + kFT, slast);
     fetch_rows<HD>(K, a.n, s1, kr);
     fetch_rows<HD>(V, a.n, s1, vr);
-    fetch_cols<HD>(KT, a.nT, s1, ktr);
     if (iw0 >= a.n || s0 > iw0 + 31) continue;
-    f32x16_t sc[2], dp[2];
+    // one 32-key half at a time (fewer live registers): S^T, dP^T, dS, dQ
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      f32x16_t sc, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kt][r] = dp[kt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int o = (kt * 32 + lq) * KLD + 16 * ks + 8 * g;
-        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ks + o), qf[ks], sc[kt], 0, 0, 0);
-        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Vs + o), df[ks], dp[kt], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ks + o), qf[ks], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Vs + o), df[ks], dp, 0, 0, 0);
       }
-    }
-    bf16x8_t db[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      bf16x8_t db[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float p = allowed(t, s, a.window) && s < a.n ? exp2f(fmaf(sc[kt][r], sl2, -m2)) * il : 0.f;
-        db[kt][r >> 3][r & 7] = (__bf16)(p * (dp[kt][r] - Dt));
+        const float p =
+            allowed(t, s, a.window) && s < a.n ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2)) * il : 0.f;
+        db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dt));
       }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(KTs, mb, kt, h, lq, g), db[kt][h],
-                                                            acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(KTs, mb, kt, h, lq, g), db[h], acc[mb],
+                                                            0, 0, 0);
+    }
   }
   if (iw0 >= a.n || iw0 + lq >= a.n) return;
   float* dq = a.dq + row * a.nq * HD + (size_t)hq * HD;
