@@ -100,7 +100,8 @@ __device__ __forceinline__ bf16x8_t perm_frag(const bf16* tT, int mb, int kt, in
 }
 
 // ---------------------------------------------------------------------------
-// forward: O and the softmax statistics (mst in natural-log units, lst the sum)
+// forward: O and the softmax statistics (mst: the reference exponent m of
+// p = 2^(scale log2(e) q.k - m), lst: the reciprocal of the row sum)
 // ---------------------------------------------------------------------------
 template <int HD>
 __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = acc[mb][r] * inv;
   if (g == 0) {
-    a.mst[row * a.nq + hq] = m * 0.6931471805599453f;  // log2 -> natural units
-    a.lst[row * a.nq + hq] = lt;
+    a.mst[row * a.nq + hq] = m;    // reference exponent, log2 units of the scaled score
+    a.lst[row * a.nq + hq] = inv;  // 1 / row sum
   }
 }
 
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
   }
   const size_t row = (size_t)b * a.n + t;
   const float sl2 = a.scale * kLog2e;
-  const float m2 = a.mst[row * a.nq + hq] * kLog2e, il = 1.f / a.lst[row * a.nq + hq];
+  const float m2 = a.mst[row * a.nq + hq], il = a.lst[row * a.nq + hq];
   const float Dt = a.D[row * a.nq + hq];
   f32x16_t acc[NMB];
 #pragma unroll
@@ -306,15 +307,33 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
 // k_bwf_sum_heads adds in head order. Workgroup ids: the eight XCDs take
 // every eighth head, and inside an XCD the key blocks with the most queries
 // start first.
+//
+// The query tiles (Q and dO rows, their transposed copies, the softmax
+// terms) reach LDS by direct global->LDS loads into two alternating
+// buffers: the next tile's loads are in flight while the current one is
+// multiplied, without registers to hold them (a wave keeps its 32 keys' k,
+// v fragments and two 32 x HD accumulators). Dense rows with the 16-byte
+// chunk index XORed by (row mod 8): row tiles are read conflict-free,
+// transposed ones with at most two lanes per bank.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+#define DORY_BWF_WAIT_VM0() __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8))
+
+// byte offset of 16-byte chunk c of row r (rows of cpr chunks)
+__device__ __forceinline__ int sw_off(int r, int c, int cpr) { return (r * cpr + (c ^ (r & 7))) * 16; }
+
+template <int HD>
+struct DkvStage {
+  static constexpr int kRow = kFT * HD * 2;  // one row tile (Q or dO), bytes
+  static constexpr int kCol = HD * kFT * 2;  // one transposed tile
+  static constexpr int kBytes = 2 * kRow + 2 * kCol + 3 * kFT * 4;  // + m, 1/l, D of the 64 queries
+};
+
 template <int HD>
 __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
-  constexpr int KLD = HD + 8, VLD = kFT + 4, NKS = HD / 16, NMB = HD / 32, NL = HD / 32;
-  __shared__ __align__(16) bf16 Qs[kFT * KLD];
-  __shared__ __align__(16) bf16 Ds_[kFT * KLD];
-  __shared__ __align__(16) bf16 QTs[HD * VLD];
-  __shared__ __align__(16) bf16 DTs[HD * VLD];
-  __shared__ float m2s[kFT], ils[kFT], Dq[kFT];
+  constexpr int NKS = HD / 16, NMB = HD / 32, CPR = HD / 8;
+  using S = DkvStage<HD>;
+  __shared__ __align__(1024) unsigned char lds[2 * S::kBytes];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lk = lane & 31, g = lane >> 5;
   const int nkb = (a.n + kFR - 1) / kFR;
   const int BH = a.B * a.nq, hpx = (BH + 7) / 8;
@@ -325,6 +344,54 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
   const int k0 = kb * kFR, kw0 = k0 + 32 * wave;
   const int s = min(kw0 + lk, a.n - 1);
   const size_t koff = ((size_t)b * a.nkv + kvh) * a.n * HD;
+  const int khi = min(k0 + kFR - 1, a.n - 1);
+  const int qlo = k0, qhi = a.window ? min(a.n - 1, khi + a.window - 1) : a.n - 1;
+  const int qfirst = qlo / kFT * kFT, qlast = qhi / kFT * kFT;
+  const bf16* Qh = a.Q + ((size_t)b * a.nq + hq) * a.n * HD;
+  const bf16* Dh = a.dO + ((size_t)b * a.nq + hq) * a.n * HD;
+  const bf16* QT = a.QT + ((size_t)b * a.nq + hq) * HD * a.nT;
+  const bf16* DT = a.dOT + ((size_t)b * a.nq + hq) * HD * a.nT;
+  const size_t srow = (size_t)b * a.n;
+
+  // direct loads of the tile at query q0 into buffer buf: every wave fills
+  // CPR/4 1 KB blocks of each row tile and HD/32 of each transposed tile
+  auto issue = [&](int q0, int buf) {
+    unsigned char* st = lds + buf * S::kBytes;
+#pragma unroll
+    for (int i = 0; i < CPR / 4; ++i) {
+      const int e = (wave * (CPR / 4) + i) * 64 + lane;
+      const int r = e / CPR, c = (e % CPR) ^ (r & 7);
+      const size_t go = (size_t)min(q0 + r, a.n - 1) * HD + 8 * c;
+      unsigned char* d0 = st + (wave * (CPR / 4) + i) * 1024;
+      __builtin_amdgcn_global_load_lds(Qh + go, (lds_void_t*)d0, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Dh + go, (lds_void_t*)(d0 + S::kRow), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i) {
+      const int e = (wave * (HD / 32) + i) * 64 + lane;
+      const int d = e >> 3, c = (e & 7) ^ (d & 7);
+      const size_t go = (size_t)d * a.nT + min(q0 + 8 * c, a.nT - 8);
+      unsigned char* d0 = st + 2 * S::kRow + (wave * (HD / 32) + i) * 1024;
+      __builtin_amdgcn_global_load_lds(QT + go, (lds_void_t*)d0, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(DT + go, (lds_void_t*)(d0 + S::kCol), 16, 0, 0);
+    }
+  };
+  // softmax terms of a tile's 64 queries: threads 0..63 load one query's
+  // into registers a tile ahead and write them to LDS before the barrier
+  float st_m = 0.f, st_l = 0.f, st_d = 0.f;
+  auto fetch_stats = [&](int q0) {
+    if (tid < kFT) {
+      const size_t r = (srow + min(q0 + tid, a.n - 1)) * a.nq + hq;
+      st_m = a.mst[r];
+      st_l = a.lst[r];
+      st_d = a.D[r];
+    }
+  };
+  // query tiles from the last down: the key blocks of one head then read the
+  // same tile at the same step (one fetch from memory, the rest from L2)
+  issue(qlast, 0);
+  fetch_stats(qlast);
+
   bf16x8_t kf[NKS], vf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -337,86 +404,76 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ak[mb][r] = av[mb][r] = 0.f;
-  const int khi = min(k0 + kFR - 1, a.n - 1);
-  const int qlo = k0, qhi = a.window ? min(a.n - 1, khi + a.window - 1) : a.n - 1;
-  const size_t qoff = ((size_t)b * a.nq + hq) * a.n * HD;
-  const bf16* QT = a.QT + ((size_t)b * a.nq + hq) * HD * a.nT;
-  const bf16* DT = a.dOT + ((size_t)b * a.nq + hq) * HD * a.nT;
-  // per-query softmax terms of a tile: threads 0..63 hold one query each
-  auto fetch_stats = [&](int q0, float& m2, float& il, float& dd) {
-    if (tid < kFT) {
-      const size_t r = (size_t)b * a.n + min(q0 + tid, a.n - 1);
-      m2 = a.mst[r * a.nq + hq];
-      il = a.lst[r * a.nq + hq];
-      dd = a.D[r * a.nq + hq];
-    }
+
+  // A operand of the second products from a transposed tile: rows = dims
+  // 32 mb .., the 16 positions of step (qt, hh) in the permuted order
+  auto tfrag = [&](const unsigned char* tT, int mb, int qt, int hh) {
+    const int d = mb * 32 + lk, c = 4 * qt + 2 * hh;
+    const u32x2_t lo = *(const u32x2_t*)(tT + sw_off(d, c, 8) + 8 * g);
+    const u32x2_t hi = *(const u32x2_t*)(tT + sw_off(d, c + 1, 8) + 8 * g);
+    const u32x4 v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    return *(const bf16x8_t*)&v;
   };
-  const int qfirst = qlo / kFT * kFT, qlast = qhi / kFT * kFT;
-  u32x4 qr[NL], dr[NL], qtr[NL], dtr[NL];
-  float m2r = 0.f, ilr = 1.f, ddr = 0.f;
-  fetch_rows<HD>(a.Q + qoff, a.n, qfirst, qr);
-  fetch_rows<HD>(a.dO + qoff, a.n, qfirst, dr);
-  fetch_cols<HD>(QT, a.nT, qfirst, qtr);
-  fetch_cols<HD>(DT, a.nT, qfirst, dtr);
-  fetch_stats(qfirst, m2r, ilr, ddr);
-  for (int q0 = qfirst; q0 <= qlast; q0 += kFT) {
-    __syncthreads();
-    put_rows<HD>(qr, Qs, KLD);
-    put_rows<HD>(dr, Ds_, KLD);
-    put_cols<HD>(qtr, QTs, VLD);
-    put_cols<HD>(dtr, DTs, VLD);
+
+  int buf = 0;
+  for (int q0 = qlast; q0 >= qfirst; q0 -= kFT, buf ^= 1) {
+    unsigned char* st = lds + buf * S::kBytes;
+    DORY_BWF_WAIT_VM0();  // this wave's loads of the current buffer (and the k, v fragments, the terms) are done
     if (tid < kFT) {
-      m2s[tid] = m2r * kLog2e;
-      ils[tid] = 1.f / ilr;
-      Dq[tid] = ddr;
+      float* t3 = (float*)(st + 2 * S::kRow + 2 * S::kCol);
+      t3[tid] = st_m;
+      t3[kFT + tid] = st_l;
+      t3[2 * kFT + tid] = st_d;
     }
-    __syncthreads();
-    const int q1 = min(q0 + kFT, qlast);
-    fetch_rows<HD>(a.Q + qoff, a.n, q1, qr);
-    fetch_rows<HD>(a.dO + qoff, a.n, q1, dr);
-    fetch_cols<HD>(QT, a.nT, q1, qtr);
-    fetch_cols<HD>(DT, a.nT, q1, dtr);
-    fetch_stats(q1, m2r, ilr, ddr);
+    __syncthreads();  // everyone's are, and the other buffer is consumed
+    if (q0 - kFT >= qfirst) {
+      issue(q0 - kFT, buf ^ 1);
+      fetch_stats(q0 - kFT);
+    }
+    const unsigned char* Qs = st;
+    const unsigned char* Ds_ = st + S::kRow;
+    const unsigned char* QTs = st + 2 * S::kRow;
+    const unsigned char* DTs = QTs + S::kCol;
+    const float* m2s = (const float*)(DTs + S::kCol);
+    const float* ils = m2s + kFT;
+    const float* Dq = ils + kFT;
     // queries of the tile that see some key of this wave
     if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
-    f32x16_t sc[2], dp[2];
+    // one 32-query half at a time: S^T, dP^T, P, dS, then dV, dK
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
+      f32x16_t sc, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[qt][r] = dp[qt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int o = (qt * 32 + lk) * KLD + 16 * ks + 8 * g;
-        sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Qs + o), kf[ks], sc[qt], 0, 0, 0);
-        dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ds_ + o), vf[ks], dp[qt], 0, 0, 0);
+        const int o = sw_off(qt * 32 + lk, 2 * ks + g, CPR);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Qs + o), kf[ks], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ds_ + o), vf[ks], dp, 0, 0, 0);
       }
-    }
-    bf16x8_t pb[2][2], db[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+      // p = 2^(s sl2 - m) / l: the exponent is at most 0 up to rounding (m is
+      // the row's reference), so the hardware exp2 needs no range handling
+      bf16x8_t pb[2], db[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
         const int t = q0 + qi;
-        const float p =
-            allowed(t, s, a.window) && t < a.n ? exp2f(fmaf(sc[qt][r], sl2, -m2s[qi])) * ils[qi] : 0.f;
-        pb[qt][r >> 3][r & 7] = (__bf16)p;
-        db[qt][r >> 3][r & 7] = (__bf16)(p * (dp[qt][r] - Dq[qi]));
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2s[qi])) * ils[qi];
+        const float p = allowed(t, s, a.window) && t < a.n ? e : 0.f;
+        pb[r >> 3][r & 7] = (__bf16)p;
+        db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq[qi]));
       }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          av[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(DTs, mb, qt, hh, lk, g), pb[qt][hh],
-                                                           av[mb], 0, 0, 0);
-          ak[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(perm_frag<VLD>(QTs, mb, qt, hh, lk, g), db[qt][hh],
-                                                           ak[mb], 0, 0, 0);
+          av[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(DTs, mb, qt, hh), pb[hh], av[mb], 0, 0, 0);
+          ak[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(QTs, mb, qt, hh), db[hh], ak[mb], 0, 0, 0);
         }
+    }
   }
   if (kw0 >= a.n || kw0 + lk >= a.n) return;
-  const size_t row = (size_t)b * a.n + s;
+  const size_t row = srow + s;
   float* dk = a.dkh + row * a.nq * HD + (size_t)hq * HD;
   float* dv = a.dvh + row * a.nq * HD + (size_t)hq * HD;
 #pragma unroll
