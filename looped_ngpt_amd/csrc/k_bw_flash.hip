@@ -155,18 +155,28 @@ __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *(const bf16x8_t*)(Ks + (kt * 32 + lq) * KLD + 16 * ks + 8 * g), qf[ks], sc[kt], 0, 0, 0);
     }
+    // masks only where some key of the tile is not allowed for some query of
+    // the wave (a wave-uniform branch); a masked score is -inf, so p = 0
+    const bool edge = s0 + kFT - 1 > iw0 || (a.window && min(iw0 + 31, a.n - 1) - s0 >= a.window);
     float tmax = -INFINITY;
+    if (edge) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        sc[kt][r] = allowed(t, s, a.window) && s < a.n ? sc[kt][r] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, sc[kt][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+          sc[kt][r] = allowed(t, s, a.window) && s < a.n ? sc[kt][r] : -INFINITY;
+          tmax = fmaxf(tmax, sc[kt][r]);
+        }
+    } else if (!fixed_ref) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[kt][r]);
+    }
     float mn = m;
-    if (!fixed_ref) mn = fmaxf(m, fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
-    const float alpha = exp2f(m - mn);
+    if (!fixed_ref) mn = fmaxf(m, fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     float ps = 0.f;
     bf16x8_t pb[2][2];
@@ -175,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void k_bwf_fwd(BwFlash a) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         bf16x2_t pr;
-        pr[0] = (__bf16)exp2f(sc[kt][r] - mn);
-        pr[1] = (__bf16)exp2f(sc[kt][r + 1] - mn);
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kt][r], sl2, -mn));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kt][r + 1], sl2, -mn));
         ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
         pb[kt][r >> 3][r & 7] = pr[0];
         pb[kt][r >> 3][(r & 7) + 1] = pr[1];
@@ -264,6 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
     fetch_rows<HD>(K, a.n, s1, kr);
     fetch_rows<HD>(V, a.n, s1, vr);
     if (iw0 >= a.n || s0 > iw0 + 31) continue;
+    const bool edge = s0 + kFT - 1 > iw0 || (a.window && min(iw0 + 31, a.n - 1) - s0 >= a.window);
     // one 32-key half at a time (fewer live registers): S^T, dP^T, dS, dQ
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -276,12 +287,14 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ks + o), qf[ks], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Vs + o), df[ks], dp, 0, 0, 0);
       }
+      // p = 2^(s sl2 - m) / l (the exponent is at most 0 up to rounding);
+      // masks only on edge tiles
       bf16x8_t db[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float p =
-            allowed(t, s, a.window) && s < a.n ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2)) * il : 0.f;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2)) * il;
+        const float p = !edge || (allowed(t, s, a.window) && s < a.n) ? e : 0.f;
         db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dt));
       }
 #pragma unroll
@@ -439,6 +452,8 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
     const float* Dq = ils + kFT;
     // queries of the tile that see some key of this wave
     if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
+    // every query of the tile sees every key of the wave: no masks
+    const bool edge = q0 < kw0 + 31 || q0 + kFT > a.n || (a.window && q0 + kFT - 1 - kw0 >= a.window);
     // one 32-query half at a time: S^T, dP^T, P, dS, then dV, dK
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
         const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
         const int t = q0 + qi;
         const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2s[qi])) * ils[qi];
-        const float p = allowed(t, s, a.window) && t < a.n ? e : 0.f;
+        const float p = !edge || (allowed(t, s, a.window) && t < a.n) ? e : 0.f;
         pb[r >> 3][r & 7] = (__bf16)p;
         db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq[qi]));
       }
