@@ -274,7 +274,6 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
     fetch_rows<HD>(K, a.n, s1, kr);
     fetch_rows<HD>(V, a.n, s1, vr);
     if (iw0 >= a.n || s0 > iw0 + 31) continue;
-    const bool edge = s0 + kFT - 1 > iw0 || (a.window && min(iw0 + 31, a.n - 1) - s0 >= a.window);
     // one 32-key half at a time (fewer live registers): S^T, dP^T, dS, dQ
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -287,14 +286,13 @@ __global__ __launch_bounds__(256, 2) void k_bwf_dq(BwFlash a) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Ks + o), qf[ks], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(Vs + o), df[ks], dp, 0, 0, 0);
       }
-      // p = 2^(s sl2 - m) / l (the exponent is at most 0 up to rounding);
-      // masks only on edge tiles
+      // p = 2^(s sl2 - m) / l (the exponent is at most 0 up to rounding)
       bf16x8_t db[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int s = s0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
         const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2)) * il;
-        const float p = !edge || (allowed(t, s, a.window) && s < a.n) ? e : 0.f;
+        const float p = allowed(t, s, a.window) && s < a.n ? e : 0.f;
         db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dt));
       }
 #pragma unroll
@@ -452,8 +450,6 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
     const float* Dq = ils + kFT;
     // queries of the tile that see some key of this wave
     if (kw0 >= a.n || q0 + kFT - 1 < kw0 || (a.window && q0 > kw0 + 31 + a.window - 1)) continue;
-    // every query of the tile sees every key of the wave: no masks
-    const bool edge = q0 < kw0 + 31 || q0 + kFT > a.n || (a.window && q0 + kFT - 1 - kw0 >= a.window);
     // one 32-query half at a time: S^T, dP^T, P, dS, then dV, dK
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -474,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void k_bwf_dkv(BwFlash a) {
         const int qi = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
         const int t = q0 + qi;
         const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m2s[qi])) * ils[qi];
-        const float p = !edge || (allowed(t, s, a.window) && t < a.n) ? e : 0.f;
+        const float p = allowed(t, s, a.window) && t < a.n ? e : 0.f;
         pb[r >> 3][r & 7] = (__bf16)p;
         db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq[qi]));
       }
