@@ -623,6 +623,204 @@ __global__ __launch_bounds__(256) void k_bw_to_heads(const float* __restrict__ s
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// ---------------------------------------------------------------------------
+// The same row kernels with the row held in registers (NPT elements per
+// thread, rows up to 256 NPT): one read of each input instead of one per
+// pass. Element for element the same operations in the same order as the
+// streaming versions above, so the results are bit-identical.
+// ---------------------------------------------------------------------------
+template <typename T, int NPT>
+__global__ __launch_bounds__(256) void k_bw_update_fwd_r(const float* __restrict__ h, const float* __restrict__ y,
+                                                         const float* __restrict__ y2,
+                                                         const float* __restrict__ alpha, int d,
+                                                         float* __restrict__ yh, float* __restrict__ ry,
+                                                         float* __restrict__ rz, float* __restrict__ hout,
+                                                         T* __restrict__ hout_t) {
+  __shared__ float sh[4];
+  const size_t r = blockIdx.x;
+  // loads from clamped indices, all issued before the first use; elements
+  // past the row read as zero
+  float yv[NPT], hv[NPT], av[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int jc = min((int)threadIdx.x + 256 * i, d - 1);
+    yv[i] = y2 ? y[r * d + jc] + y2[r * d + jc] : y[r * d + jc];
+    hv[i] = h[r * d + jc];
+    av[i] = alpha[jc];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    if ((int)threadIdx.x + 256 * i >= d) yv[i] = hv[i] = 0.f;
+    ss += yv[i] * yv[i];
+  }
+  const float ny = guard_norm(block_sum<256>(ss, sh));
+  float sz = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {  // past the row: yv = hv = 0, so z = 0
+    const int j = threadIdx.x + 256 * i;
+    const float yn = yv[i] / ny;
+    const float z = hv[i] + av[i] * (yn - hv[i]);
+    if (j < d) yh[r * d + j] = yn;
+    hv[i] = z;
+    sz += z * z;
+  }
+  const float nz = guard_norm(block_sum<256>(sz, sh));
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j < d) {
+      const float v = hv[i] / nz;
+      hout[r * d + j] = v;
+      if (hout_t) hout_t[r * d + j] = from_f<T>(v);
+    }
+  }
+  if (threadIdx.x == 0) {
+    ry[r] = ny;
+    rz[r] = nz;
+  }
+}
+
+template <typename T, int NPT>
+__global__ __launch_bounds__(256) void k_bw_swiglu_fwd_r(const float* __restrict__ P2, int F, float* __restrict__ a32,
+                                                         T* __restrict__ a_t, float* __restrict__ rs) {
+  __shared__ float sh[4];
+  const size_t r = blockIdx.x;
+  const float* u = P2 + r * 2 * F;
+  float uv[NPT], vv[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int jc = min((int)threadIdx.x + 256 * i, F - 1);
+    uv[i] = u[jc];
+    vv[i] = u[F + jc];
+  }
+  float sv[NPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    sv[i] = (int)threadIdx.x + 256 * i < F ? uv[i] * vv[i] * sigmoidf_(vv[i]) : 0.f;
+    ss += sv[i] * sv[i];
+  }
+  const float ns = guard_norm(block_sum<256>(ss, sh));
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j < F) {
+      const float v = sv[i] / ns;
+      a32[r * F + j] = v;
+      a_t[r * F + j] = from_f<T>(v);
+    }
+  }
+  if (threadIdx.x == 0) rs[r] = ns;
+}
+
+template <typename T, int NPT>
+__global__ __launch_bounds__(256) void k_bw_update_bwd_r(const float* __restrict__ dho, const float* __restrict__ ho,
+                                                         const float* __restrict__ rz, const float* __restrict__ yh,
+                                                         const float* __restrict__ ry, const float* __restrict__ h,
+                                                         const float* __restrict__ alpha, int d,
+                                                         float* __restrict__ dres, T* __restrict__ dy_t,
+                                                         float* __restrict__ contrib) {
+  __shared__ float sh[4];
+  const size_t r = blockIdx.x;
+  float gv[NPT], ov[NPT], yv[NPT], hv[NPT], av[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int jc = min((int)threadIdx.x + 256 * i, d - 1);
+    gv[i] = dho[r * d + jc];
+    ov[i] = ho[r * d + jc];
+    yv[i] = yh[r * d + jc];
+    hv[i] = h[r * d + jc];
+    av[i] = alpha[jc];
+  }
+  float s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    if ((int)threadIdx.x + 256 * i >= d) gv[i] = ov[i] = yv[i] = 0.f;
+    s1 += ov[i] * gv[i];
+  }
+  const float hd_ = block_sum<256>(s1, sh);
+  const float iz = 1.f / rz[r];
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    const float dz = (gv[i] - ov[i] * hd_) * iz;
+    if (j < d) {
+      dres[r * d + j] = dz * (1.f - av[i]);
+      contrib[r * d + j] = dz * (yv[i] - hv[i]);
+    }
+    s2 += yv[i] * dz * av[i];
+    gv[i] = dz;
+  }
+  const float yd = block_sum<256>(s2, sh);
+  const float iy = 1.f / ry[r];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j < d) dy_t[r * d + j] = from_f<T>((gv[i] * av[i] - yv[i] * yd) * iy);
+  }
+}
+
+template <typename T, int NPT>
+__global__ __launch_bounds__(256) void k_bw_swiglu_bwd_r(const float* __restrict__ da, const float* __restrict__ a32,
+                                                         const float* __restrict__ rs, const float* __restrict__ P2,
+                                                         int F, T* __restrict__ dP2) {
+  __shared__ float sh[4];
+  const size_t r = blockIdx.x;
+  float dv[NPT], av[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int jc = min((int)threadIdx.x + 256 * i, F - 1);
+    dv[i] = da[r * F + jc];
+    av[i] = a32[r * F + jc];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) s += (int)threadIdx.x + 256 * i < F ? av[i] * dv[i] : 0.f;
+  const float ad = block_sum<256>(s, sh);
+  const float is = 1.f / rs[r];
+  float uv[NPT], vv[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int jc = min((int)threadIdx.x + 256 * i, F - 1);
+    uv[i] = P2[r * 2 * F + jc];
+    vv[i] = P2[r * 2 * F + F + jc];
+  }
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j < F) {
+      const float ds = (dv[i] - av[i] * ad) * is;
+      const float u = uv[i], v = vv[i];
+      const float sg = sigmoidf_(v);
+      dP2[r * 2 * F + j] = from_f<T>(ds * v * sg);
+      dP2[r * 2 * F + F + j] = from_f<T>(ds * u * sg * (1.f + v * (1.f - sg)));
+    }
+  }
+}
+
+// elements per thread of a register-held row of n, at most max_npt (0: too
+// long, stream it). The update kernels hold two arrays and stop at 16: at 32
+// the compiler left their arrays in scratch memory.
+int row_npt(int n, int max_npt) {
+  const int npt = n <= 1024 ? 4 : n <= 2048 ? 8 : n <= 4096 ? 16 : n <= 8192 ? 32 : 0;
+  return npt <= max_npt ? npt : 0;
+}
+
+#define DORY_ROW_DISPATCH16(KERNEL, T, NPT, ...)                                             \
+  switch (NPT) {                                                                              \
+    case 4: hipLaunchKernelGGL((KERNEL<T, 4>), __VA_ARGS__); break;                          \
+    case 8: hipLaunchKernelGGL((KERNEL<T, 8>), __VA_ARGS__); break;                          \
+    default: hipLaunchKernelGGL((KERNEL<T, 16>), __VA_ARGS__); break;                        \
+  }
+#define DORY_ROW_DISPATCH(KERNEL, T, NPT, ...)                                               \
+  if ((NPT) == 32) {                                                                          \
+    hipLaunchKernelGGL((KERNEL<T, 32>), __VA_ARGS__);                                        \
+  } else {                                                                                    \
+    DORY_ROW_DISPATCH16(KERNEL, T, NPT, __VA_ARGS__)                                         \
+  }
+
 }  // namespace
 
 hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int H, int hd, int n, int B, void* dst,
@@ -698,6 +896,17 @@ hipError_t launch_bw_colsum(const float* in, int M, int d, float* out, float* pa
 
 hipError_t launch_bw_update_fwd(int dt, const float* h, const float* y, const float* alpha, int M, int d, float* yh,
                                 float* ry, float* rz, float* hout, void* hout_t, hipStream_t st, const float* y2) {
+  if (M <= 0) return hipSuccess;
+  if (const int npt = row_npt(d, 16)) {
+    if (dt == 1) {
+      DORY_ROW_DISPATCH16(k_bw_update_fwd_r, bf16, npt, dim3(M), dim3(256), 0, st, h, y, y2, alpha, d, yh, ry, rz, hout,
+                        (bf16*)hout_t)
+    } else {
+      DORY_ROW_DISPATCH16(k_bw_update_fwd_r, float, npt, dim3(M), dim3(256), 0, st, h, y, y2, alpha, d, yh, ry, rz, hout,
+                        (float*)hout_t)
+    }
+    return hipGetLastError();
+  }
   if (dt == 1)
     hipLaunchKernelGGL((k_bw_update_fwd<bf16>), dim3(M), dim3(256), 0, st, h, y, y2, alpha, d, yh, ry, rz, hout,
                        (bf16*)hout_t);
@@ -739,6 +948,15 @@ hipError_t launch_bw_gate_fwd(int dt, const float* o, const float* P1, int ldp, 
 
 hipError_t launch_bw_swiglu_fwd(int dt, const float* P2, int F, int M, float* a32, void* a_t, float* rs,
                                 hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (const int npt = row_npt(F, 32)) {
+    if (dt == 1) {
+      DORY_ROW_DISPATCH(k_bw_swiglu_fwd_r, bf16, npt, dim3(M), dim3(256), 0, st, P2, F, a32, (bf16*)a_t, rs)
+    } else {
+      DORY_ROW_DISPATCH(k_bw_swiglu_fwd_r, float, npt, dim3(M), dim3(256), 0, st, P2, F, a32, (float*)a_t, rs)
+    }
+    return hipGetLastError();
+  }
   if (dt == 1)
     hipLaunchKernelGGL((k_bw_swiglu_fwd<bf16>), dim3(M), dim3(256), 0, st, P2, F, a32, (bf16*)a_t, rs);
   else
@@ -754,6 +972,17 @@ hipError_t launch_bw_final(const float* h, const float* G, int M, int d, float* 
 hipError_t launch_bw_update_bwd(int dt, const float* dho, const float* ho, const float* rz, const float* yh,
                                 const float* ry, const float* h, const float* alpha, int M, int d, float* dres,
                                 void* dy_t, float* contrib, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (const int npt = row_npt(d, 16)) {
+    if (dt == 1) {
+      DORY_ROW_DISPATCH16(k_bw_update_bwd_r, bf16, npt, dim3(M), dim3(256), 0, st, dho, ho, rz, yh, ry, h, alpha, d, dres,
+                        (bf16*)dy_t, contrib)
+    } else {
+      DORY_ROW_DISPATCH16(k_bw_update_bwd_r, float, npt, dim3(M), dim3(256), 0, st, dho, ho, rz, yh, ry, h, alpha, d,
+                        dres, (float*)dy_t, contrib)
+    }
+    return hipGetLastError();
+  }
   if (dt == 1)
     hipLaunchKernelGGL((k_bw_update_bwd<bf16>), dim3(M), dim3(256), 0, st, dho, ho, rz, yh, ry, h, alpha, d, dres,
                        (bf16*)dy_t, contrib);
@@ -765,6 +994,15 @@ hipError_t launch_bw_update_bwd(int dt, const float* dho, const float* ho, const
 
 hipError_t launch_bw_swiglu_bwd(int dt, const float* da, const float* a32, const float* rs, const float* P2, int F,
                                 int M, void* dP2, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (const int npt = row_npt(F, 32)) {
+    if (dt == 1) {
+      DORY_ROW_DISPATCH(k_bw_swiglu_bwd_r, bf16, npt, dim3(M), dim3(256), 0, st, da, a32, rs, P2, F, (bf16*)dP2)
+    } else {
+      DORY_ROW_DISPATCH(k_bw_swiglu_bwd_r, float, npt, dim3(M), dim3(256), 0, st, da, a32, rs, P2, F, (float*)dP2)
+    }
+    return hipGetLastError();
+  }
   if (dt == 1)
     hipLaunchKernelGGL((k_bw_swiglu_bwd<bf16>), dim3(M), dim3(256), 0, st, da, a32, rs, P2, F, (bf16*)dP2);
   else

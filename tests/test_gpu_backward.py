@@ -125,6 +125,20 @@ def test_backward_bf16_split_contraction():
     _compare(cfg, got, ref, x.shape, 3e-2)
 
 
+def test_backward_bf16_long_rows():
+    """d 4352 and d_ff 8448: rows longer than the register-held row kernels take (4096 for the updates,
+    8192 for SwiGLU), so the streaming versions of those kernels run."""
+    cfg = ModelConfig(name="bw_long_rows", d_model=4352, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=8448,
+                      vocab=256, n_in=1, n_rec=2, n_out=1, window=5,
+                      layer_is_full=(False, False, True, False), rope_base_swa=1.0e4, rope_base_full=1.0e6,
+                      dtype="bf16", attn_gate=1, seed=19)
+    w = _alphas(cfg, make_weights(cfg), 96)
+    x, G = _inputs(cfg, 1, 24, 97)
+    ref = bw.block_backward(cfg, w, x.astype(np.float64), G.astype(np.float64))
+    got = _run(cfg, w, x, G)
+    _compare(cfg, got, ref, x.shape, 3e-2)
+
+
 def test_backward_argument_errors():
     cfg = _small(1, "f32")
     w = make_weights(cfg)
