@@ -607,6 +607,26 @@ __global__ __launch_bounds__(256) void k_bw_rope_norm_bwd(const float* __restric
 // head-major operand copies of the matrix-core attention (k_bw_flash.hip)
 // ---------------------------------------------------------------------------
 // dst [B][H][n][hd] (model dtype) from src rows [B*n][ld] at column off + h*hd
+// The same copy, one workgroup row per source row (blockIdx.x) and four
+// consecutive elements per thread (ld, off, hd multiples of 4, src 16-byte
+// aligned): no per-element index division.
+template <typename T>
+__global__ __launch_bounds__(256) void k_bw_to_heads4(const float* __restrict__ src, int64_t ld, int off, int H,
+                                                      int hd, int n, T* __restrict__ dst) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= H * hd) return;
+  const int64_t row = blockIdx.x;  // b n + t
+  const int64_t b = row / n;
+  const int t = (int)(row - b * n);
+  const int h = c / hd, d = c - h * hd;
+  const float4 v = *(const float4*)(src + row * ld + off + c);
+  T* o = dst + ((b * H + h) * n + t) * hd + d;
+  o[0] = from_f<T>(v.x);
+  o[1] = from_f<T>(v.y);
+  o[2] = from_f<T>(v.z);
+  o[3] = from_f<T>(v.w);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_bw_to_heads(const float* __restrict__ src, int64_t ld, int off, int H,
                                                      int hd, int n, int64_t total, T* __restrict__ dst) {
@@ -827,6 +847,14 @@ hipError_t launch_bw_to_heads(int dt, const float* src, int64_t ld, int off, int
                               hipStream_t st) {
   const int64_t total = (int64_t)B * H * n * hd;
   if (total <= 0) return hipSuccess;
+  if (ld % 4 == 0 && off % 4 == 0 && hd % 4 == 0 && ((uintptr_t)src & 15) == 0 && (H * hd + 1023) / 1024 <= 65535) {
+    const dim3 grid((unsigned)((int64_t)B * n), (unsigned)((H * hd + 1023) / 1024));
+    if (dt == 1)
+      hipLaunchKernelGGL((k_bw_to_heads4<bf16>), grid, dim3(256), 0, st, src, ld, off, H, hd, n, (bf16*)dst);
+    else
+      hipLaunchKernelGGL((k_bw_to_heads4<float>), grid, dim3(256), 0, st, src, ld, off, H, hd, n, (float*)dst);
+    return hipGetLastError();
+  }
   if (dt == 1)
     hipLaunchKernelGGL((k_bw_to_heads<bf16>), dim3(blocks_for(total)), dim3(256), 0, st, src, ld, off, H, hd, n,
                        total, (bf16*)dst);

@@ -533,6 +533,39 @@ __global__ __launch_bounds__(256) void k_bwf_heads_t(const float* __restrict__ s
   dst[e] = t < n ? from_f<bf16>(src[(b * n + t) * ld + off + (int64_t)h * hd + d]) : (bf16)0;
 }
 
+// The same copies through a 64 x 64 LDS tile per (sequence, head): float4
+// reads along the head dimension, 8-byte writes of four consecutive
+// positions (ld, off, hd multiples of 4, src 16-byte aligned). Grid:
+// (nT / 64 position tiles, hd / 64 dimension tiles, B H).
+__global__ __launch_bounds__(256) void k_bwf_heads_t64(const float* __restrict__ src, int64_t ld, int off, int H,
+                                                       int hd, int n, int nT, bf16* __restrict__ dst) {
+  __shared__ float tile[64][65];
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, bh = blockIdx.z;
+  const int64_t b = bh / H;
+  const int h = bh - (int)b * H;
+  const int rr = threadIdx.x >> 4, cc = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int t = t0 + 16 * p + rr, d = d0 + cc;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < n && d < hd) v = *(const float4*)(src + (b * n + t) * ld + off + (int64_t)h * hd + d);
+    tile[16 * p + rr][cc] = v.x;
+    tile[16 * p + rr][cc + 1] = v.y;
+    tile[16 * p + rr][cc + 2] = v.z;
+    tile[16 * p + rr][cc + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int dd = 16 * p + rr, d = d0 + dd, t = t0 + cc;
+    if (d >= hd || t >= nT) continue;
+    const uint32_t lo = (uint32_t)from_f<bf16>(tile[cc][dd]) | ((uint32_t)from_f<bf16>(tile[cc + 1][dd]) << 16);
+    const uint32_t hi =
+        (uint32_t)from_f<bf16>(tile[cc + 2][dd]) | ((uint32_t)from_f<bf16>(tile[cc + 3][dd]) << 16);
+    *(u32x2_t*)(dst + ((size_t)bh * hd + d) * nT + t) = u32x2_t{lo, hi};
+  }
+}
+
 }  // namespace
 
 bool bw_flash_supported(int dtype, int hd, int nq, int nkv) {
@@ -544,6 +577,12 @@ hipError_t launch_bw_heads_t(const float* src, int64_t ld, int off, int H, int h
   const int64_t total = (int64_t)B * H * hd * nT;
   if (total <= 0) return hipSuccess;
   if (nT < n || nT % 8) return hipErrorInvalidValue;
+  if (ld % 4 == 0 && off % 4 == 0 && hd % 4 == 0 && ((uintptr_t)src & 15) == 0 && (hd + 63) / 64 <= 65535 &&
+      (int64_t)B * H <= 65535) {
+    const dim3 grid((unsigned)((nT + 63) / 64), (unsigned)((hd + 63) / 64), (unsigned)(B * H));
+    hipLaunchKernelGGL(k_bwf_heads_t64, grid, dim3(256), 0, st, src, ld, off, H, hd, n, nT, (bf16*)dst);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_bwf_heads_t, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, ld, off, H, hd, n,
                      nT, total, (bf16*)dst);
   return hipGetLastError();
