@@ -231,6 +231,34 @@ def test_bf16_prefill_chunked(name, B, n, chunk, k, mode, ctx, steps):
     np.testing.assert_array_equal(lib_next, g_tok[:, 1:])
 
 
+@pytest.mark.parametrize("nq,nkv,hd,n,chunk", [
+    (4, 4, 64, 77, 40),     # 1 query head per kv head; second chunk starts at 40 (gathers)
+    (8, 2, 64, 90, 90),     # 4 per kv head: 12 work items of 32 queries, the second workgroup half empty
+    (6, 1, 128, 70, 64),    # 6 per kv head, hd 128: the 6-position last chunk leaves two waves idle
+    (8, 1, 64, 100, 100),   # 8 per kv head: each workgroup spans one 32-query block of all heads
+])
+def test_bf16_prefill_query_group_sizes(nq, nkv, hd, n, chunk):
+    """The prefill attention groups the query heads of a kv head into one
+    workgroup; group sizes other than the named shapes' 2 and 3, ragged
+    prompt lengths and chunk boundaries inside a 64-key ring."""
+    name = f"tiny_bf16_g{nq}x{nkv}_hd{hd}"
+    if name not in _cache:
+        m = get_config("tiny").replace(dtype="bf16", d_ff=688, n_q_heads=nq, n_kv_heads=nkv, head_dim=hd,
+                                       name=name)
+        w = make_weights(m)
+        _cache[name] = (m, w, dory.upload_weights(m, w))
+    m, w, dw = _cache[name]
+    k, mode, steps, ctx = 2, "last_loop", 6, 128
+    prompt = make_tokens(m, 23, (1, n))
+    ora = LoopedNGPT(m, w, max_ctx=ctx)
+    o_tok, o_log = ora.generate(prompt, steps, k, mode, chunk=chunk)
+    print(f"{name}: oracle done", flush=True)
+    s = session(m, dw, batch=1, max_ctx=ctx, chunk=chunk, kv_mode=mode, k=k)
+    g_tok, g_log, _ = generate(s, prompt, steps, k)
+    assert _report(f"{name} n={n} chunk={chunk}", g_log, o_log) <= BF16_TOL
+    np.testing.assert_array_equal(g_tok, o_tok)
+
+
 # ---------------------------------------------------------------------------
 # per-sequence loop counts in one batched call (last-loop caching): each
 # sequence must get what it gets alone with its own counts — the reference is
