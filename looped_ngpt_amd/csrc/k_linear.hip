@@ -294,7 +294,7 @@ static bool gemv_rows_launch(const bf16* x, int64_t ldx, const bf16* W, void* y,
 // cover HBM latency at its share of the bandwidth) with few registers.
 constexpr int kProThreads = 1024;
 constexpr int kProOut = 2;  // outputs per wave
-constexpr int kProWin = 8;  // chunk loads in flight per wave
+constexpr int kProWin = 12;  // chunk loads in flight per wave
 
 template <int MB, int CH, int EPI, int NTH = kProThreads>
 __global__ __launch_bounds__(NTH) void k_gemv_pro(GemvPro pr, const bf16* __restrict__ W,
