@@ -132,6 +132,23 @@ dory_status proj(dory_ctx* c, const void* W, const void* S, float g, const void*
   return DORY_OK;
 }
 
+// A projection into the residual branch y (output and down projections):
+// at 9..64 rows (batched decode) with too few output tiles to fill the CUs,
+// the contraction runs in two halves side by side, the second into the
+// workspace's y1, and *y1 tells the update that reads y to add it.
+dory_status proj_y(dory_ctx* c, const void* W, const void* S, float g, const void* x, int64_t ldx, float* y, int M,
+                   int N, int K, const float** y1) {
+  const Plan& P = c->plan;
+  *y1 = nullptr;
+  if (P.cfg.weight_format == DORY_WEIGHTS_DTYPE && gemm_skinny_split2_pays(P.cfg.dtype, M, N, K)) {
+    float* y1w = wsp<float>(c, P.ws.y1);
+    HIP_TRY(c, launch_gemm_skinny_split2(x, ldx, W, y, y1w, M, N, K, 1.f, c->st));
+    *y1 = y1w;
+    return DORY_OK;
+  }
+  return proj(c, W, S, g, x, ldx, y, M, N, K, 0, 1.f);
+}
+
 // The decode GEMV with the nGPT update in its prologue, for any weight format.
 dory_status proj_pro(dory_ctx* c, const GemvPro& p, const void* W, const void* S, float g, void* y, int M, int N,
                      int K, int epi) {
@@ -267,20 +284,21 @@ dory_status run_layer(dory_ctx* c, int l, int loop, int B, int n, float* h2, int
                                  C.head_dim, slots, C.window, full, st, mix, loop));
   }
 
+  const float* y1 = nullptr;
   {
     TimeScope ts(c, TIME_O);
-    DORY_TRY(proj(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, rows, C.d_model, P.q_dim, 0, 1.f));
+    DORY_TRY(proj_y(c, c->o[l], c->o_s[l], c->o_g[l], c->ws + W.ob, P.q_dim, y, rows, C.d_model, P.q_dim, &y1));
   }
-  HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st, gate));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_attn[l], xb, nullptr, rows, C.d_model, st, gate, y1));
   {
     TimeScope ts(c, TIME_UG);
     DORY_TRY(proj(c, c->ug[l], c->ug_s[l], c->ug_g[l], xb, C.d_model, c->ws + W.a, rows, 2 * C.d_ff, C.d_model, 1, 1.f));
   }
   {
     TimeScope ts(c, TIME_DOWN);
-    DORY_TRY(proj(c, c->down[l], c->down_s[l], c->down_g[l], c->ws + W.a, C.d_ff, y, rows, C.d_model, C.d_ff, 0, 1.f));
+    DORY_TRY(proj_y(c, c->down[l], c->down_s[l], c->down_g[l], c->ws + W.a, C.d_ff, y, rows, C.d_model, C.d_ff, &y1));
   }
-  HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st, gate));
+  HIP_TRY(c, launch_update(dt, h, y, c->alpha_mlp[l], xb, h2, rows, C.d_model, st, gate, y1));
   if (c->trace)
     HIP_TRY(c, hipMemcpyAsync(c->trace + (size_t)app * rows * C.d_model, h, (size_t)rows * C.d_model * 4,
                               hipMemcpyDeviceToDevice, st));

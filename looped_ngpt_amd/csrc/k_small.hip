@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
 template <typename T, int EPT>
 __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, const float* __restrict__ y,
                                                        const float* __restrict__ alpha, T* __restrict__ xb,
-                                                       float* __restrict__ h2, int d, RowGate gate) {
+                                                       float* __restrict__ h2, int d, RowGate gate,
+                                                       const float* __restrict__ y1) {
   __shared__ float sh[2][kRowThreads / 64];  // one slot per sum: no barrier before either
   if (gate.loops && gate.loop > gate.loops[blockIdx.x / gate.n]) return;  // row past its loop count
   const size_t o = (size_t)blockIdx.x * d;
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(kRowThreads) void k_update(float* __restrict__ h, c
   for (int j = 0; j < EPT; ++j) {
     const int i = threadIdx.x + j * kRowThreads;
     yv[j] = i < d ? y[o + i] : 0.f;
+    if (y1 && i < d) yv[j] += y1[o + i];  // the two halves of a split product, in order
     hv[j] = i < d ? h[o + i] : 0.f;
     ss += yv[j] * yv[j];
   }
@@ -158,13 +160,13 @@ hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, 
 }
 
 hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2, int rows,
-                         int d, hipStream_t st, RowGate gate) {
+                         int d, hipStream_t st, RowGate gate, const float* y1) {
   if (rows <= 0) return hipSuccess;
   if (gate.loops && gate.n < 1) return hipErrorInvalidValue;
   if (dtype == 0)
-    DORY_ROW_LAUNCH(k_update, float, d, rows, st, h, y, alpha, (float*)xb, h2, d, gate);
+    DORY_ROW_LAUNCH(k_update, float, d, rows, st, h, y, alpha, (float*)xb, h2, d, gate, y1);
   else
-    DORY_ROW_LAUNCH(k_update, bf16, d, rows, st, h, y, alpha, (bf16*)xb, h2, d, gate);
+    DORY_ROW_LAUNCH(k_update, bf16, d, rows, st, h, y, alpha, (bf16*)xb, h2, d, gate, y1);
   return hipGetLastError();
 }
 

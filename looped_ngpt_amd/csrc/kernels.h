@@ -28,8 +28,10 @@ hipError_t launch_embed(int dtype, const int32_t* tok, const void* E, float* h, 
                         int rows, int d, int vocab, int* err, hipStream_t st);
 
 // nGPT step per row: h = norm(h + alpha * (norm(y) - h)); xb = h (dtype); h2 (optional) = h.
+// y1 (optional): y is the sum y + y1 of a split product's two halves.
 hipError_t launch_update(int dtype, float* h, const float* y, const float* alpha, void* xb, float* h2,
-                         int rows, int d, hipStream_t st, RowGate gate = RowGate{nullptr, 0, 1});
+                         int rows, int d, hipStream_t st, RowGate gate = RowGate{nullptr, 0, 1},
+                         const float* y1 = nullptr);
 
 // Loop re-injection per row: h = norm(wh * h + we * e); xb = h (dtype).
 hipError_t launch_combine(int dtype, float* h, const float* e, float wh, float we, void* xb, int rows,
@@ -191,6 +193,13 @@ hipError_t launch_gemm(int dtype, const void* x, int64_t ldx, const void* W, voi
 // whose output tiles alone fill at most half of the CUs (gemm_split2_pays).
 // Needs K % 128 == 0 and 16-byte aligned operands, else hipErrorInvalidValue.
 bool gemm_split2_pays(int dtype, int M, int N, int K);
+// 9..64 rows (batched decode), bfloat16, float32 out: the batched-decode GEMM
+// with its contraction in two halves side by side, y0 = x[:, :K/2] . W[:, :K/2]^T
+// and y1 = the rest (the reader adds y0 + y1), when its output tiles alone
+// leave CUs idle (gemm_skinny_split2_pays). K % 128 == 0.
+bool gemm_skinny_split2_pays(int dtype, int M, int N, int K);
+hipError_t launch_gemm_skinny_split2(const void* x, int64_t ldx, const void* W, float* y0, float* y1, int M, int N,
+                                     int K, float scale, hipStream_t st);
 hipError_t launch_gemm_split2(const void* x, int64_t ldx, const void* W, float* y0, float* y1, int M, int N, int K,
                               float scale, hipStream_t st);
 

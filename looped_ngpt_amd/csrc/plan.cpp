@@ -147,6 +147,7 @@ WsLayout make_ws_layout(const Plan& p) {
   w.part = take((dec > pre ? dec : pre) * (c.head_dim + 2) * 4);
   w.ob = take(R * p.q_dim * el);
   w.y = take(R * c.d_model * 4);
+  w.y1 = take(std::min<size_t>(R, 64) * c.d_model * 4);
   w.a = take(R * c.d_ff * el);
   w.logits = take((size_t)c.max_batch * c.vocab * 4);
   w.next = take((size_t)c.max_batch * 4);

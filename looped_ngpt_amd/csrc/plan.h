@@ -43,6 +43,7 @@ struct WsLayout {
   size_t part = 0;                     // attention partials f32
   size_t ob = 0;                       // [rows, q_dim] dtype
   size_t y = 0;                        // [rows, d] f32
+  size_t y1 = 0;                       // [min(rows, 64), d] f32: second half of a split batched-decode product
   size_t a = 0;                        // [rows, d_ff] dtype
   size_t logits = 0;                   // [max_batch, vocab] f32
   size_t next = 0;                     // [max_batch] int32

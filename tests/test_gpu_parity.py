@@ -368,11 +368,14 @@ def test_nvfp4_weights_generate(name, k, mode, n, steps, ctx):
 # split merge and the tiled GEMMs (low-bit weights expanded to bfloat16)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,fmt,B", [("tiny_bf16", "bf16", 10), ("tiny_bf16", "bf16", 7),
+                                        # 36-layer widths: the output (K 3072) and down (K 8192)
+                                        # projections split their contraction in two at 9..64 rows
+                                        ("c36w", "bf16", 12), ("c36w", "bf16", 36),
                                         ("tiny_mx", "mxfp8", 10), ("tiny_mx", "mxfp8", 5),
                                         ("tiny_mx", "nvfp4", 3), ("tiny_mx", "nvfp4", 9)])
 def test_batched_decode_row_paths(name, fmt, B):
     m, w, dw = model_and_weights(name)
-    k, n, steps, ctx = 2, 40, 6, 64
+    k, n, steps, ctx = (2, 40, 6, 64) if name != "c36w" else (2, 16, 4, 64)
     prompt = make_tokens(m, 70 + B, (B, n))
     if fmt == "bf16":
         ow, gw, wf = w, dw, dory.WEIGHTS_DTYPE
