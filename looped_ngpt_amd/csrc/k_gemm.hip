@@ -430,13 +430,12 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
   }
 }
 
-template <int MB, int EPI, int D, int OB>
+template <int MB, int EPI, int D>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X, int64_t ldx,
                                                      const bf16* __restrict__ W, void* __restrict__ C, int M, int N,
                                                      int K, float scale, int64_t ldw, void* __restrict__ C1) {
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;  // weight blocks (u, v)
-  constexpr int NB = OB / 16;                    // 16-output blocks per workgroup
-  constexpr int ROWS = MB + OB * NR;             // window rows: X, then weights
+  constexpr int ROWS = MB + 16 * NR;             // window rows: X, then weights
   constexpr int NL = ROWS / 8;                   // 1 KB loads per window
   constexpr int LMAX = (NL + 3) / 4;             // loads per wave at most
   constexpr int WIN = ROWS * 128;                // window bytes
@@ -444,7 +443,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X,
   extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nout = EPI == EPI_SWIGLU ? N / 2 : N;
-  const int o0 = blockIdx.x * OB;
+  const int o0 = blockIdx.x * 16;
   const int nl = wave < NL ? (NL - wave + 3) / 4 : 0;  // this wave's loads per window (wave-uniform)
   // part blockIdx.y of a contraction split in two: columns y K .. y K + K - 1
   // of X and W (rows ldw apart), its sums into C (y = 0) or C1 (y = 1)
@@ -465,8 +464,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X,
       base = X + (size_t)min(r, M - 1) * ldx;
     } else {
       const int wr = r - MB;
-      const int o = min(o0 + wr % OB, nout - 1);
-      base = W + (size_t)((wr >= OB ? nout : 0) + o) * ldw;
+      const int o = min(o0 + (wr & 15), nout - 1);
+      base = W + (size_t)((wr >= 16 ? nout : 0) + o) * ldw;
     }
     src[i] = base + (ls ^ ((r >> 1) & 7)) * 8;
   }
@@ -481,11 +480,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X,
   // wave w multiplies X rows 16w..16w+15 (waves past MB/16 only load)
   const bool active = wave < MB / 16;
   const int r16 = lane & 15, cq = lane >> 4;
-  f32x4_t acc[NR][NB];
+  f32x4_t acc[NR];
 #pragma unroll
-  for (int j = 0; j < NR; ++j)
-#pragma unroll
-    for (int q = 0; q < NB; ++q) acc[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto mul = [&](int kt) {
     const unsigned char* st = smem + (kt % D) * WIN;
 #pragma unroll
@@ -493,12 +490,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X,
       const int c = 4 * s + cq;  // 16-byte chunk: K elements 32 s + 8 (lane / 16) ..
       const bf16x8_t a = *(const bf16x8_t*)(st + big_off(16 * wave + r16, c));
 #pragma unroll
-      for (int j = 0; j < NR; ++j)
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const bf16x8_t w = *(const bf16x8_t*)(st + big_off(MB + OB * j + 16 * q + r16, c));
-          acc[j][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j][q], 0, 0, 0);
-        }
+      for (int j = 0; j < NR; ++j) {
+        const bf16x8_t w = *(const bf16x8_t*)(st + big_off(MB + 16 * j + r16, c));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j], 0, 0, 0);
+      }
     }
   };
 
@@ -524,31 +519,28 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ X,
   }
   if (!active) return;
   // D layout of a 16x16 block: register i of lane l -> row 4 (l / 16) + i, column l % 16
+  const int o = o0 + r16;
+  if (o >= nout) return;
 #pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    const int o = o0 + 16 * q + r16;
-    if (o >= nout) break;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * wave + 4 * cq + i;
-      if (m >= M) continue;
-      if (EPI == EPI_SWIGLU)
-        ((bf16*)C)[(size_t)m * nout + o] = from_f<bf16>(acc[0][q][i] * scale * silu_(acc[NR - 1][q][i] * scale));
-      else
-        ((float*)C)[(size_t)m * N + o] = acc[0][q][i] * scale;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int m = 16 * wave + 4 * cq + i;
+    if (m >= M) continue;
+    if (EPI == EPI_SWIGLU)
+      ((bf16*)C)[(size_t)m * nout + o] = from_f<bf16>(acc[0][i] * scale * silu_(acc[1][i] * scale));
+    else
+      ((float*)C)[(size_t)m * N + o] = acc[0][i] * scale;
   }
 }
 
-template <int MB, int EPI, int D, int OB = 16>
+template <int MB, int EPI, int D>
 static void skinny_launch_mb(dim3 grid, const bf16* x, int64_t ldx, const bf16* W, void* y, int M, int N, int K,
                              float scale, hipStream_t st, int64_t ldw = -1, void* y1 = nullptr) {
   constexpr int NR = EPI == EPI_SWIGLU ? 2 : 1;
-  constexpr uint32_t lds = D * (MB + OB * NR) * 128;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_skinny<MB, EPI, D, OB>,
+  constexpr uint32_t lds = D * (MB + 16 * NR) * 128;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_skinny<MB, EPI, D>,
                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
-  dory_launch((k_gemm_skinny<MB, EPI, D, OB>), grid, dim3(256), lds, st, x, ldx, W, y, M, N, K, scale,
+  dory_launch((k_gemm_skinny<MB, EPI, D>), grid, dim3(256), lds, st, x, ldx, W, y, M, N, K, scale,
               ldw < 0 ? (int64_t)K : ldw, y1);
 }
 
