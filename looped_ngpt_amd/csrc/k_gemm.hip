@@ -8,7 +8,8 @@
 //  * k_gemm_big: M >= 1024, bfloat16, K % 64 == 0. 256 x BN workgroup tiles
 //    (BN 256 or 192), eight waves on v_mfma_f32_32x32x16_bf16, direct
 //    global->LDS loads into a three / two slot ring, XCD-aware tile order.
-//  * k_gemm_skinny: 9..64 rows (batched decode), weight-stream bound.
+//  * k_gemm_skinny: 9..64 rows (batched decode), weight-stream bound; the
+//    narrow projections' contraction optionally in two halves side by side.
 //  * k_gemm_mfma: the remaining bfloat16 shapes, 128 x 128 tiles.
 //  * k_gemm_simple: float32 models and unaligned shapes.
 #include "common.h"
@@ -409,6 +410,9 @@ static int big_tile_n(int M, int N, int splits = 1) {
 // Every workgroup streams all of X (M x K) from L2 beside its 16 weight rows;
 // operand loads taken straight from global memory in the MFMA layout (16
 // rows per 16-lane group) ran the wide projections at about half this rate.
+// A projection whose 16-output tiles leave CUs idle (N = 3072: 192 tiles) can
+// run its contraction in two halves side by side (blockIdx.y; weight rows ldw
+// apart, the second half's sums into C1), which its reader adds.
 // Requires K % 64 == 0 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
