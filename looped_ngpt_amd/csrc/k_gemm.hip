@@ -163,7 +163,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16* __restrict__ A, i
 //
 // Workgroups are spread over the 8 XCDs in contiguous runs of tiles, grouped
 // four M tiles at a time, so the tiles that run together on one XCD share A
-// and B rows in its L2. SwiGLU (BN = 256 only): B tile rows come in 32-row
+// and B rows in its L2. The grid is one workgroup per CU at most and each
+// walks its XCD's run (persistent): the next tile's first two stages go out
+// before the current tile's stores, so a tile change waits for no launch and
+// for little load latency (1-1.5% on the 8192-row shapes). SwiGLU (BN = 256 only): B tile rows come in 32-row
 // chunks u, v, u, v of the same outputs, and a wave's two 32-column blocks
 // are one (u, v) pair. Requires K % 64 == 0 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
@@ -218,8 +221,12 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
   const int nN = EPI == EPI_SWIGLU ? (F + 127) / 128 : (N + BN - 1) / BN;
   const int nt = nM * nN;
   const int per = (nt + 7) / 8;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= nt) return;
+  // persistent: the workgroups of XCD x (blockIdx.x % 8) walk that XCD's run
+  // of tiles x per .. x per + per - 1 in strides of the workgroups it holds
+  const int xs = (int)(gridDim.x >> 3);
+  const int tbase = (blockIdx.x & 7) * per, tend = min(tbase + per, nt);
+  int t = tbase + (blockIdx.x >> 3);
+  if (t >= tend) return;
   // split of the contraction (blockIdx.y): columns y K .. y K + K - 1 of A
   // and B, partial sums into C (y = 0) or C1 (y = 1)
   if (blockIdx.y) {
@@ -227,33 +234,37 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
     B += (size_t)blockIdx.y * K;
     C = C1;
   }
-  const int grp = t / (kBigGroupM * nN);
-  const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
-  const int loc = t - grp * kBigGroupM * nN;
-  const int m0 = (grp * kBigGroupM + loc % gs) * 256;
-  const int n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * BN;
-
   const int lr = lane >> 3, ls = lane & 7;
   const bf16* srcA[kLA];
   const bf16* srcB[kLB];
+  int m0, n0;
+  // tile t: its corner and this thread's direct-load sources
+  auto setup = [&](int tt) __attribute__((always_inline)) {
+    const int grp = tt / (kBigGroupM * nN);
+    const int gs = min(kBigGroupM, nM - grp * kBigGroupM);
+    const int loc = tt - grp * kBigGroupM * nN;
+    m0 = (grp * kBigGroupM + loc % gs) * 256;
+    n0 = EPI == EPI_SWIGLU ? (loc / gs) * 128 : (loc / gs) * BN;
 #pragma unroll
-  for (int i = 0; i < kLA; ++i) {
-    const int r = (wave * kLA + i) * 8 + lr;
-    srcA[i] = A + (size_t)min(m0 + r, M - 1) * lda + (ls ^ ((r >> 1) & 7)) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < kLB; ++i) {
-    const int r = (wave * kLB + i) * 8 + lr;
-    int wr;
-    if (EPI == EPI_SWIGLU) {
-      const int nb = r >> 5;
-      const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
-      wr = (nb & 1 ? F : 0) + o;
-    } else {
-      wr = min(n0 + r, N - 1);
+    for (int i = 0; i < kLA; ++i) {
+      const int r = (wave * kLA + i) * 8 + lr;
+      srcA[i] = A + (size_t)min(m0 + r, M - 1) * lda + (ls ^ ((r >> 1) & 7)) * 8;
     }
-    srcB[i] = B + (size_t)wr * ldb + (ls ^ ((r >> 1) & 7)) * 8;
-  }
+#pragma unroll
+    for (int i = 0; i < kLB; ++i) {
+      const int r = (wave * kLB + i) * 8 + lr;
+      int wr;
+      if (EPI == EPI_SWIGLU) {
+        const int nb = r >> 5;
+        const int o = min(n0 + (nb >> 1) * 32 + (r & 31), F - 1);
+        wr = (nb & 1 ? F : 0) + o;
+      } else {
+        wr = min(n0 + r, N - 1);
+      }
+      srcB[i] = B + (size_t)wr * ldb + (ls ^ ((r >> 1) & 7)) * 8;
+    }
+  };
+  setup(t);
   auto issueA = [&](int kt, int i0, int i1) {
     unsigned char* st = sA + (kt % 3) * kHA;
 #pragma unroll
@@ -266,12 +277,6 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
   };
 
   f32x16_t acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nK = K / kBigBK;
   const int l32 = lane & 31, lh = lane >> 5;
@@ -292,18 +297,26 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
   };
 
   bf16x8_t fa[2][MI], fb[2][NJ];
-  issueA(0, 0, kLA);
-  issueB(0);
-  if (nK > 1) {
-    issueA(1, 0, kLA);
-    issueB(1);
-    DORY_WAIT_VM(kLA + kLB);
-  } else {
-    DORY_WAIT_VM(0);
-  }
+  auto issue01 = [&]() __attribute__((always_inline)) {
+    issueA(0, 0, kLA);
+    issueB(0);
+    if (nK > 1) {
+      issueA(1, 0, kLA);
+      issueB(1);
+    }
+  };
+  issue01();
+  if (nK > 1) DORY_WAIT_VM(kLA + kLB); else DORY_WAIT_VM(0);
+  for (;;) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   frag(0, 0, fa[0], fb[0]);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   DORY_WAIT_LGKM0();
   constexpr int c0[3] = {0, kLA / 3, 2 * kLA / 3}, c1[3] = {kLA / 3, 2 * kLA / 3, kLA};
   for (int kt = 0; kt < nK; ++kt) {
@@ -348,27 +361,39 @@ __global__ __launch_bounds__(512) void k_gemm_big(const bf16* __restrict__ A, in
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  // the next tile's first two stages go out before this tile's stores (every
+  // wave is past the last barrier, so no stage slot is still read)
+  const int m0c = m0, n0c = n0;
+  const int tn = t + xs;
+  if (tn < tend) {
+    setup(tn);
+    issue01();
+  }
 
   // C layout of a 32x32 block: register r of lane l -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int row = m0c + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
         // this wave's blocks (0, 1) are the u and v rows of outputs n0 + wn * 32 + 0..31
-        const int o = n0 + wn * 32 + l32;
+        const int o = n0c + wn * 32 + l32;
         if (o < F)
           ((bf16*)C)[(size_t)row * F + o] = from_f<bf16>(acc[i][0][r] * scale * silu_(acc[i][1][r] * scale));
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int col = n0 + wn * TN + j * 32 + l32;
+          const int col = n0c + wn * TN + j * 32 + l32;
           if (col < N) ((float*)C)[(size_t)row * N + col] = acc[i][j][r] * scale;
         }
       }
     }
+  }
+  if (tn >= tend) break;
+  t = tn;
+  DORY_WAIT_VM(0);  // the next tile's stages (and this tile's stores)
   }
 }
 
@@ -673,9 +698,9 @@ static hipError_t gemm_dispatch(const T* x, int64_t ldx, const T* W, void* y, in
     const int bn = EPI == EPI_SWIGLU ? 256 : big_tile_n(M, N);
     const int tiles = ((M + 255) / 256) * (EPI == EPI_SWIGLU ? (nout + 127) / 128 : (N + bn - 1) / bn);
     if (bn == 192)
-      big_launch<EPI_F32, 192>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
+      big_launch<EPI_F32, 192>(dim3(std::min((tiles + 7) / 8, kNumCUs / 8) * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
     else
-      big_launch<EPI, 256>(dim3((tiles + 7) / 8 * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
+      big_launch<EPI, 256>(dim3(std::min((tiles + 7) / 8, kNumCUs / 8) * 8), (const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st, K);
   } else if (sizeof(T) == 2 && al16 && K % kStrBK == 0 && M <= 64) {
     skinny_launch<EPI>((const bf16*)x, ldx, (const bf16*)W, y, M, N, K, scale, st);
   } else if (sizeof(T) == 2 && K % 8 == 0 && al16) {
@@ -704,7 +729,7 @@ hipError_t launch_gemm_split2(const void* x, int64_t ldx, const void* W, float* 
   if (!al16 || K % (2 * kBigBK) != 0 || y0 == nullptr || y1 == nullptr) return hipErrorInvalidValue;
   const int bn = big_tile_n(M, N, 2);
   const int tiles = ((M + 255) / 256) * ((N + bn - 1) / bn);
-  const dim3 grid((tiles + 7) / 8 * 8, 2);
+  const dim3 grid(std::min((tiles + 7) / 8, kNumCUs / 16) * 8, 2);
   if (bn == 192)
     big_launch<EPI_F32, 192>(grid, (const bf16*)x, ldx, (const bf16*)W, y0, M, N, K / 2, scale, st, K, y1);
   else
