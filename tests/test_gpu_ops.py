@@ -39,6 +39,9 @@ CASES = [
     # M >= 1024: the 256x256-tile kernel (ragged M and N tiles, both epilogues, K multiple of 32)
     ("bf16", 1100, 1000, 3072, 0, 2), ("bf16", 1030, 2 * 1000, 2304, 1, 2), ("bf16", 2048, 3072, 1088, 0, 2),
     ("bf16", 1024, 2 * 384, 3072, 1, 2),
+    # more tiles than CUs: each persistent workgroup walks several tiles of its XCD's run, ragged
+    # last M and N tiles among them (561 tiles of 256 x 256; 297 SwiGLU tiles)
+    ("bf16", 4200, 8200, 1088, 0, 2), ("bf16", 2100, 2 * 4100, 640, 1, 2),
 ]
 
 
